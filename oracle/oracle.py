@@ -1,0 +1,269 @@
+"""ctypes wrapper of the fp64 CPU oracle (hikvp_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+cpu_baseline leg of the benchmark, never by the GPU library.  It converts
+host arrays (numpy or CPU torch tensors) to C-contiguous buffers and marshals
+them; all arithmetic happens in the C file.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+
+from . import build as _build
+
+F32, BF16, F64 = 0, 1, 2
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_F64P = ctypes.POINTER(ctypes.c_double)
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int64), ("N", ctypes.c_int64), ("S_kv", ctypes.c_int64),
+        ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64), ("d", ctypes.c_int64),
+        ("M_R", ctypes.c_int64), ("M_I", ctypes.c_int64), ("M", ctypes.c_int64),
+        ("q", ctypes.c_void_p), ("q_kg", ctypes.c_void_p),
+        ("root_k", ctypes.c_void_p), ("mid_k", ctypes.c_void_p),
+        ("leaf_k", ctypes.c_void_p), ("leaf_v", ctypes.c_void_p),
+        ("root_off", _I64P), ("mid_off", _I64P),
+        ("seq_k", ctypes.c_void_p), ("seq_v", ctypes.c_void_p),
+        ("K", ctypes.c_int32 * 3),
+        ("scale", ctypes.c_double),
+    ]
+
+
+class _Outputs(ctypes.Structure):
+    _fields_ = [
+        ("sel_R", _I64P), ("sel_I", _I64P), ("sel_L", _I64P),
+        ("logit_L", _F64P), ("gap", _F64P), ("n_cand", _I64P),
+        ("lse_kg", _F64P), ("lse_seq", _F64P),
+        ("lam_kg", _F64P), ("lam_seq", _F64P),
+        ("o_kg", _F64P), ("o_seq", _F64P), ("out", _F64P),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = _build.LIB
+        if not os.path.exists(path):
+            _build.build()
+        L = ctypes.CDLL(path)
+        L.oracle_tree_sizes.argtypes = [ctypes.c_int64, _I64P]
+        L.oracle_tree_sizes.restype = ctypes.c_int
+        L.oracle_topk.argtypes = [ctypes.c_int64, _F64P, _I64P, ctypes.c_int64, _I64P]
+        L.oracle_topk.restype = ctypes.c_int64
+        L.oracle_level_scores.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int, _I64P, ctypes.c_int64,
+                                          _I64P, _F64P, ctypes.c_int64]
+        L.oracle_level_scores.restype = ctypes.c_int64
+        rows_sig = [ctypes.POINTER(_Problem), ctypes.c_int64, _I64P, _I64P, _I64P]
+        L.oracle_hikvp_rows.argtypes = rows_sig + [ctypes.POINTER(_Outputs)]
+        L.oracle_hikvp_rows.restype = ctypes.c_int
+        L.oracle_select_mids_rows.argtypes = rows_sig + [ctypes.POINTER(_Outputs)]
+        L.oracle_select_mids_rows.restype = ctypes.c_int
+        L.oracle_finish_rows.argtypes = rows_sig + [_I64P, _I64P, ctypes.c_void_p, ctypes.c_void_p,
+                                                    _I64P, ctypes.POINTER(_Outputs)]
+        L.oracle_finish_rows.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _host(x):
+    """(numpy array, storage code) for a numpy array or a CPU torch tensor."""
+    if x is None:
+        return None, None
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu").contiguous()
+            if x.dtype == torch.bfloat16:
+                return x.view(torch.int16).numpy(), BF16
+            if x.dtype == torch.float32:
+                return x.numpy(), F32
+            if x.dtype == torch.float64:
+                return x.numpy(), F64
+            if x.dtype == torch.int64:
+                return x.numpy(), None
+            raise TypeError(f"unsupported tensor dtype {x.dtype}")
+    except ImportError:
+        pass
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, F32
+    if x.dtype == np.float64:
+        return x, F64
+    if x.dtype == np.int64:
+        return x, None
+    raise TypeError(f"unsupported array dtype {x.dtype}")
+
+
+def _offsets(x):
+    """int64 numpy copy of CSR offsets given as a list, array or tensor."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int64))
+
+
+def _vp(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _ip(a):
+    return None if a is None else a.ctypes.data_as(_I64P)
+
+
+def _fp(a):
+    return None if a is None else a.ctypes.data_as(_F64P)
+
+
+class Problem:
+    """One HiKVP layer call: q [B,N,Hq,d], tree keys [Hkv,M_x,d], leaf values,
+    int64 child offsets, sequence K/V [B,S_kv,Hkv,d] (None -> no sequence)."""
+
+    def __init__(self, q, root_k, mid_k, leaf_k, leaf_v, root_off, mid_off,
+                 seq_k, seq_v, K, scale=None, q_kg=None):
+        self._keep = []
+        qa, dt = _host(q)
+        B, N, Hq, d = qa.shape
+        rk, dt_r = _host(root_k)
+        mk, dt_m = _host(mid_k)
+        lk, dt_l = _host(leaf_k)
+        lv, _ = _host(leaf_v)
+        ro = _offsets(root_off)
+        mo = _offsets(mid_off)
+        sk, _ = _host(seq_k)
+        sv, _ = _host(seq_v)
+        qk, _ = _host(q_kg)
+        for other in (dt_r, dt_m):
+            if other != dt:
+                raise TypeError("all floating inputs must share one storage type")
+        Hkv = rk.shape[0]
+        self.shape = dict(B=B, N=N, Hq=Hq, Hkv=Hkv, d=d, M_R=rk.shape[1], M_I=mk.shape[1],
+                          M=(lk.shape[1] if lk is not None else int(mo[-1])),
+                          S_kv=(sk.shape[1] if sk is not None else 0))
+        self.K = tuple(int(k) for k in K)
+        self.scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+        self.dtype = dt
+        P = _Problem()
+        P.dtype = dt
+        for k in ("B", "N", "S_kv", "Hq", "Hkv", "d", "M_R", "M_I", "M"):
+            setattr(P, k, self.shape[k])
+        P.q, P.q_kg = _vp(qa), _vp(qk)
+        P.root_k, P.mid_k, P.leaf_k, P.leaf_v = _vp(rk), _vp(mk), _vp(lk), _vp(lv)
+        P.root_off, P.mid_off = _ip(ro), _ip(mo)
+        P.seq_k, P.seq_v = _vp(sk), _vp(sv)
+        P.K = (ctypes.c_int32 * 3)(*self.K)
+        P.scale = self.scale
+        self._P = P
+        self._keep = [qa, rk, mk, lk, lv, ro, mo, sk, sv, qk]
+        self.root_off, self.mid_off = ro, mo
+
+
+def all_rows(B, N, Hq):
+    """(b, n, h) of every row in memory order of [B, N, Hq]."""
+    b, n, h = np.meshgrid(np.arange(B), np.arange(N), np.arange(Hq), indexing="ij")
+    return np.stack([b.ravel(), n.ravel(), h.ravel()], axis=1).astype(np.int64)
+
+
+def _alloc_outputs(nrows, K, d):
+    KR, KI, KL = K
+    o = dict(
+        sel_R=np.full((nrows, KR), -1, np.int64), sel_I=np.full((nrows, KI), -1, np.int64),
+        sel_L=np.full((nrows, KL), -1, np.int64), logit_L=np.full((nrows, KL), np.nan),
+        gap=np.full((nrows, 3), np.inf), n_cand=np.zeros((nrows, 3), np.int64),
+        lse_kg=np.zeros(nrows), lse_seq=np.zeros(nrows), lam_kg=np.zeros(nrows),
+        lam_seq=np.zeros(nrows), o_kg=np.zeros((nrows, d)), o_seq=np.zeros((nrows, d)),
+        out=np.zeros((nrows, d)))
+    O = _Outputs()
+    for k in ("sel_R", "sel_I", "sel_L", "n_cand"):
+        setattr(O, k, _ip(o[k]) if o[k].size else None)
+    for k in ("logit_L", "gap", "lse_kg", "lse_seq", "lam_kg", "lam_seq", "o_kg", "o_seq", "out"):
+        setattr(O, k, _fp(o[k]) if o[k].size else None)
+    return o, O
+
+
+def _rows(rows):
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+    return r, np.ascontiguousarray(r[:, 0]), np.ascontiguousarray(r[:, 1]), np.ascontiguousarray(r[:, 2])
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"{what} failed with code {rc}")
+
+
+def hikvp_rows(prob: Problem, rows):
+    """Full forward for the given (b, n, h) rows; dict of numpy arrays."""
+    r, b, n, h = _rows(rows)
+    o, O = _alloc_outputs(len(r), prob.K, prob.shape["d"])
+    _check(lib().oracle_hikvp_rows(ctypes.byref(prob._P), len(r), _ip(b), _ip(n), _ip(h),
+                                   ctypes.byref(O)), "oracle_hikvp_rows")
+    return o
+
+
+def select_mids_rows(prob: Problem, rows):
+    """Two-phase mode, phase 1: sel_R, sel_I, gaps for the given rows."""
+    r, b, n, h = _rows(rows)
+    o, O = _alloc_outputs(len(r), prob.K, prob.shape["d"])
+    _check(lib().oracle_select_mids_rows(ctypes.byref(prob._P), len(r), _ip(b), _ip(n), _ip(h),
+                                         ctypes.byref(O)), "oracle_select_mids_rows")
+    return o
+
+
+def finish_rows(prob: Problem, rows, cand_off, cand_idx, cand_k, cand_v, forced_sel_L=None):
+    """Two-phase phase 2 / replay: leaf candidates passed explicitly per row."""
+    r, b, n, h = _rows(rows)
+    co = np.ascontiguousarray(np.asarray(cand_off, dtype=np.int64))
+    ci = np.ascontiguousarray(np.asarray(cand_idx, dtype=np.int64))
+    ck, dk = _host(cand_k)
+    cv, _ = _host(cand_v)
+    if dk != prob.dtype:
+        raise TypeError("candidate storage type differs from the problem's")
+    fs = None if forced_sel_L is None else np.ascontiguousarray(np.asarray(forced_sel_L, dtype=np.int64))
+    o, O = _alloc_outputs(len(r), prob.K, prob.shape["d"])
+    _check(lib().oracle_finish_rows(ctypes.byref(prob._P), len(r), _ip(b), _ip(n), _ip(h),
+                                    _ip(co), _ip(ci), _vp(ck), _vp(cv), _ip(fs), ctypes.byref(O)),
+           "oracle_finish_rows")
+    return o
+
+
+def level_scores(prob: Problem, b, n, h, level, parents=()):
+    """Candidates of one row at one level with their fp64 scaled scores."""
+    par = np.ascontiguousarray(np.asarray(parents, dtype=np.int64))
+    s = prob.shape
+    cap = max(1, s["M_R"], s["M_I"], s["M"])
+    if level == 1:
+        cap = max(1, int(np.diff(prob.root_off).max(initial=0)) * max(1, len(par)))
+    elif level == 2:
+        cap = max(1, int(np.diff(prob.mid_off).max(initial=0)) * max(1, len(par)))
+    cand = np.zeros(cap, np.int64)
+    score = np.zeros(cap)
+    c = lib().oracle_level_scores(ctypes.byref(prob._P), int(b), int(n), int(h), int(level),
+                                  _ip(par) if len(par) else None, len(par), _ip(cand), _fp(score), cap)
+    if c < 0:
+        raise RuntimeError("oracle_level_scores: capacity exceeded")
+    return cand[:c], score[:c]
+
+
+def tree_sizes(M):
+    """(S, M_I, M_R) from the clustering section's level-size formulas."""
+    out = np.zeros(3, np.int64)
+    _check(lib().oracle_tree_sizes(int(M), _ip(out)), "oracle_tree_sizes")
+    return int(out[0]), int(out[1]), int(out[2])
+
+
+def topk(score, index, K):
+    """Positions of the first min(K, n) by (score desc, index asc)."""
+    s = np.ascontiguousarray(np.asarray(score, dtype=np.float64))
+    i = np.ascontiguousarray(np.asarray(index, dtype=np.int64))
+    out = np.zeros(max(1, min(int(K), len(s))), np.int64)
+    k = lib().oracle_topk(len(s), _fp(s), _ip(i), int(K), _ip(out))
+    if k < 0:
+        raise MemoryError("oracle_topk")
+    return out[:k]
