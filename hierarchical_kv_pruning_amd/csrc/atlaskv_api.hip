@@ -1,0 +1,453 @@
+// atlaskv_api.hip -- the C ABI of libatlaskv.so (declared in include/atlaskv.h):
+// argument checks, workspace planning and the launch sequence of one HiKVP
+// attention call on the caller's stream.
+//
+// Page: "AtlasKV: Augmenting LLMs with Billion-Scale Knowledge Graphs in 20GB
+// VRAM" (digest of arXiv 2510.17934), 速读 › 怎么做的: root scores -> Top-K ->
+// children -> Top-K -> leaves -> Top-K, then the λ merge of the KG and sequence
+// softmaxes.  The launch order below follows those steps.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+
+#include "atlaskv.h"
+#include "hikvp_internal.h"
+
+using namespace hikvp;
+
+struct atlaskv_tree_view_s {
+  TreeDev dev;                 // pointers, strides, sizes (norm -> stats buffer)
+  int64_t maxfan[2];           // largest root and mid fanouts
+  BuildStats* stats;           // device buffer owned by the view (NULL if described only)
+  hipStream_t stream;
+  void* workspace;
+  size_t workspace_bytes;
+  int described_only;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+atlaskv_status fail(atlaskv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+atlaskv_status hip_fail(hipError_t e, const char* what) {
+  return fail(ATLASKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t esize(int32_t dtype) { return dtype == ATLASKV_BF16 ? 2 : 4; }
+
+constexpr int64_t kIndexLimit = (int64_t)1 << 31;  // node counts and rows are int32 on the GPU
+
+// ndim, dtype, innermost stride 1, non-negative sizes/strides, 16-byte rows.
+atlaskv_status check_tensor(const atlaskv_tensor* t, const char* name, int ndim, bool rows16) {
+  if (!t) return fail(ATLASKV_ERR_NULL, "%s is NULL", name);
+  if (t->dtype != ATLASKV_F32 && t->dtype != ATLASKV_BF16)
+    return fail(ATLASKV_ERR_DTYPE, "%s: unknown dtype %d", name, (int)t->dtype);
+  if (t->ndim != ndim) return fail(ATLASKV_ERR_SHAPE, "%s: expected %d dims, got %d", name, ndim, (int)t->ndim);
+  int64_t numel = 1;
+  for (int i = 0; i < ndim; ++i) {
+    if (t->shape[i] < 0 || t->stride[i] < 0)
+      return fail(ATLASKV_ERR_SHAPE, "%s: negative shape or stride in dim %d", name, i);
+    numel *= t->shape[i];
+  }
+  if (numel > 0 && !t->data) return fail(ATLASKV_ERR_NULL, "%s: data is NULL", name);
+  if (t->stride[ndim - 1] != 1) return fail(ATLASKV_ERR_SHAPE, "%s: innermost stride must be 1", name);
+  if (rows16 && numel > 0) {
+    const int64_t es = esize(t->dtype);
+    if (((uintptr_t)t->data) % 16) return fail(ATLASKV_ERR_SHAPE, "%s: data not 16-byte aligned", name);
+    for (int i = 0; i < ndim - 1; ++i)
+      if ((t->stride[i] * es) % 16)
+        return fail(ATLASKV_ERR_SHAPE, "%s: stride of dim %d is not a multiple of 16 bytes", name, i);
+  }
+  return ATLASKV_OK;
+}
+
+atlaskv_status check_tree_tensors(const atlaskv_tensor* root_k, const atlaskv_tensor* mid_k,
+                                  const atlaskv_tensor* leaf_k, const atlaskv_tensor* leaf_v) {
+  atlaskv_status st;
+  if ((st = check_tensor(root_k, "root_k", 3, true))) return st;
+  if ((st = check_tensor(mid_k, "mid_k", 3, true))) return st;
+  if ((st = check_tensor(leaf_k, "leaf_k", 3, true))) return st;
+  if ((st = check_tensor(leaf_v, "leaf_v", 3, true))) return st;
+  const int32_t dt = root_k->dtype;
+  if (mid_k->dtype != dt || leaf_k->dtype != dt || leaf_v->dtype != dt)
+    return fail(ATLASKV_ERR_DTYPE, "tree tensors must share one dtype");
+  const int64_t Hkv = root_k->shape[0], d = root_k->shape[2];
+  if (Hkv < 1) return fail(ATLASKV_ERR_SHAPE, "root_k: need at least one KV head");
+  if (d != 64 && d != 128) return fail(ATLASKV_ERR_UNSUPPORTED, "head dim %lld not in {64, 128}", (long long)d);
+  if (mid_k->shape[0] != Hkv || leaf_k->shape[0] != Hkv || leaf_v->shape[0] != Hkv)
+    return fail(ATLASKV_ERR_SHAPE, "tree tensors disagree on the KV head count");
+  if (mid_k->shape[2] != d || leaf_k->shape[2] != d || leaf_v->shape[2] != d)
+    return fail(ATLASKV_ERR_SHAPE, "tree tensors disagree on the head dim");
+  if (leaf_v->shape[1] != leaf_k->shape[1])
+    return fail(ATLASKV_ERR_SHAPE, "leaf_v and leaf_k disagree on the leaf count");
+  if (root_k->shape[1] >= kIndexLimit || mid_k->shape[1] >= kIndexLimit || leaf_k->shape[1] >= kIndexLimit)
+    return fail(ATLASKV_ERR_UNSUPPORTED, "node counts must be below 2^31");
+  return ATLASKV_OK;
+}
+
+void fill_tree(TreeDev& t, const atlaskv_tensor* root_k, const atlaskv_tensor* mid_k,
+               const atlaskv_tensor* leaf_k, const atlaskv_tensor* leaf_v) {
+  const atlaskv_tensor* ts[4] = {root_k, mid_k, leaf_k, leaf_v};
+  for (int i = 0; i < 4; ++i) {
+    if (i < 3) t.key[i] = ts[i]->data;
+    t.hs[i] = ts[i]->stride[0];
+    t.rs[i] = ts[i]->stride[1];
+  }
+  t.leaf_v = leaf_v->data;
+  t.count[0] = root_k->shape[1];
+  t.count[1] = mid_k->shape[1];
+  t.count[2] = leaf_k->shape[1];
+  t.Hkv = (int)root_k->shape[0];
+  t.d = (int)root_k->shape[2];
+  t.dtype = root_k->dtype;
+  t.off[0] = t.off[1] = nullptr;
+  t.norm = nullptr;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+  int B, N, Hq, S, R, G;
+  int K[3];
+  int64_t cmax;
+  double scale;
+  size_t off_scores, off_band_node, off_band_s, off_sel[3], off_okg, off_lse, total;
+};
+
+// Candidate capacity per row: roots; children of K_R roots; children of K_I mids.
+int64_t candidate_capacity(const atlaskv_tree_view_s* v, const int K[3]) {
+  const int64_t MR = v->dev.count[0], MI = v->dev.count[1], M = v->dev.count[2];
+  int64_t c1 = (K[0] < MR ? K[0] : MR) * v->maxfan[0];
+  if (c1 > MI) c1 = MI;
+  int64_t c2 = (K[1] < MI ? K[1] : MI) * v->maxfan[1];
+  if (c2 > M) c2 = M;
+  int64_t c = MR;
+  if (c1 > c) c = c1;
+  if (c2 > c) c = c2;
+  return c < 1 ? 1 : c;
+}
+
+atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
+                         const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                         const int32_t Kpl[3], const atlaskv_tensor* out,
+                         const atlaskv_attend_opts* opts, bool need_out, Plan& p) {
+  atlaskv_status st;
+  if (!v) return fail(ATLASKV_ERR_NULL, "tree view is NULL");
+  if (!Kpl) return fail(ATLASKV_ERR_NULL, "K_per_level is NULL");
+  if ((st = check_tensor(q, "q", 4, true))) return st;
+  const TreeDev& t = v->dev;
+  if (q->dtype != t.dtype) return fail(ATLASKV_ERR_DTYPE, "q dtype differs from the tree's");
+  if (q->shape[3] != t.d) return fail(ATLASKV_ERR_SHAPE, "q head dim %lld != tree head dim %d",
+                                      (long long)q->shape[3], t.d);
+  const int64_t B = q->shape[0], N = q->shape[1], Hq = q->shape[2];
+  if (Hq < 1 || Hq % t.Hkv) return fail(ATLASKV_ERR_SHAPE, "Hq=%lld is not a multiple of Hkv=%d",
+                                         (long long)Hq, t.Hkv);
+  if (B * N * Hq >= kIndexLimit) return fail(ATLASKV_ERR_UNSUPPORTED, "B*N*Hq must be below 2^31");
+  if (opts && opts->q_kg) {
+    if ((st = check_tensor(opts->q_kg, "q_kg", 4, true))) return st;
+    if (opts->q_kg->dtype != q->dtype) return fail(ATLASKV_ERR_DTYPE, "q_kg dtype differs from q's");
+    for (int i = 0; i < 4; ++i)
+      if (opts->q_kg->shape[i] != q->shape[i]) return fail(ATLASKV_ERR_SHAPE, "q_kg shape differs from q's");
+  }
+  if ((seq_k == nullptr) != (seq_v == nullptr))
+    return fail(ATLASKV_ERR_NULL, "seq_k and seq_v must both be given or both be NULL");
+  int64_t S = 0;
+  if (seq_k) {
+    if ((st = check_tensor(seq_k, "seq_k", 4, true))) return st;
+    if ((st = check_tensor(seq_v, "seq_v", 4, true))) return st;
+    if (seq_k->dtype != q->dtype || seq_v->dtype != q->dtype)
+      return fail(ATLASKV_ERR_DTYPE, "sequence K/V dtype differs from q's");
+    for (int i = 0; i < 4; ++i)
+      if (seq_v->shape[i] != seq_k->shape[i]) return fail(ATLASKV_ERR_SHAPE, "seq_v shape differs from seq_k's");
+    if (seq_k->shape[0] != B || seq_k->shape[2] != t.Hkv || seq_k->shape[3] != t.d)
+      return fail(ATLASKV_ERR_SHAPE, "seq_k must be [B, S_kv, Hkv, d]");
+    S = seq_k->shape[1];
+    if (S < N) return fail(ATLASKV_ERR_SHAPE, "S_kv=%lld < N=%lld", (long long)S, (long long)N);
+    if (S >= kIndexLimit) return fail(ATLASKV_ERR_UNSUPPORTED, "S_kv must be below 2^31");
+  }
+  if (need_out) {
+    if ((st = check_tensor(out, "out", 4, false))) return st;
+    if (out->dtype != q->dtype && out->dtype != ATLASKV_F32)
+      return fail(ATLASKV_ERR_DTYPE, "out dtype must be q's dtype or fp32");
+    for (int i = 0; i < 4; ++i)
+      if (out->shape[i] != q->shape[i]) return fail(ATLASKV_ERR_SHAPE, "out shape differs from q's");
+  }
+  for (int i = 0; i < 3; ++i)
+    if (Kpl[i] < 0 || Kpl[i] > kMaxK) return fail(ATLASKV_ERR_K, "K[%d]=%d outside 0..%d", i, Kpl[i], kMaxK);
+  const bool kg_empty = Kpl[0] == 0 || Kpl[1] == 0 || Kpl[2] == 0 || t.count[0] == 0 ||
+                        t.count[1] == 0 || t.count[2] == 0;
+  if (kg_empty && !seq_k)
+    return fail(ATLASKV_ERR_K, "both the KG half (K or tree empty) and the sequence half are empty");
+  double scale = 1.0 / sqrt((double)t.d);
+  if (opts && opts->scale != 0.0f) {
+    if (!(opts->scale > 0.0f) || isinf(opts->scale))
+      return fail(ATLASKV_ERR_UNSUPPORTED, "scale must be positive and finite");
+    scale = (double)opts->scale;
+  }
+  p.B = (int)B; p.N = (int)N; p.Hq = (int)Hq; p.S = (int)S;
+  p.R = (int)(B * N * Hq);
+  p.G = (int)(Hq / t.Hkv);
+  for (int i = 0; i < 3; ++i) p.K[i] = Kpl[i];
+  p.cmax = candidate_capacity(v, p.K);
+  p.scale = scale;
+  const size_t R = (size_t)p.R;
+  size_t o = 0;
+  p.off_scores = o;    o = align256(o + R * (size_t)p.cmax * 4);
+  p.off_band_node = o; o = align256(o + R * (size_t)p.cmax * 4);
+  p.off_band_s = o;    o = align256(o + R * (size_t)p.cmax * 8);
+  for (int i = 0; i < 3; ++i) { p.off_sel[i] = o; o = align256(o + R * (size_t)p.K[i] * 4); }
+  p.off_okg = o;       o = align256(o + R * (size_t)t.d * 4);
+  p.off_lse = o;       o = align256(o + R * 4);
+  p.total = o;
+  return ATLASKV_OK;
+}
+
+void fill_rows(RowsDev& r, const atlaskv_tensor* q, const atlaskv_attend_opts* opts, const Plan& p) {
+  const atlaskv_tensor* qk = (opts && opts->q_kg) ? opts->q_kg : q;
+  r.q = q->data;
+  r.q_kg = qk->data;
+  for (int i = 0; i < 3; ++i) { r.qs[i] = q->stride[i]; r.qks[i] = qk->stride[i]; }
+  r.B = p.B; r.N = p.N; r.Hq = p.Hq; r.G = p.G; r.R = p.R;
+  r.scale = p.scale;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* atlaskv_last_error(void) { return g_err.c_str(); }
+
+const char* atlaskv_version(void) { return "atlaskv-mi355x 0.1 (gfx950)"; }
+
+static const char* const kPhaseNames[] = {"score_root", "topk_root", "score_mid", "topk_mid",
+                                          "score_leaf", "topk_leaf_kg_attention", "seq_attention_merge"};
+static const int kPhases = (int)(sizeof kPhaseNames / sizeof kPhaseNames[0]);
+
+int32_t atlaskv_phase_count(void) { return kPhases; }
+
+const char* atlaskv_phase_name(int32_t i) { return (i >= 0 && i < kPhases) ? kPhaseNames[i] : nullptr; }
+
+atlaskv_status atlaskv_build_tree_view(const atlaskv_tensor* root_k, const atlaskv_tensor* mid_k,
+                                       const atlaskv_tensor* leaf_k, const atlaskv_tensor* leaf_v,
+                                       const int64_t* root_child_off, const int64_t* mid_child_off,
+                                       void* stream, atlaskv_tree_view* out) {
+  if (!out) return fail(ATLASKV_ERR_NULL, "out is NULL");
+  atlaskv_status st = check_tree_tensors(root_k, mid_k, leaf_k, leaf_v);
+  if (st) return st;
+  if (!root_child_off || !mid_child_off) return fail(ATLASKV_ERR_NULL, "child offsets are NULL");
+  atlaskv_tree_view_s* v = (atlaskv_tree_view_s*)calloc(1, sizeof(atlaskv_tree_view_s));
+  if (!v) return fail(ATLASKV_ERR_HIP, "host allocation failed");
+  fill_tree(v->dev, root_k, mid_k, leaf_k, leaf_v);
+  v->dev.off[0] = root_child_off;
+  v->dev.off[1] = mid_child_off;
+  v->stream = (hipStream_t)stream;
+  const int Hkv = v->dev.Hkv;
+  const size_t stats_bytes = offsetof(BuildStats, norm_bits) + sizeof(unsigned int) * 3 * (size_t)Hkv;
+  hipError_t e = hipMalloc((void**)&v->stats, stats_bytes);
+  if (e != hipSuccess) { free(v); return hip_fail(e, "hipMalloc(tree stats)"); }
+  BuildStats* host = (BuildStats*)calloc(1, stats_bytes);
+  if (!host) { (void)hipFree(v->stats); free(v); return fail(ATLASKV_ERR_HIP, "host allocation failed"); }
+  hipStream_t s = v->stream;
+  e = hipMemcpyAsync(v->stats, host, stats_bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = launch_validate(root_child_off, v->dev.count[0], v->dev.count[1], 0, v->stats, s);
+  if (e == hipSuccess) e = launch_validate(mid_child_off, v->dev.count[1], v->dev.count[2], 1, v->stats, s);
+  for (int lev = 0; lev < 3 && e == hipSuccess; ++lev)
+    e = launch_key_norms(v->dev.key[lev], v->dev.dtype, v->dev.d, Hkv, v->dev.count[lev], v->dev.hs[lev],
+                         v->dev.rs[lev], v->stats->norm_bits + (size_t)lev * Hkv, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(host, v->stats, stats_bytes, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    free(host);
+    (void)hipFree(v->stats);
+    free(v);
+    return hip_fail(e, "tree validation");
+  }
+  const int bad = host->bad;
+  v->maxfan[0] = (int64_t)host->maxfan[0];
+  v->maxfan[1] = (int64_t)host->maxfan[1];
+  free(host);
+  if (bad) {
+    (void)hipFree(v->stats);
+    free(v);
+    return fail(ATLASKV_ERR_TREE, "malformed child offsets (%s%s)", (bad & 1) ? "root->mid " : "",
+                (bad & 2) ? "mid->leaf" : "");
+  }
+  v->dev.norm = (const float*)v->stats->norm_bits;
+  *out = v;
+  return ATLASKV_OK;
+}
+
+atlaskv_status atlaskv_tree_view_describe(const atlaskv_tensor* root_k, const atlaskv_tensor* mid_k,
+                                          const atlaskv_tensor* leaf_k, const atlaskv_tensor* leaf_v,
+                                          int64_t max_root_fanout, int64_t max_mid_fanout,
+                                          atlaskv_tree_view* out) {
+  if (!out) return fail(ATLASKV_ERR_NULL, "out is NULL");
+  atlaskv_status st = check_tree_tensors(root_k, mid_k, leaf_k, leaf_v);
+  if (st) return st;
+  if (max_root_fanout < 0 || max_mid_fanout < 0 || max_root_fanout > mid_k->shape[1] ||
+      max_mid_fanout > leaf_k->shape[1])
+    return fail(ATLASKV_ERR_TREE, "maximum fanouts outside 0..level size");
+  atlaskv_tree_view_s* v = (atlaskv_tree_view_s*)calloc(1, sizeof(atlaskv_tree_view_s));
+  if (!v) return fail(ATLASKV_ERR_HIP, "host allocation failed");
+  fill_tree(v->dev, root_k, mid_k, leaf_k, leaf_v);
+  v->maxfan[0] = max_root_fanout;
+  v->maxfan[1] = max_mid_fanout;
+  v->described_only = 1;
+  *out = v;
+  return ATLASKV_OK;
+}
+
+atlaskv_status atlaskv_destroy_tree_view(atlaskv_tree_view v) {
+  if (!v) return ATLASKV_OK;
+  hipError_t e = hipSuccess;
+  if (v->stats) e = hipFree(v->stats);
+  free(v);
+  return e == hipSuccess ? ATLASKV_OK : hip_fail(e, "hipFree(tree stats)");
+}
+
+atlaskv_status atlaskv_tree_view_set_workspace(atlaskv_tree_view v, void* ws, size_t bytes) {
+  if (!v) return fail(ATLASKV_ERR_NULL, "tree view is NULL");
+  if (bytes && !ws) return fail(ATLASKV_ERR_NULL, "workspace is NULL");
+  if (((uintptr_t)ws) % 256) return fail(ATLASKV_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  v->workspace = bytes ? ws : nullptr;
+  v->workspace_bytes = bytes;
+  return ATLASKV_OK;
+}
+
+atlaskv_status atlaskv_hikvp_workspace_size(atlaskv_tree_view v, const atlaskv_tensor* q,
+                                            const atlaskv_tensor* seq_k, const int32_t K[3],
+                                            size_t* bytes) {
+  if (!bytes) return fail(ATLASKV_ERR_NULL, "bytes is NULL");
+  Plan p;
+  atlaskv_status st = plan_call(q, v, seq_k, seq_k, K, nullptr, nullptr, false, p);
+  if (st) return st;
+  *bytes = p.total;
+  return ATLASKV_OK;
+}
+
+static atlaskv_status check_all(const atlaskv_tensor* q, atlaskv_tree_view v,
+                                const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                const int32_t K[3], const atlaskv_tensor* out,
+                                const atlaskv_attend_opts* opts, Plan& p, void** ws) {
+  atlaskv_status st = plan_call(q, v, seq_k, seq_v, K, out, opts, true, p);
+  if (st) return st;
+  void* w = (opts && opts->workspace) ? opts->workspace : v->workspace;
+  size_t wb = (opts && opts->workspace) ? opts->workspace_bytes : v->workspace_bytes;
+  if (p.R > 0) {
+    if (!w) return fail(ATLASKV_ERR_WORKSPACE, "no workspace (need %zu bytes)", p.total);
+    if (((uintptr_t)w) % 256) return fail(ATLASKV_ERR_WORKSPACE, "workspace not 256-byte aligned");
+    if (wb < p.total) return fail(ATLASKV_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", wb, p.total);
+  }
+  *ws = w;
+  return ATLASKV_OK;
+}
+
+atlaskv_status atlaskv_check_args(const atlaskv_tensor* q, atlaskv_tree_view v,
+                                  const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                  const int32_t K[3], const atlaskv_tensor* out,
+                                  const atlaskv_attend_opts* opts) {
+  Plan p;
+  void* ws = nullptr;
+  return check_all(q, v, seq_k, seq_v, K, out, opts, p, &ws);
+}
+
+atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_view v,
+                                       const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                       const int32_t K[3], atlaskv_tensor* out,
+                                       const atlaskv_attend_opts* opts) {
+  Plan p;
+  void* wsv = nullptr;
+  atlaskv_status st = check_all(q, v, seq_k, seq_v, K, out, opts, p, &wsv);
+  if (st) return st;
+  if (v->described_only) return fail(ATLASKV_ERR_UNSUPPORTED, "a described-only view cannot run");
+  if (p.R == 0) return ATLASKV_OK;
+  hipStream_t s = (opts && opts->stream) ? (hipStream_t)opts->stream : v->stream;
+  char* ws = (char*)wsv;
+
+  RowsDev rows;
+  fill_rows(rows, q, opts, p);
+  int32_t* sel[3];
+  int32_t* user_sel[3] = {opts ? opts->sel_root : nullptr, opts ? opts->sel_mid : nullptr,
+                          opts ? opts->sel_leaf : nullptr};
+  for (int i = 0; i < 3; ++i) sel[i] = user_sel[i] ? user_sel[i] : (int32_t*)(ws + p.off_sel[i]);
+  float* lse_kg = (opts && opts->lse_kg) ? opts->lse_kg : (float*)(ws + p.off_lse);
+  float* o_kg = (float*)(ws + p.off_okg);
+
+  // optional timing events at phase boundaries
+  void** ev = (opts && opts->phase_events && opts->n_phase_events > 0) ? opts->phase_events : nullptr;
+  const int nev = ev ? opts->n_phase_events : 0;
+  int phase = 0;
+  auto mark = [&](hipError_t prev) -> hipError_t {
+    if (prev != hipSuccess || phase >= nev || !ev[phase]) { ++phase; return prev; }
+    hipError_t r = hipEventRecord((hipEvent_t)ev[phase], s);
+    ++phase;
+    return r;
+  };
+  hipError_t e = mark(hipSuccess);
+  for (int lev = 0; lev < 3 && e == hipSuccess; ++lev) {
+    LevelArgs a;
+    memset(&a, 0, sizeof a);
+    a.t = v->dev;
+    a.r = rows;
+    a.level = lev;
+    a.parent_sel = lev ? sel[lev - 1] : nullptr;
+    a.Kp = lev ? p.K[lev - 1] : 0;
+    a.K = p.K[lev];
+    a.scores = (float*)(ws + p.off_scores);
+    a.cmax = p.cmax;
+    a.band_slot = (int32_t*)(ws + p.off_band_node);
+    a.band_s = (double*)(ws + p.off_band_s);
+    a.sel = sel[lev];
+    a.o_kg = o_kg;
+    a.lse_kg = lse_kg;
+    e = mark(launch_score_rows(a, s));
+    if (e == hipSuccess) e = mark(launch_topk(a, s));
+  }
+  if (e == hipSuccess) {
+    SeqArgs sa;
+    memset(&sa, 0, sizeof sa);
+    sa.r = rows;
+    sa.S = p.S;
+    sa.Hkv = v->dev.Hkv;
+    sa.d = v->dev.d;
+    sa.dtype = v->dev.dtype;
+    if (seq_k) {
+      sa.k = seq_k->data;
+      sa.v = seq_v->data;
+      sa.ks[0] = seq_k->stride[0]; sa.ks[1] = seq_k->stride[1]; sa.ks[2] = seq_k->stride[2];
+      sa.vs[0] = seq_v->stride[0]; sa.vs[1] = seq_v->stride[1]; sa.vs[2] = seq_v->stride[2];
+    }
+    sa.o_kg = o_kg;
+    sa.lse_kg = lse_kg;
+    sa.out = out->data;
+    sa.os[0] = out->stride[0]; sa.os[1] = out->stride[1]; sa.os[2] = out->stride[2];
+    sa.out_dtype = out->dtype;
+    sa.lse_seq_out = opts ? opts->lse_seq : nullptr;
+    e = mark(launch_seq_merge(sa, s));
+  }
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return ATLASKV_OK;
+}
+
+atlaskv_status atlaskv_hikvp_attend(const atlaskv_tensor* q, atlaskv_tree_view v,
+                                    const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                    const int32_t K[3], atlaskv_tensor* out) {
+  return atlaskv_hikvp_attend_ex(q, v, seq_k, seq_v, K, out, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,200 @@
+/*
+ * atlaskv.h -- C ABI of libatlaskv.so: HiKVP knowledge-injected attention for
+ * one attention layer on an MI355X (gfx950) GPU.
+ *
+ * The operation (page: "AtlasKV: Augmenting LLMs with Billion-Scale Knowledge
+ * Graphs in 20GB VRAM", digest of arXiv 2510.17934):
+ *   - 速读 › 怎么做的 (quick read, how it is done): the knowledge keys form a
+ *     three-level tree (root, mid, leaf).  For each query, score the root keys,
+ *     keep the Top-K branches, score their children, keep the Top-K, and so on
+ *     down to the leaves.  The layer output is then
+ *         y = λ_kg · Softmax(logits_kg) · v̄  +  λ_seq · Softmax(logits_seq) · v
+ *     where logits_kg are the selected leaves' logits and logits_seq the
+ *     ordinary causal attention logits.
+ *   - 背景知识与设计原则 › 自注意力层机制: causal attention, logits
+ *     <q_n, k_i>/sqrt(D) over positions i <= n.
+ *   - 方法细节 › 等效注意力机制的知识增强: the λ definitions are missing from
+ *     the page; this library uses the log-sum-exp shares
+ *         λ_kg = Σexp(logits_kg) / (Σexp(logits_kg) + Σexp(logits_seq)),
+ *         λ_seq = 1 - λ_kg,
+ *     which makes the merge equal to one softmax over both logit sets, i.e.
+ *     the rectangular attention of 背景知识与设计原则 › KBLaM中的矩形注意力
+ *     restricted to the selected leaves.
+ *
+ * Semantics fixed by this library where the page is silent:
+ *   - a row is one (batch b, token n, query head h); every row selects its own
+ *     nodes.  Query head h reads KV head g = h / (Hq / Hkv) of the tree and of
+ *     the sequence (grouped-query attention); the tree topology is shared by
+ *     all KV heads;
+ *   - ranking key: the scaled logit scale * <q_kg, k>, with scale = 1/sqrt(d)
+ *     unless given; equal keys rank the lower node index first.  Selections
+ *     are exact with respect to the fp64 value of that logit computed from the
+ *     stored inputs (products exact, summed left to right over the head dim);
+ *   - K clamps to the number of candidates; K = 0 at any level empties the KG
+ *     half (then the output is plain causal attention);
+ *   - causal alignment is bottom-right: token n sees sequence positions
+ *     0 .. S_kv - N + n (so S_kv >= N); seq_k == NULL means no sequence half;
+ *   - only leaves carry values; the KG softmax runs over the K_L selected
+ *     leaves and reuses the logits computed for the selection.
+ *
+ * Memory and threading:
+ *   - every tensor is device memory owned by the caller; the library never
+ *     copies or frees it.  A tree view references its tensors until destroyed;
+ *   - atlaskv_hikvp_attend* allocate nothing: scratch memory is the caller's
+ *     workspace (size from atlaskv_hikvp_workspace_size).  Only
+ *     atlaskv_build_tree_view allocates (a few bytes of device memory per KV
+ *     head, freed by atlaskv_destroy_tree_view) and synchronises its stream;
+ *   - attend calls are asynchronous on their stream; device faults surface at
+ *     the caller's next synchronisation.  Calls on different streams need
+ *     separate workspaces; calls sharing a workspace must be stream-ordered.
+ *
+ * Errors: every entry point returns an atlaskv_status.  Argument errors are
+ * detected on the host before anything is enqueued, so a failed call writes
+ * nothing.  atlaskv_last_error() returns a message for the calling thread's
+ * most recent failure.
+ */
+#ifndef ATLASKV_H
+#define ATLASKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATLASKV_OK = 0,
+  ATLASKV_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATLASKV_ERR_DTYPE = 2,       /* unknown dtype, or inputs of different dtypes */
+  ATLASKV_ERR_SHAPE = 3,       /* shapes, strides or alignment inconsistent */
+  ATLASKV_ERR_TREE = 4,        /* malformed child offsets */
+  ATLASKV_ERR_K = 5,           /* K < 0 or K > 256, or both halves empty */
+  ATLASKV_ERR_WORKSPACE = 6,   /* workspace missing, too small or misaligned */
+  ATLASKV_ERR_UNSUPPORTED = 7, /* head dim not 64/128, node counts >= 2^31, scale <= 0 */
+  ATLASKV_ERR_HIP = 8          /* a HIP runtime call failed */
+} atlaskv_status;
+
+typedef enum { ATLASKV_F32 = 0, ATLASKV_BF16 = 1 } atlaskv_dtype;
+
+/* A strided view of caller-owned device memory.  Strides are in elements and
+ * the innermost stride must be 1; rows must start on 16-byte boundaries. */
+typedef struct {
+  void* data;
+  int32_t dtype;       /* atlaskv_dtype */
+  int32_t ndim;
+  int64_t shape[4];
+  int64_t stride[4];
+} atlaskv_tensor;
+
+typedef struct atlaskv_tree_view_s* atlaskv_tree_view;
+
+/*
+ * Build a view of a three-level key tree (方法细节 › KGKVs的层次化聚类 gives
+ * the levels; the tree itself is built offline by the caller).
+ *   root_k  [Hkv, M_R, d]   root keys
+ *   mid_k   [Hkv, M_I, d]   mid keys
+ *   leaf_k  [Hkv, M,   d]   leaf keys
+ *   leaf_v  [Hkv, M,   d]   leaf values
+ *   root_child_off  device int64 [M_R + 1]: mids of root j are
+ *                   root_child_off[j] .. root_child_off[j+1]-1
+ *   mid_child_off   device int64 [M_I + 1]: leaves of mid m likewise
+ * All float tensors share one dtype and head dim d.  Offsets must start at 0,
+ * be non-decreasing and end at M_I (resp. M); empty ranges are allowed.
+ * stream: hipStream_t (NULL = default stream) used for validation and as the
+ * default stream of attend calls.  The call validates the offsets and
+ * computes per-level key-norm bounds on the GPU, then synchronises once.
+ * Returns ATLASKV_ERR_TREE for malformed offsets; *out is set only on success.
+ */
+atlaskv_status atlaskv_build_tree_view(const atlaskv_tensor* root_k, const atlaskv_tensor* mid_k,
+                                       const atlaskv_tensor* leaf_k, const atlaskv_tensor* leaf_v,
+                                       const int64_t* root_child_off, const int64_t* mid_child_off,
+                                       void* stream, atlaskv_tree_view* out);
+
+/* Release a view (and its small device buffers).  NULL is accepted. */
+atlaskv_status atlaskv_destroy_tree_view(atlaskv_tree_view tree);
+
+/* Attach a caller-owned device workspace (256-byte aligned) used by
+ * atlaskv_hikvp_attend.  bytes = 0 detaches. */
+atlaskv_status atlaskv_tree_view_set_workspace(atlaskv_tree_view tree, void* workspace, size_t bytes);
+
+/* Workspace bytes an attend call with these shapes and K needs.  q gives
+ * B, N, Hq; seq_k may be NULL.  Host only. */
+atlaskv_status atlaskv_hikvp_workspace_size(atlaskv_tree_view tree, const atlaskv_tensor* q,
+                                            const atlaskv_tensor* seq_k,
+                                            const int32_t K_per_level[3], size_t* bytes);
+
+/*
+ * HiKVP attention for one layer, enqueued on the view's stream with the view's
+ * workspace.
+ *   q      [B, N, Hq, d]  queries (post-RoPE); also the KG query
+ *   seq_k  [B, S_kv, Hkv, d], seq_v likewise: causal sequence keys/values
+ *          (both NULL: no sequence half)
+ *   K_per_level  host int32 {K_R, K_I, K_L}, each in 0..256
+ *   out    [B, N, Hq, d]  dtype of q, or fp32
+ */
+atlaskv_status atlaskv_hikvp_attend(const atlaskv_tensor* q, atlaskv_tree_view tree,
+                                    const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                    const int32_t K_per_level[3], atlaskv_tensor* out);
+
+/* Optional controls and outputs of atlaskv_hikvp_attend_ex.  Zero-initialise
+ * and set what is needed. */
+typedef struct {
+  const atlaskv_tensor* q_kg; /* [B,N,Hq,d] KG query (the page's W̃_Q x); NULL -> q */
+  float scale;                /* logit scale; 0 -> 1/sqrt(d); must be > 0 otherwise */
+  void* stream;               /* hipStream_t; NULL -> the view's stream */
+  void* workspace;            /* NULL -> the view's workspace */
+  size_t workspace_bytes;
+  int32_t* sel_root;          /* optional device [B*N*Hq, K_R] selected roots, -1 padded */
+  int32_t* sel_mid;           /* optional device [B*N*Hq, K_I] */
+  int32_t* sel_leaf;          /* optional device [B*N*Hq, K_L] */
+  float* lse_kg;              /* optional device [B*N*Hq]: log Σexp(logits_kg), -inf if empty */
+  float* lse_seq;             /* optional device [B*N*Hq]: log Σexp(logits_seq), -inf if empty */
+  void** phase_events;        /* optional hipEvent_t[n_phase_events]: event 0 is recorded on the
+                                 launch stream before the first kernel, event i after kernel
+                                 phase i-1 (names from atlaskv_phase_name); for timing only */
+  int32_t n_phase_events;
+} atlaskv_attend_opts;
+
+/* As atlaskv_hikvp_attend, with options (opts may be NULL).  The selections
+ * are written as sets: each row's K entries are the selected node indices in
+ * candidate order, -1 padded when fewer than K candidates exist. */
+atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_view tree,
+                                       const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                       const int32_t K_per_level[3], atlaskv_tensor* out,
+                                       const atlaskv_attend_opts* opts);
+
+/* The argument checks of atlaskv_hikvp_attend_ex alone: pure host code, no
+ * HIP call, nothing enqueued.  tree may describe shapes only (see
+ * atlaskv_tree_view_describe). */
+atlaskv_status atlaskv_check_args(const atlaskv_tensor* q, atlaskv_tree_view tree,
+                                  const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                  const int32_t K_per_level[3], const atlaskv_tensor* out,
+                                  const atlaskv_attend_opts* opts);
+
+/* A host-only view for argument checking (no device work, no validation of
+ * offsets beyond their count): same tensors as atlaskv_build_tree_view plus
+ * the maximum fanouts the caller asserts.  Usable with atlaskv_check_args and
+ * atlaskv_hikvp_workspace_size; attend calls on it return
+ * ATLASKV_ERR_UNSUPPORTED. */
+atlaskv_status atlaskv_tree_view_describe(const atlaskv_tensor* root_k, const atlaskv_tensor* mid_k,
+                                          const atlaskv_tensor* leaf_k, const atlaskv_tensor* leaf_v,
+                                          int64_t max_root_fanout, int64_t max_mid_fanout,
+                                          atlaskv_tree_view* out);
+
+/* Kernel phases of one attend call, in launch order (for phase_events).
+ * atlaskv_phase_count() phases; atlaskv_phase_name(i) names phase i (NULL if
+ * out of range). */
+int32_t atlaskv_phase_count(void);
+const char* atlaskv_phase_name(int32_t phase);
+
+/* Message for the calling thread's most recent failed call ("" if none). */
+const char* atlaskv_last_error(void);
+
+/* Library version string. */
+const char* atlaskv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATLASKV_H */

@@ -1,0 +1,173 @@
+"""CPU tests of the C-ABI boundary: the library loads without a GPU, exports
+every symbol include/atlaskv.h declares, and its host-only argument checks
+return the documented status codes.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from hierarchical_kv_pruning_amd import atlaskv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(atlaskv.LIB_PATH):
+        from hierarchical_kv_pruning_amd import build
+        build.build()
+    return atlaskv.lib()
+
+
+def test_header_declarations_are_exported(lib):
+    header = open(os.path.join(ROOT, "include", "atlaskv.h")).read()
+    declared = set(re.findall(r"\b(atlaskv_[a-z_]+)\s*\(", header))
+    assert declared == set(atlaskv.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version(lib):
+    assert "gfx950" in atlaskv.version()
+
+
+def _tree(dtype=torch.bfloat16, Hkv=2, d=128, MR=4, MI=10, M=50):
+    z = lambda n: torch.zeros(Hkv, n, d, dtype=dtype)
+    return z(MR), z(MI), z(M), z(M)
+
+
+def _view(**kw):
+    rk, mk, lk, lv = _tree(**kw)
+    return atlaskv.TreeView.describe_only(rk, mk, lk, lv, 5, 9)
+
+
+def _call(view, q=None, seq=True, K=(2, 2, 4), out=None, ws_bytes=1 << 30, **opts):
+    B, N, Hq, d = 1, 4, 4, view._keep[0].shape[2]
+    dt = view._keep[0].dtype
+    if q is None:
+        q = torch.zeros(B, N, Hq, d, dtype=dt)
+    sk = torch.zeros(B, 6, view._keep[0].shape[0], d, dtype=dt) if seq else None
+    sv = torch.zeros_like(sk) if seq else None
+    if out is None:
+        out = torch.zeros(q.shape, dtype=dt)
+    ws = torch.zeros(ws_bytes // 1 if ws_bytes < 4096 else 4096, dtype=torch.uint8)
+    # a host buffer stands in for the workspace pointer: only its address and size are checked
+    fake = type("W", (), {"data_ptr": lambda self: (ws.data_ptr() + 255) // 256 * 256,
+                          "numel": lambda self: ws_bytes})()
+    return atlaskv.check_args(q, view, sk, sv, K, out, workspace=fake, **opts)
+
+
+def test_valid_call_passes(lib):
+    assert _call(_view()) == atlaskv.OK
+
+
+def test_valid_call_fp32_and_d64(lib):
+    assert _call(_view(dtype=torch.float32, d=64)) == atlaskv.OK
+
+
+def test_null_pointers(lib):
+    v = _view()
+    q = torch.zeros(1, 4, 4, 128, dtype=torch.bfloat16)
+    assert atlaskv.check_args(None, v, None, None, (1, 1, 1), q) == atlaskv.ERR_NULL
+    assert atlaskv.check_args(q, None, None, None, (1, 1, 1), q) == atlaskv.ERR_NULL
+    assert atlaskv.check_args(q, v, None, None, None, q) == atlaskv.ERR_NULL
+    sk = torch.zeros(1, 6, 2, 128, dtype=torch.bfloat16)
+    assert atlaskv.check_args(q, v, sk, None, (1, 1, 1), q) == atlaskv.ERR_NULL
+
+
+def test_dtype_mismatch(lib):
+    v = _view()
+    q = torch.zeros(1, 4, 4, 128, dtype=torch.float32)
+    assert _call(v, q=q) == atlaskv.ERR_DTYPE
+    out16 = torch.zeros(1, 4, 4, 128, dtype=torch.bfloat16)
+    assert _call(v, out=out16) == atlaskv.OK
+    out32 = torch.zeros(1, 4, 4, 128, dtype=torch.float32)
+    assert _call(v, out=out32) == atlaskv.OK  # fp32 output of bf16 inputs is allowed
+
+
+def test_shape_errors(lib):
+    v = _view()
+    assert _call(v, q=torch.zeros(1, 4, 3, 128, dtype=torch.bfloat16)) == atlaskv.ERR_SHAPE  # Hq % Hkv
+    assert _call(v, q=torch.zeros(1, 4, 4, 64, dtype=torch.bfloat16)) == atlaskv.ERR_SHAPE   # head dim
+    assert _call(v, out=torch.zeros(1, 4, 4, 64, dtype=torch.bfloat16)) == atlaskv.ERR_SHAPE
+    q = torch.zeros(1, 8, 4, 128, dtype=torch.bfloat16)                                      # S_kv < N
+    out = torch.zeros_like(q)
+    assert _call(v, q=q, out=out) == atlaskv.ERR_SHAPE
+    # non-unit innermost stride
+    qt = torch.zeros(1, 4, 128, 4, dtype=torch.bfloat16).transpose(2, 3)
+    assert _call(v, q=qt) == atlaskv.ERR_SHAPE
+
+
+def test_k_errors(lib):
+    v = _view()
+    assert _call(v, K=(-1, 2, 2)) == atlaskv.ERR_K
+    assert _call(v, K=(2, 2, 257)) == atlaskv.ERR_K
+    assert _call(v, K=(2, 2, 256)) == atlaskv.OK
+    assert _call(v, K=(0, 2, 2)) == atlaskv.OK              # empty KG half: plain causal attention
+    assert _call(v, K=(2, 2, 0), seq=False) == atlaskv.ERR_K  # both halves empty
+    assert _call(v, K=(2, 2, 2), seq=False) == atlaskv.OK
+
+
+def test_workspace_errors(lib):
+    v = _view()
+    assert _call(v, ws_bytes=16) == atlaskv.ERR_WORKSPACE
+    q = torch.zeros(1, 4, 4, 128, dtype=torch.bfloat16)
+    assert atlaskv.check_args(q, v, None, None, (1, 1, 1), q) == atlaskv.ERR_WORKSPACE  # none attached
+
+
+def test_workspace_size_grows_with_k(lib):
+    v = _view()
+    q = torch.zeros(1, 4, 4, 128, dtype=torch.bfloat16)
+    a = atlaskv.hikvp_workspace_size(v, q, None, (1, 1, 1))
+    b = atlaskv.hikvp_workspace_size(v, q, None, (4, 4, 8))
+    assert 0 < a < b
+
+
+def test_scale_must_be_positive(lib):
+    v = _view()
+    assert _call(v, scale=-1.0) == atlaskv.ERR_UNSUPPORTED
+    assert _call(v, scale=0.5) == atlaskv.OK
+
+
+def test_unsupported_head_dim(lib):
+    with pytest.raises(atlaskv.AtlasKVError) as e:
+        _view(d=96)
+    assert e.value.status == atlaskv.ERR_UNSUPPORTED
+
+
+def test_describe_rejects_bad_fanouts_and_tree_mismatch(lib):
+    rk, mk, lk, lv = _tree()
+    with pytest.raises(atlaskv.AtlasKVError) as e:
+        atlaskv.TreeView.describe_only(rk, mk, lk, lv, 11, 9)   # fanout above the mid count
+    assert e.value.status == atlaskv.ERR_TREE
+    with pytest.raises(atlaskv.AtlasKVError) as e:
+        atlaskv.TreeView.describe_only(rk, mk, lk, lv[:, :49], 5, 9)
+    assert e.value.status == atlaskv.ERR_SHAPE
+    with pytest.raises(atlaskv.AtlasKVError) as e:
+        atlaskv.TreeView.describe_only(rk, mk.float(), lk, lv, 5, 9)
+    assert e.value.status == atlaskv.ERR_DTYPE
+
+
+def test_q_kg_must_match_q(lib):
+    v = _view()
+    assert _call(v, q_kg=torch.zeros(1, 4, 4, 128, dtype=torch.bfloat16)) == atlaskv.OK
+    assert _call(v, q_kg=torch.zeros(1, 4, 2, 128, dtype=torch.bfloat16)) == atlaskv.ERR_SHAPE
+
+
+def test_error_message_is_thread_local_text(lib):
+    v = _view()
+    _call(v, K=(-1, 2, 2))
+    assert "K[0]" in atlaskv.last_error()
+
+
+def test_described_view_cannot_run(lib):
+    v = _view()
+    q = torch.zeros(1, 4, 4, 128, dtype=torch.bfloat16)
+    sk = torch.zeros(1, 6, 2, 128, dtype=torch.bfloat16)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    with pytest.raises(atlaskv.AtlasKVError) as e:
+        atlaskv.hikvp_attend_ex(q, v, sk, torch.zeros_like(sk), (1, 1, 1), torch.zeros_like(q),
+                                workspace=ws)
+    assert e.value.status in (atlaskv.ERR_UNSUPPORTED, atlaskv.ERR_WORKSPACE)

@@ -1,0 +1,194 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Small and medium workloads compare every row; the full
+workloads (1e6 prefill, 1e7 decode, 1e8 slice) compare seeded row samples
+with the oracle's two-phase mode, in the launch configuration the benchmark
+times."""
+import gc
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from hierarchical_kv_pruning_amd import atlaskv, synth
+from oracle import oracle
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _check(case, rows=None, two_phase=False, **kw):
+    rows = oracle.all_rows(case.B, case.N, case.Hq) if rows is None else rows
+    gkw = {k: v for k, v in kw.items() if k in ("K", "q", "q_kg", "scale", "with_seq", "out_dtype")}
+    okw = {k: v for k, v in kw.items() if k in ("K", "q", "q_kg", "scale", "with_seq")}
+    say(f"{case.name}: attend B={case.B} N={case.N} S={case.S_kv} Hq={case.Hq} Hkv={case.Hkv} "
+        f"d={case.d} tree={case.M_R}/{case.M_I}/{case.M} K={gkw.get('K', case.K)} rows={len(rows)}")
+    gpu = parity.gpu_run(case, **gkw)
+    ora = parity.oracle_rows(case, rows, two_phase=two_phase, **okw)
+
+    def replay(rws, selI, selL):
+        return parity.oracle_rows(case, np.array(rws), forced_sel_L=np.array(selL, np.int64),
+                                  sel_I=np.array(selI, np.int64), **okw)
+
+    rep = parity.compare(case, rows, gpu, ora, replay=replay)
+    say(f"{case.name}: {rep}")
+    return gpu, ora, rep
+
+
+def _small(name="edge", seed=0, **kw):
+    cfg = dict(dtype="f32", B=2, N=33, S_kv=45, Hq=8, Hkv=2, d=128, M_R=37, M_I=411, M=5003,
+               K=(5, 7, 19))
+    cfg.update(kw)
+    ragged = cfg.pop("ragged", True)
+    return synth.make_case(name, device=DEV, seed=seed, ragged=ragged, **cfg)
+
+
+# ---------------------------------------------------------------------------
+# small workloads, every row
+# ---------------------------------------------------------------------------
+
+def test_tiny_all_rows():
+    _check(synth.make_case("tiny", device=DEV))
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 128), ("f32", 64), ("bf16", 128), ("bf16", 64)])
+def test_ragged_tree_dtypes_and_head_dims(dtype, d):
+    _check(_small(seed=3, dtype=dtype, d=d))
+
+
+@pytest.mark.parametrize("K", [(3, 256, 256), (37, 256, 256), (1, 1, 1), (0, 4, 4), (4, 0, 4),
+                               (4, 4, 0), (200, 2, 3)])
+def test_k_edge_cases(K):
+    """K above the candidate count clamps; K = 0 at any level gives plain causal
+    attention; K = 1 everywhere."""
+    _check(_small(seed=5, M=2000), K=K)
+
+
+def test_full_k_selects_every_leaf():
+    case = _small(seed=6, M_R=4, M_I=20, M=200, K=(4, 20, 200))
+    gpu, _, _ = _check(case)
+    assert all(sorted(s[s >= 0].tolist()) == list(range(200)) for s in gpu["sel"][2])
+
+
+def test_no_sequence_half():
+    _check(_small(seed=7), with_seq=False)
+
+
+def test_sequence_longer_than_queries_and_gqa_8():
+    _check(_small(seed=8, N=17, S_kv=200, Hq=16, Hkv=2, dtype="bf16"))
+
+
+def test_single_head_group():
+    _check(_small(seed=9, Hq=3, Hkv=3, dtype="bf16"))
+
+
+def test_separate_kg_query_and_scale():
+    case = _small(seed=10, dtype="bf16")
+    qkg = torch.randn(case.q.shape, generator=torch.Generator(device=DEV).manual_seed(1),
+                      device=DEV).to(case.q.dtype)
+    _check(case, q_kg=qkg, scale=0.0625)
+
+
+def test_fp32_output_of_bf16_inputs():
+    case = _small(seed=11, dtype="bf16")
+    gpu, ora, _ = _check(case, out_dtype=torch.float32)
+    # no bf16 rounding on the output: much tighter than the bf16 bar
+    ridx = parity.row_index(case, oracle.all_rows(case.B, case.N, case.Hq))
+    assert np.max(np.abs(gpu["out"][ridx] - ora["out"])) < 1e-4
+
+
+def test_strided_query():
+    case = _small(seed=12)
+    big = torch.randn(case.B, case.N, case.Hq * 3, case.d, device=DEV, dtype=case.q.dtype)
+    q = big[:, :, 1::3, :]          # not contiguous over heads
+    q.copy_(case.q)
+    _check(case, q=q)
+
+
+def test_exact_ties_break_to_lower_index():
+    """Duplicate keys give bit-equal scores; the lower node index must win."""
+    case = _small(seed=13, M_R=6, M_I=30, M=600, ragged=False, K=(3, 4, 9))
+    with torch.no_grad():
+        case.root_k[:, 3] = case.root_k[:, 1].clone()
+        case.mid_k[:, 5::5] = case.mid_k[:, 0:25:5].clone()
+        case.leaf_k[:, 1::2] = case.leaf_k[:, 0::2].clone()
+    _check(case)
+
+
+def test_deterministic_reruns():
+    case = _small(seed=14, dtype="bf16")
+    a = parity.gpu_run(case)
+    b = parity.gpu_run(case)
+    assert np.array_equal(a["out"], b["out"])
+    for x, y in zip(a["sel"], b["sel"]):
+        assert np.array_equal(x, y)
+
+
+def test_empty_batch_writes_nothing():
+    case = _small(seed=15, N=1, S_kv=4)
+    tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
+    q = case.q[:0]
+    out = torch.empty_like(q)
+    atlaskv.hikvp_attend_ex(q, tree, case.seq_k[:0], case.seq_v[:0], case.K, out)
+    torch.cuda.synchronize()
+
+
+def test_malformed_offsets_rejected():
+    case = _small(seed=16)
+    bad = case.mid_off.clone()
+    bad[5] = bad[6] + 1
+    with pytest.raises(atlaskv.AtlasKVError) as e:
+        atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, bad)
+    assert e.value.status == atlaskv.ERR_TREE
+
+
+def test_view_workspace_entry_point():
+    """atlaskv_hikvp_attend with the view's stream and workspace."""
+    case = _small(seed=17, dtype="bf16")
+    tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
+    tree.set_workspace(atlaskv.alloc_workspace(tree, case.q, case.seq_k, case.K))
+    out = torch.empty_like(case.q)
+    atlaskv.hikvp_attend(case.q, tree, case.seq_k, case.seq_v, case.K, out)
+    torch.cuda.synchronize()
+    ref = parity.gpu_run(case, tree=tree)
+    assert np.array_equal(out.float().reshape(case.rows, -1).cpu().numpy(), ref["out"])
+
+
+# ---------------------------------------------------------------------------
+# the named workloads
+# ---------------------------------------------------------------------------
+
+def test_m1e4_all_rows():
+    _check(synth.make_case("m1e4", device=DEV))
+
+
+def _release():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_m1e6_sampled_rows():
+    case = synth.make_case("m1e6", device=DEV)
+    _check(case, rows=parity.sample_rows(case, 384, seed=1), two_phase=True)
+    del case
+    _release()
+
+
+def test_m1e7_decode_sampled_rows():
+    case = synth.make_case("m1e7_decode", device=DEV)
+    _check(case, rows=parity.sample_rows(case, 192, seed=2), two_phase=True)
+    del case
+    _release()
+
+
+def test_m1e8_slice_sampled_rows():
+    case = synth.make_case("m1e8_slice", device=DEV)
+    _check(case, rows=parity.sample_rows(case, 128, seed=3), two_phase=True)
+    del case
+    _release()
