@@ -124,22 +124,21 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
   int B, N, Hq, S, R, G;
   int K[3];
-  int64_t cmax;
+  int64_t c1max, c2max;
   double scale;
-  size_t off_scores, off_band_node, off_band_s, off_sel[3], off_okg, off_lse, total;
+  size_t off_mid, off_leaf, off_sel[3], off_okg, off_lse, total;
 };
 
-// Candidate capacity per row: roots; children of K_R roots; children of K_I mids.
-int64_t candidate_capacity(const atlaskv_tree_view_s* v, const int K[3]) {
+// Candidate capacity per row at the mid level (children of K_R distinct
+// roots) and at the leaf level (children of K_I distinct mids).
+void candidate_capacity(const atlaskv_tree_view_s* v, const int K[3], int64_t* c1, int64_t* c2) {
   const int64_t MR = v->dev.count[0], MI = v->dev.count[1], M = v->dev.count[2];
-  int64_t c1 = (K[0] < MR ? K[0] : MR) * v->maxfan[0];
-  if (c1 > MI) c1 = MI;
-  int64_t c2 = (K[1] < MI ? K[1] : MI) * v->maxfan[1];
-  if (c2 > M) c2 = M;
-  int64_t c = MR;
-  if (c1 > c) c = c1;
-  if (c2 > c) c = c2;
-  return c < 1 ? 1 : c;
+  int64_t a = (K[0] < MR ? K[0] : MR) * v->maxfan[0];
+  if (a > MI) a = MI;
+  int64_t b = (K[1] < MI ? K[1] : MI) * v->maxfan[1];
+  if (b > M) b = M;
+  *c1 = a < 1 ? 1 : a;
+  *c2 = b < 1 ? 1 : b;
 }
 
 atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
@@ -203,13 +202,16 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   p.R = (int)(B * N * Hq);
   p.G = (int)(Hq / t.Hkv);
   for (int i = 0; i < 3; ++i) p.K[i] = Kpl[i];
-  p.cmax = candidate_capacity(v, p.K);
+  candidate_capacity(v, p.K, &p.c1max, &p.c2max);
+  if (p.c1max >= kIndexLimit || p.c2max >= kIndexLimit)
+    return fail(ATLASKV_ERR_UNSUPPORTED, "candidates per row must be below 2^31");
   p.scale = scale;
   const size_t R = (size_t)p.R;
   size_t o = 0;
-  p.off_scores = o;    o = align256(o + R * (size_t)p.cmax * 4);
-  p.off_band_node = o; o = align256(o + R * (size_t)p.cmax * 4);
-  p.off_band_s = o;    o = align256(o + R * (size_t)p.cmax * 8);
+  // mid scores; the root kernel also spills its scores here when M_R is large
+  if (v->dev.count[0] > p.c1max) p.c1max = v->dev.count[0];
+  p.off_mid = o;       o = align256(o + R * (size_t)p.c1max * 4);
+  p.off_leaf = o;      o = align256(o + R * (size_t)p.c2max * 4);
   for (int i = 0; i < 3; ++i) { p.off_sel[i] = o; o = align256(o + R * (size_t)p.K[i] * 4); }
   p.off_okg = o;       o = align256(o + R * (size_t)t.d * 4);
   p.off_lse = o;       o = align256(o + R * 4);
@@ -234,8 +236,9 @@ const char* atlaskv_last_error(void) { return g_err.c_str(); }
 
 const char* atlaskv_version(void) { return "atlaskv-mi355x 0.1 (gfx950)"; }
 
-static const char* const kPhaseNames[] = {"score_root", "topk_root", "score_mid", "topk_mid",
-                                          "score_leaf", "topk_leaf_kg_attention", "seq_attention_merge"};
+static const char* const kPhaseNames[] = {"root_score_topk", "mid_bucket_gemm", "mid_topk",
+                                          "leaf_score_stream", "leaf_topk_kg_attention",
+                                          "seq_attention_merge"};
 static const int kPhases = (int)(sizeof kPhaseNames / sizeof kPhaseNames[0]);
 
 int32_t atlaskv_phase_count(void) { return kPhases; }
@@ -399,25 +402,23 @@ atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vie
     return r;
   };
   hipError_t e = mark(hipSuccess);
-  for (int lev = 0; lev < 3 && e == hipSuccess; ++lev) {
-    LevelArgs a;
-    memset(&a, 0, sizeof a);
-    a.t = v->dev;
-    a.r = rows;
-    a.level = lev;
-    a.parent_sel = lev ? sel[lev - 1] : nullptr;
-    a.Kp = lev ? p.K[lev - 1] : 0;
-    a.K = p.K[lev];
-    a.scores = (float*)(ws + p.off_scores);
-    a.cmax = p.cmax;
-    a.band_slot = (int32_t*)(ws + p.off_band_node);
-    a.band_s = (double*)(ws + p.off_band_s);
-    a.sel = sel[lev];
-    a.o_kg = o_kg;
-    a.lse_kg = lse_kg;
-    e = mark(launch_score_rows(a, s));
-    if (e == hipSuccess) e = mark(launch_topk(a, s));
-  }
+  StepArgs a;
+  memset(&a, 0, sizeof a);
+  a.t = v->dev;
+  a.r = rows;
+  for (int i = 0; i < 3; ++i) { a.K[i] = p.K[i]; a.sel[i] = sel[i]; }
+  a.c1max = p.c1max;
+  a.c2max = p.c2max;
+  a.mid_scores = (float*)(ws + p.off_mid);
+  a.leaf_scores = (float*)(ws + p.off_leaf);
+  a.o_kg = o_kg;
+  a.lse_kg = lse_kg;
+  // 速读 › 怎么做的: roots -> Top-K -> their children -> Top-K -> leaves -> Top-K
+  e = mark(launch_root(a, s));
+  if (e == hipSuccess) e = mark(launch_mid_gemm(a, s));
+  if (e == hipSuccess) e = mark(launch_mid_select(a, s));
+  if (e == hipSuccess) e = mark(launch_leaf_score(a, s));
+  if (e == hipSuccess) e = mark(launch_leaf_select(a, s));
   if (e == hipSuccess) {
     SeqArgs sa;
     memset(&sa, 0, sizeof sa);

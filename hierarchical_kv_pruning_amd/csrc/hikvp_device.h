@@ -1,0 +1,491 @@
+// hikvp_device.h -- device helpers shared by the gfx950 kernels of
+// libatlaskv.so: element unpacking, wave/block reductions, coalesced key-span
+// scoring and the exact-boundary Top-K select.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "hikvp_internal.h"
+
+namespace hikvp {
+
+struct BF16 {
+  static constexpr int kBytes = 2;
+  static constexpr int kEPV = 8;  // elements per 16-byte vector
+};
+struct F32 {
+  static constexpr int kBytes = 4;
+  static constexpr int kEPV = 4;
+};
+
+template <class E>
+__device__ inline void unpack(const uint4& v, float* f);
+template <>
+__device__ inline void unpack<BF16>(const uint4& v, float* f) {
+  f[0] = __uint_as_float(v.x << 16);
+  f[1] = __uint_as_float(v.x & 0xffff0000u);
+  f[2] = __uint_as_float(v.y << 16);
+  f[3] = __uint_as_float(v.y & 0xffff0000u);
+  f[4] = __uint_as_float(v.z << 16);
+  f[5] = __uint_as_float(v.z & 0xffff0000u);
+  f[6] = __uint_as_float(v.w << 16);
+  f[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+template <>
+__device__ inline void unpack<F32>(const uint4& v, float* f) {
+  f[0] = __uint_as_float(v.x);
+  f[1] = __uint_as_float(v.y);
+  f[2] = __uint_as_float(v.z);
+  f[3] = __uint_as_float(v.w);
+}
+
+template <class E>
+__device__ inline float load_f32(const void* base, int64_t i);
+template <>
+__device__ inline float load_f32<BF16>(const void* base, int64_t i) {
+  return __uint_as_float(((uint32_t)((const uint16_t*)base)[i]) << 16);
+}
+template <>
+__device__ inline float load_f32<F32>(const void* base, int64_t i) {
+  return ((const float*)base)[i];
+}
+
+// DPL = D/64 consecutive elements owned by one lane (value rows, outputs)
+template <class E, int DPL>
+__device__ inline void load_lane(const void* row, int lane, float* f) {
+  if constexpr (DPL == 2 && E::kBytes == 2) {
+    const uint32_t u = ((const uint32_t*)row)[lane];
+    f[0] = __uint_as_float(u << 16);
+    f[1] = __uint_as_float(u & 0xffff0000u);
+  } else if constexpr (DPL == 2 && E::kBytes == 4) {
+    const float2 v = ((const float2*)row)[lane];
+    f[0] = v.x;
+    f[1] = v.y;
+  } else {
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) f[e] = load_f32<E>(row, (int64_t)lane * DPL + e);
+  }
+}
+
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// LDS visibility within one wave (rows handled by separate waves never meet).
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Barrier of the NT threads that cooperate on one row.
+template <int NT>
+__device__ inline void group_sync() {
+  if constexpr (NT == 64) wave_sync();
+  else __syncthreads();
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger key).
+__device__ inline uint32_t ord_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float ord_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ inline int64_t q_off(const int64_t* s, int b, int n, int h) {
+  return (int64_t)b * s[0] + (int64_t)n * s[1] + (int64_t)h * s[2];
+}
+
+// Rows are processed KV-head-major (all rows reading one head's tree run
+// together, so shared child spans meet in the caches): block index ->
+// (g, b*N + n, h within the group) -> row = (b*N + n)*Hq + g*G + hw.
+__device__ inline int row_of_block(const RowsDev& r, int blk) {
+  const int hw = blk % r.G;
+  const int t = blk / r.G;
+  const int BN = r.B * r.N;
+  const int bn = t % BN;
+  const int g = t / BN;
+  return bn * r.Hq + g * r.G + hw;
+}
+
+// Candidate list of a row at one level: the children of its selected
+// parents, in the parents' order.  pre[k] = first slot of parent k,
+// base[k] = global index of parent k's first child.  One whole wave.
+__device__ inline int build_candidates(const int32_t* parents, int Kp, const int64_t* off,
+                                       int lane, int* pre, int64_t* base) {
+  int carry = 0;
+  if (lane == 0) pre[0] = 0;
+  for (int k0 = 0; k0 < Kp; k0 += 64) {
+    const int k = k0 + lane;
+    int fan = 0;
+    int64_t first = 0;
+    if (k < Kp) {
+      const int p = parents[k];
+      if (p >= 0) {
+        first = off[p];
+        fan = (int)(off[p + 1] - first);
+      }
+      base[k] = first;
+    }
+    int incl = fan;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (k < Kp) pre[k + 1] = carry + incl;
+    carry += __shfl(incl, 63);
+  }
+  return carry;
+}
+
+// Candidate slot -> global node index.  np < 0: the slot is the node (roots).
+struct SlotMap {
+  const int* pre;
+  const int64_t* base;
+  int np;
+  __device__ int64_t operator()(int c) const {
+    if (np < 0) return c;
+    int lo = 0, hi = np - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    return base[lo] + (c - pre[lo]);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Score a run of candidate keys: out[c] = <q, key[first + c]> (fp32, unscaled)
+// for c < len.  LPK lanes read one key row as 16-byte pieces, so a wave load
+// covers 64/LPK whole rows; U loads are kept in flight per lane.  NW waves
+// (w = this wave) split the run.  qf: this lane's EPV query elements.
+// ---------------------------------------------------------------------------
+template <class E, int D, int U>
+__device__ inline void score_run(const float* qf, const char* kbase, int64_t rsb,
+                                 const SlotMap& map, int len, float* out, int w, int NW,
+                                 int lane) {
+  constexpr int EPV = E::kEPV, LPK = D / EPV, KPW = 64 / LPK;
+  const int j = lane % LPK, sub = lane / LPK;
+  const int step = NW * KPW;
+  for (int c0 = w * KPW; c0 < len; c0 += step * U) {
+    uint4 kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * step + sub;
+      if (c < len) kv[u] = *(const uint4*)(kbase + map(c) * rsb + j * 16);
+      else kv[u] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * step + sub;
+      float kf[EPV];
+      unpack<E>(kv[u], kf);
+      float s = 0.f;
+#pragma unroll
+      for (int t = 0; t < EPV; ++t) s = fmaf(qf[t], kf[t], s);
+#pragma unroll
+      for (int o = LPK / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+      if (j == 0 && c < len) out[c] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Exact-boundary Top-K select over n fp32 candidate scores.
+//
+// The page ranks the candidates of each level by their attention score and
+// keeps the K best (速读 › 怎么做的).  Here the ranking key is the fp64 logit
+// s = scale * Σ_t q_t k_t, summed
+// left to right over the exact products of the stored values, ties to the
+// lower node index.  The fp32 scores f differ from the fp64 sums by at most
+// E = d * 2^-23 * |q| * max|k| (a bound for any summation order with at most
+// 2 ulp per operation).  With T the K-th largest fp32 score (radix select),
+// every candidate with f > T + 2E is certainly selected and every candidate
+// with f < T - 2E certainly is not; the candidates in between are re-scored
+// in fp64 exactly as defined and the remaining places filled by rank.
+// ---------------------------------------------------------------------------
+constexpr int kBand = 32;        // band members handled per round
+constexpr int kExactGroup = 4;   // key rows staged per exact re-score group
+
+// LDS work area of one select group (NT threads), carved from dynamic LDS.
+struct SelWork {
+  int* ctl;                      // [8]: 0 bin, 1 krem, 2 nsure, 3 nband, 4 chunk band count
+  int* hist;                     // [NT/64][256] radix histograms (one per wave)
+  int* band_slot;                // [kBand]
+  int* band_node;                // [kBand]
+  double* band_s;                // [kBand]
+  int* sel_slot;                 // [K]
+  float* sel_logit;              // [K]
+  double* best_s;                // [K]
+  int* best_node;                // [K]
+  float* kbuf;                   // [kExactGroup][D+1] staged key rows (padded: no bank conflicts)
+  float* qrow;                   // [D] KG query row, fp32 (exact copy of the stored values)
+};
+
+__host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// Bytes of a SelWork for NT threads, Top-K K, head dim D.
+__host__ __device__ inline size_t selwork_bytes(int NT, int K, int D) {
+  size_t b = 0;
+  b += align16(8 * 4);
+  b += align16((size_t)(NT / 64) * 256 * 4);
+  b += align16(kBand * 4) * 2 + align16(kBand * 8);
+  b += align16((size_t)K * 4) * 2 + align16((size_t)K * 8) + align16((size_t)K * 4);
+  b += align16((size_t)kExactGroup * (D + 1) * 4);
+  b += align16((size_t)D * 4);
+  return b;
+}
+
+__device__ inline SelWork carve_selwork(char*& p, int NT, int K, int D) {
+  SelWork w;
+  auto take = [&](size_t bytes) { char* q = p; p += align16(bytes); return q; };
+  w.ctl = (int*)take(8 * 4);
+  w.hist = (int*)take((size_t)(NT / 64) * 256 * 4);
+  w.band_slot = (int*)take(kBand * 4);
+  w.band_node = (int*)take(kBand * 4);
+  w.band_s = (double*)take(kBand * 8);
+  w.sel_slot = (int*)take((size_t)K * 4);
+  w.sel_logit = (float*)take((size_t)K * 4);
+  w.best_s = (double*)take((size_t)K * 8);
+  w.best_node = (int*)take((size_t)K * 4);
+  w.kbuf = (float*)take((size_t)kExactGroup * (D + 1) * 4);
+  w.qrow = (float*)take((size_t)D * 4);
+  return w;
+}
+
+struct KeyRows {                 // keys of one level and KV head
+  const char* base;
+  int64_t rsb;                   // row stride in bytes
+};
+
+// fp64 logits of band members [0, m): stage key rows in LDS (coalesced), then
+// one thread per member sums the products left to right.
+template <class E, int D, int NT>
+__device__ inline void exact_rescore(const SelWork& S, int m, const KeyRows& kr, double scale,
+                                     int tid) {
+  constexpr int EPV = E::kEPV, CPK = D / EPV;
+  for (int b0 = 0; b0 < m; b0 += kExactGroup) {
+    const int mm = (m - b0) < kExactGroup ? (m - b0) : kExactGroup;
+    for (int idx = tid; idx < mm * CPK; idx += NT) {
+      const int mem = idx / CPK, ch = idx % CPK;
+      const int64_t node = S.band_node[b0 + mem];
+      const uint4 v = *(const uint4*)(kr.base + node * kr.rsb + ch * 16);
+      float f[EPV];
+      unpack<E>(v, f);
+#pragma unroll
+      for (int t = 0; t < EPV; ++t) S.kbuf[mem * (D + 1) + ch * EPV + t] = f[t];
+    }
+    group_sync<NT>();
+    if (tid < mm) {
+      double acc = 0.0;
+      const float* kr_row = S.kbuf + tid * (D + 1);
+      for (int t = 0; t < D; ++t) acc += (double)S.qrow[t] * (double)kr_row[t];
+      S.band_s[b0 + tid] = scale * acc;
+    }
+    group_sync<NT>();
+  }
+}
+
+__device__ inline bool ranks_before(double sa, int na, double sb, int nb) {
+  return sa > sb || (sa == sb && na < nb);
+}
+
+// Returns the count selected (min(K, n)); out_node/out_logit hold the
+// selection sorted by candidate slot.  All NT threads must call it; S.qrow
+// must hold the KG query row.
+template <class E, int D, int NT>
+__device__ int select_topk(const float* sc, int n, int K, double err2, double scale,
+                           const SlotMap& map, const KeyRows& kr, const SelWork& S,
+                           int* out_node, float* out_logit, int tid) {
+  if (K >= n) {
+    for (int i = tid; i < n; i += NT) {
+      out_node[i] = (int)map(i);
+      out_logit[i] = (float)(scale * (double)sc[i]);
+    }
+    group_sync<NT>();
+    return n;
+  }
+  if (K <= 0) return 0;
+
+  // 1) radix select of the K-th largest fp32 score, 8 bits per pass
+  constexpr int NH = NT / 64;
+  uint32_t prefix = 0, mask = 0;
+  if (tid == 0) { S.ctl[2] = 0; S.ctl[3] = 0; }
+  int* myhist = S.hist + (tid >> 6) * 256;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < 256 * NH; i += NT) S.hist[i] = 0;
+    group_sync<NT>();
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t u = ord_key(sc[i]);
+      if ((u & mask) == prefix) atomicAdd(&myhist[(u >> shift) & 255u], 1);
+    }
+    group_sync<NT>();
+    if (tid < 64) {
+      const int lane = tid;
+      const int krem = pass == 0 ? K : S.ctl[1];
+      int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+#pragma unroll
+      for (int w = 0; w < NH; ++w) {
+        const int* hw = S.hist + w * 256 + 4 * lane;
+        c0 += hw[0];
+        c1 += hw[1];
+        c2 += hw[2];
+        c3 += hw[3];
+      }
+      const int tot = c0 + c1 + c2 + c3;
+      int suf = tot;  // inclusive suffix sum over lanes (higher lanes hold higher bins)
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_down(suf, o);
+        if (lane + o < 64) suf += t;
+      }
+      const int above = suf - tot;
+      const unsigned long long hit = __ballot(above < krem && krem <= suf);
+      const int src = __ffsll((long long)hit) - 1;
+      if (lane == src) {
+        int cum = above, bin = 4 * lane, newk = krem - cum;
+        const int cnt[4] = {c0, c1, c2, c3};
+        for (int q = 3; q >= 0; --q) {
+          if (cum + cnt[q] >= krem) { bin = 4 * lane + q; newk = krem - cum; break; }
+          cum += cnt[q];
+        }
+        S.ctl[0] = bin;
+        S.ctl[1] = newk;
+      }
+    }
+    group_sync<NT>();
+    prefix |= (uint32_t)S.ctl[0] << shift;
+    mask |= 0xffu << shift;
+  }
+  const double T = (double)ord_float(prefix);
+  // err2 = 2E; the extra terms are slack for the fp64 threshold arithmetic
+  const double W = err2 * 1.01 + 4.0 * fabs(T) * (1.0 / 8388608.0) + 1e-37;
+
+  // 2) classify: above the band (selected) or inside it
+  for (int i = tid; i < n; i += NT) {
+    const double f = (double)sc[i];
+    if (f > T + W) {
+      const int p = atomicAdd(&S.ctl[2], 1);
+      S.sel_slot[p] = i;
+      S.sel_logit[p] = (float)(scale * f);
+    } else if (f >= T - W) {
+      const int p = atomicAdd(&S.ctl[3], 1);
+      if (p < kBand) S.band_slot[p] = i;
+    }
+  }
+  group_sync<NT>();
+  const int nsure = S.ctl[2], nband = S.ctl[3];
+  const int need = K - nsure;
+
+  if (nband <= kBand) {
+    // 3) exact logits of the band, then the top `need` by (logit desc, index asc)
+    for (int i = tid; i < nband; i += NT) S.band_node[i] = (int)map(S.band_slot[i]);
+    group_sync<NT>();
+    exact_rescore<E, D, NT>(S, nband, kr, scale, tid);
+    for (int i = tid; i < nband; i += NT) {
+      const double si = S.band_s[i];
+      const int ni = S.band_node[i];
+      int rank = 0;
+      for (int j = 0; j < nband; ++j) rank += ranks_before(S.band_s[j], S.band_node[j], si, ni) ? 1 : 0;
+      if (rank < need) {
+        S.sel_slot[nsure + rank] = S.band_slot[i];
+        S.sel_logit[nsure + rank] = (float)si;
+      }
+    }
+    group_sync<NT>();
+  } else {
+    // 3') a wide band (many near-equal scores): sweep the candidates in
+    //     chunks, keeping the best `need` exact logits seen so far
+    constexpr int EPT = (kMaxK + kBand + NT - 1) / NT;
+    int nbest = 0;
+    for (int c0 = 0; c0 < n; c0 += kBand) {
+      if (tid == 0) S.ctl[4] = 0;
+      group_sync<NT>();
+      if (tid < kBand) {
+        const int i = c0 + tid;
+        if (i < n) {
+          const double f = (double)sc[i];
+          if (f <= T + W && f >= T - W) {
+            const int p = atomicAdd(&S.ctl[4], 1);
+            S.band_slot[p] = i;
+            S.band_node[p] = (int)map(i);
+          }
+        }
+      }
+      group_sync<NT>();
+      const int m = S.ctl[4];
+      if (m == 0) continue;
+      exact_rescore<E, D, NT>(S, m, kr, scale, tid);
+      const int tot = nbest + m;
+      double es[EPT];
+      int en[EPT], eslot[EPT], er[EPT];
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) {
+        const int e = tid + q * NT;
+        er[q] = kMaxK + kBand;
+        es[q] = 0.0;
+        en[q] = 0;
+        eslot[q] = 0;
+        if (e < tot) {
+          if (e < nbest) { es[q] = S.best_s[e]; en[q] = S.best_node[e]; eslot[q] = S.sel_slot[nsure + e]; }
+          else { es[q] = S.band_s[e - nbest]; en[q] = S.band_node[e - nbest]; eslot[q] = S.band_slot[e - nbest]; }
+          int rank = 0;
+          for (int x = 0; x < nbest; ++x) rank += ranks_before(S.best_s[x], S.best_node[x], es[q], en[q]) ? 1 : 0;
+          for (int x = 0; x < m; ++x) rank += ranks_before(S.band_s[x], S.band_node[x], es[q], en[q]) ? 1 : 0;
+          er[q] = rank;
+        }
+      }
+      group_sync<NT>();
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) {
+        if (er[q] < need) {
+          S.best_s[er[q]] = es[q];
+          S.best_node[er[q]] = en[q];
+          S.sel_slot[nsure + er[q]] = eslot[q];
+        }
+      }
+      nbest = tot < need ? tot : need;
+      group_sync<NT>();
+    }
+    for (int i = tid; i < need; i += NT) S.sel_logit[nsure + i] = (float)S.best_s[i];
+    group_sync<NT>();
+  }
+
+  // 4) output sorted by candidate slot (deterministic order)
+  for (int i = tid; i < K; i += NT) {
+    const int s = S.sel_slot[i];
+    int r = 0;
+    for (int j = 0; j < K; ++j) r += S.sel_slot[j] < s ? 1 : 0;
+    out_node[r] = (int)map(s);
+    out_logit[r] = S.sel_logit[i];
+  }
+  group_sync<NT>();
+  return K;
+}
+
+// 2E for a query of norm qnorm against keys of norm <= knorm (head dim D).
+template <int D>
+__device__ inline double twice_err_bound(double qnorm, double knorm) {
+  return 2.0 * qnorm * knorm * (double)D * (1.0 / 8388608.0);
+}
+
+}  // namespace hikvp

@@ -7,6 +7,7 @@
 namespace hikvp {
 
 constexpr int kMaxK = 256;        // largest Top-K per level
+constexpr int kMaxD = 128;        // largest head dim
 constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBF16 = 1;
 
@@ -32,21 +33,18 @@ struct RowsDev {
   double scale;               // logit scale (the fp64 ranking uses exactly this value)
 };
 
-struct LevelArgs {
+// One attend call's selection path (root -> mid -> leaf -> KG attention).
+struct StepArgs {
   TreeDev t;
   RowsDev r;
-  int level;                  // 0, 1, 2
-  const int32_t* parent_sel;  // [R, Kp] selection of level-1 (unused at level 0)
-  int Kp;
-  int K;                      // this level's K (before clamping)
-  float* scores;              // [R, cmax] unscaled fp32 dot products, candidate order
-  int64_t cmax;
-  int32_t* band_slot;         // [R, cmax] workspace for near-boundary candidates
-  double* band_s;             // [R, cmax]
-  int32_t* sel;               // [R, K] output selection (-1 padded)
-  float* o_kg;                // leaf level: [R, d] softmax-weighted values (fp32)
-  float* lse_kg;              // leaf level: [R]
-  int stage_lds;              // 1: the Top-K kernel stages a row's scores in LDS
+  int K[3];                   // Top-K per level (before clamping)
+  int64_t c1max;              // mid candidates per row: capacity and row stride of mid_scores
+  int64_t c2max;              // leaf candidates per row: capacity
+  float* mid_scores;          // [R, c1max] unscaled fp32 mid scores, candidate order
+  float* leaf_scores;         // [R, c2max] unscaled fp32 leaf scores, candidate order
+  int32_t* sel[3];            // [R, K[i]] selected node indices, candidate order, -1 padded
+  float* o_kg;                // [R, d] softmax-weighted leaf values (fp32)
+  float* lse_kg;              // [R] log-sum-exp of the selected leaf logits
 };
 
 struct SeqArgs {
@@ -74,8 +72,11 @@ hipError_t launch_validate(const int64_t* off, int64_t count, int64_t children, 
                            BuildStats* stats, hipStream_t s);
 hipError_t launch_key_norms(const void* key, int dtype, int d, int Hkv, int64_t rows,
                             int64_t hs, int64_t rs, unsigned int* out_bits, hipStream_t s);
-hipError_t launch_score_rows(const LevelArgs& a, hipStream_t s);
-hipError_t launch_topk(const LevelArgs& a, hipStream_t s);
+hipError_t launch_root(const StepArgs& a, hipStream_t s);
+hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s);
+hipError_t launch_mid_select(const StepArgs& a, hipStream_t s);
+hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s);
+hipError_t launch_leaf_select(const StepArgs& a, hipStream_t s);
 hipError_t launch_seq_merge(const SeqArgs& a, hipStream_t s);
 
 }  // namespace hikvp
