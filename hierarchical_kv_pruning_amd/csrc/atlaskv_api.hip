@@ -126,7 +126,8 @@ struct Plan {
   int K[3];
   int64_t c1max, c2max;
   double scale;
-  size_t off_mid, off_leaf, off_sel[3], off_okg, off_lse, total;
+  int nsplit;
+  size_t off_mid, off_leaf, off_sel[3], off_okg, off_lse, off_part, total;
 };
 
 // Candidate capacity per row at the mid level (children of K_R distinct
@@ -215,6 +216,8 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   for (int i = 0; i < 3; ++i) { p.off_sel[i] = o; o = align256(o + R * (size_t)p.K[i] * 4); }
   p.off_okg = o;       o = align256(o + R * (size_t)t.d * 4);
   p.off_lse = o;       o = align256(o + R * 4);
+  p.nsplit = seq_splits(p.B, p.N, t.Hkv, p.S);
+  p.off_part = o;      o = align256(o + (p.nsplit > 1 ? R * (size_t)p.nsplit * (t.d + 2) * 4 : 0));
   p.total = o;
   return ATLASKV_OK;
 }
@@ -439,6 +442,9 @@ atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vie
     sa.os[0] = out->stride[0]; sa.os[1] = out->stride[1]; sa.os[2] = out->stride[2];
     sa.out_dtype = out->dtype;
     sa.lse_seq_out = opts ? opts->lse_seq : nullptr;
+    sa.nsplit = p.nsplit;
+    sa.part = p.nsplit > 1 ? (float*)(ws + p.off_part) : nullptr;
+    sa.split_len = p.nsplit > 1 ? seq_split_len(p.S, p.nsplit) : (p.S > 0 ? p.S : 1);
     e = mark(launch_seq_merge(sa, s));
   }
   if (e != hipSuccess) return hip_fail(e, "kernel launch");

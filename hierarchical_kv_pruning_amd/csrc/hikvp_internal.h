@@ -59,6 +59,9 @@ struct SeqArgs {
   int64_t os[3];
   int out_dtype;
   float* lse_seq_out;         // optional [R]
+  float* part;                // [R, nsplit, d + 2] split partials (NULL: no key split)
+  int nsplit;                 // key splits per row
+  int split_len;              // keys per split (multiple of 64); >= S when not split
 };
 
 struct BuildStats {           // device-side result of tree validation
@@ -78,5 +81,7 @@ hipError_t launch_mid_select(const StepArgs& a, hipStream_t s);
 hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s);
 hipError_t launch_leaf_select(const StepArgs& a, hipStream_t s);
 hipError_t launch_seq_merge(const SeqArgs& a, hipStream_t s);
+int seq_splits(int B, int N, int Hkv, int S);   // key splits of the sequence attention
+int seq_split_len(int S, int nsplit);
 
 }  // namespace hikvp

@@ -18,18 +18,122 @@ namespace {
 // ---------------------------------------------------------------------------
 // causal sequence attention + λ merge, one workgroup per (b, n, KV head)
 // ---------------------------------------------------------------------------
+// Online-softmax state of one row over a key range: running max m, running
+// sum l and the unnormalised weighted value sum (this lane's DPL dims).
+template <int DPL>
+struct SoftmaxState {
+  float m, l, acc[DPL];
+};
+
+// Causal attention of one query row over keys [k0, k1): scores in 64-key
+// chunks (16-byte lanes, LPK lanes per key row), chunk-wise online softmax,
+// then the weighted value rows (one coalesced row load per key).
 template <class E, int D>
-__global__ __launch_bounds__(256) void k_seq_merge(SeqArgs a) {
+__device__ inline SoftmaxState<D / 64> attend_range(const SeqArgs& a, const char* kbase, const char* vbase,
+                                                    int64_t kstep, int64_t vstep, const float* qf,
+                                                    int k0, int k1, float* s_p, int lane) {
   constexpr int EPV = E::kEPV, LPK = D / EPV, KPW = 64 / LPK, DPL = D / 64, CH = 64;
-  __shared__ float s_p[4][CH];
+  const int j = lane % LPK;
+  const float scale = (float)a.r.scale;
+  SoftmaxState<DPL> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) st.acc[e] = 0.f;
+  for (int c0 = k0; c0 < k1; c0 += CH) {
+    uint4 kv[CH / KPW];
+#pragma unroll
+    for (int it = 0; it < CH / KPW; ++it) {
+      const int i = c0 + it * KPW + lane / LPK;
+      kv[it] = i < k1 ? *(const uint4*)(kbase + (int64_t)i * kstep + j * 16) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int it = 0; it < CH / KPW; ++it) {
+      const int i = c0 + it * KPW + lane / LPK;
+      float kf[EPV];
+      unpack<E>(kv[it], kf);
+      float s = 0.f;
+#pragma unroll
+      for (int t = 0; t < EPV; ++t) s = fmaf(qf[t], kf[t], s);
+#pragma unroll
+      for (int o = LPK / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+      if (j == 0) s_p[it * KPW + lane / LPK] = (i < k1) ? s * scale : -INFINITY;
+    }
+    wave_sync();
+    const float sv = s_p[lane];
+    const float mn = fmaxf(st.m, wave_max(sv));
+    const float alpha = __expf(st.m - mn);
+    const float p = __expf(sv - mn);
+    st.l = st.l * alpha + wave_sum(p);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) st.acc[e] *= alpha;
+    st.m = mn;
+    wave_sync();
+    s_p[lane] = p;
+    wave_sync();
+    const int cnt = (k1 - c0) < CH ? (k1 - c0) : CH;
+    int i = 0;
+    for (; i + 8 <= cnt; i += 8) {
+      float v[8][DPL];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) load_lane<E, DPL>(vbase + (int64_t)(c0 + i + u) * vstep, lane, v[u]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float pi = s_p[i + u];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) st.acc[e] = fmaf(pi, v[u][e], st.acc[e]);
+      }
+    }
+    for (; i < cnt; ++i) {
+      float v[DPL];
+      load_lane<E, DPL>(vbase + (int64_t)(c0 + i) * vstep, lane, v);
+      const float pi = s_p[i];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) st.acc[e] = fmaf(pi, v[e], st.acc[e]);
+    }
+    wave_sync();
+  }
+  return st;
+}
+
+// λ merge of the sequence half (lse_seq, o_seq) with the KG half of the row.
+template <class E, int D>
+__device__ inline void merge_store(const SeqArgs& a, int row, int b, int n, int h, float lse_seq,
+                                   bool has_seq, const float* oseq, int lane) {
+  constexpr int DPL = D / 64;
+  const float lkg = a.lse_kg[row];
+  float lam;
+  if (lkg == -INFINITY) lam = 0.f;
+  else if (!has_seq) lam = 1.f;
+  else lam = 1.f / (1.f + __expf(lse_seq - lkg));
+  const float* okg = a.o_kg + (int64_t)row * D;
+  const int64_t ob = q_off(a.os, b, n, h);
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    const float o = lam * okg[lane * DPL + e] + (1.f - lam) * oseq[e];
+    const int64_t at = ob + (int64_t)lane * DPL + e;
+    if (a.out_dtype == kDtypeBF16) ((uint16_t*)a.out)[at] = f32_to_bf16_rne(o);
+    else ((float*)a.out)[at] = o;
+  }
+  if (a.lse_seq_out && lane == 0) a.lse_seq_out[row] = lse_seq;
+}
+
+// One workgroup per (b, n, KV head [, key split]); one wave per query head of
+// the group, so the group's K/V rows are shared through L1.  With splits the
+// wave writes its partial (m, l, acc) and k_seq_combine finishes the row.
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_seq_attend(SeqArgs a) {
+  constexpr int EPV = E::kEPV, LPK = D / EPV, DPL = D / 64;
+  __shared__ float s_p[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
   const int g = blockIdx.x % a.Hkv;
   const int bn = blockIdx.x / a.Hkv;
   const int n = bn % a.r.N, b = bn / a.r.N;
+  const int split = blockIdx.y, nsplit = gridDim.y;
   const int G = a.r.G;
-  const int j = lane % LPK;
-  const float scale = (float)a.r.scale;
   const int vis = a.k ? a.S - a.r.N + n + 1 : 0;
+  const int k0 = split * a.split_len;
+  const int k1 = (k0 + a.split_len) < vis ? (k0 + a.split_len) : vis;
   const char* kbase = (const char*)a.k + ((int64_t)b * a.ks[0] + (int64_t)g * a.ks[2]) * E::kBytes;
   const char* vbase = (const char*)a.v + ((int64_t)b * a.vs[0] + (int64_t)g * a.vs[2]) * E::kBytes;
   const int64_t kstep = a.ks[1] * E::kBytes, vstep = a.vs[1] * E::kBytes;
@@ -40,69 +144,63 @@ __global__ __launch_bounds__(256) void k_seq_merge(SeqArgs a) {
     float qf[EPV];
     {
       const char* qp = (const char*)a.r.q + q_off(a.r.qs, b, n, h) * E::kBytes;
-      unpack<E>(*(const uint4*)(qp + j * 16), qf);
+      unpack<E>(*(const uint4*)(qp + (lane % LPK) * 16), qf);
     }
-    float acc[DPL];
+    const SoftmaxState<DPL> st =
+        attend_range<E, D>(a, kbase, vbase, kstep, vstep, qf, k0, k1, s_p[wave], lane);
+    if (nsplit > 1) {
+      float* part = a.part + ((int64_t)row * nsplit + split) * (D + 2);
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-    float m = -INFINITY, l = 0.f;
-    for (int c0 = 0; c0 < vis; c0 += CH) {
-#pragma unroll
-      for (int it = 0; it < CH / KPW; ++it) {
-        const int i = c0 + it * KPW + lane / LPK;
-        float s = 0.f;
-        if (i < vis) {
-          const uint4 kv = *(const uint4*)(kbase + (int64_t)i * kstep + j * 16);
-          float kf[EPV];
-          unpack<E>(kv, kf);
-#pragma unroll
-          for (int t = 0; t < EPV; ++t) s = fmaf(qf[t], kf[t], s);
-        }
-#pragma unroll
-        for (int o = LPK / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
-        if (j == 0) s_p[wave][it * KPW + lane / LPK] = (i < vis) ? s * scale : -INFINITY;
+      for (int e = 0; e < DPL; ++e) part[lane * DPL + e] = st.acc[e];
+      if (lane == 0) {
+        part[D] = st.m;
+        part[D + 1] = st.l;
       }
-      wave_sync();
-      const float sv = s_p[wave][lane];
-      const float mn = fmaxf(m, wave_max(sv));
-      const float alpha = __expf(m - mn);
-      const float p = __expf(sv - mn);
-      l = l * alpha + wave_sum(p);
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] *= alpha;
-      m = mn;
-      wave_sync();
-      s_p[wave][lane] = p;
-      wave_sync();
-      const int cnt = (vis - c0) < CH ? (vis - c0) : CH;
-#pragma unroll 4
-      for (int i = 0; i < cnt; ++i) {
-        const float pi = s_p[wave][i];
-        float v[DPL];
-        load_lane<E, DPL>(vbase + (int64_t)(c0 + i) * vstep, lane, v);
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(pi, v[e], acc[e]);
-      }
-      wave_sync();
+      continue;
     }
-    const float lse_seq = vis > 0 ? m + logf(l) : -INFINITY;
-    const float lkg = a.lse_kg[row];
-    float lam;
-    if (lkg == -INFINITY) lam = 0.f;
-    else if (vis == 0) lam = 1.f;
-    else lam = 1.f / (1.f + __expf(lse_seq - lkg));
-    const float inv_l = vis > 0 ? 1.f / l : 0.f;
-    const float* okg = a.o_kg + (int64_t)row * D;
-    const int64_t ob = q_off(a.os, b, n, h);
+    const bool has = vis > 0;
+    float oseq[DPL];
+    const float inv_l = has ? 1.f / st.l : 0.f;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      const float o = lam * okg[lane * DPL + e] + (1.f - lam) * (acc[e] * inv_l);
-      const int64_t at = ob + (int64_t)lane * DPL + e;
-      if (a.out_dtype == kDtypeBF16) ((uint16_t*)a.out)[at] = f32_to_bf16_rne(o);
-      else ((float*)a.out)[at] = o;
-    }
-    if (a.lse_seq_out && lane == 0) a.lse_seq_out[row] = lse_seq;
+    for (int e = 0; e < DPL; ++e) oseq[e] = st.acc[e] * inv_l;
+    merge_store<E, D>(a, row, b, n, h, has ? st.m + logf(st.l) : -INFINITY, has, oseq, lane);
   }
+}
+
+// Log-sum-exp combine of the key splits of one row (one wave per row), then
+// the λ merge with the KG half.
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_seq_combine(SeqArgs a, int nsplit) {
+  constexpr int DPL = D / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+  const int row = blockIdx.x * nwave + wave;
+  if (row >= a.r.R) return;
+  const int h = row % a.r.Hq;
+  const int bn = row / a.r.Hq;
+  const int n = bn % a.r.N, b = bn / a.r.N;
+  const float* part = a.part + (int64_t)row * nsplit * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
+  float l = 0.f, acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < nsplit; ++s) {
+      const float* ps = part + s * (D + 2);
+      const float ms = ps[D];
+      if (ms == -INFINITY) continue;
+      const float w = __expf(ms - M);
+      l = fmaf(w, ps[D + 1], l);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, ps[lane * DPL + e], acc[e]);
+    }
+  }
+  const bool has = M != -INFINITY;
+  float oseq[DPL];
+  const float inv_l = has ? 1.f / l : 0.f;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) oseq[e] = acc[e] * inv_l;
+  merge_store<E, D>(a, row, b, n, h, has ? M + logf(l) : -INFINITY, has, oseq, lane);
 }
 
 }  // namespace
@@ -116,11 +214,31 @@ __global__ __launch_bounds__(256) void k_seq_merge(SeqArgs a) {
     else return hipErrorInvalidValue;                                                                \
   } while (0)
 
+int seq_splits(int B, int N, int Hkv, int S) {
+  // enough workgroups to fill the chip (~8k); each split covers >= 128 keys
+  const int64_t items = (int64_t)B * N * Hkv;
+  if (items <= 0 || S <= 0) return 1;
+  int64_t want = (8192 + items - 1) / items;
+  const int64_t maxs = (S + 127) / 128;
+  if (want > maxs) want = maxs;
+  return want < 1 ? 1 : (int)want;
+}
+
+int seq_split_len(int S, int nsplit) {
+  int len = (S + nsplit - 1) / nsplit;
+  return (len + 63) / 64 * 64;
+}
+
 hipError_t launch_seq_merge(const SeqArgs& a, hipStream_t s) {
   if (a.r.R <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)(a.r.B * a.r.N * a.Hkv);
   const int waves = a.r.G < 4 ? a.r.G : 4;
-  HIKVP_DISPATCH(a.dtype, a.d, k_seq_merge, dim3(blocks), dim3(64 * waves), 0, s, a);
+  const int nsplit = a.part ? a.nsplit : 1;
+  HIKVP_DISPATCH(a.dtype, a.d, k_seq_attend, dim3(blocks, (unsigned)nsplit), dim3(64 * waves), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit <= 1) return e;
+  const unsigned cblocks = (unsigned)((a.r.R + 3) / 4);
+  HIKVP_DISPATCH(a.dtype, a.d, k_seq_combine, dim3(cblocks), dim3(256), 0, s, a, nsplit);
   return hipGetLastError();
 }
 
