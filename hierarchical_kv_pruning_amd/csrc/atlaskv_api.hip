@@ -128,6 +128,7 @@ struct Plan {
   double scale;
   int nsplit;
   size_t off_mid, off_leaf, off_sel[3], off_okg, off_lse, off_part, total;
+  size_t off_mid_base, off_bcnt, off_bslot, off_bhead, off_bnext, off_blist, off_bcount;
 };
 
 // Candidate capacity per row at the mid level (children of K_R distinct
@@ -203,6 +204,8 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   p.R = (int)(B * N * Hq);
   p.G = (int)(Hq / t.Hkv);
   for (int i = 0; i < 3; ++i) p.K[i] = Kpl[i];
+  if ((int64_t)p.R * p.K[1] >= kIndexLimit || (int64_t)t.Hkv * t.count[1] >= kIndexLimit)
+    return fail(ATLASKV_ERR_UNSUPPORTED, "B*N*Hq*K_I and Hkv*M_I must be below 2^31");
   candidate_capacity(v, p.K, &p.c1max, &p.c2max);
   if (p.c1max >= kIndexLimit || p.c2max >= kIndexLimit)
     return fail(ATLASKV_ERR_UNSUPPORTED, "candidates per row must be below 2^31");
@@ -214,6 +217,13 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   p.off_mid = o;       o = align256(o + R * (size_t)p.c1max * 4);
   p.off_leaf = o;      o = align256(o + R * (size_t)p.c2max * 4);
   for (int i = 0; i < 3; ++i) { p.off_sel[i] = o; o = align256(o + R * (size_t)p.K[i] * 4); }
+  p.off_mid_base = o;  o = align256(o + R * (size_t)p.K[1] * 4);
+  p.off_bcnt = o;      o = align256(o + (size_t)t.Hkv * (size_t)t.count[1] * 4);
+  p.off_bslot = o;     o = align256(o + (size_t)t.Hkv * (size_t)t.count[1] * 8 * kBucketSlots);
+  p.off_bhead = o;     o = align256(o + (size_t)t.Hkv * (size_t)t.count[1] * 4);
+  p.off_bnext = o;     o = align256(o + R * (size_t)p.K[1] * 4);
+  p.off_blist = o;     o = align256(o + R * (size_t)p.K[1] * 16);
+  p.off_bcount = o;    o = align256(o + 4);
   p.off_okg = o;       o = align256(o + R * (size_t)t.d * 4);
   p.off_lse = o;       o = align256(o + R * 4);
   p.nsplit = seq_splits(p.B, p.N, t.Hkv, p.S);
@@ -414,12 +424,20 @@ atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vie
   a.c2max = p.c2max;
   a.mid_scores = (float*)(ws + p.off_mid);
   a.leaf_scores = (float*)(ws + p.off_leaf);
+  a.mid_base = (int32_t*)(ws + p.off_mid_base);
+  a.bucket_cnt = (int32_t*)(ws + p.off_bcnt);
+  a.bucket_slot = (int2*)(ws + p.off_bslot);
+  a.bucket_head = (int32_t*)(ws + p.off_bhead);
+  a.bucket_next = (int32_t*)(ws + p.off_bnext);
+  a.bucket_desc = (int4*)(ws + p.off_blist);
+  a.bucket_count = (int32_t*)(ws + p.off_bcount);
   a.o_kg = o_kg;
   a.lse_kg = lse_kg;
   // 速读 › 怎么做的: roots -> Top-K -> their children -> Top-K -> leaves -> Top-K
   e = mark(launch_root(a, s));
   if (e == hipSuccess) e = mark(launch_mid_gemm(a, s));
   if (e == hipSuccess) e = mark(launch_mid_select(a, s));
+  if (e == hipSuccess) e = launch_leaf_buckets(a, s);
   if (e == hipSuccess) e = mark(launch_leaf_score(a, s));
   if (e == hipSuccess) e = mark(launch_leaf_select(a, s));
   if (e == hipSuccess) {

@@ -8,6 +8,7 @@ namespace hikvp {
 
 constexpr int kMaxK = 256;        // largest Top-K per level
 constexpr int kMaxD = 128;        // largest head dim
+constexpr int kBucketSlots = 16;  // members of a (head, mid) bucket stored without a list walk
 constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBF16 = 1;
 
@@ -43,6 +44,13 @@ struct StepArgs {
   float* mid_scores;          // [R, c1max] unscaled fp32 mid scores, candidate order
   float* leaf_scores;         // [R, c2max] unscaled fp32 leaf scores, candidate order
   int32_t* sel[3];            // [R, K[i]] selected node indices, candidate order, -1 padded
+  int32_t* mid_base;          // [R, K[1]] first leaf-candidate slot of each selected mid
+  int32_t* bucket_cnt;        // [Hkv * M_I] rows that selected the (head, mid)
+  int2* bucket_slot;          // [Hkv * M_I * kBucketSlots] first members: (row, first leaf slot)
+  int32_t* bucket_head;       // [Hkv * M_I] overflow members: list head, -1 none
+  int32_t* bucket_next;       // [R * K[1]] next overflow entry of the same (head, mid)
+  int4* bucket_desc;          // [R * K[1]] distinct (head, mid): key g*M_I+mid, fanout, first leaf element (lo, hi)
+  int32_t* bucket_count;      // [1] number of distinct keys
   float* o_kg;                // [R, d] softmax-weighted leaf values (fp32)
   float* lse_kg;              // [R] log-sum-exp of the selected leaf logits
 };
@@ -78,7 +86,8 @@ hipError_t launch_key_norms(const void* key, int dtype, int d, int Hkv, int64_t 
 hipError_t launch_root(const StepArgs& a, hipStream_t s);
 hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s);
 hipError_t launch_mid_select(const StepArgs& a, hipStream_t s);
-hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s);
+hipError_t launch_leaf_buckets(const StepArgs& a, hipStream_t s);  // link rows by selected (head, mid)
+hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s);   // grouped buckets + overflow members
 hipError_t launch_leaf_select(const StepArgs& a, hipStream_t s);
 hipError_t launch_seq_merge(const SeqArgs& a, hipStream_t s);
 int seq_splits(int B, int N, int Hkv, int S);   // key splits of the sequence attention

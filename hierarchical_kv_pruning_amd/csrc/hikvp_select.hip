@@ -16,9 +16,11 @@
 //               is read once per bucket instead of once per row.  Scores land
 //               in each row's candidate slots of the workspace.
 //   k_mid_select   one wave per row: Top-K_I over the row's mid scores.
-//   k_leaf_score   one workgroup per row, small LDS (high occupancy): streams
-//               the selected mids' leaf spans (contiguous in the head-major
-//               layout) and writes the row's leaf scores.
+//   k_bucket_clear / k_bucket_link  link the rows that selected each distinct
+//               (KV head, mid) into one list per bucket.
+//   k_leaf_score   one wave per bucket: streams the mid's leaf span once (it is
+//               contiguous in the head-major layout) and writes the scores of
+//               every member row into that row's candidate slots.
 //   k_leaf_select  one wave per row: Top-K_L, then the KG softmax over the
 //               selected leaves and the weighted sum of their values.
 #include <hip/hip_runtime.h>
@@ -305,40 +307,221 @@ __global__ __launch_bounds__(256) void k_mid_select(StepArgs a, size_t wave_byte
                                        a.r.scale, SlotMap{W.pre, W.base, a.K[0]}, KeyRows{kb, rsb},
                                        W.sel, W.out_node, W.out_logit, lane);
   int32_t* o1 = a.sel[1] + (int64_t)row * K1;
-  for (int i = lane; i < K1; i += 64) o1[i] = i < k1 ? W.out_node[i] : -1;
+  int32_t* ob = a.mid_base + (int64_t)row * K1;
+  const int64_t* off1 = a.t.off[1];
+  int carry = 0;
+  for (int i0 = 0; i0 < K1; i0 += 64) {
+    const int i = i0 + lane;
+    const int node = i < k1 ? W.out_node[i] : -1;
+    const int fan = node >= 0 ? (int)(off1[node + 1] - off1[node]) : 0;
+    int incl = fan;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (i < K1) {
+      o1[i] = node;
+      ob[i] = carry + incl - fan;  // first leaf-candidate slot of this mid in the row's list
+    }
+    carry += __shfl(incl, 63);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// leaf scoring: stream the selected mids' leaf spans, one workgroup per row
+// leaf scoring, deduplicated: every distinct (KV head, mid) selected by any
+// row is one bucket.  The link kernel writes one 16-byte descriptor per bucket
+// (key, fanout, element offset of the span) and stores the first
+// kBucketSlots member rows as (row, first leaf slot) pairs; later members go
+// to a linked list scored by k_leaf_score_overflow.  One wave per bucket
+// streams the mid's leaf span (contiguous in the head-major layout) once and
+// scores it for every member row, prefetching its next bucket's descriptor.
+// Each member's dot products are computed independently, so results do not
+// depend on the (atomic) member or bucket order.
 // ---------------------------------------------------------------------------
-struct StreamSmem {
-  int pre[kMaxK + 1];
-  int64_t base[kMaxK];
-  float qrow[kMaxD];
-};
+__global__ void k_bucket_clear(StepArgs a, int64_t nkeys) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nkeys;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    a.bucket_cnt[i] = 0;
+    a.bucket_head[i] = -1;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.bucket_count = 0;
+}
 
-template <class E, int D>
-__global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
-  constexpr int EPV = E::kEPV, LPK = D / EPV;
-  __shared__ StreamSmem L;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwave = blockDim.x >> 6;
-  const int row = row_of_block(a.r, blockIdx.x);
+__global__ void k_bucket_link(StepArgs a) {
+  const int K1 = a.K[1];
+  const int64_t n = (int64_t)a.r.R * K1;
+  const int MI = (int)a.t.count[1];
+  const int64_t* off1 = a.t.off[1];
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int mid = a.sel[1][e];
+    if (mid < 0) continue;
+    const int row = (int)(e / K1);
+    const int g = (row % a.r.Hq) / a.r.G;
+    const int64_t key = (int64_t)g * MI + mid;
+    const int rank = atomicAdd(&a.bucket_cnt[key], 1);
+    if (rank == 0) {
+      const int64_t f0 = off1[mid];
+      const int64_t first = (int64_t)g * a.t.hs[2] + f0 * a.t.rs[2];
+      const int v = atomicAdd(a.bucket_count, 1);
+      a.bucket_desc[v] = make_int4((int)key, (int)(off1[mid + 1] - f0), (int)(uint32_t)first,
+                                   (int)(first >> 32));
+    }
+    if (rank < kBucketSlots) {
+      a.bucket_slot[key * kBucketSlots + rank] = make_int2(row, a.mid_base[e]);
+    } else {
+      a.bucket_next[e] = atomicExch(&a.bucket_head[key], (int)e);
+    }
+  }
+}
+
+template <class E, int D, int MB>
+__device__ inline void score_members(const StepArgs& a, const char* kb, int F, int m, const int* rows,
+                                     const int* bases, const float (*qf)[E::kEPV], int lane) {
+  constexpr int EPV = E::kEPV, LPK = D / EPV, KPW = 64 / LPK, U = 4;
+  const int j = lane % LPK, sub = lane / LPK;
+  const int64_t rsb = a.t.rs[2] * E::kBytes;
+  for (int c0 = 0; c0 < F; c0 += KPW * U) {
+    uint4 kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * KPW + sub;
+      kv[u] = c < F ? *(const uint4*)(kb + c * rsb + j * 16) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * KPW + sub;
+      float kf[EPV];
+      unpack<E>(kv[u], kf);
+#pragma unroll
+      for (int mm = 0; mm < MB; ++mm) {
+        if (mm >= m) break;
+        float s = 0.f;
+#pragma unroll
+        for (int t = 0; t < EPV; ++t) s = fmaf(qf[mm][t], kf[t], s);
+#pragma unroll
+        for (int o = LPK / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+        if (j == 0 && c < F) a.leaf_scores[(int64_t)rows[mm] * a.c2max + bases[mm] + c] = s;
+      }
+    }
+  }
+}
+
+template <class E>
+__device__ inline void load_q_chunk(const StepArgs& a, int row, int j, float* qf) {
   int b, n, h;
   decode_row(a.r, row, b, n, h);
-  const int g = h / a.r.G;
   const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes;
-  for (int t = tid; t < D; t += blockDim.x) L.qrow[t] = load_f32<E>(qp, t);
-  const int K1 = a.K[1];
-  if (wave == 0) build_candidates(a.sel[1] + (int64_t)row * K1, K1, a.t.off[1], lane, L.pre, L.base);
-  __syncthreads();
-  const int n2 = L.pre[K1];
-  float qf[EPV];
+  unpack<E>(*(const uint4*)(qp + j * 16), qf);
+}
+
+// One wave per bucket: the member rows (up to 16) are the M side and the
+// span's keys the N side of 16x16 MFMA tiles, so each 16-key tile costs four
+// 16-byte loads per lane, 8 MFMAs and one 64-byte store per member.
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
+  constexpr int KCH = D * E::kBytes / 64;  // 16-byte pieces per lane per row
+  constexpr int TU = 2;                    // key tiles in flight per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+  const int quad = lane >> 4, col = lane & 15;
+  const int nb = *a.bucket_count;
+  const char* kbase = (const char*)a.t.key[2];
+  const int64_t rsb = a.t.rs[2] * E::kBytes;
+  const int stride = gridDim.x * nwave;
+  int v = blockIdx.x * nwave + wave;
+  int4 cur = v < nb ? a.bucket_desc[v] : make_int4(0, 0, 0, 0);
+  while (v < nb) {
+    const int vn = v + stride;
+    const int4 nxt = vn < nb ? a.bucket_desc[vn] : make_int4(0, 0, 0, 0);  // prefetch
+    const int key = cur.x, F = cur.y;
+    const int64_t first = (int64_t)(uint32_t)cur.z | ((int64_t)cur.w << 32);
+    const char* kb = kbase + first * E::kBytes;
+    int cnt = a.bucket_cnt[key];
+    cnt = cnt < kBucketSlots ? cnt : kBucketSlots;
+    // tile row `col` = member col: its query pieces (zeros past the members)
+    int2 mem = make_int2(-1, 0);
+    uint4 afr[KCH];
+    if (col < cnt) {
+      mem = a.bucket_slot[(int64_t)key * kBucketSlots + col];
+      int b, n, h;
+      decode_row(a.r, mem.x, b, n, h);
+      const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes;
 #pragma unroll
-  for (int t = 0; t < EPV; ++t) qf[t] = L.qrow[(lane % LPK) * EPV + t];
-  int64_t rsb;
-  const char* kb = key_base(a.t, 2, g, rsb, E::kBytes);
-  score_run<E, D, 8>(qf, kb, rsb, SlotMap{L.pre, L.base, K1}, n2, a.leaf_scores + (int64_t)row * a.c2max,
-                     wave, nwave, lane);
+      for (int m = 0; m < KCH; ++m) afr[m] = *(const uint4*)(qp + m * 64 + quad * 16);
+    } else {
+#pragma unroll
+      for (int m = 0; m < KCH; ++m) afr[m] = make_uint4(0, 0, 0, 0);
+    }
+    // the 4 members whose scores this lane stores: tile rows 4*quad .. 4*quad+3
+    int srow[4], sbase[4];
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv) {
+      srow[vv] = __shfl(mem.x, 4 * quad + vv);
+      sbase[vv] = __shfl(mem.y, 4 * quad + vv);
+    }
+    for (int t0 = 0; t0 < F; t0 += 16 * TU) {
+      uint4 bfr[TU][KCH];
+#pragma unroll
+      for (int u = 0; u < TU; ++u) {
+        const int c = t0 + u * 16 + col;
+#pragma unroll
+        for (int m = 0; m < KCH; ++m)
+          bfr[u][m] = c < F ? *(const uint4*)(kb + c * rsb + m * 64 + quad * 16) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < TU; ++u) {
+        const int c = t0 + u * 16 + col;
+        const float4_t acc = tile_dot<E, KCH>(afr, bfr[u]);
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) {
+          if (4 * quad + vv < cnt && c < F)
+            a.leaf_scores[(int64_t)srow[vv] * a.c2max + sbase[vv] + c] = acc[vv];
+        }
+      }
+    }
+    cur = nxt;
+    v = vn;
+  }
+}
+
+// Members of buckets with more than kBucketSlots rows: one wave per bucket
+// walks the overflow list, two rows per pass over the span.
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_leaf_score_overflow(StepArgs a) {
+  constexpr int EPV = E::kEPV, LPK = D / EPV, MB = 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+  const int j = lane % LPK;
+  const int nb = *a.bucket_count;
+  const int K1 = a.K[1];
+  const char* kbase = (const char*)a.t.key[2];
+  for (int v = blockIdx.x * nwave + wave; v < nb; v += gridDim.x * nwave) {
+    const int4 d = a.bucket_desc[v];
+    if (a.bucket_cnt[d.x] <= kBucketSlots) continue;
+    const int64_t first = (int64_t)(uint32_t)d.z | ((int64_t)d.w << 32);
+    const char* kb = kbase + first * E::kBytes;
+    int e = a.bucket_head[d.x];
+    while (e != -1) {  // wave-uniform walk
+      int rows[MB], bases[MB];
+      float qf[MB][EPV];
+      int m = 0;
+#pragma unroll
+      for (int mm = 0; mm < MB; ++mm) {
+        rows[mm] = -1;
+        bases[mm] = 0;
+#pragma unroll
+        for (int t = 0; t < EPV; ++t) qf[mm][t] = 0.f;
+        if (e != -1) {
+          rows[mm] = e / K1;
+          bases[mm] = a.mid_base[e];
+          load_q_chunk<E>(a, rows[mm], j, qf[mm]);
+          e = a.bucket_next[e];
+          ++m;
+        }
+      }
+      score_members<E, D, MB>(a, kb, d.y, m, rows, bases, qf, lane);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -466,9 +649,34 @@ hipError_t launch_mid_select(const StepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_leaf_buckets(const StepArgs& a, hipStream_t s) {
+  if (a.r.R <= 0 || a.K[1] <= 0) return hipSuccess;
+  const int64_t nkeys = (int64_t)a.t.Hkv * a.t.count[1];
+  int64_t blocks = (nkeys + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_bucket_clear, dim3((unsigned)blocks), dim3(256), 0, s, a, nkeys);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)a.r.R * a.K[1];
+  blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_bucket_link, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s) {
-  if (a.r.R <= 0) return hipSuccess;
-  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_score, dim3((unsigned)a.r.R), dim3(256), 0, s, a);
+  if (a.r.R <= 0 || a.K[1] <= 0) return hipSuccess;
+  // at most R * K_I distinct (head, mid) buckets
+  const int64_t nb_max = (int64_t)a.r.R * a.K[1];
+  int64_t blocks = (nb_max + 3) / 4;
+  if (blocks > 2048) blocks = 2048;
+  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_score, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  blocks = (nb_max + 3) / 4;
+  if (blocks > 2048) blocks = 2048;
+  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_score_overflow, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
