@@ -223,6 +223,7 @@ __device__ inline void score_run(const float* qf, const char* kbase, int64_t rsb
 // in fp64 exactly as defined and the remaining places filled by rank.
 // ---------------------------------------------------------------------------
 constexpr int kBand = 32;        // band members handled per round
+constexpr int kLoadBatch = 8;    // score loads kept in flight per lane in the select passes
 constexpr int kExactGroup = 4;   // key rows staged per exact re-score group
 
 // LDS work area of one select group (NT threads), carved from dynamic LDS.
@@ -236,6 +237,10 @@ struct SelWork {
   float* sel_logit;              // [K]
   double* best_s;                // [K]
   int* best_node;                // [K]
+  double* tmp_s;                 // [K + kBand] wide-band merge scratch
+  int* tmp_node;                 // [K + kBand]
+  int* tmp_slot;                 // [K + kBand]
+  int* tmp_rank;                 // [K + kBand]
   float* kbuf;                   // [kExactGroup][D+1] staged key rows (padded: no bank conflicts)
   float* qrow;                   // [D] KG query row, fp32 (exact copy of the stored values)
 };
@@ -249,6 +254,7 @@ __host__ __device__ inline size_t selwork_bytes(int NT, int K, int D) {
   b += align16((size_t)(NT / 64) * 256 * 4);
   b += align16(kBand * 4) * 2 + align16(kBand * 8);
   b += align16((size_t)K * 4) * 2 + align16((size_t)K * 8) + align16((size_t)K * 4);
+  b += align16((size_t)(K + kBand) * 8) + 3 * align16((size_t)(K + kBand) * 4);
   b += align16((size_t)kExactGroup * (D + 1) * 4);
   b += align16((size_t)D * 4);
   return b;
@@ -266,6 +272,10 @@ __device__ inline SelWork carve_selwork(char*& p, int NT, int K, int D) {
   w.sel_logit = (float*)take((size_t)K * 4);
   w.best_s = (double*)take((size_t)K * 8);
   w.best_node = (int*)take((size_t)K * 4);
+  w.tmp_s = (double*)take((size_t)(K + kBand) * 8);
+  w.tmp_node = (int*)take((size_t)(K + kBand) * 4);
+  w.tmp_slot = (int*)take((size_t)(K + kBand) * 4);
+  w.tmp_rank = (int*)take((size_t)(K + kBand) * 4);
   w.kbuf = (float*)take((size_t)kExactGroup * (D + 1) * 4);
   w.qrow = (float*)take((size_t)D * 4);
   return w;
@@ -297,6 +307,7 @@ __device__ inline void exact_rescore(const SelWork& S, int m, const KeyRows& kr,
     if (tid < mm) {
       double acc = 0.0;
       const float* kr_row = S.kbuf + tid * (D + 1);
+#pragma unroll 4
       for (int t = 0; t < D; ++t) acc += (double)S.qrow[t] * (double)kr_row[t];
       S.band_s[b0 + tid] = scale * acc;
     }
@@ -308,40 +319,141 @@ __device__ inline bool ranks_before(double sa, int na, double sb, int nb) {
   return sa > sb || (sa == sb && na < nb);
 }
 
+// Sources of a row's candidate scores for select_topk.  each(n, tid, f) calls
+// f(i, score_i) for the candidates i owned by thread tid (i = tid + k*NT);
+// at(i) reads any candidate (memory; used only by the wide-band sweep).
+template <int NT>
+struct MemScores {
+  const float* p;
+  template <class F>
+  __device__ inline void each(int n, int tid, F&& f) const {
+    for (int i0 = tid; i0 < n; i0 += NT * kLoadBatch) {
+      float x[kLoadBatch];
+#pragma unroll
+      for (int b = 0; b < kLoadBatch; ++b) x[b] = (i0 + b * NT < n) ? p[i0 + b * NT] : 0.f;
+#pragma unroll
+      for (int b = 0; b < kLoadBatch; ++b)
+        if (i0 + b * NT < n) f(i0 + b * NT, x[b]);
+    }
+  }
+  __device__ inline float at(int i) const { return p[i]; }
+};
+
+// Up to NT*SPT scores held in registers: loaded once, then every pass of the
+// select runs without memory traffic.
+template <int NT, int SPT>
+struct RegScores {
+  float v[SPT];
+  const float* p;
+  __device__ inline void load(const float* src, int n, int tid) {
+    p = src;
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) v[k] = (k * NT + tid < n) ? src[k * NT + tid] : 0.f;
+  }
+  template <class F>
+  __device__ inline void each(int n, int tid, F&& f) const {
+#pragma unroll
+    for (int k = 0; k < SPT; ++k)
+      if (k * NT + tid < n) f(k * NT + tid, v[k]);
+  }
+  __device__ inline float at(int i) const { return p[i]; }
+};
+
 // Returns the count selected (min(K, n)); out_node/out_logit hold the
 // selection sorted by candidate slot.  All NT threads must call it; S.qrow
 // must hold the KG query row.
-template <class E, int D, int NT>
-__device__ int select_topk(const float* sc, int n, int K, double err2, double scale,
+template <class E, int D, int NT, class Src>
+__device__ int select_topk(const Src& src, int n, int K, double err2, double scale,
                            const SlotMap& map, const KeyRows& kr, const SelWork& S,
                            int* out_node, float* out_logit, int tid) {
   if (K >= n) {
-    for (int i = tid; i < n; i += NT) {
+    src.each(n, tid, [&](int i, float f) {
       out_node[i] = (int)map(i);
-      out_logit[i] = (float)(scale * (double)sc[i]);
-    }
+      out_logit[i] = (float)(scale * (double)f);
+    });
     group_sync<NT>();
     return n;
   }
   if (K <= 0) return 0;
 
-  // 1) radix select of the K-th largest fp32 score, 8 bits per pass
+  // 1) radix select of the K-th largest fp32 score, 8 bits per pass.
+  //    The first digit (top byte of the order key) is nearly constant over a
+  //    score distribution, so it is counted without LDS atomics: per-thread
+  //    counters over the kWin top bytes just below the maximum, then a group
+  //    reduction.  Only if the K-th key lies below that window is the first
+  //    digit histogrammed like the others.
+  constexpr int kWin = 4;
   constexpr int NH = NT / 64;
   uint32_t prefix = 0, mask = 0;
+  int krem = K;
+  int first_pass = 0;
   if (tid == 0) { S.ctl[2] = 0; S.ctl[3] = 0; }
   int* myhist = S.hist + (tid >> 6) * 256;
-  for (int pass = 0; pass < 4; ++pass) {
+  {
+    uint32_t tmax = 0;
+    src.each(n, tid, [&](int, float f) { tmax = max(tmax, ord_key(f) >> 24); });
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, o));
+    if (NH > 1) {
+      if ((tid & 63) == 0) S.hist[tid >> 6] = (int)tmax;
+      group_sync<NT>();
+      for (int w = 0; w < NH; ++w) tmax = max(tmax, (uint32_t)S.hist[w]);
+      group_sync<NT>();
+    }
+    int cnt[kWin];
+#pragma unroll
+    for (int b = 0; b < kWin; ++b) cnt[b] = 0;
+    src.each(n, tid, [&](int, float f) {
+      const uint32_t d = tmax - (ord_key(f) >> 24);
+#pragma unroll
+      for (int c = 0; c < kWin; ++c) cnt[c] += (d == (uint32_t)c) ? 1 : 0;
+    });
+#pragma unroll
+    for (int c = 0; c < kWin; ++c) {
+      int v = cnt[c];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+      cnt[c] = v;
+    }
+    if (NH > 1) {
+      if ((tid & 63) < kWin) {
+        int mine = 0;
+#pragma unroll
+        for (int c = 0; c < kWin; ++c) mine = ((tid & 63) == c) ? cnt[c] : mine;
+        S.hist[(tid >> 6) * kWin + (tid & 63)] = mine;
+      }
+      group_sync<NT>();
+#pragma unroll
+      for (int c = 0; c < kWin; ++c) {
+        int v = 0;
+        for (int w = 0; w < NH; ++w) v += S.hist[w * kWin + c];
+        cnt[c] = v;
+      }
+      group_sync<NT>();
+    }
+    int cum = 0, found = -1;
+#pragma unroll
+    for (int c = 0; c < kWin; ++c) {
+      if (found < 0 && cum + cnt[c] >= K) { found = c; krem = K - cum; }
+      cum += cnt[c];
+    }
+    if (found >= 0) {
+      prefix = (tmax - (uint32_t)found) << 24;
+      mask = 0xff000000u;
+      first_pass = 1;
+    }
+  }
+  for (int pass = first_pass; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     for (int i = tid; i < 256 * NH; i += NT) S.hist[i] = 0;
     group_sync<NT>();
-    for (int i = tid; i < n; i += NT) {
-      const uint32_t u = ord_key(sc[i]);
+    src.each(n, tid, [&](int, float f) {
+      const uint32_t u = ord_key(f);
       if ((u & mask) == prefix) atomicAdd(&myhist[(u >> shift) & 255u], 1);
-    }
+    });
     group_sync<NT>();
     if (tid < 64) {
       const int lane = tid;
-      const int krem = pass == 0 ? K : S.ctl[1];
       int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
 #pragma unroll
       for (int w = 0; w < NH; ++w) {
@@ -360,13 +472,13 @@ __device__ int select_topk(const float* sc, int n, int K, double err2, double sc
       }
       const int above = suf - tot;
       const unsigned long long hit = __ballot(above < krem && krem <= suf);
-      const int src = __ffsll((long long)hit) - 1;
-      if (lane == src) {
+      const int src_lane = __ffsll((long long)hit) - 1;
+      if (lane == src_lane) {
         int cum = above, bin = 4 * lane, newk = krem - cum;
-        const int cnt[4] = {c0, c1, c2, c3};
+        const int cnt4[4] = {c0, c1, c2, c3};
         for (int q = 3; q >= 0; --q) {
-          if (cum + cnt[q] >= krem) { bin = 4 * lane + q; newk = krem - cum; break; }
-          cum += cnt[q];
+          if (cum + cnt4[q] >= krem) { bin = 4 * lane + q; newk = krem - cum; break; }
+          cum += cnt4[q];
         }
         S.ctl[0] = bin;
         S.ctl[1] = newk;
@@ -375,28 +487,42 @@ __device__ int select_topk(const float* sc, int n, int K, double err2, double sc
     group_sync<NT>();
     prefix |= (uint32_t)S.ctl[0] << shift;
     mask |= 0xffu << shift;
+    krem = S.ctl[1];
   }
   const double T = (double)ord_float(prefix);
   // err2 = 2E; the extra terms are slack for the fp64 threshold arithmetic
   const double W = err2 * 1.01 + 4.0 * fabs(T) * (1.0 / 8388608.0) + 1e-37;
 
-  // 2) classify: above the band (selected) or inside it
-  for (int i = tid; i < n; i += NT) {
-    const double f = (double)sc[i];
-    if (f > T + W) {
+  // 2) classify: above the band (selected) or inside it.  fp32 thresholds,
+  //    each widened beyond T +- W by far more than its own rounding, so the
+  //    band can only grow (it is resolved exactly below).
+  const float hi = (float)(T + W * 1.0001);
+  const float lo = (float)(T - W * 1.0001);
+  const float fscale = (float)scale;
+  src.each(n, tid, [&](int i, float f) {
+    if (f > hi) {
       const int p = atomicAdd(&S.ctl[2], 1);
       S.sel_slot[p] = i;
-      S.sel_logit[p] = (float)(scale * f);
-    } else if (f >= T - W) {
+      S.sel_logit[p] = fscale * f;
+    } else if (f >= lo) {
       const int p = atomicAdd(&S.ctl[3], 1);
       if (p < kBand) S.band_slot[p] = i;
     }
-  }
+  });
   group_sync<NT>();
   const int nsure = S.ctl[2], nband = S.ctl[3];
   const int need = K - nsure;
 
-  if (nband <= kBand) {
+  if (nband == need && nband <= kBand) {
+    // 3) the band holds exactly the remaining places: all of it is selected,
+    //    whatever the exact order inside it (its fp32 logits are kept)
+    for (int i = tid; i < nband; i += NT) {
+      const int slot = S.band_slot[i];
+      S.sel_slot[nsure + i] = slot;
+      S.sel_logit[nsure + i] = (float)(scale * (double)src.at(slot));
+    }
+    group_sync<NT>();
+  } else if (nband <= kBand) {
     // 3) exact logits of the band, then the top `need` by (logit desc, index asc)
     for (int i = tid; i < nband; i += NT) S.band_node[i] = (int)map(S.band_slot[i]);
     group_sync<NT>();
@@ -415,7 +541,6 @@ __device__ int select_topk(const float* sc, int n, int K, double err2, double sc
   } else {
     // 3') a wide band (many near-equal scores): sweep the candidates in
     //     chunks, keeping the best `need` exact logits seen so far
-    constexpr int EPT = (kMaxK + kBand + NT - 1) / NT;
     int nbest = 0;
     for (int c0 = 0; c0 < n; c0 += kBand) {
       if (tid == 0) S.ctl[4] = 0;
@@ -423,8 +548,8 @@ __device__ int select_topk(const float* sc, int n, int K, double err2, double sc
       if (tid < kBand) {
         const int i = c0 + tid;
         if (i < n) {
-          const double f = (double)sc[i];
-          if (f <= T + W && f >= T - W) {
+          const float f = src.at(i);
+          if (f <= hi && f >= lo) {
             const int p = atomicAdd(&S.ctl[4], 1);
             S.band_slot[p] = i;
             S.band_node[p] = (int)map(i);
@@ -436,31 +561,27 @@ __device__ int select_topk(const float* sc, int n, int K, double err2, double sc
       if (m == 0) continue;
       exact_rescore<E, D, NT>(S, m, kr, scale, tid);
       const int tot = nbest + m;
-      double es[EPT];
-      int en[EPT], eslot[EPT], er[EPT];
-#pragma unroll
-      for (int q = 0; q < EPT; ++q) {
-        const int e = tid + q * NT;
-        er[q] = kMaxK + kBand;
-        es[q] = 0.0;
-        en[q] = 0;
-        eslot[q] = 0;
-        if (e < tot) {
-          if (e < nbest) { es[q] = S.best_s[e]; en[q] = S.best_node[e]; eslot[q] = S.sel_slot[nsure + e]; }
-          else { es[q] = S.band_s[e - nbest]; en[q] = S.band_node[e - nbest]; eslot[q] = S.band_slot[e - nbest]; }
-          int rank = 0;
-          for (int x = 0; x < nbest; ++x) rank += ranks_before(S.best_s[x], S.best_node[x], es[q], en[q]) ? 1 : 0;
-          for (int x = 0; x < m; ++x) rank += ranks_before(S.band_s[x], S.band_node[x], es[q], en[q]) ? 1 : 0;
-          er[q] = rank;
-        }
+      // rank every element of (best so far) + (this chunk's band) in LDS
+      for (int e = tid; e < tot; e += NT) {
+        double es;
+        int en, eslot;
+        if (e < nbest) { es = S.best_s[e]; en = S.best_node[e]; eslot = S.sel_slot[nsure + e]; }
+        else { es = S.band_s[e - nbest]; en = S.band_node[e - nbest]; eslot = S.band_slot[e - nbest]; }
+        int rank = 0;
+        for (int x = 0; x < nbest; ++x) rank += ranks_before(S.best_s[x], S.best_node[x], es, en) ? 1 : 0;
+        for (int x = 0; x < m; ++x) rank += ranks_before(S.band_s[x], S.band_node[x], es, en) ? 1 : 0;
+        S.tmp_s[e] = es;
+        S.tmp_node[e] = en;
+        S.tmp_slot[e] = eslot;
+        S.tmp_rank[e] = rank;
       }
       group_sync<NT>();
-#pragma unroll
-      for (int q = 0; q < EPT; ++q) {
-        if (er[q] < need) {
-          S.best_s[er[q]] = es[q];
-          S.best_node[er[q]] = en[q];
-          S.sel_slot[nsure + er[q]] = eslot[q];
+      for (int e = tid; e < tot; e += NT) {
+        const int r = S.tmp_rank[e];
+        if (r < need) {
+          S.best_s[r] = S.tmp_s[e];
+          S.best_node[r] = S.tmp_node[e];
+          S.sel_slot[nsure + r] = S.tmp_slot[e];
         }
       }
       nbest = tot < need ? tot : need;

@@ -15,13 +15,14 @@
 //               j's child span with bf16 (or fp32) MFMA 16x16 tiles; the span
 //               is read once per bucket instead of once per row.  Scores land
 //               in each row's candidate slots of the workspace.
-//   k_mid_select   one wave per row: Top-K_I over the row's mid scores.
+//   k_mid_select   one wave per row (a workgroup per row for long candidate
+//               lists): Top-K_I over the row's mid scores.
 //   k_bucket_clear / k_bucket_link  link the rows that selected each distinct
 //               (KV head, mid) into one list per bucket.
 //   k_leaf_score   one wave per bucket: streams the mid's leaf span once (it is
 //               contiguous in the head-major layout) and writes the scores of
 //               every member row into that row's candidate slots.
-//   k_leaf_select  one wave per row: Top-K_L, then the KG softmax over the
+//   k_leaf_select  one wave (or workgroup) per row: Top-K_L, then the KG softmax over the
 //               selected leaves and the weighted sum of their values.
 #include <hip/hip_runtime.h>
 
@@ -45,7 +46,8 @@ __device__ inline const char* key_base(const TreeDev& t, int lev, int g, int64_t
 // ---------------------------------------------------------------------------
 // per-row select kernels: one wave per row, LDS work area carved per wave
 // ---------------------------------------------------------------------------
-constexpr int kStageMax = 2048;  // candidate scores staged in LDS up to this count
+constexpr int kStageMax = 0;     // mid/leaf scores are not staged in LDS (registers instead)
+constexpr int kRegScores = 32;   // candidate scores held per thread in the select kernels
 
 struct RowWork {
   SelWork sel;
@@ -56,14 +58,14 @@ struct RowWork {
   float* stage;                  // [stage] staged scores (or unused)
 };
 
-__host__ __device__ inline size_t rowwork_bytes(int K, int Kp, int D, int stage) {
-  return selwork_bytes(64, K, D) + 2 * align16((size_t)K * 4) + align16((size_t)(Kp + 1) * 4) +
+__host__ __device__ inline size_t rowwork_bytes(int K, int Kp, int D, int stage, int NT = 64) {
+  return selwork_bytes(NT, K, D) + 2 * align16((size_t)K * 4) + align16((size_t)(Kp + 1) * 4) +
          align16((size_t)Kp * 8) + align16((size_t)stage * 4);
 }
 
-__device__ inline RowWork carve_rowwork(char* p, int K, int Kp, int D, int stage) {
+__device__ inline RowWork carve_rowwork(char* p, int K, int Kp, int D, int stage, int NT = 64) {
   RowWork w;
-  w.sel = carve_selwork(p, 64, K, D);
+  w.sel = carve_selwork(p, NT, K, D);
   auto take = [&](size_t bytes) { char* q = p; p += align16(bytes); return q; };
   w.out_node = (int*)take((size_t)K * 4);
   w.out_logit = (float*)take((size_t)K * 4);
@@ -115,8 +117,9 @@ __global__ __launch_bounds__(256) void k_root(StepArgs a, size_t wave_bytes, int
   score_run<E, D, 4>(qf, kb, rsb, ident, MR, sc, 0, 1, lane);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   wave_sync();
-  const int k = select_topk<E, D, 64>(sc, MR, K, twice_err_bound<D>(qnorm, a.t.norm[g]), a.r.scale,
-                                      ident, KeyRows{kb, rsb}, W.sel, W.out_node, W.out_logit, lane);
+  const int k = select_topk<E, D, 64>(MemScores<64>{sc}, MR, K, twice_err_bound<D>(qnorm, a.t.norm[g]),
+                                      a.r.scale, ident, KeyRows{kb, rsb}, W.sel, W.out_node, W.out_logit,
+                                      lane);
   int32_t* out = a.sel[0] + (int64_t)row * K;
   for (int i = lane; i < K; i += 64) out[i] = i < k ? W.out_node[i] : -1;
 }
@@ -264,48 +267,70 @@ __global__ __launch_bounds__(256) void k_mid_gemm(StepArgs a) {
 // ---------------------------------------------------------------------------
 // mid-level Top-K, one wave per row
 // ---------------------------------------------------------------------------
-// Prologue of the mid/leaf select kernels: query row, candidate list of level
-// `lev` (children of the row's level-1 selection), scores staged in LDS when
-// they fit.  Returns the candidate count.
-template <class E, int D>
-__device__ inline int select_prologue(const StepArgs& a, const RowWork& W, int row, int lev,
-                                      const float* gscores, int stage, int& g, double& qnorm,
-                                      const float*& sc, int lane) {
+// Prologue of the mid/leaf select kernels (NT threads per row): query row
+// in LDS, its norm, the candidate list of level `lev` (children of the row's
+// level-1 selection).  Returns the candidate count.
+template <class E, int D, int NT>
+__device__ inline int select_prologue(const StepArgs& a, const RowWork& W, int row, int lev, int& g,
+                                      double& qnorm, int gtid) {
   int b, n, h;
   decode_row(a.r, row, b, n, h);
   g = h / a.r.G;
-  qnorm = load_query<E, D>(a.r, b, n, h, W.sel.qrow, lane);
+  const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes;
+  for (int t = gtid; t < D; t += NT) W.sel.qrow[t] = load_f32<E>(qp, t);
+  group_sync<NT>();
   const int Kp = a.K[lev - 1];
-  const int nc = build_candidates(a.sel[lev - 1] + (int64_t)row * Kp, Kp, a.t.off[lev - 1], lane,
-                                  W.pre, W.base);
-  sc = gscores;
-  if (stage) {
-    for (int i = lane; i < nc; i += 64) W.stage[i] = gscores[i];
-    sc = W.stage;
+  if (gtid < 64) {
+    float qq = 0.f;
+    for (int t = gtid; t < D; t += 64) qq = fmaf(W.sel.qrow[t], W.sel.qrow[t], qq);
+    qq = wave_sum(qq);
+    if (gtid == 0) W.sel.ctl[7] = __float_as_int((float)(sqrt((double)qq) * 1.0001));
+    build_candidates(a.sel[lev - 1] + (int64_t)row * Kp, Kp, a.t.off[lev - 1], gtid, W.pre, W.base);
   }
-  wave_sync();
-  return nc;
+  group_sync<NT>();
+  qnorm = (double)__int_as_float(W.sel.ctl[7]);
+  return W.pre[Kp];
 }
 
-template <class E, int D>
-__global__ __launch_bounds__(256) void k_mid_select(StepArgs a, size_t wave_bytes, int stage) {
+// The row's candidate scores: in registers (SPT per thread, loaded once) or,
+// for very long candidate lists, read from the workspace in every pass.
+template <int NT, int SPT>
+struct RowScores {
+  using type = RegScores<NT, SPT>;
+  __device__ static inline type make(const float* p, int cap, int tid) {
+    type r;
+    r.load(p, cap, tid);
+    return r;
+  }
+};
+template <int NT>
+struct RowScores<NT, 0> {
+  using type = MemScores<NT>;
+  __device__ static inline type make(const float* p, int, int) { return type{p}; }
+};
+
+template <class E, int D, int NT, int SPT>
+__device__ inline void mid_select_body(const StepArgs& a, size_t group_bytes) {
   extern __shared__ __align__(16) char smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
-  const int blk = blockIdx.x * nwave + wave;
-  if (blk >= a.r.R) return;
+  const int groups = blockDim.x / NT, grp = threadIdx.x / NT, gtid = threadIdx.x % NT;
+  const int blk = blockIdx.x * groups + grp;
+  if (blk >= a.r.R) return;  // whole group (whole waves) leaves together
   const int K1 = a.K[1];
-  RowWork W = carve_rowwork(smem + (size_t)wave * wave_bytes, K1, a.K[0], D, stage);
+  RowWork W = carve_rowwork(smem + (size_t)grp * group_bytes, K1, a.K[0], D, 0, NT);
   const int row = row_of_block(a.r, blk);
+  // the scores do not depend on the candidate list: load them first
+  const auto sc = RowScores<NT, SPT>::make(a.mid_scores + (int64_t)row * a.c1max, (int)a.c1max, gtid);
   int g;
   double qnorm;
-  const float* sc;
-  const int n1 = select_prologue<E, D>(a, W, row, 1, a.mid_scores + (int64_t)row * a.c1max, stage, g,
-                                       qnorm, sc, lane);
+  const int n1 = select_prologue<E, D, NT>(a, W, row, 1, g, qnorm, gtid);
   int64_t rsb;
   const char* kb = key_base(a.t, 1, g, rsb, E::kBytes);
-  const int k1 = select_topk<E, D, 64>(sc, n1, K1, twice_err_bound<D>(qnorm, a.t.norm[a.t.Hkv + g]),
-                                       a.r.scale, SlotMap{W.pre, W.base, a.K[0]}, KeyRows{kb, rsb},
-                                       W.sel, W.out_node, W.out_logit, lane);
+  const int k1 = select_topk<E, D, NT>(sc, n1, K1,
+                                       twice_err_bound<D>(qnorm, a.t.norm[a.t.Hkv + g]), a.r.scale,
+                                       SlotMap{W.pre, W.base, a.K[0]}, KeyRows{kb, rsb}, W.sel,
+                                       W.out_node, W.out_logit, gtid);
+  if (gtid >= 64) return;
+  const int lane = gtid;
   int32_t* o1 = a.sel[1] + (int64_t)row * K1;
   int32_t* ob = a.mid_base + (int64_t)row * K1;
   const int64_t* off1 = a.t.off[1];
@@ -326,6 +351,20 @@ __global__ __launch_bounds__(256) void k_mid_select(StepArgs a, size_t wave_byte
     }
     carry += __shfl(incl, 63);
   }
+}
+
+// one wave per row (candidate lists up to a few thousand) or one workgroup per row
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_mid_select(StepArgs a, size_t gb) {
+  mid_select_body<E, D, 64, 0>(a, gb);
+}
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_mid_select_wide(StepArgs a, size_t gb) {
+  mid_select_body<E, D, 256, 0>(a, gb);
+}
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_mid_select_mem(StepArgs a, size_t gb) {
+  mid_select_body<E, D, 256, 0>(a, gb);
 }
 
 // ---------------------------------------------------------------------------
@@ -527,28 +566,30 @@ __global__ __launch_bounds__(256) void k_leaf_score_overflow(StepArgs a) {
 // ---------------------------------------------------------------------------
 // leaf Top-K and the KG softmax over the selected leaves, one wave per row
 // ---------------------------------------------------------------------------
-template <class E, int D>
-__global__ __launch_bounds__(256) void k_leaf_select(StepArgs a, size_t wave_bytes, int stage) {
+template <class E, int D, int NT, int SPT>
+__device__ inline void leaf_select_body(const StepArgs& a, size_t group_bytes) {
   constexpr int DPL = D / 64;
   extern __shared__ __align__(16) char smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
-  const int blk = blockIdx.x * nwave + wave;
+  const int groups = blockDim.x / NT, grp = threadIdx.x / NT, gtid = threadIdx.x % NT;
+  const int blk = blockIdx.x * groups + grp;
   if (blk >= a.r.R) return;
   const int K2 = a.K[2];
-  RowWork W = carve_rowwork(smem + (size_t)wave * wave_bytes, K2, a.K[1], D, stage);
+  RowWork W = carve_rowwork(smem + (size_t)grp * group_bytes, K2, a.K[1], D, 0, NT);
   const int row = row_of_block(a.r, blk);
+  const auto sc = RowScores<NT, SPT>::make(a.leaf_scores + (int64_t)row * a.c2max, (int)a.c2max, gtid);
   int g;
   double qnorm;
-  const float* sc;
-  const int n2 = select_prologue<E, D>(a, W, row, 2, a.leaf_scores + (int64_t)row * a.c2max, stage, g,
-                                       qnorm, sc, lane);
+  const int n2 = select_prologue<E, D, NT>(a, W, row, 2, g, qnorm, gtid);
   int64_t rsb;
   const char* kb = key_base(a.t, 2, g, rsb, E::kBytes);
-  const int k2 = select_topk<E, D, 64>(sc, n2, K2, twice_err_bound<D>(qnorm, a.t.norm[2 * a.t.Hkv + g]),
-                                       a.r.scale, SlotMap{W.pre, W.base, a.K[1]}, KeyRows{kb, rsb},
-                                       W.sel, W.out_node, W.out_logit, lane);
+  const int k2 = select_topk<E, D, NT>(sc, n2, K2,
+                                       twice_err_bound<D>(qnorm, a.t.norm[2 * a.t.Hkv + g]), a.r.scale,
+                                       SlotMap{W.pre, W.base, a.K[1]}, KeyRows{kb, rsb}, W.sel,
+                                       W.out_node, W.out_logit, gtid);
   int32_t* o2 = a.sel[2] + (int64_t)row * K2;
-  for (int i = lane; i < K2; i += 64) o2[i] = i < k2 ? W.out_node[i] : -1;
+  for (int i = gtid; i < K2; i += NT) o2[i] = i < k2 ? W.out_node[i] : -1;
+  if (gtid >= 64) return;  // the KG half is formed by the group's first wave
+  const int lane = gtid;
 
   // KG half: softmax over the selected leaves' logits, weighted values
   float* okg = a.o_kg + (int64_t)row * D;
@@ -599,6 +640,19 @@ __global__ __launch_bounds__(256) void k_leaf_select(StepArgs a, size_t wave_byt
   if (lane == 0) a.lse_kg[row] = mx + logf(sum);
 }
 
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_leaf_select(StepArgs a, size_t gb) {
+  leaf_select_body<E, D, 64, 0>(a, gb);
+}
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_leaf_select_wide(StepArgs a, size_t gb) {
+  leaf_select_body<E, D, 256, 0>(a, gb);
+}
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_leaf_select_mem(StepArgs a, size_t gb) {
+  leaf_select_body<E, D, 256, 0>(a, gb);
+}
+
 }  // namespace
 
 #define HIKVP_DISPATCH(dtype, d, KERNEL, ...)                                                        \
@@ -612,8 +666,8 @@ __global__ __launch_bounds__(256) void k_leaf_select(StepArgs a, size_t wave_byt
 
 // Waves per block and per-wave LDS of a per-row select kernel.
 static bool row_launch_shape(int K, int Kp, int D, int64_t cands, int& wpb, size_t& wave_bytes,
-                             int& stage) {
-  stage = cands <= kStageMax ? (int)cands : 0;
+                             int& stage, bool must_stage = false) {
+  stage = (must_stage || cands <= kStageMax) ? (int)cands : 0;
   wave_bytes = rowwork_bytes(K, Kp, D, stage);
   const size_t limit = 64 * 1024;
   wpb = 4;
@@ -625,7 +679,9 @@ hipError_t launch_root(const StepArgs& a, hipStream_t s) {
   if (a.r.R <= 0) return hipSuccess;
   int wpb, stage;
   size_t wb;
-  if (!row_launch_shape(a.K[0], 0, a.t.d, a.t.count[0], wpb, wb, stage)) return hipErrorInvalidValue;
+  // root scores are produced in-kernel: keep them in LDS when they fit
+  if (!row_launch_shape(a.K[0], 0, a.t.d, a.t.count[0], wpb, wb, stage, a.t.count[0] <= 2048))
+    return hipErrorInvalidValue;
   if (!stage && a.t.count[0] > a.c1max) return hipErrorInvalidValue;  // spill buffer too small
   const unsigned blocks = (unsigned)((a.r.R + wpb - 1) / wpb);
   HIKVP_DISPATCH(a.t.dtype, a.t.d, k_root, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb, stage);
@@ -639,13 +695,22 @@ hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+
 hipError_t launch_mid_select(const StepArgs& a, hipStream_t s) {
   if (a.r.R <= 0) return hipSuccess;
+  if (a.c1max > 64 * kRegScores) {
+    const size_t gb = rowwork_bytes(a.K[1], a.K[0], a.t.d, 0, 256);
+    if (a.c1max <= 256 * kRegScores)
+      HIKVP_DISPATCH(a.t.dtype, a.t.d, k_mid_select_wide, dim3((unsigned)a.r.R), dim3(256), gb, s, a, gb);
+    else
+      HIKVP_DISPATCH(a.t.dtype, a.t.d, k_mid_select_mem, dim3((unsigned)a.r.R), dim3(256), gb, s, a, gb);
+    return hipGetLastError();
+  }
   int wpb, stage;
   size_t wb;
-  if (!row_launch_shape(a.K[1], a.K[0], a.t.d, a.c1max, wpb, wb, stage)) return hipErrorInvalidValue;
+  if (!row_launch_shape(a.K[1], a.K[0], a.t.d, 0, wpb, wb, stage)) return hipErrorInvalidValue;
   const unsigned blocks = (unsigned)((a.r.R + wpb - 1) / wpb);
-  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_mid_select, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb, stage);
+  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_mid_select, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb);
   return hipGetLastError();
 }
 
@@ -682,11 +747,19 @@ hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s) {
 
 hipError_t launch_leaf_select(const StepArgs& a, hipStream_t s) {
   if (a.r.R <= 0) return hipSuccess;
+  if (a.c2max > 64 * kRegScores) {
+    const size_t gb = rowwork_bytes(a.K[2], a.K[1], a.t.d, 0, 256);
+    if (a.c2max <= 256 * kRegScores)
+      HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_select_wide, dim3((unsigned)a.r.R), dim3(256), gb, s, a, gb);
+    else
+      HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_select_mem, dim3((unsigned)a.r.R), dim3(256), gb, s, a, gb);
+    return hipGetLastError();
+  }
   int wpb, stage;
   size_t wb;
-  if (!row_launch_shape(a.K[2], a.K[1], a.t.d, a.c2max, wpb, wb, stage)) return hipErrorInvalidValue;
+  if (!row_launch_shape(a.K[2], a.K[1], a.t.d, 0, wpb, wb, stage)) return hipErrorInvalidValue;
   const unsigned blocks = (unsigned)((a.r.R + wpb - 1) / wpb);
-  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_select, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb, stage);
+  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_select, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb);
   return hipGetLastError();
 }
 

@@ -70,6 +70,13 @@ def test_k_edge_cases(K):
     _check(_small(seed=5, M=2000), K=K)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_wide_candidate_lists(dtype):
+    """More than 2048 candidates per row at the mid and the leaf level: the
+    select kernels then use a whole workgroup per row."""
+    _check(_small(seed=21, dtype=dtype, N=5, S_kv=9, M_R=3, M_I=6000, M=30000, K=(2, 3, 40)))
+
+
 def test_full_k_selects_every_leaf():
     case = _small(seed=6, M_R=4, M_I=20, M=200, K=(4, 20, 200))
     gpu, _, _ = _check(case)
