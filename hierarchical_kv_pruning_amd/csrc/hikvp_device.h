@@ -173,6 +173,42 @@ struct SlotMap {
 };
 
 // ---------------------------------------------------------------------------
+// MFMA 16x16 tiles
+// ---------------------------------------------------------------------------
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// One 16x16 tile of <q_member, key_child> over the head dim.  Lane l feeds
+// tile row/column l%16 with the 16-byte pieces m*64 + (l/16)*16 of its row
+// (m < KCH); the same element permutation on both operands leaves the dot
+// products unchanged.
+template <class E, int KCH>
+__device__ inline float4_t tile_dot(const uint4* a, const uint4* b) {
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (E::kBytes == 2) {
+#pragma unroll
+    for (int m = 0; m < KCH; ++m) {
+      short4_t alo, ahi, blo, bhi;
+      alo = __builtin_bit_cast(short4_t, make_uint2(a[m].x, a[m].y));
+      ahi = __builtin_bit_cast(short4_t, make_uint2(a[m].z, a[m].w));
+      blo = __builtin_bit_cast(short4_t, make_uint2(b[m].x, b[m].y));
+      bhi = __builtin_bit_cast(short4_t, make_uint2(b[m].z, b[m].w));
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, blo, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, bhi, acc, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < KCH; ++m) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[m].x), __uint_as_float(b[m].x), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[m].y), __uint_as_float(b[m].y), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[m].z), __uint_as_float(b[m].z), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[m].w), __uint_as_float(b[m].w), acc, 0, 0, 0);
+    }
+  }
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
 // Score a run of candidate keys: out[c] = <q, key[first + c]> (fp32, unscaled)
 // for c < len.  LPK lanes read one key row as 16-byte pieces, so a wave load
 // covers 64/LPK whole rows; U loads are kept in flight per lane.  NW waves

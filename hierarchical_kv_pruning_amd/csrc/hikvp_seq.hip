@@ -10,6 +10,8 @@
 //     log-sum-exp shares, λ_kg = 1 / (1 + exp(lse_seq - lse_kg)).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "hikvp_device.h"
 
 namespace hikvp {
@@ -167,6 +169,205 @@ __global__ __launch_bounds__(256) void k_seq_attend(SeqArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill: flash attention on MFMA.  One workgroup per (b, KV head, 16-token
+// tile); one wave per query head of the group.  Per 16-key tile: S = Q K^T on
+// a 16x16 MFMA tile (rows = the tile's tokens), causal mask, online softmax
+// per row, then O += P V on MFMA with the V tile transposed once in LDS and
+// shared by the group's heads (P goes through a per-wave LDS tile to become
+// the A operand).  bf16 inputs use bf16 MFMA (P as a hi + lo pair of bf16),
+// fp32 inputs fp32 MFMA throughout.
+// ---------------------------------------------------------------------------
+template <class E, int D>
+struct FlashSmem {
+  static constexpr bool kB = E::kBytes == 2;
+  static constexpr int kVp = kB ? 24 : 20;   // padded key stride of the transposed V tile
+  static constexpr int kPp = kB ? 24 : 20;
+  typename std::conditional<kB, uint16_t, float>::type vt[D][kVp];
+  typename std::conditional<kB, uint16_t, float>::type p[4][16][kPp];
+  uint16_t plo[kB ? 4 : 1][16][kPp];         // bf16 residual of P (P = hi + lo)
+};
+
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_seq_flash(SeqArgs a) {
+  constexpr int EPV = E::kEPV, KCH = D * E::kBytes / 64, NCT = D / 16;
+  constexpr bool kB = E::kBytes == 2;
+  __shared__ FlashSmem<E, D> L;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+  const int quad = lane >> 4, col = lane & 15;
+  const int tiles = (a.r.N + 15) / 16;
+  const int g = blockIdx.x % a.Hkv;
+  const int t = (blockIdx.x / a.Hkv) % tiles;
+  const int b = blockIdx.x / (a.Hkv * tiles);
+  const int n0 = t * 16;
+  const int N = a.r.N, S = a.S, G = a.r.G;
+  const int nlast = (n0 + 16 < N ? n0 + 16 : N) - 1;
+  const int kseen = S - N + nlast + 1;          // keys seen by the tile's last token
+  const int split = blockIdx.y, nsplit = gridDim.y;
+  const int kbeg = split * a.split_len;
+  const int kmax = (kbeg + a.split_len) < kseen ? (kbeg + a.split_len) : kseen;
+  const float scale = (float)a.r.scale;
+  const char* kbase = (const char*)a.k + ((int64_t)b * a.ks[0] + (int64_t)g * a.ks[2]) * E::kBytes;
+  const char* vbase = (const char*)a.v + ((int64_t)b * a.vs[0] + (int64_t)g * a.vs[2]) * E::kBytes;
+  const int64_t kstep = a.ks[1] * E::kBytes, vstep = a.vs[1] * E::kBytes;
+  const int passes = (G + nwave - 1) / nwave;
+
+  for (int ps = 0; ps < passes; ++ps) {         // uniform over the workgroup (barriers inside)
+    const int hw = ps * nwave + wave;
+    const bool active = hw < G;
+    const int h = g * G + (active ? hw : 0);
+    // A operand: the tile's query rows (row = token n0 + col)
+    uint4 afr[KCH];
+    {
+      const int tok = n0 + col;
+      if (active && tok < N) {
+        const char* qp = (const char*)a.r.q + q_off(a.r.qs, b, tok, h) * E::kBytes;
+#pragma unroll
+        for (int m = 0; m < KCH; ++m) afr[m] = *(const uint4*)(qp + m * 64 + quad * 16);
+      } else {
+#pragma unroll
+        for (int m = 0; m < KCH; ++m) afr[m] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    float4_t O[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) O[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+    float mrow[4], lrow[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) { mrow[v] = -INFINITY; lrow[v] = 0.f; }
+
+    for (int k0 = kbeg; k0 < kmax; k0 += 16) {
+      // V tile (16 keys x D) into LDS, transposed: vt[dim][key]
+      __syncthreads();
+      for (int x = threadIdx.x; x < 16 * (D / EPV); x += blockDim.x) {
+        const int key = x / (D / EPV), ch = x % (D / EPV);
+        uint4 vv = make_uint4(0, 0, 0, 0);
+        if (k0 + key < S) vv = *(const uint4*)(vbase + (int64_t)(k0 + key) * vstep + ch * 16);
+        if constexpr (kB) {
+          const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            L.vt[ch * 8 + 2 * e][key] = (uint16_t)(w[e] & 0xffffu);
+            L.vt[ch * 8 + 2 * e + 1][key] = (uint16_t)(w[e] >> 16);
+          }
+        } else {
+          L.vt[ch * 4 + 0][key] = __uint_as_float(vv.x);
+          L.vt[ch * 4 + 1][key] = __uint_as_float(vv.y);
+          L.vt[ch * 4 + 2][key] = __uint_as_float(vv.z);
+          L.vt[ch * 4 + 3][key] = __uint_as_float(vv.w);
+        }
+      }
+      __syncthreads();
+      if (!active) continue;
+      // S = Q K^T for 16 tokens x 16 keys
+      uint4 bfr[KCH];
+      {
+        const int key = k0 + col;
+        if (key < S) {
+          const char* kp = kbase + (int64_t)key * kstep;
+#pragma unroll
+          for (int m = 0; m < KCH; ++m) bfr[m] = *(const uint4*)(kp + m * 64 + quad * 16);
+        } else {
+#pragma unroll
+          for (int m = 0; m < KCH; ++m) bfr[m] = make_uint4(0, 0, 0, 0);
+        }
+      }
+      const float4_t sacc = tile_dot<E, KCH>(afr, bfr);
+      float p4[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tok = n0 + quad * 4 + v;
+        const int vis = S - N + tok + 1;
+        const bool ok = tok < N && (k0 + col) < vis;
+        const float sv = ok ? sacc[v] * scale : -INFINITY;
+        float mx = sv;
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        const float mn = fmaxf(mrow[v], mx);
+        const float alpha = mn == -INFINITY ? 1.f : __expf(mrow[v] - mn);
+        const float pv = ok ? __expf(sv - mn) : 0.f;
+        float rs = pv;
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) rs += __shfl_xor(rs, o);
+        lrow[v] = lrow[v] * alpha + rs;
+        mrow[v] = mn;
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) O[c][v] *= alpha;
+        p4[v] = pv;
+      }
+      // P (rows 4*quad+v, key col) -> LDS, read back as the A operand.  For
+      // bf16 MFMA, P is split into two bf16 parts (hi + lo) so the product
+      // keeps ~16 significant bits of P.
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if constexpr (kB) {
+          const uint16_t hi = f32_to_bf16_rne(p4[v]);
+          L.p[wave][quad * 4 + v][col] = hi;
+          L.plo[wave][quad * 4 + v][col] = f32_to_bf16_rne(p4[v] - __uint_as_float((uint32_t)hi << 16));
+        } else {
+          L.p[wave][quad * 4 + v][col] = p4[v];
+        }
+      }
+      wave_sync();
+      if constexpr (kB) {
+        const short4_t pa = __builtin_bit_cast(short4_t, *(const uint2*)&L.p[wave][col][quad * 4]);
+        const short4_t pl = __builtin_bit_cast(short4_t, *(const uint2*)&L.plo[wave][col][quad * 4]);
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+          const short4_t vb = __builtin_bit_cast(short4_t, *(const uint2*)&L.vt[c * 16 + col][quad * 4]);
+          O[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[c], 0, 0, 0);
+          O[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vb, O[c], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const float pa = L.p[wave][col][st * 4 + quad];
+#pragma unroll
+          for (int c = 0; c < NCT; ++c)
+            O[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, L.vt[c * 16 + col][st * 4 + quad], O[c], 0, 0, 0);
+        }
+      }
+      wave_sync();
+    }
+    if (!active) continue;
+    // epilogue: rows 4*quad+v, dims 16c+col
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int tok = n0 + quad * 4 + v;
+      if (tok >= N) continue;
+      const int row = (b * N + tok) * a.r.Hq + h;
+      if (nsplit > 1) {  // partial (acc, m, l) for k_seq_combine
+        float* part = a.part + ((int64_t)row * nsplit + split) * (D + 2);
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) part[c * 16 + col] = O[c][v];
+        if (col == 0) {
+          part[D] = lrow[v] > 0.f ? mrow[v] : -INFINITY;
+          part[D + 1] = lrow[v];
+        }
+        continue;
+      }
+      const bool has = lrow[v] > 0.f;
+      const float lse_seq = has ? mrow[v] + logf(lrow[v]) : -INFINITY;
+      const float lkg = a.lse_kg[row];
+      float lam;
+      if (lkg == -INFINITY) lam = 0.f;
+      else if (!has) lam = 1.f;
+      else lam = 1.f / (1.f + __expf(lse_seq - lkg));
+      const float inv = has ? 1.f / lrow[v] : 0.f;
+      const float* okg = a.o_kg + (int64_t)row * D;
+      const int64_t ob = q_off(a.os, b, tok, h);
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+        const int dim = c * 16 + col;
+        const float o = lam * okg[dim] + (1.f - lam) * (O[c][v] * inv);
+        if (a.out_dtype == kDtypeBF16) ((uint16_t*)a.out)[ob + dim] = f32_to_bf16_rne(o);
+        else ((float*)a.out)[ob + dim] = o;
+      }
+      if (a.lse_seq_out && col == 0) a.lse_seq_out[row] = lse_seq;
+    }
+  }
+}
+
 // Log-sum-exp combine of the key splits of one row (one wave per row), then
 // the λ merge with the KG half.
 template <class E, int D>
@@ -215,11 +416,15 @@ __global__ __launch_bounds__(256) void k_seq_combine(SeqArgs a, int nsplit) {
   } while (0)
 
 int seq_splits(int B, int N, int Hkv, int S) {
-  // enough workgroups to fill the chip (~8k); each split covers >= 128 keys
-  const int64_t items = (int64_t)B * N * Hkv;
+  const int64_t flash = N >= 16;
+  // workgroups before splitting: one per (b, n, KV head) for decode, one per
+  // (b, 16-token tile, KV head) for the flash prefill
+  const int64_t items = flash ? (int64_t)B * ((N + 15) / 16) * Hkv : (int64_t)B * N * Hkv;
   if (items <= 0 || S <= 0) return 1;
-  int64_t want = (8192 + items - 1) / items;
-  const int64_t maxs = (S + 127) / 128;
+  const int64_t target = flash ? 1024 : 8192;   // enough workgroups to fill the chip
+  const int64_t min_keys = flash ? 64 : 128;    // keys per split at least
+  int64_t want = (target + items - 1) / items;
+  const int64_t maxs = (S + min_keys - 1) / min_keys;
   if (want > maxs) want = maxs;
   return want < 1 ? 1 : (int)want;
 }
@@ -231,6 +436,18 @@ int seq_split_len(int S, int nsplit) {
 
 hipError_t launch_seq_merge(const SeqArgs& a, hipStream_t s) {
   if (a.r.R <= 0) return hipSuccess;
+  if (a.k && a.r.N >= 16) {
+    // prefill: MFMA flash attention per (b, KV head, 16-token tile [, key split])
+    const unsigned blocks = (unsigned)(a.r.B * ((a.r.N + 15) / 16) * a.Hkv);
+    const int waves = a.r.G < 4 ? a.r.G : 4;
+    const int nsplit = a.part ? a.nsplit : 1;
+    HIKVP_DISPATCH(a.dtype, a.d, k_seq_flash, dim3(blocks, (unsigned)nsplit), dim3(64 * waves), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nsplit <= 1) return e;
+    const unsigned cblocks = (unsigned)((a.r.R + 3) / 4);
+    HIKVP_DISPATCH(a.dtype, a.d, k_seq_combine, dim3(cblocks), dim3(256), 0, s, a, nsplit);
+    return hipGetLastError();
+  }
   const unsigned blocks = (unsigned)(a.r.B * a.r.N * a.Hkv);
   const int waves = a.r.G < 4 ? a.r.G : 4;
   const int nsplit = a.part ? a.nsplit : 1;
