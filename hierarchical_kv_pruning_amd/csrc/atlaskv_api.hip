@@ -128,7 +128,9 @@ struct Plan {
   double scale;
   int nsplit;
   size_t off_mid, off_leaf, off_sel[3], off_okg, off_lse, off_part, total;
-  size_t off_mid_base, off_bcnt, off_bslot, off_bhead, off_bnext, off_blist, off_bcount;
+  size_t off_mid_base, off_bcnt, off_bslot, off_bhead, off_bnext, off_blist, off_bcount, off_bovf, off_junk;
+  size_t off_rcnt, off_rtot, off_rrank, off_rbase, off_rtoff, off_rtkey, off_rnt, off_rmem;
+  int64_t root_tiles_max;
 };
 
 // Candidate capacity per row at the mid level (children of K_R distinct
@@ -204,8 +206,9 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   p.R = (int)(B * N * Hq);
   p.G = (int)(Hq / t.Hkv);
   for (int i = 0; i < 3; ++i) p.K[i] = Kpl[i];
-  if ((int64_t)p.R * p.K[1] >= kIndexLimit || (int64_t)t.Hkv * t.count[1] >= kIndexLimit)
-    return fail(ATLASKV_ERR_UNSUPPORTED, "B*N*Hq*K_I and Hkv*M_I must be below 2^31");
+  if ((int64_t)p.R * p.K[1] >= kIndexLimit || (int64_t)t.Hkv * t.count[1] >= kIndexLimit ||
+      (int64_t)p.R * (p.K[0] + kRootTile) >= kIndexLimit)
+    return fail(ATLASKV_ERR_UNSUPPORTED, "B*N*Hq*(K_R+16), B*N*Hq*K_I and Hkv*M_I must be below 2^31");
   candidate_capacity(v, p.K, &p.c1max, &p.c2max);
   if (p.c1max >= kIndexLimit || p.c2max >= kIndexLimit)
     return fail(ATLASKV_ERR_UNSUPPORTED, "candidates per row must be below 2^31");
@@ -218,12 +221,24 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   p.off_leaf = o;      o = align256(o + R * (size_t)p.c2max * 4);
   for (int i = 0; i < 3; ++i) { p.off_sel[i] = o; o = align256(o + R * (size_t)p.K[i] * 4); }
   p.off_mid_base = o;  o = align256(o + R * (size_t)p.K[1] * 4);
+  const size_t nroot = (size_t)t.Hkv * (size_t)t.count[0];
+  p.root_tiles_max = (int64_t)(R * (size_t)p.K[0] / kRootTile + nroot);
+  p.off_rcnt = o;      o = align256(o + nroot * kRootSub * 4);
+  p.off_rtot = o;      o = align256(o + nroot * 4);
+  p.off_rrank = o;     o = align256(o + R * (size_t)p.K[0] * 4);
+  p.off_rbase = o;     o = align256(o + R * (size_t)p.K[0] * 4);
+  p.off_rtoff = o;     o = align256(o + nroot * 4);
+  p.off_rtkey = o;     o = align256(o + (size_t)p.root_tiles_max * 4);
+  p.off_rnt = o;       o = align256(o + 4);
+  p.off_rmem = o;      o = align256(o + (size_t)p.root_tiles_max * kRootTile * 8);
   p.off_bcnt = o;      o = align256(o + (size_t)t.Hkv * (size_t)t.count[1] * 4);
   p.off_bslot = o;     o = align256(o + (size_t)t.Hkv * (size_t)t.count[1] * 8 * kBucketSlots);
   p.off_bhead = o;     o = align256(o + (size_t)t.Hkv * (size_t)t.count[1] * 4);
   p.off_bnext = o;     o = align256(o + R * (size_t)p.K[1] * 4);
   p.off_blist = o;     o = align256(o + R * (size_t)p.K[1] * 16);
-  p.off_bcount = o;    o = align256(o + 4);
+  p.off_bcount = o;    o = align256(o + 8);
+  p.off_bovf = o;      o = align256(o + (R * (size_t)p.K[1] / (kBucketSlots + 1) + 1) * 4);
+  p.off_junk = o;      o = align256(o + (size_t)kJunkSlots * 64);
   p.off_okg = o;       o = align256(o + R * (size_t)t.d * 4);
   p.off_lse = o;       o = align256(o + R * 4);
   p.nsplit = seq_splits(p.B, p.N, t.Hkv, p.S);
@@ -425,19 +440,32 @@ atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vie
   a.mid_scores = (float*)(ws + p.off_mid);
   a.leaf_scores = (float*)(ws + p.off_leaf);
   a.mid_base = (int32_t*)(ws + p.off_mid_base);
+  a.root_cnt = (int32_t*)(ws + p.off_rcnt);
+  a.root_tot = (int32_t*)(ws + p.off_rtot);
+  a.root_rank = (int32_t*)(ws + p.off_rrank);
+  a.root_base = (int32_t*)(ws + p.off_rbase);
+  a.root_tile_off = (int32_t*)(ws + p.off_rtoff);
+  a.root_tile_key = (int32_t*)(ws + p.off_rtkey);
+  a.root_ntiles = (int32_t*)(ws + p.off_rnt);
+  a.root_members = (int2*)(ws + p.off_rmem);
+  a.root_tiles_max = p.root_tiles_max;
   a.bucket_cnt = (int32_t*)(ws + p.off_bcnt);
   a.bucket_slot = (int2*)(ws + p.off_bslot);
   a.bucket_head = (int32_t*)(ws + p.off_bhead);
   a.bucket_next = (int32_t*)(ws + p.off_bnext);
   a.bucket_desc = (int4*)(ws + p.off_blist);
   a.bucket_count = (int32_t*)(ws + p.off_bcount);
+  a.bucket_ovf = (int32_t*)(ws + p.off_bovf);
+  a.junk = (float*)(ws + p.off_junk);
   a.o_kg = o_kg;
   a.lse_kg = lse_kg;
   // 速读 › 怎么做的: roots -> Top-K -> their children -> Top-K -> leaves -> Top-K
-  e = mark(launch_root(a, s));
+  e = launch_clear(a, s);
+  if (e == hipSuccess) e = launch_root(a, s);
+  if (e == hipSuccess) e = mark(launch_root_groups(a, s));
   if (e == hipSuccess) e = mark(launch_mid_gemm(a, s));
   if (e == hipSuccess) e = mark(launch_mid_select(a, s));
-  if (e == hipSuccess) e = launch_leaf_buckets(a, s);
+  if (e == hipSuccess) e = launch_leaf_link(a, s);
   if (e == hipSuccess) e = mark(launch_leaf_score(a, s));
   if (e == hipSuccess) e = mark(launch_leaf_select(a, s));
   if (e == hipSuccess) {

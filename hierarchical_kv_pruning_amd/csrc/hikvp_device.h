@@ -208,6 +208,43 @@ __device__ inline float4_t tile_dot(const uint4* a, const uint4* b) {
   return acc;
 }
 
+// Half-split 16x16 tiles for streaming many rows: tile row (or column) i is
+// item i&7 over half i>>3 of the head dimension.  Lane l holds item l&7 and,
+// of that item's RB-byte row, the 16-byte pieces m*128 + ((l>>3)&1)*64 +
+// (l>>4)*16 for m < RB/128, so one load instruction covers eight whole
+// 128-byte lines (a 16-items-per-instruction layout touches sixteen half
+// lines and streams about a quarter slower).  Of the 16x16 product only the
+// two diagonal 8x8 blocks pair equal halves; their sum is the full dot
+// product of each item pair.
+__device__ inline int split_off(int lane, int m) {
+  return m * 128 + ((lane >> 3) & 1) * 64 + (lane >> 4) * 16;
+}
+
+// Four consecutive floats to a 4-byte aligned address (one 16-byte store;
+// the target permits dword-aligned vector accesses to global memory).
+struct __attribute__((packed, aligned(4))) Float4U { float x, y, z, w; };
+
+// 16-byte load marked non-temporal: data streamed once (leaf keys) then does
+// not displace reused lines such as freshly written scores.
+typedef unsigned int U32x4 __attribute__((ext_vector_type(4)));
+__device__ inline uint4 load_nt(const void* p) {
+  const U32x4 v = __builtin_nontemporal_load((const U32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline void store4u(float* p, float x, float y, float z, float w) {
+  *(Float4U*)p = Float4U{x, y, z, w};
+}
+
+// Sum the two half blocks of a half-split tile.  Lanes with (l&15) < 8 and
+// l < 32 then hold dot(row item 4*(l>>4)+v, column item l&7) in element v;
+// other lanes hold garbage.
+__device__ inline float4_t split_combine(float4_t acc, int lane) {
+  float4_t s;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) s[v] = acc[v] + __shfl(acc[v], (lane + 40) & 63);
+  return s;
+}
+
 // ---------------------------------------------------------------------------
 // Score a run of candidate keys: out[c] = <q, key[first + c]> (fp32, unscaled)
 // for c < len.  LPK lanes read one key row as 16-byte pieces, so a wave load

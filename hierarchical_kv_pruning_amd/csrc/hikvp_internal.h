@@ -8,7 +8,10 @@ namespace hikvp {
 
 constexpr int kMaxK = 256;        // largest Top-K per level
 constexpr int kMaxD = 128;        // largest head dim
-constexpr int kBucketSlots = 16;  // members of a (head, mid) bucket stored without a list walk
+constexpr int kBucketSlots = 32;  // members of a (head, mid) bucket stored without a list walk
+constexpr int kJunkSlots = 1024;  // per-wave sinks for masked-off score stores
+constexpr int kRootTile = 16;     // member rows per mid-GEMM work item
+constexpr int kRootSub = 16;      // counters per (head, root) group, picked by token
 constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBF16 = 1;
 
@@ -45,12 +48,25 @@ struct StepArgs {
   float* leaf_scores;         // [R, c2max] unscaled fp32 leaf scores, candidate order
   int32_t* sel[3];            // [R, K[i]] selected node indices, candidate order, -1 padded
   int32_t* mid_base;          // [R, K[1]] first leaf-candidate slot of each selected mid
+  // rows grouped by selected (head, root), each group padded to kRootTile rows
+  int32_t* root_cnt;          // [kRootSub, Hkv * M_R] rows per sub-counter; the scan turns
+                              // them into each sub-counter's first rank in the group
+  int32_t* root_tot;          // [Hkv * M_R] rows that selected the (head, root)
+  int32_t* root_rank;         // [R, K[0]] rank of the selection within its group
+  int32_t* root_base;         // [R, K[0]] first mid-candidate slot of each selected root
+  int32_t* root_tile_off;     // [Hkv * M_R] first work item (tile) of each group
+  int32_t* root_tile_key;     // [root_tiles_max] group (key g*M_R + root) of each tile
+  int32_t* root_ntiles;       // [1] tiles in use
+  int2* root_members;         // [root_tiles_max * kRootTile] (row, first mid slot)
+  int64_t root_tiles_max;     // R*K[0]/kRootTile + Hkv*M_R
   int32_t* bucket_cnt;        // [Hkv * M_I] rows that selected the (head, mid)
   int2* bucket_slot;          // [Hkv * M_I * kBucketSlots] first members: (row, first leaf slot)
   int32_t* bucket_head;       // [Hkv * M_I] overflow members: list head, -1 none
   int32_t* bucket_next;       // [R * K[1]] next overflow entry of the same (head, mid)
   int4* bucket_desc;          // [R * K[1]] distinct (head, mid): key g*M_I+mid, fanout, first leaf element (lo, hi)
-  int32_t* bucket_count;      // [1] number of distinct keys
+  int32_t* bucket_count;      // [2] distinct keys, keys with more than kBucketSlots rows
+  float* junk;                // [kJunkSlots * 16] write-only sinks for masked-off score lanes
+  int32_t* bucket_ovf;        // [R * K[1] / (kBucketSlots + 1) + 1] keys with overflow members
   float* o_kg;                // [R, d] softmax-weighted leaf values (fp32)
   float* lse_kg;              // [R] log-sum-exp of the selected leaf logits
 };
@@ -83,10 +99,12 @@ hipError_t launch_validate(const int64_t* off, int64_t count, int64_t children, 
                            BuildStats* stats, hipStream_t s);
 hipError_t launch_key_norms(const void* key, int dtype, int d, int Hkv, int64_t rows,
                             int64_t hs, int64_t rs, unsigned int* out_bits, hipStream_t s);
+hipError_t launch_clear(const StepArgs& a, hipStream_t s);        // bucket counters of both levels
 hipError_t launch_root(const StepArgs& a, hipStream_t s);
+hipError_t launch_root_groups(const StepArgs& a, hipStream_t s);  // rows by selected (head, root)
 hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s);
 hipError_t launch_mid_select(const StepArgs& a, hipStream_t s);
-hipError_t launch_leaf_buckets(const StepArgs& a, hipStream_t s);  // link rows by selected (head, mid)
+hipError_t launch_leaf_link(const StepArgs& a, hipStream_t s);    // rows by selected (head, mid)
 hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s);   // grouped buckets + overflow members
 hipError_t launch_leaf_select(const StepArgs& a, hipStream_t s);
 hipError_t launch_seq_merge(const SeqArgs& a, hipStream_t s);

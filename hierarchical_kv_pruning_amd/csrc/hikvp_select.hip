@@ -6,19 +6,21 @@
 // branches and keep the Top-K, and so on down to the leaves; the selected
 // leaves' softmax then forms the KG half of the merged output.
 //
+//   k_clear     zeroes the bucket counters of both levels.
 //   k_root      one wave per row: scores of all M_R root keys of the row's KV
-//               head (coalesced 16-byte lanes), exact-boundary Top-K_R.  The
-//               per-row select kernels keep a few KB of LDS per wave so many
-//               rows are in flight per CU.
-//   k_mid_gemm  one workgroup per (root j, KV head g): every row of head g that
-//               selected root j is gathered (in row order) and scored against
-//               j's child span with bf16 (or fp32) MFMA 16x16 tiles; the span
-//               is read once per bucket instead of once per row.  Scores land
-//               in each row's candidate slots of the workspace.
+//               head (coalesced 16-byte lanes), exact-boundary Top-K_R; each
+//               selection takes a rank in its (KV head, root) group and
+//               records where the root's children start in the row's mid
+//               candidate list.  The per-row select kernels keep a few KB of
+//               LDS per wave so many rows are in flight per CU.
+//   k_root_scan / k_root_fill  lay the groups out in tiles of 16 rows.
+//   k_mid_gemm  one wave per tile: the tile's rows against the root's child
+//               span on bf16 (or fp32) MFMA 16x16 tiles; the span is read once
+//               per tile instead of once per row.  Scores land in each row's
+//               candidate slots of the workspace.
 //   k_mid_select   one wave per row (a workgroup per row for long candidate
 //               lists): Top-K_I over the row's mid scores.
-//   k_bucket_clear / k_bucket_link  link the rows that selected each distinct
-//               (KV head, mid) into one list per bucket.
+//   k_bucket_link  link the rows that selected each distinct (KV head, mid).
 //   k_leaf_score   one wave per bucket: streams the mid's leaf span once (it is
 //               contiguous in the head-major layout) and writes the scores of
 //               every member row into that row's candidate slots.
@@ -122,33 +124,123 @@ __global__ __launch_bounds__(256) void k_root(StepArgs a, size_t wave_bytes, int
                                       lane);
   int32_t* out = a.sel[0] + (int64_t)row * K;
   for (int i = lane; i < K; i += 64) out[i] = i < k ? W.out_node[i] : -1;
+  // group the row under each selected (head, root): rank in the group and the
+  // first mid-candidate slot of the root's children (children of the selected
+  // roots, in selection order, form the row's mid candidate list)
+  const int64_t* off0 = a.t.off[0];
+  int carry = 0;
+  for (int i0 = 0; i0 < K; i0 += 64) {
+    const int i = i0 + lane;
+    const int node = i < k ? W.out_node[i] : -1;
+    const int fan = node >= 0 ? (int)(off0[node + 1] - off0[node]) : 0;
+    int incl = fan;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (i < K) {
+      // rank within the row's sub-counter (by token) of the group: spreading a
+      // group over kRootSub counters keeps the atomics on one address few
+      const int sub = (row / a.r.Hq) % kRootSub;
+      a.root_rank[(int64_t)row * K + i] =
+          node >= 0 ? atomicAdd(&a.root_cnt[(int64_t)sub * a.t.Hkv * MR + g * MR + node], 1) : -1;
+      a.root_base[(int64_t)row * K + i] = carry + incl - fan;
+    }
+    carry += __shfl(incl, 63);
+  }
+}
+
+// Exclusive scan of the (head, root) group sizes in tiles of kRootTile rows:
+// first tile of each group and the group of each tile.  One workgroup.
+__global__ __launch_bounds__(1024) void k_root_scan(StepArgs a) {
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nkeys = a.t.Hkv * (int)a.t.count[0];
+  int carry = 0;
+  for (int k0 = 0; k0 < nkeys; k0 += 1024) {
+    const int key = k0 + tid;
+    int tot = 0;
+    if (key < nkeys) {
+      for (int sb = 0; sb < kRootSub; ++sb) {  // sub-counts -> first rank of each sub-counter
+        const int c = a.root_cnt[(int64_t)sb * nkeys + key];
+        a.root_cnt[(int64_t)sb * nkeys + key] = tot;
+        tot += c;
+      }
+      a.root_tot[key] = tot;
+    }
+    const int pc = (tot + kRootTile - 1) / kRootTile;
+    int incl = pc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int woff = 0, total = 0;
+    for (int w = 0; w < 16; ++w) {
+      woff += w < wave ? wsum[w] : 0;
+      total += wsum[w];
+    }
+    const int first = carry + woff + incl - pc;
+    if (key < nkeys) {
+      a.root_tile_off[key] = first;
+      for (int i = 0; i < pc; ++i) a.root_tile_key[first + i] = key;
+    }
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) *a.root_ntiles = carry;
+}
+
+// Place every (row, selected root) at its group's tile rows.
+__global__ void k_root_fill(StepArgs a) {
+  const int K0 = a.K[0];
+  const int MR = (int)a.t.count[0];
+  const int64_t n = (int64_t)a.r.R * K0;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int node = a.sel[0][e];
+    if (node < 0) continue;
+    const int row = (int)(e / K0);
+    const int key = ((row % a.r.Hq) / a.r.G) * MR + node;
+    const int sub = (row / a.r.Hq) % kRootSub;
+    const int64_t nkeys = (int64_t)a.t.Hkv * MR;
+    const int64_t pos = (int64_t)a.root_tile_off[key] * kRootTile + a.root_cnt[sub * nkeys + key] + a.root_rank[e];
+    a.root_members[pos] = make_int2(row, a.root_base[e]);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// mid level: bucket GEMM on MFMA
+// mid level: one wave per tile of kRootTile rows of a (head, root) group.  The
+// rows are the M side and the root's children the N side of 16x16 MFMA tiles,
+// so the child span is read once per tile (from L2 after the group's first).
 // ---------------------------------------------------------------------------
-constexpr int kMemCap = 512;  // bucket members staged per GEMM round
-
-struct MidSmem {
-  int mem_row[kMemCap];
-  int mem_base[kMemCap];
-  int wave_cnt[4];
-};
-
 template <class E, int D>
-__device__ void mid_bucket_tiles(const StepArgs& a, const MidSmem& M, int cnt, int g,
-                                 int64_t first, int F, int wave, int nwave, int lane) {
+__global__ __launch_bounds__(256) void k_mid_gemm(StepArgs a) {
   constexpr int KCH = D * E::kBytes / 64;  // 16-byte pieces per lane per row
+  constexpr int TU = 4;                    // child tiles per round = consecutive children per lane
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
   const int quad = lane >> 4, col = lane & 15;
-  int64_t rsb;
-  const char* kb = key_base(a.t, 1, g, rsb, E::kBytes);
-  const int n_mt = (cnt + 15) >> 4, n_nt = (F + 15) >> 4;
-  for (int mt = wave; mt < n_mt; mt += nwave) {
+  float* const junk = a.junk + ((blockIdx.x * nwave + wave) % kJunkSlots) * 16;
+  const int ntiles = *a.root_ntiles;
+  const int MR = (int)a.t.count[0];
+  const int64_t* off0 = a.t.off[0];
+  for (int t = blockIdx.x * nwave + wave; t < ntiles; t += gridDim.x * nwave) {
+    const int key = a.root_tile_key[t];
+    const int toff = a.root_tile_off[key];
+    const int cnt = a.root_tot[key];
+    const int g = key / MR, j = key % MR;
+    const int64_t first = off0[j];
+    const int F = (int)(off0[j + 1] - first);
+    const int m0 = (t - toff) * kRootTile;     // first member of the tile
+    const int mi = m0 + col;
+    const int2 mem = mi < cnt ? a.root_members[(int64_t)toff * kRootTile + mi] : make_int2(-1, 0);
     uint4 afr[KCH];
-    const int ia = mt * 16 + col;
-    if (ia < cnt) {
+    if (mi < cnt) {
       int b, n, h;
-      decode_row(a.r, M.mem_row[ia], b, n, h);
+      decode_row(a.r, mem.x, b, n, h);
       const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes;
 #pragma unroll
       for (int m = 0; m < KCH; ++m) afr[m] = *(const uint4*)(qp + m * 64 + quad * 16);
@@ -156,77 +248,61 @@ __device__ void mid_bucket_tiles(const StepArgs& a, const MidSmem& M, int cnt, i
 #pragma unroll
       for (int m = 0; m < KCH; ++m) afr[m] = make_uint4(0, 0, 0, 0);
     }
-    for (int nt = 0; nt < n_nt; ++nt) {
-      uint4 bfr[KCH];
-      const int cb = nt * 16 + col;
-      if (cb < F) {
-        const char* kp = kb + (first + cb) * rsb;
+    // Rounds of TU child tiles; in tile u of a round, column col is child
+    // c0 + col*TU + u, so a lane ends the round with TU consecutive scores of
+    // each of its 4 rows (tile rows 4*quad + v), written with one 16-byte
+    // store.  Loads and stores are unconditional (clamped child, junk slot)
+    // and a round's stores follow the next round's loads, so the wait for the
+    // loads never covers the stores.
+    float* dst[4];
 #pragma unroll
-        for (int m = 0; m < KCH; ++m) bfr[m] = *(const uint4*)(kp + m * 64 + quad * 16);
-      } else {
+    for (int v = 0; v < 4; ++v) {
+      const int ms = 4 * quad + v;
+      const int srow = __shfl(mem.x, ms), sbase = __shfl(mem.y, ms);
+      dst[v] = m0 + ms < cnt ? a.mid_scores + (int64_t)srow * a.c1max + sbase + col * TU : nullptr;
+    }
+    int64_t rsb;
+    const char* kb = key_base(a.t, 1, g, rsb, E::kBytes) + first * rsb + quad * 16;
+    float4_t prev[TU];
 #pragma unroll
-        for (int m = 0; m < KCH; ++m) bfr[m] = make_uint4(0, 0, 0, 0);
-      }
-      const float4_t acc = tile_dot<E, KCH>(afr, bfr);
-      // lane holds tile rows 4*quad .. 4*quad+3 of column col
+    for (int u = 0; u < TU; ++u) prev[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+    int pc0 = -1;
+    auto load_round = [&](int c0, uint4 (&bfr)[TU][KCH]) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int i = mt * 16 + quad * 4 + v;
-        if (i < cnt && cb < F)
-          a.mid_scores[(int64_t)M.mem_row[i] * a.c1max + M.mem_base[i] + cb] = acc[v];
+      for (int u = 0; u < TU; ++u) {
+        const char* kp = kb + (int64_t)min(c0 + col * TU + u, F - 1) * rsb;
+#pragma unroll
+        for (int m = 0; m < KCH; ++m) bfr[u][m] = *(const uint4*)(kp + m * 64);
       }
+    };
+    auto store_full = [&]() {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        store4u((pc0 >= 0 && dst[v]) ? dst[v] + pc0 : junk, prev[0][v], prev[1][v], prev[2][v], prev[3][v]);
+    };
+    int c0 = 0;
+    for (; c0 + 16 * TU <= F; c0 += 16 * TU) {
+      uint4 bfr[TU][KCH];
+      load_round(c0, bfr);
+      store_full();
+#pragma unroll
+      for (int u = 0; u < TU; ++u) prev[u] = tile_dot<E, KCH>(afr, bfr[u]);
+      pc0 = c0;
     }
-  }
-}
-
-template <class E, int D>
-__global__ __launch_bounds__(256) void k_mid_gemm(StepArgs a) {
-  __shared__ MidSmem M;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwave = blockDim.x >> 6;
-  const int j = blockIdx.x, g = blockIdx.y;
-  const int64_t* off0 = a.t.off[0];
-  const int64_t first = off0[j];
-  const int F = (int)(off0[j + 1] - first);
-  const int K0 = a.K[0];
-  if (F == 0 || K0 == 0) return;
-  const int G = a.r.G;
-  const int Rg = a.r.B * a.r.N * G;
-  const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
-  int cnt = 0;
-  for (int t0 = 0; t0 < Rg; t0 += blockDim.x) {
-    const int t = t0 + tid;
-    bool member = false;
-    int r = 0, base = 0;
-    if (t < Rg) {
-      r = (t / G) * a.r.Hq + g * G + (t % G);
-      const int32_t* sr = a.sel[0] + (int64_t)r * K0;
-      int acc = 0;
-      for (int k = 0; k < K0; ++k) {
-        const int p = sr[k];
-        if (p == j) { member = true; base = acc; break; }
-        if (p >= 0) acc += (int)(off0[p + 1] - off0[p]);
-      }
-    }
-    // members in row order: wave ballots + per-wave offsets
-    const unsigned long long bal = __ballot(member);
-    if (lane == 0) M.wave_cnt[wave] = __popcll(bal);
-    __syncthreads();
-    int woff = 0, total = 0;
-    for (int w = 0; w < nwave; ++w) {
-      if (w < wave) woff += M.wave_cnt[w];
-      total += M.wave_cnt[w];
-    }
-    if (member) {
-      const int at = cnt + woff + __popcll(bal & below);
-      M.mem_row[at] = r;
-      M.mem_base[at] = base;
-    }
-    cnt += total;
-    __syncthreads();
-    if (cnt > kMemCap - (int)blockDim.x || t0 + (int)blockDim.x >= Rg) {
-      if (cnt > 0) mid_bucket_tiles<E, D>(a, M, cnt, g, first, F, wave, nwave, lane);
-      cnt = 0;
-      __syncthreads();
+    if (c0 < F) {  // last, partial round
+      uint4 bfr[TU][KCH];
+      load_round(c0, bfr);
+      store_full();
+#pragma unroll
+      for (int u = 0; u < TU; ++u) prev[u] = tile_dot<E, KCH>(afr, bfr[u]);
+      const int cl = c0 + col * TU;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int u = 0; u < TU; ++u)
+          if (dst[v] && cl + u < F) dst[v][c0 + u] = prev[u][v];
+    } else {
+      store_full();
     }
   }
 }
@@ -345,39 +421,57 @@ __global__ __launch_bounds__(256) void k_mid_select_mem(StepArgs a, size_t gb) {
 // Each member's dot products are computed independently, so results do not
 // depend on the (atomic) member or bucket order.
 // ---------------------------------------------------------------------------
-__global__ void k_bucket_clear(StepArgs a, int64_t nkeys) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nkeys;
-       i += (int64_t)gridDim.x * blockDim.x) {
+__global__ void k_clear(StepArgs a, int64_t nkeys1, int64_t nkeys0) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nkeys1; i += stride) {
     a.bucket_cnt[i] = 0;
     a.bucket_head[i] = -1;
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.bucket_count = 0;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nkeys0 * kRootSub; i += stride)
+    a.root_cnt[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x < 2) a.bucket_count[threadIdx.x] = 0;
 }
 
+// Grid-stride over the (row, mid) selections in wave-uniform steps so that a
+// wave appends its new descriptors with one atomic.
 __global__ void k_bucket_link(StepArgs a) {
   const int K1 = a.K[1];
   const int64_t n = (int64_t)a.r.R * K1;
   const int MI = (int)a.t.count[1];
   const int64_t* off1 = a.t.off[1];
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int mid = a.sel[1][e];
-    if (mid < 0) continue;
-    const int row = (int)(e / K1);
-    const int g = (row % a.r.Hq) / a.r.G;
-    const int64_t key = (int64_t)g * MI + mid;
-    const int rank = atomicAdd(&a.bucket_cnt[key], 1);
-    if (rank == 0) {
-      const int64_t f0 = off1[mid];
-      const int64_t first = (int64_t)g * a.t.hs[2] + f0 * a.t.rs[2];
-      const int v = atomicAdd(a.bucket_count, 1);
-      a.bucket_desc[v] = make_int4((int)key, (int)(off1[mid + 1] - f0), (int)(uint32_t)first,
-                                   (int)(first >> 32));
+  const int lane = threadIdx.x & 63;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e0 = blockIdx.x * (int64_t)blockDim.x + (threadIdx.x & ~63); e0 < n; e0 += stride) {
+    const int64_t e = e0 + lane;
+    const int mid = e < n ? a.sel[1][e] : -1;
+    int rank = -1, row = 0;
+    int64_t key = 0;
+    if (mid >= 0) {
+      row = (int)(e / K1);
+      const int g = (row % a.r.Hq) / a.r.G;
+      key = (int64_t)g * MI + mid;
+      rank = atomicAdd(&a.bucket_cnt[key], 1);
     }
+    const uint64_t fresh = __ballot(rank == 0);
+    if (fresh) {
+      int base = 0;
+      const int leader = __builtin_ctzll(fresh);
+      if (lane == leader) base = atomicAdd(&a.bucket_count[0], __popcll(fresh));
+      base = __shfl(base, leader);
+      if (rank == 0) {
+        const int below = __popcll(fresh & ((1ull << lane) - 1ull));
+        const int64_t f0 = off1[mid];
+        const int64_t first = (int64_t)(key / MI) * a.t.hs[2] + f0 * a.t.rs[2];
+        a.bucket_desc[base + below] = make_int4((int)key, (int)(off1[mid + 1] - f0), (int)(uint32_t)first,
+                                                (int)(first >> 32));
+      }
+    }
+    if (rank < 0) continue;
     if (rank < kBucketSlots) {
       a.bucket_slot[key * kBucketSlots + rank] = make_int2(row, a.mid_base[e]);
     } else {
       a.bucket_next[e] = atomicExch(&a.bucket_head[key], (int)e);
+      if (rank == kBucketSlots) a.bucket_ovf[atomicAdd(&a.bucket_count[1], 1)] = (int)key;
     }
   }
 }
@@ -422,16 +516,23 @@ __device__ inline void load_q_chunk(const StepArgs& a, int row, int j, float* qf
   unpack<E>(*(const uint4*)(qp + j * 16), qf);
 }
 
-// One wave per bucket: the member rows (up to 16) are the M side and the
-// span's keys the N side of 16x16 MFMA tiles, so each 16-key tile costs four
-// 16-byte loads per lane, 8 MFMAs and one 64-byte store per member.
+// One wave per bucket on half-split MFMA tiles: a group of up to 8 member rows
+// is the M side and the span's keys the N side.  A round covers 8*TU keys; in
+// its tile u, item i is key t0 + i*TU + u, so every load instruction reads
+// eight whole 128-byte lines and each lane ends the round holding TU
+// consecutive scores per member, written with one 16-byte store.  A bucket
+// with more than 8 members makes a second pass over its span (mostly L2 hits).
 template <class E, int D>
 __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
-  constexpr int KCH = D * E::kBytes / 64;  // 16-byte pieces per lane per row
-  constexpr int TU = 2;                    // key tiles in flight per wave
+  constexpr int RB = D * E::kBytes;        // bytes per key row
+  constexpr int KP = RB / 128;             // 16-byte pieces per lane per tile
+  constexpr int TU = 4;                    // tiles per round = consecutive keys per lane
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
-  const int quad = lane >> 4, col = lane & 15;
-  const int nb = *a.bucket_count;
+  const int quad = lane >> 4, item = lane & 7;
+  const bool owner = lane < 32 && (lane & 15) < 8;   // holds combined scores
+  float* const junk = a.junk + ((blockIdx.x * nwave + wave) % kJunkSlots) * 16;
+  static_assert(TU % 4 == 0 && TU <= 16, "junk slot holds 16 floats");
+  const int nb = a.bucket_count[0];
   const char* kbase = (const char*)a.t.key[2];
   const int64_t rsb = a.t.rs[2] * E::kBytes;
   const int stride = gridDim.x * nwave;
@@ -442,48 +543,84 @@ __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
     const int4 nxt = vn < nb ? a.bucket_desc[vn] : make_int4(0, 0, 0, 0);  // prefetch
     const int key = cur.x, F = cur.y;
     const int64_t first = (int64_t)(uint32_t)cur.z | ((int64_t)cur.w << 32);
-    const char* kb = kbase + first * E::kBytes;
+    const char* kp = (const char*)kbase + first * E::kBytes + split_off(lane, 0);  // + key * rsb
     int cnt = a.bucket_cnt[key];
     cnt = cnt < kBucketSlots ? cnt : kBucketSlots;
-    // tile row `col` = member col: its query pieces (zeros past the members)
-    int2 mem = make_int2(-1, 0);
-    uint4 afr[KCH];
-    if (col < cnt) {
-      mem = a.bucket_slot[(int64_t)key * kBucketSlots + col];
-      int b, n, h;
-      decode_row(a.r, mem.x, b, n, h);
-      const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes;
+    const int2 mem = lane < kBucketSlots ? a.bucket_slot[(int64_t)key * kBucketSlots + lane] : make_int2(-1, 0);
+    for (int g = 0; g * 8 < cnt; ++g) {
+      // A fragment: member g*8 + item, zeros past the members
+      uint4 afr[KP];
+      const int mi = g * 8 + item;
+      const int row = __shfl(mem.x, mi);
+      if (mi < cnt) {
+        int b, n, h;
+        decode_row(a.r, row, b, n, h);
+        const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes + split_off(lane, 0);
 #pragma unroll
-      for (int m = 0; m < KCH; ++m) afr[m] = *(const uint4*)(qp + m * 64 + quad * 16);
-    } else {
+        for (int m = 0; m < KP; ++m) afr[m] = *(const uint4*)(qp + m * 128);
+      } else {
 #pragma unroll
-      for (int m = 0; m < KCH; ++m) afr[m] = make_uint4(0, 0, 0, 0);
-    }
-    // the 4 members whose scores this lane stores: tile rows 4*quad .. 4*quad+3
-    int srow[4], sbase[4];
-#pragma unroll
-    for (int vv = 0; vv < 4; ++vv) {
-      srow[vv] = __shfl(mem.x, 4 * quad + vv);
-      sbase[vv] = __shfl(mem.y, 4 * quad + vv);
-    }
-    for (int t0 = 0; t0 < F; t0 += 16 * TU) {
-      uint4 bfr[TU][KCH];
-#pragma unroll
-      for (int u = 0; u < TU; ++u) {
-        const int c = t0 + u * 16 + col;
-#pragma unroll
-        for (int m = 0; m < KCH; ++m)
-          bfr[u][m] = c < F ? *(const uint4*)(kb + c * rsb + m * 64 + quad * 16) : make_uint4(0, 0, 0, 0);
+        for (int m = 0; m < KP; ++m) afr[m] = make_uint4(0, 0, 0, 0);
       }
+      // owners store members g*8 + 4*quad + vv, keys t0 + item*TU .. + TU-1
+      float* dst[4];
 #pragma unroll
-      for (int u = 0; u < TU; ++u) {
-        const int c = t0 + u * 16 + col;
-        const float4_t acc = tile_dot<E, KCH>(afr, bfr[u]);
+      for (int vv = 0; vv < 4; ++vv) {
+        const int ms = g * 8 + 4 * (quad & 1) + vv;
+        const int srow = __shfl(mem.x, ms), sbase = __shfl(mem.y, ms);
+        dst[vv] = (owner && ms < cnt) ? a.leaf_scores + (int64_t)srow * a.c2max + sbase + item * TU : nullptr;
+      }
+      // Each round issues its loads, then writes the previous round's scores,
+      // then waits for the loads.  The memory counter completes in issue
+      // order, stores included, so every round issues the same four 16-byte
+      // stores (lanes with nothing to write aim at this wave's junk slot) and
+      // a fixed number of loads (keys past the span re-read its last row):
+      // the wait for a round's loads then never covers the stores after them.
+      float4_t prev[TU];
+#pragma unroll
+      for (int u = 0; u < TU; ++u) prev[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+      int pt0 = -1;                        // round held in prev, -1 none
+      auto load_round = [&](int t0, uint4 (&bfr)[TU][KP]) {
+#pragma unroll
+        for (int u = 0; u < TU; ++u) {
+          const int c = min(t0 + item * TU + u, F - 1);
+          const char* p = kp + (int64_t)c * rsb;
+#pragma unroll
+          for (int m = 0; m < KP; ++m) bfr[u][m] = load_nt(p + m * 128);
+        }
+      };
+      auto store_full = [&]() {            // prev holds a full round (or none)
 #pragma unroll
         for (int vv = 0; vv < 4; ++vv) {
-          if (4 * quad + vv < cnt && c < F)
-            a.leaf_scores[(int64_t)srow[vv] * a.c2max + sbase[vv] + c] = acc[vv];
+          float* d = (pt0 >= 0 && dst[vv]) ? dst[vv] + pt0 : junk;
+#pragma unroll
+          for (int u = 0; u < TU; u += 4)
+            store4u(d + u, prev[u][vv], prev[u + 1][vv], prev[u + 2][vv], prev[u + 3][vv]);
         }
+      };
+      int t0 = 0;
+      for (; t0 + 8 * TU <= F; t0 += 8 * TU) {
+        uint4 bfr[TU][KP];
+        load_round(t0, bfr);
+        store_full();
+#pragma unroll
+        for (int u = 0; u < TU; ++u) prev[u] = split_combine(tile_dot<E, KP>(afr, bfr[u]), lane);
+        pt0 = t0;
+      }
+      if (t0 < F) {  // last, partial round
+        uint4 bfr[TU][KP];
+        load_round(t0, bfr);
+        store_full();
+#pragma unroll
+        for (int u = 0; u < TU; ++u) prev[u] = split_combine(tile_dot<E, KP>(afr, bfr[u]), lane);
+        const int c0 = t0 + item * TU;
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv)
+#pragma unroll
+          for (int u = 0; u < TU; ++u)
+            if (dst[vv] && c0 + u < F) dst[vv][t0 + u] = prev[u][vv];
+      } else {
+        store_full();
       }
     }
     cur = nxt;
@@ -491,22 +628,24 @@ __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
   }
 }
 
-// Members of buckets with more than kBucketSlots rows: one wave per bucket
-// walks the overflow list, two rows per pass over the span.
+// Members of buckets with more than kBucketSlots rows: one wave per listed
+// bucket walks its overflow list, two rows per pass over the span.
 template <class E, int D>
 __global__ __launch_bounds__(256) void k_leaf_score_overflow(StepArgs a) {
   constexpr int EPV = E::kEPV, LPK = D / EPV, MB = 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
   const int j = lane % LPK;
-  const int nb = *a.bucket_count;
+  const int nov = a.bucket_count[1];
   const int K1 = a.K[1];
+  const int MI = (int)a.t.count[1];
   const char* kbase = (const char*)a.t.key[2];
-  for (int v = blockIdx.x * nwave + wave; v < nb; v += gridDim.x * nwave) {
-    const int4 d = a.bucket_desc[v];
-    if (a.bucket_cnt[d.x] <= kBucketSlots) continue;
-    const int64_t first = (int64_t)(uint32_t)d.z | ((int64_t)d.w << 32);
-    const char* kb = kbase + first * E::kBytes;
-    int e = a.bucket_head[d.x];
+  for (int v = blockIdx.x * nwave + wave; v < nov; v += gridDim.x * nwave) {
+    const int key = a.bucket_ovf[v];
+    const int g = key / MI, mid = key % MI;
+    const int64_t f0 = a.t.off[1][mid];
+    const int F = (int)(a.t.off[1][mid + 1] - f0);
+    const char* kb = kbase + ((int64_t)g * a.t.hs[2] + f0 * a.t.rs[2]) * E::kBytes;
+    int e = a.bucket_head[key];
     while (e != -1) {  // wave-uniform walk
       int rows[MB], bases[MB];
       float qf[MB][EPV];
@@ -525,7 +664,7 @@ __global__ __launch_bounds__(256) void k_leaf_score_overflow(StepArgs a) {
           ++m;
         }
       }
-      score_members<E, D, MB>(a, kb, d.y, m, rows, bases, qf, lane);
+      score_members<E, D, MB>(a, kb, F, m, rows, bases, qf, lane);
     }
   }
 }
@@ -655,13 +794,24 @@ hipError_t launch_root(const StepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s) {
-  if (a.r.R <= 0 || a.t.count[0] <= 0 || a.K[0] <= 0) return hipSuccess;
-  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_mid_gemm, dim3((unsigned)a.t.count[0], (unsigned)a.t.Hkv), dim3(256),
-                 0, s, a);
+hipError_t launch_root_groups(const StepArgs& a, hipStream_t s) {
+  if (a.r.R <= 0 || a.K[0] <= 0 || a.t.count[0] <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_root_scan, dim3(1), dim3(1024), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int64_t blocks = ((int64_t)a.r.R * a.K[0] + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_root_fill, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
+hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s) {
+  if (a.r.R <= 0 || a.t.count[0] <= 0 || a.K[0] <= 0) return hipSuccess;
+  int64_t blocks = (a.root_tiles_max + 3) / 4;
+  if (blocks > 4096) blocks = 4096;
+  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_mid_gemm, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_mid_select(const StepArgs& a, hipStream_t s) {
   if (a.r.R <= 0) return hipSuccess;
@@ -681,17 +831,20 @@ hipError_t launch_mid_select(const StepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_leaf_buckets(const StepArgs& a, hipStream_t s) {
-  if (a.r.R <= 0 || a.K[1] <= 0) return hipSuccess;
-  const int64_t nkeys = (int64_t)a.t.Hkv * a.t.count[1];
-  int64_t blocks = (nkeys + 255) / 256;
+hipError_t launch_clear(const StepArgs& a, hipStream_t s) {
+  if (a.r.R <= 0) return hipSuccess;
+  const int64_t nkeys1 = (int64_t)a.t.Hkv * a.t.count[1], nkeys0 = (int64_t)a.t.Hkv * a.t.count[0];
+  int64_t blocks = ((nkeys1 > nkeys0 ? nkeys1 : nkeys0) + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(k_bucket_clear, dim3((unsigned)blocks), dim3(256), 0, s, a, nkeys);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_clear, dim3((unsigned)blocks), dim3(256), 0, s, a, nkeys1, nkeys0);
+  return hipGetLastError();
+}
+
+hipError_t launch_leaf_link(const StepArgs& a, hipStream_t s) {
+  if (a.r.R <= 0 || a.K[1] <= 0) return hipSuccess;
   const int64_t n = (int64_t)a.r.R * a.K[1];
-  blocks = (n + 255) / 256;
+  int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(k_bucket_link, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
@@ -706,8 +859,9 @@ hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s) {
   HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_score, dim3((unsigned)blocks), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  blocks = (nb_max + 3) / 4;
-  if (blocks > 2048) blocks = 2048;
+  // at most R * K_I / (kBucketSlots + 1) buckets overflow
+  blocks = (nb_max / (kBucketSlots + 1) + 4) / 4;
+  if (blocks > 1024) blocks = 1024;
   HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_score_overflow, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
