@@ -85,7 +85,9 @@ def algorithmic_bytes(case, sel):
         "root_score_topk": roots_b + q_b,
         "mid_bucket_gemm": mids_b,
         "mid_topk": 0,
+        "leaf_bucket_link": 0,
         "leaf_score_stream": leafk_b,
+        "leaf_score_overflow": 0,
         "leaf_topk_kg_attention": leafv_b,
         "seq_attention_merge": seq_b + out_b,
         "_total": roots_b + mids_b + leafk_b + leafv_b + seq_b + q_b + out_b,

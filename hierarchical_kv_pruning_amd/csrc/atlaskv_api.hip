@@ -265,8 +265,8 @@ const char* atlaskv_last_error(void) { return g_err.c_str(); }
 const char* atlaskv_version(void) { return "atlaskv-mi355x 0.1 (gfx950)"; }
 
 static const char* const kPhaseNames[] = {"root_score_topk", "mid_bucket_gemm", "mid_topk",
-                                          "leaf_score_stream", "leaf_topk_kg_attention",
-                                          "seq_attention_merge"};
+                                          "leaf_bucket_link", "leaf_score_stream", "leaf_score_overflow",
+                                          "leaf_topk_kg_attention", "seq_attention_merge"};
 static const int kPhases = (int)(sizeof kPhaseNames / sizeof kPhaseNames[0]);
 
 int32_t atlaskv_phase_count(void) { return kPhases; }
@@ -465,8 +465,9 @@ atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vie
   if (e == hipSuccess) e = mark(launch_root_groups(a, s));
   if (e == hipSuccess) e = mark(launch_mid_gemm(a, s));
   if (e == hipSuccess) e = mark(launch_mid_select(a, s));
-  if (e == hipSuccess) e = launch_leaf_link(a, s);
+  if (e == hipSuccess) e = mark(launch_leaf_link(a, s));
   if (e == hipSuccess) e = mark(launch_leaf_score(a, s));
+  if (e == hipSuccess) e = mark(launch_leaf_overflow(a, s));
   if (e == hipSuccess) e = mark(launch_leaf_select(a, s));
   if (e == hipSuccess) {
     SeqArgs sa;

@@ -105,7 +105,8 @@ hipError_t launch_root_groups(const StepArgs& a, hipStream_t s);  // rows by sel
 hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s);
 hipError_t launch_mid_select(const StepArgs& a, hipStream_t s);
 hipError_t launch_leaf_link(const StepArgs& a, hipStream_t s);    // rows by selected (head, mid)
-hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s);   // grouped buckets + overflow members
+hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s);   // buckets' first kBucketSlots members
+hipError_t launch_leaf_overflow(const StepArgs& a, hipStream_t s);  // members past kBucketSlots
 hipError_t launch_leaf_select(const StepArgs& a, hipStream_t s);
 hipError_t launch_seq_merge(const SeqArgs& a, hipStream_t s);
 int seq_splits(int B, int N, int Hkv, int S);   // key splits of the sequence attention

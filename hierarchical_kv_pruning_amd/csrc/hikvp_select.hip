@@ -857,10 +857,14 @@ hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s) {
   int64_t blocks = (nb_max + 3) / 4;
   if (blocks > 2048) blocks = 2048;
   HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_score, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_leaf_overflow(const StepArgs& a, hipStream_t s) {
+  if (a.r.R <= 0 || a.K[1] <= 0) return hipSuccess;
   // at most R * K_I / (kBucketSlots + 1) buckets overflow
-  blocks = (nb_max / (kBucketSlots + 1) + 4) / 4;
+  const int64_t nb_max = (int64_t)a.r.R * a.K[1];
+  int64_t blocks = (nb_max / (kBucketSlots + 1) + 4) / 4;
   if (blocks > 1024) blocks = 1024;
   HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_score_overflow, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -171,3 +171,14 @@ def test_described_view_cannot_run(lib):
         atlaskv.hikvp_attend_ex(q, v, sk, torch.zeros_like(sk), (1, 1, 1), torch.zeros_like(q),
                                 workspace=ws)
     assert e.value.status in (atlaskv.ERR_UNSUPPORTED, atlaskv.ERR_WORKSPACE)
+
+
+def test_phase_names_in_launch_order(lib):
+    """The timing phases follow the descent: roots (with their row grouping),
+    mid GEMM, mid Top-K, leaf bucket link, leaf scoring (first members, then
+    overflow members), leaf Top-K with the KG softmax, sequence attention."""
+    assert atlaskv.phase_names() == [
+        "root_score_topk", "mid_bucket_gemm", "mid_topk", "leaf_bucket_link", "leaf_score_stream",
+        "leaf_score_overflow", "leaf_topk_kg_attention", "seq_attention_merge"]
+    assert lib.atlaskv_phase_name(-1) is None
+    assert lib.atlaskv_phase_name(lib.atlaskv_phase_count()) is None
