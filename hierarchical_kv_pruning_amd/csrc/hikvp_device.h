@@ -89,15 +89,88 @@ __device__ inline void group_sync() {
   else __syncthreads();
 }
 
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+// ---------------------------------------------------------------------------
+// Cross-lane reductions and scans on DPP (data-parallel primitives: a VALU
+// operand read from another lane of the same 16-lane row, a few cycles) and
+// v_readlane, instead of LDS-crossbar shuffles (~100+ cycles each).
+// Control words: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_shr:n =
+// 0x110+n, row_mirror = 0x140, row_half_mirror = 0x141, row_bcast:15 = 0x142,
+// row_bcast:31 = 0x143.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROWS = 0xf, int BANKS = 0xf, bool ZERO = true>
+__device__ inline int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, BANKS, ZERO);
+}
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+// Inclusive prefix sum over the wave's 64 lanes.
+__device__ inline int wave_incl_sum(int x) {
+  x += dpp_i<0x111>(0, x);
+  x += dpp_i<0x112>(0, x);
+  x += dpp_i<0x114>(0, x);
+  x += dpp_i<0x118>(0, x);
+  x += dpp_i<0x142, 0xa, 0xf, false>(0, x);  // rows 1, 3 add lane 15 of the row before
+  x += dpp_i<0x143, 0xc, 0xf, false>(0, x);  // rows 2, 3 add lane 31
+  return x;
+}
+__device__ inline int wave_sum_i(int x) { return __builtin_amdgcn_readlane(wave_incl_sum(x), 63); }
+
+// Reduction within aligned groups of L lanes (L = 2..16): after the quad,
+// half-row and row steps every lane of the group holds the result.
+template <int L, class T, class Op>
+__device__ inline T group_reduce16(T v, Op op) {
+  if constexpr (L >= 2) v = op(v, dpp_f<0xB1>(v));
+  if constexpr (L >= 4) v = op(v, dpp_f<0x4E>(v));
+  if constexpr (L >= 8) v = op(v, dpp_f<0x141>(v));
+  if constexpr (L >= 16) v = op(v, dpp_f<0x140>(v));
   return v;
 }
-__device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+struct AddF { __device__ float operator()(float a, float b) const { return a + b; } };
+struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+
+// Sum / max within aligned groups of L lanes (L = 1..64), every lane of the
+// group getting the result.
+template <int L>
+__device__ inline float group_sum(float v) {
+  v = group_reduce16<(L < 16 ? L : 16)>(v, AddF{});
+  if constexpr (L >= 32) v += __shfl_xor(v, 16);
+  if constexpr (L >= 64) v += __shfl_xor(v, 32);
   return v;
+}
+template <int L>
+__device__ inline float group_max(float v) {
+  v = group_reduce16<(L < 16 ? L : 16)>(v, MaxF{});
+  if constexpr (L >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  if constexpr (L >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+// Whole-wave sum / max, uniform result (row results combined through
+// v_readlane in a fixed order).
+__device__ inline float wave_sum(float v) {
+  v = group_reduce16<16>(v, AddF{});
+  return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
+}
+__device__ inline float wave_max(float v) {
+  v = group_reduce16<16>(v, MaxF{});
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48))));
+}
+__device__ inline uint32_t wave_max_u(uint32_t x) {
+  x = max(x, (uint32_t)dpp_i<0xB1>((int)x, (int)x));
+  x = max(x, (uint32_t)dpp_i<0x4E>((int)x, (int)x));
+  x = max(x, (uint32_t)dpp_i<0x141>((int)x, (int)x));
+  x = max(x, (uint32_t)dpp_i<0x140>((int)x, (int)x));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48)));
 }
 
 // Order-preserving map of fp32 to uint32 (larger float -> larger key).
@@ -144,14 +217,9 @@ __device__ inline int build_candidates(const int32_t* parents, int Kp, const int
       }
       base[k] = first;
     }
-    int incl = fan;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
+    const int incl = wave_incl_sum(fan);
     if (k < Kp) pre[k + 1] = carry + incl;
-    carry += __shfl(incl, 63);
+    carry += __builtin_amdgcn_readlane(incl, 63);
   }
   return carry;
 }
@@ -274,8 +342,7 @@ __device__ inline void score_run(const float* qf, const char* kbase, int64_t rsb
       float s = 0.f;
 #pragma unroll
       for (int t = 0; t < EPV; ++t) s = fmaf(qf[t], kf[t], s);
-#pragma unroll
-      for (int o = LPK / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+      s = group_sum<LPK>(s);
       if (j == 0 && c < len) out[c] = s;
     }
   }
@@ -465,8 +532,7 @@ __device__ int select_topk(const Src& src, int n, int K, double err2, double sca
   {
     uint32_t tmax = 0;
     src.each(n, tid, [&](int, float f) { tmax = max(tmax, ord_key(f) >> 24); });
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, o));
+    tmax = wave_max_u(tmax);
     if (NH > 1) {
       if ((tid & 63) == 0) S.hist[tid >> 6] = (int)tmax;
       group_sync<NT>();
@@ -482,12 +548,7 @@ __device__ int select_topk(const Src& src, int n, int K, double err2, double sca
       for (int c = 0; c < kWin; ++c) cnt[c] += (d == (uint32_t)c) ? 1 : 0;
     });
 #pragma unroll
-    for (int c = 0; c < kWin; ++c) {
-      int v = cnt[c];
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-      cnt[c] = v;
-    }
+    for (int c = 0; c < kWin; ++c) cnt[c] = wave_sum_i(cnt[c]);
     if (NH > 1) {
       if ((tid & 63) < kWin) {
         int mine = 0;
@@ -537,12 +598,9 @@ __device__ int select_topk(const Src& src, int n, int K, double err2, double sca
         c3 += hw[3];
       }
       const int tot = c0 + c1 + c2 + c3;
-      int suf = tot;  // inclusive suffix sum over lanes (higher lanes hold higher bins)
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_down(suf, o);
-        if (lane + o < 64) suf += t;
-      }
+      // inclusive suffix sum over lanes (higher lanes hold higher bins)
+      const int incl = wave_incl_sum(tot);
+      const int suf = __builtin_amdgcn_readlane(incl, 63) - incl + tot;
       const int above = suf - tot;
       const unsigned long long hit = __ballot(above < krem && krem <= suf);
       const int src_lane = __ffsll((long long)hit) - 1;

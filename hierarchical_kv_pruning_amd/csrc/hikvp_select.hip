@@ -133,12 +133,7 @@ __global__ __launch_bounds__(256) void k_root(StepArgs a, size_t wave_bytes, int
     const int i = i0 + lane;
     const int node = i < k ? W.out_node[i] : -1;
     const int fan = node >= 0 ? (int)(off0[node + 1] - off0[node]) : 0;
-    int incl = fan;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
+    const int incl = wave_incl_sum(fan);
     if (i < K) {
       // rank within the row's sub-counter (by token) of the group: spreading a
       // group over kRootSub counters keeps the atomics on one address few
@@ -147,7 +142,7 @@ __global__ __launch_bounds__(256) void k_root(StepArgs a, size_t wave_bytes, int
           node >= 0 ? atomicAdd(&a.root_cnt[(int64_t)sub * a.t.Hkv * MR + g * MR + node], 1) : -1;
       a.root_base[(int64_t)row * K + i] = carry + incl - fan;
     }
-    carry += __shfl(incl, 63);
+    carry += __builtin_amdgcn_readlane(incl, 63);
   }
 }
 
@@ -170,12 +165,7 @@ __global__ __launch_bounds__(1024) void k_root_scan(StepArgs a) {
       a.root_tot[key] = tot;
     }
     const int pc = (tot + kRootTile - 1) / kRootTile;
-    int incl = pc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
+    const int incl = wave_incl_sum(pc);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     int woff = 0, total = 0;
@@ -382,17 +372,12 @@ __device__ inline void mid_select_body(const StepArgs& a, size_t group_bytes) {
     const int i = i0 + lane;
     const int node = i < k1 ? W.out_node[i] : -1;
     const int fan = node >= 0 ? (int)(off1[node + 1] - off1[node]) : 0;
-    int incl = fan;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
+    const int incl = wave_incl_sum(fan);
     if (i < K1) {
       o1[i] = node;
       ob[i] = carry + incl - fan;  // first leaf-candidate slot of this mid in the row's list
     }
-    carry += __shfl(incl, 63);
+    carry += __builtin_amdgcn_readlane(incl, 63);
   }
 }
 
@@ -457,7 +442,7 @@ __global__ void k_bucket_link(StepArgs a) {
       int base = 0;
       const int leader = __builtin_ctzll(fresh);
       if (lane == leader) base = atomicAdd(&a.bucket_count[0], __popcll(fresh));
-      base = __shfl(base, leader);
+      base = __builtin_amdgcn_readlane(base, leader);
       if (rank == 0) {
         const int below = __popcll(fresh & ((1ull << lane) - 1ull));
         const int64_t f0 = off1[mid];
@@ -500,8 +485,7 @@ __device__ inline void score_members(const StepArgs& a, const char* kb, int F, i
         float s = 0.f;
 #pragma unroll
         for (int t = 0; t < EPV; ++t) s = fmaf(qf[mm][t], kf[t], s);
-#pragma unroll
-        for (int o = LPK / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+        s = group_sum<LPK>(s);
         if (j == 0 && c < F) a.leaf_scores[(int64_t)rows[mm] * a.c2max + bases[mm] + c] = s;
       }
     }

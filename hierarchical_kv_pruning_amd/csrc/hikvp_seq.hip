@@ -57,8 +57,7 @@ __device__ inline SoftmaxState<D / 64> attend_range(const SeqArgs& a, const char
       float s = 0.f;
 #pragma unroll
       for (int t = 0; t < EPV; ++t) s = fmaf(qf[t], kf[t], s);
-#pragma unroll
-      for (int o = LPK / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+      s = group_sum<LPK>(s);
       if (j == 0) s_p[it * KPW + lane / LPK] = (i < k1) ? s * scale : -INFINITY;
     }
     wave_sync();
@@ -280,15 +279,11 @@ __global__ __launch_bounds__(256) void k_seq_flash(SeqArgs a) {
         const int vis = S - N + tok + 1;
         const bool ok = tok < N && (k0 + col) < vis;
         const float sv = ok ? sacc[v] * scale : -INFINITY;
-        float mx = sv;
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        const float mx = group_max<16>(sv);  // the tile row's 16 keys: one DPP row
         const float mn = fmaxf(mrow[v], mx);
         const float alpha = mn == -INFINITY ? 1.f : __expf(mrow[v] - mn);
         const float pv = ok ? __expf(sv - mn) : 0.f;
-        float rs = pv;
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) rs += __shfl_xor(rs, o);
+        const float rs = group_sum<16>(pv);
         lrow[v] = lrow[v] * alpha + rs;
         mrow[v] = mn;
 #pragma unroll

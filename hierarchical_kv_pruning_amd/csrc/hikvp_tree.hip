@@ -49,8 +49,7 @@ __global__ __launch_bounds__(256) void k_key_norms(const void* key, int64_t rows
 #pragma unroll
       for (int t = 0; t < EPV; ++t) s = fmaf(kf[t], kf[t], s);
     }
-#pragma unroll
-    for (int o = LPK / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    s = group_sum<LPK>(s);
     mx = fmaxf(mx, s);
   }
   mx = wave_max(mx);
