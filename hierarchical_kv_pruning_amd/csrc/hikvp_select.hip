@@ -49,7 +49,6 @@ __device__ inline const char* key_base(const TreeDev& t, int lev, int g, int64_t
 // per-row select kernels: one wave per row, LDS work area carved per wave
 // ---------------------------------------------------------------------------
 constexpr int kStageMax = 0;     // mid/leaf scores are not staged in LDS (registers instead)
-constexpr int kRegScores = 32;   // candidate scores held per thread in the select kernels
 
 struct RowWork {
   SelWork sel;
@@ -381,18 +380,12 @@ __device__ inline void mid_select_body(const StepArgs& a, size_t group_bytes) {
   }
 }
 
-// one wave per row (candidate lists up to a few thousand) or one workgroup per row
-template <class E, int D>
+// One wave per row (short candidate lists) or one workgroup per row; the
+// scores are held in registers (SPT per thread, sized to the list at launch)
+// or re-read from the workspace in every pass (SPT = 0, long lists).
+template <class E, int D, int NT, int SPT>
 __global__ __launch_bounds__(256) void k_mid_select(StepArgs a, size_t gb) {
-  mid_select_body<E, D, 64, 0>(a, gb);
-}
-template <class E, int D>
-__global__ __launch_bounds__(256) void k_mid_select_wide(StepArgs a, size_t gb) {
-  mid_select_body<E, D, 256, 0>(a, gb);
-}
-template <class E, int D>
-__global__ __launch_bounds__(256) void k_mid_select_mem(StepArgs a, size_t gb) {
-  mid_select_body<E, D, 256, 0>(a, gb);
+  mid_select_body<E, D, NT, SPT>(a, gb);
 }
 
 // ---------------------------------------------------------------------------
@@ -705,7 +698,21 @@ __device__ inline void leaf_select_body(const StepArgs& a, size_t group_bytes) {
   float acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  // value rows gathered VB at a time, so the row's K_L rows take one or two
+  // memory round trips
+  constexpr int VB = 16;  // more would cost occupancy (registers) for the whole kernel
   int i = 0;
+  for (; i + VB <= k2; i += VB) {
+    float v[VB][DPL];
+#pragma unroll
+    for (int u = 0; u < VB; ++u) load_lane<E, DPL>(vb + (int64_t)W.out_node[i + u] * vrs, lane, v[u]);
+#pragma unroll
+    for (int u = 0; u < VB; ++u) {
+      const float w = W.out_logit[i + u];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, v[u][e], acc[e]);
+    }
+  }
   for (; i + 8 <= k2; i += 8) {
     float v[8][DPL];
 #pragma unroll
@@ -730,17 +737,9 @@ __device__ inline void leaf_select_body(const StepArgs& a, size_t group_bytes) {
   if (lane == 0) a.lse_kg[row] = mx + logf(sum);
 }
 
-template <class E, int D>
+template <class E, int D, int NT, int SPT>
 __global__ __launch_bounds__(256) void k_leaf_select(StepArgs a, size_t gb) {
-  leaf_select_body<E, D, 64, 0>(a, gb);
-}
-template <class E, int D>
-__global__ __launch_bounds__(256) void k_leaf_select_wide(StepArgs a, size_t gb) {
-  leaf_select_body<E, D, 256, 0>(a, gb);
-}
-template <class E, int D>
-__global__ __launch_bounds__(256) void k_leaf_select_mem(StepArgs a, size_t gb) {
-  leaf_select_body<E, D, 256, 0>(a, gb);
+  leaf_select_body<E, D, NT, SPT>(a, gb);
 }
 
 }  // namespace
@@ -752,6 +751,46 @@ __global__ __launch_bounds__(256) void k_leaf_select_mem(StepArgs a, size_t gb) 
     else if ((dtype) == kDtypeF32 && (d) == 128) hipLaunchKernelGGL((KERNEL<F32, 128>), __VA_ARGS__); \
     else if ((dtype) == kDtypeF32 && (d) == 64) hipLaunchKernelGGL((KERNEL<F32, 64>), __VA_ARGS__);  \
     else return hipErrorInvalidValue;                                                                \
+  } while (0)
+
+#define HIKVP_DISPATCH_SEL(dtype, d, KERNEL, NT, SPT, ...)                                          \
+  do {                                                                                               \
+    if ((dtype) == kDtypeBF16 && (d) == 128) hipLaunchKernelGGL((KERNEL<BF16, 128, NT, SPT>), __VA_ARGS__); \
+    else if ((dtype) == kDtypeBF16 && (d) == 64) hipLaunchKernelGGL((KERNEL<BF16, 64, NT, SPT>), __VA_ARGS__); \
+    else if ((dtype) == kDtypeF32 && (d) == 128) hipLaunchKernelGGL((KERNEL<F32, 128, NT, SPT>), __VA_ARGS__); \
+    else if ((dtype) == kDtypeF32 && (d) == 64) hipLaunchKernelGGL((KERNEL<F32, 64, NT, SPT>), __VA_ARGS__); \
+    else return hipErrorInvalidValue;                                                                \
+  } while (0)
+
+// Per-row select shape: one wave per row while the list fits 16 scores per
+// lane, else a 256-thread workgroup with 8, 16 or 32 scores per thread held
+// in registers (the fewest that cover the list: fewer registers held means
+// more rows in flight, which these latency-bound kernels need); lists above
+// 8192 are re-read from the workspace in every pass.
+#define HIKVP_SELECT_LAUNCH(a, cap, KERNEL, Kc, Kp, s)                                               \
+  do {                                                                                               \
+    const int64_t cap_ = (cap);                                                                      \
+    if (cap_ <= 64 * 16) {                                                                           \
+      int wpb, stage;                                                                                \
+      size_t wb;                                                                                     \
+      if (!row_launch_shape((Kc), (Kp), (a).t.d, 0, wpb, wb, stage)) return hipErrorInvalidValue;   \
+      const unsigned blocks = (unsigned)(((a).r.R + wpb - 1) / wpb);                                 \
+      if (cap_ <= 64 * 8)                                                                            \
+        HIKVP_DISPATCH_SEL((a).t.dtype, (a).t.d, KERNEL, 64, 8, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb); \
+      else                                                                                           \
+        HIKVP_DISPATCH_SEL((a).t.dtype, (a).t.d, KERNEL, 64, 16, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb); \
+    } else {                                                                                         \
+      const size_t gb = rowwork_bytes((Kc), (Kp), (a).t.d, 0, 256);                                  \
+      const dim3 grid((unsigned)(a).r.R);                                                            \
+      if (cap_ <= 256 * 8)                                                                           \
+        HIKVP_DISPATCH_SEL((a).t.dtype, (a).t.d, KERNEL, 256, 8, grid, dim3(256), gb, s, a, gb);      \
+      else if (cap_ <= 256 * 16)                                                                     \
+        HIKVP_DISPATCH_SEL((a).t.dtype, (a).t.d, KERNEL, 256, 16, grid, dim3(256), gb, s, a, gb);     \
+      else if (cap_ <= 256 * 32)                                                                     \
+        HIKVP_DISPATCH_SEL((a).t.dtype, (a).t.d, KERNEL, 256, 32, grid, dim3(256), gb, s, a, gb);     \
+      else                                                                                           \
+        HIKVP_DISPATCH_SEL((a).t.dtype, (a).t.d, KERNEL, 256, 0, grid, dim3(256), gb, s, a, gb);      \
+    }                                                                                                \
   } while (0)
 
 // Waves per block and per-wave LDS of a per-row select kernel.
@@ -799,19 +838,7 @@ hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s) {
 
 hipError_t launch_mid_select(const StepArgs& a, hipStream_t s) {
   if (a.r.R <= 0) return hipSuccess;
-  if (a.c1max > 64 * kRegScores) {
-    const size_t gb = rowwork_bytes(a.K[1], a.K[0], a.t.d, 0, 256);
-    if (a.c1max <= 256 * kRegScores)
-      HIKVP_DISPATCH(a.t.dtype, a.t.d, k_mid_select_wide, dim3((unsigned)a.r.R), dim3(256), gb, s, a, gb);
-    else
-      HIKVP_DISPATCH(a.t.dtype, a.t.d, k_mid_select_mem, dim3((unsigned)a.r.R), dim3(256), gb, s, a, gb);
-    return hipGetLastError();
-  }
-  int wpb, stage;
-  size_t wb;
-  if (!row_launch_shape(a.K[1], a.K[0], a.t.d, 0, wpb, wb, stage)) return hipErrorInvalidValue;
-  const unsigned blocks = (unsigned)((a.r.R + wpb - 1) / wpb);
-  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_mid_select, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb);
+  HIKVP_SELECT_LAUNCH(a, a.c1max, k_mid_select, a.K[1], a.K[0], s);
   return hipGetLastError();
 }
 
@@ -856,19 +883,7 @@ hipError_t launch_leaf_overflow(const StepArgs& a, hipStream_t s) {
 
 hipError_t launch_leaf_select(const StepArgs& a, hipStream_t s) {
   if (a.r.R <= 0) return hipSuccess;
-  if (a.c2max > 64 * kRegScores) {
-    const size_t gb = rowwork_bytes(a.K[2], a.K[1], a.t.d, 0, 256);
-    if (a.c2max <= 256 * kRegScores)
-      HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_select_wide, dim3((unsigned)a.r.R), dim3(256), gb, s, a, gb);
-    else
-      HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_select_mem, dim3((unsigned)a.r.R), dim3(256), gb, s, a, gb);
-    return hipGetLastError();
-  }
-  int wpb, stage;
-  size_t wb;
-  if (!row_launch_shape(a.K[2], a.K[1], a.t.d, 0, wpb, wb, stage)) return hipErrorInvalidValue;
-  const unsigned blocks = (unsigned)((a.r.R + wpb - 1) / wpb);
-  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_select, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb);
+  HIKVP_SELECT_LAUNCH(a, a.c2max, k_leaf_select, a.K[2], a.K[1], s);
   return hipGetLastError();
 }
 

@@ -41,6 +41,11 @@ def _check(case, rows=None, two_phase=False, **kw):
     return gpu, ora, rep
 
 
+def _release():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 def _small(name="edge", seed=0, **kw):
     cfg = dict(dtype="f32", B=2, N=33, S_kv=45, Hq=8, Hkv=2, d=128, M_R=37, M_I=411, M=5003,
                K=(5, 7, 19))
@@ -167,17 +172,28 @@ def test_view_workspace_entry_point():
     assert np.array_equal(out.float().reshape(case.rows, -1).cpu().numpy(), ref["out"])
 
 
+@pytest.mark.parametrize("K,F1,F2", [
+    ((2, 4, 8), 300, 1000),    # mid list 600: one wave, 16 per lane; leaf 4000: 256 threads, 16 each
+    ((3, 2, 8), 500, 3000),    # mid 1500: 256 threads, 8 each; leaf 6000: 256 threads, 32 each
+    ((2, 2, 8), 5000, 20),     # mid 10000: 256 threads, re-read from the workspace; leaf 40: 8 per lane
+])
+def test_select_launch_shapes(K, F1, F2):
+    """Balanced trees whose per-row candidate lists (K_R*F1 mids, K_I*F2
+    leaves) land in each register / workgroup shape of the select kernels."""
+    MR = 4
+    case = synth.make_case("shapes", device=DEV, seed=31, ragged=False, dtype="bf16", B=1, N=5, S_kv=7,
+                           Hq=4, Hkv=1, d=64, M_R=MR, M_I=MR * F1, M=MR * F1 * F2, K=K)
+    _check(case, two_phase=True)
+    del case
+    _release()
+
+
 # ---------------------------------------------------------------------------
 # the named workloads
 # ---------------------------------------------------------------------------
 
 def test_m1e4_all_rows():
     _check(synth.make_case("m1e4", device=DEV))
-
-
-def _release():
-    gc.collect()
-    torch.cuda.empty_cache()
 
 
 def test_m1e6_sampled_rows():
