@@ -17,86 +17,6 @@
 namespace hikvp {
 namespace {
 
-// ---------------------------------------------------------------------------
-// causal sequence attention + λ merge, one workgroup per (b, n, KV head)
-// ---------------------------------------------------------------------------
-// Online-softmax state of one row over a key range: running max m, running
-// sum l and the unnormalised weighted value sum (this lane's DPL dims).
-template <int DPL>
-struct SoftmaxState {
-  float m, l, acc[DPL];
-};
-
-// Causal attention of one query row over keys [k0, k1): scores in 64-key
-// chunks (16-byte lanes, LPK lanes per key row), chunk-wise online softmax,
-// then the weighted value rows (one coalesced row load per key).
-template <class E, int D>
-__device__ inline SoftmaxState<D / 64> attend_range(const SeqArgs& a, const char* kbase, const char* vbase,
-                                                    int64_t kstep, int64_t vstep, const float* qf,
-                                                    int k0, int k1, float* s_p, int lane) {
-  constexpr int EPV = E::kEPV, LPK = D / EPV, KPW = 64 / LPK, DPL = D / 64, CH = 64;
-  const int j = lane % LPK;
-  const float scale = (float)a.r.scale;
-  SoftmaxState<DPL> st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) st.acc[e] = 0.f;
-  for (int c0 = k0; c0 < k1; c0 += CH) {
-    uint4 kv[CH / KPW];
-#pragma unroll
-    for (int it = 0; it < CH / KPW; ++it) {
-      const int i = c0 + it * KPW + lane / LPK;
-      kv[it] = i < k1 ? *(const uint4*)(kbase + (int64_t)i * kstep + j * 16) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int it = 0; it < CH / KPW; ++it) {
-      const int i = c0 + it * KPW + lane / LPK;
-      float kf[EPV];
-      unpack<E>(kv[it], kf);
-      float s = 0.f;
-#pragma unroll
-      for (int t = 0; t < EPV; ++t) s = fmaf(qf[t], kf[t], s);
-      s = group_sum<LPK>(s);
-      if (j == 0) s_p[it * KPW + lane / LPK] = (i < k1) ? s * scale : -INFINITY;
-    }
-    wave_sync();
-    const float sv = s_p[lane];
-    const float mn = fmaxf(st.m, wave_max(sv));
-    const float alpha = __expf(st.m - mn);
-    const float p = __expf(sv - mn);
-    st.l = st.l * alpha + wave_sum(p);
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) st.acc[e] *= alpha;
-    st.m = mn;
-    wave_sync();
-    s_p[lane] = p;
-    wave_sync();
-    const int cnt = (k1 - c0) < CH ? (k1 - c0) : CH;
-    int i = 0;
-    for (; i + 8 <= cnt; i += 8) {
-      float v[8][DPL];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) load_lane<E, DPL>(vbase + (int64_t)(c0 + i + u) * vstep, lane, v[u]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float pi = s_p[i + u];
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) st.acc[e] = fmaf(pi, v[u][e], st.acc[e]);
-      }
-    }
-    for (; i < cnt; ++i) {
-      float v[DPL];
-      load_lane<E, DPL>(vbase + (int64_t)(c0 + i) * vstep, lane, v);
-      const float pi = s_p[i];
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) st.acc[e] = fmaf(pi, v[e], st.acc[e]);
-    }
-    wave_sync();
-  }
-  return st;
-}
-
 // λ merge of the sequence half (lse_seq, o_seq) with the KG half of the row.
 template <class E, int D>
 __device__ inline void merge_store(const SeqArgs& a, int row, int b, int n, int h, float lse_seq,
@@ -119,52 +39,172 @@ __device__ inline void merge_store(const SeqArgs& a, int row, int b, int n, int 
   if (a.lse_seq_out && lane == 0) a.lse_seq_out[row] = lse_seq;
 }
 
-// One workgroup per (b, n, KV head [, key split]); one wave per query head of
-// the group, so the group's K/V rows are shared through L1.  With splits the
-// wave writes its partial (m, l, acc) and k_seq_combine finishes the row.
+// ---------------------------------------------------------------------------
+// Decode (fewer than 16 query tokens): one wave per (b, n, KV head, group of
+// up to 4 query heads [, key split]).  The wave streams its key range in
+// chunks of 16 keys; a 16-lane DPP row holds one 256-byte key (or value) row,
+// lane c owning dims [c*EPL, c*EPL+EPL) with EPL = D/16, so each load
+// instruction covers four whole rows and K and V are read once for all the
+// group's heads.  Scores are 16-lane DPP sums; the softmax statistics are
+// wave-uniform (v_readlane); every lane of a row keeps that row's
+// probabilities, so P V accumulates on VALU without LDS.  The four rows'
+// partial sums are combined at the end.
+// ---------------------------------------------------------------------------
+// EPL consecutive elements of a row as raw 32-bit words (8, 16 or 32 bytes),
+// unpacked to fp32 where used: holding rows packed keeps the registers low.
+template <class E, int EPL>
+struct RawElems {
+  static constexpr int kWords = EPL * E::kBytes / 4;
+  uint32_t w[kWords];
+  __device__ inline void load(const char* p) {
+    if constexpr (kWords == 2) {
+      const uint2 v = *(const uint2*)p;
+      w[0] = v.x; w[1] = v.y;
+    } else {
+#pragma unroll
+      for (int k = 0; k < kWords; k += 4) {
+        const uint4 v = *(const uint4*)(p + 4 * k);
+        w[k] = v.x; w[k + 1] = v.y; w[k + 2] = v.z; w[k + 3] = v.w;
+      }
+    }
+  }
+  __device__ inline float operator[](int e) const {
+    if constexpr (E::kBytes == 2) return __uint_as_float(e & 1 ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+    else return __uint_as_float(w[e]);
+  }
+};
+
 template <class E, int D>
-__global__ __launch_bounds__(256) void k_seq_attend(SeqArgs a) {
-  constexpr int EPV = E::kEPV, LPK = D / EPV, DPL = D / 64;
-  __shared__ float s_p[4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
-  const int g = blockIdx.x % a.Hkv;
-  const int bn = blockIdx.x / a.Hkv;
-  const int n = bn % a.r.N, b = bn / a.r.N;
+__global__ __launch_bounds__(64) void k_seq_decode(SeqArgs a) {
+  constexpr int EPL = D / 16, HG = 4, CK = 16;
+  const int lane = threadIdx.x, r = lane >> 4, c = lane & 15;
+  const int G = a.r.G, HGP = (G + HG - 1) / HG;
+  int t = blockIdx.x;
+  const int hgp = t % HGP; t /= HGP;
+  const int g = t % a.Hkv; t /= a.Hkv;
+  const int n = t % a.r.N, b = t / a.r.N;
+  const int nh = (G - hgp * HG) < HG ? (G - hgp * HG) : HG;   // heads of this wave
   const int split = blockIdx.y, nsplit = gridDim.y;
-  const int G = a.r.G;
   const int vis = a.k ? a.S - a.r.N + n + 1 : 0;
   const int k0 = split * a.split_len;
   const int k1 = (k0 + a.split_len) < vis ? (k0 + a.split_len) : vis;
-  const char* kbase = (const char*)a.k + ((int64_t)b * a.ks[0] + (int64_t)g * a.ks[2]) * E::kBytes;
-  const char* vbase = (const char*)a.v + ((int64_t)b * a.vs[0] + (int64_t)g * a.vs[2]) * E::kBytes;
-  const int64_t kstep = a.ks[1] * E::kBytes, vstep = a.vs[1] * E::kBytes;
+  const float scale = (float)a.r.scale;
 
-  for (int hw = wave; hw < G; hw += nwave) {
-    const int h = g * G + hw;
-    const int row = (b * a.r.N + n) * a.r.Hq + h;
-    float qf[EPV];
-    {
-      const char* qp = (const char*)a.r.q + q_off(a.r.qs, b, n, h) * E::kBytes;
-      unpack<E>(*(const uint4*)(qp + (lane % LPK) * 16), qf);
+  float qf[HG][EPL];
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh) {
+    const int h = g * G + hgp * HG + (hh < nh ? hh : 0);
+    RawElems<E, EPL> qr;
+    qr.load((const char*)a.r.q + (q_off(a.r.qs, b, n, h) + c * EPL) * E::kBytes);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[hh][e] = qr[e];
+  }
+  float m[HG], l[HG], acc[HG][EPL];
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
+  }
+  if (k0 < k1) {
+    const char* kb = (const char*)a.k + ((int64_t)b * a.ks[0] + (int64_t)g * a.ks[2] + c * EPL) * E::kBytes;
+    const char* vb = (const char*)a.v + ((int64_t)b * a.vs[0] + (int64_t)g * a.vs[2] + c * EPL) * E::kBytes;
+    const int64_t kstep = a.ks[1] * E::kBytes, vstep = a.vs[1] * E::kBytes;
+    for (int c0 = k0; c0 < k1; c0 += CK) {
+      RawElems<E, EPL> kf[CK / 4], vf[CK / 4];
+#pragma unroll
+      for (int i = 0; i < CK / 4; ++i) {   // key c0 + 4i + r; past the range: its last key (masked)
+        const int key = min(c0 + 4 * i + r, k1 - 1);
+        kf[i].load(kb + (int64_t)key * kstep);
+        vf[i].load(vb + (int64_t)key * vstep);
+      }
+      float p[CK / 4][HG];
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        float sc[CK / 4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < CK / 4; ++i) {
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) d = fmaf(qf[hh][e], kf[i][e], d);
+          d = group_sum<16>(d);
+          sc[i] = (c0 + 4 * i + r < k1) ? d * scale : -INFINITY;
+          mx = fmaxf(mx, sc[i]);
+        }
+        // chunk max over the four rows, wave-uniform
+        mx = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 0)),
+                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 16))),
+                   fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 32)),
+                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 48))));
+        const float mn = fmaxf(m[hh], mx);   // finite: key c0 is in range
+        const float alpha = __expf(m[hh] - mn);
+        float ls = 0.f;
+#pragma unroll
+        for (int i = 0; i < CK / 4; ++i) {
+          p[i][hh] = __expf(sc[i] - mn);
+          ls += p[i][hh];
+        }
+        ls = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), 0)) +
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), 16))) +
+             (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), 32)) +
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), 48)));
+        l[hh] = l[hh] * alpha + ls;
+        m[hh] = mn;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[hh][e] *= alpha;
+      }
+#pragma unroll
+      for (int i = 0; i < CK / 4; ++i)
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(p[i][hh], vf[i][e], acc[hh][e]);
     }
-    const SoftmaxState<DPL> st =
-        attend_range<E, D>(a, kbase, vbase, kstep, vstep, qf, k0, k1, s_p[wave], lane);
-    if (nsplit > 1) {
+  }
+  // sum the four rows' partial weighted values (keys = r mod 4)
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float v = acc[hh][e];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      acc[hh][e] = v;
+    }
+  if (r != 0) return;
+  for (int hh = 0; hh < nh; ++hh) {
+    const int h = g * G + hgp * HG + hh;
+    const int row = (b * a.r.N + n) * a.r.Hq + h;
+    if (nsplit > 1) {  // partial (acc, m, l) for k_seq_combine
       float* part = a.part + ((int64_t)row * nsplit + split) * (D + 2);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) part[lane * DPL + e] = st.acc[e];
-      if (lane == 0) {
-        part[D] = st.m;
-        part[D + 1] = st.l;
+      for (int e = 0; e < EPL; ++e) part[c * EPL + e] = acc[hh][e];
+      if (c == 0) {
+        part[D] = l[hh] > 0.f ? m[hh] : -INFINITY;
+        part[D + 1] = l[hh];
       }
       continue;
     }
-    const bool has = vis > 0;
-    float oseq[DPL];
-    const float inv_l = has ? 1.f / st.l : 0.f;
+    const bool has = l[hh] > 0.f;
+    const float lse_seq = has ? m[hh] + logf(l[hh]) : -INFINITY;
+    const float lkg = a.lse_kg[row];
+    float lam;
+    if (lkg == -INFINITY) lam = 0.f;
+    else if (!has) lam = 1.f;
+    else lam = 1.f / (1.f + __expf(lse_seq - lkg));
+    const float inv = has ? 1.f / l[hh] : 0.f;
+    const float* okg = a.o_kg + (int64_t)row * D;
+    const int64_t ob = q_off(a.os, b, n, h);
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) oseq[e] = st.acc[e] * inv_l;
-    merge_store<E, D>(a, row, b, n, h, has ? st.m + logf(st.l) : -INFINITY, has, oseq, lane);
+    for (int e = 0; e < EPL; ++e) {
+      const int dim = c * EPL + e;
+      const float o = lam * okg[dim] + (1.f - lam) * (acc[hh][e] * inv);
+      if (a.out_dtype == kDtypeBF16) ((uint16_t*)a.out)[ob + dim] = f32_to_bf16_rne(o);
+      else ((float*)a.out)[ob + dim] = o;
+    }
+    if (a.lse_seq_out && c == 0) a.lse_seq_out[row] = lse_seq;
   }
 }
 
@@ -443,10 +483,10 @@ hipError_t launch_seq_merge(const SeqArgs& a, hipStream_t s) {
     HIKVP_DISPATCH(a.dtype, a.d, k_seq_combine, dim3(cblocks), dim3(256), 0, s, a, nsplit);
     return hipGetLastError();
   }
-  const unsigned blocks = (unsigned)(a.r.B * a.r.N * a.Hkv);
-  const int waves = a.r.G < 4 ? a.r.G : 4;
+  // decode: one wave per (b, n, KV head, group of 4 query heads [, key split])
+  const unsigned blocks = (unsigned)(a.r.B * a.r.N * a.Hkv * ((a.r.G + 3) / 4));
   const int nsplit = a.part ? a.nsplit : 1;
-  HIKVP_DISPATCH(a.dtype, a.d, k_seq_attend, dim3(blocks, (unsigned)nsplit), dim3(64 * waves), 0, s, a);
+  HIKVP_DISPATCH(a.dtype, a.d, k_seq_decode, dim3(blocks, (unsigned)nsplit), dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit <= 1) return e;
   const unsigned cblocks = (unsigned)((a.r.R + 3) / 4);
