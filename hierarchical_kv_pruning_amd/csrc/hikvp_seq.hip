@@ -74,6 +74,24 @@ struct RawElems {
   }
 };
 
+// <q, k> over a lane's EPL elements: bf16 pairs on v_dot2_f32_bf16 (products
+// exact in fp32), fp32 on FMA.
+typedef __bf16 Bf16x2 __attribute__((ext_vector_type(2)));
+template <class E, int EPL>
+__device__ inline float dot_elems(const RawElems<E, EPL>& x, const RawElems<E, EPL>& y) {
+  float d = 0.f;
+  if constexpr (E::kBytes == 2) {
+#pragma unroll
+    for (int k = 0; k < RawElems<E, EPL>::kWords; ++k)
+      d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(Bf16x2, x.w[k]), __builtin_bit_cast(Bf16x2, y.w[k]), d,
+                                          false);
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) d = fmaf(x[e], y[e], d);
+  }
+  return d;
+}
+
 template <class E, int D>
 __global__ __launch_bounds__(64) void k_seq_decode(SeqArgs a) {
   constexpr int EPL = D / 16, HG = 4, CK = 16;
@@ -90,14 +108,11 @@ __global__ __launch_bounds__(64) void k_seq_decode(SeqArgs a) {
   const int k1 = (k0 + a.split_len) < vis ? (k0 + a.split_len) : vis;
   const float scale = (float)a.r.scale;
 
-  float qf[HG][EPL];
+  RawElems<E, EPL> qr[HG];                 // queries stay packed (bf16: v_dot2 on pairs)
 #pragma unroll
   for (int hh = 0; hh < HG; ++hh) {
     const int h = g * G + hgp * HG + (hh < nh ? hh : 0);
-    RawElems<E, EPL> qr;
-    qr.load((const char*)a.r.q + (q_off(a.r.qs, b, n, h) + c * EPL) * E::kBytes);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qf[hh][e] = qr[e];
+    qr[hh].load((const char*)a.r.q + (q_off(a.r.qs, b, n, h) + c * EPL) * E::kBytes);
   }
   float m[HG], l[HG], acc[HG][EPL];
 #pragma unroll
@@ -111,14 +126,26 @@ __global__ __launch_bounds__(64) void k_seq_decode(SeqArgs a) {
     const char* kb = (const char*)a.k + ((int64_t)b * a.ks[0] + (int64_t)g * a.ks[2] + c * EPL) * E::kBytes;
     const char* vb = (const char*)a.v + ((int64_t)b * a.vs[0] + (int64_t)g * a.vs[2] + c * EPL) * E::kBytes;
     const int64_t kstep = a.ks[1] * E::kBytes, vstep = a.vs[1] * E::kBytes;
+    // chunk loads are issued one chunk ahead (key c0 + 4i + r; past the range
+    // its last key, masked)
+    RawElems<E, EPL> kn[CK / 4], vn[CK / 4];
+    auto load_chunk = [&](int c0) {
+#pragma unroll
+      for (int i = 0; i < CK / 4; ++i) {
+        const int key = min(c0 + 4 * i + r, k1 - 1);
+        kn[i].load(kb + (int64_t)key * kstep);
+        vn[i].load(vb + (int64_t)key * vstep);
+      }
+    };
+    load_chunk(k0);
     for (int c0 = k0; c0 < k1; c0 += CK) {
       RawElems<E, EPL> kf[CK / 4], vf[CK / 4];
 #pragma unroll
-      for (int i = 0; i < CK / 4; ++i) {   // key c0 + 4i + r; past the range: its last key (masked)
-        const int key = min(c0 + 4 * i + r, k1 - 1);
-        kf[i].load(kb + (int64_t)key * kstep);
-        vf[i].load(vb + (int64_t)key * vstep);
+      for (int i = 0; i < CK / 4; ++i) {
+        kf[i] = kn[i];
+        vf[i] = vn[i];
       }
+      if (c0 + CK < k1) load_chunk(c0 + CK);
       float p[CK / 4][HG];
 #pragma unroll
       for (int hh = 0; hh < HG; ++hh) {
@@ -126,9 +153,7 @@ __global__ __launch_bounds__(64) void k_seq_decode(SeqArgs a) {
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < CK / 4; ++i) {
-          float d = 0.f;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) d = fmaf(qf[hh][e], kf[i][e], d);
+          float d = dot_elems(qr[hh], kf[i]);
           d = group_sum<16>(d);
           sc[i] = (c0 + 4 * i + r < k1) ? d * scale : -INFINITY;
           mx = fmaxf(mx, sc[i]);
@@ -456,7 +481,9 @@ int seq_splits(int B, int N, int Hkv, int S) {
   // (b, 16-token tile, KV head) for the flash prefill
   const int64_t items = flash ? (int64_t)B * ((N + 15) / 16) * Hkv : (int64_t)B * N * Hkv;
   if (items <= 0 || S <= 0) return 1;
-  const int64_t target = flash ? 1024 : 8192;   // enough workgroups to fill the chip
+  // prefill: enough workgroups to fill the chip; decode: about one round of
+  // resident waves (3 per SIMD), so every wave streams one long key range
+  const int64_t target = flash ? 1024 : 3072;
   const int64_t min_keys = flash ? 64 : 128;    // keys per split at least
   int64_t want = (target + items - 1) / items;
   const int64_t maxs = (S + min_keys - 1) / min_keys;
