@@ -131,6 +131,7 @@ struct Plan {
   size_t off_mid_base, off_bcnt, off_bslot, off_bhead, off_bnext, off_blist, off_bcount, off_bovf, off_junk;
   size_t off_rcnt, off_rtot, off_rrank, off_rbase, off_rtoff, off_rtkey, off_rnt, off_rmem;
   int64_t root_tiles_max;
+  int32_t desc_per_sub, bucket_q;
 };
 
 // Candidate capacity per row at the mid level (children of K_R distinct
@@ -231,12 +232,16 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   p.off_rtkey = o;     o = align256(o + (size_t)p.root_tiles_max * 4);
   p.off_rnt = o;       o = align256(o + 4);
   p.off_rmem = o;      o = align256(o + (size_t)p.root_tiles_max * kRootTile * 8);
-  p.off_bcnt = o;      o = align256(o + (size_t)t.Hkv * (size_t)t.count[1] * 4);
-  p.off_bslot = o;     o = align256(o + (size_t)t.Hkv * (size_t)t.count[1] * 8 * kBucketSlots);
-  p.off_bhead = o;     o = align256(o + (size_t)t.Hkv * (size_t)t.count[1] * 4);
+  p.bucket_q = (int32_t)(((size_t)t.Hkv * (size_t)t.count[1] + 63) / 64);
+  const size_t nbix = (size_t)p.bucket_q * 64;
+  p.off_bcnt = o;      o = align256(o + nbix * 4);
+  p.off_bslot = o;     o = align256(o + nbix * 8 * kBucketSlots);
+  p.off_bhead = o;     o = align256(o + nbix * 4);
   p.off_bnext = o;     o = align256(o + R * (size_t)p.K[1] * 4);
-  p.off_blist = o;     o = align256(o + R * (size_t)p.K[1] * 16);
-  p.off_bcount = o;    o = align256(o + 8);
+  // chunk c of 64 selections appends to sub-list c mod kDescSub
+  p.desc_per_sub = (int32_t)(((R * (size_t)p.K[1] + 63) / 64 + kDescSub - 1) / kDescSub * 64);
+  p.off_blist = o;     o = align256(o + (size_t)p.desc_per_sub * kDescSub * 16);
+  p.off_bcount = o;    o = align256(o + (kDescSub + 1) * 4);
   p.off_bovf = o;      o = align256(o + (R * (size_t)p.K[1] / (kBucketSlots + 1) + 1) * 4);
   p.off_junk = o;      o = align256(o + (size_t)kJunkSlots * 64);
   p.off_okg = o;       o = align256(o + R * (size_t)t.d * 4);
@@ -455,6 +460,8 @@ atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vie
   a.bucket_next = (int32_t*)(ws + p.off_bnext);
   a.bucket_desc = (int4*)(ws + p.off_blist);
   a.bucket_count = (int32_t*)(ws + p.off_bcount);
+  a.desc_per_sub = p.desc_per_sub;
+  a.bucket_q = p.bucket_q;
   a.bucket_ovf = (int32_t*)(ws + p.off_bovf);
   a.junk = (float*)(ws + p.off_junk);
   a.o_kg = o_kg;

@@ -12,6 +12,7 @@ constexpr int kBucketSlots = 32;  // members of a (head, mid) bucket stored with
 constexpr int kJunkSlots = 1024;  // per-wave sinks for masked-off score stores
 constexpr int kRootTile = 16;     // member rows per mid-GEMM work item
 constexpr int kRootSub = 16;      // counters per (head, root) group, picked by token
+constexpr int kDescSub = 64;      // bucket descriptor sub-lists, picked by 64-selection chunk
 constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBF16 = 1;
 
@@ -59,17 +60,30 @@ struct StepArgs {
   int32_t* root_ntiles;       // [1] tiles in use
   int2* root_members;         // [root_tiles_max * kRootTile] (row, first mid slot)
   int64_t root_tiles_max;     // R*K[0]/kRootTile + Hkv*M_R
-  int32_t* bucket_cnt;        // [Hkv * M_I] rows that selected the (head, mid)
-  int2* bucket_slot;          // [Hkv * M_I * kBucketSlots] first members: (row, first leaf slot)
-  int32_t* bucket_head;       // [Hkv * M_I] overflow members: list head, -1 none
+  // (head, mid) bucket arrays are indexed by bucket_index(key) (below), which
+  // spreads neighbouring mids (siblings, selected together) over cache lines
+  int32_t* bucket_cnt;        // [64 * bucket_q] rows that selected the (head, mid)
+  int2* bucket_slot;          // [64 * bucket_q * kBucketSlots] first members: (row, first leaf slot)
+  int32_t* bucket_head;       // [64 * bucket_q] overflow members: list head, -1 none
   int32_t* bucket_next;       // [R * K[1]] next overflow entry of the same (head, mid)
-  int4* bucket_desc;          // [R * K[1]] distinct (head, mid): key g*M_I+mid, fanout, first leaf element (lo, hi)
-  int32_t* bucket_count;      // [2] distinct keys, keys with more than kBucketSlots rows
+  int4* bucket_desc;          // [kDescSub, desc_per_sub] distinct (head, mid): key g*M_I+mid, fanout,
+                              // first leaf element (lo, hi); sub-list s holds buckets first
+                              // registered by a chunk c of 64 selections with c mod kDescSub = s
+  int32_t* bucket_count;      // [kDescSub + 1] descriptors per sub-list; [kDescSub]: keys with more
+                              // than kBucketSlots rows
+  int32_t desc_per_sub;       // ceil(ceil(R*K[1] / 64) / kDescSub) * 64: a sub-list's capacity
+  int32_t bucket_q;           // ceil(Hkv * M_I / 64)
   float* junk;                // [kJunkSlots * 16] write-only sinks for masked-off score lanes
-  int32_t* bucket_ovf;        // [R * K[1] / (kBucketSlots + 1) + 1] keys with overflow members
+  int32_t* bucket_ovf;        // [R * K[1] / (kBucketSlots + 1) + 1] keys (g*M_I + mid) with overflow members
   float* o_kg;                // [R, d] softmax-weighted leaf values (fp32)
   float* lse_kg;              // [R] log-sum-exp of the selected leaf logits
 };
+
+// Bucket array index of key = g*M_I + mid: a bijective transpose of [0, 64*q)
+// (consecutive keys land 4*q bytes apart).
+__device__ inline int64_t bucket_index(const StepArgs& a, int64_t key) {
+  return (key & 63) * a.bucket_q + (key >> 6);
+}
 
 struct SeqArgs {
   RowsDev r;
@@ -104,7 +118,7 @@ hipError_t launch_root(const StepArgs& a, hipStream_t s);
 hipError_t launch_root_groups(const StepArgs& a, hipStream_t s);  // rows by selected (head, root)
 hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s);
 hipError_t launch_mid_select(const StepArgs& a, hipStream_t s);
-hipError_t launch_leaf_link(const StepArgs& a, hipStream_t s);    // rows by selected (head, mid)
+hipError_t launch_leaf_link(const StepArgs& a, hipStream_t s);    // rows grouped by selected (head, mid)
 hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s);   // buckets' first kBucketSlots members
 hipError_t launch_leaf_overflow(const StepArgs& a, hipStream_t s);  // members past kBucketSlots
 hipError_t launch_leaf_select(const StepArgs& a, hipStream_t s);

@@ -20,7 +20,7 @@
 //               candidate slots of the workspace.
 //   k_mid_select   one wave per row (a workgroup per row for long candidate
 //               lists): Top-K_I over the row's mid scores.
-//   k_bucket_link  link the rows that selected each distinct (KV head, mid).
+//   k_bucket_link  registers each selection in its (KV head, mid) bucket.
 //   k_leaf_score   one wave per bucket: streams the mid's leaf span once (it is
 //               contiguous in the head-major layout) and writes the scores of
 //               every member row into that row's candidate slots.
@@ -407,50 +407,62 @@ __global__ void k_clear(StepArgs a, int64_t nkeys1, int64_t nkeys0) {
   }
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nkeys0 * kRootSub; i += stride)
     a.root_cnt[i] = 0;
-  if (blockIdx.x == 0 && threadIdx.x < 2) a.bucket_count[threadIdx.x] = 0;
+  if (blockIdx.x == 0 && threadIdx.x <= kDescSub) a.bucket_count[threadIdx.x] = 0;
 }
 
-// Grid-stride over the (row, mid) selections in wave-uniform steps so that a
-// wave appends its new descriptors with one atomic.
+// Register selection e = (row, mid) in its (KV head, mid) bucket, given its
+// rank from the bucket's counter (-1: nothing to register): the first
+// kBucketSlots members in fixed slots (row, first leaf slot), later ones in
+// the bucket's list; a new bucket appends its 16-byte descriptor (bucket
+// index, fanout, first leaf element) to descriptor sub-list `sub`, one atomic
+// per wave.  All lanes of a wave call it.
+__device__ inline void register_in_bucket(const StepArgs& a, int64_t e, int row, int sub, int g, int64_t key,
+                                          int rank, int64_t f0, int fan, int slot_base, int lane) {
+  const uint64_t fresh = __ballot(rank == 0);
+  if (fresh) {
+    int got = 0;
+    const int leader = __builtin_ctzll(fresh);
+    if (lane == leader) got = atomicAdd(&a.bucket_count[sub], __popcll(fresh));
+    const int64_t base = (int64_t)sub * a.desc_per_sub + __builtin_amdgcn_readlane(got, leader);
+    if (rank == 0) {
+      const int below = __popcll(fresh & ((1ull << lane) - 1ull));
+      const int64_t first = (int64_t)g * a.t.hs[2] + f0 * a.t.rs[2];
+      a.bucket_desc[base + below] = make_int4((int)bucket_index(a, key), fan, (int)(uint32_t)first,
+                                              (int)(first >> 32));
+    }
+  }
+  if (rank < 0) return;
+  const int64_t bix = bucket_index(a, key);
+  if (rank < kBucketSlots) {
+    a.bucket_slot[bix * kBucketSlots + rank] = make_int2(row, slot_base);
+  } else {
+    a.bucket_next[e] = atomicExch(&a.bucket_head[bix], (int)e);
+    if (rank == kBucketSlots) a.bucket_ovf[atomicAdd(&a.bucket_count[kDescSub], 1)] = (int)key;
+  }
+}
+
+// One thread per (row, selected mid), grid-stride in wave-uniform chunks of
+// 64 selections: their rank atomics are in flight together, and chunk c
+// appends its new descriptors to sub-list c mod kDescSub (one counter for all
+// chunks would serialise one atomic per chunk on one address).  A sub-list
+// receives at most ceil(ceil(n/64)/kDescSub) chunks, 64 entries each.
 __global__ void k_bucket_link(StepArgs a) {
   const int K1 = a.K[1];
   const int64_t n = (int64_t)a.r.R * K1;
-  const int MI = (int)a.t.count[1];
   const int64_t* off1 = a.t.off[1];
   const int lane = threadIdx.x & 63;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t e0 = blockIdx.x * (int64_t)blockDim.x + (threadIdx.x & ~63); e0 < n; e0 += stride) {
+    const int sub = (int)((e0 >> 6) % kDescSub);
     const int64_t e = e0 + lane;
     const int mid = e < n ? a.sel[1][e] : -1;
-    int rank = -1, row = 0;
-    int64_t key = 0;
-    if (mid >= 0) {
-      row = (int)(e / K1);
-      const int g = (row % a.r.Hq) / a.r.G;
-      key = (int64_t)g * MI + mid;
-      rank = atomicAdd(&a.bucket_cnt[key], 1);
-    }
-    const uint64_t fresh = __ballot(rank == 0);
-    if (fresh) {
-      int base = 0;
-      const int leader = __builtin_ctzll(fresh);
-      if (lane == leader) base = atomicAdd(&a.bucket_count[0], __popcll(fresh));
-      base = __builtin_amdgcn_readlane(base, leader);
-      if (rank == 0) {
-        const int below = __popcll(fresh & ((1ull << lane) - 1ull));
-        const int64_t f0 = off1[mid];
-        const int64_t first = (int64_t)(key / MI) * a.t.hs[2] + f0 * a.t.rs[2];
-        a.bucket_desc[base + below] = make_int4((int)key, (int)(off1[mid + 1] - f0), (int)(uint32_t)first,
-                                                (int)(first >> 32));
-      }
-    }
-    if (rank < 0) continue;
-    if (rank < kBucketSlots) {
-      a.bucket_slot[key * kBucketSlots + rank] = make_int2(row, a.mid_base[e]);
-    } else {
-      a.bucket_next[e] = atomicExch(&a.bucket_head[key], (int)e);
-      if (rank == kBucketSlots) a.bucket_ovf[atomicAdd(&a.bucket_count[1], 1)] = (int)key;
-    }
+    const int row = (int)(e / K1);
+    const int g = (row % a.r.Hq) / a.r.G;
+    const int64_t key = (int64_t)g * a.t.count[1] + (mid >= 0 ? mid : 0);
+    const int rank = mid >= 0 ? atomicAdd(&a.bucket_cnt[bucket_index(a, key)], 1) : -1;
+    const int64_t f0 = mid >= 0 ? off1[mid] : 0;
+    const int fan = mid >= 0 ? (int)(off1[mid + 1] - f0) : 0;
+    register_in_bucket(a, e, row, sub, g, key, rank, f0, fan, mid >= 0 ? a.mid_base[e] : 0, lane);
   }
 }
 
@@ -509,16 +521,25 @@ __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
   const bool owner = lane < 32 && (lane & 15) < 8;   // holds combined scores
   float* const junk = a.junk + ((blockIdx.x * nwave + wave) % kJunkSlots) * 16;
   static_assert(TU % 4 == 0 && TU <= 16, "junk slot holds 16 floats");
-  const int nb = a.bucket_count[0];
+  // descriptor v of the concatenated sub-lists: lane s holds sub-list s's
+  // count and its inclusive prefix
+  const int scnt = a.bucket_count[lane];  // lane < kDescSub = 64
+  const int sincl = wave_incl_sum(scnt);
+  const int nb = __builtin_amdgcn_readlane(sincl, 63);
+  auto desc_at = [&](int v) {
+    const int sub = __popcll(__ballot(sincl <= v));
+    const int first = __builtin_amdgcn_readlane(sincl - scnt, sub);
+    return a.bucket_desc[(int64_t)sub * a.desc_per_sub + (v - first)];
+  };
   const char* kbase = (const char*)a.t.key[2];
   const int64_t rsb = a.t.rs[2] * E::kBytes;
   const int stride = gridDim.x * nwave;
   int v = blockIdx.x * nwave + wave;
-  int4 cur = v < nb ? a.bucket_desc[v] : make_int4(0, 0, 0, 0);
+  int4 cur = v < nb ? desc_at(v) : make_int4(0, 0, 0, 0);
   while (v < nb) {
     const int vn = v + stride;
-    const int4 nxt = vn < nb ? a.bucket_desc[vn] : make_int4(0, 0, 0, 0);  // prefetch
-    const int key = cur.x, F = cur.y;
+    const int4 nxt = vn < nb ? desc_at(vn) : make_int4(0, 0, 0, 0);  // prefetch
+    const int key = cur.x, F = cur.y;   // key: bucket array index
     const int64_t first = (int64_t)(uint32_t)cur.z | ((int64_t)cur.w << 32);
     const char* kp = (const char*)kbase + first * E::kBytes + split_off(lane, 0);  // + key * rsb
     int cnt = a.bucket_cnt[key];
@@ -612,17 +633,18 @@ __global__ __launch_bounds__(256) void k_leaf_score_overflow(StepArgs a) {
   constexpr int EPV = E::kEPV, LPK = D / EPV, MB = 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
   const int j = lane % LPK;
-  const int nov = a.bucket_count[1];
+  const int nov = a.bucket_count[kDescSub];
   const int K1 = a.K[1];
   const int MI = (int)a.t.count[1];
   const char* kbase = (const char*)a.t.key[2];
   for (int v = blockIdx.x * nwave + wave; v < nov; v += gridDim.x * nwave) {
     const int key = a.bucket_ovf[v];
     const int g = key / MI, mid = key % MI;
+    const int64_t bix = bucket_index(a, key);
     const int64_t f0 = a.t.off[1][mid];
     const int F = (int)(a.t.off[1][mid + 1] - f0);
     const char* kb = kbase + ((int64_t)g * a.t.hs[2] + f0 * a.t.rs[2]) * E::kBytes;
-    int e = a.bucket_head[key];
+    int e = a.bucket_head[bix];
     while (e != -1) {  // wave-uniform walk
       int rows[MB], bases[MB];
       float qf[MB][EPV];
@@ -844,7 +866,7 @@ hipError_t launch_mid_select(const StepArgs& a, hipStream_t s) {
 
 hipError_t launch_clear(const StepArgs& a, hipStream_t s) {
   if (a.r.R <= 0) return hipSuccess;
-  const int64_t nkeys1 = (int64_t)a.t.Hkv * a.t.count[1], nkeys0 = (int64_t)a.t.Hkv * a.t.count[0];
+  const int64_t nkeys1 = (int64_t)a.bucket_q * 64, nkeys0 = (int64_t)a.t.Hkv * a.t.count[0];
   int64_t blocks = ((nkeys1 > nkeys0 ? nkeys1 : nkeys0) + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
