@@ -89,7 +89,8 @@ def algorithmic_bytes(case, sel):
         "leaf_score_stream": leafk_b,
         "leaf_score_overflow": 0,
         "leaf_topk_kg_attention": leafv_b,
-        "seq_attention_merge": seq_b + out_b,
+        "seq_attention": seq_b,
+        "seq_split_combine": out_b,
         "_total": roots_b + mids_b + leafk_b + leafv_b + seq_b + q_b + out_b,
         "_parts": dict(roots=roots_b, mids=mids_b, leaf_keys=leafk_b, leaf_values=leafv_b,
                        sequence_kv=seq_b, q=q_b, out=out_b),

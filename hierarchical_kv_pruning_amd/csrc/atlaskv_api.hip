@@ -271,7 +271,7 @@ const char* atlaskv_version(void) { return "atlaskv-mi355x 0.1 (gfx950)"; }
 
 static const char* const kPhaseNames[] = {"root_score_topk", "mid_bucket_gemm", "mid_topk",
                                           "leaf_bucket_link", "leaf_score_stream", "leaf_score_overflow",
-                                          "leaf_topk_kg_attention", "seq_attention_merge"};
+                                          "leaf_topk_kg_attention", "seq_attention", "seq_split_combine"};
 static const int kPhases = (int)(sizeof kPhaseNames / sizeof kPhaseNames[0]);
 
 int32_t atlaskv_phase_count(void) { return kPhases; }
@@ -499,7 +499,8 @@ atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vie
     sa.nsplit = p.nsplit;
     sa.part = p.nsplit > 1 ? (float*)(ws + p.off_part) : nullptr;
     sa.split_len = p.nsplit > 1 ? seq_split_len(p.S, p.nsplit) : (p.S > 0 ? p.S : 1);
-    e = mark(launch_seq_merge(sa, s));
+    e = mark(launch_seq_attend(sa, s));
+    if (e == hipSuccess) e = mark(launch_seq_combine(sa, s));
   }
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return ATLASKV_OK;

@@ -122,7 +122,8 @@ hipError_t launch_leaf_link(const StepArgs& a, hipStream_t s);    // rows groupe
 hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s);   // buckets' first kBucketSlots members
 hipError_t launch_leaf_overflow(const StepArgs& a, hipStream_t s);  // members past kBucketSlots
 hipError_t launch_leaf_select(const StepArgs& a, hipStream_t s);
-hipError_t launch_seq_merge(const SeqArgs& a, hipStream_t s);
+hipError_t launch_seq_attend(const SeqArgs& a, hipStream_t s);   // + λ merge when keys are not split
+hipError_t launch_seq_combine(const SeqArgs& a, hipStream_t s);  // split partials: LSE combine + λ merge
 int seq_splits(int B, int N, int Hkv, int S);   // key splits of the sequence attention
 int seq_split_len(int S, int nsplit);
 

@@ -496,26 +496,25 @@ int seq_split_len(int S, int nsplit) {
   return (len + 63) / 64 * 64;
 }
 
-hipError_t launch_seq_merge(const SeqArgs& a, hipStream_t s) {
+hipError_t launch_seq_attend(const SeqArgs& a, hipStream_t s) {
   if (a.r.R <= 0) return hipSuccess;
+  const int nsplit = a.part ? a.nsplit : 1;
   if (a.k && a.r.N >= 16) {
     // prefill: MFMA flash attention per (b, KV head, 16-token tile [, key split])
     const unsigned blocks = (unsigned)(a.r.B * ((a.r.N + 15) / 16) * a.Hkv);
     const int waves = a.r.G < 4 ? a.r.G : 4;
-    const int nsplit = a.part ? a.nsplit : 1;
     HIKVP_DISPATCH(a.dtype, a.d, k_seq_flash, dim3(blocks, (unsigned)nsplit), dim3(64 * waves), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || nsplit <= 1) return e;
-    const unsigned cblocks = (unsigned)((a.r.R + 3) / 4);
-    HIKVP_DISPATCH(a.dtype, a.d, k_seq_combine, dim3(cblocks), dim3(256), 0, s, a, nsplit);
     return hipGetLastError();
   }
   // decode: one wave per (b, n, KV head, group of 4 query heads [, key split])
   const unsigned blocks = (unsigned)(a.r.B * a.r.N * a.Hkv * ((a.r.G + 3) / 4));
-  const int nsplit = a.part ? a.nsplit : 1;
   HIKVP_DISPATCH(a.dtype, a.d, k_seq_decode, dim3(blocks, (unsigned)nsplit), dim3(64), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nsplit <= 1) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_seq_combine(const SeqArgs& a, hipStream_t s) {
+  const int nsplit = a.part ? a.nsplit : 1;
+  if (a.r.R <= 0 || nsplit <= 1) return hipSuccess;  // unsplit rows were merged by the attention kernel
   const unsigned cblocks = (unsigned)((a.r.R + 3) / 4);
   HIKVP_DISPATCH(a.dtype, a.d, k_seq_combine, dim3(cblocks), dim3(256), 0, s, a, nsplit);
   return hipGetLastError();

@@ -176,9 +176,10 @@ def test_described_view_cannot_run(lib):
 def test_phase_names_in_launch_order(lib):
     """The timing phases follow the descent: roots (with their row grouping),
     mid GEMM, mid Top-K, leaf bucket link, leaf scoring (first members, then
-    overflow members), leaf Top-K with the KG softmax, sequence attention."""
+    overflow members), leaf Top-K with the KG softmax, sequence attention (with
+    the merge when keys are not split), the combine of key splits."""
     assert atlaskv.phase_names() == [
         "root_score_topk", "mid_bucket_gemm", "mid_topk", "leaf_bucket_link", "leaf_score_stream",
-        "leaf_score_overflow", "leaf_topk_kg_attention", "seq_attention_merge"]
+        "leaf_score_overflow", "leaf_topk_kg_attention", "seq_attention", "seq_split_combine"]
     assert lib.atlaskv_phase_name(-1) is None
     assert lib.atlaskv_phase_name(lib.atlaskv_phase_count()) is None
