@@ -502,7 +502,7 @@ struct RegScores {
 // Returns the count selected (min(K, n)); out_node/out_logit hold the
 // selection sorted by candidate slot.  All NT threads must call it; S.qrow
 // must hold the KG query row.
-template <class E, int D, int NT, class Src>
+template <class E, int D, int NT, class Src, bool kShortLists = false>
 __device__ int select_topk(const Src& src, int n, int K, double err2, double scale,
                            const SlotMap& map, const KeyRows& kr, const SelWork& S,
                            int* out_node, float* out_logit, int tid) {
@@ -529,7 +529,35 @@ __device__ int select_topk(const Src& src, int n, int K, double err2, double sca
   int first_pass = 0;
   if (tid == 0) { S.ctl[2] = 0; S.ctl[3] = 0; }
   int* myhist = S.hist + (tid >> 6) * 256;
-  {
+  if constexpr (kShortLists && NT == 64) {
+    if (K <= 16 && n <= 256) {
+      // short list, small K (a few scores per lane): the K-th largest key by
+      // repeated maxima, each round the largest key below the previous
+      // round's, its copies counted (ties leave together); no LDS, no
+      // barriers.  Sets the full 32-bit prefix: the radix passes are skipped.
+      uint32_t prev = 0xffffffffu;  // above every finite score's key
+      int cum = 0;
+      for (int r = 0; r <= K; ++r) {
+        uint32_t lm = 0;
+        int lc = 0;
+        src.each(n, tid, [&](int, float f) {
+          const uint32_t u = ord_key(f);
+          lc += (u == prev) ? 1 : 0;
+          if (u < prev) lm = max(lm, u);
+        });
+        lm = wave_max_u(lm);
+        if (r > 0) {
+          cum += wave_sum_i(lc);   // copies of the previous round's key
+          if (cum >= K) break;     // prefix holds the K-th largest key
+        }
+        prefix = lm;
+        prev = lm;
+      }
+      first_pass = 4;
+      wave_sync();  // the classification counters zeroed above, before use
+    }
+  }
+  if (first_pass == 0) {
     uint32_t tmax = 0;
     src.each(n, tid, [&](int, float f) { tmax = max(tmax, ord_key(f) >> 24); });
     tmax = wave_max_u(tmax);

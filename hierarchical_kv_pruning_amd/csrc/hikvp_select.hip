@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void k_root(StepArgs a, size_t wave_bytes, int
   score_run<E, D, 4>(qf, kb, rsb, ident, MR, sc, 0, 1, lane);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   wave_sync();
-  const int k = select_topk<E, D, 64>(MemScores<64>{sc}, MR, K, twice_err_bound<D>(qnorm, a.t.norm[g]),
+  const int k = select_topk<E, D, 64, MemScores<64>, true>(MemScores<64>{sc}, MR, K, twice_err_bound<D>(qnorm, a.t.norm[g]),
                                       a.r.scale, ident, KeyRows{kb, rsb}, W.sel, W.out_node, W.out_logit,
                                       lane);
   int32_t* out = a.sel[0] + (int64_t)row * K;
