@@ -96,6 +96,18 @@ def test_sequence_longer_than_queries_and_gqa_8():
     _check(_small(seed=8, N=17, S_kv=200, Hq=16, Hkv=2, dtype="bf16"))
 
 
+@pytest.mark.parametrize("N,S_kv,Hq,Hkv", [
+    (1, 300, 16, 2),     # decode, 8 query heads per KV head: two groups of 4 per wave
+    (3, 50, 6, 2),       # 3 tokens, 3 heads per KV head: a partial group
+    (2, 9, 10, 2),       # 5 heads per KV head (4 + 1), keys shorter than one chunk
+    (15, 700, 8, 1),     # the longest query block on the decode path, keys split
+])
+def test_decode_head_groups(N, S_kv, Hq, Hkv):
+    """Query blocks below 16 tokens take the decode kernel, which handles a KV
+    head's query heads in groups of four per wave."""
+    _check(_small(seed=40 + N, dtype="bf16", N=N, S_kv=S_kv, Hq=Hq, Hkv=Hkv, B=3))
+
+
 def test_single_head_group():
     _check(_small(seed=9, Hq=3, Hkv=3, dtype="bf16"))
 
