@@ -10,7 +10,11 @@ compulsory HBM bytes and their rate against the 8 TB/s peak, the roofline of
 the dominant kernel (algorithmic bytes / live HIP-event duration), and the
 fp64 CPU oracle's rate on a bounded row sample of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--workload m1e6]
+  python bench.py [--steps K] [--warmup W] [--workload m1e6] [--tree-placement hbm|host-leaves]
+
+With --tree-placement host-leaves the leaf keys and values sit in pinned host
+memory and the kernels read the selected spans over the host link; the
+roofline is then the link's (PCIe 5.0 x16).
 """
 import argparse
 import hashlib
@@ -29,6 +33,7 @@ sys.path.insert(0, ROOT)
 from hierarchical_kv_pruning_amd import atlaskv, synth  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, AMD's published figure
+PEAK_LINK_GBPS = 64.0           # MI355X host interface, PCIe 5.0 x16, one direction (published)
 KERNEL_SOURCES = [os.path.join(ROOT, "hierarchical_kv_pruning_amd", "csrc", f)
                   for f in ("hikvp_device.h", "hikvp_select.hip", "hikvp_seq.hip")]
 PROFILES = os.path.join(ROOT, "profiles")
@@ -182,6 +187,9 @@ def main():
                     help="extra steps timed one by one after evicting the 256 MB MALL")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--tree-placement", default="hbm", choices=["hbm", "host-leaves"],
+                    help="host-leaves: leaf keys and values in pinned host memory, read by the "
+                         "kernels over the host link (roots, mids, offsets stay in HBM)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -196,6 +204,29 @@ def main():
     atlaskv.lib()
     log(f"workload {args.workload}: generating on {torch.cuda.get_device_name(0)}")
     case = synth.make_case(args.workload, device=dev)
+    link_copy_gbps = None
+    if args.tree_placement == "host-leaves":
+        log("moving leaf keys and values to pinned host memory")
+        for f in ("leaf_k", "leaf_v"):
+            t = getattr(case, f)
+            h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+            h.copy_(t)
+            setattr(case, f, h)
+            del t, h
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        # the link's copy-engine ceiling: 1 GiB pinned host -> device
+        src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+        dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src, non_blocking=True)
+        b.record()
+        torch.cuda.synchronize()
+        link_copy_gbps = (1 << 30) / (a.elapsed_time(b) * 1e-3) / 1e9
+        del src, dst
     tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
     ws = atlaskv.alloc_workspace(tree, case.q, case.seq_k, case.K)
     out = torch.empty_like(case.q)
@@ -264,7 +295,8 @@ def main():
     tokens = case.B * case.N
     dom = max((p for p in phases if p in ab), key=lambda p: phase_ms[p])
     achieved = ab[dom] / (phase_ms[dom] * 1e-3) / 1e9
-    traffic = read_traffic(dom, case.name)
+    on_host = args.tree_placement == "host-leaves"
+    traffic = None if on_host else read_traffic(dom, case.name)
     path_gbps = ab["_total"] / (ms_per_step * 1e-3) / 1e9
 
     line = {
@@ -277,7 +309,8 @@ def main():
         "dtype": case.dtype, "data": "synthetic (seeded clustered-Gaussian key tree, Gaussian values, queries and sequence K/V)",
         "config": {"workload": case.name, "B": case.B, "N": case.N, "S_kv": case.S_kv, "Hq": case.Hq,
                    "Hkv": case.Hkv, "d": case.d, "tree": [case.M_R, case.M_I, case.M], "K": list(case.K),
-                   "tokens_per_step": tokens, "parallelism": "single GPU"},
+                   "tokens_per_step": tokens, "parallelism": "single GPU",
+                   "tree_placement": args.tree_placement},
         "path_hbm": {"compulsory_bytes": ab["_total"], "achieved_gbps": path_gbps,
                      "frac_of_peak": path_gbps / PEAK_HBM_GBPS, "parts": ab["_parts"],
                      "cold_ms_per_step": cold},
@@ -287,6 +320,13 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": ab[dom]},
         "cpu_baseline": None,
     }
+    if on_host:
+        # leaf keys and values cross the host link; the dominant kernel is bound by it
+        peak = PEAK_LINK_GBPS
+        line["roofline"].update(bound="host_link", peak=peak, frac=achieved / peak)
+        link_b = ab["_parts"]["leaf_keys"] + ab["_parts"]["leaf_values"]
+        line["host_link"] = {"bytes": link_b, "achieved_gbps": link_b / (ms_per_step * 1e-3) / 1e9,
+                             "peak_gbps": peak, "copy_engine_gbps": link_copy_gbps}
     if not args.no_cpu_baseline:
         log(f"cpu baseline (~{args.cpu_seconds:.0f} s of oracle time)")
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

@@ -25,7 +25,8 @@ _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 # every exported symbol of include/atlaskv.h
 EXPORTS = ["atlaskv_build_tree_view", "atlaskv_destroy_tree_view", "atlaskv_tree_view_set_workspace",
            "atlaskv_hikvp_workspace_size", "atlaskv_hikvp_attend", "atlaskv_hikvp_attend_ex",
-           "atlaskv_check_args", "atlaskv_tree_view_describe", "atlaskv_phase_count",
+           "atlaskv_check_args", "atlaskv_tree_view_describe", "atlaskv_tree_view_placement",
+           "atlaskv_phase_count",
            "atlaskv_phase_name", "atlaskv_last_error", "atlaskv_version"]
 
 
@@ -75,6 +76,7 @@ def lib():
         L.atlaskv_check_args.argtypes = [T, ctypes.c_void_p, T, T, i32x3, T, P(AttendOpts)]
         L.atlaskv_tree_view_describe.argtypes = [T, T, T, T, ctypes.c_int64, ctypes.c_int64,
                                                  P(ctypes.c_void_p)]
+        L.atlaskv_tree_view_placement.argtypes = [ctypes.c_void_p]
         for name in EXPORTS[:-4]:
             getattr(L, name).restype = ctypes.c_int
         L.atlaskv_phase_count.restype = ctypes.c_int32
@@ -129,16 +131,21 @@ class TreeView:
         self._keep = (root_k, mid_k, leaf_k, leaf_v, root_child_off, mid_child_off)
         for off in (root_child_off, mid_child_off):
             if off.dtype != torch.int64 or not off.is_contiguous():
-                raise TypeError("child offsets must be contiguous int64 device tensors")
+                raise TypeError("child offsets must be contiguous int64 tensors")
+        # any tree array may be pinned host memory; the view runs on the device of
+        # its device-resident arrays (else the current device)
+        dev = next((t.device for t in self._keep if t.is_cuda), None)
+        if dev is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
         self.handle = ctypes.c_void_p()
         self._descs = [describe(t) for t in (root_k, mid_k, leaf_k, leaf_v)]
         st = lib().atlaskv_build_tree_view(*[ctypes.byref(x) for x in self._descs],
                                            ctypes.c_void_p(root_child_off.data_ptr()),
                                            ctypes.c_void_p(mid_child_off.data_ptr()),
-                                           _stream_handle(stream, root_k.device),
+                                           _stream_handle(stream, dev),
                                            ctypes.byref(self.handle))
         _raise(st)
-        self.device = root_k.device
+        self.device = dev
         self._workspace = None
 
     @classmethod
@@ -154,6 +161,12 @@ class TreeView:
         self.device = root_k.device
         self._workspace = None
         return self
+
+    @property
+    def placement(self):
+        """atlaskv_tree_view_placement: bit i set when tree array i (root_k,
+        mid_k, leaf_k, leaf_v, root offsets, mid offsets) is pinned host memory."""
+        return lib().atlaskv_tree_view_placement(self.handle)
 
     def set_workspace(self, ws):
         """atlaskv_tree_view_set_workspace with a uint8 device tensor (None detaches)."""

@@ -28,6 +28,7 @@ struct atlaskv_tree_view_s {
   void* workspace;
   size_t workspace_bytes;
   int described_only;
+  int host_mask;               // bit i: tree tensor i (root_k, mid_k, leaf_k, leaf_v) in pinned host memory
 };
 
 namespace {
@@ -120,6 +121,39 @@ void fill_tree(TreeDev& t, const atlaskv_tensor* root_k, const atlaskv_tensor* m
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// The address kernels on the current device use for `p`: device memory of
+// this device as is, pinned host memory through its device mapping (the
+// kernels then read it over the host link).  Pageable host memory and memory
+// of another device are refused.  *host is set when `p` is host memory.
+atlaskv_status device_address(const void* p, const char* name, const void** dev, int* host) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipPointerAttribute_t at;
+  e = hipPointerGetAttributes(&at, p);
+  if (e != hipSuccess || at.type == hipMemoryTypeUnregistered) {
+    if (e != hipSuccess) (void)hipGetLastError();  // leave no pending error for the caller's next call
+    return fail(ATLASKV_ERR_UNSUPPORTED,
+                "%s is neither device memory nor pinned host memory (pageable host memory "
+                "cannot be read by the kernels; allocate it pinned)", name);
+  }
+  if (at.type == hipMemoryTypeHost) {
+    // the mapping may be reported for the allocation's start or for `p` itself:
+    // keep p's offset from the reported host address either way
+    *dev = at.devicePointer && at.hostPointer
+               ? (const void*)((const char*)at.devicePointer + ((const char*)p - (const char*)at.hostPointer))
+               : p;
+    *host = 1;
+    return ATLASKV_OK;
+  }
+  if (at.type == hipMemoryTypeDevice && at.device != cur)
+    return fail(ATLASKV_ERR_UNSUPPORTED, "%s is memory of device %d, the current device is %d", name,
+                at.device, cur);
+  *dev = p;
+  *host = 0;
+  return ATLASKV_OK;
+}
 
 struct Plan {
   int B, N, Hq, S, R, G;
@@ -289,8 +323,23 @@ atlaskv_status atlaskv_build_tree_view(const atlaskv_tensor* root_k, const atlas
   atlaskv_tree_view_s* v = (atlaskv_tree_view_s*)calloc(1, sizeof(atlaskv_tree_view_s));
   if (!v) return fail(ATLASKV_ERR_HIP, "host allocation failed");
   fill_tree(v->dev, root_k, mid_k, leaf_k, leaf_v);
-  v->dev.off[0] = root_child_off;
-  v->dev.off[1] = mid_child_off;
+  {
+    const void* given[6] = {root_k->data, mid_k->data, leaf_k->data, leaf_v->data, root_child_off,
+                            mid_child_off};
+    static const char* const names[6] = {"root_k", "mid_k", "leaf_k", "leaf_v", "root_child_off",
+                                         "mid_child_off"};
+    const void* addr[6];
+    for (int i = 0; i < 6; ++i) {
+      int host = 0;
+      st = device_address(given[i], names[i], &addr[i], &host);
+      if (st) { free(v); return st; }
+      if (host) v->host_mask |= 1 << i;
+    }
+    for (int i = 0; i < 3; ++i) v->dev.key[i] = addr[i];
+    v->dev.leaf_v = addr[3];
+    v->dev.off[0] = (const int64_t*)addr[4];
+    v->dev.off[1] = (const int64_t*)addr[5];
+  }
   v->stream = (hipStream_t)stream;
   const int Hkv = v->dev.Hkv;
   const size_t stats_bytes = offsetof(BuildStats, norm_bits) + sizeof(unsigned int) * 3 * (size_t)Hkv;
@@ -300,8 +349,8 @@ atlaskv_status atlaskv_build_tree_view(const atlaskv_tensor* root_k, const atlas
   if (!host) { (void)hipFree(v->stats); free(v); return fail(ATLASKV_ERR_HIP, "host allocation failed"); }
   hipStream_t s = v->stream;
   e = hipMemcpyAsync(v->stats, host, stats_bytes, hipMemcpyHostToDevice, s);
-  if (e == hipSuccess) e = launch_validate(root_child_off, v->dev.count[0], v->dev.count[1], 0, v->stats, s);
-  if (e == hipSuccess) e = launch_validate(mid_child_off, v->dev.count[1], v->dev.count[2], 1, v->stats, s);
+  if (e == hipSuccess) e = launch_validate(v->dev.off[0], v->dev.count[0], v->dev.count[1], 0, v->stats, s);
+  if (e == hipSuccess) e = launch_validate(v->dev.off[1], v->dev.count[1], v->dev.count[2], 1, v->stats, s);
   for (int lev = 0; lev < 3 && e == hipSuccess; ++lev)
     e = launch_key_norms(v->dev.key[lev], v->dev.dtype, v->dev.d, Hkv, v->dev.count[lev], v->dev.hs[lev],
                          v->dev.rs[lev], v->stats->norm_bits + (size_t)lev * Hkv, s);
@@ -347,6 +396,8 @@ atlaskv_status atlaskv_tree_view_describe(const atlaskv_tensor* root_k, const at
   *out = v;
   return ATLASKV_OK;
 }
+
+int32_t atlaskv_tree_view_placement(atlaskv_tree_view v) { return v ? v->host_mask : -1; }
 
 atlaskv_status atlaskv_destroy_tree_view(atlaskv_tree_view v) {
   if (!v) return ATLASKV_OK;

@@ -38,8 +38,10 @@
  *     leaves and reuses the logits computed for the selection.
  *
  * Memory and threading:
- *   - every tensor is device memory owned by the caller; the library never
- *     copies or frees it.  A tree view references its tensors until destroyed;
+ *   - every tensor is device memory owned by the caller, except that the
+ *     tree's tensors may instead live in pinned host memory (below); the
+ *     library never copies or frees them.  A tree view references its tensors
+ *     until destroyed;
  *   - atlaskv_hikvp_attend* allocate nothing: scratch memory is the caller's
  *     workspace (size from atlaskv_hikvp_workspace_size).  Only
  *     atlaskv_build_tree_view allocates (a few bytes of device memory per KV
@@ -105,11 +107,28 @@ typedef struct atlaskv_tree_view_s* atlaskv_tree_view;
  * default stream of attend calls.  The call validates the offsets and
  * computes per-level key-norm bounds on the GPU, then synchronises once.
  * Returns ATLASKV_ERR_TREE for malformed offsets; *out is set only on success.
+ *
+ * Host-tiered trees (速读 › 怎么做的 keeps only the root keys in GPU memory
+ * and brings each lower level in from CPU memory as the descent reaches it;
+ * 速读 › 效果如何 names that traffic as the method's I/O cost): any of the six
+ * tree arrays may be pinned host memory (hipHostMalloc, or a torch tensor
+ * with pin_memory=True) instead of device memory.  The kernels then read it
+ * through its device mapping over the host link: each level's selected spans
+ * are fetched by the kernel that scores them, once per (KV head, node) group,
+ * so only the selected mids' leaf spans and the selected leaves' values cross
+ * the link.  Results are identical to a device-resident tree.  Pageable host
+ * memory, or device memory of another GPU, gives ATLASKV_ERR_UNSUPPORTED
+ * before anything is enqueued.
  */
 atlaskv_status atlaskv_build_tree_view(const atlaskv_tensor* root_k, const atlaskv_tensor* mid_k,
                                        const atlaskv_tensor* leaf_k, const atlaskv_tensor* leaf_v,
                                        const int64_t* root_child_off, const int64_t* mid_child_off,
                                        void* stream, atlaskv_tree_view* out);
+
+/* Where a view's tree lives: bit i set when tree array i (0 root_k, 1 mid_k,
+ * 2 leaf_k, 3 leaf_v, 4 root_child_off, 5 mid_child_off) is pinned host
+ * memory; 0 for an all-device tree, -1 for NULL. */
+int32_t atlaskv_tree_view_placement(atlaskv_tree_view tree);
 
 /* Release a view (and its small device buffers).  NULL is accepted. */
 atlaskv_status atlaskv_destroy_tree_view(atlaskv_tree_view tree);

@@ -201,6 +201,66 @@ def test_select_launch_shapes(K, F1, F2):
 
 
 # ---------------------------------------------------------------------------
+# host-tiered trees: tree arrays in pinned host memory, read over the host link
+# ---------------------------------------------------------------------------
+
+def _pinned(t):
+    h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    h.copy_(t)
+    return h
+
+
+_TREE_FIELDS = ("root_k", "mid_k", "leaf_k", "leaf_v", "root_off", "mid_off")
+
+
+def _view(case):
+    return atlaskv.TreeView(*[getattr(case, f) for f in _TREE_FIELDS])
+
+
+@pytest.mark.parametrize("fields,mask", [(("leaf_k", "leaf_v"), 0b001100),
+                                         (_TREE_FIELDS, 0b111111)])
+def test_host_tiered_tree_matches_device_tree(fields, mask):
+    """Leaves (or the whole tree) in pinned host memory: the view reports the
+    placement, selections and outputs equal the device-resident tree's bit for
+    bit, and the oracle agrees."""
+    case = _small(seed=41, dtype="bf16")
+    dev_tree = _view(case)
+    assert dev_tree.placement == 0
+    ref = parity.gpu_run(case, tree=dev_tree)
+    dev_tree.close()
+    for f in fields:
+        setattr(case, f, _pinned(getattr(case, f)))
+    host_tree = _view(case)
+    assert host_tree.placement == mask
+    got = parity.gpu_run(case, tree=host_tree)
+    host_tree.close()
+    assert np.array_equal(got["out"], ref["out"])
+    for a, b in zip(got["sel"], ref["sel"]):
+        assert np.array_equal(a, b)
+    _check(case)
+
+
+def test_host_tiered_leaves_fp32_ragged():
+    case = _small(seed=42, dtype="f32", K=(4, 9, 33))
+    case.leaf_k, case.leaf_v = _pinned(case.leaf_k), _pinned(case.leaf_v)
+    _check(case)
+
+
+def test_pageable_host_tree_rejected():
+    """Pageable host memory cannot be read by the kernels: the view refuses it
+    before anything is enqueued and leaves no pending HIP error behind."""
+    case = _small(seed=43, dtype="bf16")
+    with pytest.raises(atlaskv.AtlasKVError) as e:
+        atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k.cpu(), case.leaf_v, case.root_off,
+                         case.mid_off)
+    assert e.value.status == atlaskv.ERR_UNSUPPORTED
+    assert "leaf_k" in atlaskv.last_error()
+    x = torch.arange(1000, device=DEV, dtype=torch.float32)
+    assert float(x.sum().item()) == 499500.0
+    _check(case)
+
+
+# ---------------------------------------------------------------------------
 # the named workloads
 # ---------------------------------------------------------------------------
 
