@@ -438,3 +438,36 @@ int oracle_finish_rows(const oracle_problem* P, int64_t rows, const int64_t* b,
   }
   return rc;
 }
+
+/*
+ * Unpruned equivalent attention (背景知识与设计原则 › KBLaM中的矩形注意力: one
+ * softmax over every knowledge logit and the visible sequence logits;
+ * 方法细节 › 等效注意力机制的知识增强 writes the same output as the λ merge of
+ * a KG softmax and a sequence softmax, with nothing pruned while fine-tuning).
+ * The KG logits of row (b, n, h) are scale * <q_kg, leaf_k[g][m]> for every
+ * leaf m < M of KV head g, in index order; roots, mids and K are not used.
+ */
+int oracle_flat_rows(const oracle_problem* P, int64_t rows, const int64_t* b,
+                     const int64_t* n, const int64_t* h, const oracle_outputs* O) {
+  if (!P || !P->q || !P->leaf_k || !P->leaf_v || !b || !n || !h) return -1;
+  if (P->d <= 0 || P->Hq <= 0 || P->Hkv <= 0 || P->Hq % P->Hkv || P->M < 0) return -1;
+  if (P->S_kv > 0 && (P->S_kv < P->N || !P->seq_k || !P->seq_v)) return -1;
+  const int64_t d = P->d, M = P->M;
+  const size_t cap = (size_t)(M > 0 ? M : 1);
+  double* logit = (double*)malloc(cap * sizeof(double));
+  const void** vrow = (const void**)malloc(cap * sizeof(void*));
+  int64_t* voff = (int64_t*)malloc(cap * sizeof(int64_t));
+  int rc = (!logit || !vrow || !voff) ? -3 : 0;
+  for (int64_t r = 0; r < rows && !rc; ++r) {
+    const int64_t g = h[r] / (P->Hq / P->Hkv);
+    const int64_t qb = q_base(P, b[r], n[r], h[r]);
+    for (int64_t m = 0; m < M; ++m) {
+      voff[m] = (g * M + m) * d;
+      vrow[m] = P->leaf_v;
+      logit[m] = P->scale * dot(kg_query(P), qb, P->leaf_k, voff[m], P->dtype, d);
+    }
+    rc = finish_row(P, b[r], n[r], h[r], M, logit, vrow, voff, r, O);
+  }
+  free(logit); free(vrow); free(voff);
+  return rc;
+}

@@ -125,6 +125,13 @@ int oracle_finish_rows(const oracle_problem* P, int64_t rows, const int64_t* b,
                        const void* cand_k, const void* cand_v,
                        const int64_t* forced_sel_L, const oracle_outputs* O);
 
+/* Unpruned equivalent attention for the given rows: the KG half is the
+ * softmax over the logits of all M leaves of the row's KV head, merged with
+ * the causal sequence half exactly as above.  Fills lse_kg, lse_seq, lam_kg,
+ * lam_seq, o_kg, o_seq and out; selection outputs are left untouched. */
+int oracle_flat_rows(const oracle_problem* P, int64_t rows, const int64_t* b,
+                     const int64_t* n, const int64_t* h, const oracle_outputs* O);
+
 #ifdef __cplusplus
 }
 #endif

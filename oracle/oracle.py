@@ -70,6 +70,8 @@ def lib():
         L.oracle_finish_rows.argtypes = rows_sig + [_I64P, _I64P, ctypes.c_void_p, ctypes.c_void_p,
                                                     _I64P, ctypes.POINTER(_Outputs)]
         L.oracle_finish_rows.restype = ctypes.c_int
+        L.oracle_flat_rows.argtypes = rows_sig + [ctypes.POINTER(_Outputs)]
+        L.oracle_flat_rows.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -204,6 +206,17 @@ def hikvp_rows(prob: Problem, rows):
     o, O = _alloc_outputs(len(r), prob.K, prob.shape["d"])
     _check(lib().oracle_hikvp_rows(ctypes.byref(prob._P), len(r), _ip(b), _ip(n), _ip(h),
                                    ctypes.byref(O)), "oracle_hikvp_rows")
+    return o
+
+
+def flat_rows(prob: Problem, rows):
+    """Unpruned equivalent attention (the KG softmax runs over every leaf of
+    the row's KV head) for the given rows; dict of numpy arrays (selection
+    entries stay at their -1 / NaN fill)."""
+    r, b, n, h = _rows(rows)
+    o, O = _alloc_outputs(len(r), prob.K, prob.shape["d"])
+    _check(lib().oracle_flat_rows(ctypes.byref(prob._P), len(r), _ip(b), _ip(n), _ip(h),
+                                  ctypes.byref(O)), "oracle_flat_rows")
     return o
 
 

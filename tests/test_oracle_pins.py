@@ -85,18 +85,20 @@ def test_hand_worked_tree(oracle_mod):
 # full K == the rectangular (KBLaM) joint softmax over all M leaves
 # ---------------------------------------------------------------------------
 
-def _rectangular(q, leaf_k, leaf_v, seq_k, seq_v, scale):
+def _rectangular(q, leaf_k, leaf_v, seq_k, seq_v, scale, q_kg=None):
     """KBLaM中的矩形注意力: one softmax over every KB logit plus the causal
-    sequence logits (bottom-right aligned when S_kv > N); numpy fp64."""
+    sequence logits (bottom-right aligned when S_kv > N); numpy fp64.  The KB
+    logits use q_kg when given (the KB query of the projection heads)."""
     B, N, Hq, d = q.shape
     Hkv = leaf_k.shape[0]
     S = 0 if seq_k is None else seq_k.shape[1]
+    qk = q if q_kg is None else q_kg
     out = np.zeros((B, N, Hq, d))
     for b in range(B):
         for n in range(N):
             for h in range(Hq):
                 g = h * Hkv // Hq
-                kg = scale * (leaf_k[g] @ q[b, n, h])
+                kg = scale * (leaf_k[g] @ qk[b, n, h])
                 vis = S - N + n + 1 if S else 0
                 sq = scale * (seq_k[b, :vis, g] @ q[b, n, h]) if vis else np.zeros(0)
                 allx = np.concatenate([kg, sq])
@@ -128,6 +130,76 @@ def test_full_k_equals_rectangular_attention(oracle_mod, seed):
     # every leaf selected exactly once
     for r in range(o["sel_L"].shape[0]):
         assert sorted(o["sel_L"][r].tolist()) == list(range(M))
+
+
+# ---------------------------------------------------------------------------
+# unpruned equivalent attention (the flat KG softmax over every leaf)
+# ---------------------------------------------------------------------------
+
+def _random_shape(rng):
+    Hkv = int(rng.integers(1, 3))
+    Hq = Hkv * int(rng.integers(1, 4))
+    N = int(rng.integers(1, 6))
+    S = N + int(rng.integers(0, 4))
+    MR = int(rng.integers(1, 5))
+    MI = MR + int(rng.integers(0, 8))
+    M = MI + int(rng.integers(0, 300))
+    return dict(B=2, N=N, S=S, Hq=Hq, Hkv=Hkv, d=int(rng.integers(1, 9)), MR=MR, MI=MI, M=M)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("use_qkg", [False, True])
+def test_flat_equals_rectangular_attention(oracle_mod, seed, use_qkg):
+    """The oracle's unpruned path against the rectangular formula written
+    out in numpy, with and without a separate KB query."""
+    rng = np.random.default_rng(100 + seed)
+    c = _small_case(100 + seed, **_random_shape(rng))
+    qkg = torch.randn(c.q.shape, generator=torch.Generator().manual_seed(seed)).double() if use_qkg else None
+    P = _problem(oracle_mod, c, q_kg=qkg)
+    o = oracle_mod.flat_rows(P, oracle_mod.all_rows(c.B, c.N, c.Hq))
+    ref = _rectangular(c.q.double().numpy(), c.leaf_k.double().numpy(), c.leaf_v.double().numpy(),
+                       c.seq_k.double().numpy(), c.seq_v.double().numpy(), P.scale,
+                       None if qkg is None else qkg.numpy())
+    np.testing.assert_allclose(o["out"], ref.reshape(-1, c.d), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(o["lam_kg"] + o["lam_seq"], 1.0, rtol=0, atol=1e-15)
+    merged = o["lam_kg"][:, None] * o["o_kg"] + o["lam_seq"][:, None] * o["o_seq"]
+    np.testing.assert_allclose(merged, o["out"], rtol=1e-13, atol=1e-13)
+
+
+def test_flat_equals_descent_at_full_k(oracle_mod):
+    """With K at least every fanout sum nothing is pruned, so the descent's
+    KG half (its own candidate order) equals the flat one."""
+    c = _small_case(120, B=2, N=4, S=6, Hq=6, Hkv=2, d=7, MR=4, MI=13, M=157)
+    rows = oracle_mod.all_rows(c.B, c.N, c.Hq)
+    a = oracle_mod.flat_rows(_problem(oracle_mod, c), rows)
+    b = oracle_mod.hikvp_rows(_problem(oracle_mod, c, (c.M_R, c.M_I, c.M)), rows)
+    for k in ("out", "o_kg", "lse_kg", "lse_seq", "lam_kg"):
+        np.testing.assert_allclose(a[k], b[k], rtol=1e-12, atol=1e-12)
+    # the flat call leaves the selection outputs untouched
+    assert (a["sel_L"] == -1).all() and (a["sel_R"] == -1).all()
+
+
+def test_flat_single_leaf_without_sequence_returns_its_value(oracle_mod):
+    c = _small_case(121, N=3, S=3, MR=1, MI=1, M=1)
+    o = oracle_mod.flat_rows(_problem(oracle_mod, c, drop_seq=True), oracle_mod.all_rows(c.B, c.N, c.Hq))
+    G = c.Hq // c.Hkv
+    for r, (b, n, h) in enumerate(oracle_mod.all_rows(c.B, c.N, c.Hq)):
+        np.testing.assert_array_equal(o["out"][r], c.leaf_v[h // G, 0].double().numpy())
+    assert (o["lam_kg"] == 1.0).all() and (o["lam_seq"] == 0.0).all()
+
+
+def test_flat_logit_shift_by_value_shift(oracle_mod):
+    """Adding a constant vector to every value (leaves and sequence) adds it
+    to the output: the joint weights sum to one."""
+    c = _small_case(122, M=60)
+    rows = oracle_mod.all_rows(c.B, c.N, c.Hq)
+    o = oracle_mod.flat_rows(_problem(oracle_mod, c), rows)
+    shift = torch.linspace(-2.0, 3.0, c.d, dtype=torch.float64)
+    c2 = _small_case(122, M=60)
+    c2.leaf_v = c2.leaf_v.double() + shift
+    c2.seq_v = c2.seq_v.double() + shift
+    o2 = oracle_mod.flat_rows(_problem(oracle_mod, c2), rows)
+    np.testing.assert_allclose(o2["out"], o["out"] + shift.numpy(), rtol=1e-12, atol=1e-12)
 
 
 def test_full_k_without_sequence(oracle_mod):
