@@ -34,6 +34,8 @@ from hierarchical_kv_pruning_amd import atlaskv, synth  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, AMD's published figure
 PEAK_LINK_GBPS = 64.0           # MI355X host interface, PCIe 5.0 x16, one direction (published)
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix-core peak (published)
+PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 vector peak (published)
 KERNEL_SOURCES = [os.path.join(ROOT, "hierarchical_kv_pruning_amd", "csrc", f)
                   for f in ("hikvp_device.h", "hikvp_select.hip", "hikvp_seq.hip")]
 PROFILES = os.path.join(ROOT, "profiles")
@@ -175,6 +177,43 @@ def cpu_baseline(case, seconds):
 
 # ---------------------------------------------------------------------------
 
+def flat_line(args, case, ms_per_step, phase_ms, cold, tokens):
+    """JSON line of the unpruned path: every leaf key and value is read once;
+    the dominant kernel is the flash pass over the leaves, 4*d flops per
+    (row, leaf) pair (scores and weighted values)."""
+    eb = 2 if case.dtype == "bf16" else 4
+    row_b = case.d * eb
+    leaves_b = 2 * case.Hkv * case.M * row_b
+    seq_b = 2 * case.B * case.S_kv * case.Hkv * row_b
+    total_b = leaves_b + seq_b + 2 * case.rows * row_b
+    flops = 4.0 * case.rows * case.M * case.d
+    t = phase_ms["flat_kg_partial"] * 1e-3
+    peak_f = PEAK_BF16_TFLOPS if case.dtype == "bf16" else PEAK_FP32_TFLOPS
+    t_mfma, t_hbm = flops / (peak_f * 1e12), leaves_b / (PEAK_HBM_GBPS * 1e9)
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma" if case.dtype == "bf16" else "alu", "achieved": flops / t / 1e12,
+                "peak": peak_f, "unit": "TFLOP/s", "frac": flops / t / 1e12 / peak_f,
+                "algorithmic_flops": flops}
+    else:
+        roof = {"bound": "hbm", "achieved": leaves_b / t / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": leaves_b / t / 1e9 / PEAK_HBM_GBPS, "algorithmic_bytes": leaves_b}
+    roof.update(kernel="flat_kg_partial", traffic=None,
+                hbm_gbps=leaves_b / t / 1e9, tflops=flops / t / 1e12)
+    return {
+        "metric": "query tokens/s per layer through unpruned equivalent attention (all M leaves)",
+        "value": tokens / (ms_per_step * 1e-3), "unit": "query tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": case.dtype,
+        "data": "synthetic (seeded clustered-Gaussian key tree, Gaussian values, queries and sequence K/V)",
+        "config": {"workload": case.name, "path": "flat", "B": case.B, "N": case.N, "S_kv": case.S_kv,
+                   "Hq": case.Hq, "Hkv": case.Hkv, "d": case.d, "M": case.M, "tokens_per_step": tokens,
+                   "parallelism": "single GPU", "tree_placement": args.tree_placement},
+        "path_hbm": {"compulsory_bytes": total_b, "achieved_gbps": total_b / (ms_per_step * 1e-3) / 1e9,
+                     "cold_ms_per_step": cold},
+        "phase_ms": phase_ms, "roofline": roof, "cpu_baseline": None,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +226,8 @@ def main():
                     help="extra steps timed one by one after evicting the 256 MB MALL")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--path", default="hikvp", choices=["hikvp", "flat"],
+                    help="flat: the unpruned equivalent attention (KG softmax over every leaf)")
     ap.add_argument("--tree-placement", default="hbm", choices=["hbm", "host-leaves"],
                     help="host-leaves: leaf keys and values in pinned host memory, read by the "
                          "kernels over the host link (roots, mids, offsets stay in HBM)")
@@ -228,14 +269,22 @@ def main():
         link_copy_gbps = (1 << 30) / (a.elapsed_time(b) * 1e-3) / 1e9
         del src, dst
     tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
-    ws = atlaskv.alloc_workspace(tree, case.q, case.seq_k, case.K)
+    flat = args.path == "flat"
+    if flat:
+        ws = atlaskv.alloc_flat_workspace(tree, case.q, case.seq_k)
+    else:
+        ws = atlaskv.alloc_workspace(tree, case.q, case.seq_k, case.K)
     out = torch.empty_like(case.q)
     R = case.rows
     sel = [torch.empty(R, k, dtype=torch.int32, device=dev) for k in case.K]
-    phases = atlaskv.phase_names()
+    phases = atlaskv.flat_phase_names() if flat else atlaskv.phase_names()
     stream = torch.cuda.current_stream(dev)
 
     def step(events=None):
+        if flat:
+            atlaskv.flat_attend_ex(case.q, tree, case.seq_k, case.seq_v, out, workspace=ws,
+                                   phase_events=events, stream=stream)
+            return
         atlaskv.hikvp_attend_ex(case.q, tree, case.seq_k, case.seq_v, case.K, out, workspace=ws,
                                 sel_root=sel[0], sel_mid=sel[1], sel_leaf=sel[2],
                                 phase_events=events, stream=stream)
@@ -290,9 +339,13 @@ def main():
         log(f"calibration copy of {n} bytes done")
         del src, dst
 
+    tokens = case.B * case.N
+    if flat:
+        print(json.dumps(flat_line(args, case, ms_per_step, phase_ms, cold, tokens)), flush=True)
+        tree.close()
+        return
     host_sel = [s.cpu().numpy() for s in sel]
     ab = algorithmic_bytes(case, host_sel)
-    tokens = case.B * case.N
     dom = max((p for p in phases if p in ab), key=lambda p: phase_ms[p])
     achieved = ab[dom] / (phase_ms[dom] * 1e-3) / 1e9
     on_host = args.tree_placement == "host-leaves"

@@ -26,7 +26,8 @@ _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 EXPORTS = ["atlaskv_build_tree_view", "atlaskv_destroy_tree_view", "atlaskv_tree_view_set_workspace",
            "atlaskv_hikvp_workspace_size", "atlaskv_hikvp_attend", "atlaskv_hikvp_attend_ex",
            "atlaskv_check_args", "atlaskv_tree_view_describe", "atlaskv_tree_view_placement",
-           "atlaskv_phase_count",
+           "atlaskv_flat_workspace_size", "atlaskv_flat_attend_ex", "atlaskv_flat_check_args",
+           "atlaskv_flat_phase_count", "atlaskv_flat_phase_name", "atlaskv_phase_count",
            "atlaskv_phase_name", "atlaskv_last_error", "atlaskv_version"]
 
 
@@ -77,8 +78,14 @@ def lib():
         L.atlaskv_tree_view_describe.argtypes = [T, T, T, T, ctypes.c_int64, ctypes.c_int64,
                                                  P(ctypes.c_void_p)]
         L.atlaskv_tree_view_placement.argtypes = [ctypes.c_void_p]
+        L.atlaskv_flat_workspace_size.argtypes = [ctypes.c_void_p, T, T, P(ctypes.c_size_t)]
+        L.atlaskv_flat_attend_ex.argtypes = [T, ctypes.c_void_p, T, T, T, P(AttendOpts)]
+        L.atlaskv_flat_check_args.argtypes = [T, ctypes.c_void_p, T, T, T, P(AttendOpts)]
         for name in EXPORTS[:-4]:
             getattr(L, name).restype = ctypes.c_int
+        L.atlaskv_flat_phase_count.restype = ctypes.c_int32
+        L.atlaskv_flat_phase_name.argtypes = [ctypes.c_int32]
+        L.atlaskv_flat_phase_name.restype = ctypes.c_char_p
         L.atlaskv_phase_count.restype = ctypes.c_int32
         L.atlaskv_phase_name.argtypes = [ctypes.c_int32]
         L.atlaskv_phase_name.restype = ctypes.c_char_p
@@ -260,6 +267,44 @@ def check_args(q, tree, seq_k, seq_v, K, out, **opts):
                                   _ref(dv), _k(K) if K is not None else None, _ref(do), ctypes.byref(o))
     del keep
     return st
+
+
+def flat_workspace_size(tree, q, seq_k):
+    n = ctypes.c_size_t()
+    dq, dk = describe(q), describe(seq_k)
+    _raise(lib().atlaskv_flat_workspace_size(tree.handle, ctypes.byref(dq), _ref(dk), ctypes.byref(n)))
+    return n.value
+
+
+def alloc_flat_workspace(tree, q, seq_k):
+    """A torch uint8 device buffer large enough for a flat attend call."""
+    n = flat_workspace_size(tree, q, seq_k)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def flat_attend_ex(q, tree, seq_k, seq_v, out, **opts):
+    """atlaskv_flat_attend_ex: the KG half over every leaf (no pruning)."""
+    dq, dk, dv, do = describe(q), describe(seq_k), describe(seq_v), describe(out)
+    o, keep = _opts(device=q.device, **opts)
+    _raise(lib().atlaskv_flat_attend_ex(ctypes.byref(dq), tree.handle, _ref(dk), _ref(dv),
+                                        ctypes.byref(do), ctypes.byref(o)))
+    del keep
+    return out
+
+
+def flat_check_args(q, tree, seq_k, seq_v, out, **opts):
+    """atlaskv_flat_check_args: status code of the host-side checks."""
+    dq, dk, dv, do = describe(q), describe(seq_k), describe(seq_v), describe(out)
+    o, keep = _opts(**opts)
+    st = lib().atlaskv_flat_check_args(_ref(dq), tree.handle if tree is not None else None, _ref(dk),
+                                       _ref(dv), _ref(do), ctypes.byref(o))
+    del keep
+    return st
+
+
+def flat_phase_names():
+    L = lib()
+    return [L.atlaskv_flat_phase_name(i).decode() for i in range(L.atlaskv_flat_phase_count())]
 
 
 def phase_names():

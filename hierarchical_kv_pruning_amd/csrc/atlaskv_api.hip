@@ -166,6 +166,8 @@ struct Plan {
   size_t off_rcnt, off_rtot, off_rrank, off_rbase, off_rtoff, off_rtkey, off_rnt, off_rmem;
   int64_t root_tiles_max;
   int32_t desc_per_sub, bucket_q;
+  int flat_nsplit, flat_split_len, flat_row_tiles;  // unpruned path only
+  size_t off_fpart;
 };
 
 // Candidate capacity per row at the mid level (children of K_R distinct
@@ -180,13 +182,15 @@ void candidate_capacity(const atlaskv_tree_view_s* v, const int K[3], int64_t* c
   *c2 = b < 1 ? 1 : b;
 }
 
+// flat: the unpruned path (every leaf; K is not used and may be NULL).
 atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
                          const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
                          const int32_t Kpl[3], const atlaskv_tensor* out,
-                         const atlaskv_attend_opts* opts, bool need_out, Plan& p) {
+                         const atlaskv_attend_opts* opts, bool need_out, Plan& p, bool flat = false) {
   atlaskv_status st;
+  memset(&p, 0, sizeof p);
   if (!v) return fail(ATLASKV_ERR_NULL, "tree view is NULL");
-  if (!Kpl) return fail(ATLASKV_ERR_NULL, "K_per_level is NULL");
+  if (!Kpl && !flat) return fail(ATLASKV_ERR_NULL, "K_per_level is NULL");
   if ((st = check_tensor(q, "q", 4, true))) return st;
   const TreeDev& t = v->dev;
   if (q->dtype != t.dtype) return fail(ATLASKV_ERR_DTYPE, "q dtype differs from the tree's");
@@ -225,10 +229,12 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
     for (int i = 0; i < 4; ++i)
       if (out->shape[i] != q->shape[i]) return fail(ATLASKV_ERR_SHAPE, "out shape differs from q's");
   }
-  for (int i = 0; i < 3; ++i)
-    if (Kpl[i] < 0 || Kpl[i] > kMaxK) return fail(ATLASKV_ERR_K, "K[%d]=%d outside 0..%d", i, Kpl[i], kMaxK);
-  const bool kg_empty = Kpl[0] == 0 || Kpl[1] == 0 || Kpl[2] == 0 || t.count[0] == 0 ||
-                        t.count[1] == 0 || t.count[2] == 0;
+  if (!flat)
+    for (int i = 0; i < 3; ++i)
+      if (Kpl[i] < 0 || Kpl[i] > kMaxK) return fail(ATLASKV_ERR_K, "K[%d]=%d outside 0..%d", i, Kpl[i], kMaxK);
+  const bool kg_empty = flat ? t.count[2] == 0
+                             : (Kpl[0] == 0 || Kpl[1] == 0 || Kpl[2] == 0 || t.count[0] == 0 ||
+                                t.count[1] == 0 || t.count[2] == 0);
   if (kg_empty && !seq_k)
     return fail(ATLASKV_ERR_K, "both the KG half (K or tree empty) and the sequence half are empty");
   double scale = 1.0 / sqrt((double)t.d);
@@ -240,6 +246,25 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   p.B = (int)B; p.N = (int)N; p.Hq = (int)Hq; p.S = (int)S;
   p.R = (int)(B * N * Hq);
   p.G = (int)(Hq / t.Hkv);
+  p.scale = scale;
+  if (flat) {
+    if (t.count[2] >= kIndexLimit) return fail(ATLASKV_ERR_UNSUPPORTED, "M must be below 2^31");
+    const int64_t eb = t.dtype == ATLASKV_BF16 ? 2 : 4;
+    if (t.rs[2] * eb >= ((int64_t)1 << 25) || t.rs[3] * eb >= ((int64_t)1 << 25))
+      return fail(ATLASKV_ERR_UNSUPPORTED, "leaf row strides must be below 32 MB");
+    const size_t R = (size_t)p.R;
+    size_t o = 0;
+    p.flat_nsplit = flat_splits(p.B, p.N, p.Hq, t.Hkv, t.count[2], t.dtype);
+    p.flat_split_len = flat_split_len(t.count[2], p.flat_nsplit);
+    p.flat_row_tiles = flat_row_tiles(p.B, p.N, p.G);
+    p.off_okg = o;   o = align256(o + R * (size_t)t.d * 4);
+    p.off_lse = o;   o = align256(o + R * 4);
+    p.off_fpart = o; o = align256(o + R * (size_t)p.flat_nsplit * (t.d + 4) * 4);
+    p.nsplit = seq_splits(p.B, p.N, t.Hkv, p.S);
+    p.off_part = o;  o = align256(o + (p.nsplit > 1 ? R * (size_t)p.nsplit * (t.d + 2) * 4 : 0));
+    p.total = o;
+    return ATLASKV_OK;
+  }
   for (int i = 0; i < 3; ++i) p.K[i] = Kpl[i];
   if ((int64_t)p.R * p.K[1] >= kIndexLimit || (int64_t)t.Hkv * t.count[1] >= kIndexLimit ||
       (int64_t)p.R * (p.K[0] + kRootTile) >= kIndexLimit)
@@ -293,6 +318,56 @@ void fill_rows(RowsDev& r, const atlaskv_tensor* q, const atlaskv_attend_opts* o
   for (int i = 0; i < 3; ++i) { r.qs[i] = q->stride[i]; r.qks[i] = qk->stride[i]; }
   r.B = p.B; r.N = p.N; r.Hq = p.Hq; r.G = p.G; r.R = p.R;
   r.scale = p.scale;
+}
+
+// Optional timing events at phase boundaries: event 0 before the first
+// kernel, event i after phase i-1.
+struct PhaseMarks {
+  void** ev;
+  int nev, phase;
+  hipStream_t s;
+  PhaseMarks(const atlaskv_attend_opts* opts, hipStream_t st)
+      : ev((opts && opts->phase_events && opts->n_phase_events > 0) ? opts->phase_events : nullptr),
+        nev(ev ? opts->n_phase_events : 0), phase(0), s(st) {}
+  hipError_t mark(hipError_t prev) {
+    if (prev != hipSuccess || phase >= nev || !ev[phase]) { ++phase; return prev; }
+    hipError_t r = hipEventRecord((hipEvent_t)ev[phase], s);
+    ++phase;
+    return r;
+  }
+};
+
+// Sequence half (背景知识与设计原则 › 自注意力层机制) and the λ merge with the
+// KG half held in o_kg / lse_kg: two phases (attention, split combine).
+hipError_t launch_seq_half(const Plan& p, const RowsDev& rows, const atlaskv_tree_view_s* v,
+                           const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                           const atlaskv_tensor* out, const atlaskv_attend_opts* opts, float* o_kg,
+                           float* lse_kg, char* ws, hipStream_t s, PhaseMarks& pm) {
+  SeqArgs sa;
+  memset(&sa, 0, sizeof sa);
+  sa.r = rows;
+  sa.S = p.S;
+  sa.Hkv = v->dev.Hkv;
+  sa.d = v->dev.d;
+  sa.dtype = v->dev.dtype;
+  if (seq_k) {
+    sa.k = seq_k->data;
+    sa.v = seq_v->data;
+    sa.ks[0] = seq_k->stride[0]; sa.ks[1] = seq_k->stride[1]; sa.ks[2] = seq_k->stride[2];
+    sa.vs[0] = seq_v->stride[0]; sa.vs[1] = seq_v->stride[1]; sa.vs[2] = seq_v->stride[2];
+  }
+  sa.o_kg = o_kg;
+  sa.lse_kg = lse_kg;
+  sa.out = out->data;
+  sa.os[0] = out->stride[0]; sa.os[1] = out->stride[1]; sa.os[2] = out->stride[2];
+  sa.out_dtype = out->dtype;
+  sa.lse_seq_out = opts ? opts->lse_seq : nullptr;
+  sa.nsplit = p.nsplit;
+  sa.part = p.nsplit > 1 ? (float*)(ws + p.off_part) : nullptr;
+  sa.split_len = p.nsplit > 1 ? seq_split_len(p.S, p.nsplit) : (p.S > 0 ? p.S : 1);
+  hipError_t e = pm.mark(launch_seq_attend(sa, s));
+  if (e == hipSuccess) e = pm.mark(launch_seq_combine(sa, s));
+  return e;
 }
 
 }  // namespace
@@ -430,8 +505,9 @@ atlaskv_status atlaskv_hikvp_workspace_size(atlaskv_tree_view v, const atlaskv_t
 static atlaskv_status check_all(const atlaskv_tensor* q, atlaskv_tree_view v,
                                 const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
                                 const int32_t K[3], const atlaskv_tensor* out,
-                                const atlaskv_attend_opts* opts, Plan& p, void** ws) {
-  atlaskv_status st = plan_call(q, v, seq_k, seq_v, K, out, opts, true, p);
+                                const atlaskv_attend_opts* opts, Plan& p, void** ws,
+                                bool flat = false) {
+  atlaskv_status st = plan_call(q, v, seq_k, seq_v, K, out, opts, true, p, flat);
   if (st) return st;
   void* w = (opts && opts->workspace) ? opts->workspace : v->workspace;
   size_t wb = (opts && opts->workspace) ? opts->workspace_bytes : v->workspace_bytes;
@@ -475,16 +551,8 @@ atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vie
   float* lse_kg = (opts && opts->lse_kg) ? opts->lse_kg : (float*)(ws + p.off_lse);
   float* o_kg = (float*)(ws + p.off_okg);
 
-  // optional timing events at phase boundaries
-  void** ev = (opts && opts->phase_events && opts->n_phase_events > 0) ? opts->phase_events : nullptr;
-  const int nev = ev ? opts->n_phase_events : 0;
-  int phase = 0;
-  auto mark = [&](hipError_t prev) -> hipError_t {
-    if (prev != hipSuccess || phase >= nev || !ev[phase]) { ++phase; return prev; }
-    hipError_t r = hipEventRecord((hipEvent_t)ev[phase], s);
-    ++phase;
-    return r;
-  };
+  PhaseMarks pm(opts, s);
+  auto mark = [&](hipError_t prev) { return pm.mark(prev); };
   hipError_t e = mark(hipSuccess);
   StepArgs a;
   memset(&a, 0, sizeof a);
@@ -527,32 +595,7 @@ atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vie
   if (e == hipSuccess) e = mark(launch_leaf_score(a, s));
   if (e == hipSuccess) e = mark(launch_leaf_overflow(a, s));
   if (e == hipSuccess) e = mark(launch_leaf_select(a, s));
-  if (e == hipSuccess) {
-    SeqArgs sa;
-    memset(&sa, 0, sizeof sa);
-    sa.r = rows;
-    sa.S = p.S;
-    sa.Hkv = v->dev.Hkv;
-    sa.d = v->dev.d;
-    sa.dtype = v->dev.dtype;
-    if (seq_k) {
-      sa.k = seq_k->data;
-      sa.v = seq_v->data;
-      sa.ks[0] = seq_k->stride[0]; sa.ks[1] = seq_k->stride[1]; sa.ks[2] = seq_k->stride[2];
-      sa.vs[0] = seq_v->stride[0]; sa.vs[1] = seq_v->stride[1]; sa.vs[2] = seq_v->stride[2];
-    }
-    sa.o_kg = o_kg;
-    sa.lse_kg = lse_kg;
-    sa.out = out->data;
-    sa.os[0] = out->stride[0]; sa.os[1] = out->stride[1]; sa.os[2] = out->stride[2];
-    sa.out_dtype = out->dtype;
-    sa.lse_seq_out = opts ? opts->lse_seq : nullptr;
-    sa.nsplit = p.nsplit;
-    sa.part = p.nsplit > 1 ? (float*)(ws + p.off_part) : nullptr;
-    sa.split_len = p.nsplit > 1 ? seq_split_len(p.S, p.nsplit) : (p.S > 0 ? p.S : 1);
-    e = mark(launch_seq_attend(sa, s));
-    if (e == hipSuccess) e = mark(launch_seq_combine(sa, s));
-  }
+  if (e == hipSuccess) e = launch_seq_half(p, rows, v, seq_k, seq_v, out, opts, o_kg, lse_kg, ws, s, pm);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return ATLASKV_OK;
 }
@@ -561,6 +604,69 @@ atlaskv_status atlaskv_hikvp_attend(const atlaskv_tensor* q, atlaskv_tree_view v
                                     const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
                                     const int32_t K[3], atlaskv_tensor* out) {
   return atlaskv_hikvp_attend_ex(q, v, seq_k, seq_v, K, out, nullptr);
+}
+
+static const char* const kFlatPhaseNames[] = {"flat_kg_partial", "flat_kg_combine", "seq_attention",
+                                              "seq_split_combine"};
+static const int kFlatPhases = (int)(sizeof kFlatPhaseNames / sizeof kFlatPhaseNames[0]);
+
+int32_t atlaskv_flat_phase_count(void) { return kFlatPhases; }
+
+const char* atlaskv_flat_phase_name(int32_t i) {
+  return (i >= 0 && i < kFlatPhases) ? kFlatPhaseNames[i] : nullptr;
+}
+
+atlaskv_status atlaskv_flat_workspace_size(atlaskv_tree_view v, const atlaskv_tensor* q,
+                                           const atlaskv_tensor* seq_k, size_t* bytes) {
+  if (!bytes) return fail(ATLASKV_ERR_NULL, "bytes is NULL");
+  Plan p;
+  atlaskv_status st = plan_call(q, v, seq_k, seq_k, nullptr, nullptr, nullptr, false, p, true);
+  if (st) return st;
+  *bytes = p.total;
+  return ATLASKV_OK;
+}
+
+atlaskv_status atlaskv_flat_attend_ex(const atlaskv_tensor* q, atlaskv_tree_view v,
+                                      const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                      atlaskv_tensor* out, const atlaskv_attend_opts* opts) {
+  Plan p;
+  void* wsv = nullptr;
+  atlaskv_status st = check_all(q, v, seq_k, seq_v, nullptr, out, opts, p, &wsv, true);
+  if (st) return st;
+  if (v->described_only) return fail(ATLASKV_ERR_UNSUPPORTED, "a described-only view cannot run");
+  if (p.R == 0) return ATLASKV_OK;
+  hipStream_t s = (opts && opts->stream) ? (hipStream_t)opts->stream : v->stream;
+  char* ws = (char*)wsv;
+  RowsDev rows;
+  fill_rows(rows, q, opts, p);
+  float* lse_kg = (opts && opts->lse_kg) ? opts->lse_kg : (float*)(ws + p.off_lse);
+  float* o_kg = (float*)(ws + p.off_okg);
+  PhaseMarks pm(opts, s);
+  hipError_t e = pm.mark(hipSuccess);
+  FlatArgs fa;
+  memset(&fa, 0, sizeof fa);
+  fa.t = v->dev;
+  fa.r = rows;
+  fa.nsplit = p.flat_nsplit;
+  fa.split_len = p.flat_split_len;
+  fa.row_tiles = p.flat_row_tiles;
+  fa.part = (float*)(ws + p.off_fpart);
+  fa.o_kg = o_kg;
+  fa.lse_kg = lse_kg;
+  // KG half over every leaf, then the sequence half and the λ merge as in the pruned path
+  if (e == hipSuccess) e = pm.mark(launch_flat_partial(fa, s));
+  if (e == hipSuccess) e = pm.mark(launch_flat_combine(fa, s));
+  if (e == hipSuccess) e = launch_seq_half(p, rows, v, seq_k, seq_v, out, opts, o_kg, lse_kg, ws, s, pm);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return ATLASKV_OK;
+}
+
+atlaskv_status atlaskv_flat_check_args(const atlaskv_tensor* q, atlaskv_tree_view v,
+                                       const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                       const atlaskv_tensor* out, const atlaskv_attend_opts* opts) {
+  Plan p;
+  void* ws = nullptr;
+  return check_all(q, v, seq_k, seq_v, nullptr, out, opts, p, &ws, true);
 }
 
 }  // extern "C"

@@ -102,6 +102,18 @@ struct SeqArgs {
   int split_len;              // keys per split (multiple of 64); >= S when not split
 };
 
+// One unpruned (flat) KG attention call: every leaf of the row's KV head.
+struct FlatArgs {
+  TreeDev t;
+  RowsDev r;
+  int nsplit;                 // leaf-key ranges per (KV head, row tile)
+  int split_len;              // keys per range (multiple of 64)
+  int row_tiles;              // 128-row tiles of one KV head's B*N*G rows
+  float* part;                // [R, nsplit, d + 4] per range: o (relative to m), m (log2 units), sum, pad
+  float* o_kg;                // [R, d]
+  float* lse_kg;              // [R]
+};
+
 struct BuildStats {           // device-side result of tree validation
   int bad;                    // non-zero: malformed offsets
   int pad;
@@ -124,6 +136,11 @@ hipError_t launch_leaf_overflow(const StepArgs& a, hipStream_t s);  // members p
 hipError_t launch_leaf_select(const StepArgs& a, hipStream_t s);
 hipError_t launch_seq_attend(const SeqArgs& a, hipStream_t s);   // + λ merge when keys are not split
 hipError_t launch_seq_combine(const SeqArgs& a, hipStream_t s);  // split partials: LSE combine + λ merge
+hipError_t launch_flat_partial(const FlatArgs& a, hipStream_t s);  // per (head, rows, key range)
+hipError_t launch_flat_combine(const FlatArgs& a, hipStream_t s);  // ranges -> o_kg, lse_kg
+int flat_row_tiles(int B, int N, int G);
+int flat_splits(int B, int N, int Hq, int Hkv, int64_t M, int dtype);
+int flat_split_len(int64_t M, int nsplit);
 int seq_splits(int B, int N, int Hkv, int S);   // key splits of the sequence attention
 int seq_split_len(int S, int nsplit);
 

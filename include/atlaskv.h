@@ -207,6 +207,37 @@ atlaskv_status atlaskv_tree_view_describe(const atlaskv_tensor* root_k, const at
 int32_t atlaskv_phase_count(void);
 const char* atlaskv_phase_name(int32_t phase);
 
+/*
+ * Unpruned equivalent attention (flat KG half).  背景知识与设计原则 ›
+ * KBLaM中的矩形注意力 defines one softmax over the logits of every knowledge
+ * key together with the visible sequence logits; 方法细节 ›
+ * 等效注意力机制的知识增强 writes that same output as the λ merge of a KG
+ * softmax and a sequence softmax and uses it, with nothing pruned, while
+ * fine-tuning.  Here the KG half is the softmax over the logits
+ * scale * <q_kg, leaf_k[g][m]> of ALL M leaves of the row's KV head g (the
+ * roots and mids of the view are not read), weighted over leaf_v; the
+ * sequence half and the merge are those of atlaskv_hikvp_attend.  The result
+ * equals atlaskv_hikvp_attend with K at least every fanout sum, for any M.
+ * Arguments as atlaskv_hikvp_attend_ex without K: q, seq_k/seq_v, out and
+ * opts (q_kg, scale, stream, workspace, lse_kg, lse_seq, phase_events;
+ * sel_* are ignored).  The workspace size comes from
+ * atlaskv_flat_workspace_size.  bf16 trees run on matrix cores (scores and
+ * softmax weights rounded to bf16 operands, fp32 accumulation); fp32 trees on
+ * plain fp32 arithmetic.
+ */
+atlaskv_status atlaskv_flat_workspace_size(atlaskv_tree_view tree, const atlaskv_tensor* q,
+                                           const atlaskv_tensor* seq_k, size_t* bytes);
+atlaskv_status atlaskv_flat_attend_ex(const atlaskv_tensor* q, atlaskv_tree_view tree,
+                                      const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                      atlaskv_tensor* out, const atlaskv_attend_opts* opts);
+/* The argument checks of atlaskv_flat_attend_ex alone (pure host code). */
+atlaskv_status atlaskv_flat_check_args(const atlaskv_tensor* q, atlaskv_tree_view tree,
+                                       const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                       const atlaskv_tensor* out, const atlaskv_attend_opts* opts);
+/* Kernel phases of one flat call, in launch order (for phase_events). */
+int32_t atlaskv_flat_phase_count(void);
+const char* atlaskv_flat_phase_name(int32_t phase);
+
 /* Message for the calling thread's most recent failed call ("" if none). */
 const char* atlaskv_last_error(void);
 

@@ -183,3 +183,48 @@ def test_phase_names_in_launch_order(lib):
         "leaf_score_overflow", "leaf_topk_kg_attention", "seq_attention", "seq_split_combine"]
     assert lib.atlaskv_phase_name(-1) is None
     assert lib.atlaskv_phase_name(lib.atlaskv_phase_count()) is None
+
+
+def test_flat_phase_names_in_launch_order(lib):
+    assert atlaskv.flat_phase_names() == ["flat_kg_partial", "flat_kg_combine", "seq_attention",
+                                          "seq_split_combine"]
+    assert lib.atlaskv_flat_phase_name(-1) is None
+    assert lib.atlaskv_flat_phase_name(lib.atlaskv_flat_phase_count()) is None
+
+
+def _flat_call(view, q=None, seq=True, out=None, ws_bytes=1 << 30, **opts):
+    B, N, Hq, d = 1, 4, 4, view._keep[0].shape[2]
+    dt = view._keep[0].dtype
+    if q is None:
+        q = torch.zeros(B, N, Hq, d, dtype=dt)
+    sk = torch.zeros(B, 6, view._keep[0].shape[0], d, dtype=dt) if seq else None
+    sv = torch.zeros_like(sk) if seq else None
+    if out is None:
+        out = torch.zeros(q.shape, dtype=dt)
+    ws = torch.zeros(4096, dtype=torch.uint8)
+    fake = type("W", (), {"data_ptr": lambda self: (ws.data_ptr() + 255) // 256 * 256,
+                          "numel": lambda self: ws_bytes})()
+    return atlaskv.flat_check_args(q, view, sk, sv, out, workspace=fake, **opts)
+
+
+def test_flat_argument_checks(lib):
+    """The unpruned path takes no K; shape, dtype and workspace rules are the
+    pruned path's, and a tree with leaves always has a KG half."""
+    v = _view()
+    assert _flat_call(v) == atlaskv.OK
+    assert _flat_call(v, seq=False) == atlaskv.OK
+    assert _flat_call(_view(dtype=torch.float32, d=64)) == atlaskv.OK
+    assert _flat_call(v, q=torch.zeros(1, 4, 3, 128, dtype=torch.bfloat16)) == atlaskv.ERR_SHAPE
+    assert _flat_call(v, q=torch.zeros(1, 4, 4, 128, dtype=torch.float32)) == atlaskv.ERR_DTYPE
+    assert _flat_call(v, ws_bytes=16) == atlaskv.ERR_WORKSPACE
+    assert _flat_call(v, scale=-2.0) == atlaskv.ERR_UNSUPPORTED
+    q = torch.zeros(1, 4, 4, 128, dtype=torch.bfloat16)
+    assert atlaskv.flat_check_args(q, v, None, None, q) == atlaskv.ERR_WORKSPACE  # none attached
+
+
+def test_flat_workspace_grows_with_leaves(lib):
+    q = torch.zeros(1, 4, 4, 128, dtype=torch.bfloat16)
+    small = atlaskv.flat_workspace_size(_view(M=50), q, None)
+    big = atlaskv.flat_workspace_size(_view(M=50000), q, None)
+    assert 0 < small <= big
+
