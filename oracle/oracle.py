@@ -130,6 +130,8 @@ class Problem:
 
     def __init__(self, q, root_k, mid_k, leaf_k, leaf_v, root_off, mid_off,
                  seq_k, seq_v, K, scale=None, q_kg=None):
+        self._args = (q, root_k, mid_k, leaf_k, leaf_v, root_off, mid_off, seq_k, seq_v, K)
+        self._kw = dict(scale=scale, q_kg=q_kg)
         self._keep = []
         qa, dt = _host(q)
         B, N, Hq, d = qa.shape
@@ -218,6 +220,96 @@ def flat_rows(prob: Problem, rows):
     _check(lib().oracle_flat_rows(ctypes.byref(prob._P), len(r), _ip(b), _ip(n), _ip(h),
                                   ctypes.byref(O)), "oracle_flat_rows")
     return o
+
+
+# ---------------------------------------------------------------------------
+# shared selections: one descent per group of rows
+# ---------------------------------------------------------------------------
+
+SHARE_KV_GROUP, SHARE_SEQUENCE = 1, 2
+
+
+def _round_bf16_bits(x):
+    """Round fp64 values once to bf16 (nearest, ties to even), from the fp64
+    bit pattern; returns the 16-bit codes.  Normal range and zero only."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    u = x.view(np.uint64)
+    sign = (u >> np.uint64(63)).astype(np.uint64)
+    exp = ((u >> np.uint64(52)) & np.uint64(0x7FF)).astype(np.int64)
+    man = (u & np.uint64((1 << 52) - 1)) | np.uint64(1 << 52)      # 53-bit significand
+    keep = man >> np.uint64(45)                                     # 8 significant bits
+    rest = man & np.uint64((1 << 45) - 1)
+    half = np.uint64(1 << 44)
+    up = (rest > half) | ((rest == half) & ((keep & np.uint64(1)) == np.uint64(1)))
+    keep = keep + up.astype(np.uint64)
+    carry = keep >> np.uint64(8)                                    # 2^8: next binade
+    keep = np.where(carry > 0, keep >> np.uint64(1), keep)
+    e = exp - 1023 + 127 + carry.astype(np.int64)
+    zero = (u & np.uint64((1 << 63) - 1)) == 0
+    if np.any(~zero & ((e <= 0) | (e >= 255))):
+        raise ValueError("group query outside the bf16 normal range")
+    bits = (sign << np.uint64(15)) | (np.clip(e, 0, 255).astype(np.uint64) << np.uint64(7)) | (keep & np.uint64(0x7F))
+    return np.where(zero, sign << np.uint64(15), bits).astype(np.uint16)
+
+
+def group_queries(prob: Problem, share):
+    """Each row's group query [B, N, Hq, d] in the problem's storage type.
+
+    The group of row (b, n, h) is every row of the same sequence b and KV head
+    g = h // G at token n (share = SHARE_KV_GROUP) or at any token
+    (SHARE_SEQUENCE).  Its query is the sum of the members' KG queries (fp64,
+    exact for stored values), rounded once to the storage type: ranking nodes
+    by it ranks them by the sum of the members' logits up to that rounding.
+    """
+    q, q_kg = prob._args[0], prob._kw["q_kg"]
+    qa, dt = _host(q if q_kg is None else q_kg)
+    x = qa.view(np.uint16).astype(np.uint32) << 16 if dt == BF16 else qa
+    x = np.asarray(x.view(np.float32) if dt == BF16 else x, dtype=np.float64)
+    B, N, Hq, d = x.shape
+    s = prob.shape
+    G = Hq // s["Hkv"]
+    g = x.reshape(B, N, s["Hkv"], G, d).sum(axis=3)                 # [B, N, Hkv, d]
+    if share == SHARE_SEQUENCE:
+        g = np.broadcast_to(g.sum(axis=1, keepdims=True), g.shape)
+    elif share != SHARE_KV_GROUP:
+        raise ValueError("share must be SHARE_KV_GROUP or SHARE_SEQUENCE")
+    full = np.repeat(g, G, axis=2)                                   # back to [B, N, Hq, d]
+    import torch
+    if dt == BF16:
+        return torch.from_numpy(_round_bf16_bits(full).view(np.int16)).view(torch.bfloat16)
+    if dt == F32:
+        return torch.from_numpy(np.ascontiguousarray(full.astype(np.float32)))
+    return torch.from_numpy(np.ascontiguousarray(full))
+
+
+def shared_rows(prob: Problem, rows, share):
+    """Shared-selection variant for the given rows: the descent (roots, mids,
+    leaves, Top-K per level) runs on the row's group query; the row's KG
+    softmax then runs over the group's selected leaves with its own KG query
+    and logits, and merges with its own sequence half as in hikvp_rows.
+    Returns the finish outputs plus the group selections (sel_R, sel_I,
+    sel_L, gap) under the group query."""
+    gq = group_queries(prob, share)
+    args = prob._args
+    grp = Problem(*args, scale=prob._kw["scale"], q_kg=gq)
+    sel = hikvp_rows(grp, rows)
+    r = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+    G = prob.shape["Hq"] // prob.shape["Hkv"]
+    lk, lv = args[3], args[4]
+    off, idx, ks, vs = [0], [], [], []
+    for i, (b, n, h) in enumerate(r):
+        lv_i = [int(m) for m in sel["sel_L"][i] if m >= 0]
+        idx.extend(lv_i)
+        ks.append(lk[h // G, lv_i])
+        vs.append(lv[h // G, lv_i])
+        off.append(off[-1] + len(lv_i))
+    import torch
+    ks = torch.cat(ks) if len(idx) else lk[0, :0]
+    vs = torch.cat(vs) if len(idx) else lv[0, :0]
+    fin = finish_rows(prob, r, off, idx, ks, vs, forced_sel_L=sel["sel_L"])
+    for k in ("sel_R", "sel_I", "sel_L", "gap", "n_cand"):
+        fin[k] = sel[k]
+    return fin
 
 
 def select_mids_rows(prob: Problem, rows):

@@ -517,3 +517,116 @@ def test_replay_with_forced_selection(oracle_mod):
     alt = oracle_mod.finish_rows(P, rows, off, idx, ks, vs, forced_sel_L=forced)
     np.testing.assert_allclose(alt["o_kg"], c.leaf_v.double().numpy()[
         [h * c.Hkv // c.Hq for (_, _, h) in rows], forced[:, 0]], rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# shared selections (one descent per KV group or per sequence)
+# ---------------------------------------------------------------------------
+
+def _bf16_value(bits):
+    return float(np.array([int(bits) << 16], np.uint32).view(np.float32)[0])
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_round_bf16_is_nearest_ties_to_even(oracle_mod, seed):
+    """The group-query rounding against its definition: the nearest bf16 of
+    the two that bracket x, the even code on a tie."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(4000) * 10.0 ** rng.integers(-3, 4, 4000)
+    # exact ties: a bf16 value plus half an ulp
+    base = np.array([_bf16_value(b) for b in rng.integers(0x3C00, 0x4400, 200)])
+    half_ulp = 2.0 ** (np.frexp(base)[1] - 9.0)                # |base| in [2^(e-1), 2^e)
+    x = np.concatenate([x, base + half_ulp * np.where(rng.random(200) < 0.5, 1, -1),
+                        [0.0, -0.0, 1.0, -3.0]])
+    got = oracle_mod._round_bf16_bits(x)
+    nties = 0
+    for xi, gi in zip(x, got):
+        t = int(np.array([xi], np.float32).view(np.uint32)[0]) >> 16       # a nearby code
+        cands = [c & 0xFFFF for c in (t - 1, t, t + 1, t + 2) if np.isfinite(_bf16_value(c & 0xFFFF))]
+        best = min(cands, key=lambda c: (abs(_bf16_value(c) - xi), c & 1))
+        assert abs(_bf16_value(int(gi)) - xi) == abs(_bf16_value(best) - xi), (xi, gi, best)
+        ties = [c for c in cands if abs(_bf16_value(c) - xi) == abs(_bf16_value(int(gi)) - xi)]
+        if len(ties) > 1:
+            assert int(gi) & 1 == 0, (xi, gi)
+            nties += 1
+    assert nties >= 150   # the constructed half-ulp points are exact ties
+
+
+def test_shared_kv_group_of_one_is_per_row(oracle_mod):
+    """Hq == Hkv: a KV group is one row, its summed query is the row's own,
+    so the shared variant equals the per-row descent."""
+    c = _small_case(130, B=2, N=4, S=6, Hq=3, Hkv=3, d=8, MR=4, MI=15, M=90, K=(2, 3, 5))
+    rows = oracle_mod.all_rows(c.B, c.N, c.Hq)
+    a = oracle_mod.shared_rows(_problem(oracle_mod, c, f64=False), rows, oracle_mod.SHARE_KV_GROUP)
+    b = oracle_mod.hikvp_rows(_problem(oracle_mod, c, f64=False), rows)
+    for k in ("sel_R", "sel_I", "sel_L", "out", "lse_kg", "lse_seq"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_shared_sequence_with_one_token_is_kv_group(oracle_mod):
+    c = _small_case(131, B=3, N=1, S=5, Hq=4, Hkv=2, d=8, MR=4, MI=15, M=90, K=(2, 3, 5))
+    rows = oracle_mod.all_rows(c.B, c.N, c.Hq)
+    P = _problem(oracle_mod, c, f64=False)
+    a = oracle_mod.shared_rows(P, rows, oracle_mod.SHARE_SEQUENCE)
+    b = oracle_mod.shared_rows(P, rows, oracle_mod.SHARE_KV_GROUP)
+    for k in ("sel_L", "out"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+@pytest.mark.parametrize("share", [1, 2])
+def test_shared_selection_is_top_k_of_summed_logits(oracle_mod, share):
+    """fp64 storage (the group query needs no rounding): every level's shared
+    selection is the brute-force Top-K of the members' summed logits, and each
+    row's output is its own softmax over the group's leaves plus its causal
+    sequence half, written out in numpy."""
+    c = _small_case(132, B=2, N=3, S=4, Hq=4, Hkv=2, d=6, MR=5, MI=17, M=120, K=(2, 3, 4))
+    P = _problem(oracle_mod, c)
+    rows = oracle_mod.all_rows(c.B, c.N, c.Hq)
+    o = oracle_mod.shared_rows(P, rows, share)
+    q = c.q.double().numpy()
+    G = c.Hq // c.Hkv
+    ro, mo = c.root_off.numpy(), c.mid_off.numpy()
+    keys = [c.root_k.double().numpy(), c.mid_k.double().numpy(), c.leaf_k.double().numpy()]
+    for i, (b, n, h) in enumerate(rows):
+        g = h // G
+        toks = [n] if share == 1 else list(range(c.N))
+        members = [(b, t, hh) for t in toks for hh in range(g * G, (g + 1) * G)]
+        parents = None
+        for lev, (key, Kl) in enumerate(zip(("sel_R", "sel_I", "sel_L"), c.K)):
+            if lev == 0:
+                cand = np.arange(c.M_R)
+            else:
+                off = ro if lev == 1 else mo
+                cand = np.concatenate([np.arange(off[p], off[p + 1]) for p in parents])
+            score = np.zeros(len(cand))
+            for (mb, mn, mh) in members:        # sum of the members' fp64 logits
+                score += P.scale * (keys[lev][g, cand] @ q[mb, mn, mh])
+            order = sorted(range(len(cand)), key=lambda j: (-score[j], cand[j]))
+            want = sorted(cand[j] for j in order[:Kl])
+            assert sorted(x for x in o[key][i] if x >= 0) == want, (i, key)
+            parents = want
+        # the row's own softmax over the group's leaves and its causal half
+        lv = c.leaf_v.double().numpy()[g, parents]
+        kg = P.scale * (keys[2][g, parents] @ q[b, n, h])
+        vis = c.S_kv - c.N + n + 1
+        sq = P.scale * (c.seq_k.double().numpy()[b, :vis, g] @ q[b, n, h])
+        allx = np.concatenate([kg, sq])
+        w = np.exp(allx - allx.max())
+        ref = (w[:len(kg)] @ lv + w[len(kg):] @ c.seq_v.double().numpy()[b, :vis, g]) / w.sum()
+        np.testing.assert_allclose(o["out"][i], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_shared_group_query_rounds_the_sum_once(oracle_mod):
+    """bf16 storage: the group query is the exact member sum rounded once."""
+    c = synth.make_case("custom", seed=133, ragged=True, dtype="bf16", B=1, N=3, S_kv=3, Hq=4,
+                        Hkv=2, d=8, M_R=3, M_I=7, M=23, K=(2, 2, 3))
+    P = _problem(oracle_mod, c, f64=False)
+    gq = oracle_mod.group_queries(P, oracle_mod.SHARE_KV_GROUP).float().numpy()
+    q = c.q.double().numpy()
+    want = q.reshape(1, 3, 2, 2, 8).sum(axis=3)
+    for b, n, h in oracle_mod.all_rows(1, 3, 4):
+        exact = want[b, n, h // 2]
+        np.testing.assert_array_equal(gq[b, n, h], [_bf16_value(x) for x in oracle_mod._round_bf16_bits(exact)])
+        # and it is within half a bf16 ulp of the exact sum
+        assert np.all(np.abs(gq[b, n, h] - exact) <= np.abs(exact) * 2.0 ** -8 + 1e-300)
+
