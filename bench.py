@@ -56,19 +56,22 @@ def kernel_source_hash():
 # algorithmic bytes: what the method must move per step (each byte once)
 # ---------------------------------------------------------------------------
 
-def algorithmic_bytes(case, sel):
+def algorithmic_bytes(case, sel, share=0):
     """Per-phase compulsory bytes of one step, from the step's selections.
 
     roots: every root key; mids: the child spans of the distinct selected
     (KV head, root) pairs; leaf keys: the child spans of the distinct selected
     (KV head, mid) pairs; leaf values: the distinct selected (KV head, leaf)
-    rows; sequence: K and V once; q read once, out written once.
+    rows; sequence: K and V once; q read once, out written once.  With shared
+    selections `sel` holds the group selections (rows of groups (b, n, g) or
+    (b, g)) and the per-row KG softmax re-reads the groups' selected leaf keys
+    (their values are counted once already).
     """
     eb = 2 if case.dtype == "bf16" else 4
     row_b = case.d * eb
     G = case.Hq // case.Hkv
     R = case.rows
-    head = (np.arange(R) % case.Hq) // G
+    head = (np.arange(R) % case.Hq) // G if share == 0 else np.arange(sel[0].shape[0]) % case.Hkv
     ro = case.root_off.cpu().numpy()
     mo = case.mid_off.cpu().numpy()
 
@@ -88,6 +91,22 @@ def algorithmic_bytes(case, sel):
     q_b = R * row_b
     out_b = R * row_b
     seq_b = 2 * case.B * case.S_kv * case.Hkv * row_b
+    if share:
+        return {
+            "group_query": q_b,
+            "root_score_topk": roots_b,
+            "mid_bucket_gemm": mids_b,
+            "mid_topk": 0, "leaf_bucket_link": 0,
+            "leaf_score_stream": leafk_b,
+            "leaf_score_overflow": 0,
+            "leaf_topk_kg_attention": leafv_b,
+            "shared_kg_attention": leafv_b,   # the selected leaves' keys (values counted above)
+            "seq_attention": seq_b,
+            "seq_split_combine": out_b,
+            "_total": roots_b + mids_b + leafk_b + 2 * leafv_b + seq_b + q_b + out_b,
+            "_parts": dict(roots=roots_b, mids=mids_b, leaf_keys=leafk_b, leaf_values=leafv_b,
+                           selected_leaf_keys=leafv_b, sequence_kv=seq_b, q=q_b, out=out_b),
+        }
     return {
         "root_score_topk": roots_b + q_b,
         "mid_bucket_gemm": mids_b,
@@ -228,6 +247,9 @@ def main():
                     help="also run a plain device copy of this size (counter calibration)")
     ap.add_argument("--path", default="hikvp", choices=["hikvp", "flat"],
                     help="flat: the unpruned equivalent attention (KG softmax over every leaf)")
+    ap.add_argument("--share", default="none", choices=["none", "kv-group", "sequence"],
+                    help="shared selections: one descent per KV head and token, or per KV head "
+                         "and sequence (pruned path only)")
     ap.add_argument("--tree-placement", default="hbm", choices=["hbm", "host-leaves"],
                     help="host-leaves: leaf keys and values in pinned host memory, read by the "
                          "kernels over the host link (roots, mids, offsets stay in HBM)")
@@ -270,20 +292,33 @@ def main():
         del src, dst
     tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
     flat = args.path == "flat"
+    share = {"none": 0, "kv-group": atlaskv.SHARE_KV_GROUP, "sequence": atlaskv.SHARE_SEQUENCE}[args.share]
+    if flat and share:
+        print("--share applies to the pruned path only", file=sys.stderr)
+        sys.exit(2)
     if flat:
         ws = atlaskv.alloc_flat_workspace(tree, case.q, case.seq_k)
+    elif share:
+        ws = atlaskv.alloc_shared_workspace(tree, case.q, case.seq_k, case.K, share)
     else:
         ws = atlaskv.alloc_workspace(tree, case.q, case.seq_k, case.K)
     out = torch.empty_like(case.q)
     R = case.rows
-    sel = [torch.empty(R, k, dtype=torch.int32, device=dev) for k in case.K]
-    phases = atlaskv.flat_phase_names() if flat else atlaskv.phase_names()
+    nsel = R if not share else case.B * (case.N if share == atlaskv.SHARE_KV_GROUP else 1) * case.Hkv
+    sel = [torch.empty(nsel, k, dtype=torch.int32, device=dev) for k in case.K]
+    phases = (atlaskv.flat_phase_names() if flat else
+              atlaskv.shared_phase_names() if share else atlaskv.phase_names())
     stream = torch.cuda.current_stream(dev)
 
     def step(events=None):
         if flat:
             atlaskv.flat_attend_ex(case.q, tree, case.seq_k, case.seq_v, out, workspace=ws,
                                    phase_events=events, stream=stream)
+            return
+        if share:
+            atlaskv.shared_attend_ex(case.q, tree, case.seq_k, case.seq_v, case.K, share, out,
+                                     workspace=ws, sel_root=sel[0], sel_mid=sel[1], sel_leaf=sel[2],
+                                     phase_events=events, stream=stream)
             return
         atlaskv.hikvp_attend_ex(case.q, tree, case.seq_k, case.seq_v, case.K, out, workspace=ws,
                                 sel_root=sel[0], sel_mid=sel[1], sel_leaf=sel[2],
@@ -345,7 +380,27 @@ def main():
         tree.close()
         return
     host_sel = [s.cpu().numpy() for s in sel]
-    ab = algorithmic_bytes(case, host_sel)
+    ab = algorithmic_bytes(case, host_sel, share)
+    recall = None
+    if share:
+        # leaves of the per-row selection that the shared selection also holds
+        ws1 = atlaskv.alloc_workspace(tree, case.q, case.seq_k, case.K)
+        own = torch.empty(R, case.K[2], dtype=torch.int32, device=dev)
+        atlaskv.hikvp_attend_ex(case.q, tree, case.seq_k, case.seq_v, case.K, torch.empty_like(case.q),
+                                workspace=ws1, sel_leaf=own, stream=stream)
+        torch.cuda.synchronize()
+        own = own.cpu().numpy()
+        G = case.Hq // case.Hkv
+        rows = np.arange(R)
+        h, t = rows % case.Hq, rows // case.Hq
+        grp = (t * case.Hkv + h // G) if share == atlaskv.SHARE_KV_GROUP else \
+            ((t // case.N) * case.Hkv + h // G)
+        hit = tot = 0
+        for r in range(R):
+            a = set(own[r][own[r] >= 0].tolist())
+            hit += len(a & set(host_sel[2][grp[r]].tolist()))
+            tot += len(a)
+        recall = hit / max(tot, 1)
     dom = max((p for p in phases if p in ab), key=lambda p: phase_ms[p])
     achieved = ab[dom] / (phase_ms[dom] * 1e-3) / 1e9
     on_host = args.tree_placement == "host-leaves"
@@ -363,7 +418,7 @@ def main():
         "config": {"workload": case.name, "B": case.B, "N": case.N, "S_kv": case.S_kv, "Hq": case.Hq,
                    "Hkv": case.Hkv, "d": case.d, "tree": [case.M_R, case.M_I, case.M], "K": list(case.K),
                    "tokens_per_step": tokens, "parallelism": "single GPU",
-                   "tree_placement": args.tree_placement},
+                   "tree_placement": args.tree_placement, "share": args.share},
         "path_hbm": {"compulsory_bytes": ab["_total"], "achieved_gbps": path_gbps,
                      "frac_of_peak": path_gbps / PEAK_HBM_GBPS, "parts": ab["_parts"],
                      "cold_ms_per_step": cold},
@@ -373,6 +428,8 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": ab[dom]},
         "cpu_baseline": None,
     }
+    if share:
+        line["recall_vs_per_row"] = recall
     if on_host:
         # leaf keys and values cross the host link; the dominant kernel is bound by it
         peak = PEAK_LINK_GBPS

@@ -27,7 +27,9 @@ EXPORTS = ["atlaskv_build_tree_view", "atlaskv_destroy_tree_view", "atlaskv_tree
            "atlaskv_hikvp_workspace_size", "atlaskv_hikvp_attend", "atlaskv_hikvp_attend_ex",
            "atlaskv_check_args", "atlaskv_tree_view_describe", "atlaskv_tree_view_placement",
            "atlaskv_flat_workspace_size", "atlaskv_flat_attend_ex", "atlaskv_flat_check_args",
-           "atlaskv_flat_phase_count", "atlaskv_flat_phase_name", "atlaskv_phase_count",
+           "atlaskv_flat_phase_count", "atlaskv_flat_phase_name", "atlaskv_shared_workspace_size",
+           "atlaskv_shared_attend_ex", "atlaskv_shared_check_args", "atlaskv_shared_phase_count",
+           "atlaskv_shared_phase_name", "atlaskv_phase_count",
            "atlaskv_phase_name", "atlaskv_last_error", "atlaskv_version"]
 
 
@@ -81,11 +83,20 @@ def lib():
         L.atlaskv_flat_workspace_size.argtypes = [ctypes.c_void_p, T, T, P(ctypes.c_size_t)]
         L.atlaskv_flat_attend_ex.argtypes = [T, ctypes.c_void_p, T, T, T, P(AttendOpts)]
         L.atlaskv_flat_check_args.argtypes = [T, ctypes.c_void_p, T, T, T, P(AttendOpts)]
+        L.atlaskv_shared_workspace_size.argtypes = [ctypes.c_void_p, T, T, i32x3, ctypes.c_int32,
+                                                    P(ctypes.c_size_t)]
+        L.atlaskv_shared_attend_ex.argtypes = [T, ctypes.c_void_p, T, T, i32x3, ctypes.c_int32, T,
+                                               P(AttendOpts)]
+        L.atlaskv_shared_check_args.argtypes = [T, ctypes.c_void_p, T, T, i32x3, ctypes.c_int32, T,
+                                                P(AttendOpts)]
         for name in EXPORTS[:-4]:
             getattr(L, name).restype = ctypes.c_int
         L.atlaskv_flat_phase_count.restype = ctypes.c_int32
         L.atlaskv_flat_phase_name.argtypes = [ctypes.c_int32]
         L.atlaskv_flat_phase_name.restype = ctypes.c_char_p
+        L.atlaskv_shared_phase_count.restype = ctypes.c_int32
+        L.atlaskv_shared_phase_name.argtypes = [ctypes.c_int32]
+        L.atlaskv_shared_phase_name.restype = ctypes.c_char_p
         L.atlaskv_phase_count.restype = ctypes.c_int32
         L.atlaskv_phase_name.argtypes = [ctypes.c_int32]
         L.atlaskv_phase_name.restype = ctypes.c_char_p
@@ -305,6 +316,48 @@ def flat_check_args(q, tree, seq_k, seq_v, out, **opts):
 def flat_phase_names():
     L = lib()
     return [L.atlaskv_flat_phase_name(i).decode() for i in range(L.atlaskv_flat_phase_count())]
+
+
+SHARE_KV_GROUP, SHARE_SEQUENCE = 1, 2
+
+
+def shared_workspace_size(tree, q, seq_k, K, share):
+    n = ctypes.c_size_t()
+    dq, dk = describe(q), describe(seq_k)
+    _raise(lib().atlaskv_shared_workspace_size(tree.handle, ctypes.byref(dq), _ref(dk), _k(K), int(share),
+                                               ctypes.byref(n)))
+    return n.value
+
+
+def alloc_shared_workspace(tree, q, seq_k, K, share):
+    n = shared_workspace_size(tree, q, seq_k, K, share)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def shared_attend_ex(q, tree, seq_k, seq_v, K, share, out, **opts):
+    """atlaskv_shared_attend_ex: one descent per KV group (share=1) or per
+    sequence (share=2); sel_* options receive the group selections."""
+    dq, dk, dv, do = describe(q), describe(seq_k), describe(seq_v), describe(out)
+    o, keep = _opts(device=q.device, **opts)
+    _raise(lib().atlaskv_shared_attend_ex(ctypes.byref(dq), tree.handle, _ref(dk), _ref(dv), _k(K),
+                                          int(share), ctypes.byref(do), ctypes.byref(o)))
+    del keep
+    return out
+
+
+def shared_check_args(q, tree, seq_k, seq_v, K, share, out, **opts):
+    dq, dk, dv, do = describe(q), describe(seq_k), describe(seq_v), describe(out)
+    o, keep = _opts(**opts)
+    st = lib().atlaskv_shared_check_args(_ref(dq), tree.handle if tree is not None else None, _ref(dk),
+                                         _ref(dv), _k(K) if K is not None else None, int(share), _ref(do),
+                                         ctypes.byref(o))
+    del keep
+    return st
+
+
+def shared_phase_names():
+    L = lib()
+    return [L.atlaskv_shared_phase_name(i).decode() for i in range(L.atlaskv_shared_phase_count())]
 
 
 def phase_names():

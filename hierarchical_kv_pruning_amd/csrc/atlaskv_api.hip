@@ -168,6 +168,8 @@ struct Plan {
   int32_t desc_per_sub, bucket_q;
   int flat_nsplit, flat_split_len, flat_row_tiles;  // unpruned path only
   size_t off_fpart;
+  int group_rows;                                    // shared selections only
+  size_t off_gq, off_gpart;
 };
 
 // Candidate capacity per row at the mid level (children of K_R distinct
@@ -182,11 +184,29 @@ void candidate_capacity(const atlaskv_tree_view_s* v, const int K[3], int64_t* c
   *c2 = b < 1 ? 1 : b;
 }
 
-// flat: the unpruned path (every leaf; K is not used and may be NULL).
+enum { kModeHikvp = 0, kModeFlat = 1, kModeSharedKvGroup = 2, kModeSharedSequence = 3 };
+
+// The group rows of a shared-selection call: [B, Ng, Hkv, d] contiguous in
+// the tree's dtype, Ng = N (one group per KV head and token) or 1 (per KV
+// head and sequence).  Only the shape matters for planning.
+atlaskv_tensor group_rows_desc(int64_t B, int64_t Ng, int Hkv, int d, int dtype, void* data) {
+  atlaskv_tensor g;
+  memset(&g, 0, sizeof g);
+  g.data = data;
+  g.dtype = dtype;
+  g.ndim = 4;
+  g.shape[0] = B; g.shape[1] = Ng; g.shape[2] = Hkv; g.shape[3] = d;
+  g.stride[3] = 1; g.stride[2] = d; g.stride[1] = (int64_t)Hkv * d; g.stride[0] = Ng * Hkv * (int64_t)d;
+  return g;
+}
+
+// mode: kModeHikvp (the pruned path), kModeFlat (every leaf; K is not used and
+// may be NULL) or a shared-selection mode (the descent runs on group rows).
 atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
                          const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
                          const int32_t Kpl[3], const atlaskv_tensor* out,
-                         const atlaskv_attend_opts* opts, bool need_out, Plan& p, bool flat = false) {
+                         const atlaskv_attend_opts* opts, bool need_out, Plan& p, int mode = kModeHikvp) {
+  const bool flat = mode == kModeFlat;
   atlaskv_status st;
   memset(&p, 0, sizeof p);
   if (!v) return fail(ATLASKV_ERR_NULL, "tree view is NULL");
@@ -266,6 +286,26 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
     return ATLASKV_OK;
   }
   for (int i = 0; i < 3; ++i) p.K[i] = Kpl[i];
+  if (mode == kModeSharedKvGroup || mode == kModeSharedSequence) {
+    // the group descent's own workspace, then group queries, per-row KG half, sequence partials
+    const int64_t Ng = mode == kModeSharedSequence ? 1 : N;
+    atlaskv_tensor gd = group_rows_desc(B, Ng, t.Hkv, t.d, t.dtype, (void*)(uintptr_t)256);
+    Plan pg;
+    if ((st = plan_call(&gd, v, seq_k, seq_v, Kpl, nullptr, nullptr, false, pg, kModeHikvp))) return st;
+    const size_t R = (size_t)p.R;
+    size_t o = align256(pg.total);
+    p.group_rows = (int)(B * Ng * t.Hkv);
+    p.off_gq = o;    o = align256(o + (size_t)p.group_rows * t.d * esize(t.dtype));
+    int tn = 1;
+    const int chunks = group_chunks(p.N, (int)Ng, &tn);
+    p.off_gpart = o; o = align256(o + (size_t)p.group_rows * chunks * t.d * 8);
+    p.off_okg = o;   o = align256(o + R * (size_t)t.d * 4);
+    p.off_lse = o;   o = align256(o + R * 4);
+    p.nsplit = seq_splits(p.B, p.N, t.Hkv, p.S);
+    p.off_part = o;  o = align256(o + (p.nsplit > 1 ? R * (size_t)p.nsplit * (t.d + 2) * 4 : 0));
+    p.total = o;
+    return ATLASKV_OK;
+  }
   if ((int64_t)p.R * p.K[1] >= kIndexLimit || (int64_t)t.Hkv * t.count[1] >= kIndexLimit ||
       (int64_t)p.R * (p.K[0] + kRootTile) >= kIndexLimit)
     return fail(ATLASKV_ERR_UNSUPPORTED, "B*N*Hq*(K_R+16), B*N*Hq*K_I and Hkv*M_I must be below 2^31");
@@ -367,6 +407,55 @@ hipError_t launch_seq_half(const Plan& p, const RowsDev& rows, const atlaskv_tre
   sa.split_len = p.nsplit > 1 ? seq_split_len(p.S, p.nsplit) : (p.S > 0 ? p.S : 1);
   hipError_t e = pm.mark(launch_seq_attend(sa, s));
   if (e == hipSuccess) e = pm.mark(launch_seq_combine(sa, s));
+  return e;
+}
+
+// The pruned descent for `rows` (速读 › 怎么做的: roots -> Top-K -> their
+// children -> Top-K -> leaves -> Top-K, then the KG softmax over the selected
+// leaves into o_kg / lse_kg): seven timing phases.
+hipError_t launch_descent(const Plan& p, const RowsDev& rows, const atlaskv_tree_view_s* v, char* ws,
+                          int32_t* const sel[3], float* o_kg, float* lse_kg, hipStream_t s, PhaseMarks& pm) {
+  auto mark = [&](hipError_t prev) { return pm.mark(prev); };
+  StepArgs a;
+  memset(&a, 0, sizeof a);
+  a.t = v->dev;
+  a.r = rows;
+  for (int i = 0; i < 3; ++i) { a.K[i] = p.K[i]; a.sel[i] = sel[i]; }
+  a.c1max = p.c1max;
+  a.c2max = p.c2max;
+  a.mid_scores = (float*)(ws + p.off_mid);
+  a.leaf_scores = (float*)(ws + p.off_leaf);
+  a.mid_base = (int32_t*)(ws + p.off_mid_base);
+  a.root_cnt = (int32_t*)(ws + p.off_rcnt);
+  a.root_tot = (int32_t*)(ws + p.off_rtot);
+  a.root_rank = (int32_t*)(ws + p.off_rrank);
+  a.root_base = (int32_t*)(ws + p.off_rbase);
+  a.root_tile_off = (int32_t*)(ws + p.off_rtoff);
+  a.root_tile_key = (int32_t*)(ws + p.off_rtkey);
+  a.root_ntiles = (int32_t*)(ws + p.off_rnt);
+  a.root_members = (int2*)(ws + p.off_rmem);
+  a.root_tiles_max = p.root_tiles_max;
+  a.bucket_cnt = (int32_t*)(ws + p.off_bcnt);
+  a.bucket_slot = (int2*)(ws + p.off_bslot);
+  a.bucket_head = (int32_t*)(ws + p.off_bhead);
+  a.bucket_next = (int32_t*)(ws + p.off_bnext);
+  a.bucket_desc = (int4*)(ws + p.off_blist);
+  a.bucket_count = (int32_t*)(ws + p.off_bcount);
+  a.desc_per_sub = p.desc_per_sub;
+  a.bucket_q = p.bucket_q;
+  a.bucket_ovf = (int32_t*)(ws + p.off_bovf);
+  a.junk = (float*)(ws + p.off_junk);
+  a.o_kg = o_kg;
+  a.lse_kg = lse_kg;
+  hipError_t e = launch_clear(a, s);
+  if (e == hipSuccess) e = launch_root(a, s);
+  if (e == hipSuccess) e = mark(launch_root_groups(a, s));
+  if (e == hipSuccess) e = mark(launch_mid_gemm(a, s));
+  if (e == hipSuccess) e = mark(launch_mid_select(a, s));
+  if (e == hipSuccess) e = mark(launch_leaf_link(a, s));
+  if (e == hipSuccess) e = mark(launch_leaf_score(a, s));
+  if (e == hipSuccess) e = mark(launch_leaf_overflow(a, s));
+  if (e == hipSuccess) e = mark(launch_leaf_select(a, s));
   return e;
 }
 
@@ -506,8 +595,8 @@ static atlaskv_status check_all(const atlaskv_tensor* q, atlaskv_tree_view v,
                                 const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
                                 const int32_t K[3], const atlaskv_tensor* out,
                                 const atlaskv_attend_opts* opts, Plan& p, void** ws,
-                                bool flat = false) {
-  atlaskv_status st = plan_call(q, v, seq_k, seq_v, K, out, opts, true, p, flat);
+                                int mode = kModeHikvp) {
+  atlaskv_status st = plan_call(q, v, seq_k, seq_v, K, out, opts, true, p, mode);
   if (st) return st;
   void* w = (opts && opts->workspace) ? opts->workspace : v->workspace;
   size_t wb = (opts && opts->workspace) ? opts->workspace_bytes : v->workspace_bytes;
@@ -552,49 +641,8 @@ atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vie
   float* o_kg = (float*)(ws + p.off_okg);
 
   PhaseMarks pm(opts, s);
-  auto mark = [&](hipError_t prev) { return pm.mark(prev); };
-  hipError_t e = mark(hipSuccess);
-  StepArgs a;
-  memset(&a, 0, sizeof a);
-  a.t = v->dev;
-  a.r = rows;
-  for (int i = 0; i < 3; ++i) { a.K[i] = p.K[i]; a.sel[i] = sel[i]; }
-  a.c1max = p.c1max;
-  a.c2max = p.c2max;
-  a.mid_scores = (float*)(ws + p.off_mid);
-  a.leaf_scores = (float*)(ws + p.off_leaf);
-  a.mid_base = (int32_t*)(ws + p.off_mid_base);
-  a.root_cnt = (int32_t*)(ws + p.off_rcnt);
-  a.root_tot = (int32_t*)(ws + p.off_rtot);
-  a.root_rank = (int32_t*)(ws + p.off_rrank);
-  a.root_base = (int32_t*)(ws + p.off_rbase);
-  a.root_tile_off = (int32_t*)(ws + p.off_rtoff);
-  a.root_tile_key = (int32_t*)(ws + p.off_rtkey);
-  a.root_ntiles = (int32_t*)(ws + p.off_rnt);
-  a.root_members = (int2*)(ws + p.off_rmem);
-  a.root_tiles_max = p.root_tiles_max;
-  a.bucket_cnt = (int32_t*)(ws + p.off_bcnt);
-  a.bucket_slot = (int2*)(ws + p.off_bslot);
-  a.bucket_head = (int32_t*)(ws + p.off_bhead);
-  a.bucket_next = (int32_t*)(ws + p.off_bnext);
-  a.bucket_desc = (int4*)(ws + p.off_blist);
-  a.bucket_count = (int32_t*)(ws + p.off_bcount);
-  a.desc_per_sub = p.desc_per_sub;
-  a.bucket_q = p.bucket_q;
-  a.bucket_ovf = (int32_t*)(ws + p.off_bovf);
-  a.junk = (float*)(ws + p.off_junk);
-  a.o_kg = o_kg;
-  a.lse_kg = lse_kg;
-  // 速读 › 怎么做的: roots -> Top-K -> their children -> Top-K -> leaves -> Top-K
-  e = launch_clear(a, s);
-  if (e == hipSuccess) e = launch_root(a, s);
-  if (e == hipSuccess) e = mark(launch_root_groups(a, s));
-  if (e == hipSuccess) e = mark(launch_mid_gemm(a, s));
-  if (e == hipSuccess) e = mark(launch_mid_select(a, s));
-  if (e == hipSuccess) e = mark(launch_leaf_link(a, s));
-  if (e == hipSuccess) e = mark(launch_leaf_score(a, s));
-  if (e == hipSuccess) e = mark(launch_leaf_overflow(a, s));
-  if (e == hipSuccess) e = mark(launch_leaf_select(a, s));
+  hipError_t e = pm.mark(hipSuccess);
+  if (e == hipSuccess) e = launch_descent(p, rows, v, ws, sel, o_kg, lse_kg, s, pm);
   if (e == hipSuccess) e = launch_seq_half(p, rows, v, seq_k, seq_v, out, opts, o_kg, lse_kg, ws, s, pm);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return ATLASKV_OK;
@@ -604,6 +652,101 @@ atlaskv_status atlaskv_hikvp_attend(const atlaskv_tensor* q, atlaskv_tree_view v
                                     const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
                                     const int32_t K[3], atlaskv_tensor* out) {
   return atlaskv_hikvp_attend_ex(q, v, seq_k, seq_v, K, out, nullptr);
+}
+
+static const char* const kSharedPhaseNames[] = {
+    "group_query", "root_score_topk", "mid_bucket_gemm", "mid_topk", "leaf_bucket_link",
+    "leaf_score_stream", "leaf_score_overflow", "leaf_topk_kg_attention", "shared_kg_attention",
+    "seq_attention", "seq_split_combine"};
+static const int kSharedPhases = (int)(sizeof kSharedPhaseNames / sizeof kSharedPhaseNames[0]);
+
+int32_t atlaskv_shared_phase_count(void) { return kSharedPhases; }
+
+const char* atlaskv_shared_phase_name(int32_t i) {
+  return (i >= 0 && i < kSharedPhases) ? kSharedPhaseNames[i] : nullptr;
+}
+
+static int shared_mode(int32_t share) {
+  return share == ATLASKV_SHARE_KV_GROUP ? kModeSharedKvGroup
+         : share == ATLASKV_SHARE_SEQUENCE ? kModeSharedSequence : -1;
+}
+
+atlaskv_status atlaskv_shared_workspace_size(atlaskv_tree_view v, const atlaskv_tensor* q,
+                                             const atlaskv_tensor* seq_k, const int32_t K[3],
+                                             int32_t share, size_t* bytes) {
+  if (!bytes) return fail(ATLASKV_ERR_NULL, "bytes is NULL");
+  const int mode = shared_mode(share);
+  if (mode < 0) return fail(ATLASKV_ERR_UNSUPPORTED, "share must be ATLASKV_SHARE_KV_GROUP or _SEQUENCE");
+  Plan p;
+  atlaskv_status st = plan_call(q, v, seq_k, seq_k, K, nullptr, nullptr, false, p, mode);
+  if (st) return st;
+  *bytes = p.total;
+  return ATLASKV_OK;
+}
+
+atlaskv_status atlaskv_shared_check_args(const atlaskv_tensor* q, atlaskv_tree_view v,
+                                         const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                         const int32_t K[3], int32_t share, const atlaskv_tensor* out,
+                                         const atlaskv_attend_opts* opts) {
+  const int mode = shared_mode(share);
+  if (mode < 0) return fail(ATLASKV_ERR_UNSUPPORTED, "share must be ATLASKV_SHARE_KV_GROUP or _SEQUENCE");
+  Plan p;
+  void* ws = nullptr;
+  return check_all(q, v, seq_k, seq_v, K, out, opts, p, &ws, mode);
+}
+
+atlaskv_status atlaskv_shared_attend_ex(const atlaskv_tensor* q, atlaskv_tree_view v,
+                                        const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                        const int32_t K[3], int32_t share, atlaskv_tensor* out,
+                                        const atlaskv_attend_opts* opts) {
+  const int mode = shared_mode(share);
+  if (mode < 0) return fail(ATLASKV_ERR_UNSUPPORTED, "share must be ATLASKV_SHARE_KV_GROUP or _SEQUENCE");
+  Plan p;
+  void* wsv = nullptr;
+  atlaskv_status st = check_all(q, v, seq_k, seq_v, K, out, opts, p, &wsv, mode);
+  if (st) return st;
+  if (v->described_only) return fail(ATLASKV_ERR_UNSUPPORTED, "a described-only view cannot run");
+  if (p.R == 0) return ATLASKV_OK;
+  hipStream_t s = (opts && opts->stream) ? (hipStream_t)opts->stream : v->stream;
+  char* ws = (char*)wsv;
+  const int Ng = mode == kModeSharedSequence ? 1 : p.N;
+  // the group rows and their descent's workspace (at the start of ws)
+  atlaskv_tensor gd = group_rows_desc(p.B, Ng, v->dev.Hkv, v->dev.d, v->dev.dtype, ws + p.off_gq);
+  Plan pg;
+  if ((st = plan_call(&gd, v, seq_k, seq_v, K, nullptr, nullptr, false, pg, kModeHikvp))) return st;
+  RowsDev rows, grows;
+  fill_rows(rows, q, opts, p);
+  fill_rows(grows, &gd, nullptr, pg);
+  grows.scale = p.scale;
+  int32_t* sel[3];
+  int32_t* user_sel[3] = {opts ? opts->sel_root : nullptr, opts ? opts->sel_mid : nullptr,
+                          opts ? opts->sel_leaf : nullptr};
+  for (int i = 0; i < 3; ++i) sel[i] = user_sel[i] ? user_sel[i] : (int32_t*)(ws + pg.off_sel[i]);
+  float* lse_kg = (opts && opts->lse_kg) ? opts->lse_kg : (float*)(ws + p.off_lse);
+  float* o_kg = (float*)(ws + p.off_okg);
+  SharedArgs sa;
+  memset(&sa, 0, sizeof sa);
+  sa.t = v->dev;
+  sa.r = rows;
+  sa.B = p.B;
+  sa.Ng = Ng;
+  sa.gq = ws + p.off_gq;
+  sa.gpart = (double*)(ws + p.off_gpart);
+  sa.chunks = group_chunks(p.N, Ng, &sa.tn);
+  sa.sel_leaf = sel[2];
+  sa.KL = p.K[2];
+  sa.o_kg = o_kg;
+  sa.lse_kg = lse_kg;
+  PhaseMarks pm(opts, s);
+  hipError_t e = pm.mark(hipSuccess);
+  if (e == hipSuccess) e = pm.mark(launch_group_query(sa, s));
+  // the descent on the group rows; its own KG softmax lands in its workspace
+  if (e == hipSuccess)
+    e = launch_descent(pg, grows, v, ws, sel, (float*)(ws + pg.off_okg), (float*)(ws + pg.off_lse), s, pm);
+  if (e == hipSuccess) e = pm.mark(launch_shared_kg(sa, s));
+  if (e == hipSuccess) e = launch_seq_half(p, rows, v, seq_k, seq_v, out, opts, o_kg, lse_kg, ws, s, pm);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return ATLASKV_OK;
 }
 
 static const char* const kFlatPhaseNames[] = {"flat_kg_partial", "flat_kg_combine", "seq_attention",
@@ -620,7 +763,7 @@ atlaskv_status atlaskv_flat_workspace_size(atlaskv_tree_view v, const atlaskv_te
                                            const atlaskv_tensor* seq_k, size_t* bytes) {
   if (!bytes) return fail(ATLASKV_ERR_NULL, "bytes is NULL");
   Plan p;
-  atlaskv_status st = plan_call(q, v, seq_k, seq_k, nullptr, nullptr, nullptr, false, p, true);
+  atlaskv_status st = plan_call(q, v, seq_k, seq_k, nullptr, nullptr, nullptr, false, p, kModeFlat);
   if (st) return st;
   *bytes = p.total;
   return ATLASKV_OK;
@@ -631,7 +774,7 @@ atlaskv_status atlaskv_flat_attend_ex(const atlaskv_tensor* q, atlaskv_tree_view
                                       atlaskv_tensor* out, const atlaskv_attend_opts* opts) {
   Plan p;
   void* wsv = nullptr;
-  atlaskv_status st = check_all(q, v, seq_k, seq_v, nullptr, out, opts, p, &wsv, true);
+  atlaskv_status st = check_all(q, v, seq_k, seq_v, nullptr, out, opts, p, &wsv, kModeFlat);
   if (st) return st;
   if (v->described_only) return fail(ATLASKV_ERR_UNSUPPORTED, "a described-only view cannot run");
   if (p.R == 0) return ATLASKV_OK;
@@ -666,7 +809,7 @@ atlaskv_status atlaskv_flat_check_args(const atlaskv_tensor* q, atlaskv_tree_vie
                                        const atlaskv_tensor* out, const atlaskv_attend_opts* opts) {
   Plan p;
   void* ws = nullptr;
-  return check_all(q, v, seq_k, seq_v, nullptr, out, opts, p, &ws, true);
+  return check_all(q, v, seq_k, seq_v, nullptr, out, opts, p, &ws, kModeFlat);
 }
 
 }  // extern "C"

@@ -114,6 +114,20 @@ struct FlatArgs {
   float* lse_kg;              // [R]
 };
 
+// Shared selections: the real rows and their groups' leaf selections.
+struct SharedArgs {
+  TreeDev t;
+  RowsDev r;                  // the real rows (their own q / q_kg)
+  int B, Ng;                  // groups: [B, Ng, Hkv], Ng = N (per token) or 1 (per sequence)
+  void* gq;                   // [B, Ng, Hkv, d] group queries, tree dtype
+  double* gpart;              // [B*Ng*Hkv, chunks, d] fp64 partial sums over chunks of tn tokens
+  int chunks, tn;
+  const int32_t* sel_leaf;    // [B*Ng*Hkv, KL] leaves selected for each group, -1 padded
+  int KL;
+  float* o_kg;                // [R, d]
+  float* lse_kg;              // [R]
+};
+
 struct BuildStats {           // device-side result of tree validation
   int bad;                    // non-zero: malformed offsets
   int pad;
@@ -138,6 +152,9 @@ hipError_t launch_seq_attend(const SeqArgs& a, hipStream_t s);   // + λ merge w
 hipError_t launch_seq_combine(const SeqArgs& a, hipStream_t s);  // split partials: LSE combine + λ merge
 hipError_t launch_flat_partial(const FlatArgs& a, hipStream_t s);  // per (head, rows, key range)
 hipError_t launch_flat_combine(const FlatArgs& a, hipStream_t s);  // ranges -> o_kg, lse_kg
+hipError_t launch_group_query(const SharedArgs& a, hipStream_t s);  // member sums -> gq
+int group_chunks(int N, int Ng, int* tn);                           // token chunks of a group sum
+hipError_t launch_shared_kg(const SharedArgs& a, hipStream_t s);    // per-row softmax over group leaves
 int flat_row_tiles(int B, int N, int G);
 int flat_splits(int B, int N, int Hq, int Hkv, int64_t M, int dtype);
 int flat_split_len(int64_t M, int nsplit);

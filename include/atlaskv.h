@@ -238,6 +238,45 @@ atlaskv_status atlaskv_flat_check_args(const atlaskv_tensor* q, atlaskv_tree_vie
 int32_t atlaskv_flat_phase_count(void);
 const char* atlaskv_flat_phase_name(int32_t phase);
 
+/*
+ * Shared selections.  速读 › 怎么做的 picks the Top-K branches of the current
+ * query; its memory bound (the C_m·M^(1/3) + N term) reads like one selected
+ * key set shared by many tokens.  In this variant a group of rows shares one
+ * descent:
+ *   ATLASKV_SHARE_KV_GROUP  the G query heads of one KV head at one token
+ *                           (B*N*Hkv groups);
+ *   ATLASKV_SHARE_SEQUENCE  every token and query head of one KV head in one
+ *                           sequence (B*Hkv groups).
+ * The group's query is the exact sum of its members' KG queries rounded once
+ * (nearest, ties to even) to the tree's dtype; ranking nodes by it ranks them
+ * by the members' summed logits.  The sum is formed in fp64 (token chunks,
+ * then chunks), exact whenever it fits 53 bits, i.e. unless the members'
+ * magnitudes span more than ~2^40.
+ * The descent (roots -> mids -> leaves, Top-K per level, ties to the lower
+ * index) runs on the group queries; every row then takes the softmax of its
+ * own KG logits over its group's K_L selected leaves, and its own sequence
+ * half and λ merge as in atlaskv_hikvp_attend.  Arguments as
+ * atlaskv_hikvp_attend_ex plus `share`; opts->sel_root/sel_mid/sel_leaf, when
+ * given, receive the GROUP selections, [groups, K_x] in group order
+ * (b, n, g) or (b, g).  Workspace size from atlaskv_shared_workspace_size.
+ */
+typedef enum { ATLASKV_SHARE_KV_GROUP = 1, ATLASKV_SHARE_SEQUENCE = 2 } atlaskv_share;
+atlaskv_status atlaskv_shared_workspace_size(atlaskv_tree_view tree, const atlaskv_tensor* q,
+                                             const atlaskv_tensor* seq_k, const int32_t K_per_level[3],
+                                             int32_t share, size_t* bytes);
+atlaskv_status atlaskv_shared_attend_ex(const atlaskv_tensor* q, atlaskv_tree_view tree,
+                                        const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                        const int32_t K_per_level[3], int32_t share,
+                                        atlaskv_tensor* out, const atlaskv_attend_opts* opts);
+/* The argument checks of atlaskv_shared_attend_ex alone (pure host code). */
+atlaskv_status atlaskv_shared_check_args(const atlaskv_tensor* q, atlaskv_tree_view tree,
+                                         const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                         const int32_t K_per_level[3], int32_t share,
+                                         const atlaskv_tensor* out, const atlaskv_attend_opts* opts);
+/* Kernel phases of one shared-selection call, in launch order. */
+int32_t atlaskv_shared_phase_count(void);
+const char* atlaskv_shared_phase_name(int32_t phase);
+
 /* Message for the calling thread's most recent failed call ("" if none). */
 const char* atlaskv_last_error(void);
 

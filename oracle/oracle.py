@@ -257,9 +257,11 @@ def group_queries(prob: Problem, share):
 
     The group of row (b, n, h) is every row of the same sequence b and KV head
     g = h // G at token n (share = SHARE_KV_GROUP) or at any token
-    (SHARE_SEQUENCE).  Its query is the sum of the members' KG queries (fp64,
-    exact for stored values), rounded once to the storage type: ranking nodes
-    by it ranks them by the sum of the members' logits up to that rounding.
+    (SHARE_SEQUENCE).  Its query is the exact sum of the members' stored KG
+    queries, rounded once to the storage type: ranking nodes by it ranks them
+    by the sum of the members' logits up to that rounding.  math.fsum gives the
+    exact sum rounded to fp64, which is the exact sum itself whenever that
+    fits 53 bits (always, unless the members' magnitudes span ~2^40).
     """
     q, q_kg = prob._args[0], prob._kw["q_kg"]
     qa, dt = _host(q if q_kg is None else q_kg)
@@ -268,11 +270,18 @@ def group_queries(prob: Problem, share):
     B, N, Hq, d = x.shape
     s = prob.shape
     G = Hq // s["Hkv"]
-    g = x.reshape(B, N, s["Hkv"], G, d).sum(axis=3)                 # [B, N, Hkv, d]
-    if share == SHARE_SEQUENCE:
-        g = np.broadcast_to(g.sum(axis=1, keepdims=True), g.shape)
-    elif share != SHARE_KV_GROUP:
+    if share not in (SHARE_KV_GROUP, SHARE_SEQUENCE):
         raise ValueError("share must be SHARE_KV_GROUP or SHARE_SEQUENCE")
+    xg = x.reshape(B, N, s["Hkv"], G, d)
+    g = np.zeros((B, N, s["Hkv"], d))
+    for b in range(B):
+        for kv in range(s["Hkv"]):
+            if share == SHARE_SEQUENCE:
+                members = xg[b, :, kv].reshape(N * G, d)
+                g[b, :, kv] = [math.fsum(members[:, t]) for t in range(d)]
+            else:
+                for n in range(N):
+                    g[b, n, kv] = [math.fsum(xg[b, n, kv, :, t]) for t in range(d)]
     full = np.repeat(g, G, axis=2)                                   # back to [B, N, Hq, d]
     import torch
     if dt == BF16:

@@ -228,3 +228,25 @@ def test_flat_workspace_grows_with_leaves(lib):
     big = atlaskv.flat_workspace_size(_view(M=50000), q, None)
     assert 0 < small <= big
 
+
+def test_shared_phase_names_and_checks(lib):
+    assert atlaskv.shared_phase_names() == [
+        "group_query", "root_score_topk", "mid_bucket_gemm", "mid_topk", "leaf_bucket_link",
+        "leaf_score_stream", "leaf_score_overflow", "leaf_topk_kg_attention", "shared_kg_attention",
+        "seq_attention", "seq_split_combine"]
+    v = _view()
+    q = torch.zeros(1, 4, 4, 128, dtype=torch.bfloat16)
+    sk = torch.zeros(1, 6, 2, 128, dtype=torch.bfloat16)
+    ws = torch.zeros(4096, dtype=torch.uint8)
+    fake = type("W", (), {"data_ptr": lambda self: (ws.data_ptr() + 255) // 256 * 256,
+                          "numel": lambda self: 1 << 30})()
+    for share in (atlaskv.SHARE_KV_GROUP, atlaskv.SHARE_SEQUENCE):
+        assert atlaskv.shared_check_args(q, v, sk, sk, (2, 2, 4), share, q, workspace=fake) == atlaskv.OK
+        assert atlaskv.shared_check_args(q, v, sk, sk, (2, 2, 300), share, q, workspace=fake) == atlaskv.ERR_K
+        assert atlaskv.shared_workspace_size(v, q, sk, (2, 2, 4), share) > 0
+    assert atlaskv.shared_check_args(q, v, sk, sk, (2, 2, 4), 3, q, workspace=fake) == atlaskv.ERR_UNSUPPORTED
+    # a sequence group holds every token: no larger group rows than per token
+    a = atlaskv.shared_workspace_size(v, q, sk, (2, 2, 4), atlaskv.SHARE_SEQUENCE)
+    b = atlaskv.shared_workspace_size(v, q, sk, (2, 2, 4), atlaskv.SHARE_KV_GROUP)
+    assert a <= b
+
