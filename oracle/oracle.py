@@ -321,6 +321,112 @@ def shared_rows(prob: Problem, rows, share):
     return fin
 
 
+# ---------------------------------------------------------------------------
+# folded projections: one base-embedding tree for every head
+# ---------------------------------------------------------------------------
+
+def _as_f64(t):
+    a, dt = _host(t)
+    if dt == BF16:
+        return (a.view(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64), dt
+    return np.asarray(a, dtype=np.float64), dt
+
+
+def _round_to(x, dt):
+    """fp64 values rounded once to a storage type, as a torch tensor."""
+    import torch
+    if dt == BF16:
+        return torch.from_numpy(_round_bf16_bits(x).view(np.int16)).view(torch.bfloat16)
+    if dt == F32:
+        return torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32)))
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+
+
+def folded_query(q_kg, w_k):
+    """q'[b,n,h] = W_K[g]^T q_kg[b,n,h]: the exact sum of the products (math.fsum
+    over the head dim), rounded once to the storage type.  W_K [Hkv, d, D_E]
+    maps a base key k (width D_E) to the head's projected key W_K[g] k, so
+    <q_kg, W_K[g] k> = <q', k>."""
+    q, dt = _as_f64(q_kg)
+    w, _ = _as_f64(w_k)
+    B, N, Hq, d = q.shape
+    Hkv, d2, DE = w.shape
+    G = Hq // Hkv
+    out = np.zeros((B, N, Hq, DE))
+    for b in range(B):
+        for n in range(N):
+            for h in range(Hq):
+                prod = w[h // G] * q[b, n, h][:, None]          # [d, D_E], exact products
+                out[b, n, h] = [math.fsum(prod[:, j]) for j in range(DE)]
+    return _round_to(out, dt)
+
+
+def folded_rows(base_tree, q, w_k, w_v, seq_k, seq_v, K, rows, scale=None, q_kg=None):
+    """Folded-projection variant (方法细节 › KBLaM中的矩形注意力 gives the
+    projected keys and values W_K k and W_V v of per-layer heads; one base
+    tree serves every head): the descent over the base tree (root_k, mid_k,
+    leaf_k, leaf_v with one head, width D_E, offsets) runs on the folded
+    queries q'; the KG half of row (b, n, h) is W_V[g] applied to the
+    softmax-weighted base values, merged with the causal sequence half over
+    seq_k / seq_v [B, S, Hkv, d].  Returns dict(out, lse_kg, lse_seq, sel_R,
+    sel_I, sel_L, gap, o_kg)."""
+    import torch
+    root_k, mid_k, leaf_k, leaf_v, root_off, mid_off = base_tree
+    d = q.shape[-1]
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    qf = folded_query(q if q_kg is None else q_kg, w_k)
+    P = Problem(qf, root_k, mid_k, leaf_k, leaf_v, root_off, mid_off, None, None, K, scale=sc)
+    r = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+    ph1 = select_mids_rows(P, r)                 # roots and mids under q'
+    KL = int(K[2])
+    lv64, _ = _as_f64(leaf_v)
+    DE = lv64.shape[-1]
+    sel_L = np.full((len(r), KL), -1, np.int64)
+    gap = ph1["gap"].copy()
+    a = np.full(len(r), -np.inf)
+    o_base = np.zeros((len(r), DE))
+    for i, (b, n, h) in enumerate(r):
+        parents = [int(m) for m in ph1["sel_I"][i] if m >= 0]
+        cand, score = level_scores(P, b, n, h, 2, parents) if parents and KL > 0 else (np.zeros(0, np.int64), np.zeros(0))
+        pos = topk(score, cand, KL) if len(cand) and KL > 0 else np.zeros(0, np.int64)
+        sel_L[i, :len(pos)] = cand[pos]
+        ranked = sorted(range(len(cand)), key=lambda j: (-score[j], cand[j]))
+        if 0 < KL < len(cand):
+            s0, s1 = score[ranked[KL - 1]], score[ranked[KL]]
+            gap[i, 2] = abs(s0 - s1) / max(abs(s0), abs(s1)) if max(abs(s0), abs(s1)) > 0 else 0.0
+        if len(pos):
+            lg = score[pos]
+            a[i] = lg.max() + math.log(math.fsum(np.exp(lg - lg.max())))
+            w = np.exp(lg - a[i])
+            o_base[i] = w @ lv64[0, cand[pos]]
+    kg = dict(sel_R=ph1["sel_R"], sel_I=ph1["sel_I"], sel_L=sel_L, gap=gap, lse_kg=a, o_kg=o_base)
+    # the sequence half alone: the same oracle with the KG half emptied (K = 0)
+    # over a one-node stub tree with the layer's KV heads and head dim
+    sq = None
+    if seq_k is not None:
+        stub = torch.zeros(w_k.shape[0], 1, d, dtype=q.dtype)
+        off = torch.tensor([0, 1], dtype=torch.int64)
+        sq = hikvp_rows(Problem(q, stub, stub, stub, stub, off, off, seq_k, seq_v, (0, 0, 0), scale=sc),
+                        rows)
+    wv, _ = _as_f64(w_v)
+    G = q.shape[2] // w_k.shape[0]
+    o_kg = np.stack([wv[h // G] @ kg["o_kg"][i] for i, (b, n, h) in enumerate(r)]) if len(r) else np.zeros((0, d))
+    a = kg["lse_kg"]
+    if sq is None:
+        c = np.full(len(r), -np.inf)
+        o_seq = np.zeros_like(o_kg)
+    else:
+        c, o_seq = sq["lse_seq"], sq["o_seq"]
+    out = np.zeros_like(o_kg)
+    for i in range(len(r)):
+        if a[i] == -np.inf and c[i] == -np.inf:
+            raise RuntimeError("both halves empty")
+        lam = 0.0 if a[i] == -np.inf else (1.0 if c[i] == -np.inf else 1.0 / (1.0 + math.exp(c[i] - a[i])))
+        out[i] = lam * o_kg[i] + (1.0 - lam) * o_seq[i]
+    return dict(out=out, o_kg=o_kg, lse_kg=a, lse_seq=c, sel_R=kg["sel_R"], sel_I=kg["sel_I"],
+                sel_L=kg["sel_L"], gap=kg["gap"])
+
+
 def select_mids_rows(prob: Problem, rows):
     """Two-phase mode, phase 1: sel_R, sel_I, gaps for the given rows."""
     r, b, n, h = _rows(rows)

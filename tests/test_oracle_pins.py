@@ -630,3 +630,68 @@ def test_shared_group_query_rounds_the_sum_once(oracle_mod):
         # and it is within half a bf16 ulp of the exact sum
         assert np.all(np.abs(gq[b, n, h] - exact) <= np.abs(exact) * 2.0 ** -8 + 1e-300)
 
+
+# ---------------------------------------------------------------------------
+# folded projections (one base-embedding tree for every head)
+# ---------------------------------------------------------------------------
+
+def _base_tree(seed, DE, MR, MI, M, dtype=torch.float64):
+    c = synth.make_case("custom", seed=seed, ragged=True, dtype="f32", B=1, N=1, S_kv=1, Hq=1, Hkv=1,
+                        d=DE, M_R=MR, M_I=MI, M=M, K=(1, 1, 1))
+    return (c.root_k.to(dtype), c.mid_k.to(dtype), c.leaf_k.to(dtype), c.leaf_v.to(dtype),
+            c.root_off, c.mid_off)
+
+
+def test_folded_with_identity_projections_is_the_per_row_path(oracle_mod):
+    """One KV head, W_K = W_V = I (D_E = d): folding changes nothing, so the
+    result is the per-row descent over the base tree itself."""
+    d = 8
+    tree = _base_tree(140, d, 4, 15, 90)
+    c = _small_case(140, B=2, N=3, S=5, Hq=3, Hkv=1, d=d, MR=4, MI=15, M=90)
+    q, sk, sv = c.q.double(), c.seq_k.double(), c.seq_v.double()
+    eye = torch.eye(d, dtype=torch.float64)[None]
+    rows = oracle_mod.all_rows(c.B, c.N, c.Hq)
+    K = (2, 3, 5)
+    a = oracle_mod.folded_rows(tree, q, eye, eye, sk, sv, K, rows)
+    b = oracle_mod.hikvp_rows(oracle_mod.Problem(q, *tree[:4], tree[4], tree[5], sk, sv, K), rows)
+    for k in ("sel_R", "sel_I", "sel_L"):
+        np.testing.assert_array_equal(a[k], b[k])
+    np.testing.assert_allclose(a["out"], b["out"], rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_folded_equals_projected_per_head_trees(oracle_mod, seed):
+    """fp64 storage: scoring the base tree with W_K^T q equals scoring the
+    per-head projected tree W_K k with q, and W_V applied after the weighted
+    sum equals weighting the projected values W_V v: the folded variant must
+    equal the per-row descent over explicitly projected per-head trees."""
+    rng = np.random.default_rng(seed)
+    d, DE, Hkv, Hq = 6, 9, 2, 4
+    tree = _base_tree(150 + seed, DE, 4, 13, 110)
+    c = _small_case(150 + seed, B=2, N=3, S=4, Hq=Hq, Hkv=Hkv, d=d, MR=4, MI=13, M=110)
+    q, sk, sv = c.q.double(), c.seq_k.double(), c.seq_v.double()
+    wk = torch.from_numpy(rng.standard_normal((Hkv, d, DE)) / 3.0)
+    wv = torch.from_numpy(rng.standard_normal((Hkv, d, DE)) / 3.0)
+    proj = lambda t, w: torch.stack([t[0] @ w[g].T for g in range(Hkv)])   # [Hkv, M_x, d]
+    rk, mk, lk, lv, ro, mo = tree
+    K = (2, 4, 6)
+    rows = oracle_mod.all_rows(c.B, c.N, c.Hq)
+    a = oracle_mod.folded_rows(tree, q, wk, wv, sk, sv, K, rows)
+    b = oracle_mod.hikvp_rows(oracle_mod.Problem(q, proj(rk, wk), proj(mk, wk), proj(lk, wk), proj(lv, wv),
+                                                 ro, mo, sk, sv, K), rows)
+    for k in ("sel_R", "sel_I", "sel_L"):
+        np.testing.assert_array_equal(a[k], b[k])
+    np.testing.assert_allclose(a["out"], b["out"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(a["lse_kg"], b["lse_kg"], rtol=1e-12, atol=1e-12)
+
+
+def test_folded_query_rounds_the_exact_product_sum_once(oracle_mod):
+    rng = np.random.default_rng(7)
+    q = torch.from_numpy(rng.standard_normal((1, 2, 2, 8))).to(torch.bfloat16)
+    wk = torch.from_numpy(rng.standard_normal((1, 8, 5))).to(torch.bfloat16)
+    got = oracle_mod.folded_query(q, wk).float().double().numpy()
+    exact = np.einsum("bnht,td->bnhd", q.double().numpy(), wk.double().numpy()[0])
+    assert np.all(np.abs(got - exact) <= np.abs(exact) * 2.0 ** -8 + 1e-30)   # half a bf16 ulp
+    codes = oracle_mod._round_bf16_bits(exact.reshape(-1))
+    np.testing.assert_array_equal(got.reshape(-1), [_bf16_value(x) for x in codes])
+
