@@ -250,6 +250,9 @@ def main():
     ap.add_argument("--share", default="none", choices=["none", "kv-group", "sequence"],
                     help="shared selections: one descent per KV head and token, or per KV head "
                          "and sequence (pruned path only)")
+    ap.add_argument("--fold", action="store_true",
+                    help="folded projections: one-head base tree (head 0 of the workload's tree, width "
+                         "D_E = d) shared by all heads through random per-head W_K / W_V [Hkv, d, D_E]")
     ap.add_argument("--tree-placement", default="hbm", choices=["hbm", "host-leaves"],
                     help="host-leaves: leaf keys and values in pinned host memory, read by the "
                          "kernels over the host link (roots, mids, offsets stay in HBM)")
@@ -293,11 +296,27 @@ def main():
     tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
     flat = args.path == "flat"
     share = {"none": 0, "kv-group": atlaskv.SHARE_KV_GROUP, "sequence": atlaskv.SHARE_SEQUENCE}[args.share]
+    fold = args.fold
+    if fold and (flat or share):
+        print("--fold applies to the per-row pruned path only", file=sys.stderr)
+        sys.exit(2)
+    if fold:
+        # the base tree: head 0 of the workload's tree; per-head projections of the layer
+        tree.close()
+        base = [t[:1].contiguous() for t in (case.root_k, case.mid_k, case.leaf_k, case.leaf_v)]
+        tree = atlaskv.TreeView(*base, case.root_off, case.mid_off)
+        gen = torch.Generator(device=dev).manual_seed(17)
+        w_k = (torch.randn(case.Hkv, case.d, case.d, generator=gen, device=dev) / case.d ** 0.5).to(case.q.dtype)
+        w_v = (torch.randn(case.Hkv, case.d, case.d, generator=gen, device=dev) / case.d ** 0.5).to(case.q.dtype)
+        case.root_k, case.mid_k, case.leaf_k, case.leaf_v = base
+        torch.cuda.empty_cache()
     if flat and share:
         print("--share applies to the pruned path only", file=sys.stderr)
         sys.exit(2)
     if flat:
         ws = atlaskv.alloc_flat_workspace(tree, case.q, case.seq_k)
+    elif fold:
+        ws = atlaskv.alloc_folded_workspace(tree, case.q, w_k, case.seq_k, case.K)
     elif share:
         ws = atlaskv.alloc_shared_workspace(tree, case.q, case.seq_k, case.K, share)
     else:
@@ -306,7 +325,7 @@ def main():
     R = case.rows
     nsel = R if not share else case.B * (case.N if share == atlaskv.SHARE_KV_GROUP else 1) * case.Hkv
     sel = [torch.empty(nsel, k, dtype=torch.int32, device=dev) for k in case.K]
-    phases = (atlaskv.flat_phase_names() if flat else
+    phases = (atlaskv.flat_phase_names() if flat else atlaskv.folded_phase_names() if fold else
               atlaskv.shared_phase_names() if share else atlaskv.phase_names())
     stream = torch.cuda.current_stream(dev)
 
@@ -314,6 +333,11 @@ def main():
         if flat:
             atlaskv.flat_attend_ex(case.q, tree, case.seq_k, case.seq_v, out, workspace=ws,
                                    phase_events=events, stream=stream)
+            return
+        if fold:
+            atlaskv.folded_attend_ex(case.q, tree, w_k, w_v, case.seq_k, case.seq_v, case.K, out, workspace=ws,
+                                     sel_root=sel[0], sel_mid=sel[1], sel_leaf=sel[2], phase_events=events,
+                                     stream=stream)
             return
         if share:
             atlaskv.shared_attend_ex(case.q, tree, case.seq_k, case.seq_v, case.K, share, out,
@@ -380,7 +404,16 @@ def main():
         tree.close()
         return
     host_sel = [s.cpu().numpy() for s in sel]
-    ab = algorithmic_bytes(case, host_sel, share)
+    if fold:  # every row reads the one base tree: KV head 0 for the byte count
+        saved = (case.Hkv, case.Hq)
+        case.Hkv, case.Hq = 1, case.Hq
+        ab = algorithmic_bytes(case, host_sel, 0)
+        case.Hkv, case.Hq = saved
+        seq_fix = 2 * case.B * case.S_kv * case.Hkv * case.d * (2 if case.dtype == "bf16" else 4)
+        ab["_total"] += seq_fix - ab["seq_attention"]
+        ab["_parts"]["sequence_kv"] = ab["seq_attention"] = seq_fix
+    else:
+        ab = algorithmic_bytes(case, host_sel, share)
     recall = None
     if share:
         # leaves of the per-row selection that the shared selection also holds
@@ -418,7 +451,7 @@ def main():
         "config": {"workload": case.name, "B": case.B, "N": case.N, "S_kv": case.S_kv, "Hq": case.Hq,
                    "Hkv": case.Hkv, "d": case.d, "tree": [case.M_R, case.M_I, case.M], "K": list(case.K),
                    "tokens_per_step": tokens, "parallelism": "single GPU",
-                   "tree_placement": args.tree_placement, "share": args.share},
+                   "tree_placement": args.tree_placement, "share": args.share, "fold": fold},
         "path_hbm": {"compulsory_bytes": ab["_total"], "achieved_gbps": path_gbps,
                      "frac_of_peak": path_gbps / PEAK_HBM_GBPS, "parts": ab["_parts"],
                      "cold_ms_per_step": cold},

@@ -29,7 +29,9 @@ EXPORTS = ["atlaskv_build_tree_view", "atlaskv_destroy_tree_view", "atlaskv_tree
            "atlaskv_flat_workspace_size", "atlaskv_flat_attend_ex", "atlaskv_flat_check_args",
            "atlaskv_flat_phase_count", "atlaskv_flat_phase_name", "atlaskv_shared_workspace_size",
            "atlaskv_shared_attend_ex", "atlaskv_shared_check_args", "atlaskv_shared_phase_count",
-           "atlaskv_shared_phase_name", "atlaskv_phase_count",
+           "atlaskv_shared_phase_name", "atlaskv_folded_workspace_size", "atlaskv_folded_attend_ex",
+           "atlaskv_folded_check_args", "atlaskv_folded_phase_count", "atlaskv_folded_phase_name",
+           "atlaskv_phase_count",
            "atlaskv_phase_name", "atlaskv_last_error", "atlaskv_version"]
 
 
@@ -89,6 +91,9 @@ def lib():
                                                P(AttendOpts)]
         L.atlaskv_shared_check_args.argtypes = [T, ctypes.c_void_p, T, T, i32x3, ctypes.c_int32, T,
                                                 P(AttendOpts)]
+        L.atlaskv_folded_workspace_size.argtypes = [ctypes.c_void_p, T, T, T, i32x3, P(ctypes.c_size_t)]
+        L.atlaskv_folded_attend_ex.argtypes = [T, ctypes.c_void_p, T, T, T, T, i32x3, T, P(AttendOpts)]
+        L.atlaskv_folded_check_args.argtypes = [T, ctypes.c_void_p, T, T, T, T, i32x3, T, P(AttendOpts)]
         for name in EXPORTS[:-4]:
             getattr(L, name).restype = ctypes.c_int
         L.atlaskv_flat_phase_count.restype = ctypes.c_int32
@@ -97,6 +102,9 @@ def lib():
         L.atlaskv_shared_phase_count.restype = ctypes.c_int32
         L.atlaskv_shared_phase_name.argtypes = [ctypes.c_int32]
         L.atlaskv_shared_phase_name.restype = ctypes.c_char_p
+        L.atlaskv_folded_phase_count.restype = ctypes.c_int32
+        L.atlaskv_folded_phase_name.argtypes = [ctypes.c_int32]
+        L.atlaskv_folded_phase_name.restype = ctypes.c_char_p
         L.atlaskv_phase_count.restype = ctypes.c_int32
         L.atlaskv_phase_name.argtypes = [ctypes.c_int32]
         L.atlaskv_phase_name.restype = ctypes.c_char_p
@@ -358,6 +366,47 @@ def shared_check_args(q, tree, seq_k, seq_v, K, share, out, **opts):
 def shared_phase_names():
     L = lib()
     return [L.atlaskv_shared_phase_name(i).decode() for i in range(L.atlaskv_shared_phase_count())]
+
+
+def folded_workspace_size(tree, q, w_k, seq_k, K):
+    n = ctypes.c_size_t()
+    dq, dw, dk = describe(q), describe(w_k), describe(seq_k)
+    _raise(lib().atlaskv_folded_workspace_size(tree.handle, ctypes.byref(dq), ctypes.byref(dw), _ref(dk),
+                                               _k(K), ctypes.byref(n)))
+    return n.value
+
+
+def alloc_folded_workspace(tree, q, w_k, seq_k, K):
+    n = folded_workspace_size(tree, q, w_k, seq_k, K)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def folded_attend_ex(q, tree, w_k, w_v, seq_k, seq_v, K, out, **opts):
+    """atlaskv_folded_attend_ex: a one-head base tree of width D_E, per-head
+    projections w_k / w_v [Hkv, d, D_E]."""
+    dq, dwk, dwv = describe(q), describe(w_k), describe(w_v)
+    dk, dv, do = describe(seq_k), describe(seq_v), describe(out)
+    o, keep = _opts(device=q.device, **opts)
+    _raise(lib().atlaskv_folded_attend_ex(ctypes.byref(dq), tree.handle, ctypes.byref(dwk), ctypes.byref(dwv),
+                                          _ref(dk), _ref(dv), _k(K), ctypes.byref(do), ctypes.byref(o)))
+    del keep
+    return out
+
+
+def folded_check_args(q, tree, w_k, w_v, seq_k, seq_v, K, out, **opts):
+    dq, dwk, dwv = describe(q), describe(w_k), describe(w_v)
+    dk, dv, do = describe(seq_k), describe(seq_v), describe(out)
+    o, keep = _opts(**opts)
+    st = lib().atlaskv_folded_check_args(_ref(dq), tree.handle if tree is not None else None, _ref(dwk),
+                                         _ref(dwv), _ref(dk), _ref(dv), _k(K) if K is not None else None,
+                                         _ref(do), ctypes.byref(o))
+    del keep
+    return st
+
+
+def folded_phase_names():
+    L = lib()
+    return [L.atlaskv_folded_phase_name(i).decode() for i in range(L.atlaskv_folded_phase_count())]
 
 
 def phase_names():

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libatlaskv.so")
-SOURCES = ["atlaskv_api.hip", "hikvp_select.hip", "hikvp_seq.hip", "hikvp_tree.hip", "hikvp_flat.hip", "hikvp_shared.hip"]
+SOURCES = ["atlaskv_api.hip", "hikvp_select.hip", "hikvp_seq.hip", "hikvp_tree.hip", "hikvp_flat.hip", "hikvp_shared.hip", "hikvp_folded.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

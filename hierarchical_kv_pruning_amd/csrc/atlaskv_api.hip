@@ -170,6 +170,8 @@ struct Plan {
   size_t off_fpart;
   int group_rows;                                    // shared selections only
   size_t off_gq, off_gpart;
+  int fold_Hkv, fold_d, fold_kg_empty;               // folded projections only
+  size_t off_qf;
 };
 
 // Candidate capacity per row at the mid level (children of K_R distinct
@@ -360,6 +362,104 @@ void fill_rows(RowsDev& r, const atlaskv_tensor* q, const atlaskv_attend_opts* o
   r.scale = p.scale;
 }
 
+// Folded projections: the tree is a one-head base tree of width D_E; the
+// layer has Hkv heads of width d with W_K, W_V [Hkv, d, D_E].  pd receives the
+// plan of the descent on the folded rows [B, N, Hq, D_E] (unset when the KG
+// half is empty).
+atlaskv_status plan_folded(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
+                           const atlaskv_tensor* w_k, const atlaskv_tensor* w_v,
+                           const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v, const int32_t Kpl[3],
+                           const atlaskv_tensor* out, const atlaskv_attend_opts* opts, bool need_out,
+                           Plan& p, Plan& pd) {
+  atlaskv_status st;
+  memset(&p, 0, sizeof p);
+  memset(&pd, 0, sizeof pd);
+  if (!v) return fail(ATLASKV_ERR_NULL, "tree view is NULL");
+  if (!Kpl) return fail(ATLASKV_ERR_NULL, "K_per_level is NULL");
+  const TreeDev& t = v->dev;
+  if (t.Hkv != 1) return fail(ATLASKV_ERR_SHAPE, "folded projections need a one-head base tree (Hkv=%d)", t.Hkv);
+  if ((st = check_tensor(w_k, "w_k", 3, true))) return st;
+  if ((st = check_tensor(w_v, "w_v", 3, true))) return st;
+  if (w_k->dtype != t.dtype || w_v->dtype != t.dtype)
+    return fail(ATLASKV_ERR_DTYPE, "w_k / w_v dtype differs from the tree's");
+  const int64_t Hkv = w_k->shape[0], d = w_k->shape[1];
+  for (int i = 0; i < 3; ++i)
+    if (w_v->shape[i] != w_k->shape[i]) return fail(ATLASKV_ERR_SHAPE, "w_v shape differs from w_k's");
+  if (w_k->shape[2] != t.d)
+    return fail(ATLASKV_ERR_SHAPE, "w_k is [Hkv, d, D_E] with D_E = the tree width %d", t.d);
+  if (d != 64 && d != 128) return fail(ATLASKV_ERR_UNSUPPORTED, "head dim d must be 64 or 128");
+  if (Hkv < 1) return fail(ATLASKV_ERR_SHAPE, "w_k has no heads");
+  if ((st = check_tensor(q, "q", 4, true))) return st;
+  if (q->dtype != t.dtype) return fail(ATLASKV_ERR_DTYPE, "q dtype differs from the tree's");
+  if (q->shape[3] != d) return fail(ATLASKV_ERR_SHAPE, "q head dim differs from w_k's d");
+  const int64_t B = q->shape[0], N = q->shape[1], Hq = q->shape[2];
+  if (Hq < 1 || Hq % Hkv) return fail(ATLASKV_ERR_SHAPE, "Hq is not a multiple of Hkv");
+  if (B * N * Hq >= kIndexLimit) return fail(ATLASKV_ERR_UNSUPPORTED, "B*N*Hq must be below 2^31");
+  if (opts && opts->q_kg) {
+    if ((st = check_tensor(opts->q_kg, "q_kg", 4, true))) return st;
+    if (opts->q_kg->dtype != q->dtype) return fail(ATLASKV_ERR_DTYPE, "q_kg dtype differs from q's");
+    for (int i = 0; i < 4; ++i)
+      if (opts->q_kg->shape[i] != q->shape[i]) return fail(ATLASKV_ERR_SHAPE, "q_kg shape differs from q's");
+  }
+  if ((seq_k == nullptr) != (seq_v == nullptr))
+    return fail(ATLASKV_ERR_NULL, "seq_k and seq_v must both be given or both be NULL");
+  int64_t S = 0;
+  if (seq_k) {
+    if ((st = check_tensor(seq_k, "seq_k", 4, true))) return st;
+    if ((st = check_tensor(seq_v, "seq_v", 4, true))) return st;
+    if (seq_k->dtype != q->dtype || seq_v->dtype != q->dtype)
+      return fail(ATLASKV_ERR_DTYPE, "sequence K/V dtype differs from q's");
+    for (int i = 0; i < 4; ++i)
+      if (seq_v->shape[i] != seq_k->shape[i]) return fail(ATLASKV_ERR_SHAPE, "seq_v shape differs from seq_k's");
+    if (seq_k->shape[0] != B || seq_k->shape[2] != Hkv || seq_k->shape[3] != d)
+      return fail(ATLASKV_ERR_SHAPE, "seq_k must be [B, S_kv, Hkv, d]");
+    S = seq_k->shape[1];
+    if (S < N) return fail(ATLASKV_ERR_SHAPE, "S_kv=%lld < N=%lld", (long long)S, (long long)N);
+    if (S >= kIndexLimit) return fail(ATLASKV_ERR_UNSUPPORTED, "S_kv must be below 2^31");
+  }
+  if (need_out) {
+    if ((st = check_tensor(out, "out", 4, false))) return st;
+    if (out->dtype != q->dtype && out->dtype != ATLASKV_F32)
+      return fail(ATLASKV_ERR_DTYPE, "out dtype must be q's dtype or fp32");
+    for (int i = 0; i < 4; ++i)
+      if (out->shape[i] != q->shape[i]) return fail(ATLASKV_ERR_SHAPE, "out shape differs from q's");
+  }
+  for (int i = 0; i < 3; ++i)
+    if (Kpl[i] < 0 || Kpl[i] > kMaxK) return fail(ATLASKV_ERR_K, "K[%d]=%d outside 0..%d", i, Kpl[i], kMaxK);
+  const bool kg_empty = Kpl[0] == 0 || Kpl[1] == 0 || Kpl[2] == 0 || t.count[0] == 0 || t.count[1] == 0 ||
+                        t.count[2] == 0;
+  if (kg_empty && !seq_k)
+    return fail(ATLASKV_ERR_K, "both the KG half (K or tree empty) and the sequence half are empty");
+  double scale = 1.0 / sqrt((double)d);
+  if (opts && opts->scale != 0.0f) {
+    if (!(opts->scale > 0.0f) || isinf(opts->scale))
+      return fail(ATLASKV_ERR_UNSUPPORTED, "scale must be positive and finite");
+    scale = (double)opts->scale;
+  }
+  p.B = (int)B; p.N = (int)N; p.Hq = (int)Hq; p.S = (int)S;
+  p.R = (int)(B * N * Hq);
+  p.G = (int)(Hq / Hkv);
+  p.scale = scale;
+  for (int i = 0; i < 3; ++i) p.K[i] = Kpl[i];
+  p.fold_Hkv = (int)Hkv;
+  p.fold_d = (int)d;
+  p.fold_kg_empty = kg_empty;
+  size_t o = 0;
+  if (!kg_empty) {
+    atlaskv_tensor qd = group_rows_desc(B, N, (int)Hq, t.d, t.dtype, (void*)(uintptr_t)256);
+    if ((st = plan_call(&qd, v, nullptr, nullptr, Kpl, nullptr, nullptr, false, pd, kModeHikvp))) return st;
+    o = align256(pd.total);
+  }
+  const size_t R = (size_t)p.R;
+  p.off_qf = o;   o = align256(o + R * (size_t)t.d * esize(t.dtype));
+  p.off_okg = o;  o = align256(o + R * (size_t)d * 4);
+  p.off_lse = o;  o = align256(o + R * 4);
+  p.nsplit = seq_splits(p.B, p.N, (int)Hkv, p.S);
+  p.off_part = o; o = align256(o + (p.nsplit > 1 ? R * (size_t)p.nsplit * (d + 2) * 4 : 0));
+  p.total = o;
+  return ATLASKV_OK;
+}
+
 // Optional timing events at phase boundaries: event 0 before the first
 // kernel, event i after phase i-1.
 struct PhaseMarks {
@@ -379,7 +479,7 @@ struct PhaseMarks {
 
 // Sequence half (背景知识与设计原则 › 自注意力层机制) and the λ merge with the
 // KG half held in o_kg / lse_kg: two phases (attention, split combine).
-hipError_t launch_seq_half(const Plan& p, const RowsDev& rows, const atlaskv_tree_view_s* v,
+hipError_t launch_seq_half(const Plan& p, const RowsDev& rows, int Hkv, int d, int dtype,
                            const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
                            const atlaskv_tensor* out, const atlaskv_attend_opts* opts, float* o_kg,
                            float* lse_kg, char* ws, hipStream_t s, PhaseMarks& pm) {
@@ -387,9 +487,9 @@ hipError_t launch_seq_half(const Plan& p, const RowsDev& rows, const atlaskv_tre
   memset(&sa, 0, sizeof sa);
   sa.r = rows;
   sa.S = p.S;
-  sa.Hkv = v->dev.Hkv;
-  sa.d = v->dev.d;
-  sa.dtype = v->dev.dtype;
+  sa.Hkv = Hkv;
+  sa.d = d;
+  sa.dtype = dtype;
   if (seq_k) {
     sa.k = seq_k->data;
     sa.v = seq_v->data;
@@ -643,7 +743,7 @@ atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vie
   PhaseMarks pm(opts, s);
   hipError_t e = pm.mark(hipSuccess);
   if (e == hipSuccess) e = launch_descent(p, rows, v, ws, sel, o_kg, lse_kg, s, pm);
-  if (e == hipSuccess) e = launch_seq_half(p, rows, v, seq_k, seq_v, out, opts, o_kg, lse_kg, ws, s, pm);
+  if (e == hipSuccess) e = launch_seq_half(p, rows, v->dev.Hkv, v->dev.d, v->dev.dtype, seq_k, seq_v, out, opts, o_kg, lse_kg, ws, s, pm);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return ATLASKV_OK;
 }
@@ -744,7 +844,113 @@ atlaskv_status atlaskv_shared_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vi
   if (e == hipSuccess)
     e = launch_descent(pg, grows, v, ws, sel, (float*)(ws + pg.off_okg), (float*)(ws + pg.off_lse), s, pm);
   if (e == hipSuccess) e = pm.mark(launch_shared_kg(sa, s));
-  if (e == hipSuccess) e = launch_seq_half(p, rows, v, seq_k, seq_v, out, opts, o_kg, lse_kg, ws, s, pm);
+  if (e == hipSuccess) e = launch_seq_half(p, rows, v->dev.Hkv, v->dev.d, v->dev.dtype, seq_k, seq_v, out, opts, o_kg, lse_kg, ws, s, pm);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return ATLASKV_OK;
+}
+
+static const char* const kFoldedPhaseNames[] = {
+    "fold_query", "root_score_topk", "mid_bucket_gemm", "mid_topk", "leaf_bucket_link",
+    "leaf_score_stream", "leaf_score_overflow", "leaf_topk_kg_attention", "unfold_values",
+    "seq_attention", "seq_split_combine"};
+static const int kFoldedPhases = (int)(sizeof kFoldedPhaseNames / sizeof kFoldedPhaseNames[0]);
+
+int32_t atlaskv_folded_phase_count(void) { return kFoldedPhases; }
+
+const char* atlaskv_folded_phase_name(int32_t i) {
+  return (i >= 0 && i < kFoldedPhases) ? kFoldedPhaseNames[i] : nullptr;
+}
+
+atlaskv_status atlaskv_folded_workspace_size(atlaskv_tree_view v, const atlaskv_tensor* q,
+                                             const atlaskv_tensor* w_k, const atlaskv_tensor* seq_k,
+                                             const int32_t K[3], size_t* bytes) {
+  if (!bytes) return fail(ATLASKV_ERR_NULL, "bytes is NULL");
+  Plan p, pd;
+  atlaskv_status st = plan_folded(q, v, w_k, w_k, seq_k, seq_k, K, nullptr, nullptr, false, p, pd);
+  if (st) return st;
+  *bytes = p.total;
+  return ATLASKV_OK;
+}
+
+static atlaskv_status check_folded(const atlaskv_tensor* q, atlaskv_tree_view v, const atlaskv_tensor* w_k,
+                                   const atlaskv_tensor* w_v, const atlaskv_tensor* seq_k,
+                                   const atlaskv_tensor* seq_v, const int32_t K[3], const atlaskv_tensor* out,
+                                   const atlaskv_attend_opts* opts, Plan& p, Plan& pd, void** ws) {
+  atlaskv_status st = plan_folded(q, v, w_k, w_v, seq_k, seq_v, K, out, opts, true, p, pd);
+  if (st) return st;
+  void* w = (opts && opts->workspace) ? opts->workspace : v->workspace;
+  size_t wb = (opts && opts->workspace) ? opts->workspace_bytes : v->workspace_bytes;
+  if (p.R > 0) {
+    if (!w) return fail(ATLASKV_ERR_WORKSPACE, "no workspace (need %zu bytes)", p.total);
+    if (((uintptr_t)w) % 256) return fail(ATLASKV_ERR_WORKSPACE, "workspace not 256-byte aligned");
+    if (wb < p.total) return fail(ATLASKV_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", wb, p.total);
+  }
+  *ws = w;
+  return ATLASKV_OK;
+}
+
+atlaskv_status atlaskv_folded_check_args(const atlaskv_tensor* q, atlaskv_tree_view v,
+                                         const atlaskv_tensor* w_k, const atlaskv_tensor* w_v,
+                                         const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                         const int32_t K[3], const atlaskv_tensor* out,
+                                         const atlaskv_attend_opts* opts) {
+  Plan p, pd;
+  void* ws = nullptr;
+  return check_folded(q, v, w_k, w_v, seq_k, seq_v, K, out, opts, p, pd, &ws);
+}
+
+atlaskv_status atlaskv_folded_attend_ex(const atlaskv_tensor* q, atlaskv_tree_view v,
+                                        const atlaskv_tensor* w_k, const atlaskv_tensor* w_v,
+                                        const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                        const int32_t K[3], atlaskv_tensor* out,
+                                        const atlaskv_attend_opts* opts) {
+  Plan p, pd;
+  void* wsv = nullptr;
+  atlaskv_status st = check_folded(q, v, w_k, w_v, seq_k, seq_v, K, out, opts, p, pd, &wsv);
+  if (st) return st;
+  if (v->described_only) return fail(ATLASKV_ERR_UNSUPPORTED, "a described-only view cannot run");
+  if (p.R == 0) return ATLASKV_OK;
+  hipStream_t s = (opts && opts->stream) ? (hipStream_t)opts->stream : v->stream;
+  char* ws = (char*)wsv;
+  RowsDev rows;
+  fill_rows(rows, q, opts, p);
+  float* lse_kg = (opts && opts->lse_kg) ? opts->lse_kg : (float*)(ws + p.off_lse);
+  float* o_kg = (float*)(ws + p.off_okg);
+  FoldArgs fa;
+  memset(&fa, 0, sizeof fa);
+  fa.r = rows;
+  fa.w_k = w_k->data;
+  fa.w_v = w_v->data;
+  fa.wks[0] = w_k->stride[0]; fa.wks[1] = w_k->stride[1];
+  fa.wvs[0] = w_v->stride[0]; fa.wvs[1] = w_v->stride[1];
+  fa.d = p.fold_d;
+  fa.DE = v->dev.d;
+  fa.dtype = v->dev.dtype;
+  fa.qf = ws + p.off_qf;
+  fa.o_base = p.fold_kg_empty ? nullptr : (const float*)(ws + pd.off_okg);
+  fa.o_kg = o_kg;
+  fa.lse_kg = lse_kg;
+  PhaseMarks pm(opts, s);
+  hipError_t e = pm.mark(hipSuccess);
+  if (p.fold_kg_empty) {
+    // no descent: seven empty phases keep the event numbering
+    for (int i = 0; i < 8 && e == hipSuccess; ++i) e = pm.mark(hipSuccess);
+  } else {
+    e = pm.mark(launch_fold_query(fa, s));
+    atlaskv_tensor qd = group_rows_desc(p.B, p.N, p.Hq, v->dev.d, v->dev.dtype, fa.qf);
+    RowsDev frows;
+    fill_rows(frows, &qd, nullptr, pd);
+    frows.scale = p.scale;
+    int32_t* sel[3];
+    int32_t* user_sel[3] = {opts ? opts->sel_root : nullptr, opts ? opts->sel_mid : nullptr,
+                            opts ? opts->sel_leaf : nullptr};
+    for (int i = 0; i < 3; ++i) sel[i] = user_sel[i] ? user_sel[i] : (int32_t*)(ws + pd.off_sel[i]);
+    if (e == hipSuccess) e = launch_descent(pd, frows, v, ws, sel, (float*)(ws + pd.off_okg), lse_kg, s, pm);
+  }
+  if (e == hipSuccess) e = pm.mark(launch_unfold_values(fa, p.fold_kg_empty != 0, s));
+  if (e == hipSuccess)
+    e = launch_seq_half(p, rows, p.fold_Hkv, p.fold_d, v->dev.dtype, seq_k, seq_v, out, opts, o_kg, lse_kg, ws,
+                        s, pm);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return ATLASKV_OK;
 }
@@ -799,7 +1005,7 @@ atlaskv_status atlaskv_flat_attend_ex(const atlaskv_tensor* q, atlaskv_tree_view
   // KG half over every leaf, then the sequence half and the λ merge as in the pruned path
   if (e == hipSuccess) e = pm.mark(launch_flat_partial(fa, s));
   if (e == hipSuccess) e = pm.mark(launch_flat_combine(fa, s));
-  if (e == hipSuccess) e = launch_seq_half(p, rows, v, seq_k, seq_v, out, opts, o_kg, lse_kg, ws, s, pm);
+  if (e == hipSuccess) e = launch_seq_half(p, rows, v->dev.Hkv, v->dev.d, v->dev.dtype, seq_k, seq_v, out, opts, o_kg, lse_kg, ws, s, pm);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return ATLASKV_OK;
 }

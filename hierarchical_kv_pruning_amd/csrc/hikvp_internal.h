@@ -128,6 +128,19 @@ struct SharedArgs {
   float* lse_kg;              // [R]
 };
 
+// Folded projections: the layer's rows, its per-head W_K / W_V [Hkv, d, D_E].
+struct FoldArgs {
+  RowsDev r;                  // the layer's rows (q_kg of width d)
+  const void* w_k;            // [Hkv, d, D_E]: projected key of head g = W_K[g] k
+  const void* w_v;            // [Hkv, d, D_E]
+  int64_t wks[2], wvs[2];     // element strides of head and row (innermost 1)
+  int d, DE, dtype;
+  void* qf;                   // [R, D_E] folded queries W_K[g]^T q_kg, tree dtype
+  const float* o_base;        // [R, D_E] softmax-weighted base values (the descent's KG half)
+  float* o_kg;                // [R, d]
+  float* lse_kg;              // [R] (written only when the KG half is empty)
+};
+
 struct BuildStats {           // device-side result of tree validation
   int bad;                    // non-zero: malformed offsets
   int pad;
@@ -155,6 +168,8 @@ hipError_t launch_flat_combine(const FlatArgs& a, hipStream_t s);  // ranges -> 
 hipError_t launch_group_query(const SharedArgs& a, hipStream_t s);  // member sums -> gq
 int group_chunks(int N, int Ng, int* tn);                           // token chunks of a group sum
 hipError_t launch_shared_kg(const SharedArgs& a, hipStream_t s);    // per-row softmax over group leaves
+hipError_t launch_fold_query(const FoldArgs& a, hipStream_t s);                  // q' = W_K^T q
+hipError_t launch_unfold_values(const FoldArgs& a, bool kg_empty, hipStream_t s);  // o_kg = W_V o_base
 int flat_row_tiles(int B, int N, int G);
 int flat_splits(int B, int N, int Hq, int Hkv, int64_t M, int dtype);
 int flat_split_len(int64_t M, int nsplit);

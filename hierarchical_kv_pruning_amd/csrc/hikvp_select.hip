@@ -466,59 +466,105 @@ __global__ void k_bucket_link(StepArgs a) {
   }
 }
 
-template <class E, int D, int MB>
-__device__ inline void score_members(const StepArgs& a, const char* kb, int F, int m, const int* rows,
-                                     const int* bases, const float (*qf)[E::kEPV], int lane) {
-  constexpr int EPV = E::kEPV, LPK = D / EPV, KPW = 64 / LPK, U = 4;
-  const int j = lane % LPK, sub = lane / LPK;
-  const int64_t rsb = a.t.rs[2] * E::kBytes;
-  for (int c0 = 0; c0 < F; c0 += KPW * U) {
-    uint4 kv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + u * KPW + sub;
-      kv[u] = c < F ? *(const uint4*)(kb + c * rsb + j * 16) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + u * KPW + sub;
-      float kf[EPV];
-      unpack<E>(kv[u], kf);
-#pragma unroll
-      for (int mm = 0; mm < MB; ++mm) {
-        if (mm >= m) break;
-        float s = 0.f;
-#pragma unroll
-        for (int t = 0; t < EPV; ++t) s = fmaf(qf[mm][t], kf[t], s);
-        s = group_sum<LPK>(s);
-        if (j == 0 && c < F) a.leaf_scores[(int64_t)rows[mm] * a.c2max + bases[mm] + c] = s;
-      }
-    }
-  }
-}
-
-template <class E>
-__device__ inline void load_q_chunk(const StepArgs& a, int row, int j, float* qf) {
-  int b, n, h;
-  decode_row(a.r, row, b, n, h);
-  const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes;
-  unpack<E>(*(const uint4*)(qp + j * 16), qf);
-}
-
-// One wave per bucket on half-split MFMA tiles: a group of up to 8 member rows
-// is the M side and the span's keys the N side.  A round covers 8*TU keys; in
-// its tile u, item i is key t0 + i*TU + u, so every load instruction reads
-// eight whole 128-byte lines and each lane ends the round holding TU
-// consecutive scores per member, written with one 16-byte store.  A bucket
-// with more than 8 members makes a second pass over its span (mostly L2 hits).
+// Scores of one group of up to 8 member rows of a bucket over its leaf span,
+// on half-split MFMA tiles: the group is the M side and the span's keys the N
+// side.  Lanes g0 .. g0+7 of mem hold the members (row, first leaf slot),
+// gcnt of them valid.  A round covers 8*TU keys; in its tile u, item i is key
+// t0 + i*TU + u, so every load instruction reads eight whole 128-byte lines
+// and each lane ends the round holding TU consecutive scores per member,
+// written with one 16-byte store.  Every member's scores go through exactly
+// this arithmetic, whichever group or kernel it lands in, so they do not
+// depend on the (atomic) order in which members joined the bucket.
 template <class E, int D>
-__global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
+__device__ inline void score_member_group(const StepArgs& a, const char* kp, int64_t rsb, int F, int2 mem,
+                                          int g0, int gcnt, float* junk, int lane) {
   constexpr int RB = D * E::kBytes;        // bytes per key row
   constexpr int KP = RB / 128;             // 16-byte pieces per lane per tile
   constexpr int TU = 4;                    // tiles per round = consecutive keys per lane
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
   const int quad = lane >> 4, item = lane & 7;
   const bool owner = lane < 32 && (lane & 15) < 8;   // holds combined scores
+  // A fragment: member `item`, zeros past the members
+  uint4 afr[KP];
+  const int row = __shfl(mem.x, g0 + item);
+  if (item < gcnt) {
+    int b, n, h;
+    decode_row(a.r, row, b, n, h);
+    const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes + split_off(lane, 0);
+#pragma unroll
+    for (int m = 0; m < KP; ++m) afr[m] = *(const uint4*)(qp + m * 128);
+  } else {
+#pragma unroll
+    for (int m = 0; m < KP; ++m) afr[m] = make_uint4(0, 0, 0, 0);
+  }
+  // owners store members 4*quad + vv, keys t0 + item*TU .. + TU-1
+  float* dst[4];
+#pragma unroll
+  for (int vv = 0; vv < 4; ++vv) {
+    const int ms = 4 * (quad & 1) + vv;
+    const int srow = __shfl(mem.x, g0 + ms), sbase = __shfl(mem.y, g0 + ms);
+    dst[vv] = (owner && ms < gcnt) ? a.leaf_scores + (int64_t)srow * a.c2max + sbase + item * TU : nullptr;
+  }
+  // Each round issues its loads, then writes the previous round's scores,
+  // then waits for the loads.  The memory counter completes in issue
+  // order, stores included, so every round issues the same four 16-byte
+  // stores (lanes with nothing to write aim at this wave's junk slot) and
+  // a fixed number of loads (keys past the span re-read its last row):
+  // the wait for a round's loads then never covers the stores after them.
+  float4_t prev[TU];
+#pragma unroll
+  for (int u = 0; u < TU; ++u) prev[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+  int pt0 = -1;                        // round held in prev, -1 none
+  auto load_round = [&](int t0, uint4 (&bfr)[TU][KP]) {
+#pragma unroll
+    for (int u = 0; u < TU; ++u) {
+      const int c = min(t0 + item * TU + u, F - 1);
+      const char* p = kp + (int64_t)c * rsb;
+#pragma unroll
+      for (int m = 0; m < KP; ++m) bfr[u][m] = load_nt(p + m * 128);
+    }
+  };
+  auto store_full = [&]() {            // prev holds a full round (or none)
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv) {
+      float* d = (pt0 >= 0 && dst[vv]) ? dst[vv] + pt0 : junk;
+#pragma unroll
+      for (int u = 0; u < TU; u += 4)
+        store4u(d + u, prev[u][vv], prev[u + 1][vv], prev[u + 2][vv], prev[u + 3][vv]);
+    }
+  };
+  int t0 = 0;
+  for (; t0 + 8 * TU <= F; t0 += 8 * TU) {
+    uint4 bfr[TU][KP];
+    load_round(t0, bfr);
+    store_full();
+#pragma unroll
+    for (int u = 0; u < TU; ++u) prev[u] = split_combine(tile_dot<E, KP>(afr, bfr[u]), lane);
+    pt0 = t0;
+  }
+  if (t0 < F) {  // last, partial round
+    uint4 bfr[TU][KP];
+    load_round(t0, bfr);
+    store_full();
+#pragma unroll
+    for (int u = 0; u < TU; ++u) prev[u] = split_combine(tile_dot<E, KP>(afr, bfr[u]), lane);
+    const int c0 = t0 + item * TU;
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv)
+#pragma unroll
+      for (int u = 0; u < TU; ++u)
+        if (dst[vv] && c0 + u < F) dst[vv][t0 + u] = prev[u][vv];
+  } else {
+    store_full();
+  }
+}
+
+// One wave per bucket: its first kBucketSlots members, 8 at a time (a bucket
+// with more than 8 members makes further passes over its span, mostly L2
+// hits); members past kBucketSlots are left to k_leaf_score_overflow.
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
+  constexpr int TU = 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
   float* const junk = a.junk + ((blockIdx.x * nwave + wave) % kJunkSlots) * 16;
   static_assert(TU % 4 == 0 && TU <= 16, "junk slot holds 16 floats");
   // descriptor v of the concatenated sub-lists: lane s holds sub-list s's
@@ -545,125 +591,41 @@ __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
     int cnt = a.bucket_cnt[key];
     cnt = cnt < kBucketSlots ? cnt : kBucketSlots;
     const int2 mem = lane < kBucketSlots ? a.bucket_slot[(int64_t)key * kBucketSlots + lane] : make_int2(-1, 0);
-    for (int g = 0; g * 8 < cnt; ++g) {
-      // A fragment: member g*8 + item, zeros past the members
-      uint4 afr[KP];
-      const int mi = g * 8 + item;
-      const int row = __shfl(mem.x, mi);
-      if (mi < cnt) {
-        int b, n, h;
-        decode_row(a.r, row, b, n, h);
-        const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes + split_off(lane, 0);
-#pragma unroll
-        for (int m = 0; m < KP; ++m) afr[m] = *(const uint4*)(qp + m * 128);
-      } else {
-#pragma unroll
-        for (int m = 0; m < KP; ++m) afr[m] = make_uint4(0, 0, 0, 0);
-      }
-      // owners store members g*8 + 4*quad + vv, keys t0 + item*TU .. + TU-1
-      float* dst[4];
-#pragma unroll
-      for (int vv = 0; vv < 4; ++vv) {
-        const int ms = g * 8 + 4 * (quad & 1) + vv;
-        const int srow = __shfl(mem.x, ms), sbase = __shfl(mem.y, ms);
-        dst[vv] = (owner && ms < cnt) ? a.leaf_scores + (int64_t)srow * a.c2max + sbase + item * TU : nullptr;
-      }
-      // Each round issues its loads, then writes the previous round's scores,
-      // then waits for the loads.  The memory counter completes in issue
-      // order, stores included, so every round issues the same four 16-byte
-      // stores (lanes with nothing to write aim at this wave's junk slot) and
-      // a fixed number of loads (keys past the span re-read its last row):
-      // the wait for a round's loads then never covers the stores after them.
-      float4_t prev[TU];
-#pragma unroll
-      for (int u = 0; u < TU; ++u) prev[u] = float4_t{0.f, 0.f, 0.f, 0.f};
-      int pt0 = -1;                        // round held in prev, -1 none
-      auto load_round = [&](int t0, uint4 (&bfr)[TU][KP]) {
-#pragma unroll
-        for (int u = 0; u < TU; ++u) {
-          const int c = min(t0 + item * TU + u, F - 1);
-          const char* p = kp + (int64_t)c * rsb;
-#pragma unroll
-          for (int m = 0; m < KP; ++m) bfr[u][m] = load_nt(p + m * 128);
-        }
-      };
-      auto store_full = [&]() {            // prev holds a full round (or none)
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv) {
-          float* d = (pt0 >= 0 && dst[vv]) ? dst[vv] + pt0 : junk;
-#pragma unroll
-          for (int u = 0; u < TU; u += 4)
-            store4u(d + u, prev[u][vv], prev[u + 1][vv], prev[u + 2][vv], prev[u + 3][vv]);
-        }
-      };
-      int t0 = 0;
-      for (; t0 + 8 * TU <= F; t0 += 8 * TU) {
-        uint4 bfr[TU][KP];
-        load_round(t0, bfr);
-        store_full();
-#pragma unroll
-        for (int u = 0; u < TU; ++u) prev[u] = split_combine(tile_dot<E, KP>(afr, bfr[u]), lane);
-        pt0 = t0;
-      }
-      if (t0 < F) {  // last, partial round
-        uint4 bfr[TU][KP];
-        load_round(t0, bfr);
-        store_full();
-#pragma unroll
-        for (int u = 0; u < TU; ++u) prev[u] = split_combine(tile_dot<E, KP>(afr, bfr[u]), lane);
-        const int c0 = t0 + item * TU;
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv)
-#pragma unroll
-          for (int u = 0; u < TU; ++u)
-            if (dst[vv] && c0 + u < F) dst[vv][t0 + u] = prev[u][vv];
-      } else {
-        store_full();
-      }
-    }
+    for (int g0 = 0; g0 < cnt; g0 += 8)
+      score_member_group<E, D>(a, kp, rsb, F, mem, g0, min(8, cnt - g0), junk, lane);
     cur = nxt;
     v = vn;
   }
 }
 
 // Members of buckets with more than kBucketSlots rows: one wave per listed
-// bucket walks its overflow list, two rows per pass over the span.
+// bucket walks its overflow list and scores the members 8 at a time with the
+// same group arithmetic as k_leaf_score.
 template <class E, int D>
 __global__ __launch_bounds__(256) void k_leaf_score_overflow(StepArgs a) {
-  constexpr int EPV = E::kEPV, LPK = D / EPV, MB = 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
-  const int j = lane % LPK;
+  float* const junk = a.junk + ((blockIdx.x * nwave + wave) % kJunkSlots) * 16;
   const int nov = a.bucket_count[kDescSub];
   const int K1 = a.K[1];
   const int MI = (int)a.t.count[1];
   const char* kbase = (const char*)a.t.key[2];
+  const int64_t rsb = a.t.rs[2] * E::kBytes;
   for (int v = blockIdx.x * nwave + wave; v < nov; v += gridDim.x * nwave) {
     const int key = a.bucket_ovf[v];
     const int g = key / MI, mid = key % MI;
     const int64_t bix = bucket_index(a, key);
     const int64_t f0 = a.t.off[1][mid];
     const int F = (int)(a.t.off[1][mid + 1] - f0);
-    const char* kb = kbase + ((int64_t)g * a.t.hs[2] + f0 * a.t.rs[2]) * E::kBytes;
+    const char* kp = kbase + ((int64_t)g * a.t.hs[2] + f0 * a.t.rs[2]) * E::kBytes + split_off(lane, 0);
     int e = a.bucket_head[bix];
-    while (e != -1) {  // wave-uniform walk
-      int rows[MB], bases[MB];
-      float qf[MB][EPV];
-      int m = 0;
-#pragma unroll
-      for (int mm = 0; mm < MB; ++mm) {
-        rows[mm] = -1;
-        bases[mm] = 0;
-#pragma unroll
-        for (int t = 0; t < EPV; ++t) qf[mm][t] = 0.f;
-        if (e != -1) {
-          rows[mm] = e / K1;
-          bases[mm] = a.mid_base[e];
-          load_q_chunk<E>(a, rows[mm], j, qf[mm]);
-          e = a.bucket_next[e];
-          ++m;
-        }
+    while (e != -1) {  // wave-uniform walk: lane i takes the group's i-th entry
+      int mine = -1, gcnt = 0;
+      for (; gcnt < 8 && e != -1; ++gcnt) {
+        if (lane == gcnt) mine = e;
+        e = a.bucket_next[e];
       }
-      score_members<E, D, MB>(a, kb, F, m, rows, bases, qf, lane);
+      const int2 gm = (lane < gcnt) ? make_int2(mine / K1, a.mid_base[mine]) : make_int2(-1, 0);
+      score_member_group<E, D>(a, kp, rsb, F, gm, 0, gcnt, junk, lane);
     }
   }
 }

@@ -277,6 +277,46 @@ atlaskv_status atlaskv_shared_check_args(const atlaskv_tensor* q, atlaskv_tree_v
 int32_t atlaskv_shared_phase_count(void);
 const char* atlaskv_shared_phase_name(int32_t phase);
 
+/*
+ * Folded projections: one base-embedding tree for every head.
+ * 背景知识与设计原则 › KBLaM中的矩形注意力 scores a head's query against
+ * projected knowledge keys W_K k and weights projected values W_V v, with
+ * per-layer heads W_K, W_V mapping the encoder width D_E to the head dim d;
+ * 方法细节 › KGKVs的层次化聚类 builds the tree over the base embeddings.
+ * Because <q, W_K k> = <W_K^T q, k> and sum p W_V v = W_V sum p v, the tree
+ * need not be projected per head:
+ *   tree   a view whose root_k / mid_k / leaf_k / leaf_v are the base
+ *          embeddings, ONE head ([1, M_x, D_E]), D_E in {64, 128};
+ *   w_k, w_v  [Hkv, d, D_E]: head g's projected key is w_k[g] k, its
+ *          projected value w_v[g] v; d in {64, 128};
+ *   q, seq_k, seq_v, out as atlaskv_hikvp_attend with the layer's Hkv and d.
+ * Row (b, n, h) with g = h / (Hq/Hkv) folds its KG query into
+ * q' = w_k[g]^T q_kg (exact product sum, rounded once to the tree dtype),
+ * runs the pruned descent over the base tree with q' (logit scale 1/sqrt(d)
+ * unless given), applies w_v[g] to its softmax-weighted base values, and
+ * merges with its causal sequence half.  The result equals
+ * atlaskv_hikvp_attend on the per-head projected trees (w_k[g] k, w_v[g] v)
+ * up to the rounding of q'.  opts->sel_* receive per-row selections of base
+ * nodes.  Workspace size from atlaskv_folded_workspace_size.
+ */
+atlaskv_status atlaskv_folded_workspace_size(atlaskv_tree_view tree, const atlaskv_tensor* q,
+                                             const atlaskv_tensor* w_k, const atlaskv_tensor* seq_k,
+                                             const int32_t K_per_level[3], size_t* bytes);
+atlaskv_status atlaskv_folded_attend_ex(const atlaskv_tensor* q, atlaskv_tree_view tree,
+                                        const atlaskv_tensor* w_k, const atlaskv_tensor* w_v,
+                                        const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                        const int32_t K_per_level[3], atlaskv_tensor* out,
+                                        const atlaskv_attend_opts* opts);
+/* The argument checks of atlaskv_folded_attend_ex alone (pure host code). */
+atlaskv_status atlaskv_folded_check_args(const atlaskv_tensor* q, atlaskv_tree_view tree,
+                                         const atlaskv_tensor* w_k, const atlaskv_tensor* w_v,
+                                         const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                         const int32_t K_per_level[3], const atlaskv_tensor* out,
+                                         const atlaskv_attend_opts* opts);
+/* Kernel phases of one folded call, in launch order. */
+int32_t atlaskv_folded_phase_count(void);
+const char* atlaskv_folded_phase_name(int32_t phase);
+
 /* Message for the calling thread's most recent failed call ("" if none). */
 const char* atlaskv_last_error(void);
 

@@ -342,22 +342,22 @@ def _round_to(x, dt):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
 
 
-def folded_query(q_kg, w_k):
+def folded_query(q_kg, w_k, rows=None):
     """q'[b,n,h] = W_K[g]^T q_kg[b,n,h]: the exact sum of the products (math.fsum
     over the head dim), rounded once to the storage type.  W_K [Hkv, d, D_E]
     maps a base key k (width D_E) to the head's projected key W_K[g] k, so
-    <q_kg, W_K[g] k> = <q', k>."""
+    <q_kg, W_K[g] k> = <q', k>.  rows: only these (b, n, h) are formed (the
+    others stay zero)."""
     q, dt = _as_f64(q_kg)
     w, _ = _as_f64(w_k)
     B, N, Hq, d = q.shape
     Hkv, d2, DE = w.shape
     G = Hq // Hkv
     out = np.zeros((B, N, Hq, DE))
-    for b in range(B):
-        for n in range(N):
-            for h in range(Hq):
-                prod = w[h // G] * q[b, n, h][:, None]          # [d, D_E], exact products
-                out[b, n, h] = [math.fsum(prod[:, j]) for j in range(DE)]
+    todo = all_rows(B, N, Hq) if rows is None else np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+    for b, n, h in todo:
+        prod = w[h // G] * q[b, n, h][:, None]                  # [d, D_E], exact products
+        out[b, n, h] = [math.fsum(prod[:, j]) for j in range(DE)]
     return _round_to(out, dt)
 
 
@@ -374,7 +374,7 @@ def folded_rows(base_tree, q, w_k, w_v, seq_k, seq_v, K, rows, scale=None, q_kg=
     root_k, mid_k, leaf_k, leaf_v, root_off, mid_off = base_tree
     d = q.shape[-1]
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    qf = folded_query(q if q_kg is None else q_kg, w_k)
+    qf = folded_query(q if q_kg is None else q_kg, w_k, rows)
     P = Problem(qf, root_k, mid_k, leaf_k, leaf_v, root_off, mid_off, None, None, K, scale=sc)
     r = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
     ph1 = select_mids_rows(P, r)                 # roots and mids under q'

@@ -250,3 +250,27 @@ def test_shared_phase_names_and_checks(lib):
     b = atlaskv.shared_workspace_size(v, q, sk, (2, 2, 4), atlaskv.SHARE_KV_GROUP)
     assert a <= b
 
+
+def test_folded_phase_names_and_checks(lib):
+    assert atlaskv.folded_phase_names() == [
+        "fold_query", "root_score_topk", "mid_bucket_gemm", "mid_topk", "leaf_bucket_link",
+        "leaf_score_stream", "leaf_score_overflow", "leaf_topk_kg_attention", "unfold_values",
+        "seq_attention", "seq_split_combine"]
+    base = _view(Hkv=1, d=128)                      # one-head base tree, D_E = 128
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)          # layer: Hq 8, d 64
+    wk = torch.zeros(2, 64, 128, dtype=torch.bfloat16)          # Hkv 2
+    sk = torch.zeros(1, 6, 2, 64, dtype=torch.bfloat16)
+    ws = torch.zeros(4096, dtype=torch.uint8)
+    fake = type("W", (), {"data_ptr": lambda self: (ws.data_ptr() + 255) // 256 * 256,
+                          "numel": lambda self: 1 << 30})()
+    call = lambda **kw: atlaskv.folded_check_args(kw.get("q", q), kw.get("tree", base), kw.get("wk", wk),
+                                                  kw.get("wv", wk), kw.get("sk", sk), kw.get("sk", sk),
+                                                  kw.get("K", (2, 2, 4)), kw.get("q", q), workspace=fake)
+    assert call() == atlaskv.OK
+    assert call(tree=_view(Hkv=2, d=128)) == atlaskv.ERR_SHAPE                   # not a base tree
+    assert call(wk=torch.zeros(2, 64, 64, dtype=torch.bfloat16)) == atlaskv.ERR_SHAPE   # D_E mismatch
+    assert call(sk=torch.zeros(1, 6, 1, 64, dtype=torch.bfloat16)) == atlaskv.ERR_SHAPE  # seq heads
+    assert call(q=torch.zeros(1, 4, 7, 64, dtype=torch.bfloat16)) == atlaskv.ERR_SHAPE   # Hq % Hkv
+    assert call(K=(0, 2, 2)) == atlaskv.OK                                        # pure causal
+    assert atlaskv.folded_workspace_size(base, q, wk, sk, (2, 2, 4)) > 0
+

@@ -1,0 +1,157 @@
+"""GPU parity of folded projections (one base-embedding tree for every head;
+W_K^T folded into the query, W_V applied after the softmax-weighted base
+values) against the fp64 oracle, through the C ABI.  Selections of base
+nodes are compared per row as sets (1e-6 boundary-gap exemption); outputs to
+the usual bar on an fp32 output (fp32 max-abs <= 1e-5; bf16 max-abs <= 2e-2 x
+RMS, cosine >= 0.9999), and a bf16 output must be that fp32 output rounded to
+nearest even."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from hierarchical_kv_pruning_amd import atlaskv, synth
+from oracle import oracle
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(f"[gpu-folded] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def bf16_rne(x):
+    u = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).view(torch.int32).to(torch.int64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & ~0xFFFF
+    return u.to(torch.int32).view(torch.float32).numpy().astype(np.float64)
+
+
+class Folded:
+    """A one-head base tree of width DE plus a layer (q, sequence K/V, W_K, W_V)."""
+
+    def __init__(self, seed, dtype="bf16", DE=128, d=128, B=2, N=9, S=13, Hq=8, Hkv=2,
+                 MR=37, MI=411, M=5003, K=(5, 7, 19), ragged=True):
+        base = synth.make_case("base", device=DEV, seed=seed, ragged=ragged, dtype=dtype, B=1, N=1, S_kv=1,
+                               Hq=1, Hkv=1, d=DE, M_R=MR, M_I=MI, M=M, K=K)
+        layer = synth.make_case("layer", device=DEV, seed=seed + 1000, ragged=False, dtype=dtype, B=B, N=N,
+                                S_kv=S, Hq=Hq, Hkv=Hkv, d=d, M_R=1, M_I=1, M=1, K=K)
+        self.tree = (base.root_k, base.mid_k, base.leaf_k, base.leaf_v, base.root_off, base.mid_off)
+        self.q, self.seq_k, self.seq_v = layer.q, layer.seq_k, layer.seq_v
+        g = torch.Generator(device=DEV).manual_seed(seed + 2000)
+        dt = self.q.dtype
+        self.w_k = (torch.randn(Hkv, d, DE, generator=g, device=DEV) / DE ** 0.5).to(dt)
+        self.w_v = (torch.randn(Hkv, d, DE, generator=g, device=DEV) / DE ** 0.5).to(dt)
+        self.K, self.B, self.N, self.Hq, self.Hkv, self.d, self.DE = tuple(K), B, N, Hq, Hkv, d, DE
+        self.dtype, self.R = dtype, B * N * Hq
+        self.name = f"folded(DE={DE}, d={d}, M={M})"
+
+
+def run(f, K=None, out_dtype=None, with_seq=True, q_kg=None):
+    K = f.K if K is None else tuple(K)
+    sk, sv = (f.seq_k, f.seq_v) if with_seq else (None, None)
+    tree = atlaskv.TreeView(*f.tree)
+    ws = atlaskv.alloc_folded_workspace(tree, f.q, f.w_k, sk, K)
+    out = torch.full(f.q.shape, float("nan"), dtype=out_dtype or f.q.dtype, device=DEV)
+    sels = [torch.full((f.R, k), -7, dtype=torch.int32, device=DEV) for k in K]
+    lse = torch.full((f.R,), 7.0, dtype=torch.float32, device=DEV)
+    atlaskv.folded_attend_ex(f.q, tree, f.w_k, f.w_v, sk, sv, K, out, workspace=ws, q_kg=q_kg,
+                             sel_root=sels[0], sel_mid=sels[1], sel_leaf=sels[2], lse_kg=lse)
+    torch.cuda.synchronize()
+    tree.close()
+    return dict(out=out.float().reshape(f.R, -1).cpu().numpy().astype(np.float64),
+                sel=[s.cpu().numpy() for s in sels], lse_kg=lse.cpu().numpy())
+
+
+def check(f, rows=None, K=None, with_seq=True, q_kg=None):
+    K = f.K if K is None else tuple(K)
+    rows = oracle.all_rows(f.B, f.N, f.Hq) if rows is None else rows
+    say(f"{f.name}: B={f.B} N={f.N} Hq={f.Hq} Hkv={f.Hkv} K={K} dtype={f.dtype} rows={len(rows)}")
+    gpu = run(f, K=K, out_dtype=torch.float32, with_seq=with_seq, q_kg=q_kg)
+    if f.dtype == "bf16":
+        b16 = run(f, K=K, with_seq=with_seq, q_kg=q_kg)
+        np.testing.assert_array_equal(b16["out"], bf16_rne(gpu["out"]))
+    h = lambda t: None if t is None else t.detach().cpu()
+    ora = oracle.folded_rows(tuple(h(t) for t in f.tree), h(f.q), h(f.w_k), h(f.w_v),
+                             h(f.seq_k) if with_seq else None, h(f.seq_v) if with_seq else None, K, rows,
+                             q_kg=h(q_kg))
+    ridx = (rows[:, 0] * f.N + rows[:, 1]) * f.Hq + rows[:, 2]
+    exempt = 0
+    for i, r in enumerate(ridx):
+        for lev, key in enumerate(("sel_R", "sel_I", "sel_L")):
+            g_set = sorted(int(x) for x in gpu["sel"][lev][r] if x >= 0)
+            o_set = sorted(int(x) for x in ora[key][i] if x >= 0)
+            if g_set != o_set:
+                assert ora["gap"][i][lev] < parity.GAP_EXEMPT, (tuple(rows[i]), lev, g_set, o_set)
+                exempt += 1
+                break
+    assert exempt == 0 or exempt < len(rows) // 50, exempt
+    g, o = gpu["out"][ridx], ora["out"]
+    keep = np.ones(len(ridx), bool)
+    if exempt:  # a near-tie changed the selection: those rows are left to the selection check
+        for i, r in enumerate(ridx):
+            keep[i] = all(sorted(x for x in gpu["sel"][lev][r] if x >= 0) ==
+                          sorted(x for x in ora[k][i] if x >= 0) for lev, k in enumerate(("sel_R", "sel_I", "sel_L")))
+    err = float(np.abs(g[keep] - o[keep]).max(initial=0.0))
+    rep = dict(rows=len(rows), exempt=exempt, max_abs=err)
+    if f.dtype == "f32":
+        assert err <= 1e-5, rep
+    else:
+        rms = float(np.sqrt(np.mean(o[keep] ** 2)))
+        cos = float(np.sum(g[keep] * o[keep]) / (np.linalg.norm(g[keep]) * np.linalg.norm(o[keep])))
+        rep.update(rms=rms, cos=cos)
+        assert err <= 2e-2 * rms, rep
+        assert cos >= 0.9999, rep
+    fin = np.isfinite(ora["lse_kg"])
+    assert np.array_equal(np.isfinite(gpu["lse_kg"][ridx]), fin)
+    if fin.any():
+        assert np.max(np.abs(gpu["lse_kg"][ridx][fin] - ora["lse_kg"][fin])) <= 1e-3
+    say(f"{f.name}: {rep}")
+    return gpu, ora
+
+
+@pytest.mark.parametrize("dtype,DE,d", [("bf16", 128, 128), ("bf16", 64, 128), ("bf16", 128, 64),
+                                        ("f32", 128, 128), ("f32", 64, 64)])
+def test_folded_widths_and_dtypes(dtype, DE, d):
+    check(Folded(1, dtype=dtype, DE=DE, d=d))
+
+
+def test_folded_k_edges_and_no_sequence():
+    f = Folded(2, M=3001)
+    check(f, K=(1, 1, 1))
+    check(f, K=(0, 4, 4))          # empty KG half: plain causal attention
+    check(f, K=(37, 256, 256))
+    check(f, with_seq=False)
+
+
+def test_folded_separate_kg_query_and_gqa():
+    f = Folded(3, Hq=12, Hkv=3)
+    q_kg = torch.randn(f.q.shape, generator=torch.Generator(device=DEV).manual_seed(4), device=DEV).to(f.q.dtype)
+    check(f, q_kg=q_kg)
+
+
+def test_folded_identity_projections_match_the_per_row_path():
+    """One KV head, W_K = W_V = I: the folded call selects exactly what the
+    per-row path selects on the base tree itself."""
+    f = Folded(5, Hq=4, Hkv=1, DE=128, d=128)
+    f.w_k = torch.eye(128, dtype=f.q.dtype, device=DEV)[None].contiguous()
+    f.w_v = f.w_k.clone()
+    gpu, _ = check(f)
+    case = type("C", (), {})()
+    case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off = f.tree
+    case.q, case.seq_k, case.seq_v, case.K = f.q, f.seq_k, f.seq_v, f.K
+    per_row = parity.gpu_run(case)
+    for lev in range(3):
+        a = [sorted(x for x in r if x >= 0) for r in gpu["sel"][lev]]
+        b = [sorted(x for x in r if x >= 0) for r in per_row["sel"][lev]]
+        assert a == b, lev
+
+
+def test_folded_one_million_base_leaves_sampled_rows():
+    """The m1e6 layer (32/8 heads, 512 tokens, K 8/8/32) over a one-head base
+    tree of 1e6 leaves at D_E = 128."""
+    f = Folded(6, B=1, N=512, S=512, Hq=32, Hkv=8, MR=100, MI=10000, M=1000000, K=(8, 8, 32), ragged=False)
+    check(f, rows=parity.sample_rows(type("C", (), dict(B=1, N=512, Hq=32))(), 256, seed=9))
