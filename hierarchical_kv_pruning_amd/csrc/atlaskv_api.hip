@@ -243,6 +243,8 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
     S = seq_k->shape[1];
     if (S < N) return fail(ATLASKV_ERR_SHAPE, "S_kv=%lld < N=%lld", (long long)S, (long long)N);
     if (S >= kIndexLimit) return fail(ATLASKV_ERR_UNSUPPORTED, "S_kv must be below 2^31");
+    if ((seq_k->stride[1] | seq_v->stride[1]) * esize(seq_k->dtype) >= ((int64_t)1 << 25))
+      return fail(ATLASKV_ERR_UNSUPPORTED, "sequence position strides must be below 32 MB");
   }
   if (need_out) {
     if ((st = check_tensor(out, "out", 4, false))) return st;
@@ -282,7 +284,7 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
     p.off_okg = o;   o = align256(o + R * (size_t)t.d * 4);
     p.off_lse = o;   o = align256(o + R * 4);
     p.off_fpart = o; o = align256(o + R * (size_t)p.flat_nsplit * (t.d + 4) * 4);
-    p.nsplit = seq_splits(p.B, p.N, t.Hkv, p.S);
+    p.nsplit = seq_splits(p.B, p.N, t.Hkv, p.G, p.S, t.dtype);
     p.off_part = o;  o = align256(o + (p.nsplit > 1 ? R * (size_t)p.nsplit * (t.d + 2) * 4 : 0));
     p.total = o;
     return ATLASKV_OK;
@@ -303,7 +305,7 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
     p.off_gpart = o; o = align256(o + (size_t)p.group_rows * chunks * t.d * 8);
     p.off_okg = o;   o = align256(o + R * (size_t)t.d * 4);
     p.off_lse = o;   o = align256(o + R * 4);
-    p.nsplit = seq_splits(p.B, p.N, t.Hkv, p.S);
+    p.nsplit = seq_splits(p.B, p.N, t.Hkv, p.G, p.S, t.dtype);
     p.off_part = o;  o = align256(o + (p.nsplit > 1 ? R * (size_t)p.nsplit * (t.d + 2) * 4 : 0));
     p.total = o;
     return ATLASKV_OK;
@@ -347,7 +349,7 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   p.off_junk = o;      o = align256(o + (size_t)kJunkSlots * 64);
   p.off_okg = o;       o = align256(o + R * (size_t)t.d * 4);
   p.off_lse = o;       o = align256(o + R * 4);
-  p.nsplit = seq_splits(p.B, p.N, t.Hkv, p.S);
+  p.nsplit = seq_splits(p.B, p.N, t.Hkv, p.G, p.S, t.dtype);
   p.off_part = o;      o = align256(o + (p.nsplit > 1 ? R * (size_t)p.nsplit * (t.d + 2) * 4 : 0));
   p.total = o;
   return ATLASKV_OK;
@@ -416,6 +418,8 @@ atlaskv_status plan_folded(const atlaskv_tensor* q, const atlaskv_tree_view_s* v
     S = seq_k->shape[1];
     if (S < N) return fail(ATLASKV_ERR_SHAPE, "S_kv=%lld < N=%lld", (long long)S, (long long)N);
     if (S >= kIndexLimit) return fail(ATLASKV_ERR_UNSUPPORTED, "S_kv must be below 2^31");
+    if ((seq_k->stride[1] | seq_v->stride[1]) * esize(seq_k->dtype) >= ((int64_t)1 << 25))
+      return fail(ATLASKV_ERR_UNSUPPORTED, "sequence position strides must be below 32 MB");
   }
   if (need_out) {
     if ((st = check_tensor(out, "out", 4, false))) return st;
@@ -454,7 +458,7 @@ atlaskv_status plan_folded(const atlaskv_tensor* q, const atlaskv_tree_view_s* v
   p.off_qf = o;   o = align256(o + R * (size_t)t.d * esize(t.dtype));
   p.off_okg = o;  o = align256(o + R * (size_t)d * 4);
   p.off_lse = o;  o = align256(o + R * 4);
-  p.nsplit = seq_splits(p.B, p.N, (int)Hkv, p.S);
+  p.nsplit = seq_splits(p.B, p.N, (int)Hkv, p.G, p.S, t.dtype);
   p.off_part = o; o = align256(o + (p.nsplit > 1 ? R * (size_t)p.nsplit * (d + 2) * 4 : 0));
   p.total = o;
   return ATLASKV_OK;

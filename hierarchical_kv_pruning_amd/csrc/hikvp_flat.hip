@@ -9,110 +9,15 @@
 // writes a partial (o relative to its running max, max, sum) that
 // k_flat_combine merges into o_kg / lse_kg.  The sequence half and the λ merge
 // then run exactly as for the pruned path.
-#include "hikvp_device.h"
+#include "hikvp_flash.h"
 
 namespace hikvp {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+using namespace flash;
 
 constexpr int kFlatRows = 128;  // query rows per workgroup, 32 per wave
-constexpr int kFlatKeys = 64;   // keys per LDS block
-// true: softmax weights enter the value product as bf16 hi + lo (two products
-// with the same value operand), weight error ~2^-17 instead of bf16's 2^-9.
-// Measured 25% slower at 1e6 leaves; the single bf16 weight already keeps the
-// output well inside 2e-2 of its RMS (rounding errors of 1e6 weights average
-// out), so it is off.
-constexpr bool kPSplit = false;
-constexpr float kLog2e = 1.4426950408889634f;
-// partial record of one (row, key range): o[D], m, sum, 2 pad floats (16-byte rows)
-
-// LDS geometry of one block (dwords).  Keys: [64 key rows][D/2 + 4]; the
-// 4-dword pad puts the 16-byte operand reads of 8 consecutive key rows on
-// distinct bank groups.  Values, transposed: [D rows][32 + 4] with two keys'
-// bf16 values packed per dword, so a lane reads 4 consecutive keys of one
-// value column as 8 bytes.
-template <int D> struct FlatLds {
-  static constexpr int kKS = D / 2 + 4;
-  static constexpr int kVS = kFlatKeys / 2 + 4;
-  static constexpr int kKDw = kFlatKeys * kKS;
-  static constexpr int kVDw = D * kVS;
-  static constexpr int kBufDw = kKDw + kVDw;
-};
-
-__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Eight fp32 values as bf16 operand elements, rounded to nearest even by the
-// hardware conversion (v_cvt_pk_bf16_f32): element 2j in the low half of dword j.
-__device__ inline u32x4 pack_bf16x8(const float* p) {
-  u32x4 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    r[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p[2 * j], p[2 * j + 1]}, bf16x2));
-  return r;
-}
-
-// One wave's staging share of a key block: 4 x 16 bytes of keys, and 2 key
-// pairs x 16 bytes of values (one d-chunk of two consecutive keys each).
-template <int D> struct Stage {
-  static constexpr int kKChunks = kFlatKeys * D / 8 / 256;    // 16-byte key chunks per thread
-  static constexpr int kVItems = (kFlatKeys / 2) * (D / 8) / 256;  // (key pair, d chunk) per thread
-  u32x4 k[kKChunks];
-  u32x4 va[kVItems], vb[kVItems];
-};
-
-// kblk / vblk: the block's first key / value row (uniform); nkeys >= 1 valid
-// rows, the ragged tail clamped to the last one.  Offsets inside a block fit
-// 32 bits (row strides below 32 MB are checked on the host).
-template <int D>
-__device__ inline void stage_load(Stage<D>& st, const char* kblk, uint32_t krs, const char* vblk,
-                                  uint32_t vrs, int nkeys, int tid) {
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
-#pragma unroll
-  for (int i = 0; i < Stage<D>::kKChunks; ++i) {
-    const int c = tid + 256 * i;
-    const uint32_t key = (uint32_t)min(c / CPR, nkeys - 1);
-    st.k[i] = *(const u32x4*)(kblk + (key * krs + (uint32_t)(c % CPR) * 16u));
-  }
-#pragma unroll
-  for (int i = 0; i < Stage<D>::kVItems; ++i) {
-    const int it = tid + 256 * i;
-    const int pr = it % (kFlatKeys / 2), ch = it / (kFlatKeys / 2);
-    const uint32_t ka = (uint32_t)min(2 * pr, nkeys - 1), kb = (uint32_t)min(2 * pr + 1, nkeys - 1);
-    st.va[i] = *(const u32x4*)(vblk + (ka * vrs + (uint32_t)ch * 16u));
-    st.vb[i] = *(const u32x4*)(vblk + (kb * vrs + (uint32_t)ch * 16u));
-  }
-}
-
-template <int D>
-__device__ inline void stage_store(const Stage<D>& st, uint32_t* buf, int tid) {
-  using L = FlatLds<D>;
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int i = 0; i < Stage<D>::kKChunks; ++i) {
-    const int c = tid + 256 * i;
-    *(u32x4*)(buf + (c / CPR) * L::kKS + (c % CPR) * 4) = st.k[i];
-  }
-  uint32_t* vt = buf + L::kKDw;
-#pragma unroll
-  for (int i = 0; i < Stage<D>::kVItems; ++i) {
-    const int it = tid + 256 * i;
-    const int pr = it % (kFlatKeys / 2), ch = it / (kFlatKeys / 2);
-    uint32_t* col = vt + (ch * 8) * L::kVS + pr;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // value columns 8ch + 2w (low halves) and 8ch + 2w + 1 (high halves)
-      col[(2 * w) * L::kVS] = __builtin_amdgcn_perm(st.vb[i][w], st.va[i][w], 0x05040100u);
-      col[(2 * w + 1) * L::kVS] = __builtin_amdgcn_perm(st.vb[i][w], st.va[i][w], 0x07060302u);
-    }
-  }
-}
+constexpr int kFlatKeys = kKeys;
 
 // Work item of a workgroup: (KV head, key split) pairs are spread over the 8
 // XCDs (workgroup i runs on XCD i mod 8); the row tiles of one pair are
@@ -131,8 +36,7 @@ __device__ inline bool flat_item(const FlatArgs& a, int& g, int& split, int& til
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void k_flat_mfma(FlatArgs a) {
-  using L = FlatLds<D>;
-  __shared__ __attribute__((aligned(16))) uint32_t lds[2 * L::kBufDw];
+  __shared__ __attribute__((aligned(16))) uint32_t lds[2 * Lds<D>::kBufDw];
   int g, split, tile;
   if (!flat_item(a, g, split, tile)) return;  // uniform per workgroup, before any barrier
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -140,8 +44,7 @@ void k_flat_mfma(FlatArgs a) {
   const int G = a.r.G, TG = a.r.B * a.r.N * G;
   const int64_t M = a.t.count[2];
   const int64_t key_lo = (int64_t)split * a.split_len;
-  const int64_t key_hi = min(M, key_lo + a.split_len);
-  const int nblk = key_lo < key_hi ? (int)((key_hi - key_lo + kFlatKeys - 1) / kFlatKeys) : 0;
+  const int nkeys = (int)max<int64_t>(0, min(M, key_lo + a.split_len) - key_lo);
 
   // this lane's query row (column of the transposed score tile)
   const int u = tile * kFlatRows + wave * 32 + col;
@@ -149,136 +52,27 @@ void k_flat_mfma(FlatArgs a) {
   const int tok = valid ? u / G : 0, j = valid ? u % G : 0;
   const int b = tok / a.r.N, n = tok % a.r.N, hq = g * G + j;
   const int64_t row = (int64_t)tok * a.r.Hq + hq;
-
-  // Q^T operands: lane (query col, half h) holds d = 16*ds + 8h .. +7
-  constexpr int DS = D / 16;
-  u32x4 qop[DS];
-  {
-    const uint16_t* qp = (const uint16_t*)a.r.q_kg + b * a.r.qks[0] + n * a.r.qks[1] + hq * a.r.qks[2];
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds)
-      qop[ds] = valid ? *(const u32x4*)(qp + 16 * ds + 8 * half) : u32x4{0u, 0u, 0u, 0u};
-  }
-  const char* kbase = (const char*)a.t.key[2] + (int64_t)g * a.t.hs[2] * 2;
-  const char* vbase = (const char*)a.t.leaf_v + (int64_t)g * a.t.hs[3] * 2;
+  u32x4 qop[D / 16];
+  load_query<D>(valid ? (const uint16_t*)a.r.q_kg + b * a.r.qks[0] + n * a.r.qks[1] + hq * a.r.qks[2] : nullptr,
+                half, qop);
   const uint32_t krs = (uint32_t)(a.t.rs[2] * 2), vrs = (uint32_t)(a.t.rs[3] * 2);
-  const float sl2 = (float)a.r.scale * kLog2e;
-
-  constexpr int DT = D / 32;
-  f32x16 acc_o[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc_o[dt] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  Stage<D> st;
-  if (nblk > 0) {
-    stage_load<D>(st, kbase + key_lo * krs, krs, vbase + key_lo * vrs, vrs,
-                  (int)min<int64_t>(kFlatKeys, key_hi - key_lo), tid);
-    stage_store<D>(st, lds, tid);
-  }
-  __syncthreads();
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int64_t k0 = key_lo + (int64_t)blk * kFlatKeys;
-    const int nk = (int)min<int64_t>(kFlatKeys, key_hi - k0);
-    if (blk + 1 < nblk)
-      stage_load<D>(st, kbase + (k0 + kFlatKeys) * krs, krs, vbase + (k0 + kFlatKeys) * vrs, vrs,
-                    (int)min<int64_t>(kFlatKeys, key_hi - k0 - kFlatKeys), tid);
-    const uint32_t* kb = lds + (blk & 1) * L::kBufDw;
-    const uint32_t* vt = kb + L::kKDw;
-
-    // S^T = K Q^T: two 32-key tiles; element i of tile kt is key kt*32 + 8(i/4) + 4h + i%4
-    f32x16 s[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = f32x16{};
-      const uint32_t* kr = kb + (kt * 32 + col) * L::kKS + 4 * half;
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*(const u32x4*)(kr + 8 * ds)),
-                                                        as_bf16x8(qop[ds]), s[kt], 0, 0, 0);
-    }
-    // online softmax in log2 units; the lane's query column is its own
-    if (nk < kFlatKeys) {  // ragged last block (uniform)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kt * 32 + 8 * (i >> 2) + 4 * half + (i & 3) >= nk) s[kt][i] = -INFINITY;
-    }
-    float mb = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mb = fmaxf(mb, s[kt][i]);
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const float m_new = fmaxf(m_run, mb * sl2);  // finite: every block holds a valid key
-    // rescale only when some row's running maximum grew (rare after the first blocks)
-    const bool grow = m_new > m_run;
-    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
-    }
-    m_run = m_new;
-    float ps = 0.f;
-    u32x4 pop[2][2], pol[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][8 * h2 + e], sl2, -m_new));
-          ps += p[e];
-        }
-        pop[kt][h2] = pack_bf16x8(p);
-        if constexpr (kPSplit) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t w = pop[kt][h2][e >> 1];
-            p[e] -= __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
-          }
-          pol[kt][h2] = pack_bf16x8(p);
-        }
-      }
-    l_run = l_run * alpha + ps;
-    // O^T += V^T P^T: k-step (kt, h2) covers keys kt*32 + 16*h2 .. +15; slot e of
-    // half h is key kt*32 + 16*h2 + 8(e/4) + 4h + e%4, the same key as P's slot
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint32_t* vr = vt + (dt * 32 + col) * L::kVS + 2 * half;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const u32x2 lo = *(const u32x2*)(vr + 16 * kt + 8 * h2);
-          const u32x2 hi = *(const u32x2*)(vr + 16 * kt + 8 * h2 + 4);
-          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(pop[kt][h2]),
-                                                              acc_o[dt], 0, 0, 0);
-          if constexpr (kPSplit)
-            acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(pol[kt][h2]),
-                                                                acc_o[dt], 0, 0, 0);
-        }
-    }
-    if (blk + 1 < nblk) stage_store<D>(st, lds + ((blk + 1) & 1) * L::kBufDw, tid);
-    __syncthreads();
-  }
-  l_run += __shfl_xor(l_run, 32);
+  const char* kbase = (const char*)a.t.key[2] + (int64_t)g * a.t.hs[2] * 2 + key_lo * krs;
+  const char* vbase = (const char*)a.t.leaf_v + (int64_t)g * a.t.hs[3] * 2 + key_lo * vrs;
+  State<D> S;
+  run<D, 256, false>(S, qop, kbase, krs, vbase, vrs, nkeys, nkeys, nkeys, (float)a.r.scale * kLog2e, lds);
   if (!valid) return;
   float* pp = a.part + ((size_t)row * a.nsplit + split) * (D + 4);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int d0 = dt * 32 + 8 * q4 + 4 * half;
-      *(float4*)(pp + d0) = make_float4(acc_o[dt][4 * q4], acc_o[dt][4 * q4 + 1], acc_o[dt][4 * q4 + 2],
-                                        acc_o[dt][4 * q4 + 3]);
+      *(float4*)(pp + d0) = make_float4(S.acc[dt][4 * q4], S.acc[dt][4 * q4 + 1], S.acc[dt][4 * q4 + 2],
+                                        S.acc[dt][4 * q4 + 3]);
     }
   if (half == 0) {
-    pp[D] = nblk > 0 ? m_run : -INFINITY;
-    pp[D + 1] = l_run;
+    pp[D] = S.m;
+    pp[D + 1] = S.l;
   }
 }
 

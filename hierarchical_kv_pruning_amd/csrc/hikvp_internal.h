@@ -173,7 +173,7 @@ hipError_t launch_unfold_values(const FoldArgs& a, bool kg_empty, hipStream_t s)
 int flat_row_tiles(int B, int N, int G);
 int flat_splits(int B, int N, int Hq, int Hkv, int64_t M, int dtype);
 int flat_split_len(int64_t M, int nsplit);
-int seq_splits(int B, int N, int Hkv, int S);   // key splits of the sequence attention
+int seq_splits(int B, int N, int Hkv, int G, int S, int dtype);  // key splits of the sequence attention
 int seq_split_len(int S, int nsplit);
 
 }  // namespace hikvp

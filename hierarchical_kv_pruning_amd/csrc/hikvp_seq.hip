@@ -13,6 +13,7 @@
 #include <type_traits>
 
 #include "hikvp_device.h"
+#include "hikvp_flash.h"
 
 namespace hikvp {
 namespace {
@@ -464,6 +465,94 @@ __global__ __launch_bounds__(256) void k_seq_combine(SeqArgs a, int nsplit) {
   merge_store<E, D>(a, row, b, n, h, has ? M + logf(l) : -INFINITY, has, oseq, lane);
 }
 
+// Prefill, bf16: the matrix-core flash core with a causal mask.  A workgroup
+// of two waves takes 64 rows of one (b, KV head) -- row u is token u / G,
+// query head g*G + u % G -- and one key range of its causal span.  Token n
+// sees positions 0 .. S - N + n.  With one key range the epilogue merges with
+// the KG half and stores the output; otherwise it writes the (o, m, l)
+// partial that k_seq_combine merges.
+constexpr int kSeqRows = 64;
+constexpr int64_t kSeqMfmaTarget = 512;  // workgroups to aim for before splitting keys
+
+template <int D>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2)))
+void k_seq_mfma(SeqArgs a, int tiles) {
+  using namespace flash;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[2 * Lds<D>::kBufDw];
+  const int nsplit = a.part ? a.nsplit : 1;
+  int bid = blockIdx.x;
+  const int split = bid % nsplit;
+  bid /= nsplit;
+  const int tile = bid % tiles;
+  bid /= tiles;
+  const int g = bid % a.Hkv, b = bid / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int G = a.r.G, NG = a.r.N * G;
+  const int u = tile * kSeqRows + wave * 32 + col;
+  const bool valid = u < NG;
+  const int n = valid ? u / G : 0, h = g * G + (valid ? u % G : 0);
+  const int off = a.S - a.r.N;                       // token n sees positions 0 .. off + n
+  const int n_first = (tile * kSeqRows) / G;
+  const int n_last = min(a.r.N - 1, (tile * kSeqRows + kSeqRows - 1) / G);
+  const int64_t key_lo = (int64_t)split * a.split_len;
+  const int span = off + n_last + 1;                 // keys any row of the tile sees
+  const int nkeys = (int)max<int64_t>(0, min<int64_t>(span, key_lo + a.split_len) - key_lo);
+  const int lim = valid ? (int)max<int64_t>(0, min<int64_t>(nkeys, off + n + 1 - key_lo)) : nkeys;
+  const int lim_min = (int)max<int64_t>(0, min<int64_t>(nkeys, off + n_first + 1 - key_lo));
+  u32x4 qop[D / 16];
+  load_query<D>(valid ? (const uint16_t*)a.r.q + q_off(a.r.qs, b, n, h) : nullptr, half, qop);
+  const uint32_t krs = (uint32_t)(a.ks[1] * 2), vrs = (uint32_t)(a.vs[1] * 2);
+  const char* kbase = (const char*)a.k + ((int64_t)b * a.ks[0] + (int64_t)g * a.ks[2]) * 2 + key_lo * krs;
+  const char* vbase = (const char*)a.v + ((int64_t)b * a.vs[0] + (int64_t)g * a.vs[2]) * 2 + key_lo * vrs;
+  State<D> S;
+  run<D, 128, true>(S, qop, kbase, krs, vbase, vrs, nkeys, lim, lim_min, (float)a.r.scale * kLog2e, lds);
+  if (!valid) return;
+  const int64_t row = ((int64_t)b * a.r.N + n) * a.r.Hq + h;
+  constexpr float kLn2 = 0.6931471805599453f;
+  const bool has = S.l > 0.f;
+  if (nsplit > 1) {  // partial (o, m, l) for k_seq_combine, m in natural-log units
+    float* part = a.part + (row * nsplit + split) * (D + 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        store4u(part + dt * 32 + 8 * q4 + 4 * half, S.acc[dt][4 * q4], S.acc[dt][4 * q4 + 1],
+                S.acc[dt][4 * q4 + 2], S.acc[dt][4 * q4 + 3]);
+    if (half == 0) {
+      part[D] = has ? S.m * kLn2 : -INFINITY;
+      part[D + 1] = S.l;
+    }
+    return;
+  }
+  const float lse_seq = has ? (S.m + log2f(S.l)) * kLn2 : -INFINITY;
+  const float lkg = a.lse_kg[row];
+  float lam;
+  if (lkg == -INFINITY) lam = 0.f;
+  else if (!has) lam = 1.f;
+  else lam = 1.f / (1.f + __expf(lse_seq - lkg));
+  const float inv = has ? 1.f / S.l : 0.f;
+  const float* okg = a.o_kg + row * D;
+  const int64_t ob = q_off(a.os, b, n, h);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = dt * 32 + 8 * q4 + 4 * half;
+      const float4 kg = *(const float4*)(okg + d0);
+      const float o[4] = {lam * kg.x + (1.f - lam) * (S.acc[dt][4 * q4] * inv),
+                          lam * kg.y + (1.f - lam) * (S.acc[dt][4 * q4 + 1] * inv),
+                          lam * kg.z + (1.f - lam) * (S.acc[dt][4 * q4 + 2] * inv),
+                          lam * kg.w + (1.f - lam) * (S.acc[dt][4 * q4 + 3] * inv)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (a.out_dtype == kDtypeBF16) ((uint16_t*)a.out)[ob + d0 + e] = f32_to_bf16_rne(o[e]);
+        else ((float*)a.out)[ob + d0 + e] = o[e];
+      }
+    }
+  if (a.lse_seq_out && half == 0) a.lse_seq_out[row] = lse_seq;
+}
+
 }  // namespace
 
 #define HIKVP_DISPATCH(dtype, d, KERNEL, ...)                                                        \
@@ -475,7 +564,21 @@ __global__ __launch_bounds__(256) void k_seq_combine(SeqArgs a, int nsplit) {
     else return hipErrorInvalidValue;                                                                \
   } while (0)
 
-int seq_splits(int B, int N, int Hkv, int S) {
+static bool seq_uses_mfma(int N, int dtype) { return N >= 16 && dtype == kDtypeBF16; }
+
+static int seq_mfma_tiles(int N, int G) { return (N * G + kSeqRows - 1) / kSeqRows; }
+
+int seq_splits(int B, int N, int Hkv, int G, int S, int dtype) {
+  if (seq_uses_mfma(N, dtype)) {
+    // 64-row tiles of one (b, KV head); split the keys only while there are
+    // fewer tiles than a round of the chip, at least 4 blocks a range
+    const int64_t items = (int64_t)B * Hkv * seq_mfma_tiles(N, G);
+    if (items <= 0 || S <= 0) return 1;
+    int64_t want = (kSeqMfmaTarget + items - 1) / items;
+    const int64_t maxs = (S + 255) / 256;
+    if (want > maxs) want = maxs;
+    return want < 1 ? 1 : (int)want;
+  }
   const int64_t flash = N >= 16;
   // workgroups before splitting: one per (b, n, KV head) for decode, one per
   // (b, 16-token tile, KV head) for the flash prefill
@@ -499,6 +602,13 @@ int seq_split_len(int S, int nsplit) {
 hipError_t launch_seq_attend(const SeqArgs& a, hipStream_t s) {
   if (a.r.R <= 0) return hipSuccess;
   const int nsplit = a.part ? a.nsplit : 1;
+  if (a.k && seq_uses_mfma(a.r.N, a.dtype)) {
+    const int tiles = seq_mfma_tiles(a.r.N, a.r.G);
+    const unsigned blocks = (unsigned)(a.r.B * a.Hkv * tiles * nsplit);
+    if (a.d == 128) hipLaunchKernelGGL(k_seq_mfma<128>, dim3(blocks), dim3(128), 0, s, a, tiles);
+    else hipLaunchKernelGGL(k_seq_mfma<64>, dim3(blocks), dim3(128), 0, s, a, tiles);
+    return hipGetLastError();
+  }
   if (a.k && a.r.N >= 16) {
     // prefill: MFMA flash attention per (b, KV head, 16-token tile [, key split])
     const unsigned blocks = (unsigned)(a.r.B * ((a.r.N + 15) / 16) * a.Hkv);
