@@ -13,6 +13,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+#include <new>
 #include <string>
 
 #include "atlaskv.h"
@@ -29,11 +31,24 @@ struct atlaskv_tree_view_s {
   size_t workspace_bytes;
   int described_only;
   int host_mask;               // bit i: tree tensor i (root_k, mid_k, leaf_k, leaf_v) in pinned host memory
+  // the sequence half runs on aux, forked from and joined back to the call's
+  // stream with two events; mu keeps one call's fork sequence whole
+  hipStream_t aux;
+  hipEvent_t fork, join;
+  std::mutex mu;
 };
 
 namespace {
 
 thread_local std::string g_err;
+
+// Frees a view and whatever of its HIP objects exist (not its tree stats).
+void release_view(atlaskv_tree_view_s* v) {
+  if (v->join) (void)hipEventDestroy(v->join);
+  if (v->fork) (void)hipEventDestroy(v->fork);
+  if (v->aux) (void)hipStreamDestroy(v->aux);
+  delete v;
+}
 
 atlaskv_status fail(atlaskv_status st, const char* fmt, ...) {
   char buf[512];
@@ -285,7 +300,7 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
     p.off_lse = o;   o = align256(o + R * 4);
     p.off_fpart = o; o = align256(o + R * (size_t)p.flat_nsplit * (t.d + 4) * 4);
     p.nsplit = seq_splits(p.B, p.N, t.Hkv, p.G, p.S, t.dtype);
-    p.off_part = o;  o = align256(o + (p.nsplit > 1 ? R * (size_t)p.nsplit * (t.d + 2) * 4 : 0));
+    p.off_part = o;  o = align256(o + R * (size_t)p.nsplit * (t.d + 2) * 4);
     p.total = o;
     return ATLASKV_OK;
   }
@@ -306,7 +321,7 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
     p.off_okg = o;   o = align256(o + R * (size_t)t.d * 4);
     p.off_lse = o;   o = align256(o + R * 4);
     p.nsplit = seq_splits(p.B, p.N, t.Hkv, p.G, p.S, t.dtype);
-    p.off_part = o;  o = align256(o + (p.nsplit > 1 ? R * (size_t)p.nsplit * (t.d + 2) * 4 : 0));
+    p.off_part = o;  o = align256(o + R * (size_t)p.nsplit * (t.d + 2) * 4);
     p.total = o;
     return ATLASKV_OK;
   }
@@ -350,7 +365,7 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   p.off_okg = o;       o = align256(o + R * (size_t)t.d * 4);
   p.off_lse = o;       o = align256(o + R * 4);
   p.nsplit = seq_splits(p.B, p.N, t.Hkv, p.G, p.S, t.dtype);
-  p.off_part = o;      o = align256(o + (p.nsplit > 1 ? R * (size_t)p.nsplit * (t.d + 2) * 4 : 0));
+  p.off_part = o;      o = align256(o + R * (size_t)p.nsplit * (t.d + 2) * 4);
   p.total = o;
   return ATLASKV_OK;
 }
@@ -459,7 +474,7 @@ atlaskv_status plan_folded(const atlaskv_tensor* q, const atlaskv_tree_view_s* v
   p.off_okg = o;  o = align256(o + R * (size_t)d * 4);
   p.off_lse = o;  o = align256(o + R * 4);
   p.nsplit = seq_splits(p.B, p.N, (int)Hkv, p.G, p.S, t.dtype);
-  p.off_part = o; o = align256(o + (p.nsplit > 1 ? R * (size_t)p.nsplit * (d + 2) * 4 : 0));
+  p.off_part = o; o = align256(o + R * (size_t)p.nsplit * (d + 2) * 4);
   p.total = o;
   return ATLASKV_OK;
 }
@@ -482,12 +497,23 @@ struct PhaseMarks {
 };
 
 // Sequence half (背景知识与设计原则 › 自注意力层机制) and the λ merge with the
-// KG half held in o_kg / lse_kg: two phases (attention, split combine).
-hipError_t launch_seq_half(const Plan& p, const RowsDev& rows, int Hkv, int d, int dtype,
-                           const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
-                           const atlaskv_tensor* out, const atlaskv_attend_opts* opts, float* o_kg,
-                           float* lse_kg, char* ws, hipStream_t s, PhaseMarks& pm) {
+// KG half held in o_kg / lse_kg.  The causal attention does not depend on the
+// KG half, so unless phase timing is requested it runs concurrently: it is
+// enqueued on the view's aux stream, forked from the call's stream before the
+// KG kernels, writes (o, m, l) partials, and the call's stream waits for it
+// before k_seq_combine merges both halves.  Serially, two phases (attention,
+// split combine) run after the KG half, through the same partials and merge.
+struct SeqHalf {
   SeqArgs sa;
+  bool overlap;
+};
+
+SeqHalf seq_prepare(const Plan& p, const RowsDev& rows, int Hkv, int d, int dtype,
+                    const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v, const atlaskv_tensor* out,
+                    const atlaskv_attend_opts* opts, float* o_kg, float* lse_kg, char* ws,
+                    const atlaskv_tree_view_s* v) {
+  SeqHalf h;
+  SeqArgs& sa = h.sa;
   memset(&sa, 0, sizeof sa);
   sa.r = rows;
   sa.S = p.S;
@@ -507,10 +533,35 @@ hipError_t launch_seq_half(const Plan& p, const RowsDev& rows, int Hkv, int d, i
   sa.out_dtype = out->dtype;
   sa.lse_seq_out = opts ? opts->lse_seq : nullptr;
   sa.nsplit = p.nsplit;
-  sa.part = p.nsplit > 1 ? (float*)(ws + p.off_part) : nullptr;
+  h.overlap = seq_k && v->aux && !(opts && opts->phase_events && opts->n_phase_events > 0);
+  // with a sequence the merge is always k_seq_combine's, so the serial and
+  // the overlapped order produce the same bits
+  sa.part = seq_k ? (float*)(ws + p.off_part) : nullptr;
   sa.split_len = p.nsplit > 1 ? seq_split_len(p.S, p.nsplit) : (p.S > 0 ? p.S : 1);
-  hipError_t e = pm.mark(launch_seq_attend(sa, s));
-  if (e == hipSuccess) e = pm.mark(launch_seq_combine(sa, s));
+  return h;
+}
+
+// Before the KG half: the fork (when overlapping).
+hipError_t seq_start(const SeqHalf& h, atlaskv_tree_view_s* v, hipStream_t s) {
+  if (!h.overlap) return hipSuccess;
+  std::lock_guard<std::mutex> lock(v->mu);  // one call's record / wait / launch / record stay together
+  hipError_t e = hipEventRecord(v->fork, s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(v->aux, v->fork, 0);
+  if (e == hipSuccess) e = launch_seq_attend(h.sa, v->aux);
+  if (e == hipSuccess) e = hipEventRecord(v->join, v->aux);
+  return e;
+}
+
+// After the KG half: the join and the combine, or the serial sequence half.
+hipError_t seq_finish(const SeqHalf& h, atlaskv_tree_view_s* v, hipStream_t s, PhaseMarks& pm) {
+  if (h.overlap) {
+    // a later call's join only comes later on aux: waiting on it is still enough
+    hipError_t e = hipStreamWaitEvent(s, v->join, 0);
+    if (e == hipSuccess) e = launch_seq_combine(h.sa, s);
+    return e;
+  }
+  hipError_t e = pm.mark(launch_seq_attend(h.sa, s));
+  if (e == hipSuccess) e = pm.mark(launch_seq_combine(h.sa, s));
   return e;
 }
 
@@ -588,7 +639,7 @@ atlaskv_status atlaskv_build_tree_view(const atlaskv_tensor* root_k, const atlas
   atlaskv_status st = check_tree_tensors(root_k, mid_k, leaf_k, leaf_v);
   if (st) return st;
   if (!root_child_off || !mid_child_off) return fail(ATLASKV_ERR_NULL, "child offsets are NULL");
-  atlaskv_tree_view_s* v = (atlaskv_tree_view_s*)calloc(1, sizeof(atlaskv_tree_view_s));
+  atlaskv_tree_view_s* v = new (std::nothrow) atlaskv_tree_view_s();
   if (!v) return fail(ATLASKV_ERR_HIP, "host allocation failed");
   fill_tree(v->dev, root_k, mid_k, leaf_k, leaf_v);
   {
@@ -600,7 +651,7 @@ atlaskv_status atlaskv_build_tree_view(const atlaskv_tensor* root_k, const atlas
     for (int i = 0; i < 6; ++i) {
       int host = 0;
       st = device_address(given[i], names[i], &addr[i], &host);
-      if (st) { free(v); return st; }
+      if (st) { release_view(v); return st; }
       if (host) v->host_mask |= 1 << i;
     }
     for (int i = 0; i < 3; ++i) v->dev.key[i] = addr[i];
@@ -611,10 +662,14 @@ atlaskv_status atlaskv_build_tree_view(const atlaskv_tensor* root_k, const atlas
   v->stream = (hipStream_t)stream;
   const int Hkv = v->dev.Hkv;
   const size_t stats_bytes = offsetof(BuildStats, norm_bits) + sizeof(unsigned int) * 3 * (size_t)Hkv;
-  hipError_t e = hipMalloc((void**)&v->stats, stats_bytes);
-  if (e != hipSuccess) { free(v); return hip_fail(e, "hipMalloc(tree stats)"); }
+  hipError_t e = hipStreamCreateWithFlags(&v->aux, hipStreamNonBlocking);  // default priority
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&v->fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&v->join, hipEventDisableTiming);
+  if (e != hipSuccess) { release_view(v); return hip_fail(e, "stream/event creation"); }
+  e = hipMalloc((void**)&v->stats, stats_bytes);
+  if (e != hipSuccess) { release_view(v); return hip_fail(e, "hipMalloc(tree stats)"); }
   BuildStats* host = (BuildStats*)calloc(1, stats_bytes);
-  if (!host) { (void)hipFree(v->stats); free(v); return fail(ATLASKV_ERR_HIP, "host allocation failed"); }
+  if (!host) { (void)hipFree(v->stats); release_view(v); return fail(ATLASKV_ERR_HIP, "host allocation failed"); }
   hipStream_t s = v->stream;
   e = hipMemcpyAsync(v->stats, host, stats_bytes, hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = launch_validate(v->dev.off[0], v->dev.count[0], v->dev.count[1], 0, v->stats, s);
@@ -627,7 +682,7 @@ atlaskv_status atlaskv_build_tree_view(const atlaskv_tensor* root_k, const atlas
   if (e != hipSuccess) {
     free(host);
     (void)hipFree(v->stats);
-    free(v);
+    release_view(v);
     return hip_fail(e, "tree validation");
   }
   const int bad = host->bad;
@@ -636,7 +691,7 @@ atlaskv_status atlaskv_build_tree_view(const atlaskv_tensor* root_k, const atlas
   free(host);
   if (bad) {
     (void)hipFree(v->stats);
-    free(v);
+    release_view(v);
     return fail(ATLASKV_ERR_TREE, "malformed child offsets (%s%s)", (bad & 1) ? "root->mid " : "",
                 (bad & 2) ? "mid->leaf" : "");
   }
@@ -655,7 +710,7 @@ atlaskv_status atlaskv_tree_view_describe(const atlaskv_tensor* root_k, const at
   if (max_root_fanout < 0 || max_mid_fanout < 0 || max_root_fanout > mid_k->shape[1] ||
       max_mid_fanout > leaf_k->shape[1])
     return fail(ATLASKV_ERR_TREE, "maximum fanouts outside 0..level size");
-  atlaskv_tree_view_s* v = (atlaskv_tree_view_s*)calloc(1, sizeof(atlaskv_tree_view_s));
+  atlaskv_tree_view_s* v = new (std::nothrow) atlaskv_tree_view_s();
   if (!v) return fail(ATLASKV_ERR_HIP, "host allocation failed");
   fill_tree(v->dev, root_k, mid_k, leaf_k, leaf_v);
   v->maxfan[0] = max_root_fanout;
@@ -671,7 +726,7 @@ atlaskv_status atlaskv_destroy_tree_view(atlaskv_tree_view v) {
   if (!v) return ATLASKV_OK;
   hipError_t e = hipSuccess;
   if (v->stats) e = hipFree(v->stats);
-  free(v);
+  release_view(v);
   return e == hipSuccess ? ATLASKV_OK : hip_fail(e, "hipFree(tree stats)");
 }
 
@@ -745,9 +800,12 @@ atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vie
   float* o_kg = (float*)(ws + p.off_okg);
 
   PhaseMarks pm(opts, s);
+  const SeqHalf sh = seq_prepare(p, rows, v->dev.Hkv, v->dev.d, v->dev.dtype, seq_k, seq_v, out, opts, o_kg,
+                                 lse_kg, ws, v);
   hipError_t e = pm.mark(hipSuccess);
+  if (e == hipSuccess) e = seq_start(sh, v, s);
   if (e == hipSuccess) e = launch_descent(p, rows, v, ws, sel, o_kg, lse_kg, s, pm);
-  if (e == hipSuccess) e = launch_seq_half(p, rows, v->dev.Hkv, v->dev.d, v->dev.dtype, seq_k, seq_v, out, opts, o_kg, lse_kg, ws, s, pm);
+  if (e == hipSuccess) e = seq_finish(sh, v, s, pm);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return ATLASKV_OK;
 }
@@ -842,13 +900,16 @@ atlaskv_status atlaskv_shared_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vi
   sa.o_kg = o_kg;
   sa.lse_kg = lse_kg;
   PhaseMarks pm(opts, s);
+  const SeqHalf sh = seq_prepare(p, rows, v->dev.Hkv, v->dev.d, v->dev.dtype, seq_k, seq_v, out, opts, o_kg,
+                                 lse_kg, ws, v);
   hipError_t e = pm.mark(hipSuccess);
+  if (e == hipSuccess) e = seq_start(sh, v, s);
   if (e == hipSuccess) e = pm.mark(launch_group_query(sa, s));
   // the descent on the group rows; its own KG softmax lands in its workspace
   if (e == hipSuccess)
     e = launch_descent(pg, grows, v, ws, sel, (float*)(ws + pg.off_okg), (float*)(ws + pg.off_lse), s, pm);
   if (e == hipSuccess) e = pm.mark(launch_shared_kg(sa, s));
-  if (e == hipSuccess) e = launch_seq_half(p, rows, v->dev.Hkv, v->dev.d, v->dev.dtype, seq_k, seq_v, out, opts, o_kg, lse_kg, ws, s, pm);
+  if (e == hipSuccess) e = seq_finish(sh, v, s, pm);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return ATLASKV_OK;
 }
@@ -935,11 +996,14 @@ atlaskv_status atlaskv_folded_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vi
   fa.o_kg = o_kg;
   fa.lse_kg = lse_kg;
   PhaseMarks pm(opts, s);
+  const SeqHalf sh = seq_prepare(p, rows, p.fold_Hkv, p.fold_d, v->dev.dtype, seq_k, seq_v, out, opts, o_kg,
+                                 lse_kg, ws, v);
   hipError_t e = pm.mark(hipSuccess);
+  if (e == hipSuccess) e = seq_start(sh, v, s);
   if (p.fold_kg_empty) {
     // no descent: seven empty phases keep the event numbering
     for (int i = 0; i < 8 && e == hipSuccess; ++i) e = pm.mark(hipSuccess);
-  } else {
+  } else if (e == hipSuccess) {
     e = pm.mark(launch_fold_query(fa, s));
     atlaskv_tensor qd = group_rows_desc(p.B, p.N, p.Hq, v->dev.d, v->dev.dtype, fa.qf);
     RowsDev frows;
@@ -953,8 +1017,7 @@ atlaskv_status atlaskv_folded_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vi
   }
   if (e == hipSuccess) e = pm.mark(launch_unfold_values(fa, p.fold_kg_empty != 0, s));
   if (e == hipSuccess)
-    e = launch_seq_half(p, rows, p.fold_Hkv, p.fold_d, v->dev.dtype, seq_k, seq_v, out, opts, o_kg, lse_kg, ws,
-                        s, pm);
+    e = seq_finish(sh, v, s, pm);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return ATLASKV_OK;
 }
@@ -995,7 +1058,10 @@ atlaskv_status atlaskv_flat_attend_ex(const atlaskv_tensor* q, atlaskv_tree_view
   float* lse_kg = (opts && opts->lse_kg) ? opts->lse_kg : (float*)(ws + p.off_lse);
   float* o_kg = (float*)(ws + p.off_okg);
   PhaseMarks pm(opts, s);
+  const SeqHalf sh = seq_prepare(p, rows, v->dev.Hkv, v->dev.d, v->dev.dtype, seq_k, seq_v, out, opts, o_kg,
+                                 lse_kg, ws, v);
   hipError_t e = pm.mark(hipSuccess);
+  if (e == hipSuccess) e = seq_start(sh, v, s);
   FlatArgs fa;
   memset(&fa, 0, sizeof fa);
   fa.t = v->dev;
@@ -1009,7 +1075,7 @@ atlaskv_status atlaskv_flat_attend_ex(const atlaskv_tensor* q, atlaskv_tree_view
   // KG half over every leaf, then the sequence half and the λ merge as in the pruned path
   if (e == hipSuccess) e = pm.mark(launch_flat_partial(fa, s));
   if (e == hipSuccess) e = pm.mark(launch_flat_combine(fa, s));
-  if (e == hipSuccess) e = launch_seq_half(p, rows, v->dev.Hkv, v->dev.d, v->dev.dtype, seq_k, seq_v, out, opts, o_kg, lse_kg, ws, s, pm);
+  if (e == hipSuccess) e = seq_finish(sh, v, s, pm);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return ATLASKV_OK;
 }

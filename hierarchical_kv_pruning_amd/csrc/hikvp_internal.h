@@ -97,7 +97,8 @@ struct SeqArgs {
   int64_t os[3];
   int out_dtype;
   float* lse_seq_out;         // optional [R]
-  float* part;                // [R, nsplit, d + 2] split partials (NULL: no key split)
+  float* part;                // [R, nsplit, d + 2] partials for k_seq_combine (NULL: the attention
+                              // kernel merges and stores the output itself; needs nsplit == 1)
   int nsplit;                 // key splits per row
   int split_len;              // keys per split (multiple of 64); >= S when not split
 };

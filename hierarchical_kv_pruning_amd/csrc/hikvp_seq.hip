@@ -203,7 +203,7 @@ __global__ __launch_bounds__(64) void k_seq_decode(SeqArgs a) {
   for (int hh = 0; hh < nh; ++hh) {
     const int h = g * G + hgp * HG + hh;
     const int row = (b * a.r.N + n) * a.r.Hq + h;
-    if (nsplit > 1) {  // partial (acc, m, l) for k_seq_combine
+    if (a.part) {  // partial (acc, m, l) for k_seq_combine
       float* part = a.part + ((int64_t)row * nsplit + split) * (D + 2);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) part[c * EPL + e] = acc[hh][e];
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(256) void k_seq_flash(SeqArgs a) {
       const int tok = n0 + quad * 4 + v;
       if (tok >= N) continue;
       const int row = (b * N + tok) * a.r.Hq + h;
-      if (nsplit > 1) {  // partial (acc, m, l) for k_seq_combine
+      if (a.part) {  // partial (acc, m, l) for k_seq_combine
         float* part = a.part + ((int64_t)row * nsplit + split) * (D + 2);
 #pragma unroll
         for (int c = 0; c < NCT; ++c) part[c * 16 + col] = O[c][v];
@@ -511,7 +511,7 @@ void k_seq_mfma(SeqArgs a, int tiles) {
   const int64_t row = ((int64_t)b * a.r.N + n) * a.r.Hq + h;
   constexpr float kLn2 = 0.6931471805599453f;
   const bool has = S.l > 0.f;
-  if (nsplit > 1) {  // partial (o, m, l) for k_seq_combine, m in natural-log units
+  if (a.part) {  // partial (o, m, l) for k_seq_combine, m in natural-log units
     float* part = a.part + (row * nsplit + split) * (D + 2);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -624,7 +624,7 @@ hipError_t launch_seq_attend(const SeqArgs& a, hipStream_t s) {
 
 hipError_t launch_seq_combine(const SeqArgs& a, hipStream_t s) {
   const int nsplit = a.part ? a.nsplit : 1;
-  if (a.r.R <= 0 || nsplit <= 1) return hipSuccess;  // unsplit rows were merged by the attention kernel
+  if (a.r.R <= 0 || !a.part) return hipSuccess;  // without partials the attention kernel merged
   const unsigned cblocks = (unsigned)((a.r.R + 3) / 4);
   HIKVP_DISPATCH(a.dtype, a.d, k_seq_combine, dim3(cblocks), dim3(256), 0, s, a, nsplit);
   return hipGetLastError();

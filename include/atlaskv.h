@@ -45,10 +45,17 @@
  *   - atlaskv_hikvp_attend* allocate nothing: scratch memory is the caller's
  *     workspace (size from atlaskv_hikvp_workspace_size).  Only
  *     atlaskv_build_tree_view allocates (a few bytes of device memory per KV
- *     head, freed by atlaskv_destroy_tree_view) and synchronises its stream;
+ *     head, one stream and two events, freed by atlaskv_destroy_tree_view) and
+ *     synchronises its stream;
  *   - attend calls are asynchronous on their stream; device faults surface at
  *     the caller's next synchronisation.  Calls on different streams need
  *     separate workspaces; calls sharing a workspace must be stream-ordered.
+ *     Unless phase events are requested, the causal sequence half runs on a
+ *     second stream that the view owns (default priority), forked from the
+ *     call's stream by an event before the KG kernels and joined back before
+ *     the merge, so it overlaps the KG half; the call's stream still orders
+ *     everything the call reads and writes.  With phase events the halves run
+ *     one after the other on the call's stream (same results, bit for bit).
  *
  * Errors: every entry point returns an atlaskv_status.  Argument errors are
  * detected on the host before anything is enqueued, so a failed call writes

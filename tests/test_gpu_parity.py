@@ -169,6 +169,29 @@ def test_deterministic_with_overflowing_buckets():
     _check(case, K=K)
 
 
+@pytest.mark.parametrize("N,S_kv", [(33, 45), (1, 300)])
+def test_overlapped_and_serial_sequence_half_agree(N, S_kv):
+    """Without phase events the sequence half runs on the view's second stream
+    beside the KG half and k_seq_combine merges; with phase events it runs
+    after the KG half.  Both write the same bits (prefill and decode)."""
+    case = _small(seed=23, dtype="bf16", B=2, N=N, S_kv=S_kv, Hq=8, Hkv=2)
+    tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
+    ws = atlaskv.alloc_workspace(tree, case.q, case.seq_k, case.K)
+    outs = []
+    for timed in (False, True, False):
+        out = torch.full(case.q.shape, float("nan"), dtype=torch.float32, device=DEV)
+        lse = torch.full((case.rows,), 7.0, dtype=torch.float32, device=DEV)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(atlaskv.phase_names()) + 1)] if timed else None
+        atlaskv.hikvp_attend_ex(case.q, tree, case.seq_k, case.seq_v, case.K, out, workspace=ws, lse_seq=lse,
+                                phase_events=evs)
+        torch.cuda.synchronize()
+        outs.append((out.cpu().numpy(), lse.cpu().numpy()))
+    tree.close()
+    for o, l in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(l, outs[0][1])
+    assert np.isfinite(outs[0][0]).all()
+
+
 def test_empty_batch_writes_nothing():
     case = _small(seed=15, N=1, S_kv=4)
     tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
