@@ -32,9 +32,13 @@ struct atlaskv_tree_view_s {
   int described_only;
   int host_mask;               // bit i: tree tensor i (root_k, mid_k, leaf_k, leaf_v) in pinned host memory
   // the sequence half runs on aux, forked from and joined back to the call's
-  // stream with two events; mu keeps one call's fork sequence whole
+  // stream with two events; parts 1.. of a split descent run on part_s[],
+  // forked with part_fork and joined with part_join[]; mu keeps one call's
+  // fork sequences whole
   hipStream_t aux;
-  hipEvent_t fork, join;
+  hipEvent_t fork, join, part_fork;
+  hipStream_t part_s[kMaxParts - 1];
+  hipEvent_t part_join[kMaxParts - 1];
   std::mutex mu;
 };
 
@@ -44,6 +48,11 @@ thread_local std::string g_err;
 
 // Frees a view and whatever of its HIP objects exist (not its tree stats).
 void release_view(atlaskv_tree_view_s* v) {
+  for (int i = 0; i < kMaxParts - 1; ++i) {
+    if (v->part_join[i]) (void)hipEventDestroy(v->part_join[i]);
+    if (v->part_s[i]) (void)hipStreamDestroy(v->part_s[i]);
+  }
+  if (v->part_fork) (void)hipEventDestroy(v->part_fork);
   if (v->join) (void)hipEventDestroy(v->join);
   if (v->fork) (void)hipEventDestroy(v->fork);
   if (v->aux) (void)hipStreamDestroy(v->aux);
@@ -178,9 +187,16 @@ struct Plan {
   int nsplit;
   size_t off_mid, off_leaf, off_sel[3], off_okg, off_lse, off_part, total;
   size_t off_mid_base, off_bcnt, off_bslot, off_bhead, off_bnext, off_blist, off_bcount, off_bovf, off_junk;
-  size_t off_rcnt, off_rtot, off_rrank, off_rbase, off_rtoff, off_rtkey, off_rnt, off_rmem;
+  size_t off_rcnt, off_rtot, off_rtoff, off_rtkey, off_rnt, off_rmem;
   int64_t root_tiles_max;
   int32_t desc_per_sub, bucket_q;
+  // descent parts: KV heads [part_g[i], part_g[i+1]) with their own tile,
+  // descriptor, count and overflow-key regions (totals above: one part over
+  // all heads uses the regions concatenated)
+  int nparts;
+  int part_g[kMaxParts + 1];
+  int64_t part_tiles[kMaxParts], part_ovf[kMaxParts];
+  int32_t part_desc[kMaxParts];
   int flat_nsplit, flat_split_len, flat_row_tiles;  // unpruned path only
   size_t off_fpart;
   int group_rows;                                    // shared selections only
@@ -341,14 +357,28 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   for (int i = 0; i < 3; ++i) { p.off_sel[i] = o; o = align256(o + R * (size_t)p.K[i] * 4); }
   p.off_mid_base = o;  o = align256(o + R * (size_t)p.K[1] * 4);
   const size_t nroot = (size_t)t.Hkv * (size_t)t.count[0];
-  p.root_tiles_max = (int64_t)(R * (size_t)p.K[0] / kRootTile + nroot);
+  // the descent runs in concurrent parts (ranges of KV heads) when there
+  // are enough rows for each part's kernels to fill the GPU
+  p.nparts = descent_parts(t.Hkv, (int64_t)R);
+  int64_t tiles_all = 0, ovf_all = 0, desc_all = 0;
+  for (int i = 0; i < p.nparts; ++i) {
+    p.part_g[i] = i * t.Hkv / p.nparts;
+    p.part_g[i + 1] = (i + 1) * t.Hkv / p.nparts;
+    const int64_t heads = p.part_g[i + 1] - p.part_g[i], rows = heads * p.B * p.N * p.G;
+    p.part_tiles[i] = rows * p.K[0] / kRootTile + heads * t.count[0] + 1;
+    p.part_desc[i] = (int32_t)(((int64_t)row_chunks((int)rows, p.K[1]) + kDescSub - 1) / kDescSub *
+                               row_chunk_entries(p.K[1]));
+    p.part_ovf[i] = rows * p.K[1] / (kBucketSlots + 1) + 1;
+    tiles_all += p.part_tiles[i];
+    desc_all += p.part_desc[i];
+    ovf_all += p.part_ovf[i];
+  }
+  p.root_tiles_max = tiles_all;
   p.off_rcnt = o;      o = align256(o + nroot * kRootSub * 4);
   p.off_rtot = o;      o = align256(o + nroot * 4);
-  p.off_rrank = o;     o = align256(o + R * (size_t)p.K[0] * 4);
-  p.off_rbase = o;     o = align256(o + R * (size_t)p.K[0] * 4);
   p.off_rtoff = o;     o = align256(o + nroot * 4);
   p.off_rtkey = o;     o = align256(o + (size_t)p.root_tiles_max * 4);
-  p.off_rnt = o;       o = align256(o + 4);
+  p.off_rnt = o;       o = align256(o + kMaxParts * 4);
   p.off_rmem = o;      o = align256(o + (size_t)p.root_tiles_max * kRootTile * 8);
   p.bucket_q = (int32_t)(((size_t)t.Hkv * (size_t)t.count[1] + 63) / 64);
   const size_t nbix = (size_t)p.bucket_q * 64;
@@ -356,11 +386,12 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   p.off_bslot = o;     o = align256(o + nbix * 8 * kBucketSlots);
   p.off_bhead = o;     o = align256(o + nbix * 4);
   p.off_bnext = o;     o = align256(o + R * (size_t)p.K[1] * 4);
-  // chunk c of 64 selections appends to sub-list c mod kDescSub
-  p.desc_per_sub = (int32_t)(((R * (size_t)p.K[1] + 63) / 64 + kDescSub - 1) / kDescSub * 64);
-  p.off_blist = o;     o = align256(o + (size_t)p.desc_per_sub * kDescSub * 16);
-  p.off_bcount = o;    o = align256(o + (kDescSub + 1) * 4);
-  p.off_bovf = o;      o = align256(o + (R * (size_t)p.K[1] / (kBucketSlots + 1) + 1) * 4);
+  // link chunk c appends to sub-list c mod kDescSub (of its part)
+  if (desc_all >= kIndexLimit) return fail(ATLASKV_ERR_UNSUPPORTED, "bucket descriptor capacity above 2^31");
+  p.desc_per_sub = (int32_t)desc_all;
+  p.off_blist = o;     o = align256(o + (size_t)desc_all * kDescSub * 16);
+  p.off_bcount = o;    o = align256(o + (size_t)kMaxParts * (kDescSub + 1) * 4);
+  p.off_bovf = o;      o = align256(o + (size_t)ovf_all * 4);
   p.off_junk = o;      o = align256(o + (size_t)kJunkSlots * 64);
   p.off_okg = o;       o = align256(o + R * (size_t)t.d * 4);
   p.off_lse = o;       o = align256(o + R * 4);
@@ -565,12 +596,31 @@ hipError_t seq_finish(const SeqHalf& h, atlaskv_tree_view_s* v, hipStream_t s, P
   return e;
 }
 
+// One part of the descent (KV heads [a.g0, a.g1)) on stream s.
+hipError_t descent_part(const StepArgs& a, hipStream_t s, PhaseMarks& pm) {
+  auto mark = [&](hipError_t prev) { return pm.mark(prev); };
+  hipError_t e = launch_clear(a, s);
+  if (e == hipSuccess) e = launch_root(a, s);
+  if (e == hipSuccess) e = mark(launch_root_groups(a, s));
+  if (e == hipSuccess) e = mark(launch_mid_gemm(a, s));
+  if (e == hipSuccess) e = mark(launch_mid_select(a, s));
+  if (e == hipSuccess) e = mark(launch_leaf_link(a, s));
+  if (e == hipSuccess) e = mark(launch_leaf_score(a, s));
+  if (e == hipSuccess) e = mark(launch_leaf_overflow(a, s));
+  if (e == hipSuccess) e = mark(launch_leaf_select(a, s));
+  return e;
+}
+
 // The pruned descent for `rows` (速读 › 怎么做的: roots -> Top-K -> their
 // children -> Top-K -> leaves -> Top-K, then the KG softmax over the selected
-// leaves into o_kg / lse_kg): seven timing phases.
-hipError_t launch_descent(const Plan& p, const RowsDev& rows, const atlaskv_tree_view_s* v, char* ws,
+// leaves into o_kg / lse_kg): seven timing phases.  Every index structure of
+// the descent is keyed by KV head, so the heads split into parts that share
+// no state; part 0 runs on s and parts 1.. on the view's part streams
+// (forked from s, joined back to it), so that one part's kernel tails and
+// launch gaps are filled by the others' work.  With phase timing requested
+// the descent runs as one part over all heads, serially on s.
+hipError_t launch_descent(const Plan& p, const RowsDev& rows, atlaskv_tree_view_s* v, char* ws,
                           int32_t* const sel[3], float* o_kg, float* lse_kg, hipStream_t s, PhaseMarks& pm) {
-  auto mark = [&](hipError_t prev) { return pm.mark(prev); };
   StepArgs a;
   memset(&a, 0, sizeof a);
   a.t = v->dev;
@@ -583,8 +633,6 @@ hipError_t launch_descent(const Plan& p, const RowsDev& rows, const atlaskv_tree
   a.mid_base = (int32_t*)(ws + p.off_mid_base);
   a.root_cnt = (int32_t*)(ws + p.off_rcnt);
   a.root_tot = (int32_t*)(ws + p.off_rtot);
-  a.root_rank = (int32_t*)(ws + p.off_rrank);
-  a.root_base = (int32_t*)(ws + p.off_rbase);
   a.root_tile_off = (int32_t*)(ws + p.off_rtoff);
   a.root_tile_key = (int32_t*)(ws + p.off_rtkey);
   a.root_ntiles = (int32_t*)(ws + p.off_rnt);
@@ -602,15 +650,46 @@ hipError_t launch_descent(const Plan& p, const RowsDev& rows, const atlaskv_tree
   a.junk = (float*)(ws + p.off_junk);
   a.o_kg = o_kg;
   a.lse_kg = lse_kg;
-  hipError_t e = launch_clear(a, s);
-  if (e == hipSuccess) e = launch_root(a, s);
-  if (e == hipSuccess) e = mark(launch_root_groups(a, s));
-  if (e == hipSuccess) e = mark(launch_mid_gemm(a, s));
-  if (e == hipSuccess) e = mark(launch_mid_select(a, s));
-  if (e == hipSuccess) e = mark(launch_leaf_link(a, s));
-  if (e == hipSuccess) e = mark(launch_leaf_score(a, s));
-  if (e == hipSuccess) e = mark(launch_leaf_overflow(a, s));
-  if (e == hipSuccess) e = mark(launch_leaf_select(a, s));
+  const int per_head = rows.B * rows.N * rows.G;  // row blocks per KV head
+  if (p.nparts < 2 || !v->part_s[0] || pm.ev) {
+    a.g0 = 0;
+    a.g1 = a.t.Hkv;
+    a.blk0 = 0;
+    a.blk1 = rows.R;
+    return descent_part(a, s, pm);
+  }
+  StepArgs part[kMaxParts];
+  int64_t tiles = 0, ovf = 0, desc = 0;
+  for (int i = 0; i < p.nparts; ++i) {
+    StepArgs& b = part[i];
+    b = a;
+    b.g0 = p.part_g[i];
+    b.g1 = p.part_g[i + 1];
+    b.blk0 = b.g0 * per_head;
+    b.blk1 = b.g1 * per_head;
+    b.root_tile_key = a.root_tile_key + tiles;
+    b.root_members = a.root_members + tiles * kRootTile;
+    b.root_tiles_max = p.part_tiles[i];
+    b.root_ntiles = a.root_ntiles + i;
+    b.bucket_desc = a.bucket_desc + desc * kDescSub;
+    b.desc_per_sub = p.part_desc[i];
+    b.bucket_count = a.bucket_count + i * (kDescSub + 1);
+    b.bucket_ovf = a.bucket_ovf + ovf;
+    tiles += p.part_tiles[i];
+    desc += p.part_desc[i];
+    ovf += p.part_ovf[i];
+  }
+  std::lock_guard<std::mutex> lock(v->mu);  // one call's records / waits / launches stay together
+  hipError_t e = hipEventRecord(v->part_fork, s);
+  for (int i = 1; i < p.nparts && e == hipSuccess; ++i) {
+    hipStream_t ps = v->part_s[i - 1];
+    PhaseMarks none(nullptr, ps);
+    e = hipStreamWaitEvent(ps, v->part_fork, 0);
+    if (e == hipSuccess) e = descent_part(part[i], ps, none);
+    if (e == hipSuccess) e = hipEventRecord(v->part_join[i - 1], ps);
+  }
+  if (e == hipSuccess) e = descent_part(part[0], s, pm);
+  for (int i = 1; i < p.nparts && e == hipSuccess; ++i) e = hipStreamWaitEvent(s, v->part_join[i - 1], 0);
   return e;
 }
 
@@ -662,9 +741,15 @@ atlaskv_status atlaskv_build_tree_view(const atlaskv_tensor* root_k, const atlas
   v->stream = (hipStream_t)stream;
   const int Hkv = v->dev.Hkv;
   const size_t stats_bytes = offsetof(BuildStats, norm_bits) + sizeof(unsigned int) * 3 * (size_t)Hkv;
-  hipError_t e = hipStreamCreateWithFlags(&v->aux, hipStreamNonBlocking);  // default priority
+  // all streams at the default priority
+  hipError_t e = hipStreamCreateWithFlags(&v->aux, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&v->fork, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&v->join, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&v->part_fork, hipEventDisableTiming);
+  for (int i = 0; i < kMaxParts - 1 && e == hipSuccess; ++i) {
+    e = hipStreamCreateWithFlags(&v->part_s[i], hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&v->part_join[i], hipEventDisableTiming);
+  }
   if (e != hipSuccess) { release_view(v); return hip_fail(e, "stream/event creation"); }
   e = hipMalloc((void**)&v->stats, stats_bytes);
   if (e != hipSuccess) { release_view(v); return hip_fail(e, "hipMalloc(tree stats)"); }

@@ -200,16 +200,21 @@ __device__ inline int row_of_block(const RowsDev& r, int blk) {
 
 // Candidate list of a row at one level: the children of its selected
 // parents, in the parents' order.  pre[k] = first slot of parent k,
-// base[k] = global index of parent k's first child.  One whole wave.
+// base[k] = global index of parent k's first child.  One whole wave; the
+// span (first0, fan0) of parent `lane` (< 64) is passed in, read early.
 __device__ inline int build_candidates(const int32_t* parents, int Kp, const int64_t* off,
-                                       int lane, int* pre, int64_t* base) {
+                                       int lane, int* pre, int64_t* base, int64_t first0, int fan0) {
   int carry = 0;
   if (lane == 0) pre[0] = 0;
   for (int k0 = 0; k0 < Kp; k0 += 64) {
     const int k = k0 + lane;
     int fan = 0;
     int64_t first = 0;
-    if (k < Kp) {
+    if (k0 == 0) {
+      first = first0;
+      fan = fan0;
+      if (k < Kp) base[k] = first;
+    } else if (k < Kp) {
       const int p = parents[k];
       if (p >= 0) {
         first = off[p];

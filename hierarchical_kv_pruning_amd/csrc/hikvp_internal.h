@@ -12,8 +12,32 @@ constexpr int kBucketSlots = 32;  // members of a (head, mid) bucket stored with
 constexpr int kJunkSlots = 1024;  // per-wave sinks for masked-off score stores
 constexpr int kRootTile = 16;     // member rows per mid-GEMM work item
 constexpr int kRootSub = 16;      // counters per (head, root) group, picked by token
-constexpr int kDescSub = 64;      // bucket descriptor sub-lists, picked by 64-selection chunk
+constexpr int kDescSub = 64;      // bucket descriptor sub-lists, picked by link chunk
+constexpr int kMaxParts = 2;      // descent parts (KV-head ranges run concurrently)
 constexpr int kDtypeF32 = 0;
+
+// Row-aligned work chunks of the kernels that scan a row's K selections in
+// one wave (root fill, bucket link): floor(64 / K) whole rows each when
+// K <= 64, else one row each; and the most selections one chunk holds.
+// Parts of a split descent: as many KV-head ranges as keep kPartRows rows or
+// more each (at most kMaxParts, at most one per head).  Two concurrent parts
+// measured faster than one at 16384 rows and no slower at 4096; more parts
+// (more streams) measured slower.
+constexpr int64_t kPartRows = 2048;
+inline int descent_parts(int Hkv, int64_t rows) {
+  int64_t n = rows / kPartRows;
+  if (n > kMaxParts) n = kMaxParts;
+  if (n > Hkv) n = Hkv;
+  return n < 1 ? 1 : (int)n;
+}
+
+__host__ __device__ inline int row_chunks(int R, int K1) {
+  return K1 <= 0 ? 0 : K1 <= 64 ? (R + 64 / K1 - 1) / (64 / K1) : R;
+}
+__host__ __device__ inline int row_chunk_entries(int K1) {
+  return K1 <= 0 ? 0 : K1 <= 64 ? 64 / K1 * K1 : K1;
+}
+
 constexpr int kDtypeBF16 = 1;
 
 // A three-level key tree in device memory.  Levels: 0 root, 1 mid, 2 leaf.
@@ -38,10 +62,17 @@ struct RowsDev {
   double scale;               // logit scale (the fp64 ranking uses exactly this value)
 };
 
-// One attend call's selection path (root -> mid -> leaf -> KG attention).
+// One attend call's selection path (root -> mid -> leaf -> KG attention),
+// for the rows of KV heads [g0, g1): row blocks [blk0, blk1) in the
+// KV-head-major block order of row_of_block.  Every index structure below
+// is keyed by KV head (or by row), so parts with disjoint heads can run
+// concurrently; the per-part ones (tiles, descriptors, counts, overflow
+// keys) point into the part's own region.
 struct StepArgs {
   TreeDev t;
   RowsDev r;
+  int g0, g1;                 // KV heads of this part
+  int blk0, blk1;             // row blocks of this part
   int K[3];                   // Top-K per level (before clamping)
   int64_t c1max;              // mid candidates per row: capacity and row stride of mid_scores
   int64_t c2max;              // leaf candidates per row: capacity
@@ -53,13 +84,11 @@ struct StepArgs {
   int32_t* root_cnt;          // [kRootSub, Hkv * M_R] rows per sub-counter; the scan turns
                               // them into each sub-counter's first rank in the group
   int32_t* root_tot;          // [Hkv * M_R] rows that selected the (head, root)
-  int32_t* root_rank;         // [R, K[0]] rank of the selection within its group
-  int32_t* root_base;         // [R, K[0]] first mid-candidate slot of each selected root
   int32_t* root_tile_off;     // [Hkv * M_R] first work item (tile) of each group
   int32_t* root_tile_key;     // [root_tiles_max] group (key g*M_R + root) of each tile
   int32_t* root_ntiles;       // [1] tiles in use
   int2* root_members;         // [root_tiles_max * kRootTile] (row, first mid slot)
-  int64_t root_tiles_max;     // R*K[0]/kRootTile + Hkv*M_R
+  int64_t root_tiles_max;     // rows*K[0]/kRootTile + heads*M_R + 1 (rows, heads of the part)
   // (head, mid) bucket arrays are indexed by bucket_index(key) (below), which
   // spreads neighbouring mids (siblings, selected together) over cache lines
   int32_t* bucket_cnt;        // [64 * bucket_q] rows that selected the (head, mid)
@@ -68,13 +97,13 @@ struct StepArgs {
   int32_t* bucket_next;       // [R * K[1]] next overflow entry of the same (head, mid)
   int4* bucket_desc;          // [kDescSub, desc_per_sub] distinct (head, mid): key g*M_I+mid, fanout,
                               // first leaf element (lo, hi); sub-list s holds buckets first
-                              // registered by a chunk c of 64 selections with c mod kDescSub = s
+                              // registered by a link chunk c with c mod kDescSub = s
   int32_t* bucket_count;      // [kDescSub + 1] descriptors per sub-list; [kDescSub]: keys with more
                               // than kBucketSlots rows
-  int32_t desc_per_sub;       // ceil(ceil(R*K[1] / 64) / kDescSub) * 64: a sub-list's capacity
+  int32_t desc_per_sub;       // ceil(row_chunks(rows, K[1]) / kDescSub) * row_chunk_entries(K[1])
   int32_t bucket_q;           // ceil(Hkv * M_I / 64)
   float* junk;                // [kJunkSlots * 16] write-only sinks for masked-off score lanes
-  int32_t* bucket_ovf;        // [R * K[1] / (kBucketSlots + 1) + 1] keys (g*M_I + mid) with overflow members
+  int32_t* bucket_ovf;        // [rows * K[1] / (kBucketSlots + 1) + 1] keys (g*M_I + mid) with overflow members
   float* o_kg;                // [R, d] softmax-weighted leaf values (fp32)
   float* lse_kg;              // [R] log-sum-exp of the selected leaf logits
 };

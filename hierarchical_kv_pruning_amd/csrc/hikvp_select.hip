@@ -6,21 +6,24 @@
 // branches and keep the Top-K, and so on down to the leaves; the selected
 // leaves' softmax then forms the KG half of the merged output.
 //
-//   k_clear     zeroes the bucket counters of both levels.
+//   k_clear     zeroes the group and bucket counters of the part's KV heads.
 //   k_root      one wave per row: scores of all M_R root keys of the row's KV
 //               head (coalesced 16-byte lanes), exact-boundary Top-K_R; each
-//               selection takes a rank in its (KV head, root) group and
-//               records where the root's children start in the row's mid
-//               candidate list.  The per-row select kernels keep a few KB of
-//               LDS per wave so many rows are in flight per CU.
-//   k_root_scan / k_root_fill  lay the groups out in tiles of 16 rows.
+//               selection is counted in its (KV head, root) group.  The
+//               per-row select kernels keep a few KB of LDS per wave so many
+//               rows are in flight per CU.
+//   k_root_scan / k_root_fill  lay the groups out in tiles of 16 rows; the
+//               fill also records where each selected root's children start
+//               in the row's mid candidate list.
 //   k_mid_gemm  one wave per tile: the tile's rows against the root's child
 //               span on bf16 (or fp32) MFMA 16x16 tiles; the span is read once
 //               per tile instead of once per row.  Scores land in each row's
 //               candidate slots of the workspace.
 //   k_mid_select   one wave per row (a workgroup per row for long candidate
 //               lists): Top-K_I over the row's mid scores.
-//   k_bucket_link  registers each selection in its (KV head, mid) bucket.
+//   k_bucket_link  registers each selection in its (KV head, mid) bucket,
+//               with where the mid's children start in the row's leaf
+//               candidate list.
 //   k_leaf_score   one wave per bucket: streams the mid's leaf span once (it is
 //               contiguous in the head-major layout) and writes the scores of
 //               every member row into that row's candidate slots.
@@ -95,8 +98,8 @@ __global__ __launch_bounds__(256) void k_root(StepArgs a, size_t wave_bytes, int
   constexpr int EPV = E::kEPV, LPK = D / EPV;
   extern __shared__ __align__(16) char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
-  const int blk = blockIdx.x * nwave + wave;
-  if (blk >= a.r.R) return;  // whole wave; waves never meet at a barrier
+  const int blk = a.blk0 + blockIdx.x * nwave + wave;
+  if (blk >= a.blk1) return;  // whole wave; waves never meet at a barrier
   const int MR = (int)a.t.count[0];
   const int K = a.K[0];
   RowWork W = carve_rowwork(smem + (size_t)wave * wave_bytes, K, 0, D, stage);
@@ -123,26 +126,13 @@ __global__ __launch_bounds__(256) void k_root(StepArgs a, size_t wave_bytes, int
                                       lane);
   int32_t* out = a.sel[0] + (int64_t)row * K;
   for (int i = lane; i < K; i += 64) out[i] = i < k ? W.out_node[i] : -1;
-  // group the row under each selected (head, root): rank in the group and the
-  // first mid-candidate slot of the root's children (children of the selected
-  // roots, in selection order, form the row's mid candidate list)
-  const int64_t* off0 = a.t.off[0];
-  int carry = 0;
-  for (int i0 = 0; i0 < K; i0 += 64) {
-    const int i = i0 + lane;
-    const int node = i < k ? W.out_node[i] : -1;
-    const int fan = node >= 0 ? (int)(off0[node + 1] - off0[node]) : 0;
-    const int incl = wave_incl_sum(fan);
-    if (i < K) {
-      // rank within the row's sub-counter (by token) of the group: spreading a
-      // group over kRootSub counters keeps the atomics on one address few
-      const int sub = (row / a.r.Hq) % kRootSub;
-      a.root_rank[(int64_t)row * K + i] =
-          node >= 0 ? atomicAdd(&a.root_cnt[(int64_t)sub * a.t.Hkv * MR + g * MR + node], 1) : -1;
-      a.root_base[(int64_t)row * K + i] = carry + incl - fan;
-    }
-    carry += __builtin_amdgcn_readlane(incl, 63);
-  }
+  // count the row in each selected (head, root) group, on the row's
+  // sub-counter (by token): spreading a group over kRootSub counters keeps
+  // the atomics on one address few.  Nothing waits for these atomics; the
+  // row's rank in the group is taken when k_root_fill places it.
+  const int sub = (row / a.r.Hq) % kRootSub;
+  for (int i = lane; i < k; i += 64)
+    atomicAdd(&a.root_cnt[(int64_t)sub * a.t.Hkv * MR + g * MR + W.out_node[i]], 1);
 }
 
 // Exclusive scan of the (head, root) group sizes in tiles of kRootTile rows:
@@ -150,15 +140,17 @@ __global__ __launch_bounds__(256) void k_root(StepArgs a, size_t wave_bytes, int
 __global__ __launch_bounds__(1024) void k_root_scan(StepArgs a) {
   __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nkeys = a.t.Hkv * (int)a.t.count[0];
+  const int MR = (int)a.t.count[0];
+  const int nall = a.t.Hkv * MR;                 // sub-counter stride
+  const int nkeys = (a.g1 - a.g0) * MR, kb = a.g0 * MR;  // the part's groups
   int carry = 0;
   for (int k0 = 0; k0 < nkeys; k0 += 1024) {
-    const int key = k0 + tid;
+    const int key = kb + k0 + tid;
     int tot = 0;
-    if (key < nkeys) {
+    if (k0 + tid < nkeys) {
       for (int sb = 0; sb < kRootSub; ++sb) {  // sub-counts -> first rank of each sub-counter
-        const int c = a.root_cnt[(int64_t)sb * nkeys + key];
-        a.root_cnt[(int64_t)sb * nkeys + key] = tot;
+        const int c = a.root_cnt[(int64_t)sb * nall + key];
+        a.root_cnt[(int64_t)sb * nall + key] = tot;
         tot += c;
       }
       a.root_tot[key] = tot;
@@ -173,7 +165,7 @@ __global__ __launch_bounds__(1024) void k_root_scan(StepArgs a) {
       total += wsum[w];
     }
     const int first = carry + woff + incl - pc;
-    if (key < nkeys) {
+    if (k0 + tid < nkeys) {
       a.root_tile_off[key] = first;
       for (int i = 0; i < pc; ++i) a.root_tile_key[first + i] = key;
     }
@@ -183,21 +175,49 @@ __global__ __launch_bounds__(1024) void k_root_scan(StepArgs a) {
   if (tid == 0) *a.root_ntiles = carry;
 }
 
-// Place every (row, selected root) at its group's tile rows.
-__global__ void k_root_fill(StepArgs a) {
-  const int K0 = a.K[0];
+// Place the selections e of lanes `ok` (one wave; s0 the start lane of each
+// lane's row, carry the fanouts of the row's selections before this part) in
+// their groups' tile rows: the rank comes from the row's sub-counter, which
+// k_root_scan turned into the sub-counter's first rank; the first
+// mid-candidate slot of the root's children is the sum of the fanouts of the
+// row's earlier selected roots (children of the selected roots, in selection
+// order, form the row's mid candidate list), an in-wave segmented scan.
+__device__ inline int fill_part(const StepArgs& a, bool ok, int64_t e, int row, int s0, int carry, int lane) {
   const int MR = (int)a.t.count[0];
-  const int64_t n = (int64_t)a.r.R * K0;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int node = a.sel[0][e];
-    if (node < 0) continue;
-    const int row = (int)(e / K0);
+  const int64_t* off0 = a.t.off[0];
+  const int node = ok ? a.sel[0][e] : -1;
+  const int fan = node >= 0 ? (int)(off0[node + 1] - off0[node]) : 0;
+  const int incl = wave_incl_sum(fan);
+  const int excl = incl - fan;
+  const int base = carry + excl - __shfl(excl, s0);
+  if (node >= 0) {
     const int key = ((row % a.r.Hq) / a.r.G) * MR + node;
     const int sub = (row / a.r.Hq) % kRootSub;
-    const int64_t nkeys = (int64_t)a.t.Hkv * MR;
-    const int64_t pos = (int64_t)a.root_tile_off[key] * kRootTile + a.root_cnt[sub * nkeys + key] + a.root_rank[e];
-    a.root_members[pos] = make_int2(row, a.root_base[e]);
+    const int rank = atomicAdd(&a.root_cnt[(int64_t)sub * a.t.Hkv * MR + key], 1);
+    a.root_members[(int64_t)a.root_tile_off[key] * kRootTile + rank] = make_int2(row, base);
+  }
+  return carry + __builtin_amdgcn_readlane(incl, 63);
+}
+
+// One wave per row-aligned chunk of the root selections.
+__global__ void k_root_fill(StepArgs a) {
+  const int K0 = a.K[0];
+  const int lane = threadIdx.x & 63;
+  const int wave = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  const int nwaves = (int)((gridDim.x * blockDim.x) >> 6);
+  const int nch = row_chunks(a.blk1 - a.blk0, K0);
+  for (int c = wave; c < nch; c += nwaves) {
+    if (K0 <= 64) {
+      const int rpc = 64 / K0, rr = lane / K0, blk = a.blk0 + c * rpc + rr;
+      const bool ok = rr < rpc && blk < a.blk1;
+      const int row = ok ? row_of_block(a.r, blk) : 0;
+      fill_part(a, ok, (int64_t)row * K0 + lane % K0, row, rr < rpc ? rr * K0 : lane, 0, lane);
+    } else {
+      const int row = row_of_block(a.r, a.blk0 + c);
+      int carry = 0;
+      for (int i0 = 0; i0 < K0; i0 += 64)
+        carry = fill_part(a, i0 + lane < K0, (int64_t)row * K0 + i0 + lane, row, 0, carry, lane);
+    }
   }
 }
 
@@ -299,17 +319,38 @@ __global__ __launch_bounds__(256) void k_mid_gemm(StepArgs a) {
 // ---------------------------------------------------------------------------
 // mid-level Top-K, one wave per row
 // ---------------------------------------------------------------------------
+// First parent of a select prologue, read by the caller before anything
+// else so that the parents' spans are on their way while the row's scores
+// and query arrive: parent gtid (< 64) of the row at level lev - 1, or -1.
+__device__ inline int first_parent(const StepArgs& a, int row, int lev, int gtid) {
+  const int Kp = a.K[lev - 1];
+  return gtid < Kp && gtid < 64 ? a.sel[lev - 1][(int64_t)row * Kp + gtid] : -1;
+}
+
 // Prologue of the mid/leaf select kernels (NT threads per row): query row
 // in LDS, its norm, the candidate list of level `lev` (children of the row's
-// level-1 selection).  Returns the candidate count.
+// level-1 selection; p0 from first_parent).  Returns the candidate count.
 template <class E, int D, int NT>
 __device__ inline int select_prologue(const StepArgs& a, const RowWork& W, int row, int lev, int& g,
-                                      double& qnorm, int gtid) {
+                                      double& qnorm, int gtid, int p0) {
+  constexpr int QPT = (D + NT - 1) / NT;
   int b, n, h;
   decode_row(a.r, row, b, n, h);
   g = h / a.r.G;
   const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes;
-  for (int t = gtid; t < D; t += NT) W.sel.qrow[t] = load_f32<E>(qp, t);
+  float qv[QPT];
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) qv[j] = gtid + j * NT < D ? load_f32<E>(qp, gtid + j * NT) : 0.f;
+  const int64_t* off = a.t.off[lev - 1];
+  int64_t first0 = 0;
+  int fan0 = 0;
+  if (p0 >= 0) {
+    first0 = off[p0];
+    fan0 = (int)(off[p0 + 1] - first0);
+  }
+#pragma unroll
+  for (int j = 0; j < QPT; ++j)
+    if (gtid + j * NT < D) W.sel.qrow[gtid + j * NT] = qv[j];
   group_sync<NT>();
   const int Kp = a.K[lev - 1];
   if (gtid < 64) {
@@ -317,7 +358,7 @@ __device__ inline int select_prologue(const StepArgs& a, const RowWork& W, int r
     for (int t = gtid; t < D; t += 64) qq = fmaf(W.sel.qrow[t], W.sel.qrow[t], qq);
     qq = wave_sum(qq);
     if (gtid == 0) W.sel.ctl[7] = __float_as_int((float)(sqrt((double)qq) * 1.0001));
-    build_candidates(a.sel[lev - 1] + (int64_t)row * Kp, Kp, a.t.off[lev - 1], gtid, W.pre, W.base);
+    build_candidates(a.sel[lev - 1] + (int64_t)row * Kp, Kp, off, gtid, W.pre, W.base, first0, fan0);
   }
   group_sync<NT>();
   qnorm = (double)__int_as_float(W.sel.ctl[7]);
@@ -345,39 +386,25 @@ template <class E, int D, int NT, int SPT>
 __device__ inline void mid_select_body(const StepArgs& a, size_t group_bytes) {
   extern __shared__ __align__(16) char smem[];
   const int groups = blockDim.x / NT, grp = threadIdx.x / NT, gtid = threadIdx.x % NT;
-  const int blk = blockIdx.x * groups + grp;
-  if (blk >= a.r.R) return;  // whole group (whole waves) leaves together
+  const int blk = a.blk0 + blockIdx.x * groups + grp;
+  if (blk >= a.blk1) return;  // whole group (whole waves) leaves together
   const int K1 = a.K[1];
   RowWork W = carve_rowwork(smem + (size_t)grp * group_bytes, K1, a.K[0], D, 0, NT);
   const int row = row_of_block(a.r, blk);
-  // the scores do not depend on the candidate list: load them first
+  const int p0 = first_parent(a, row, 1, gtid);
+  // the scores do not depend on the candidate list: load them next
   const auto sc = RowScores<NT, SPT>::make(a.mid_scores + (int64_t)row * a.c1max, (int)a.c1max, gtid);
   int g;
   double qnorm;
-  const int n1 = select_prologue<E, D, NT>(a, W, row, 1, g, qnorm, gtid);
+  const int n1 = select_prologue<E, D, NT>(a, W, row, 1, g, qnorm, gtid, p0);
   int64_t rsb;
   const char* kb = key_base(a.t, 1, g, rsb, E::kBytes);
   const int k1 = select_topk<E, D, NT>(sc, n1, K1,
                                        twice_err_bound<D>(qnorm, a.t.norm[a.t.Hkv + g]), a.r.scale,
                                        SlotMap{W.pre, W.base, a.K[0]}, KeyRows{kb, rsb}, W.sel,
                                        W.out_node, W.out_logit, gtid);
-  if (gtid >= 64) return;
-  const int lane = gtid;
   int32_t* o1 = a.sel[1] + (int64_t)row * K1;
-  int32_t* ob = a.mid_base + (int64_t)row * K1;
-  const int64_t* off1 = a.t.off[1];
-  int carry = 0;
-  for (int i0 = 0; i0 < K1; i0 += 64) {
-    const int i = i0 + lane;
-    const int node = i < k1 ? W.out_node[i] : -1;
-    const int fan = node >= 0 ? (int)(off1[node + 1] - off1[node]) : 0;
-    const int incl = wave_incl_sum(fan);
-    if (i < K1) {
-      o1[i] = node;
-      ob[i] = carry + incl - fan;  // first leaf-candidate slot of this mid in the row's list
-    }
-    carry += __builtin_amdgcn_readlane(incl, 63);
-  }
+  for (int i = gtid; i < K1; i += NT) o1[i] = i < k1 ? W.out_node[i] : -1;
 }
 
 // One wave per row (short candidate lists) or one workgroup per row; the
@@ -399,14 +426,25 @@ __global__ __launch_bounds__(256) void k_mid_select(StepArgs a, size_t gb) {
 // Each member's dot products are computed independently, so results do not
 // depend on the (atomic) member or bucket order.
 // ---------------------------------------------------------------------------
-__global__ void k_clear(StepArgs a, int64_t nkeys1, int64_t nkeys0) {
+__global__ void k_clear(StepArgs a) {
+  const int64_t MI = a.t.count[1], MR = a.t.count[0];
+  const int64_t nk1 = (a.g1 - a.g0) * MI, nk0 = (a.g1 - a.g0) * MR;  // the part's keys
+  const int64_t nall = (int64_t)a.t.Hkv * MR;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nkeys1; i += stride) {
-    a.bucket_cnt[i] = 0;
-    a.bucket_head[i] = -1;
+  if (a.g0 == 0 && a.g1 == a.t.Hkv) {  // all heads: the whole arrays, in order
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < (int64_t)a.bucket_q * 64; i += stride) {
+      a.bucket_cnt[i] = 0;
+      a.bucket_head[i] = -1;
+    }
+  } else {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nk1; i += stride) {
+      const int64_t bix = bucket_index(a, a.g0 * MI + i);
+      a.bucket_cnt[bix] = 0;
+      a.bucket_head[bix] = -1;
+    }
   }
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nkeys0 * kRootSub; i += stride)
-    a.root_cnt[i] = 0;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nk0 * kRootSub; i += stride)
+    a.root_cnt[(i / nk0) * nall + a.g0 * MR + i % nk0] = 0;
   if (blockIdx.x == 0 && threadIdx.x <= kDescSub) a.bucket_count[threadIdx.x] = 0;
 }
 
@@ -441,28 +479,54 @@ __device__ inline void register_in_bucket(const StepArgs& a, int64_t e, int row,
   }
 }
 
-// One thread per (row, selected mid), grid-stride in wave-uniform chunks of
-// 64 selections: their rank atomics are in flight together, and chunk c
-// appends its new descriptors to sub-list c mod kDescSub (one counter for all
-// chunks would serialise one atomic per chunk on one address).  A sub-list
-// receives at most ceil(ceil(n/64)/kDescSub) chunks, 64 entries each.
+// Link the selections e of lanes `ok` (one wave; row start lane `s0` of each
+// lane's row, `carry` the fanouts of the row's selections before this part):
+// the first leaf-candidate slot of selection e is the sum of the fanouts of
+// the row's earlier selections (children of the selected mids, in selection
+// order, form the row's leaf candidate list), an in-wave segmented scan.
+// Returns carry plus this part's fanouts (for parts holding one row).
+__device__ inline int link_part(const StepArgs& a, bool ok, int64_t e, int row, int s0, int sub, int carry,
+                                int lane) {
+  const int64_t* off1 = a.t.off[1];
+  const int mid = ok ? a.sel[1][e] : -1;
+  const int g = (row % a.r.Hq) / a.r.G;
+  const int64_t key = (int64_t)g * a.t.count[1] + (mid >= 0 ? mid : 0);
+  const int rank = mid >= 0 ? atomicAdd(&a.bucket_cnt[bucket_index(a, key)], 1) : -1;
+  const int64_t f0 = mid >= 0 ? off1[mid] : 0;
+  const int fan = mid >= 0 ? (int)(off1[mid + 1] - f0) : 0;
+  const int incl = wave_incl_sum(fan);
+  const int excl = incl - fan;
+  const int base = carry + excl - __shfl(excl, s0);
+  if (ok) a.mid_base[e] = base;
+  register_in_bucket(a, e, row, sub, g, key, rank, f0, fan, base, lane);
+  return carry + __builtin_amdgcn_readlane(incl, 63);
+}
+
+// One wave per chunk of whole rows' selections: floor(64 / K_I) rows when
+// K_I <= 64, else one row in ceil(K_I / 64) parts.  Chunk c appends its new
+// descriptors to sub-list c mod kDescSub (one counter for all chunks would
+// serialise one atomic per chunk on one address), so a sub-list receives at
+// most ceil(chunks / kDescSub) chunks of at most row_chunk_entries(K_I)
+// entries each.
 __global__ void k_bucket_link(StepArgs a) {
   const int K1 = a.K[1];
-  const int64_t n = (int64_t)a.r.R * K1;
-  const int64_t* off1 = a.t.off[1];
   const int lane = threadIdx.x & 63;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t e0 = blockIdx.x * (int64_t)blockDim.x + (threadIdx.x & ~63); e0 < n; e0 += stride) {
-    const int sub = (int)((e0 >> 6) % kDescSub);
-    const int64_t e = e0 + lane;
-    const int mid = e < n ? a.sel[1][e] : -1;
-    const int row = (int)(e / K1);
-    const int g = (row % a.r.Hq) / a.r.G;
-    const int64_t key = (int64_t)g * a.t.count[1] + (mid >= 0 ? mid : 0);
-    const int rank = mid >= 0 ? atomicAdd(&a.bucket_cnt[bucket_index(a, key)], 1) : -1;
-    const int64_t f0 = mid >= 0 ? off1[mid] : 0;
-    const int fan = mid >= 0 ? (int)(off1[mid + 1] - f0) : 0;
-    register_in_bucket(a, e, row, sub, g, key, rank, f0, fan, mid >= 0 ? a.mid_base[e] : 0, lane);
+  const int wave = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  const int nwaves = (int)((gridDim.x * blockDim.x) >> 6);
+  const int nch = row_chunks(a.blk1 - a.blk0, K1);
+  for (int c = wave; c < nch; c += nwaves) {
+    const int sub = c % kDescSub;
+    if (K1 <= 64) {
+      const int rpc = 64 / K1, rr = lane / K1, blk = a.blk0 + c * rpc + rr;
+      const bool ok = rr < rpc && blk < a.blk1;
+      const int row = ok ? row_of_block(a.r, blk) : 0;
+      link_part(a, ok, (int64_t)row * K1 + lane % K1, row, rr < rpc ? rr * K1 : lane, sub, 0, lane);
+    } else {
+      const int row = row_of_block(a.r, a.blk0 + c);
+      int carry = 0;
+      for (int i0 = 0; i0 < K1; i0 += 64)
+        carry = link_part(a, i0 + lane < K1, (int64_t)row * K1 + i0 + lane, row, 0, sub, carry, lane);
+    }
   }
 }
 
@@ -638,15 +702,16 @@ __device__ inline void leaf_select_body(const StepArgs& a, size_t group_bytes) {
   constexpr int DPL = D / 64;
   extern __shared__ __align__(16) char smem[];
   const int groups = blockDim.x / NT, grp = threadIdx.x / NT, gtid = threadIdx.x % NT;
-  const int blk = blockIdx.x * groups + grp;
-  if (blk >= a.r.R) return;
+  const int blk = a.blk0 + blockIdx.x * groups + grp;
+  if (blk >= a.blk1) return;
   const int K2 = a.K[2];
   RowWork W = carve_rowwork(smem + (size_t)grp * group_bytes, K2, a.K[1], D, 0, NT);
   const int row = row_of_block(a.r, blk);
+  const int p0 = first_parent(a, row, 2, gtid);
   const auto sc = RowScores<NT, SPT>::make(a.leaf_scores + (int64_t)row * a.c2max, (int)a.c2max, gtid);
   int g;
   double qnorm;
-  const int n2 = select_prologue<E, D, NT>(a, W, row, 2, g, qnorm, gtid);
+  const int n2 = select_prologue<E, D, NT>(a, W, row, 2, g, qnorm, gtid, p0);
   int64_t rsb;
   const char* kb = key_base(a.t, 2, g, rsb, E::kBytes);
   const int k2 = select_topk<E, D, NT>(sc, n2, K2,
@@ -758,14 +823,14 @@ __global__ __launch_bounds__(256) void k_leaf_select(StepArgs a, size_t gb) {
       int wpb, stage;                                                                                \
       size_t wb;                                                                                     \
       if (!row_launch_shape((Kc), (Kp), (a).t.d, 0, wpb, wb, stage)) return hipErrorInvalidValue;   \
-      const unsigned blocks = (unsigned)(((a).r.R + wpb - 1) / wpb);                                 \
+      const unsigned blocks = (unsigned)(((a).blk1 - (a).blk0 + wpb - 1) / wpb);                     \
       if (cap_ <= 64 * 8)                                                                            \
         HIKVP_DISPATCH_SEL((a).t.dtype, (a).t.d, KERNEL, 64, 8, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb); \
       else                                                                                           \
         HIKVP_DISPATCH_SEL((a).t.dtype, (a).t.d, KERNEL, 64, 16, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb); \
     } else {                                                                                         \
       const size_t gb = rowwork_bytes((Kc), (Kp), (a).t.d, 0, 256);                                  \
-      const dim3 grid((unsigned)(a).r.R);                                                            \
+      const dim3 grid((unsigned)((a).blk1 - (a).blk0));                                              \
       if (cap_ <= 256 * 8)                                                                           \
         HIKVP_DISPATCH_SEL((a).t.dtype, (a).t.d, KERNEL, 256, 8, grid, dim3(256), gb, s, a, gb);      \
       else if (cap_ <= 256 * 16)                                                                     \
@@ -789,31 +854,31 @@ static bool row_launch_shape(int K, int Kp, int D, int64_t cands, int& wpb, size
 }
 
 hipError_t launch_root(const StepArgs& a, hipStream_t s) {
-  if (a.r.R <= 0) return hipSuccess;
+  if (a.blk1 <= a.blk0) return hipSuccess;
   int wpb, stage;
   size_t wb;
   // root scores are produced in-kernel: keep them in LDS when they fit
   if (!row_launch_shape(a.K[0], 0, a.t.d, a.t.count[0], wpb, wb, stage, a.t.count[0] <= 2048))
     return hipErrorInvalidValue;
   if (!stage && a.t.count[0] > a.c1max) return hipErrorInvalidValue;  // spill buffer too small
-  const unsigned blocks = (unsigned)((a.r.R + wpb - 1) / wpb);
+  const unsigned blocks = (unsigned)((a.blk1 - a.blk0 + wpb - 1) / wpb);
   HIKVP_DISPATCH(a.t.dtype, a.t.d, k_root, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb, stage);
   return hipGetLastError();
 }
 
 hipError_t launch_root_groups(const StepArgs& a, hipStream_t s) {
-  if (a.r.R <= 0 || a.K[0] <= 0 || a.t.count[0] <= 0) return hipSuccess;
+  if (a.blk1 <= a.blk0 || a.K[0] <= 0 || a.t.count[0] <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_root_scan, dim3(1), dim3(1024), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int64_t blocks = ((int64_t)a.r.R * a.K[0] + 255) / 256;
+  int64_t blocks = ((int64_t)row_chunks(a.blk1 - a.blk0, a.K[0]) + 3) / 4;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(k_root_fill, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s) {
-  if (a.r.R <= 0 || a.t.count[0] <= 0 || a.K[0] <= 0) return hipSuccess;
+  if (a.blk1 <= a.blk0 || a.t.count[0] <= 0 || a.K[0] <= 0) return hipSuccess;
   int64_t blocks = (a.root_tiles_max + 3) / 4;
   if (blocks > 4096) blocks = 4096;
   HIKVP_DISPATCH(a.t.dtype, a.t.d, k_mid_gemm, dim3((unsigned)blocks), dim3(256), 0, s, a);
@@ -821,34 +886,34 @@ hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_mid_select(const StepArgs& a, hipStream_t s) {
-  if (a.r.R <= 0) return hipSuccess;
+  if (a.blk1 <= a.blk0) return hipSuccess;
   HIKVP_SELECT_LAUNCH(a, a.c1max, k_mid_select, a.K[1], a.K[0], s);
   return hipGetLastError();
 }
 
 hipError_t launch_clear(const StepArgs& a, hipStream_t s) {
-  if (a.r.R <= 0) return hipSuccess;
-  const int64_t nkeys1 = (int64_t)a.bucket_q * 64, nkeys0 = (int64_t)a.t.Hkv * a.t.count[0];
-  int64_t blocks = ((nkeys1 > nkeys0 ? nkeys1 : nkeys0) + 255) / 256;
+  if (a.blk1 <= a.blk0) return hipSuccess;
+  const int64_t nk1 = (a.g0 == 0 && a.g1 == a.t.Hkv) ? (int64_t)a.bucket_q * 64 : (int64_t)(a.g1 - a.g0) * a.t.count[1];
+  const int64_t nk0 = (int64_t)(a.g1 - a.g0) * a.t.count[0] * kRootSub;
+  int64_t blocks = ((nk1 > nk0 ? nk1 : nk0) + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(k_clear, dim3((unsigned)blocks), dim3(256), 0, s, a, nkeys1, nkeys0);
+  hipLaunchKernelGGL(k_clear, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_leaf_link(const StepArgs& a, hipStream_t s) {
-  if (a.r.R <= 0 || a.K[1] <= 0) return hipSuccess;
-  const int64_t n = (int64_t)a.r.R * a.K[1];
-  int64_t blocks = (n + 255) / 256;
+  if (a.blk1 <= a.blk0 || a.K[1] <= 0) return hipSuccess;
+  int64_t blocks = ((int64_t)row_chunks(a.blk1 - a.blk0, a.K[1]) + 3) / 4;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(k_bucket_link, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s) {
-  if (a.r.R <= 0 || a.K[1] <= 0) return hipSuccess;
-  // at most R * K_I distinct (head, mid) buckets
-  const int64_t nb_max = (int64_t)a.r.R * a.K[1];
+  if (a.blk1 <= a.blk0 || a.K[1] <= 0) return hipSuccess;
+  // at most rows * K_I distinct (head, mid) buckets
+  const int64_t nb_max = (int64_t)(a.blk1 - a.blk0) * a.K[1];
   int64_t blocks = (nb_max + 3) / 4;
   if (blocks > 2048) blocks = 2048;
   HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_score, dim3((unsigned)blocks), dim3(256), 0, s, a);
@@ -856,9 +921,9 @@ hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_leaf_overflow(const StepArgs& a, hipStream_t s) {
-  if (a.r.R <= 0 || a.K[1] <= 0) return hipSuccess;
-  // at most R * K_I / (kBucketSlots + 1) buckets overflow
-  const int64_t nb_max = (int64_t)a.r.R * a.K[1];
+  if (a.blk1 <= a.blk0 || a.K[1] <= 0) return hipSuccess;
+  // at most rows * K_I / (kBucketSlots + 1) buckets overflow
+  const int64_t nb_max = (int64_t)(a.blk1 - a.blk0) * a.K[1];
   int64_t blocks = (nb_max / (kBucketSlots + 1) + 4) / 4;
   if (blocks > 1024) blocks = 1024;
   HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_score_overflow, dim3((unsigned)blocks), dim3(256), 0, s, a);
@@ -866,7 +931,7 @@ hipError_t launch_leaf_overflow(const StepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_leaf_select(const StepArgs& a, hipStream_t s) {
-  if (a.r.R <= 0) return hipSuccess;
+  if (a.blk1 <= a.blk0) return hipSuccess;
   HIKVP_SELECT_LAUNCH(a, a.c2max, k_leaf_select, a.K[2], a.K[1], s);
   return hipGetLastError();
 }

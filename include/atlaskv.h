@@ -45,17 +45,22 @@
  *   - atlaskv_hikvp_attend* allocate nothing: scratch memory is the caller's
  *     workspace (size from atlaskv_hikvp_workspace_size).  Only
  *     atlaskv_build_tree_view allocates (a few bytes of device memory per KV
- *     head, one stream and two events, freed by atlaskv_destroy_tree_view) and
- *     synchronises its stream;
+ *     head, two streams and four events, freed by atlaskv_destroy_tree_view)
+ *     and synchronises its stream;
  *   - attend calls are asynchronous on their stream; device faults surface at
  *     the caller's next synchronisation.  Calls on different streams need
  *     separate workspaces; calls sharing a workspace must be stream-ordered.
  *     Unless phase events are requested, the causal sequence half runs on a
  *     second stream that the view owns (default priority), forked from the
  *     call's stream by an event before the KG kernels and joined back before
- *     the merge, so it overlaps the KG half; the call's stream still orders
- *     everything the call reads and writes.  With phase events the halves run
- *     one after the other on the call's stream (same results, bit for bit).
+ *     the merge, so it overlaps the KG half.  With 4096 query rows or more
+ *     (B*N*Hq, or groups for shared selections) and two KV heads or more, the
+ *     KG descent itself runs in two concurrent parts (the two halves of the KV
+ *     heads, which share no index structure), the second on the view's other
+ *     stream, forked and joined the same way.  The call's stream still orders
+ *     everything the call reads and writes.  With phase events the halves and
+ *     parts run one after the other on the call's stream (same results, bit
+ *     for bit).
  *
  * Errors: every entry point returns an atlaskv_status.  Argument errors are
  * detected on the host before anything is enqueued, so a failed call writes

@@ -192,6 +192,35 @@ def test_overlapped_and_serial_sequence_half_agree(N, S_kv):
     assert np.isfinite(outs[0][0]).all()
 
 
+@pytest.mark.parametrize("Hq,Hkv,N", [(32, 8, 64), (12, 3, 192)])
+def test_split_descent_matches_serial_and_oracle(Hq, Hkv, N):
+    """With 4096 rows or more the KG descent runs as two concurrent parts (the
+    halves of the KV heads, uneven for Hkv = 3) on two streams; with phase
+    events it runs as one part.  Selections, KG log-sum-exps and outputs agree
+    bit for bit, and sampled rows match the oracle."""
+    case = _small(seed=29, dtype="bf16", B=2, N=N, S_kv=N + 7, Hq=Hq, Hkv=Hkv, M_R=61, M_I=907, M=20011,
+                  K=(6, 9, 24))
+    assert case.rows >= 4096
+    tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
+    ws = atlaskv.alloc_workspace(tree, case.q, case.seq_k, case.K)
+    runs = []
+    for timed in (False, True, False):
+        out = torch.full(case.q.shape, float("nan"), dtype=torch.float32, device=DEV)
+        lse = torch.full((case.rows,), 7.0, dtype=torch.float32, device=DEV)
+        sels = [torch.full((case.rows, k), -7, dtype=torch.int32, device=DEV) for k in case.K]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(atlaskv.phase_names()) + 1)] if timed else None
+        say(f"split descent: Hq={Hq} Hkv={Hkv} rows={case.rows} timed={timed}")
+        atlaskv.hikvp_attend_ex(case.q, tree, case.seq_k, case.seq_v, case.K, out, workspace=ws, lse_kg=lse,
+                                sel_root=sels[0], sel_mid=sels[1], sel_leaf=sels[2], phase_events=evs)
+        torch.cuda.synchronize()
+        runs.append([out.cpu().numpy(), lse.cpu().numpy()] + [x.cpu().numpy() for x in sels])
+    tree.close()
+    for r in runs[1:]:
+        for a, b in zip(r, runs[0]):
+            assert np.array_equal(a, b)
+    _check(case, rows=parity.sample_rows(case, 96, seed=31), two_phase=True)
+
+
 def test_empty_batch_writes_nothing():
     case = _small(seed=15, N=1, S_kv=4)
     tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
