@@ -234,6 +234,178 @@ __global__ __launch_bounds__(64) void k_seq_decode(SeqArgs a) {
   }
 }
 
+// Decode on the matrix cores (bf16): the same work items and V layout as
+// k_seq_decode, with the scores S^T = K Q^T of a 16-key chunk on
+// v_mfma_f32_16x16x32_bf16: the chunk's keys are the M side (lane l feeds key
+// l%16 with dims 32m + 8(l/16) .. +8, m < D/32), the group's heads the N side
+// (head column l%16, zero beyond the group).  Lane (r, c) then holds the
+// scores of keys 4r .. 4r+3 for head c, which is also the key set of its V
+// rows, so the online softmax runs in place (in-lane over four keys, across
+// the four 16-lane rows by two xor shuffles) and each lane takes the
+// probability of its keys under head hh, and the head's rescale factor, from
+// lane (r, hh) by a DPP row broadcast; P V accumulates on VALU.
+template <int D>
+__device__ inline float row_bcast(float x, int hh) {
+  switch (hh) {  // DPP row_newbcast:hh (lane hh of each 16-lane row)
+    case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150, 0xf, 0xf, false));
+    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x151, 0xf, 0xf, false));
+    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x152, 0xf, 0xf, false));
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x153, 0xf, 0xf, false));
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void k_seq_decode_mfma(SeqArgs a) {
+  typedef __bf16 Bf16x8 __attribute__((ext_vector_type(8)));
+  typedef float Float4 __attribute__((ext_vector_type(4)));
+  constexpr int EPL = D / 16, HG = 4, CK = 16, KM = D / 32;
+  const int lane = threadIdx.x, r = lane >> 4, c = lane & 15;
+  const int G = a.r.G, HGP = (G + HG - 1) / HG;
+  int t = blockIdx.x;
+  const int hgp = t % HGP; t /= HGP;
+  const int g = t % a.Hkv; t /= a.Hkv;
+  const int n = t % a.r.N, b = t / a.r.N;
+  const int nh = (G - hgp * HG) < HG ? (G - hgp * HG) : HG;   // heads of this wave
+  const int split = blockIdx.y, nsplit = gridDim.y;
+  const int vis = a.k ? a.S - a.r.N + n + 1 : 0;
+  const int k0 = split * a.split_len;
+  const int k1 = (k0 + a.split_len) < vis ? (k0 + a.split_len) : vis;
+  const float scale = (float)a.r.scale;
+
+  // B operand: head column c of the group, dims 32m + 8r .. +8 (zero past the group)
+  uint4 qb[KM];
+#pragma unroll
+  for (int m = 0; m < KM; ++m) qb[m] = make_uint4(0, 0, 0, 0);
+  if (c < nh) {
+    const char* qp = (const char*)a.r.q + q_off(a.r.qs, b, n, g * G + hgp * HG + c) * 2;
+#pragma unroll
+    for (int m = 0; m < KM; ++m) qb[m] = *(const uint4*)(qp + (32 * m + 8 * r) * 2);
+  }
+  float m_run = -INFINITY, l_run = 0.f;   // head c's softmax state (same in all four rows)
+  float acc[HG][EPL];
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
+  if (k0 < k1) {
+    const char* kb = (const char*)a.k + ((int64_t)b * a.ks[0] + (int64_t)g * a.ks[2]) * 2;
+    const char* vb = (const char*)a.v + ((int64_t)b * a.vs[0] + (int64_t)g * a.vs[2] + c * EPL) * 2;
+    const int64_t kstep = a.ks[1] * 2, vstep = a.vs[1] * 2;
+    // chunk loads are issued one chunk ahead (keys past the range re-read the
+    // last key and are masked): K in the MFMA layout, V rows c0 + 4r + i.  K
+    // is single-buffered: the next chunk's keys load once the scores of this
+    // one are on the matrix cores, while the softmax and P V run.
+    uint4 kn[KM];
+    RawElems<BF16, EPL> vn[CK / 4];
+    auto load_k = [&](int c0) {
+      const char* kp = kb + (int64_t)min(c0 + c, k1 - 1) * kstep + (8 * r) * 2;
+#pragma unroll
+      for (int m = 0; m < KM; ++m) kn[m] = *(const uint4*)(kp + 64 * m);
+    };
+    auto load_v = [&](int c0) {
+#pragma unroll
+      for (int i = 0; i < CK / 4; ++i) vn[i].load(vb + (int64_t)min(c0 + 4 * r + i, k1 - 1) * vstep);
+    };
+    load_k(k0);
+    load_v(k0);
+    for (int c0 = k0; c0 < k1; c0 += CK) {
+      RawElems<BF16, EPL> vf[CK / 4];
+#pragma unroll
+      for (int i = 0; i < CK / 4; ++i) vf[i] = vn[i];
+      Float4 sv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < KM; ++m)
+        sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(Bf16x8, kn[m]), __builtin_bit_cast(Bf16x8, qb[m]),
+                                                    sv, 0, 0, 0);
+      if (c0 + CK < k1) {
+        load_k(c0 + CK);
+        load_v(c0 + CK);
+      }
+      float sc[4], mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sc[i] = (c0 + 4 * r + i < k1) ? sv[i] * scale : -INFINITY;
+        mx = fmaxf(mx, sc[i]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m_run, mx);   // finite: key c0 is in range
+      const float alpha = __expf(m_run - mn);
+      float p[4], ls = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __expf(sc[i] - mn);
+        ls += p[i];
+      }
+      ls += __shfl_xor(ls, 16);
+      ls += __shfl_xor(ls, 32);
+      l_run = l_run * alpha + ls;
+      m_run = mn;
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        const float al = row_bcast<D>(alpha, hh);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[hh][e] *= al;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pw = row_bcast<D>(p[i], hh);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(pw, vf[i][e], acc[hh][e]);
+        }
+      }
+    }
+  }
+  // sum the four rows' partial weighted values (keys 4r .. 4r+3 of each chunk)
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float v = acc[hh][e];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      acc[hh][e] = v;
+    }
+  float m[HG], l[HG];
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh) {
+    m[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_run), hh));
+    l[hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_run), hh));
+  }
+  if (r != 0) return;
+  for (int hh = 0; hh < nh; ++hh) {
+    const int h = g * G + hgp * HG + hh;
+    const int row = (b * a.r.N + n) * a.r.Hq + h;
+    if (a.part) {  // partial (acc, m, l) for k_seq_combine
+      float* part = a.part + ((int64_t)row * nsplit + split) * (D + 2);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) part[c * EPL + e] = acc[hh][e];
+      if (c == 0) {
+        part[D] = l[hh] > 0.f ? m[hh] : -INFINITY;
+        part[D + 1] = l[hh];
+      }
+      continue;
+    }
+    const bool has = l[hh] > 0.f;
+    const float lse_seq = has ? m[hh] + logf(l[hh]) : -INFINITY;
+    const float lkg = a.lse_kg[row];
+    float lam;
+    if (lkg == -INFINITY) lam = 0.f;
+    else if (!has) lam = 1.f;
+    else lam = 1.f / (1.f + __expf(lse_seq - lkg));
+    const float inv = has ? 1.f / l[hh] : 0.f;
+    const float* okg = a.o_kg + (int64_t)row * D;
+    const int64_t ob = q_off(a.os, b, n, h);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int dim = c * EPL + e;
+      const float o = lam * okg[dim] + (1.f - lam) * (acc[hh][e] * inv);
+      if (a.out_dtype == kDtypeBF16) ((uint16_t*)a.out)[ob + dim] = f32_to_bf16_rne(o);
+      else ((float*)a.out)[ob + dim] = o;
+    }
+    if (a.lse_seq_out && c == 0) a.lse_seq_out[row] = lse_seq;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Prefill: flash attention on MFMA.  One workgroup per (b, KV head, 16-token
 // tile); one wave per query head of the group.  Per 16-key tile: S = Q K^T on
@@ -618,6 +790,11 @@ hipError_t launch_seq_attend(const SeqArgs& a, hipStream_t s) {
   }
   // decode: one wave per (b, n, KV head, group of 4 query heads [, key split])
   const unsigned blocks = (unsigned)(a.r.B * a.r.N * a.Hkv * ((a.r.G + 3) / 4));
+  if (a.dtype == kDtypeBF16) {
+    if (a.d == 128) hipLaunchKernelGGL(k_seq_decode_mfma<128>, dim3(blocks, (unsigned)nsplit), dim3(64), 0, s, a);
+    else hipLaunchKernelGGL(k_seq_decode_mfma<64>, dim3(blocks, (unsigned)nsplit), dim3(64), 0, s, a);
+    return hipGetLastError();
+  }
   HIKVP_DISPATCH(a.dtype, a.d, k_seq_decode, dim3(blocks, (unsigned)nsplit), dim3(64), 0, s, a);
   return hipGetLastError();
 }
