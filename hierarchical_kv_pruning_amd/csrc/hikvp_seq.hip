@@ -756,9 +756,11 @@ int seq_splits(int B, int N, int Hkv, int G, int S, int dtype) {
   // (b, 16-token tile, KV head) for the flash prefill
   const int64_t items = flash ? (int64_t)B * ((N + 15) / 16) * Hkv : (int64_t)B * N * Hkv;
   if (items <= 0 || S <= 0) return 1;
-  // prefill: enough workgroups to fill the chip; decode: about one round of
-  // resident waves (3 per SIMD), so every wave streams one long key range
-  const int64_t target = flash ? 1024 : 3072;
+  // prefill: enough workgroups to fill the chip; decode: about one wave per
+  // SIMD, each streaming one long key range.  More decode waves measured
+  // slower alone and much slower beside the KG descent, whose kernels then
+  // find no registers free on the SIMDs the decode waves hold.
+  const int64_t target = flash ? 1024 : 1024;
   const int64_t min_keys = flash ? 64 : 128;    // keys per split at least
   int64_t want = (target + items - 1) / items;
   const int64_t maxs = (S + min_keys - 1) / min_keys;
