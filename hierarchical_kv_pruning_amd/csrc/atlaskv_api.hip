@@ -529,11 +529,12 @@ struct PhaseMarks {
 
 // Sequence half (背景知识与设计原则 › 自注意力层机制) and the λ merge with the
 // KG half held in o_kg / lse_kg.  The causal attention does not depend on the
-// KG half, so unless phase timing is requested it runs concurrently: it is
-// enqueued on the view's aux stream, forked from the call's stream before the
-// KG kernels, writes (o, m, l) partials, and the call's stream waits for it
-// before k_seq_combine merges both halves.  Serially, two phases (attention,
-// split combine) run after the KG half, through the same partials and merge.
+// KG half, so for decode (query blocks under 16 tokens) and unless phase
+// timing is requested it runs concurrently: it is enqueued on the view's aux
+// stream, forked from the call's stream before the KG kernels, writes
+// (o, m, l) partials, and the call's stream waits for it before
+// k_seq_combine merges both halves.  Otherwise two phases (attention, split
+// combine) run after the KG half, through the same partials and merge.
 struct SeqHalf {
   SeqArgs sa;
   bool overlap;
@@ -564,7 +565,12 @@ SeqHalf seq_prepare(const Plan& p, const RowsDev& rows, int Hkv, int d, int dtyp
   sa.out_dtype = out->dtype;
   sa.lse_seq_out = opts ? opts->lse_seq : nullptr;
   sa.nsplit = p.nsplit;
-  h.overlap = seq_k && v->aux && !(opts && opts->phase_events && opts->n_phase_events > 0);
+  // Overlap only the decode kernels (query blocks under 16 tokens): one light
+  // HBM-bound wave per SIMD that the descent's kernels run beside.  The
+  // prefill kernels hold most of a SIMD's registers and LDS per wave, and
+  // beside them the descent's kernels measured slower than running the
+  // prefill attention after the descent.
+  h.overlap = seq_k && v->aux && p.N < 16 && !(opts && opts->phase_events && opts->n_phase_events > 0);
   // with a sequence the merge is always k_seq_combine's, so the serial and
   // the overlapped order produce the same bits
   sa.part = seq_k ? (float*)(ws + p.off_part) : nullptr;

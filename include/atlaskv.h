@@ -50,10 +50,11 @@
  *   - attend calls are asynchronous on their stream; device faults surface at
  *     the caller's next synchronisation.  Calls on different streams need
  *     separate workspaces; calls sharing a workspace must be stream-ordered.
- *     Unless phase events are requested, the causal sequence half runs on a
- *     second stream that the view owns (default priority), forked from the
- *     call's stream by an event before the KG kernels and joined back before
- *     the merge, so it overlaps the KG half.  With 4096 query rows or more
+ *     For query blocks under 16 tokens (decode) and unless phase events are
+ *     requested, the causal sequence half runs on a second stream that the
+ *     view owns (default priority), forked from the call's stream by an
+ *     event before the KG kernels and joined back before the merge, so it
+ *     overlaps the KG half; longer query blocks run it after the KG half.  With 4096 query rows or more
  *     (B*N*Hq, or groups for shared selections) and two KV heads or more, the
  *     KG descent itself runs in two concurrent parts (the two halves of the KV
  *     heads, which share no index structure), the second on the view's other

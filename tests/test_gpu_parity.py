@@ -171,9 +171,10 @@ def test_deterministic_with_overflowing_buckets():
 
 @pytest.mark.parametrize("N,S_kv", [(33, 45), (1, 300)])
 def test_overlapped_and_serial_sequence_half_agree(N, S_kv):
-    """Without phase events the sequence half runs on the view's second stream
-    beside the KG half and k_seq_combine merges; with phase events it runs
-    after the KG half.  Both write the same bits (prefill and decode)."""
+    """Without phase events a decode block's sequence half runs on the view's
+    second stream beside the KG half and k_seq_combine merges; with phase
+    events (and for prefill blocks) it runs after the KG half.  Both write the
+    same bits."""
     case = _small(seed=23, dtype="bf16", B=2, N=N, S_kv=S_kv, Hq=8, Hkv=2)
     tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
     ws = atlaskv.alloc_workspace(tree, case.q, case.seq_k, case.K)
