@@ -222,6 +222,16 @@ def test_split_descent_matches_serial_and_oracle(Hq, Hkv, N):
     _check(case, rows=parity.sample_rows(case, 96, seed=31), two_phase=True)
 
 
+@pytest.mark.parametrize("K", [(0, 4, 4), (4, 0, 4), (4, 4, 0), (61, 256, 256), (1, 1, 1)])
+def test_split_descent_k_edges(K):
+    """The two-part descent (4096 rows, two KV heads) with empty levels, K
+    above the candidate counts (buckets far past 32 members) and K = 1."""
+    case = _small(seed=37, dtype="bf16", B=2, N=128, S_kv=131, Hq=16, Hkv=2, M_R=61, M_I=907, M=9001,
+                  K=(6, 9, 24))
+    assert case.rows >= 4096
+    _check(case, rows=parity.sample_rows(case, 64, seed=41), two_phase=True, K=K)
+
+
 def test_empty_batch_writes_nothing():
     case = _small(seed=15, N=1, S_kv=4)
     tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
