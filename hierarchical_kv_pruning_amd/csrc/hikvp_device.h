@@ -307,6 +307,8 @@ __device__ inline uint4 load_nt(const void* p) {
 __device__ inline void store4u(float* p, float x, float y, float z, float w) {
   *(Float4U*)p = Float4U{x, y, z, w};
 }
+struct __attribute__((packed, aligned(4))) Float2U { float x, y; };
+__device__ inline void store2u(float* p, float x, float y) { *(Float2U*)p = Float2U{x, y}; }
 
 // Sum the two half blocks of a half-split tile.  Lanes with (l&15) < 8 and
 // l < 32 then hold dot(row item 4*(l>>4)+v, column item l&7) in element v;

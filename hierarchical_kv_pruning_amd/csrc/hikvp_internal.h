@@ -10,7 +10,7 @@ constexpr int kMaxK = 256;        // largest Top-K per level
 constexpr int kMaxD = 128;        // largest head dim
 constexpr int kBucketSlots = 32;  // members of a (head, mid) bucket stored without a list walk
 constexpr int kJunkSlots = 1024;  // per-wave sinks for masked-off score stores
-constexpr int kRootTile = 16;     // member rows per mid-GEMM work item
+constexpr int kRootTile = 32;     // member rows per mid-GEMM work item (two 16-row MFMA halves)
 constexpr int kRootSub = 16;      // counters per (head, root) group, picked by token
 constexpr int kDescSub = 64;      // bucket descriptor sub-lists, picked by link chunk
 constexpr int kMaxParts = 2;      // descent parts (KV-head ranges run concurrently)

@@ -12,7 +12,7 @@
 //               selection is counted in its (KV head, root) group.  The
 //               per-row select kernels keep a few KB of LDS per wave so many
 //               rows are in flight per CU.
-//   k_root_scan / k_root_fill  lay the groups out in tiles of 16 rows; the
+//   k_root_scan / k_root_fill  lay the groups out in tiles of 32 rows; the
 //               fill also records where each selected root's children start
 //               in the row's mid candidate list.
 //   k_mid_gemm  one wave per tile: the tile's rows against the root's child
@@ -222,14 +222,18 @@ __global__ void k_root_fill(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// mid level: one wave per tile of kRootTile rows of a (head, root) group.  The
-// rows are the M side and the root's children the N side of 16x16 MFMA tiles,
-// so the child span is read once per tile (from L2 after the group's first).
+// mid level: one wave per tile of kRootTile (32) rows of a (head, root)
+// group, as two 16-row halves.  The rows are the M side and the root's
+// children the N side of 16x16 MFMA tiles; each child fragment loaded serves
+// both halves, so the child span is read once per 32 rows (from L2 after the
+// group's first tile).
 // ---------------------------------------------------------------------------
 template <class E, int D>
 __global__ __launch_bounds__(256) void k_mid_gemm(StepArgs a) {
   constexpr int KCH = D * E::kBytes / 64;  // 16-byte pieces per lane per row
-  constexpr int TU = 4;                    // child tiles per round = consecutive children per lane
+  constexpr int TU = 2;                    // child tiles per round = consecutive children per lane
+  constexpr int HR = kRootTile / 16;       // 16-row halves per tile
+  static_assert(kRootTile == 32, "two 16-row halves per tile");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
   const int quad = lane >> 4, col = lane & 15;
   float* const junk = a.junk + ((blockIdx.x * nwave + wave) % kJunkSlots) * 16;
@@ -244,37 +248,43 @@ __global__ __launch_bounds__(256) void k_mid_gemm(StepArgs a) {
     const int64_t first = off0[j];
     const int F = (int)(off0[j + 1] - first);
     const int m0 = (t - toff) * kRootTile;     // first member of the tile
-    const int mi = m0 + col;
-    const int2 mem = mi < cnt ? a.root_members[(int64_t)toff * kRootTile + mi] : make_int2(-1, 0);
-    uint4 afr[KCH];
-    if (mi < cnt) {
-      int b, n, h;
-      decode_row(a.r, mem.x, b, n, h);
-      const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes;
+    const bool two = m0 + 16 < cnt;            // wave-uniform: the second half has members
+    uint4 afr[HR][KCH];
+    float* dst[HR][4];
 #pragma unroll
-      for (int m = 0; m < KCH; ++m) afr[m] = *(const uint4*)(qp + m * 64 + quad * 16);
-    } else {
+    for (int hh = 0; hh < HR; ++hh) {
+      const int mi = m0 + 16 * hh + col;
+      const int2 mem = mi < cnt ? a.root_members[(int64_t)toff * kRootTile + mi] : make_int2(-1, 0);
+      if (mi < cnt) {
+        int b, n, h;
+        decode_row(a.r, mem.x, b, n, h);
+        const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes;
 #pragma unroll
-      for (int m = 0; m < KCH; ++m) afr[m] = make_uint4(0, 0, 0, 0);
+        for (int m = 0; m < KCH; ++m) afr[hh][m] = *(const uint4*)(qp + m * 64 + quad * 16);
+      } else {
+#pragma unroll
+        for (int m = 0; m < KCH; ++m) afr[hh][m] = make_uint4(0, 0, 0, 0);
+      }
+      // Rounds of TU child tiles; in tile u, column col is child c0 + col*TU
+      // + u, so a lane ends the round with TU consecutive scores of each of
+      // its 4 rows (half rows 4*quad + v), written with one 8-byte store.
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int ms = 4 * quad + v;
+        const int srow = __shfl(mem.x, ms), sbase = __shfl(mem.y, ms);
+        dst[hh][v] = m0 + 16 * hh + ms < cnt ? a.mid_scores + (int64_t)srow * a.c1max + sbase + col * TU : nullptr;
+      }
     }
-    // Rounds of TU child tiles; in tile u of a round, column col is child
-    // c0 + col*TU + u, so a lane ends the round with TU consecutive scores of
-    // each of its 4 rows (tile rows 4*quad + v), written with one 16-byte
-    // store.  Loads and stores are unconditional (clamped child, junk slot)
-    // and a round's stores follow the next round's loads, so the wait for the
-    // loads never covers the stores.
-    float* dst[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int ms = 4 * quad + v;
-      const int srow = __shfl(mem.x, ms), sbase = __shfl(mem.y, ms);
-      dst[v] = m0 + ms < cnt ? a.mid_scores + (int64_t)srow * a.c1max + sbase + col * TU : nullptr;
-    }
+    // Loads and stores are unconditional (clamped child, junk slot) and a
+    // round's stores follow the next round's loads, so the wait for the loads
+    // never covers the stores.
     int64_t rsb;
     const char* kb = key_base(a.t, 1, g, rsb, E::kBytes) + first * rsb + quad * 16;
-    float4_t prev[TU];
+    float4_t prev[HR][TU];
 #pragma unroll
-    for (int u = 0; u < TU; ++u) prev[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int hh = 0; hh < HR; ++hh)
+#pragma unroll
+      for (int u = 0; u < TU; ++u) prev[hh][u] = float4_t{0.f, 0.f, 0.f, 0.f};
     int pc0 = -1;
     auto load_round = [&](int c0, uint4 (&bfr)[TU][KCH]) {
 #pragma unroll
@@ -286,30 +296,40 @@ __global__ __launch_bounds__(256) void k_mid_gemm(StepArgs a) {
     };
     auto store_full = [&]() {
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        store4u((pc0 >= 0 && dst[v]) ? dst[v] + pc0 : junk, prev[0][v], prev[1][v], prev[2][v], prev[3][v]);
+      for (int hh = 0; hh < HR; ++hh)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          store2u((pc0 >= 0 && dst[hh][v]) ? dst[hh][v] + pc0 : junk, prev[hh][0][v], prev[hh][1][v]);
+    };
+    auto compute = [&](const uint4 (&bfr)[TU][KCH]) {
+#pragma unroll
+      for (int u = 0; u < TU; ++u) prev[0][u] = tile_dot<E, KCH>(afr[0], bfr[u]);
+      if (two) {
+#pragma unroll
+        for (int u = 0; u < TU; ++u) prev[1][u] = tile_dot<E, KCH>(afr[1], bfr[u]);
+      }
     };
     int c0 = 0;
     for (; c0 + 16 * TU <= F; c0 += 16 * TU) {
       uint4 bfr[TU][KCH];
       load_round(c0, bfr);
       store_full();
-#pragma unroll
-      for (int u = 0; u < TU; ++u) prev[u] = tile_dot<E, KCH>(afr, bfr[u]);
+      compute(bfr);
       pc0 = c0;
     }
     if (c0 < F) {  // last, partial round
       uint4 bfr[TU][KCH];
       load_round(c0, bfr);
       store_full();
-#pragma unroll
-      for (int u = 0; u < TU; ++u) prev[u] = tile_dot<E, KCH>(afr, bfr[u]);
+      compute(bfr);
       const int cl = c0 + col * TU;
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+      for (int hh = 0; hh < HR; ++hh)
 #pragma unroll
-        for (int u = 0; u < TU; ++u)
-          if (dst[v] && cl + u < F) dst[v][c0 + u] = prev[u][v];
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int u = 0; u < TU; ++u)
+            if (dst[hh][v] && cl + u < F) dst[hh][v][c0 + u] = prev[hh][u][v];
     } else {
       store_full();
     }
