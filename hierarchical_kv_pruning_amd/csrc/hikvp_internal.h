@@ -21,9 +21,10 @@ constexpr int kDtypeF32 = 0;
 // K <= 64, else one row each; and the most selections one chunk holds.
 // Parts of a split descent: as many KV-head ranges as keep kPartRows rows or
 // more each (at most kMaxParts, at most one per head).  Two concurrent parts
-// measured faster than one at 16384 rows and no slower at 4096; more parts
-// (more streams) measured slower.
-constexpr int64_t kPartRows = 2048;
+// measured faster than one at 16384 rows (0.588 -> 0.542 ms) and much slower
+// at 4096 rows with a small tree (0.094 -> 0.152 ms: the leaf stream is too
+// short to hide the other part's work); more parts measured slower.
+constexpr int64_t kPartRows = 8192;
 inline int descent_parts(int Hkv, int64_t rows) {
   int64_t n = rows / kPartRows;
   if (n > kMaxParts) n = kMaxParts;

@@ -54,11 +54,12 @@
  *     requested, the causal sequence half runs on a second stream that the
  *     view owns (default priority), forked from the call's stream by an
  *     event before the KG kernels and joined back before the merge, so it
- *     overlaps the KG half; longer query blocks run it after the KG half.  With 4096 query rows or more
- *     (B*N*Hq, or groups for shared selections) and two KV heads or more, the
- *     KG descent itself runs in two concurrent parts (the two halves of the KV
- *     heads, which share no index structure), the second on the view's other
- *     stream, forked and joined the same way.  The call's stream still orders
+ *     overlaps the KG half; longer query blocks run it after the KG half.
+ *     With 16384 query rows or more (B*N*Hq, or groups for shared
+ *     selections) and two KV heads or more, the KG descent itself runs in two
+ *     concurrent parts (the two halves of the KV heads, which share no index
+ *     structure), the second on the view's other stream, forked and joined
+ *     the same way.  The call's stream still orders
  *     everything the call reads and writes.  With phase events the halves and
  *     parts run one after the other on the call's stream (same results, bit
  *     for bit).

@@ -193,15 +193,15 @@ def test_overlapped_and_serial_sequence_half_agree(N, S_kv):
     assert np.isfinite(outs[0][0]).all()
 
 
-@pytest.mark.parametrize("Hq,Hkv,N", [(32, 8, 64), (12, 3, 192)])
+@pytest.mark.parametrize("Hq,Hkv,N", [(32, 8, 256), (12, 3, 683)])
 def test_split_descent_matches_serial_and_oracle(Hq, Hkv, N):
-    """With 4096 rows or more the KG descent runs as two concurrent parts (the
+    """With 16384 rows or more the KG descent runs as two concurrent parts (the
     halves of the KV heads, uneven for Hkv = 3) on two streams; with phase
     events it runs as one part.  Selections, KG log-sum-exps and outputs agree
     bit for bit, and sampled rows match the oracle."""
     case = _small(seed=29, dtype="bf16", B=2, N=N, S_kv=N + 7, Hq=Hq, Hkv=Hkv, M_R=61, M_I=907, M=20011,
                   K=(6, 9, 24))
-    assert case.rows >= 4096
+    assert case.rows >= 16384
     tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
     ws = atlaskv.alloc_workspace(tree, case.q, case.seq_k, case.K)
     runs = []
@@ -219,17 +219,19 @@ def test_split_descent_matches_serial_and_oracle(Hq, Hkv, N):
     for r in runs[1:]:
         for a, b in zip(r, runs[0]):
             assert np.array_equal(a, b)
-    _check(case, rows=parity.sample_rows(case, 96, seed=31), two_phase=True)
+    # fp32 output: with N = 256+ the early tokens' outputs reach ~12x the RMS,
+    # where a bf16 output's own rounding (2^-9 of the value) exceeds 2e-2 x RMS
+    _check(case, rows=parity.sample_rows(case, 96, seed=31), two_phase=True, out_dtype=torch.float32)
 
 
 @pytest.mark.parametrize("K", [(0, 4, 4), (4, 0, 4), (4, 4, 0), (61, 256, 256), (1, 1, 1)])
 def test_split_descent_k_edges(K):
-    """The two-part descent (4096 rows, two KV heads) with empty levels, K
+    """The two-part descent (16384 rows, two KV heads) with empty levels, K
     above the candidate counts (buckets far past 32 members) and K = 1."""
-    case = _small(seed=37, dtype="bf16", B=2, N=128, S_kv=131, Hq=16, Hkv=2, M_R=61, M_I=907, M=9001,
+    case = _small(seed=37, dtype="bf16", B=2, N=512, S_kv=515, Hq=16, Hkv=2, M_R=61, M_I=907, M=9001,
                   K=(6, 9, 24))
-    assert case.rows >= 4096
-    _check(case, rows=parity.sample_rows(case, 64, seed=41), two_phase=True, K=K)
+    assert case.rows >= 16384
+    _check(case, rows=parity.sample_rows(case, 64, seed=41), two_phase=True, K=K, out_dtype=torch.float32)
 
 
 def test_empty_batch_writes_nothing():
