@@ -234,6 +234,48 @@ def test_split_descent_k_edges(K):
     _check(case, rows=parity.sample_rows(case, 64, seed=41), two_phase=True, K=K, out_dtype=torch.float32)
 
 
+def test_threads_sharing_a_view():
+    """Two host threads call the split descent (16384 rows) and a decode call
+    on one view, each on its own stream and workspace: the view's part and
+    sequence streams are shared through its mutex, and every result equals
+    the one-thread result bit for bit."""
+    import threading
+    case = _small(seed=43, dtype="bf16", B=2, N=256, S_kv=260, Hq=32, Hkv=8, M_R=61, M_I=907, M=20011,
+                  K=(6, 9, 24))
+    dec = _small(seed=44, dtype="bf16", B=16, N=1, S_kv=300, Hq=32, Hkv=8, M_R=61, M_I=907, M=20011,
+                 K=(6, 9, 24))
+    dec.root_k, dec.mid_k, dec.leaf_k, dec.leaf_v = case.root_k, case.mid_k, case.leaf_k, case.leaf_v
+    dec.root_off, dec.mid_off = case.root_off, case.mid_off
+    tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
+
+    def run(c, stream, reps):
+        ws = atlaskv.alloc_workspace(tree, c.q, c.seq_k, c.K)
+        outs = []
+        with torch.cuda.stream(stream):
+            for _ in range(reps):
+                out = torch.empty(c.q.shape, dtype=torch.float32, device=DEV)
+                atlaskv.hikvp_attend_ex(c.q, tree, c.seq_k, c.seq_v, c.K, out, workspace=ws, stream=stream)
+                outs.append(out)
+        stream.synchronize()
+        return [o.cpu().numpy() for o in outs]
+
+    say("threads sharing a view: one-thread references")
+    ref_a = run(case, torch.cuda.Stream(), 1)[0]
+    ref_b = run(dec, torch.cuda.Stream(), 1)[0]
+    results = {}
+    s_a, s_b = torch.cuda.Stream(), torch.cuda.Stream()
+    ta = threading.Thread(target=lambda: results.__setitem__("a", run(case, s_a, 3)))
+    tb = threading.Thread(target=lambda: results.__setitem__("b", run(dec, s_b, 3)))
+    say("threads sharing a view: two threads, three calls each")
+    ta.start(); tb.start(); ta.join(); tb.join()
+    tree.close()
+    assert len(results["a"]) == 3 and len(results["b"]) == 3
+    for o in results["a"]:
+        assert np.array_equal(o, ref_a)
+    for o in results["b"]:
+        assert np.array_equal(o, ref_b)
+
+
 def test_empty_batch_writes_nothing():
     case = _small(seed=15, N=1, S_kv=4)
     tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
