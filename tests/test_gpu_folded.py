@@ -133,6 +133,22 @@ def test_folded_separate_kg_query_and_gqa():
     check(f, q_kg=q_kg)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_folded_strided_projections(dtype):
+    """W_K / W_V as views with padded rows (row stride D_E + 16 bytes, heads
+    further apart): the kernels follow the strides."""
+    f = Folded(7, dtype=dtype)
+    pad = 16 // (2 if dtype == "bf16" else 4)
+    for name in ("w_k", "w_v"):
+        w = getattr(f, name)
+        wide = torch.zeros(w.shape[0], w.shape[1] + 1, w.shape[2] + pad, dtype=w.dtype, device=DEV)
+        wide[:, :w.shape[1], :w.shape[2]] = w
+        view = wide[:, :w.shape[1], :w.shape[2]]
+        assert not view.is_contiguous()
+        setattr(f, name, view)
+    check(f)
+
+
 def test_folded_identity_projections_match_the_per_row_path():
     """One KV head, W_K = W_V = I: the folded call selects exactly what the
     per-row path selects on the base tree itself."""
