@@ -103,7 +103,7 @@ struct StepArgs {
                               // than kBucketSlots rows
   int32_t desc_per_sub;       // ceil(row_chunks(rows, K[1]) / kDescSub) * row_chunk_entries(K[1])
   int32_t bucket_q;           // ceil(Hkv * M_I / 64)
-  float* junk;                // [kJunkSlots * 16] write-only sinks for masked-off score lanes
+  float* junk;                // [kJunkSlots * 16] write-only sinks for the mid GEMM's idle score lanes
   int32_t* bucket_ovf;        // [rows * K[1] / (kBucketSlots + 1) + 1] keys (g*M_I + mid) with overflow members
   float* o_kg;                // [R, d] softmax-weighted leaf values (fp32)
   float* lse_kg;              // [R] log-sum-exp of the selected leaf logits

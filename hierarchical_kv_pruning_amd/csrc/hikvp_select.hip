@@ -561,7 +561,7 @@ __global__ void k_bucket_link(StepArgs a) {
 // depend on the (atomic) order in which members joined the bucket.
 template <class E, int D>
 __device__ inline void score_member_group(const StepArgs& a, const char* kp, int64_t rsb, int F, int2 mem,
-                                          int g0, int gcnt, float* junk, int lane) {
+                                          int g0, int gcnt, int lane) {
   constexpr int RB = D * E::kBytes;        // bytes per key row
   constexpr int KP = RB / 128;             // 16-byte pieces per lane per tile
   constexpr int TU = 4;                    // tiles per round = consecutive keys per lane
@@ -589,11 +589,10 @@ __device__ inline void score_member_group(const StepArgs& a, const char* kp, int
     dst[vv] = (owner && ms < gcnt) ? a.leaf_scores + (int64_t)srow * a.c2max + sbase + item * TU : nullptr;
   }
   // Each round issues its loads, then writes the previous round's scores,
-  // then waits for the loads.  The memory counter completes in issue
-  // order, stores included, so every round issues the same four 16-byte
-  // stores (lanes with nothing to write aim at this wave's junk slot) and
-  // a fixed number of loads (keys past the span re-read its last row):
-  // the wait for a round's loads then never covers the stores after them.
+  // then waits for the loads; loads are unconditional (keys past the span
+  // re-read its last row).  Score stores are predicated per lane: sending the
+  // idle lanes to a junk slot instead, so that every round issues the same
+  // stores, measured ~2 % slower.
   float4_t prev[TU];
 #pragma unroll
   for (int u = 0; u < TU; ++u) prev[u] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -610,10 +609,10 @@ __device__ inline void score_member_group(const StepArgs& a, const char* kp, int
   auto store_full = [&]() {            // prev holds a full round (or none)
 #pragma unroll
     for (int vv = 0; vv < 4; ++vv) {
-      float* d = (pt0 >= 0 && dst[vv]) ? dst[vv] + pt0 : junk;
+      float* d = (pt0 >= 0 && dst[vv]) ? dst[vv] + pt0 : nullptr;
 #pragma unroll
       for (int u = 0; u < TU; u += 4)
-        store4u(d + u, prev[u][vv], prev[u + 1][vv], prev[u + 2][vv], prev[u + 3][vv]);
+        if (d) store4u(d + u, prev[u][vv], prev[u + 1][vv], prev[u + 2][vv], prev[u + 3][vv]);
     }
   };
   int t0 = 0;
@@ -647,10 +646,7 @@ __device__ inline void score_member_group(const StepArgs& a, const char* kp, int
 // hits); members past kBucketSlots are left to k_leaf_score_overflow.
 template <class E, int D>
 __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
-  constexpr int TU = 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
-  float* const junk = a.junk + ((blockIdx.x * nwave + wave) % kJunkSlots) * 16;
-  static_assert(TU % 4 == 0 && TU <= 16, "junk slot holds 16 floats");
   // descriptor v of the concatenated sub-lists: lane s holds sub-list s's
   // count and its inclusive prefix
   const int scnt = a.bucket_count[lane];  // lane < kDescSub = 64
@@ -676,7 +672,7 @@ __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
     cnt = cnt < kBucketSlots ? cnt : kBucketSlots;
     const int2 mem = lane < kBucketSlots ? a.bucket_slot[(int64_t)key * kBucketSlots + lane] : make_int2(-1, 0);
     for (int g0 = 0; g0 < cnt; g0 += 8)
-      score_member_group<E, D>(a, kp, rsb, F, mem, g0, min(8, cnt - g0), junk, lane);
+      score_member_group<E, D>(a, kp, rsb, F, mem, g0, min(8, cnt - g0), lane);
     cur = nxt;
     v = vn;
   }
@@ -688,7 +684,6 @@ __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
 template <class E, int D>
 __global__ __launch_bounds__(256) void k_leaf_score_overflow(StepArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
-  float* const junk = a.junk + ((blockIdx.x * nwave + wave) % kJunkSlots) * 16;
   const int nov = a.bucket_count[kDescSub];
   const int K1 = a.K[1];
   const int MI = (int)a.t.count[1];
@@ -709,7 +704,7 @@ __global__ __launch_bounds__(256) void k_leaf_score_overflow(StepArgs a) {
         e = a.bucket_next[e];
       }
       const int2 gm = (lane < gcnt) ? make_int2(mine / K1, a.mid_base[mine]) : make_int2(-1, 0);
-      score_member_group<E, D>(a, kp, rsb, F, gm, 0, gcnt, junk, lane);
+      score_member_group<E, D>(a, kp, rsb, F, gm, 0, gcnt, lane);
     }
   }
 }
@@ -762,47 +757,46 @@ __device__ inline void leaf_select_body(const StepArgs& a, size_t group_bytes) {
   }
   sum = wave_sum(sum);
   wave_sync();
-  const char* vb = (const char*)a.t.leaf_v + (int64_t)g * a.t.hs[3] * E::kBytes;
+  // Value rows are read 16 bytes a lane, LPK lanes a row, so one load
+  // instruction covers KPW rows and VU instructions in flight cover the
+  // K_L rows of a row in one or two memory round trips; each lane sums its
+  // dims over the rows of its lane group, then the KPW groups are added.
+  constexpr int EPV = E::kEPV, LPK = D / EPV, KPW = 64 / LPK;
+  constexpr int VU = 8;
+  const int sub = lane / LPK, ch = lane % LPK;
+  const char* vb = (const char*)a.t.leaf_v + (int64_t)g * a.t.hs[3] * E::kBytes + ch * 16;
   const int64_t vrs = a.t.rs[3] * E::kBytes;
-  float acc[DPL];
+  float acc[EPV];
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-  // value rows gathered VB at a time, so the row's K_L rows take one or two
-  // memory round trips
-  constexpr int VB = 16;  // more would cost occupancy (registers) for the whole kernel
-  int i = 0;
-  for (; i + VB <= k2; i += VB) {
-    float v[VB][DPL];
+  for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
+  for (int i0 = 0; i0 < k2; i0 += KPW * VU) {
+    uint4 raw[VU];
 #pragma unroll
-    for (int u = 0; u < VB; ++u) load_lane<E, DPL>(vb + (int64_t)W.out_node[i + u] * vrs, lane, v[u]);
+    for (int u = 0; u < VU; ++u) {
+      const int i = i0 + u * KPW + sub;
+      raw[u] = i < k2 ? *(const uint4*)(vb + (int64_t)W.out_node[i] * vrs) : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-    for (int u = 0; u < VB; ++u) {
-      const float w = W.out_logit[i + u];
+    for (int u = 0; u < VU; ++u) {
+      const int i = i0 + u * KPW + sub;
+      const float w = i < k2 ? W.out_logit[i] : 0.f;
+      float v[EPV];
+      unpack<E>(raw[u], v);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, v[u][e], acc[e]);
+      for (int e = 0; e < EPV; ++e) acc[e] = fmaf(w, v[e], acc[e]);
     }
   }
-  for (; i + 8 <= k2; i += 8) {
-    float v[8][DPL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) load_lane<E, DPL>(vb + (int64_t)W.out_node[i + u] * vrs, lane, v[u]);
+  for (int m = LPK; m < 64; m <<= 1)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float w = W.out_logit[i + u];
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, v[u][e], acc[e]);
-    }
-  }
-  for (; i < k2; ++i) {
-    float v[DPL];
-    load_lane<E, DPL>(vb + (int64_t)W.out_node[i] * vrs, lane, v);
-    const float w = W.out_logit[i];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(w, v[e], acc[e]);
-  }
+    for (int e = 0; e < EPV; ++e) acc[e] += __shfl_xor(acc[e], m);
   const float inv = 1.f / sum;
+  if (sub == 0) {
+    float4* dst = (float4*)(okg + ch * EPV);
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) okg[lane * DPL + e] = acc[e] * inv;
+    for (int e = 0; e < EPV; e += 4)
+      dst[e / 4] = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+  }
   if (lane == 0) a.lse_kg[row] = mx + logf(sum);
 }
 
