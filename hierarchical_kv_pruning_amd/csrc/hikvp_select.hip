@@ -148,10 +148,15 @@ __global__ __launch_bounds__(1024) void k_root_scan(StepArgs a) {
     const int key = kb + k0 + tid;
     int tot = 0;
     if (k0 + tid < nkeys) {
-      for (int sb = 0; sb < kRootSub; ++sb) {  // sub-counts -> first rank of each sub-counter
-        const int c = a.root_cnt[(int64_t)sb * nall + key];
+      // sub-counts -> first rank of each sub-counter; all loads are issued
+      // before the first store, so they take one memory round trip
+      int c[kRootSub];
+#pragma unroll
+      for (int sb = 0; sb < kRootSub; ++sb) c[sb] = a.root_cnt[(int64_t)sb * nall + key];
+#pragma unroll
+      for (int sb = 0; sb < kRootSub; ++sb) {
         a.root_cnt[(int64_t)sb * nall + key] = tot;
-        tot += c;
+        tot += c[sb];
       }
       a.root_tot[key] = tot;
     }
