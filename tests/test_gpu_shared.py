@@ -135,6 +135,15 @@ def test_shared_ragged_dtypes_and_head_dims(share, dtype, d):
 
 
 @pytest.mark.parametrize("share", [KVG, SEQ])
+@pytest.mark.parametrize("Hq,dtype,d", [(6, "bf16", 128), (12, "f32", 64), (16, "bf16", 64)])
+def test_shared_group_sizes(share, Hq, dtype, d):
+    """KV groups of 3, 6 and 8 query heads: the KG kernel takes a group's
+    heads four at a time, so these cover a partial set of four, a full set
+    plus a partial one, and two full sets."""
+    check(_small(6, Hq=Hq, Hkv=2, dtype=dtype, d=d), share)
+
+
+@pytest.mark.parametrize("share", [KVG, SEQ])
 def test_shared_k_edges_and_no_sequence(share):
     case = _small(2, M=3001)
     check(case, share, K=(1, 1, 1))
