@@ -321,41 +321,6 @@ __device__ inline float4_t split_combine(float4_t acc, int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// Score a run of candidate keys: out[c] = <q, key[first + c]> (fp32, unscaled)
-// for c < len.  LPK lanes read one key row as 16-byte pieces, so a wave load
-// covers 64/LPK whole rows; U loads are kept in flight per lane.  NW waves
-// (w = this wave) split the run.  qf: this lane's EPV query elements.
-// ---------------------------------------------------------------------------
-template <class E, int D, int U>
-__device__ inline void score_run(const float* qf, const char* kbase, int64_t rsb,
-                                 const SlotMap& map, int len, float* out, int w, int NW,
-                                 int lane) {
-  constexpr int EPV = E::kEPV, LPK = D / EPV, KPW = 64 / LPK;
-  const int j = lane % LPK, sub = lane / LPK;
-  const int step = NW * KPW;
-  for (int c0 = w * KPW; c0 < len; c0 += step * U) {
-    uint4 kv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + u * step + sub;
-      if (c < len) kv[u] = *(const uint4*)(kbase + map(c) * rsb + j * 16);
-      else kv[u] = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + u * step + sub;
-      float kf[EPV];
-      unpack<E>(kv[u], kf);
-      float s = 0.f;
-#pragma unroll
-      for (int t = 0; t < EPV; ++t) s = fmaf(qf[t], kf[t], s);
-      s = group_sum<LPK>(s);
-      if (j == 0 && c < len) out[c] = s;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Exact-boundary Top-K select over n fp32 candidate scores.
 //
 // The page ranks the candidates of each level by their attention score and

@@ -7,11 +7,13 @@
 // leaves' softmax then forms the KG half of the merged output.
 //
 //   k_clear     zeroes the group and bucket counters of the part's KV heads.
-//   k_root      one wave per row: scores of all M_R root keys of the row's KV
-//               head (coalesced 16-byte lanes), exact-boundary Top-K_R; each
-//               selection is counted in its (KV head, root) group.  The
-//               per-row select kernels keep a few KB of LDS per wave so many
-//               rows are in flight per CU.
+//   k_root_mfma one wave per 16 rows of one KV head: their scores against all
+//               M_R root keys of the head on MFMA 16x16 tiles (a root key is
+//               read once per 16 rows).
+//   k_root      one wave per row: exact-boundary Top-K_R over the row's root
+//               scores; each selection is counted in its (KV head, root)
+//               group.  The per-row select kernels keep a few KB of LDS per
+//               wave so many rows are in flight per CU.
 //   k_root_scan / k_root_fill  lay the groups out in tiles of 32 rows; the
 //               fill also records where each selected root's children start
 //               in the row's mid candidate list.
@@ -93,9 +95,70 @@ __device__ inline double load_query(const RowsDev& r, int b, int n, int h, float
   return sqrt((double)qq) * 1.0001;
 }
 
+// Root scores on MFMA: one wave per 16 consecutive rows of one KV head and
+// kRootChunk of its roots (the rows are the M side, 16 roots the N side of
+// each 16x16 tile, the chunk's tiles loaded at once), so a root key is read
+// once per 16 rows instead of once per row.  The raw dot products (the
+// select applies the scale) land in each row's slots of the mid-score buffer
+// (indexed by row, like the mid level's scores, so concurrent descent parts
+// touch disjoint slots), which k_root reads before the mid level reuses them.
+constexpr int kRootChunk = 64;  // roots per k_root_mfma wave
+
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_root_mfma(StepArgs a, int tph, int nrc) {
+  constexpr int KCH = D * E::kBytes / 64;  // 16-byte pieces per lane per row
+  constexpr int NU = kRootChunk / 16;      // root tiles in flight
+  const int lane = threadIdx.x & 63, quad = lane >> 4, col = lane & 15;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= (a.g1 - a.g0) * tph * nrc) return;
+  const int rc = w % nrc, t = w / nrc;     // root chunk, row tile
+  const int g = a.g0 + t / tph, m0 = (t % tph) * 16;
+  const int per_head = a.r.B * a.r.N * a.r.G;  // rows of one KV head
+  const int hb = g * per_head;                 // its first block
+  const int MR = (int)a.t.count[0];
+  uint4 afr[KCH];
+  if (m0 + col < per_head) {
+    int b, n, h;
+    decode_row(a.r, row_of_block(a.r, hb + m0 + col), b, n, h);
+    const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes + quad * 16;
+#pragma unroll
+    for (int m = 0; m < KCH; ++m) afr[m] = *(const uint4*)(qp + m * 64);
+  } else {
+#pragma unroll
+    for (int m = 0; m < KCH; ++m) afr[m] = make_uint4(0, 0, 0, 0);
+  }
+  // this lane's outputs: rows m0 + 4*quad + v, root j0 + 16*u + col
+  float* dst[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int mv = m0 + 4 * quad + v;
+    dst[v] = mv < per_head ? a.mid_scores + (int64_t)row_of_block(a.r, hb + mv) * a.c1max : nullptr;
+  }
+  int64_t rsb;
+  const char* kb = key_base(a.t, 0, g, rsb, E::kBytes) + quad * 16;
+  const int j1 = min(MR, (rc + 1) * kRootChunk);
+  for (int j0 = rc * kRootChunk; j0 < j1; j0 += 16 * NU) {
+    uint4 bfr[NU][KCH];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const char* kp = kb + (int64_t)min(j0 + 16 * u + col, j1 - 1) * rsb;
+#pragma unroll
+      for (int m = 0; m < KCH; ++m) bfr[u][m] = *(const uint4*)(kp + m * 64);
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const float4_t sc = tile_dot<E, KCH>(afr, bfr[u]);
+      const int j = j0 + 16 * u + col;
+      if (j < j1)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (dst[v]) dst[v][j] = sc[v];
+    }
+  }
+}
+
 template <class E, int D>
 __global__ __launch_bounds__(256) void k_root(StepArgs a, size_t wave_bytes, int stage) {
-  constexpr int EPV = E::kEPV, LPK = D / EPV;
   extern __shared__ __align__(16) char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
   const int blk = a.blk0 + blockIdx.x * nwave + wave;
@@ -103,24 +166,23 @@ __global__ __launch_bounds__(256) void k_root(StepArgs a, size_t wave_bytes, int
   const int MR = (int)a.t.count[0];
   const int K = a.K[0];
   RowWork W = carve_rowwork(smem + (size_t)wave * wave_bytes, K, 0, D, stage);
-  float* sc = stage ? W.stage : a.mid_scores + (int64_t)blk * a.c1max;  // spill: reuse the mid buffer
-
   const int row = row_of_block(a.r, blk);
+  // the row's scores, from k_root_mfma in the row's slots of the mid-score
+  // buffer (by row, as the mid level uses it: concurrent parts own disjoint
+  // rows), staged in LDS when they fit
+  const float* gsc = a.mid_scores + (int64_t)row * a.c1max;
+  float* sc = stage ? W.stage : a.mid_scores + (int64_t)row * a.c1max;
   int b, n, h;
   decode_row(a.r, row, b, n, h);
   const int g = h / a.r.G;
+  if (stage)
+    for (int j = lane; j < MR; j += 64) sc[j] = gsc[j];
   const double qnorm = load_query<E, D>(a.r, b, n, h, W.sel.qrow, lane);
   wave_sync();
-  float qf[EPV];
-#pragma unroll
-  for (int t = 0; t < EPV; ++t) qf[t] = W.sel.qrow[(lane % LPK) * EPV + t];
 
   int64_t rsb;
   const char* kb = key_base(a.t, 0, g, rsb, E::kBytes);
   const SlotMap ident{nullptr, nullptr, -1};
-  score_run<E, D, 4>(qf, kb, rsb, ident, MR, sc, 0, 1, lane);
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  wave_sync();
   const int k = select_topk<E, D, 64, MemScores<64>, true>(MemScores<64>{sc}, MR, K, twice_err_bound<D>(qnorm, a.t.norm[g]),
                                       a.r.scale, ident, KeyRows{kb, rsb}, W.sel, W.out_node, W.out_logit,
                                       lane);
@@ -876,10 +938,17 @@ hipError_t launch_root(const StepArgs& a, hipStream_t s) {
   if (a.blk1 <= a.blk0) return hipSuccess;
   int wpb, stage;
   size_t wb;
-  // root scores are produced in-kernel: keep them in LDS when they fit
+  // the root scores come from k_root_mfma through the mid-score buffer (which
+  // holds at least M_R slots a row); k_root stages them in LDS when they fit
   if (!row_launch_shape(a.K[0], 0, a.t.d, a.t.count[0], wpb, wb, stage, a.t.count[0] <= 2048))
     return hipErrorInvalidValue;
-  if (!stage && a.t.count[0] > a.c1max) return hipErrorInvalidValue;  // spill buffer too small
+  if (a.t.count[0] > a.c1max) return hipErrorInvalidValue;  // score buffer too small
+  const int64_t per_head = (int64_t)a.r.B * a.r.N * a.r.G;
+  const int tph = (int)((per_head + 15) / 16);
+  const int nrc = (int)((a.t.count[0] + kRootChunk - 1) / kRootChunk);
+  const int64_t waves = (int64_t)(a.g1 - a.g0) * tph * nrc;
+  if (waves > 0)
+    HIKVP_DISPATCH(a.t.dtype, a.t.d, k_root_mfma, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a, tph, nrc);
   const unsigned blocks = (unsigned)((a.blk1 - a.blk0 + wpb - 1) / wpb);
   HIKVP_DISPATCH(a.t.dtype, a.t.d, k_root, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb, stage);
   return hipGetLastError();
