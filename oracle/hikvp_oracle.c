@@ -158,6 +158,18 @@ int64_t oracle_level_scores(const oracle_problem* P, int64_t b, int64_t n,
   return cnt;
 }
 
+int oracle_candidate_scores(const oracle_problem* P, int64_t b, int64_t n,
+                            int64_t h, int64_t nc, const void* cand_k,
+                            double* score) {
+  if (!P || nc < 0 || (nc > 0 && (!cand_k || !score))) return -1;
+  const int64_t d = P->d;
+  const int64_t qb = q_base(P, b, n, h);
+  const void* qk = kg_query(P);
+  for (int64_t i = 0; i < nc; ++i)
+    score[i] = P->scale * dot(qk, qb, cand_k, i * d, P->dtype, d);
+  return 0;
+}
+
 /* ---- the per-row pieces --------------------------------------------------- */
 
 static int64_t max_children(const int64_t* off, int64_t count) {

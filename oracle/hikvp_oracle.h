@@ -102,6 +102,15 @@ int64_t oracle_level_scores(const oracle_problem* P, int64_t b, int64_t n,
                             int64_t n_parents, int64_t* cand, double* score,
                             int64_t cap);
 
+/* Scores of nc candidate keys given explicitly ([nc, d] in P->dtype), for
+ * row (b, n, h): score[i] = scale * <q_kg, cand_k[i]>, the same sequential
+ * fp64 dot product as oracle_level_scores (used where the leaf array is not
+ * on the host, e.g. to rank a row's leaf candidates under given parents).
+ * Returns 0, or -1 for a bad argument. */
+int oracle_candidate_scores(const oracle_problem* P, int64_t b, int64_t n,
+                            int64_t h, int64_t nc, const void* cand_k,
+                            double* score);
+
 /* Full forward for rows (b[i], n[i], h[i]).  Returns 0, or a negative code:
  * -1 bad argument, -2 both the KG set and the sequence part empty for a row,
  * -3 out of memory. */

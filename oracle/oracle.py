@@ -3,7 +3,10 @@
 TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
 cpu_baseline leg of the benchmark, never by the GPU library.  It converts
 host arrays (numpy or CPU torch tensors) to C-contiguous buffers and marshals
-them; all arithmetic happens in the C file.
+them.  Scoring, Top-K, the KG and sequence softmaxes and the merge run in the
+C file; the variant helpers further down (group queries of shared selections,
+folded queries and the folded KG half) do their extra steps here in fp64
+numpy and math.fsum, each written out in the function that uses it.
 """
 import ctypes
 import math
@@ -50,7 +53,8 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        path = _build.LIB
+        # HIKVP_ORACLE_LIB: another build of the same source (the sanitizer test's)
+        path = os.environ.get("HIKVP_ORACLE_LIB") or _build.LIB
         if not os.path.exists(path):
             _build.build()
         L = ctypes.CDLL(path)
@@ -62,6 +66,9 @@ def lib():
                                           ctypes.c_int64, ctypes.c_int, _I64P, ctypes.c_int64,
                                           _I64P, _F64P, ctypes.c_int64]
         L.oracle_level_scores.restype = ctypes.c_int64
+        L.oracle_candidate_scores.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int64, ctypes.c_int64,
+                                              ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, _F64P]
+        L.oracle_candidate_scores.restype = ctypes.c_int
         rows_sig = [ctypes.POINTER(_Problem), ctypes.c_int64, _I64P, _I64P, _I64P]
         L.oracle_hikvp_rows.argtypes = rows_sig + [ctypes.POINTER(_Outputs)]
         L.oracle_hikvp_rows.restype = ctypes.c_int
@@ -361,7 +368,8 @@ def folded_query(q_kg, w_k, rows=None):
     return _round_to(out, dt)
 
 
-def folded_rows(base_tree, q, w_k, w_v, seq_k, seq_v, K, rows, scale=None, q_kg=None):
+def folded_rows(base_tree, q, w_k, w_v, seq_k, seq_v, K, rows, scale=None, q_kg=None,
+                forced_sel_I=None, forced_sel_L=None):
     """Folded-projection variant (方法细节 › KBLaM中的矩形注意力 gives the
     projected keys and values W_K k and W_V v of per-layer heads; one base
     tree serves every head): the descent over the base tree (root_k, mid_k,
@@ -369,7 +377,11 @@ def folded_rows(base_tree, q, w_k, w_v, seq_k, seq_v, K, rows, scale=None, q_kg=
     queries q'; the KG half of row (b, n, h) is W_V[g] applied to the
     softmax-weighted base values, merged with the causal sequence half over
     seq_k / seq_v [B, S, Hkv, d].  Returns dict(out, lse_kg, lse_seq, sel_R,
-    sel_I, sel_L, gap, o_kg)."""
+    sel_I, sel_L, gap, o_kg).
+
+    Replay: with forced_sel_I and forced_sel_L ([rows, K_I], [rows, K_L],
+    -1 padded) the leaf candidates are the children of the given mids and the
+    KG softmax runs over the given leaves instead of the oracle's choice."""
     import torch
     root_k, mid_k, leaf_k, leaf_v, root_off, mid_off = base_tree
     d = q.shape[-1]
@@ -386,9 +398,14 @@ def folded_rows(base_tree, q, w_k, w_v, seq_k, seq_v, K, rows, scale=None, q_kg=
     a = np.full(len(r), -np.inf)
     o_base = np.zeros((len(r), DE))
     for i, (b, n, h) in enumerate(r):
-        parents = [int(m) for m in ph1["sel_I"][i] if m >= 0]
+        sel_mid = ph1["sel_I"][i] if forced_sel_I is None else np.asarray(forced_sel_I[i])
+        parents = [int(m) for m in sel_mid if m >= 0]
         cand, score = level_scores(P, b, n, h, 2, parents) if parents and KL > 0 else (np.zeros(0, np.int64), np.zeros(0))
-        pos = topk(score, cand, KL) if len(cand) and KL > 0 else np.zeros(0, np.int64)
+        if forced_sel_L is not None:
+            where = {int(c): j for j, c in enumerate(cand)}
+            pos = np.asarray([where[int(x)] for x in forced_sel_L[i] if x >= 0], np.int64)
+        else:
+            pos = topk(score, cand, KL) if len(cand) and KL > 0 else np.zeros(0, np.int64)
         sel_L[i, :len(pos)] = cand[pos]
         ranked = sorted(range(len(cand)), key=lambda j: (-score[j], cand[j]))
         if 0 < KL < len(cand):
@@ -469,6 +486,19 @@ def level_scores(prob: Problem, b, n, h, level, parents=()):
     if c < 0:
         raise RuntimeError("oracle_level_scores: capacity exceeded")
     return cand[:c], score[:c]
+
+
+def candidate_scores(prob: Problem, b, n, h, cand_k):
+    """fp64 scaled scores of explicitly given candidate keys [nc, d] (the
+    problem's storage type) for row (b, n, h)."""
+    ck, dk = _host(cand_k)
+    if len(ck) and dk != prob.dtype:
+        raise TypeError("candidate storage type differs from the problem's")
+    out = np.zeros(max(1, len(ck)))
+    _check(lib().oracle_candidate_scores(ctypes.byref(prob._P), int(b), int(n), int(h), len(ck),
+                                         _vp(ck) if len(ck) else None, _fp(out)),
+           "oracle_candidate_scores")
+    return out[:len(ck)]
 
 
 def tree_sizes(M):

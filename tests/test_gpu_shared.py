@@ -1,8 +1,9 @@
 """GPU parity of the shared-selection variant (one descent per KV group or per
 sequence on the group's summed query) against the fp64 oracle, through the C
 ABI.  Group selections are compared as sets (the same 1e-6 boundary-gap
-exemption as the per-row path, exempt groups compared in replay mode with the
-GPU's leaves); outputs to the same bar: fp32 max-abs <= 1e-5, bf16 max-abs
+exemption as the per-row path: an exempt group's selections must be valid
+Top-Ks of the oracle's scores under the GPU's own parents, and its rows are
+compared in replay mode with the GPU's leaves); outputs to the same bar: fp32 max-abs <= 1e-5, bf16 max-abs
 <= 2e-2 x RMS and cosine >= 0.9999.
 
 For bf16 inputs the bar is applied to an fp32 output (the API's other output
@@ -81,14 +82,17 @@ def check(case, share, rows=None, **kw):
     ora = oracle.shared_rows(P, rows, share)
     grp = group_of(case, rows, share)
     exempt = []
+    Pg = None
     for i, gi in enumerate(grp):
-        for lev, key in enumerate(("sel_R", "sel_I", "sel_L")):
-            g_set = sorted(int(x) for x in gpu["sel"][lev][gi] if x >= 0)
-            o_set = sorted(int(x) for x in ora[key][i] if x >= 0)
-            if g_set != o_set:
-                assert ora["gap"][i][lev] < parity.GAP_EXEMPT, (tuple(rows[i]), lev, g_set, o_set)
-                exempt.append(i)
-                break
+        g = [gpu["sel"][lev][gi] for lev in range(3)]
+        lev = parity.first_mismatch(g, ora, i)
+        if lev < 0:
+            continue
+        assert ora["gap"][i][lev] < parity.GAP_EXEMPT, (tuple(rows[i]), lev, ora["gap"][i][lev])
+        if Pg is None:  # the descent's problem: the group queries as KG queries
+            Pg = oracle.Problem(*P._args, scale=P._kw["scale"], q_kg=oracle.group_queries(P, share))
+        parity.check_selection_chain(case, Pg, rows[i], g)
+        exempt.append(i)
     out_o = ora["out"].copy()
     if exempt:  # replay: the oracle finishes those rows over the GPU's group leaves
         rr = np.asarray(rows)[exempt]
@@ -104,6 +108,7 @@ def check(case, share, rows=None, **kw):
         rep = oracle.finish_rows(P, rr, off, idx, torch.cat(ks), torch.cat(vs),
                                  forced_sel_L=gpu["sel"][2][grp[exempt]].astype(np.int64))
         out_o[exempt] = rep["out"]
+        rep_lse = rep["lse_kg"]
     ridx = parity.row_index(case, rows)
     g, o = gpu["out"][ridx], out_o
     err = float(np.abs(g - o).max(initial=0.0))
@@ -116,8 +121,10 @@ def check(case, share, rows=None, **kw):
         rep.update(rms=rms, cos=cos)
         assert err <= 2e-2 * rms, rep
         assert cos >= 0.9999, rep
-    fin = np.isfinite(ora["lse_kg"])
-    assert np.array_equal(np.isfinite(gpu["lse_kg"][ridx]), fin)
+    lk_o = ora["lse_kg"].copy()
+    if exempt:
+        lk_o[exempt] = rep_lse
+    rep["lse_kg_err"] = parity.check_lse("lse_kg", gpu["lse_kg"][ridx], lk_o, parity.LSE_TOL[case.dtype])
     say(f"{case.name}: {rep}")
     return gpu, ora
 
