@@ -1,8 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
-same seeded inputs.  Small and medium workloads compare every row; the full
-workloads (1e6 prefill, 1e7 decode, 1e8 slice) compare seeded row samples
-with the oracle's two-phase mode, in the launch configuration the benchmark
-times."""
+same seeded inputs.  Every workload compares every row; the full workloads
+(1e6 prefill, 1e7 decode, 1e8 slice) use the oracle's two-phase mode (roots
+and mids on the host, each row's leaf candidates copied from the device) in
+the launch configuration the benchmark times."""
 import gc
 import sys
 
@@ -36,7 +36,8 @@ def _check(case, rows=None, two_phase=False, **kw):
         return parity.oracle_rows(case, np.array(rws), forced_sel_L=np.array(selL, np.int64),
                                   sel_I=np.array(selI, np.int64), **okw)
 
-    rep = parity.compare(case, rows, gpu, ora, replay=replay)
+    P = parity.oracle_problem(case, leaves=False, **okw)
+    rep = parity.compare(case, rows, gpu, ora, replay=replay, problem=P)
     say(f"{case.name}: {rep}")
     return gpu, ora, rep
 
@@ -86,6 +87,20 @@ def test_full_k_selects_every_leaf():
     case = _small(seed=6, M_R=4, M_I=20, M=200, K=(4, 20, 200))
     gpu, _, _ = _check(case)
     assert all(sorted(s[s >= 0].tolist()) == list(range(200)) for s in gpu["sel"][2])
+
+
+def test_k_above_every_candidate_count_equals_full_k():
+    """K = 1000 at every level (above 256) clamps to each level's candidates:
+    the same selections and bits as K = (M_R, M_I, M) on a 4/20/200 tree, the
+    caller's selection rows (stride 1000) -1 padded past them."""
+    case = _small(seed=61, M_R=4, M_I=20, M=200, K=(4, 20, 200))
+    full = parity.gpu_run(case, K=(4, 20, 200))
+    big = parity.gpu_run(case, K=(1000, 1000, 1000))
+    assert np.array_equal(full["out"], big["out"]) and np.array_equal(full["lse_kg"], big["lse_kg"])
+    for a, b in zip(full["sel"], big["sel"]):
+        assert b.shape[1] == 1000
+        assert np.array_equal(a, b[:, :a.shape[1]]) and np.all(b[:, a.shape[1]:] == -1)
+    _check(case, K=(1000, 1000, 1000))
 
 
 def test_no_sequence_half():
@@ -221,7 +236,7 @@ def test_split_descent_matches_serial_and_oracle(Hq, Hkv, N):
             assert np.array_equal(a, b)
     # fp32 output: with N = 256+ the early tokens' outputs reach ~12x the RMS,
     # where a bf16 output's own rounding (2^-9 of the value) exceeds 2e-2 x RMS
-    _check(case, rows=parity.sample_rows(case, 96, seed=31), two_phase=True, out_dtype=torch.float32)
+    _check(case, two_phase=True, out_dtype=torch.float32)
 
 
 @pytest.mark.parametrize("K", [(0, 4, 4), (4, 0, 4), (4, 4, 0), (61, 256, 256), (1, 1, 1)])
@@ -390,22 +405,22 @@ def test_m1e4_all_rows():
     _check(synth.make_case("m1e4", device=DEV))
 
 
-def test_m1e6_sampled_rows():
+def test_m1e6_all_rows():
     case = synth.make_case("m1e6", device=DEV)
-    _check(case, rows=parity.sample_rows(case, 384, seed=1), two_phase=True)
+    _check(case, two_phase=True)
     del case
     _release()
 
 
-def test_m1e7_decode_sampled_rows():
+def test_m1e7_decode_all_rows():
     case = synth.make_case("m1e7_decode", device=DEV)
-    _check(case, rows=parity.sample_rows(case, 192, seed=2), two_phase=True)
+    _check(case, two_phase=True)
     del case
     _release()
 
 
-def test_m1e8_slice_sampled_rows():
+def test_m1e8_slice_all_rows():
     case = synth.make_case("m1e8_slice", device=DEV)
-    _check(case, rows=parity.sample_rows(case, 128, seed=3), two_phase=True)
+    _check(case, two_phase=True)
     del case
     _release()
