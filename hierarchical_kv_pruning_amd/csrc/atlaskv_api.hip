@@ -181,7 +181,8 @@ atlaskv_status device_address(const void* p, const char* name, const void** dev,
 
 struct Plan {
   int B, N, Hq, S, R, G;
-  int K[3];
+  int K[3];                    // Top-K per level, clamped to the level's candidate capacity
+  int Kuser[3];                // as given (row stride of the caller's selection outputs)
   int64_t c1max, c2max;
   double scale;
   int nsplit;
@@ -286,7 +287,7 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   }
   if (!flat)
     for (int i = 0; i < 3; ++i)
-      if (Kpl[i] < 0 || Kpl[i] > kMaxK) return fail(ATLASKV_ERR_K, "K[%d]=%d outside 0..%d", i, Kpl[i], kMaxK);
+      if (Kpl[i] < 0) return fail(ATLASKV_ERR_K, "K[%d]=%d is negative", i, Kpl[i]);
   const bool kg_empty = flat ? t.count[2] == 0
                              : (Kpl[0] == 0 || Kpl[1] == 0 || Kpl[2] == 0 || t.count[0] == 0 ||
                                 t.count[1] == 0 || t.count[2] == 0);
@@ -320,7 +321,25 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
     p.total = o;
     return ATLASKV_OK;
   }
-  for (int i = 0; i < 3; ++i) p.K[i] = Kpl[i];
+  // K clamps to the most candidates a row can have at each level (all roots;
+  // the children of K_R roots; the children of K_I mids), so any K at or above
+  // that selects every candidate; the kernels take at most kMaxK a level.
+  {
+    int64_t cap = t.count[0];
+    for (int i = 0; i < 3; ++i) {
+      p.Kuser[i] = Kpl[i];
+      int64_t k = Kpl[i];
+      if (k > 0 && k > (cap > 1 ? cap : 1)) k = cap > 1 ? cap : 1;
+      if (k > kMaxK)
+        return fail(ATLASKV_ERR_K, "K[%d]=%d: more than %d selections from %lld candidates a row is unsupported",
+                    i, Kpl[i], kMaxK, (long long)cap);
+      p.K[i] = (int)k;
+      if (i < 2) {
+        cap = k * v->maxfan[i];
+        if (cap > t.count[i + 1]) cap = t.count[i + 1];
+      }
+    }
+  }
   if (mode == kModeSharedKvGroup || mode == kModeSharedSequence) {
     // the group descent's own workspace, then group queries, per-row KG half, sequence partials
     const int64_t Ng = mode == kModeSharedSequence ? 1 : N;
@@ -410,6 +429,33 @@ void fill_rows(RowsDev& r, const atlaskv_tensor* q, const atlaskv_attend_opts* o
   r.scale = p.scale;
 }
 
+// Selection arrays of one descent (plan pd): the caller's outputs where their
+// row stride (the K the caller gave) equals the clamped K the kernels use,
+// else the workspace's, copied into the caller's -1-padded rows afterwards.
+struct SelTargets {
+  int32_t* sel[3];
+  int32_t* user[3];            // caller outputs still to fill from sel (NULL: none)
+};
+
+SelTargets sel_targets(const Plan& pd, const atlaskv_attend_opts* opts, char* ws) {
+  SelTargets t;
+  int32_t* u[3] = {opts ? opts->sel_root : nullptr, opts ? opts->sel_mid : nullptr,
+                   opts ? opts->sel_leaf : nullptr};
+  for (int i = 0; i < 3; ++i) {
+    const bool direct = u[i] && pd.Kuser[i] == pd.K[i];
+    t.sel[i] = direct ? u[i] : (int32_t*)(ws + pd.off_sel[i]);
+    t.user[i] = direct ? nullptr : u[i];
+  }
+  return t;
+}
+
+hipError_t finish_sel(const SelTargets& t, const Plan& pd, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < 3 && e == hipSuccess; ++i)
+    if (t.user[i]) e = launch_expand_sel(t.sel[i], pd.K[i], t.user[i], pd.Kuser[i], pd.R, s);
+  return e;
+}
+
 // Folded projections: the tree is a one-head base tree of width D_E; the
 // layer has Hkv heads of width d with W_K, W_V [Hkv, d, D_E].  pd receives the
 // plan of the descent on the folded rows [B, N, Hq, D_E] (unset when the KG
@@ -475,7 +521,7 @@ atlaskv_status plan_folded(const atlaskv_tensor* q, const atlaskv_tree_view_s* v
       if (out->shape[i] != q->shape[i]) return fail(ATLASKV_ERR_SHAPE, "out shape differs from q's");
   }
   for (int i = 0; i < 3; ++i)
-    if (Kpl[i] < 0 || Kpl[i] > kMaxK) return fail(ATLASKV_ERR_K, "K[%d]=%d outside 0..%d", i, Kpl[i], kMaxK);
+    if (Kpl[i] < 0) return fail(ATLASKV_ERR_K, "K[%d]=%d is negative", i, Kpl[i]);
   const bool kg_empty = Kpl[0] == 0 || Kpl[1] == 0 || Kpl[2] == 0 || t.count[0] == 0 || t.count[1] == 0 ||
                         t.count[2] == 0;
   if (kg_empty && !seq_k)
@@ -490,7 +536,25 @@ atlaskv_status plan_folded(const atlaskv_tensor* q, const atlaskv_tree_view_s* v
   p.R = (int)(B * N * Hq);
   p.G = (int)(Hq / Hkv);
   p.scale = scale;
-  for (int i = 0; i < 3; ++i) p.K[i] = Kpl[i];
+  // K clamps to the most candidates a row can have at each level (all roots;
+  // the children of K_R roots; the children of K_I mids), so any K at or above
+  // that selects every candidate; the kernels take at most kMaxK a level.
+  {
+    int64_t cap = t.count[0];
+    for (int i = 0; i < 3; ++i) {
+      p.Kuser[i] = Kpl[i];
+      int64_t k = Kpl[i];
+      if (k > 0 && k > (cap > 1 ? cap : 1)) k = cap > 1 ? cap : 1;
+      if (k > kMaxK)
+        return fail(ATLASKV_ERR_K, "K[%d]=%d: more than %d selections from %lld candidates a row is unsupported",
+                    i, Kpl[i], kMaxK, (long long)cap);
+      p.K[i] = (int)k;
+      if (i < 2) {
+        cap = k * v->maxfan[i];
+        if (cap > t.count[i + 1]) cap = t.count[i + 1];
+      }
+    }
+  }
   p.fold_Hkv = (int)Hkv;
   p.fold_d = (int)d;
   p.fold_kg_empty = kg_empty;
@@ -883,10 +947,7 @@ atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vie
 
   RowsDev rows;
   fill_rows(rows, q, opts, p);
-  int32_t* sel[3];
-  int32_t* user_sel[3] = {opts ? opts->sel_root : nullptr, opts ? opts->sel_mid : nullptr,
-                          opts ? opts->sel_leaf : nullptr};
-  for (int i = 0; i < 3; ++i) sel[i] = user_sel[i] ? user_sel[i] : (int32_t*)(ws + p.off_sel[i]);
+  const SelTargets st3 = sel_targets(p, opts, ws);
   float* lse_kg = (opts && opts->lse_kg) ? opts->lse_kg : (float*)(ws + p.off_lse);
   float* o_kg = (float*)(ws + p.off_okg);
 
@@ -895,8 +956,9 @@ atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vie
                                  lse_kg, ws, v);
   hipError_t e = pm.mark(hipSuccess);
   if (e == hipSuccess) e = seq_start(sh, v, s);
-  if (e == hipSuccess) e = launch_descent(p, rows, v, ws, sel, o_kg, lse_kg, s, pm);
+  if (e == hipSuccess) e = launch_descent(p, rows, v, ws, st3.sel, o_kg, lse_kg, s, pm);
   if (e == hipSuccess) e = seq_finish(sh, v, s, pm);
+  if (e == hipSuccess) e = finish_sel(st3, p, s);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return ATLASKV_OK;
 }
@@ -971,10 +1033,8 @@ atlaskv_status atlaskv_shared_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vi
   fill_rows(rows, q, opts, p);
   fill_rows(grows, &gd, nullptr, pg);
   grows.scale = p.scale;
-  int32_t* sel[3];
-  int32_t* user_sel[3] = {opts ? opts->sel_root : nullptr, opts ? opts->sel_mid : nullptr,
-                          opts ? opts->sel_leaf : nullptr};
-  for (int i = 0; i < 3; ++i) sel[i] = user_sel[i] ? user_sel[i] : (int32_t*)(ws + pg.off_sel[i]);
+  const SelTargets st3 = sel_targets(pg, opts, ws);
+  int32_t* const* sel = st3.sel;
   float* lse_kg = (opts && opts->lse_kg) ? opts->lse_kg : (float*)(ws + p.off_lse);
   float* o_kg = (float*)(ws + p.off_okg);
   SharedArgs sa;
@@ -1001,6 +1061,7 @@ atlaskv_status atlaskv_shared_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vi
     e = launch_descent(pg, grows, v, ws, sel, (float*)(ws + pg.off_okg), (float*)(ws + pg.off_lse), s, pm);
   if (e == hipSuccess) e = pm.mark(launch_shared_kg(sa, s));
   if (e == hipSuccess) e = seq_finish(sh, v, s, pm);
+  if (e == hipSuccess) e = finish_sel(st3, pg, s);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return ATLASKV_OK;
 }
@@ -1100,11 +1161,9 @@ atlaskv_status atlaskv_folded_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vi
     RowsDev frows;
     fill_rows(frows, &qd, nullptr, pd);
     frows.scale = p.scale;
-    int32_t* sel[3];
-    int32_t* user_sel[3] = {opts ? opts->sel_root : nullptr, opts ? opts->sel_mid : nullptr,
-                            opts ? opts->sel_leaf : nullptr};
-    for (int i = 0; i < 3; ++i) sel[i] = user_sel[i] ? user_sel[i] : (int32_t*)(ws + pd.off_sel[i]);
-    if (e == hipSuccess) e = launch_descent(pd, frows, v, ws, sel, (float*)(ws + pd.off_okg), lse_kg, s, pm);
+    const SelTargets st3 = sel_targets(pd, opts, ws);
+    if (e == hipSuccess) e = launch_descent(pd, frows, v, ws, st3.sel, (float*)(ws + pd.off_okg), lse_kg, s, pm);
+    if (e == hipSuccess) e = finish_sel(st3, pd, s);
   }
   if (e == hipSuccess) e = pm.mark(launch_unfold_values(fa, p.fold_kg_empty != 0, s));
   if (e == hipSuccess)

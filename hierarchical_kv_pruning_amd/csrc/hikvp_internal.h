@@ -74,7 +74,7 @@ struct StepArgs {
   RowsDev r;
   int g0, g1;                 // KV heads of this part
   int blk0, blk1;             // row blocks of this part
-  int K[3];                   // Top-K per level (before clamping)
+  int K[3];                   // Top-K per level (plan-clamped; a row takes min(K, its candidates))
   int64_t c1max;              // mid candidates per row: capacity and row stride of mid_scores
   int64_t c2max;              // leaf candidates per row: capacity
   float* mid_scores;          // [R, c1max] unscaled fp32 mid scores, candidate order
@@ -183,6 +183,8 @@ hipError_t launch_validate(const int64_t* off, int64_t count, int64_t children, 
                            BuildStats* stats, hipStream_t s);
 hipError_t launch_key_norms(const void* key, int dtype, int d, int Hkv, int64_t rows,
                             int64_t hs, int64_t rs, unsigned int* out_bits, hipStream_t s);
+// dst[r, i] = src[r, i] for i < Ks, -1 for Ks <= i < Kd (rows r < R)
+hipError_t launch_expand_sel(const int32_t* src, int Ks, int32_t* dst, int Kd, int R, hipStream_t s);
 hipError_t launch_clear(const StepArgs& a, hipStream_t s);        // bucket counters of both levels
 hipError_t launch_root(const StepArgs& a, hipStream_t s);
 hipError_t launch_root_groups(const StepArgs& a, hipStream_t s);  // rows by selected (head, root)

@@ -9,6 +9,17 @@
 namespace hikvp {
 namespace {
 
+// Selections computed with a K clamped below the caller's: copied into the
+// caller's rows of Kd entries, -1 past the computed ones.
+__global__ void k_expand_sel(const int32_t* src, int Ks, int32_t* dst, int Kd, int64_t total) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / Kd;
+    const int c = (int)(i % Kd);
+    dst[i] = c < Ks ? src[r * Ks + c] : -1;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // tree-view set-up
 // ---------------------------------------------------------------------------
@@ -84,6 +95,15 @@ hipError_t launch_key_norms(const void* key, int dtype, int d, int Hkv, int64_t 
   if (blocks > 2048) blocks = 2048;
   HIKVP_DISPATCH(dtype, d, k_key_norms, dim3((unsigned)blocks, (unsigned)Hkv), dim3(256), 0, s, key,
                  rows, hs, rs, out_bits);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_sel(const int32_t* src, int Ks, int32_t* dst, int Kd, int R, hipStream_t s) {
+  const int64_t total = (int64_t)R * Kd;
+  if (total <= 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_expand_sel, dim3((unsigned)blocks), dim3(256), 0, s, src, Ks, dst, Kd, total);
   return hipGetLastError();
 }
 

@@ -31,7 +31,13 @@
  *     are exact with respect to the fp64 value of that logit computed from the
  *     stored inputs (products exact, summed left to right over the head dim);
  *   - K clamps to the number of candidates; K = 0 at any level empties the KG
- *     half (then the output is plain causal attention);
+ *     half (then the output is plain causal attention).  Before anything
+ *     runs, each level's K is clamped to the most candidates a row can have
+ *     there (M_R roots; the children of K_R roots under the largest root
+ *     fanout, at most M_I; the children of K_I mids likewise, at most M), so
+ *     K at or above that bound selects every candidate whatever its value.
+ *     Only a clamped K above 256 (more than 256 selections out of more than
+ *     256 candidates) is refused, with ATLASKV_ERR_K;
  *   - causal alignment is bottom-right: token n sees sequence positions
  *     0 .. S_kv - N + n (so S_kv >= N); seq_k == NULL means no sequence half;
  *   - only leaves carry values; the KG softmax runs over the K_L selected
@@ -85,7 +91,7 @@ typedef enum {
   ATLASKV_ERR_DTYPE = 2,       /* unknown dtype, or inputs of different dtypes */
   ATLASKV_ERR_SHAPE = 3,       /* shapes, strides or alignment inconsistent */
   ATLASKV_ERR_TREE = 4,        /* malformed child offsets */
-  ATLASKV_ERR_K = 5,           /* K < 0 or K > 256, or both halves empty */
+  ATLASKV_ERR_K = 5,           /* K < 0, a clamped K above 256, or both halves empty */
   ATLASKV_ERR_WORKSPACE = 6,   /* workspace missing, too small or misaligned */
   ATLASKV_ERR_UNSUPPORTED = 7, /* head dim not 64/128, node counts >= 2^31, scale <= 0 */
   ATLASKV_ERR_HIP = 8          /* a HIP runtime call failed */
@@ -163,7 +169,7 @@ atlaskv_status atlaskv_hikvp_workspace_size(atlaskv_tree_view tree, const atlask
  *   q      [B, N, Hq, d]  queries (post-RoPE); also the KG query
  *   seq_k  [B, S_kv, Hkv, d], seq_v likewise: causal sequence keys/values
  *          (both NULL: no sequence half)
- *   K_per_level  host int32 {K_R, K_I, K_L}, each in 0..256
+ *   K_per_level  host int32 {K_R, K_I, K_L}, each >= 0 (clamped per level, see above)
  *   out    [B, N, Hq, d]  dtype of q, or fp32
  */
 atlaskv_status atlaskv_hikvp_attend(const atlaskv_tensor* q, atlaskv_tree_view tree,
@@ -190,8 +196,9 @@ typedef struct {
 } atlaskv_attend_opts;
 
 /* As atlaskv_hikvp_attend, with options (opts may be NULL).  The selections
- * are written as sets: each row's K entries are the selected node indices in
- * candidate order, -1 padded when fewer than K candidates exist. */
+ * are written as sets: each row's K entries (K as given, the row stride of
+ * the selection outputs) are the selected node indices in candidate order,
+ * -1 padded when fewer than K candidates exist. */
 atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_view tree,
                                        const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
                                        const int32_t K_per_level[3], atlaskv_tensor* out,

@@ -103,11 +103,39 @@ def test_shape_errors(lib):
 def test_k_errors(lib):
     v = _view()
     assert _call(v, K=(-1, 2, 2)) == atlaskv.ERR_K
-    assert _call(v, K=(2, 2, 257)) == atlaskv.ERR_K
+    assert _call(v, K=(2, -1, 2)) == atlaskv.ERR_K
+    assert _call(v, K=(2, 2, 257)) == atlaskv.OK             # clamps to the 2 * 9 leaf candidates
     assert _call(v, K=(2, 2, 256)) == atlaskv.OK
     assert _call(v, K=(0, 2, 2)) == atlaskv.OK              # empty KG half: plain causal attention
     assert _call(v, K=(2, 2, 0), seq=False) == atlaskv.ERR_K  # both halves empty
     assert _call(v, K=(2, 2, 2), seq=False) == atlaskv.OK
+
+
+def test_k_clamps_to_each_levels_candidates(lib):
+    """K clamps before the 256 limit applies: the tree has 4 roots (fanout
+    <= 5) and 10 mids (fanout <= 9), so K = (1000, 1000, 1000) is (4, 10, 50)
+    -- every candidate -- and plans the same workspace."""
+    v = _view()
+    q = torch.zeros(1, 4, 4, 128, dtype=torch.bfloat16)
+    assert _call(v, K=(1000, 1000, 1000)) == atlaskv.OK
+    assert _call(v, K=(2**31 - 1, 7, 2**31 - 1)) == atlaskv.OK
+    a = atlaskv.hikvp_workspace_size(v, q, None, (1000, 1000, 1000))
+    b = atlaskv.hikvp_workspace_size(v, q, None, (4, 10, 50))
+    assert a == b
+    # K_I clamps to K_R' * 5 = 10 under K_R = 2 ... and to M_I = 10 in any case
+    assert atlaskv.hikvp_workspace_size(v, q, None, (2, 1000, 4)) == atlaskv.hikvp_workspace_size(v, q, None, (2, 10, 4))
+
+
+def test_k_above_256_with_more_candidates_is_refused(lib):
+    """Only a clamped K above 256 is refused: 300 roots, K_R = 257..300."""
+    rk, mk, lk, lv = _tree(MR=300, MI=300, M=600)
+    v = atlaskv.TreeView.describe_only(rk, mk, lk, lv, 1, 2)
+    assert _call(v, K=(256, 4, 4)) == atlaskv.OK
+    assert _call(v, K=(257, 4, 4)) == atlaskv.ERR_K
+    assert "256" in atlaskv.last_error()
+    assert _call(v, K=(300, 300, 600)) == atlaskv.ERR_K
+    # K_I = 300 with K_R = 4 roots of fanout 1: clamps to 4
+    assert _call(v, K=(4, 300, 600)) == atlaskv.OK
 
 
 def test_workspace_errors(lib):
@@ -242,7 +270,8 @@ def test_shared_phase_names_and_checks(lib):
                           "numel": lambda self: 1 << 30})()
     for share in (atlaskv.SHARE_KV_GROUP, atlaskv.SHARE_SEQUENCE):
         assert atlaskv.shared_check_args(q, v, sk, sk, (2, 2, 4), share, q, workspace=fake) == atlaskv.OK
-        assert atlaskv.shared_check_args(q, v, sk, sk, (2, 2, 300), share, q, workspace=fake) == atlaskv.ERR_K
+        assert atlaskv.shared_check_args(q, v, sk, sk, (2, 2, 300), share, q, workspace=fake) == atlaskv.OK
+        assert atlaskv.shared_check_args(q, v, sk, sk, (2, -2, 3), share, q, workspace=fake) == atlaskv.ERR_K
         assert atlaskv.shared_workspace_size(v, q, sk, (2, 2, 4), share) > 0
     assert atlaskv.shared_check_args(q, v, sk, sk, (2, 2, 4), 3, q, workspace=fake) == atlaskv.ERR_UNSUPPORTED
     # a sequence group holds every token: no larger group rows than per token
