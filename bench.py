@@ -12,6 +12,13 @@ fp64 CPU oracle's rate on a bounded row sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload m1e6] [--tree-placement hbm|host-leaves]
 
+Timing: W warm-up steps, then K steps each timed alone with HIP events on the
+launch stream after a 1 GiB write has evicted the 256 MB MALL (cold); the
+headline is their median (p10 / p90 beside it).  The same K steps back to
+back give the warm figure.  Run without --workload, the benchmark first
+measures the m1e7_decode and m1e8_slice workloads (one JSON line each on
+stderr) and ends with the m1e6 line on stdout.
+
 With --tree-placement host-leaves the leaf keys and values sit in pinned host
 memory and the kernels read the selected spans over the host link; the
 roofline is then the link's (PCIe 5.0 x16).
@@ -36,8 +43,8 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, AMD's published figure
 PEAK_LINK_GBPS = 64.0           # MI355X host interface, PCIe 5.0 x16, one direction (published)
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix-core peak (published)
 PEAK_FP32_TFLOPS = 157.3        # MI355X fp32 vector peak (published)
-KERNEL_SOURCES = [os.path.join(ROOT, "hierarchical_kv_pruning_amd", "csrc", f)
-                  for f in ("hikvp_device.h", "hikvp_select.hip", "hikvp_seq.hip")]
+CSRC = os.path.join(ROOT, "hierarchical_kv_pruning_amd", "csrc")
+INCLUDE = os.path.join(ROOT, "include")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -45,9 +52,18 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def kernel_sources():
+    """Every source the library is built from (kernels, launch planning, ABI)."""
+    out = []
+    for d in (CSRC, INCLUDE):
+        out += [os.path.join(d, f) for f in sorted(os.listdir(d)) if f.endswith((".hip", ".h"))]
+    return out
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in kernel_sources():
+        h.update(os.path.relpath(f, ROOT).encode())
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
@@ -150,7 +166,31 @@ def read_traffic(kernel, workload):
 # CPU oracle baseline (bounded sample, two-phase: leaves fetched per row)
 # ---------------------------------------------------------------------------
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(case, seconds):
+    """The oracle on one host core (this thread pinned to it while it runs)."""
+    old = os.sched_getaffinity(0)
+    core = max(old)
+    os.sched_setaffinity(0, {core})
+    try:
+        res = _cpu_baseline(case, seconds)
+    finally:
+        os.sched_setaffinity(0, old)
+    res["host"] = {"nproc": os.cpu_count(), "cores_allowed": len(old), "pinned_core": core,
+                   "cpu_model": cpu_model()}
+    return res
+
+
+def _cpu_baseline(case, seconds):
     from oracle import oracle  # test infrastructure: only this leg uses it
 
     h = lambda t: None if t is None else t.detach().cpu()
@@ -190,13 +230,13 @@ def cpu_baseline(case, seconds):
     tokens_per_s = 1.0 / (per_row * case.Hq)
     return {"value": tokens_per_s, "unit": "query tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{rows_done} of {len(allr)} rows (b,n,h) of workload {case.name}, seeded; "
-                      f"fp64 single-thread C oracle, {t2:.1f} s; leaf candidates copied to host "
-                      f"per row outside the timed calls; tokens/s = rows/s / Hq"}
+                      f"fp64 single-thread C oracle pinned to one core, {t2:.1f} s; leaf candidates "
+                      f"copied to host per row outside the timed calls; tokens/s = rows/s / Hq"}
 
 
 # ---------------------------------------------------------------------------
 
-def flat_line(args, case, ms_per_step, phase_ms, cold, tokens):
+def flat_line(args, case, tm, phase_ms, tokens):
     """JSON line of the unpruned path: every leaf key and value is read once;
     the dominant kernel is the flash pass over the leaves, 4*d flops per
     (row, leaf) pair (scores and weighted values)."""
@@ -218,31 +258,35 @@ def flat_line(args, case, ms_per_step, phase_ms, cold, tokens):
                 "frac": leaves_b / t / 1e9 / PEAK_HBM_GBPS, "algorithmic_bytes": leaves_b}
     roof.update(kernel="flat_kg_partial", traffic=None,
                 hbm_gbps=leaves_b / t / 1e9, tflops=flops / t / 1e12)
+    ms_per_step = tm["ms_per_step"]
     return {
         "metric": "query tokens/s per layer through unpruned equivalent attention (all M leaves)",
         "value": tokens / (ms_per_step * 1e-3), "unit": "query tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "timing": tm,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": case.dtype,
         "data": "synthetic (seeded clustered-Gaussian key tree, Gaussian values, queries and sequence K/V)",
         "config": {"workload": case.name, "path": "flat", "B": case.B, "N": case.N, "S_kv": case.S_kv,
                    "Hq": case.Hq, "Hkv": case.Hkv, "d": case.d, "M": case.M, "tokens_per_step": tokens,
                    "parallelism": "single GPU", "tree_placement": args.tree_placement},
         "path_hbm": {"compulsory_bytes": total_b, "achieved_gbps": total_b / (ms_per_step * 1e-3) / 1e9,
-                     "cold_ms_per_step": cold},
+                     "frac_of_peak": total_b / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS},
         "phase_ms": phase_ms, "roofline": roof, "cpu_baseline": None,
     }
 
 
-def main():
+def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50,
+                    help="timed steps (each alone after a MALL flush; their median is the headline)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="m1e6", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--workload", default=None, choices=sorted(synth.CONFIGS),
+                    help="one workload only (default: m1e7_decode and m1e8_slice on stderr, then m1e6)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-reps", type=int, default=10,
-                    help="extra steps timed one by one after evicting the 256 MB MALL")
+    ap.add_argument("--phase-steps", type=int, default=None,
+                    help="steps of the per-phase event loop (default: --steps, at most 20)")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration)")
     ap.add_argument("--path", default="hikvp", choices=["hikvp", "flat"],
@@ -251,25 +295,68 @@ def main():
                     help="shared selections: one descent per KV head and token, or per KV head "
                          "and sequence (pruned path only)")
     ap.add_argument("--fold", action="store_true",
-                    help="folded projections: one-head base tree (head 0 of the workload's tree, width "
-                         "D_E = d) shared by all heads through random per-head W_K / W_V [Hkv, d, D_E]")
+                    help="folded projections: one-head base tree shared by all heads through random "
+                         "per-head W_K / W_V [Hkv, d, D_E]")
+    ap.add_argument("--fold-width", type=int, default=0,
+                    help="base width D_E of the folded tree (default: the head dim, using the workload's "
+                         "head-0 tree; otherwise a fresh base tree of that width with the workload's topology)")
     ap.add_argument("--tree-placement", default="hbm", choices=["hbm", "host-leaves"],
                     help="host-leaves: leaf keys and values in pinned host memory, read by the "
                          "kernels over the host link (roots, mids, offsets stay in HBM)")
-    args = ap.parse_args()
+    return ap.parse_args(argv)
 
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
-              file=sys.stderr)
-        sys.exit(2)
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
 
-    dev = torch.device("cuda:0")
-    atlaskv.lib()
-    log(f"workload {args.workload}: generating on {torch.cuda.get_device_name(0)}")
-    case = synth.make_case(args.workload, device=dev)
+def time_steps(step, stream, steps, warmup, dev):
+    """Warm-up, then `steps` cold steps (each after evicting the MALL, timed
+    alone) and `steps` warm steps back to back; times in ms."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)   # 1 GiB > the 256 MB MALL
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in pairs:
+        flush.add_(1)
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    cold = np.array([a.elapsed_time(b) for a, b in pairs])
+    del flush
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    warm = t0.elapsed_time(t1) / steps
+    return {"ms_per_step": float(np.median(cold)), "cold_p10_ms": float(np.percentile(cold, 10)),
+            "cold_p90_ms": float(np.percentile(cold, 90)), "cold_steps": int(steps),
+            "warm_ms_per_step": float(warm), "protocol": "median of cold steps (1 GiB written between "
+            "steps to evict the 256 MB MALL; each step timed alone with HIP events on the launch stream)"}
+
+
+def fold_inputs(case, args, dev):
+    """Base tree and per-head projections of a folded run."""
+    DE = args.fold_width or case.d
+    if DE == case.d:
+        base = [t[:1].contiguous() for t in (case.root_k, case.mid_k, case.leaf_k, case.leaf_v)]
+        base_off = (case.root_off, case.mid_off)
+    else:
+        b = synth.make_case("base", device=dev, seed=synth.CONFIGS[case.name]["seed"] + 500, ragged=False, dtype=case.dtype, B=1, N=1,
+                            S_kv=1, Hq=1, Hkv=1, d=DE, M_R=case.M_R, M_I=case.M_I, M=case.M, K=case.K)
+        base = [b.root_k, b.mid_k, b.leaf_k, b.leaf_v]
+        base_off = (b.root_off, b.mid_off)
+    gen = torch.Generator(device=dev).manual_seed(17)
+    w_k = (torch.randn(case.Hkv, case.d, DE, generator=gen, device=dev) / DE ** 0.5).to(case.q.dtype)
+    w_v = (torch.randn(case.Hkv, case.d, DE, generator=gen, device=dev) / DE ** 0.5).to(case.q.dtype)
+    return base, base_off, w_k, w_v, DE
+
+
+def run_one(args, workload, dev, with_cpu):
+    log(f"workload {workload}: generating on {torch.cuda.get_device_name(0)}")
+    case = synth.make_case(workload, device=dev)
     link_copy_gbps = None
     if args.tree_placement == "host-leaves":
         log("moving leaf keys and values to pinned host memory")
@@ -293,26 +380,20 @@ def main():
         torch.cuda.synchronize()
         link_copy_gbps = (1 << 30) / (a.elapsed_time(b) * 1e-3) / 1e9
         del src, dst
-    tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
     flat = args.path == "flat"
     share = {"none": 0, "kv-group": atlaskv.SHARE_KV_GROUP, "sequence": atlaskv.SHARE_SEQUENCE}[args.share]
     fold = args.fold
     if fold and (flat or share):
-        print("--fold applies to the per-row pruned path only", file=sys.stderr)
-        sys.exit(2)
-    if fold:
-        # the base tree: head 0 of the workload's tree; per-head projections of the layer
-        tree.close()
-        base = [t[:1].contiguous() for t in (case.root_k, case.mid_k, case.leaf_k, case.leaf_v)]
-        tree = atlaskv.TreeView(*base, case.root_off, case.mid_off)
-        gen = torch.Generator(device=dev).manual_seed(17)
-        w_k = (torch.randn(case.Hkv, case.d, case.d, generator=gen, device=dev) / case.d ** 0.5).to(case.q.dtype)
-        w_v = (torch.randn(case.Hkv, case.d, case.d, generator=gen, device=dev) / case.d ** 0.5).to(case.q.dtype)
-        case.root_k, case.mid_k, case.leaf_k, case.leaf_v = base
-        torch.cuda.empty_cache()
+        raise SystemExit("--fold applies to the per-row pruned path only")
     if flat and share:
-        print("--share applies to the pruned path only", file=sys.stderr)
-        sys.exit(2)
+        raise SystemExit("--share applies to the pruned path only")
+    DE = case.d
+    if fold:
+        base, base_off, w_k, w_v, DE = fold_inputs(case, args, dev)
+        case.root_k, case.mid_k, case.leaf_k, case.leaf_v = base
+        case.root_off, case.mid_off = base_off
+        torch.cuda.empty_cache()
+    tree = atlaskv.TreeView(case.root_k, case.mid_k, case.leaf_k, case.leaf_v, case.root_off, case.mid_off)
     if flat:
         ws = atlaskv.alloc_flat_workspace(tree, case.q, case.seq_k)
     elif fold:
@@ -333,66 +414,37 @@ def main():
         if flat:
             atlaskv.flat_attend_ex(case.q, tree, case.seq_k, case.seq_v, out, workspace=ws,
                                    phase_events=events, stream=stream)
-            return
-        if fold:
+        elif fold:
             atlaskv.folded_attend_ex(case.q, tree, w_k, w_v, case.seq_k, case.seq_v, case.K, out, workspace=ws,
                                      sel_root=sel[0], sel_mid=sel[1], sel_leaf=sel[2], phase_events=events,
                                      stream=stream)
-            return
-        if share:
+        elif share:
             atlaskv.shared_attend_ex(case.q, tree, case.seq_k, case.seq_v, case.K, share, out,
                                      workspace=ws, sel_root=sel[0], sel_mid=sel[1], sel_leaf=sel[2],
                                      phase_events=events, stream=stream)
-            return
-        atlaskv.hikvp_attend_ex(case.q, tree, case.seq_k, case.seq_v, case.K, out, workspace=ws,
-                                sel_root=sel[0], sel_mid=sel[1], sel_leaf=sel[2],
-                                phase_events=events, stream=stream)
+        else:
+            atlaskv.hikvp_attend_ex(case.q, tree, case.seq_k, case.seq_v, case.K, out, workspace=ws,
+                                    sel_root=sel[0], sel_mid=sel[1], sel_leaf=sel[2],
+                                    phase_events=events, stream=stream)
 
-    log(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(args.steps)]
+    log(f"{workload}: warmup {args.warmup}, {args.steps} cold steps, {args.steps} warm steps")
+    tm = time_steps(step, stream, args.steps, args.warmup, dev)
+    ms_per_step = tm["ms_per_step"]
+    # per-phase kernel times from separate steps with phase events (the library
+    # then runs everything serially on the call's stream)
+    nph = args.phase_steps if args.phase_steps is not None else min(args.steps, 20)
+    nph = max(1, nph)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(nph)]
     for row in evs:
         for e in row:
             e.record(stream)           # create the underlying HIP events before timing
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    # per-phase kernel times from separate steps with phase events (the library
-    # then runs the sequence half after the KG half instead of beside it)
-    log(f"phase timing {args.steps} steps")
-    for i in range(args.steps):
+    log(f"{workload}: phase timing {nph} steps")
+    for i in range(nph):
         step(evs[i])
     torch.cuda.synchronize()
-    phase_ms = {p: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+    phase_ms = {p: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(nph)]))
                 for j, p in enumerate(phases)}
-
-    # cold steps: MALL evicted between steps, each step timed alone
-    cold = None
-    if args.cold_reps > 0:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        ts = []
-        for _ in range(args.cold_reps):
-            flush.add_(1)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            step()
-            b.record(stream)
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b))
-        cold = float(np.median(ts))
-        del flush
 
     if args.calib_copy_gib > 0:
         n = int(args.calib_copy_gib * (1 << 30))
@@ -406,18 +458,23 @@ def main():
 
     tokens = case.B * case.N
     if flat:
-        print(json.dumps(flat_line(args, case, ms_per_step, phase_ms, cold, tokens)), flush=True)
+        line = flat_line(args, case, tm, phase_ms, tokens)
         tree.close()
-        return
+        return line
     host_sel = [s.cpu().numpy() for s in sel]
     if fold:  # every row reads the one base tree: KV head 0 for the byte count
-        saved = (case.Hkv, case.Hq)
-        case.Hkv, case.Hq = 1, case.Hq
+        saved = (case.Hkv, case.Hq, case.d)
+        case.Hkv, case.d = 1, DE
         ab = algorithmic_bytes(case, host_sel, 0)
-        case.Hkv, case.Hq = saved
-        seq_fix = 2 * case.B * case.S_kv * case.Hkv * case.d * (2 if case.dtype == "bf16" else 4)
-        ab["_total"] += seq_fix - ab["seq_attention"]
+        case.Hkv, case.Hq, case.d = saved
+        eb = 2 if case.dtype == "bf16" else 4
+        seq_fix = 2 * case.B * case.S_kv * case.Hkv * case.d * eb
+        qo_fix = 2 * case.rows * case.d * eb
+        ab["_total"] += seq_fix - ab["seq_attention"] + qo_fix - ab["_parts"]["q"] - ab["_parts"]["out"]
         ab["_parts"]["sequence_kv"] = ab["seq_attention"] = seq_fix
+        ab["_parts"]["q"] = ab["_parts"]["out"] = case.rows * case.d * eb
+        ab["_parts"]["projections"] = 2 * case.Hkv * case.d * DE * eb
+        ab["_total"] += ab["_parts"]["projections"]
     else:
         ab = algorithmic_bytes(case, host_sel, share)
     recall = None
@@ -443,7 +500,7 @@ def main():
     dom = max((p for p in phases if p in ab), key=lambda p: phase_ms[p])
     achieved = ab[dom] / (phase_ms[dom] * 1e-3) / 1e9
     on_host = args.tree_placement == "host-leaves"
-    traffic = None if on_host else read_traffic(dom, case.name)
+    traffic = None if (on_host or fold or share) else read_traffic(dom, case.name)
     path_gbps = ab["_total"] / (ms_per_step * 1e-3) / 1e9
 
     line = {
@@ -457,14 +514,18 @@ def main():
         "config": {"workload": case.name, "B": case.B, "N": case.N, "S_kv": case.S_kv, "Hq": case.Hq,
                    "Hkv": case.Hkv, "d": case.d, "tree": [case.M_R, case.M_I, case.M], "K": list(case.K),
                    "tokens_per_step": tokens, "parallelism": "single GPU",
-                   "tree_placement": args.tree_placement, "share": args.share, "fold": fold},
+                   "tree_placement": args.tree_placement, "share": args.share, "fold": fold,
+                   **({"fold_width": DE} if fold else {})},
+        "timing": tm,
+        "warm_value": tokens / (tm["warm_ms_per_step"] * 1e-3),
         "path_hbm": {"compulsory_bytes": ab["_total"], "achieved_gbps": path_gbps,
                      "frac_of_peak": path_gbps / PEAK_HBM_GBPS, "parts": ab["_parts"],
-                     "cold_ms_per_step": cold},
+                     "warm_frac_of_peak": ab["_total"] / (tm["warm_ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBPS},
         "phase_ms": phase_ms,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": traffic, "algorithmic_bytes": ab[dom]},
+                     "traffic": traffic, "algorithmic_bytes": ab[dom],
+                     "path_frac": path_gbps / PEAK_HBM_GBPS},
         "cpu_baseline": None,
     }
     if share:
@@ -476,12 +537,35 @@ def main():
         link_b = ab["_parts"]["leaf_keys"] + ab["_parts"]["leaf_values"]
         line["host_link"] = {"bytes": link_b, "achieved_gbps": link_b / (ms_per_step * 1e-3) / 1e9,
                              "peak_gbps": peak, "copy_engine_gbps": link_copy_gbps}
-    if not args.no_cpu_baseline:
-        log(f"cpu baseline (~{args.cpu_seconds:.0f} s of oracle time)")
-        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
-        line["cpu_baseline"]["host"] = {"nproc": os.cpu_count()}
     tree.close()
-    print(json.dumps(line), flush=True)
+    del ws, out, sel
+    if with_cpu and not args.no_cpu_baseline:
+        log(f"cpu baseline (~{args.cpu_seconds:.0f} s of oracle time, one core)")
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    del case
+    torch.cuda.empty_cache()
+    return line
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    atlaskv.lib()
+    if args.workload is not None:
+        print(json.dumps(run_one(args, args.workload, dev, with_cpu=True)), flush=True)
+        return
+    # the other target workloads first (stderr), the headline workload last (stdout)
+    for extra in ("m1e7_decode", "m1e8_slice"):
+        line = run_one(args, extra, dev, with_cpu=False)
+        print(json.dumps(line), file=sys.stderr, flush=True)
+    print(json.dumps(run_one(args, "m1e6", dev, with_cpu=True)), flush=True)
 
 
 if __name__ == "__main__":
