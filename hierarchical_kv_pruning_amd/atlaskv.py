@@ -14,7 +14,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libatlaskv.so")
+# ATLASKV_LIB names another build of the same sources (the host-sanitizer test's)
+LIB_PATH = os.environ.get("ATLASKV_LIB") or os.path.join(_HERE, "libatlaskv.so")
 
 OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_TREE, ERR_K, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP = range(9)
 STATUS_NAMES = ["OK", "ERR_NULL", "ERR_DTYPE", "ERR_SHAPE", "ERR_TREE", "ERR_K", "ERR_WORKSPACE",

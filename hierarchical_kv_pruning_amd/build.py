@@ -30,15 +30,17 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
+    """Compile every source into one shared library at `out` (extra_flags:
+    e.g. host-only sanitizer flags, each behind -Xarch_host)."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

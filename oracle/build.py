@@ -11,15 +11,22 @@ SRC = os.path.join(HERE, "hikvp_oracle.c")
 LIB = os.path.join(HERE, "liboracle_hikvp.so")
 
 
-def build(force: bool = True) -> str:
-    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
-        return LIB
-    tmp = LIB + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+SANITIZE = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+            "-fno-omit-frame-pointer"]
+
+
+def build(force: bool = True, out: str = LIB, sanitize: bool = False) -> str:
+    """gcc build of the oracle at `out`; sanitize: an AddressSanitizer +
+    UndefinedBehaviorSanitizer build of the same source (same -ffp-contract)."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(SRC):
+        return out
+    tmp = out + ".tmp"
+    opt = SANITIZE if sanitize else ["-O2"]
+    cmd = ["gcc", *opt, "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
            "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
