@@ -12,10 +12,10 @@ fp64 CPU oracle's rate on a bounded row sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload m1e6] [--tree-placement hbm|host-leaves]
 
-Timing: W warm-up steps, then K steps each timed alone with HIP events on the
-launch stream after a 1 GiB write has evicted the 256 MB MALL (cold); the
-headline is their median (p10 / p90 beside it).  The same K steps back to
-back give the warm figure.  Run without --workload, the benchmark first
+Timing: W warm-up steps, then max(K, 50) steps each timed alone with HIP
+events on the launch stream after a 1 GiB write has evicted the 256 MB MALL
+(cold); the headline is their median (p10 / p90 beside it).  K steps back
+to back give the warm figure.  Run without --workload, the benchmark first
 measures the m1e7_decode and m1e8_slice workloads (one JSON line each on
 stderr) and ends with the m1e6 line on stdout.
 
@@ -279,7 +279,8 @@ def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50,
-                    help="timed steps (each alone after a MALL flush; their median is the headline)")
+                    help="timed steps: max(steps, 50) cold steps, each alone after a MALL flush (their "
+                         "median is the headline), and `steps` warm steps back to back")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, choices=sorted(synth.CONFIGS),
                     help="one workload only (default: m1e7_decode and m1e8_slice on stderr, then m1e6)")
@@ -306,14 +307,19 @@ def parse_args(argv=None):
     return ap.parse_args(argv)
 
 
+MIN_COLD_STEPS = 50
+
+
 def time_steps(step, stream, steps, warmup, dev):
-    """Warm-up, then `steps` cold steps (each after evicting the MALL, timed
-    alone) and `steps` warm steps back to back; times in ms."""
+    """Warm-up, then max(steps, 50) cold steps (each after evicting the MALL,
+    timed alone: the headline is their median) and `steps` warm steps back to
+    back; times in ms."""
+    ncold = max(steps, MIN_COLD_STEPS)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)   # 1 GiB > the 256 MB MALL
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ncold)]
     torch.cuda.synchronize()
     for a, b in pairs:
         flush.add_(1)
@@ -332,7 +338,7 @@ def time_steps(step, stream, steps, warmup, dev):
     torch.cuda.synchronize()
     warm = t0.elapsed_time(t1) / steps
     return {"ms_per_step": float(np.median(cold)), "cold_p10_ms": float(np.percentile(cold, 10)),
-            "cold_p90_ms": float(np.percentile(cold, 90)), "cold_steps": int(steps),
+            "cold_p90_ms": float(np.percentile(cold, 90)), "cold_steps": int(ncold),
             "warm_ms_per_step": float(warm), "protocol": "median of cold steps (1 GiB written between "
             "steps to evict the 256 MB MALL; each step timed alone with HIP events on the launch stream)"}
 

@@ -176,8 +176,14 @@ def oracle_rows(case, rows, two_phase=False, forced_sel_L=None, sel_I=None, **kw
     chunks = _row_chunks(case, len(rows), K)
     if len(chunks) == 1:
         return work(chunks[0])
+    parts = [None] * len(chunks)
+    step = max(1, len(chunks) // 8)
     with concurrent.futures.ThreadPoolExecutor(max_workers=WORKERS) as ex:
-        parts = list(ex.map(work, chunks))
+        futs = {ex.submit(work, c): i for i, c in enumerate(chunks)}
+        for done, f in enumerate(concurrent.futures.as_completed(futs), 1):
+            parts[futs[f]] = f.result()
+            if done % step == 0 or done == len(chunks):
+                print(f"[oracle] {done}/{len(chunks)} row chunks ({len(rows)} rows)", flush=True)
     return _concat(parts)
 
 
