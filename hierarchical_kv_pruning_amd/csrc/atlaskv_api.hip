@@ -186,7 +186,7 @@ struct Plan {
   int64_t c1max, c2max;
   double scale;
   int nsplit;
-  size_t off_mid, off_leaf, off_sel[3], off_okg, off_lse, off_part, total;
+  size_t off_mid, off_mid_meta, off_leaf, off_sel[3], off_okg, off_lse, off_part, total;
   size_t off_mid_base, off_bcnt, off_bslot, off_bhead, off_bnext, off_blist, off_bcount, off_bovf, off_junk;
   size_t off_rcnt, off_rtot, off_rtoff, off_rtkey, off_rnt, off_rmem;
   int64_t root_tiles_max;
@@ -364,14 +364,15 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
       (int64_t)p.R * (p.K[0] + kRootTile) >= kIndexLimit)
     return fail(ATLASKV_ERR_UNSUPPORTED, "B*N*Hq*(K_R+16), B*N*Hq*K_I and Hkv*M_I must be below 2^31");
   candidate_capacity(v, p.K, &p.c1max, &p.c2max);
-  if (p.c1max >= kIndexLimit || p.c2max >= kIndexLimit)
-    return fail(ATLASKV_ERR_UNSUPPORTED, "candidates per row must be below 2^31");
+  if (p.c1max >= kMaxMidCands || p.c2max >= kIndexLimit)
+    return fail(ATLASKV_ERR_UNSUPPORTED, "candidates per row must be below 2^24 (mid) and 2^31 (leaf)");
   p.scale = scale;
   const size_t R = (size_t)p.R;
   size_t o = 0;
   // mid scores; the root kernel also spills its scores here when M_R is large
   if (v->dev.count[0] > p.c1max) p.c1max = v->dev.count[0];
-  p.off_mid = o;       o = align256(o + R * (size_t)p.c1max * 4);
+  p.off_mid = o;       o = align256(o + R * (size_t)p.c1max * 8);
+  p.off_mid_meta = o;  o = align256(o + R * (size_t)p.K[0] * 16);
   p.off_leaf = o;      o = align256(o + R * (size_t)p.c2max * 4);
   for (int i = 0; i < 3; ++i) { p.off_sel[i] = o; o = align256(o + R * (size_t)p.K[i] * 4); }
   p.off_mid_base = o;  o = align256(o + R * (size_t)p.K[1] * 4);
@@ -593,15 +594,21 @@ struct PhaseMarks {
 
 // Sequence half (背景知识与设计原则 › 自注意力层机制) and the λ merge with the
 // KG half held in o_kg / lse_kg.  The causal attention does not depend on the
-// KG half, so for decode (query blocks under 16 tokens) and unless phase
-// timing is requested it runs concurrently: it is enqueued on the view's aux
-// stream, forked from the call's stream before the KG kernels, writes
-// (o, m, l) partials, and the call's stream waits for it before
-// k_seq_combine merges both halves.  Otherwise two phases (attention, split
-// combine) run after the KG half, through the same partials and merge.
+// KG half, so unless phase timing is requested it runs concurrently on the
+// view's aux stream and writes (o, m, l) partials; the call's stream waits for
+// it before k_seq_combine merges both halves.  Decode blocks (under 16
+// tokens: one light HBM-bound wave per SIMD) fork before the KG kernels.
+// Prefill blocks fork just before the last descent part's leaf stream: the
+// matrix-core prefill kernels hold most of a SIMD's registers and LDS, which
+// slowed the latency-bound descent kernels beside them, while the leaf
+// stream, bound by HBM, leaves the SIMDs room.  With phase timing both
+// phases (attention, split combine) run after the KG half, through the same
+// partials and merge.
 struct SeqHalf {
   SeqArgs sa;
-  bool overlap;
+  bool overlap;                // on the aux stream, joined before k_seq_combine
+  bool at_leaf;                // forked before the last part's leaf stream (else before the KG half)
+  mutable bool forked;         // the fork was enqueued (else the half runs after the KG half)
 };
 
 SeqHalf seq_prepare(const Plan& p, const RowsDev& rows, int Hkv, int d, int dtype,
@@ -629,12 +636,9 @@ SeqHalf seq_prepare(const Plan& p, const RowsDev& rows, int Hkv, int d, int dtyp
   sa.out_dtype = out->dtype;
   sa.lse_seq_out = opts ? opts->lse_seq : nullptr;
   sa.nsplit = p.nsplit;
-  // Overlap only the decode kernels (query blocks under 16 tokens): one light
-  // HBM-bound wave per SIMD that the descent's kernels run beside.  The
-  // prefill kernels hold most of a SIMD's registers and LDS per wave, and
-  // beside them the descent's kernels measured slower than running the
-  // prefill attention after the descent.
-  h.overlap = seq_k && v->aux && p.N < 16 && !(opts && opts->phase_events && opts->n_phase_events > 0);
+  h.overlap = seq_k && v->aux && !(opts && opts->phase_events && opts->n_phase_events > 0);
+  h.at_leaf = h.overlap && p.N >= 16;
+  h.forked = false;
   // with a sequence the merge is always k_seq_combine's, so the serial and
   // the overlapped order produce the same bits
   sa.part = seq_k ? (float*)(ws + p.off_part) : nullptr;
@@ -642,20 +646,28 @@ SeqHalf seq_prepare(const Plan& p, const RowsDev& rows, int Hkv, int d, int dtyp
   return h;
 }
 
-// Before the KG half: the fork (when overlapping).
-hipError_t seq_start(const SeqHalf& h, atlaskv_tree_view_s* v, hipStream_t s) {
-  if (!h.overlap) return hipSuccess;
-  std::lock_guard<std::mutex> lock(v->mu);  // one call's record / wait / launch / record stay together
-  hipError_t e = hipEventRecord(v->fork, s);
+// The fork itself, from stream `from`; the caller holds the view's mutex (one
+// call's record / wait / launch / record stay together).
+hipError_t seq_fork_locked(const SeqHalf& h, atlaskv_tree_view_s* v, hipStream_t from) {
+  hipError_t e = hipEventRecord(v->fork, from);
   if (e == hipSuccess) e = hipStreamWaitEvent(v->aux, v->fork, 0);
   if (e == hipSuccess) e = launch_seq_attend(h.sa, v->aux);
   if (e == hipSuccess) e = hipEventRecord(v->join, v->aux);
+  h.forked = e == hipSuccess;
   return e;
 }
 
-// After the KG half: the join and the combine, or the serial sequence half.
+// Before the KG half: the fork of a decode block's sequence half.
+hipError_t seq_start(const SeqHalf& h, atlaskv_tree_view_s* v, hipStream_t s) {
+  if (!h.overlap || h.at_leaf) return hipSuccess;
+  std::lock_guard<std::mutex> lock(v->mu);
+  return seq_fork_locked(h, v, s);
+}
+
+// After the KG half: the join and the combine, or the serial sequence half
+// (also when no descent ran to fork a prefill half from).
 hipError_t seq_finish(const SeqHalf& h, atlaskv_tree_view_s* v, hipStream_t s, PhaseMarks& pm) {
-  if (h.overlap) {
+  if (h.forked) {
     // a later call's join only comes later on aux: waiting on it is still enough
     hipError_t e = hipStreamWaitEvent(s, v->join, 0);
     if (e == hipSuccess) e = launch_seq_combine(h.sa, s);
@@ -666,8 +678,16 @@ hipError_t seq_finish(const SeqHalf& h, atlaskv_tree_view_s* v, hipStream_t s, P
   return e;
 }
 
-// One part of the descent (KV heads [a.g0, a.g1)) on stream s.
-hipError_t descent_part(const StepArgs& a, hipStream_t s, PhaseMarks& pm) {
+// A prefill block's sequence half, forked from a descent part's stream just
+// before its leaf stream (NULL: none to fork there).
+struct LateFork {
+  const SeqHalf* h;
+  atlaskv_tree_view_s* v;
+};
+
+// One part of the descent (KV heads [a.g0, a.g1)) on stream s; the caller
+// holds the view's mutex when `fork` is given.
+hipError_t descent_part(const StepArgs& a, hipStream_t s, PhaseMarks& pm, const LateFork* fork = nullptr) {
   auto mark = [&](hipError_t prev) { return pm.mark(prev); };
   hipError_t e = launch_clear(a, s);
   if (e == hipSuccess) e = launch_root(a, s);
@@ -675,6 +695,7 @@ hipError_t descent_part(const StepArgs& a, hipStream_t s, PhaseMarks& pm) {
   if (e == hipSuccess) e = mark(launch_mid_gemm(a, s));
   if (e == hipSuccess) e = mark(launch_mid_select(a, s));
   if (e == hipSuccess) e = mark(launch_leaf_link(a, s));
+  if (e == hipSuccess && fork && fork->h) e = seq_fork_locked(*fork->h, fork->v, s);
   if (e == hipSuccess) e = mark(launch_leaf_score(a, s));
   if (e == hipSuccess) e = mark(launch_leaf_overflow(a, s));
   if (e == hipSuccess) e = mark(launch_leaf_select(a, s));
@@ -690,7 +711,10 @@ hipError_t descent_part(const StepArgs& a, hipStream_t s, PhaseMarks& pm) {
 // launch gaps are filled by the others' work.  With phase timing requested
 // the descent runs as one part over all heads, serially on s.
 hipError_t launch_descent(const Plan& p, const RowsDev& rows, atlaskv_tree_view_s* v, char* ws,
-                          int32_t* const sel[3], float* o_kg, float* lse_kg, hipStream_t s, PhaseMarks& pm) {
+                          int32_t* const sel[3], float* o_kg, float* lse_kg, hipStream_t s, PhaseMarks& pm,
+                          const SeqHalf* seq = nullptr) {
+  // a prefill sequence half to fork before the last part's leaf stream
+  const LateFork late{(seq && seq->overlap && seq->at_leaf) ? seq : nullptr, v};
   StepArgs a;
   memset(&a, 0, sizeof a);
   a.t = v->dev;
@@ -698,7 +722,8 @@ hipError_t launch_descent(const Plan& p, const RowsDev& rows, atlaskv_tree_view_
   for (int i = 0; i < 3; ++i) { a.K[i] = p.K[i]; a.sel[i] = sel[i]; }
   a.c1max = p.c1max;
   a.c2max = p.c2max;
-  a.mid_scores = (float*)(ws + p.off_mid);
+  a.mid_pairs = (uint2*)(ws + p.off_mid);
+  a.mid_meta = (int4*)(ws + p.off_mid_meta);
   a.leaf_scores = (float*)(ws + p.off_leaf);
   a.mid_base = (int32_t*)(ws + p.off_mid_base);
   a.root_cnt = (int32_t*)(ws + p.off_rcnt);
@@ -726,7 +751,9 @@ hipError_t launch_descent(const Plan& p, const RowsDev& rows, atlaskv_tree_view_
     a.g1 = a.t.Hkv;
     a.blk0 = 0;
     a.blk1 = rows.R;
-    return descent_part(a, s, pm);
+    if (!late.h) return descent_part(a, s, pm);
+    std::lock_guard<std::mutex> lock(v->mu);
+    return descent_part(a, s, pm, &late);
   }
   StepArgs part[kMaxParts];
   int64_t tiles = 0, ovf = 0, desc = 0;
@@ -755,7 +782,7 @@ hipError_t launch_descent(const Plan& p, const RowsDev& rows, atlaskv_tree_view_
     hipStream_t ps = v->part_s[i - 1];
     PhaseMarks none(nullptr, ps);
     e = hipStreamWaitEvent(ps, v->part_fork, 0);
-    if (e == hipSuccess) e = descent_part(part[i], ps, none);
+    if (e == hipSuccess) e = descent_part(part[i], ps, none, i == p.nparts - 1 ? &late : nullptr);
     if (e == hipSuccess) e = hipEventRecord(v->part_join[i - 1], ps);
   }
   if (e == hipSuccess) e = descent_part(part[0], s, pm);
@@ -956,7 +983,7 @@ atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vie
                                  lse_kg, ws, v);
   hipError_t e = pm.mark(hipSuccess);
   if (e == hipSuccess) e = seq_start(sh, v, s);
-  if (e == hipSuccess) e = launch_descent(p, rows, v, ws, st3.sel, o_kg, lse_kg, s, pm);
+  if (e == hipSuccess) e = launch_descent(p, rows, v, ws, st3.sel, o_kg, lse_kg, s, pm, &sh);
   if (e == hipSuccess) e = seq_finish(sh, v, s, pm);
   if (e == hipSuccess) e = finish_sel(st3, p, s);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
@@ -1058,7 +1085,7 @@ atlaskv_status atlaskv_shared_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vi
   if (e == hipSuccess) e = pm.mark(launch_group_query(sa, s));
   // the descent on the group rows; its own KG softmax lands in its workspace
   if (e == hipSuccess)
-    e = launch_descent(pg, grows, v, ws, sel, (float*)(ws + pg.off_okg), (float*)(ws + pg.off_lse), s, pm);
+    e = launch_descent(pg, grows, v, ws, sel, (float*)(ws + pg.off_okg), (float*)(ws + pg.off_lse), s, pm, &sh);
   if (e == hipSuccess) e = pm.mark(launch_shared_kg(sa, s));
   if (e == hipSuccess) e = seq_finish(sh, v, s, pm);
   if (e == hipSuccess) e = finish_sel(st3, pg, s);
@@ -1162,7 +1189,7 @@ atlaskv_status atlaskv_folded_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vi
     fill_rows(frows, &qd, nullptr, pd);
     frows.scale = p.scale;
     const SelTargets st3 = sel_targets(pd, opts, ws);
-    if (e == hipSuccess) e = launch_descent(pd, frows, v, ws, st3.sel, (float*)(ws + pd.off_okg), lse_kg, s, pm);
+    if (e == hipSuccess) e = launch_descent(pd, frows, v, ws, st3.sel, (float*)(ws + pd.off_okg), lse_kg, s, pm, &sh);
     if (e == hipSuccess) e = finish_sel(st3, pd, s);
   }
   if (e == hipSuccess) e = pm.mark(launch_unfold_values(fa, p.fold_kg_empty != 0, s));

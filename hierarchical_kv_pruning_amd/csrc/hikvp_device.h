@@ -230,7 +230,9 @@ __device__ inline int build_candidates(const int32_t* parents, int Kp, const int
 }
 
 // Candidate slot -> global node index.  np < 0: the slot is the node (roots).
+// Entries of a select are the slots themselves (in candidate order).
 struct SlotMap {
+  static constexpr bool kOrdered = true;   // entry order is candidate order
   const int* pre;
   const int64_t* base;
   int np;
@@ -243,7 +245,43 @@ struct SlotMap {
     }
     return base[lo] + (c - pre[lo]);
   }
+  __device__ int slot(int e) const { return e; }
 };
+
+// Entries of a compacted candidate list: entry e holds candidate slot slots[e]
+// (in no particular order); nodes through the level's slot map.
+struct CompactMap {
+  static constexpr bool kOrdered = false;
+  const int* slots;
+  SlotMap inner;
+  __device__ int64_t operator()(int e) const { return inner(slots[e]); }
+  __device__ int slot(int e) const { return slots[e]; }
+};
+
+// Reductions and scans within each 16-lane DPP row (every lane of the row
+// gets the result; rows are independent).
+__device__ inline uint32_t row_max_u(uint32_t x) {
+  x = max(x, (uint32_t)dpp_i<0xB1>((int)x, (int)x));
+  x = max(x, (uint32_t)dpp_i<0x4E>((int)x, (int)x));
+  x = max(x, (uint32_t)dpp_i<0x141>((int)x, (int)x));
+  x = max(x, (uint32_t)dpp_i<0x140>((int)x, (int)x));
+  return x;
+}
+__device__ inline int row_sum_i(int x) {
+  x += dpp_i<0xB1>(x, x);
+  x += dpp_i<0x4E>(x, x);
+  x += dpp_i<0x141>(x, x);
+  x += dpp_i<0x140>(x, x);
+  return x;
+}
+// Inclusive prefix sum within each 16-lane row (lane order).
+__device__ inline int row_incl_sum(int x) {
+  x += dpp_i<0x111>(0, x);
+  x += dpp_i<0x112>(0, x);
+  x += dpp_i<0x114>(0, x);
+  x += dpp_i<0x118>(0, x);
+  return x;
+}
 
 // ---------------------------------------------------------------------------
 // MFMA 16x16 tiles
@@ -474,14 +512,28 @@ struct RegScores {
 // Returns the count selected (min(K, n)); out_node/out_logit hold the
 // selection sorted by candidate slot.  All NT threads must call it; S.qrow
 // must hold the KG query row.
-template <class E, int D, int NT, class Src, bool kShortLists = false>
+// The KG query row S.qrow is read only by the exact re-score of the band;
+// a caller that has not staged it passes a QLoad that stages it (all NT
+// threads call it, at most once, before the first re-score).
+struct QueryStaged {
+  __device__ void operator()() const {}
+};
+
+template <class E, int D, int NT, class Src, bool kShortLists = false, class Map = SlotMap,
+          class QLoad = QueryStaged>
 __device__ int select_topk(const Src& src, int n, int K, double err2, double scale,
-                           const SlotMap& map, const KeyRows& kr, const SelWork& S,
-                           int* out_node, float* out_logit, int tid) {
+                           const Map& map, const KeyRows& kr, const SelWork& S,
+                           int* out_node, float* out_logit, int tid, const QLoad& qload = QLoad{}) {
   if (K >= n) {
     src.each(n, tid, [&](int i, float f) {
-      out_node[i] = (int)map(i);
-      out_logit[i] = (float)(scale * (double)f);
+      int r = i;
+      if constexpr (!Map::kOrdered) {  // output in candidate order
+        const int si = map.slot(i);
+        r = 0;
+        for (int j = 0; j < n; ++j) r += map.slot(j) < si ? 1 : 0;
+      }
+      out_node[r] = (int)map(i);
+      out_logit[r] = (float)(scale * (double)f);
     });
     group_sync<NT>();
     return n;
@@ -656,6 +708,7 @@ __device__ int select_topk(const Src& src, int n, int K, double err2, double sca
   } else if (nband <= kBand) {
     // 3) exact logits of the band, then the top `need` by (logit desc, index asc)
     for (int i = tid; i < nband; i += NT) S.band_node[i] = (int)map(S.band_slot[i]);
+    qload();
     group_sync<NT>();
     exact_rescore<E, D, NT>(S, nband, kr, scale, tid);
     for (int i = tid; i < nband; i += NT) {
@@ -672,6 +725,7 @@ __device__ int select_topk(const Src& src, int n, int K, double err2, double sca
   } else {
     // 3') a wide band (many near-equal scores): sweep the candidates in
     //     chunks, keeping the best `need` exact logits seen so far
+    qload();
     int nbest = 0;
     for (int c0 = 0; c0 < n; c0 += kBand) {
       if (tid == 0) S.ctl[4] = 0;
@@ -724,10 +778,10 @@ __device__ int select_topk(const Src& src, int n, int K, double err2, double sca
 
   // 4) output sorted by candidate slot (deterministic order)
   for (int i = tid; i < K; i += NT) {
-    const int s = S.sel_slot[i];
+    const int s = map.slot(S.sel_slot[i]);
     int r = 0;
-    for (int j = 0; j < K; ++j) r += S.sel_slot[j] < s ? 1 : 0;
-    out_node[r] = (int)map(s);
+    for (int j = 0; j < K; ++j) r += map.slot(S.sel_slot[j]) < s ? 1 : 0;
+    out_node[r] = (int)map(S.sel_slot[i]);
     out_logit[r] = S.sel_logit[i];
   }
   group_sync<NT>();

@@ -10,9 +10,11 @@ constexpr int kMaxK = 256;        // largest Top-K per level
 constexpr int kMaxD = 128;        // largest head dim
 constexpr int kBucketSlots = 32;  // members of a (head, mid) bucket stored without a list walk
 constexpr int kJunkSlots = 1024;  // per-wave sinks for masked-off score stores
-constexpr int kRootTile = 32;     // member rows per mid-GEMM work item (two 16-row MFMA halves)
+constexpr int kRootTile = 64;     // member rows per mid-GEMM work item (four waves of 16 rows)
 constexpr int kRootSub = 16;      // counters per (head, root) group, picked by token
 constexpr int kDescSub = 64;      // bucket descriptor sub-lists, picked by link chunk
+constexpr int kFilterK = 32;      // largest K_I the mid tiles filter their scores for (else all are kept)
+constexpr int64_t kMaxMidCands = (int64_t)1 << 24;  // mid candidates per row (slot bases pack in 24 bits)
 constexpr int kMaxParts = 2;      // descent parts (KV-head ranges run concurrently)
 constexpr int kDtypeF32 = 0;
 
@@ -75,9 +77,14 @@ struct StepArgs {
   int g0, g1;                 // KV heads of this part
   int blk0, blk1;             // row blocks of this part
   int K[3];                   // Top-K per level (plan-clamped; a row takes min(K, its candidates))
-  int64_t c1max;              // mid candidates per row: capacity and row stride of mid_scores
+  int64_t c1max;              // mid candidates per row: capacity and row stride of mid_pairs
   int64_t c2max;              // leaf candidates per row: capacity
-  float* mid_scores;          // [R, c1max] unscaled fp32 mid scores, candidate order
+  uint2* mid_pairs;           // [R, c1max] surviving mid candidates: (unscaled fp32 score bits, child
+                              // index within its root's span), those of the row's k-th selected root
+                              // from slot pre[k] on; the row's first 2*c1max floats also carry the
+                              // root scores between the root kernels
+  int4* mid_meta;             // [R, K[0]] per (row, selected root): survivors, first candidate slot,
+                              // first child (mid index), the row's |q_kg| bound (fp32 bits)
   float* leaf_scores;         // [R, c2max] unscaled fp32 leaf scores, candidate order
   int32_t* sel[3];            // [R, K[i]] selected node indices, candidate order, -1 padded
   int32_t* mid_base;          // [R, K[1]] first leaf-candidate slot of each selected mid
@@ -88,7 +95,7 @@ struct StepArgs {
   int32_t* root_tile_off;     // [Hkv * M_R] first work item (tile) of each group
   int32_t* root_tile_key;     // [root_tiles_max] group (key g*M_R + root) of each tile
   int32_t* root_ntiles;       // [1] tiles in use
-  int2* root_members;         // [root_tiles_max * kRootTile] (row, first mid slot)
+  int2* root_members;         // [root_tiles_max * kRootTile] (row, first mid slot | selection index << 24)
   int64_t root_tiles_max;     // rows*K[0]/kRootTile + heads*M_R + 1 (rows, heads of the part)
   // (head, mid) bucket arrays are indexed by bucket_index(key) (below), which
   // spreads neighbouring mids (siblings, selected together) over cache lines

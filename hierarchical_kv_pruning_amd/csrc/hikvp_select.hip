@@ -95,13 +95,19 @@ __device__ inline double load_query(const RowsDev& r, int b, int n, int h, float
   return sqrt((double)qq) * 1.0001;
 }
 
+// The root scores of a row, between k_root_mfma and k_root: the first M_R
+// floats of the row's mid-candidate region (c1max >= M_R pairs).
+__device__ inline float* root_score_row(const StepArgs& a, int row) {
+  return (float*)(a.mid_pairs + (int64_t)row * a.c1max);
+}
+
 // Root scores on MFMA: one wave per 16 consecutive rows of one KV head and
 // kRootChunk of its roots (the rows are the M side, 16 roots the N side of
 // each 16x16 tile, the chunk's tiles loaded at once), so a root key is read
 // once per 16 rows instead of once per row.  The raw dot products (the
-// select applies the scale) land in each row's slots of the mid-score buffer
-// (indexed by row, like the mid level's scores, so concurrent descent parts
-// touch disjoint slots), which k_root reads before the mid level reuses them.
+// select applies the scale) land in each row's mid-candidate region (indexed
+// by row, like the mid level's candidates, so concurrent descent parts touch
+// disjoint rows), which k_root reads before the mid level reuses it.
 constexpr int kRootChunk = 64;  // roots per k_root_mfma wave
 
 template <class E, int D>
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(256) void k_root_mfma(StepArgs a, int tph, int nrc)
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int mv = m0 + 4 * quad + v;
-    dst[v] = mv < per_head ? a.mid_scores + (int64_t)row_of_block(a.r, hb + mv) * a.c1max : nullptr;
+    dst[v] = mv < per_head ? root_score_row(a, row_of_block(a.r, hb + mv)) : nullptr;
   }
   int64_t rsb;
   const char* kb = key_base(a.t, 0, g, rsb, E::kBytes) + quad * 16;
@@ -167,11 +173,11 @@ __global__ __launch_bounds__(256) void k_root(StepArgs a, size_t wave_bytes, int
   const int K = a.K[0];
   RowWork W = carve_rowwork(smem + (size_t)wave * wave_bytes, K, 0, D, stage);
   const int row = row_of_block(a.r, blk);
-  // the row's scores, from k_root_mfma in the row's slots of the mid-score
-  // buffer (by row, as the mid level uses it: concurrent parts own disjoint
-  // rows), staged in LDS when they fit
-  const float* gsc = a.mid_scores + (int64_t)row * a.c1max;
-  float* sc = stage ? W.stage : a.mid_scores + (int64_t)row * a.c1max;
+  // the row's scores, from k_root_mfma in the row's mid-candidate region (by
+  // row, as the mid level uses it: concurrent parts own disjoint rows),
+  // staged in LDS when they fit
+  const float* gsc = root_score_row(a, row);
+  float* sc = stage ? W.stage : root_score_row(a, row);
   int b, n, h;
   decode_row(a.r, row, b, n, h);
   const int g = h / a.r.G;
@@ -261,7 +267,8 @@ __device__ inline int fill_part(const StepArgs& a, bool ok, int64_t e, int row, 
     const int key = ((row % a.r.Hq) / a.r.G) * MR + node;
     const int sub = (row / a.r.Hq) % kRootSub;
     const int rank = atomicAdd(&a.root_cnt[(int64_t)sub * a.t.Hkv * MR + key], 1);
-    a.root_members[(int64_t)a.root_tile_off[key] * kRootTile + rank] = make_int2(row, base);
+    const int k = (int)(e - (int64_t)row * a.K[0]);   // the root's place in the row's selection
+    a.root_members[(int64_t)a.root_tile_off[key] * kRootTile + rank] = make_int2(row, base | (k << 24));
   }
   return carry + __builtin_amdgcn_readlane(incl, 63);
 }
@@ -289,117 +296,264 @@ __global__ void k_root_fill(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// mid level: one wave per tile of kRootTile (32) rows of a (head, root)
-// group, as two 16-row halves.  The rows are the M side and the root's
-// children the N side of 16x16 MFMA tiles; each child fragment loaded serves
-// both halves, so the child span is read once per 32 rows (from L2 after the
-// group's first tile).
+// mid level: one workgroup of kMidWaves waves per tile of kRootTile rows of a
+// (head, root) group, 16 rows a wave.  The root's children are staged 32 at a
+// time in LDS (double-buffered: the next round is loaded while this one is
+// scored), so the child span is read from L2 once per 64 rows; each wave
+// scores its rows (the M side of 16x16 MFMA tiles) against them (the N side).
+//
+// Only candidates that can still be among the row's K_I best are written.
+// The children are scored in chunks of 128; the 16 lanes holding a row each
+// keep the kLaneTop largest scores they have seen, and after each chunk the
+// row's threshold T becomes the K_I-th largest score of the union of those
+// lane lists (a subset of the scores seen, so T never exceeds the K_I-th
+// largest score of the row's whole candidate list).  The chunk keeps its
+// children with f >= T - Wf, Wf being twice the band half-width the select
+// uses: every candidate the select could take -- above its band or inside it
+// -- survives, so the select over the survivors takes exactly what it would
+// take over all candidates.  The survivors of the row's k-th selected root go
+// to the row's pairs from that root's first candidate slot on, as (score
+// bits, child index); mid_meta[row, k] records their count, that slot, the
+// root's first child and the row's query-norm bound.
 // ---------------------------------------------------------------------------
+constexpr int kMidWaves = kRootTile / 16;  // waves per mid workgroup
+constexpr int kLaneTop = 2;                // largest scores each lane keeps per row
+constexpr int kChunkRounds = 4;            // rounds of 32 children between threshold updates
+constexpr int kMidPad = 16;                // LDS row padding (bytes) against bank conflicts
+
+// K-th largest order key of the union of the lane lists top[v][0..kLaneTop)
+// of each row v (the 16 lanes of this lane's DPP row hold the row; 0 = empty
+// entry), 0 while fewer than K keys exist.  Each entry counts the entries
+// greater than it (the lane's others, and every entry of the other 15 lanes
+// through 15 DPP row rotations); the K-th largest is the smallest entry with
+// fewer than K greater.  Branch-free.
+template <int N>
+__device__ inline uint32_t row_ror_n(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x120 + N, 0xf, 0xf, false);
+}
+template <int N>
+__device__ inline void rank_step(const uint32_t (&top)[4][kLaneTop], int (&gt)[4][kLaneTop]) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+#pragma unroll
+    for (int j = 0; j < kLaneTop; ++j) {
+      const uint32_t o = row_ror_n<N>(top[v][j]);
+#pragma unroll
+      for (int i = 0; i < kLaneTop; ++i) gt[v][i] += o > top[v][i] ? 1 : 0;
+    }
+}
+__device__ inline void rows_union_kth(const uint32_t (&top)[4][kLaneTop], int K, uint32_t (&kth)[4]) {
+  int gt[4][kLaneTop];
+#pragma unroll
+  for (int v = 0; v < 4; ++v)
+#pragma unroll
+    for (int i = 0; i < kLaneTop; ++i) {
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < kLaneTop; ++j) c += top[v][j] > top[v][i] ? 1 : 0;
+      gt[v][i] = c;
+    }
+  rank_step<1>(top, gt);  rank_step<2>(top, gt);  rank_step<3>(top, gt);  rank_step<4>(top, gt);
+  rank_step<5>(top, gt);  rank_step<6>(top, gt);  rank_step<7>(top, gt);  rank_step<8>(top, gt);
+  rank_step<9>(top, gt);  rank_step<10>(top, gt); rank_step<11>(top, gt); rank_step<12>(top, gt);
+  rank_step<13>(top, gt); rank_step<14>(top, gt); rank_step<15>(top, gt);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    uint32_t m = 0xffffffffu;
+#pragma unroll
+    for (int i = 0; i < kLaneTop; ++i) m = gt[v][i] < K ? min(m, top[v][i]) : m;
+    kth[v] = ~row_max_u(~m);               // the row's minimum; 0 if an empty entry ranks below K
+  }
+}
+
+// A round's children staged by the workgroup: thread tid's 16-byte pieces
+// p = tid + i*NT, piece p being part p % (RB/16) of child c0 + p / (RB/16)
+// (clamped into the span), loaded to registers then put in LDS rows of LRB.
+// (Native 4 x u32 vectors: copies of the HIP vector struct through a private
+// array were lowered to memcpy through scratch.)
+template <int RB, int NT, int PPT>
+__device__ inline void stage_round(U32x4 (&stg)[PPT], const char* kb, int64_t rsb, int c0, int F, int tid) {
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int p = tid + i * NT, c = p / (RB / 16), o = p % (RB / 16);
+    stg[i] = *(const U32x4*)(kb + (int64_t)min(c0 + c, F - 1) * rsb + o * 16);
+  }
+}
+template <int RB, int LRB, int NT, int PPT>
+__device__ inline void stage_put(const U32x4 (&stg)[PPT], char* buf, int tid) {
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int p = tid + i * NT, c = p / (RB / 16), o = p % (RB / 16);
+    *(U32x4*)(buf + c * LRB + o * 16) = stg[i];
+  }
+}
+
 template <class E, int D>
-__global__ __launch_bounds__(256) void k_mid_gemm(StepArgs a) {
+__global__ __launch_bounds__(64 * kMidWaves) void k_mid_gemm(StepArgs a) {
   constexpr int KCH = D * E::kBytes / 64;  // 16-byte pieces per lane per row
+  constexpr int RB = D * E::kBytes;        // bytes per key row
+  constexpr int LRB = RB + kMidPad;        // LDS bytes per staged child
   constexpr int TU = 2;                    // child tiles per round = consecutive children per lane
-  constexpr int HR = kRootTile / 16;       // 16-row halves per tile
-  static_assert(kRootTile == 32, "two 16-row halves per tile");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+  constexpr int RC = 16 * TU;              // children per round
+  constexpr int CR = kChunkRounds;         // rounds per chunk
+  constexpr int NV = CR * TU;              // keys per lane per row in a chunk
+  constexpr int NT = 64 * kMidWaves;
+  constexpr int PPT = RC * RB / 16 / NT;   // 16-byte pieces each thread stages per round
+  static_assert(PPT >= 1 && RC * RB / 16 == PPT * NT, "a round's children split evenly over the threads");
+  __shared__ __align__(16) char lds[2][RC * LRB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int quad = lane >> 4, col = lane & 15;
-  float* const junk = a.junk + ((blockIdx.x * nwave + wave) % kJunkSlots) * 16;
   const int ntiles = *a.root_ntiles;
   const int MR = (int)a.t.count[0];
+  const int K0 = a.K[0], K1 = a.K[1];
+  const bool filt = K1 <= kFilterK;
   const int64_t* off0 = a.t.off[0];
-  for (int t = blockIdx.x * nwave + wave; t < ntiles; t += gridDim.x * nwave) {
+  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {  // uniform over the workgroup
     const int key = a.root_tile_key[t];
     const int toff = a.root_tile_off[key];
     const int cnt = a.root_tot[key];
     const int g = key / MR, j = key % MR;
     const int64_t first = off0[j];
     const int F = (int)(off0[j + 1] - first);
-    const int m0 = (t - toff) * kRootTile;     // first member of the tile
-    const bool two = m0 + 16 < cnt;            // wave-uniform: the second half has members
-    uint4 afr[HR][KCH];
-    float* dst[HR][4];
-#pragma unroll
-    for (int hh = 0; hh < HR; ++hh) {
-      const int mi = m0 + 16 * hh + col;
-      const int2 mem = mi < cnt ? a.root_members[(int64_t)toff * kRootTile + mi] : make_int2(-1, 0);
-      if (mi < cnt) {
+    const int m0 = (t - toff) * kRootTile + 16 * wave;  // the wave's first member
+    const bool active = m0 < cnt;                       // wave-uniform
+    const float knorm = a.t.norm[a.t.Hkv + g];
+    int64_t rsb;
+    const char* kb = key_base(a.t, 1, g, rsb, E::kBytes) + first * rsb;
+    if (F > 0) {  // round 0 staged
+      U32x4 stg[PPT];
+      stage_round<RB, NT, PPT>(stg, kb, rsb, 0, F, tid);
+      stage_put<RB, LRB, NT, PPT>(stg, lds[0], tid);
+    }
+    // A fragment (members) and this lane's output rows (member 4*quad + v):
+    // row, first slot | selection index << 24 (row -1: none)
+    uint4 afr[KCH];
+    int orow[4], obk[4];
+    float qnv[4], wf[4];                       // query-norm bound, filter margin
+    {
+      const int mi = m0 + col;
+      const int2 mem = active && mi < cnt ? a.root_members[(int64_t)toff * kRootTile + mi] : make_int2(-1, 0);
+      float qq = 0.f;
+      if (mem.x >= 0) {
         int b, n, h;
         decode_row(a.r, mem.x, b, n, h);
         const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes;
 #pragma unroll
-        for (int m = 0; m < KCH; ++m) afr[hh][m] = *(const uint4*)(qp + m * 64 + quad * 16);
+        for (int m = 0; m < KCH; ++m) {
+          afr[m] = *(const uint4*)(qp + m * 64 + quad * 16);
+          float f[E::kEPV];
+          unpack<E>(afr[m], f);
+#pragma unroll
+          for (int e = 0; e < E::kEPV; ++e) qq = fmaf(f[e], f[e], qq);
+        }
       } else {
 #pragma unroll
-        for (int m = 0; m < KCH; ++m) afr[hh][m] = make_uint4(0, 0, 0, 0);
+        for (int m = 0; m < KCH; ++m) afr[m] = make_uint4(0, 0, 0, 0);
       }
-      // Rounds of TU child tiles; in tile u, column col is child c0 + col*TU
-      // + u, so a lane ends the round with TU consecutive scores of each of
-      // its 4 rows (half rows 4*quad + v), written with one 8-byte store.
+      qq += __shfl_xor(qq, 16);
+      qq += __shfl_xor(qq, 32);                // member col's |q|^2 (every quad)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int ms = 4 * quad + v;
-        const int srow = __shfl(mem.x, ms), sbase = __shfl(mem.y, ms);
-        dst[hh][v] = m0 + 16 * hh + ms < cnt ? a.mid_scores + (int64_t)srow * a.c1max + sbase + col * TU : nullptr;
+        orow[v] = __shfl(mem.x, ms);           // -1 past the members
+        obk[v] = __shfl(mem.y, ms);
+        // the row's |q| bound (fp32 sum of squares in any order: 0.1 %
+        // slack) and twice the select's band half-width for it (its error
+        // bound 2E and its slack on T, |T| <= |q| max|k|)
+        qnv[v] = sqrtf(__shfl(qq, ms)) * 1.001f;
+        const float e2 = 2.f * qnv[v] * knorm * (float)D * (1.f / 8388608.f);
+        wf[v] = 2.f * (e2 * 1.01f + 4.f * qnv[v] * knorm * (1.f / 8388608.f)) + 1e-30f;
       }
     }
-    // Loads and stores are unconditional (clamped child, junk slot) and a
-    // round's stores follow the next round's loads, so the wait for the loads
-    // never covers the stores.
-    int64_t rsb;
-    const char* kb = key_base(a.t, 1, g, rsb, E::kBytes) + first * rsb + quad * 16;
-    float4_t prev[HR][TU];
+    uint32_t top[4][kLaneTop], kth[4];
+    int run[4];                                // survivors written per output row
 #pragma unroll
-    for (int hh = 0; hh < HR; ++hh)
+    for (int v = 0; v < 4; ++v) {
+      run[v] = 0;
+      kth[v] = 0;
 #pragma unroll
-      for (int u = 0; u < TU; ++u) prev[hh][u] = float4_t{0.f, 0.f, 0.f, 0.f};
-    int pc0 = -1;
-    auto load_round = [&](int c0, uint4 (&bfr)[TU][KCH]) {
-#pragma unroll
-      for (int u = 0; u < TU; ++u) {
-        const char* kp = kb + (int64_t)min(c0 + col * TU + u, F - 1) * rsb;
-#pragma unroll
-        for (int m = 0; m < KCH; ++m) bfr[u][m] = *(const uint4*)(kp + m * 64);
-      }
-    };
-    auto store_full = [&]() {
-#pragma unroll
-      for (int hh = 0; hh < HR; ++hh)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          store2u((pc0 >= 0 && dst[hh][v]) ? dst[hh][v] + pc0 : junk, prev[hh][0][v], prev[hh][1][v]);
-    };
-    auto compute = [&](const uint4 (&bfr)[TU][KCH]) {
-#pragma unroll
-      for (int u = 0; u < TU; ++u) prev[0][u] = tile_dot<E, KCH>(afr[0], bfr[u]);
-      if (two) {
-#pragma unroll
-        for (int u = 0; u < TU; ++u) prev[1][u] = tile_dot<E, KCH>(afr[1], bfr[u]);
-      }
-    };
-    int c0 = 0;
-    for (; c0 + 16 * TU <= F; c0 += 16 * TU) {
-      uint4 bfr[TU][KCH];
-      load_round(c0, bfr);
-      store_full();
-      compute(bfr);
-      pc0 = c0;
+      for (int i = 0; i < kLaneTop; ++i) top[v][i] = 0;
     }
-    if (c0 < F) {  // last, partial round
-      uint4 bfr[TU][KCH];
-      load_round(c0, bfr);
-      store_full();
-      compute(bfr);
-      const int cl = c0 + col * TU;
+    __syncthreads();                           // round 0 staged
+    const int nr = (F + RC - 1) / RC;
+    for (int cc = 0; cc < nr; cc += CR) {      // chunks of CR rounds
+      uint32_t x[4][NV];                       // the chunk's keys (0: past the span)
 #pragma unroll
-      for (int hh = 0; hh < HR; ++hh)
+      for (int r = 0; r < CR; ++r) {
+        const int rr = cc + r;
+        if (rr < nr) {                         // uniform over the workgroup
+          const bool more = rr + 1 < nr;
+          U32x4 stg[PPT];                      // the next round, in flight while this one is scored
+          if (more) stage_round<RB, NT, PPT>(stg, kb, rsb, (rr + 1) * RC, F, tid);
+          if (active) {
+            // in tile u, lane column col is child rr*RC + col*TU + u
+            const char* lb = lds[rr & 1] + quad * 16;
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+            for (int u = 0; u < TU; ++u) {
+              uint4 bfr[KCH];
+#pragma unroll
+              for (int m = 0; m < KCH; ++m) bfr[m] = *(const uint4*)(lb + (col * TU + u) * LRB + m * 64);
+              const float4_t p = tile_dot<E, KCH>(afr, bfr);
+              const bool valid = rr * RC + col * TU + u < F;
+#pragma unroll
+              for (int v = 0; v < 4; ++v) x[v][r * TU + u] = valid ? ord_key(p[v]) : 0u;
+            }
+          }
+          if (more) stage_put<RB, LRB, NT, PPT>(stg, lds[(rr + 1) & 1], tid);
+          __syncthreads();
+        } else {
 #pragma unroll
           for (int u = 0; u < TU; ++u)
-            if (dst[hh][v] && cl + u < F) dst[hh][v][c0 + u] = prev[hh][u][v];
-    } else {
-      store_full();
+#pragma unroll
+            for (int v = 0; v < 4; ++v) x[v][r * TU + u] = 0u;
+        }
+      }
+      if (!active) continue;
+      uint32_t lo[4] = {0u, 0u, 0u, 0u};       // keep every valid child
+      if (filt) {
+        // the lane lists take the new keys, then the row threshold moves up
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int q = 0; q < NV; ++q) {
+            uint32_t y = x[v][q];
+#pragma unroll
+            for (int i = 0; i < kLaneTop; ++i) {
+              const uint32_t hi = max(y, top[v][i]);
+              y = min(y, top[v][i]);
+              top[v][i] = hi;
+            }
+          }
+        rows_union_kth(top, K1, kth);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (kth[v]) lo[v] = ord_key(ord_float(kth[v]) - wf[v]);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        int nk = 0;
+#pragma unroll
+        for (int q = 0; q < NV; ++q) nk += (x[v][q] != 0u && x[v][q] >= lo[v]) ? 1 : 0;
+        const int incl = row_incl_sum(nk);
+        if (orow[v] >= 0) {
+          uint2* d = a.mid_pairs + (int64_t)orow[v] * a.c1max + (obk[v] & 0xffffff);
+          int pos = run[v] + incl - nk;
+#pragma unroll
+          for (int q = 0; q < NV; ++q)
+            if (x[v][q] != 0u && x[v][q] >= lo[v])
+              d[pos++] = make_uint2(__float_as_uint(ord_float(x[v][q])),
+                                    (uint32_t)(cc * RC + RC * (q / TU) + col * TU + (q % TU)));
+        }
+        run[v] += __shfl(incl, (lane & 48) | 15);   // the row's total: the DPP row's last lane
+      }
     }
+    if (active && col == 0)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (orow[v] >= 0)
+          a.mid_meta[(int64_t)orow[v] * K0 + (int)((uint32_t)obk[v] >> 24)] =
+              make_int4(run[v], obk[v] & 0xffffff, (int)first, (int)__float_as_uint(qnv[v]));
+    __syncthreads();                           // the staging buffers are free for the next tile
   }
 }
 
@@ -469,37 +623,180 @@ struct RowScores<NT, 0> {
   __device__ static inline type make(const float* p, int, int) { return type{p}; }
 };
 
-template <class E, int D, int NT, int SPT>
-__device__ inline void mid_select_body(const StepArgs& a, size_t group_bytes) {
-  extern __shared__ __align__(16) char smem[];
-  const int groups = blockDim.x / NT, grp = threadIdx.x / NT, gtid = threadIdx.x % NT;
-  const int blk = a.blk0 + blockIdx.x * groups + grp;
-  if (blk >= a.blk1) return;  // whole group (whole waves) leaves together
-  const int K1 = a.K[1];
-  RowWork W = carve_rowwork(smem + (size_t)grp * group_bytes, K1, a.K[0], D, 0, NT);
-  const int row = row_of_block(a.r, blk);
-  const int p0 = first_parent(a, row, 1, gtid);
-  // the scores do not depend on the candidate list: load them next
-  const auto sc = RowScores<NT, SPT>::make(a.mid_scores + (int64_t)row * a.c1max, (int)a.c1max, gtid);
-  int g;
-  double qnorm;
-  const int n1 = select_prologue<E, D, NT>(a, W, row, 1, g, qnorm, gtid, p0);
-  int64_t rsb;
-  const char* kb = key_base(a.t, 1, g, rsb, E::kBytes);
-  const int k1 = select_topk<E, D, NT>(sc, n1, K1,
-                                       twice_err_bound<D>(qnorm, a.t.norm[a.t.Hkv + g]), a.r.scale,
-                                       SlotMap{W.pre, W.base, a.K[0]}, KeyRows{kb, rsb}, W.sel,
-                                       W.out_node, W.out_logit, gtid);
-  int32_t* o1 = a.sel[1] + (int64_t)row * K1;
-  for (int i = gtid; i < K1; i += NT) o1[i] = i < k1 ? W.out_node[i] : -1;
+// Mid-level Top-K over the row's surviving candidates (k_mid_gemm): entry e
+// is the e-th survivor in (selected root k, position) order; its candidate
+// slot is pre[k] + j and its node base[k] + j, for the child index j stored
+// with its score.
+struct MidEntries {
+  const uint2* pairs;         // the row's mid-candidate region
+  const int* cpre;            // [K0 + 1] first entry of each selected root's survivors (LDS)
+  const int* pre;             // [K0 + 1] first candidate slot of each selected root (LDS)
+  const int64_t* base;        // [K0] first child node of each selected root (LDS)
+  int K0;
+  __device__ inline int root_of(int e) const {  // the k with cpre[k] <= e < cpre[k + 1]
+    int lo = 0, hi = K0 - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cpre[mid] <= e) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  }
+  __device__ inline uint2 pair(int e, int& k) const {
+    k = root_of(e);
+    return pairs[pre[k] + (e - cpre[k])];
+  }
+};
+
+// Up to 64 * SPT entries loaded once: scores in registers, (k, j) packed in LDS.
+template <int SPT>
+struct MidRegScores {
+  float v[SPT];
+  MidEntries m;
+  template <class F>
+  __device__ inline void each(int n, int tid, F&& f) const {
+#pragma unroll
+    for (int k = 0; k < SPT; ++k)
+      if (k * 64 + tid < n) f(k * 64 + tid, v[k]);
+  }
+  __device__ inline float at(int e) const {
+    int k;
+    return __uint_as_float(m.pair(e, k).x);
+  }
+};
+struct MidRegMap {
+  static constexpr bool kOrdered = false;
+  const int* kj;              // [n] (k << 24) | j per entry (LDS)
+  const int* pre;
+  const int64_t* base;
+  __device__ int64_t operator()(int e) const { return base[(uint32_t)kj[e] >> 24] + (kj[e] & 0xffffff); }
+  __device__ int slot(int e) const { return pre[(uint32_t)kj[e] >> 24] + (kj[e] & 0xffffff); }
+};
+
+// Longer lists: every pass reads the entries from the workspace.
+struct MidMemScores {
+  MidEntries m;
+  template <class F>
+  __device__ inline void each(int n, int tid, F&& f) const {
+    for (int e = tid; e < n; e += 64) {
+      int k;
+      f(e, __uint_as_float(m.pair(e, k).x));
+    }
+  }
+  __device__ inline float at(int e) const {
+    int k;
+    return __uint_as_float(m.pair(e, k).x);
+  }
+};
+struct MidMemMap {
+  static constexpr bool kOrdered = false;
+  MidEntries m;
+  __device__ int64_t operator()(int e) const {
+    int k;
+    const uint2 p = m.pair(e, k);
+    return m.base[k] + p.y;
+  }
+  __device__ int slot(int e) const {
+    int k;
+    const uint2 p = m.pair(e, k);
+    return m.pre[k] + (int)p.y;
+  }
+};
+
+// LDS of one k_mid_select wave: the select's work area, cpre, (k, j) of the
+// register-held entries.
+__host__ __device__ inline size_t mid_select_wave_bytes(int K1, int K0, int D, int SPT) {
+  return rowwork_bytes(K1, K0, D, 0) + align16((size_t)(K0 + 1) * 4) + align16((size_t)64 * SPT * 4);
 }
 
-// One wave per row (short candidate lists) or one workgroup per row; the
-// scores are held in registers (SPT per thread, sized to the list at launch)
-// or re-read from the workspace in every pass (SPT = 0, long lists).
-template <class E, int D, int NT, int SPT>
-__global__ __launch_bounds__(256) void k_mid_select(StepArgs a, size_t gb) {
-  mid_select_body<E, D, NT, SPT>(a, gb);
+// Stages the row's KG query in the select's work area (exact fp32 copy), for
+// the exact re-score of a band, which needs it.
+template <class E, int D>
+struct StageQuery {
+  const char* qp;
+  float* qrow;
+  int lane;
+  __device__ void operator()() const {
+    for (int t = lane; t < D; t += 64) qrow[t] = load_f32<E>(qp, t);
+    wave_sync();
+  }
+};
+
+// One wave per row: the row's survivors from mid_meta (no parent or offset
+// lookups: the mid tiles recorded each selected root's first slot and first
+// child), Top-K_I over them.
+template <class E, int D, int SPT>
+__device__ inline void mid_select_row(StepArgs a, size_t wave_bytes) {
+  extern __shared__ __align__(16) char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+  const int blk = a.blk0 + blockIdx.x * nwave + wave;
+  if (blk >= a.blk1) return;  // whole wave; waves never meet at a barrier
+  const int K0 = a.K[0], K1 = a.K[1];
+  char* p = smem + (size_t)wave * wave_bytes;
+  RowWork W = carve_rowwork(p, K1, K0, D, 0);
+  p += rowwork_bytes(K1, K0, D, 0);
+  int* cpre = (int*)p;
+  p += align16((size_t)(K0 + 1) * 4);
+  int* kj = (int*)p;
+  const int row = row_of_block(a.r, blk);
+  int b, n, h;
+  decode_row(a.r, row, b, n, h);
+  const int g = h / a.r.G;
+  // survivors, first slot and first child of each selected root
+  int carry = 0;
+  float qn = 0.f;
+  if (lane == 0) cpre[0] = 0;
+  for (int k0 = 0; k0 < K0; k0 += 64) {
+    const int k = k0 + lane;
+    const int4 m = k < K0 ? a.mid_meta[(int64_t)row * K0 + k] : make_int4(0, 0, 0, 0);
+    if (k < K0) {
+      W.pre[k] = m.y;
+      W.base[k] = m.z;
+    }
+    if (k0 == 0) qn = __int_as_float(__builtin_amdgcn_readlane(m.w, 0));
+    const int incl = wave_incl_sum(m.x);
+    if (k < K0) cpre[k + 1] = carry + incl;
+    carry += __builtin_amdgcn_readlane(incl, 63);
+  }
+  wave_sync();
+  const int cnt = carry;
+  const MidEntries me{a.mid_pairs + (int64_t)row * a.c1max, cpre, W.pre, W.base, K0};
+  int64_t rsb;
+  const char* kb = key_base(a.t, 1, g, rsb, E::kBytes);
+  const double err2 = twice_err_bound<D>((double)qn, a.t.norm[a.t.Hkv + g]);
+  const StageQuery<E, D> ql{(const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes, W.sel.qrow, lane};
+  int k1;
+  if (cnt <= 64 * SPT) {
+    MidRegScores<SPT> src;
+    src.m = me;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int e = i * 64 + lane;
+      src.v[i] = 0.f;
+      if (e < cnt) {
+        int k;
+        const uint2 pr = me.pair(e, k);
+        src.v[i] = __uint_as_float(pr.x);
+        kj[e] = (k << 24) | (int)pr.y;
+      }
+    }
+    wave_sync();
+    k1 = select_topk<E, D, 64, MidRegScores<SPT>, true, MidRegMap, StageQuery<E, D>>(
+        src, cnt, K1, err2, a.r.scale, MidRegMap{kj, W.pre, W.base}, KeyRows{kb, rsb}, W.sel, W.out_node,
+        W.out_logit, lane, ql);
+  } else {
+    k1 = select_topk<E, D, 64, MidMemScores, false, MidMemMap, StageQuery<E, D>>(
+        MidMemScores{me}, cnt, K1, err2, a.r.scale, MidMemMap{me}, KeyRows{kb, rsb}, W.sel, W.out_node,
+        W.out_logit, lane, ql);
+  }
+  int32_t* o1 = a.sel[1] + (int64_t)row * K1;
+  for (int i = lane; i < K1; i += 64) o1[i] = i < k1 ? W.out_node[i] : -1;
+}
+
+constexpr int kMidSelectSPT = 16;   // survivors a lane holds in registers (1024 a row)
+
+template <class E, int D>
+__global__ __launch_bounds__(256) void k_mid_select(StepArgs a, size_t wave_bytes) {
+  mid_select_row<E, D, kMidSelectSPT>(a, wave_bytes);
 }
 
 // ---------------------------------------------------------------------------
@@ -967,15 +1264,21 @@ hipError_t launch_root_groups(const StepArgs& a, hipStream_t s) {
 
 hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s) {
   if (a.blk1 <= a.blk0 || a.t.count[0] <= 0 || a.K[0] <= 0) return hipSuccess;
-  int64_t blocks = (a.root_tiles_max + 3) / 4;
-  if (blocks > 4096) blocks = 4096;
-  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_mid_gemm, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  int64_t blocks = a.root_tiles_max;       // one workgroup per tile (grid-stride past 8192)
+  if (blocks > 8192) blocks = 8192;
+  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_mid_gemm, dim3((unsigned)blocks), dim3(64 * kMidWaves), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_mid_select(const StepArgs& a, hipStream_t s) {
   if (a.blk1 <= a.blk0) return hipSuccess;
-  HIKVP_SELECT_LAUNCH(a, a.c1max, k_mid_select, a.K[1], a.K[0], s);
+  // one wave per row; up to 1024 surviving candidates held in registers
+  const size_t wb = mid_select_wave_bytes(a.K[1], a.K[0], a.t.d, kMidSelectSPT);
+  int wpb = 4;
+  while (wpb > 1 && wb * wpb > 64 * 1024) --wpb;
+  if (wb * wpb > 64 * 1024) return hipErrorInvalidValue;
+  const unsigned blocks = (unsigned)((a.blk1 - a.blk0 + wpb - 1) / wpb);
+  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_mid_select, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb);
   return hipGetLastError();
 }
 
