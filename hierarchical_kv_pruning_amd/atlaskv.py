@@ -32,7 +32,7 @@ EXPORTS = ["atlaskv_build_tree_view", "atlaskv_destroy_tree_view", "atlaskv_tree
            "atlaskv_shared_attend_ex", "atlaskv_shared_check_args", "atlaskv_shared_phase_count",
            "atlaskv_shared_phase_name", "atlaskv_folded_workspace_size", "atlaskv_folded_attend_ex",
            "atlaskv_folded_check_args", "atlaskv_folded_phase_count", "atlaskv_folded_phase_name",
-           "atlaskv_phase_count",
+           "atlaskv_hikvp_attend_noalloc", "atlaskv_phase_count", "atlaskv_noalloc_scratch_bytes",
            "atlaskv_phase_name", "atlaskv_last_error", "atlaskv_version"]
 
 
@@ -79,6 +79,9 @@ def lib():
         L.atlaskv_hikvp_workspace_size.argtypes = [ctypes.c_void_p, T, T, i32x3, P(ctypes.c_size_t)]
         L.atlaskv_hikvp_attend.argtypes = [T, ctypes.c_void_p, T, T, i32x3, T]
         L.atlaskv_hikvp_attend_ex.argtypes = [T, ctypes.c_void_p, T, T, i32x3, T, P(AttendOpts)]
+        L.atlaskv_hikvp_attend_noalloc.argtypes = [T, ctypes.c_void_p, T, T, i32x3, T, P(AttendOpts)]
+        L.atlaskv_noalloc_scratch_bytes.argtypes = []
+        L.atlaskv_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.atlaskv_check_args.argtypes = [T, ctypes.c_void_p, T, T, i32x3, T, P(AttendOpts)]
         L.atlaskv_tree_view_describe.argtypes = [T, T, T, T, ctypes.c_int64, ctypes.c_int64,
                                                  P(ctypes.c_void_p)]
@@ -277,6 +280,21 @@ def hikvp_attend_ex(q, tree, seq_k, seq_v, K, out, **opts):
                                          ctypes.byref(do), ctypes.byref(o)))
     del keep
     return out
+
+
+def hikvp_attend_noalloc(q, tree, seq_k, seq_v, K, out, **opts):
+    """atlaskv_hikvp_attend_noalloc: the library's fixed device workspace (no
+    allocation); keyword options as in atlaskv_attend_opts, except workspace."""
+    dq, dk, dv, do = describe(q), describe(seq_k), describe(seq_v), describe(out)
+    o, keep = _opts(device=q.device, **opts)
+    _raise(lib().atlaskv_hikvp_attend_noalloc(ctypes.byref(dq), tree.handle, _ref(dk), _ref(dv), _k(K),
+                                              ctypes.byref(do), ctypes.byref(o)))
+    del keep
+    return out
+
+
+def noalloc_scratch_bytes():
+    return int(lib().atlaskv_noalloc_scratch_bytes())
 
 
 def check_args(q, tree, seq_k, seq_v, K, out, **opts):

@@ -790,6 +790,34 @@ hipError_t launch_descent(const Plan& p, const RowsDev& rows, atlaskv_tree_view_
   return e;
 }
 
+// Workspace of atlaskv_hikvp_attend_noalloc: a device array of fixed size,
+// one copy per GPU the library runs on, held until the process ends.  Host
+// code must use its device address (hipGetSymbolAddress, per device), never
+// the array's name, which names a host-side stand-in.
+constexpr size_t kNoAllocScratchBytes = (size_t)256 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device (NULL: not yet)
+
+// The current device's scratch address, looked up once per device.
+atlaskv_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATLASKV_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e == hipSuccess ? hipErrorInvalidSymbol : e, "hipGetSymbolAddress");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATLASKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -995,6 +1023,30 @@ atlaskv_status atlaskv_hikvp_attend(const atlaskv_tensor* q, atlaskv_tree_view v
                                     const int32_t K[3], atlaskv_tensor* out) {
   return atlaskv_hikvp_attend_ex(q, v, seq_k, seq_v, K, out, nullptr);
 }
+
+atlaskv_status atlaskv_hikvp_attend_noalloc(const atlaskv_tensor* q, atlaskv_tree_view v,
+                                            const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                            const int32_t K[3], atlaskv_tensor* out,
+                                            const atlaskv_attend_opts* opts) {
+  if (opts && opts->workspace)
+    return fail(ATLASKV_ERR_WORKSPACE, "the no-allocation entry point uses its own fixed workspace");
+  Plan p;
+  void* wsv = nullptr;
+  atlaskv_attend_opts o;
+  memset(&o, 0, sizeof o);
+  if (opts) o = *opts;
+  o.workspace = (void*)(uintptr_t)256;     // a stand-in: the checks read only its size and alignment
+  o.workspace_bytes = kNoAllocScratchBytes;
+  atlaskv_status st = check_all(q, v, seq_k, seq_v, K, out, &o, p, &wsv);
+  if (st == ATLASKV_ERR_WORKSPACE)
+    return fail(ATLASKV_ERR_WORKSPACE, "the call needs %zu workspace bytes; the fixed scratch holds %zu",
+                p.total, kNoAllocScratchBytes);
+  if (st) return st;
+  if ((st = scratch_address(&o.workspace))) return st;
+  return atlaskv_hikvp_attend_ex(q, v, seq_k, seq_v, K, out, &o);
+}
+
+size_t atlaskv_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 static const char* const kSharedPhaseNames[] = {
     "group_query", "root_score_topk", "mid_bucket_gemm", "mid_topk", "leaf_bucket_link",

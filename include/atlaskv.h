@@ -204,6 +204,28 @@ atlaskv_status atlaskv_hikvp_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vie
                                        const int32_t K_per_level[3], atlaskv_tensor* out,
                                        const atlaskv_attend_opts* opts);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): as
+ * atlaskv_hikvp_attend_ex, but the workspace is a fixed device array inside
+ * the library -- one per GPU, atlaskv_noalloc_scratch_bytes() bytes (256 MiB),
+ * held until the process ends -- so the call performs no allocation of any
+ * kind.  opts->workspace must be NULL (ATLASKV_ERR_WORKSPACE otherwise); a
+ * call whose workspace would exceed the array fails with
+ * ATLASKV_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU
+ * shares that GPU's array and leaves its contents behind (each call
+ * initialises what it reads), so calls that overlap in time on one GPU --
+ * on different streams or host threads -- race and must be serialised by the
+ * caller.  Results equal atlaskv_hikvp_attend_ex's bit for bit.
+ */
+atlaskv_status atlaskv_hikvp_attend_noalloc(const atlaskv_tensor* q, atlaskv_tree_view tree,
+                                            const atlaskv_tensor* seq_k, const atlaskv_tensor* seq_v,
+                                            const int32_t K_per_level[3], atlaskv_tensor* out,
+                                            const atlaskv_attend_opts* opts);
+
+/* Size in bytes of the fixed workspace of atlaskv_hikvp_attend_noalloc. */
+size_t atlaskv_noalloc_scratch_bytes(void);
+
 /* The argument checks of atlaskv_hikvp_attend_ex alone: pure host code, no
  * HIP call, nothing enqueued.  tree may describe shapes only (see
  * atlaskv_tree_view_describe). */
