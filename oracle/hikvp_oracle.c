@@ -38,6 +38,15 @@ static double dot(const void* a, int64_t a0, const void* b, int64_t b0,
   return acc;
 }
 
+/* The same with the two operands in their own storage types (an fp64 query
+ * against keys of the problem's storage type). */
+static double dot2(const void* a, int adt, int64_t a0, const void* b, int bdt, int64_t b0,
+                   int64_t d) {
+  double acc = 0.0;
+  for (int64_t t = 0; t < d; ++t) acc += load(a, adt, a0 + t) * load(b, bdt, b0 + t);
+  return acc;
+}
+
 /* ---- level sizes (方法细节 › KGKVs的层次化聚类) --------------------------- */
 
 typedef unsigned __int128 u128;
@@ -122,6 +131,14 @@ static int64_t q_base(const oracle_problem* P, int64_t b, int64_t n, int64_t h) 
 
 static const void* kg_query(const oracle_problem* P) { return P->q_kg ? P->q_kg : P->q; }
 
+/* storage type of the KG query: fp64 when q_kg is given as an exact query */
+static int kg_dtype(const oracle_problem* P) { return (P->q_kg && P->q_kg_f64) ? ORACLE_F64 : P->dtype; }
+
+/* scale * <KG query of the row at qb, key row at kb of `keys`> */
+static double kg_score(const oracle_problem* P, int64_t qb, const void* keys, int64_t kb) {
+  return P->scale * dot2(kg_query(P), kg_dtype(P), qb, keys, P->dtype, kb, P->d);
+}
+
 int64_t oracle_level_scores(const oracle_problem* P, int64_t b, int64_t n,
                             int64_t h, int level, const int64_t* parents,
                             int64_t n_parents, int64_t* cand, double* score,
@@ -129,14 +146,13 @@ int64_t oracle_level_scores(const oracle_problem* P, int64_t b, int64_t n,
   const int64_t d = P->d;
   const int64_t g = h / (P->Hq / P->Hkv);
   const int64_t qb = q_base(P, b, n, h);
-  const void* qk = kg_query(P);
   int64_t cnt = 0;
   if (level == 0) {
     /* the current query against every root key */
     for (int64_t j = 0; j < P->M_R; ++j) {
       if (cnt >= cap) return -1;
       cand[cnt] = j;
-      score[cnt] = P->scale * dot(qk, qb, P->root_k, (g * P->M_R + j) * d, P->dtype, d);
+      score[cnt] = kg_score(P, qb, P->root_k, (g * P->M_R + j) * d);
       ++cnt;
     }
     return cnt;
@@ -151,7 +167,7 @@ int64_t oracle_level_scores(const oracle_problem* P, int64_t b, int64_t n,
     for (int64_t c = off[par]; c < off[par + 1]; ++c) {
       if (cnt >= cap) return -1;
       cand[cnt] = c;
-      score[cnt] = P->scale * dot(qk, qb, keys, (g * level_size + c) * d, P->dtype, d);
+      score[cnt] = kg_score(P, qb, keys, (g * level_size + c) * d);
       ++cnt;
     }
   }
@@ -164,9 +180,8 @@ int oracle_candidate_scores(const oracle_problem* P, int64_t b, int64_t n,
   if (!P || nc < 0 || (nc > 0 && (!cand_k || !score))) return -1;
   const int64_t d = P->d;
   const int64_t qb = q_base(P, b, n, h);
-  const void* qk = kg_query(P);
   for (int64_t i = 0; i < nc; ++i)
-    score[i] = P->scale * dot(qk, qb, cand_k, i * d, P->dtype, d);
+    score[i] = kg_score(P, qb, cand_k, i * d);
   return 0;
 }
 
@@ -330,10 +345,8 @@ static int leaf_and_finish(const oracle_problem* P, int64_t b, int64_t n, int64_
                            int64_t nc, const int64_t* cidx, const void* const* krow,
                            const int64_t* koff, const void* const* vrow, const int64_t* voff,
                            const int64_t* forced, int64_t r, const oracle_outputs* O) {
-  const int64_t d = P->d;
   const int64_t KL = P->K[2];
   const int64_t qb = q_base(P, b, n, h);
-  const void* qk = kg_query(P);
   double* score = (double*)malloc((size_t)(nc > 0 ? nc : 1) * sizeof(double));
   int64_t* pos = (int64_t*)malloc((size_t)(nc > 0 ? nc : 1) * sizeof(int64_t));
   int64_t* sel = (int64_t*)malloc((size_t)(KL + 1) * sizeof(int64_t));
@@ -344,7 +357,7 @@ static int leaf_and_finish(const oracle_problem* P, int64_t b, int64_t n, int64_
   int64_t k = 0;
   if (!rc) {
     for (int64_t i = 0; i < nc; ++i)
-      score[i] = P->scale * dot(qk, qb, krow[i], koff[i], P->dtype, d);
+      score[i] = kg_score(P, qb, krow[i], koff[i]);
     if (O->gap) O->gap[r * 3 + 2] = boundary_gap(nc, score, cidx, KL);
     if (O->n_cand) O->n_cand[r * 3 + 2] = nc;
     if (forced) {
@@ -476,7 +489,7 @@ int oracle_flat_rows(const oracle_problem* P, int64_t rows, const int64_t* b,
     for (int64_t m = 0; m < M; ++m) {
       voff[m] = (g * M + m) * d;
       vrow[m] = P->leaf_v;
-      logit[m] = P->scale * dot(kg_query(P), qb, P->leaf_k, voff[m], P->dtype, d);
+      logit[m] = kg_score(P, qb, P->leaf_k, voff[m]);
     }
     rc = finish_row(P, b[r], n[r], h[r], M, logit, vrow, voff, r, O);
   }

@@ -63,6 +63,8 @@ typedef struct {
   const void* seq_v;       /* [B, S_kv, Hkv, d] */
   int32_t K[3];            /* Top-K per level: root, mid, leaf */
   double scale;            /* logit scale, normally 1/sqrt(d) */
+  int32_t q_kg_f64;        /* nonzero: q_kg holds fp64 values (an exact KG query, e.g. a sum
+                              or a product of stored values, not rounded to dtype) */
 } oracle_problem;
 
 /* Per-row outputs; any pointer may be NULL.  Row i of a call fills entry i. */

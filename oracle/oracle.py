@@ -34,6 +34,7 @@ class _Problem(ctypes.Structure):
         ("seq_k", ctypes.c_void_p), ("seq_v", ctypes.c_void_p),
         ("K", ctypes.c_int32 * 3),
         ("scale", ctypes.c_double),
+        ("q_kg_f64", ctypes.c_int32),
     ]
 
 
@@ -133,7 +134,10 @@ def _fp(a):
 
 class Problem:
     """One HiKVP layer call: q [B,N,Hq,d], tree keys [Hkv,M_x,d], leaf values,
-    int64 child offsets, sequence K/V [B,S_kv,Hkv,d] (None -> no sequence)."""
+    int64 child offsets, sequence K/V [B,S_kv,Hkv,d] (None -> no sequence).
+    q_kg (optional, [B,N,Hq,d]) is the KG query, in the storage type or in
+    fp64: an exact query (a sum or product of stored values) is ranked and
+    scored as it is, never rounded to the storage type."""
 
     def __init__(self, q, root_k, mid_k, leaf_k, leaf_v, root_off, mid_off,
                  seq_k, seq_v, K, scale=None, q_kg=None):
@@ -150,10 +154,12 @@ class Problem:
         mo = _offsets(mid_off)
         sk, _ = _host(seq_k)
         sv, _ = _host(seq_v)
-        qk, _ = _host(q_kg)
+        qk, dt_qk = _host(q_kg)
         for other in (dt_r, dt_m):
             if other != dt:
                 raise TypeError("all floating inputs must share one storage type")
+        if qk is not None and dt_qk not in (dt, F64):
+            raise TypeError("q_kg must be in the storage type or fp64 (an exact query)")
         Hkv = rk.shape[0]
         self.shape = dict(B=B, N=N, Hq=Hq, Hkv=Hkv, d=d, M_R=rk.shape[1], M_I=mk.shape[1],
                           M=(lk.shape[1] if lk is not None else int(mo[-1])),
@@ -171,6 +177,7 @@ class Problem:
         P.seq_k, P.seq_v = _vp(sk), _vp(sv)
         P.K = (ctypes.c_int32 * 3)(*self.K)
         P.scale = self.scale
+        P.q_kg_f64 = 1 if (qk is not None and dt_qk == F64 and dt != F64) else 0
         self._P = P
         self._keep = [qa, rk, mk, lk, lv, ro, mo, sk, sv, qk]
         self.root_off, self.mid_off = ro, mo
@@ -236,39 +243,17 @@ def flat_rows(prob: Problem, rows):
 SHARE_KV_GROUP, SHARE_SEQUENCE = 1, 2
 
 
-def _round_bf16_bits(x):
-    """Round fp64 values once to bf16 (nearest, ties to even), from the fp64
-    bit pattern; returns the 16-bit codes.  Normal range and zero only."""
-    x = np.ascontiguousarray(x, dtype=np.float64)
-    u = x.view(np.uint64)
-    sign = (u >> np.uint64(63)).astype(np.uint64)
-    exp = ((u >> np.uint64(52)) & np.uint64(0x7FF)).astype(np.int64)
-    man = (u & np.uint64((1 << 52) - 1)) | np.uint64(1 << 52)      # 53-bit significand
-    keep = man >> np.uint64(45)                                     # 8 significant bits
-    rest = man & np.uint64((1 << 45) - 1)
-    half = np.uint64(1 << 44)
-    up = (rest > half) | ((rest == half) & ((keep & np.uint64(1)) == np.uint64(1)))
-    keep = keep + up.astype(np.uint64)
-    carry = keep >> np.uint64(8)                                    # 2^8: next binade
-    keep = np.where(carry > 0, keep >> np.uint64(1), keep)
-    e = exp - 1023 + 127 + carry.astype(np.int64)
-    zero = (u & np.uint64((1 << 63) - 1)) == 0
-    if np.any(~zero & ((e <= 0) | (e >= 255))):
-        raise ValueError("group query outside the bf16 normal range")
-    bits = (sign << np.uint64(15)) | (np.clip(e, 0, 255).astype(np.uint64) << np.uint64(7)) | (keep & np.uint64(0x7F))
-    return np.where(zero, sign << np.uint64(15), bits).astype(np.uint16)
-
-
 def group_queries(prob: Problem, share):
-    """Each row's group query [B, N, Hq, d] in the problem's storage type.
+    """Each row's group query [B, N, Hq, d] as fp64 (torch.float64).
 
     The group of row (b, n, h) is every row of the same sequence b and KV head
     g = h // G at token n (share = SHARE_KV_GROUP) or at any token
     (SHARE_SEQUENCE).  Its query is the exact sum of the members' stored KG
-    queries, rounded once to the storage type: ranking nodes by it ranks them
-    by the sum of the members' logits up to that rounding.  math.fsum gives the
-    exact sum rounded to fp64, which is the exact sum itself whenever that
-    fits 53 bits (always, unless the members' magnitudes span ~2^40).
+    queries, not rounded to the storage type: <sum_m q_m, k> is the sum of
+    the members' logits, so ranking nodes by it ranks them by the summed
+    logits.  math.fsum gives the exact sum rounded to fp64, which is the exact
+    sum itself whenever that fits 53 bits (always, unless the members'
+    magnitudes span ~2^40).
     """
     q, q_kg = prob._args[0], prob._kw["q_kg"]
     qa, dt = _host(q if q_kg is None else q_kg)
@@ -291,10 +276,6 @@ def group_queries(prob: Problem, share):
                     g[b, n, kv] = [math.fsum(xg[b, n, kv, :, t]) for t in range(d)]
     full = np.repeat(g, G, axis=2)                                   # back to [B, N, Hq, d]
     import torch
-    if dt == BF16:
-        return torch.from_numpy(_round_bf16_bits(full).view(np.int16)).view(torch.bfloat16)
-    if dt == F32:
-        return torch.from_numpy(np.ascontiguousarray(full.astype(np.float32)))
     return torch.from_numpy(np.ascontiguousarray(full))
 
 
@@ -339,22 +320,13 @@ def _as_f64(t):
     return np.asarray(a, dtype=np.float64), dt
 
 
-def _round_to(x, dt):
-    """fp64 values rounded once to a storage type, as a torch tensor."""
-    import torch
-    if dt == BF16:
-        return torch.from_numpy(_round_bf16_bits(x).view(np.int16)).view(torch.bfloat16)
-    if dt == F32:
-        return torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32)))
-    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
-
-
 def folded_query(q_kg, w_k, rows=None):
-    """q'[b,n,h] = W_K[g]^T q_kg[b,n,h]: the exact sum of the products (math.fsum
-    over the head dim), rounded once to the storage type.  W_K [Hkv, d, D_E]
-    maps a base key k (width D_E) to the head's projected key W_K[g] k, so
-    <q_kg, W_K[g] k> = <q', k>.  rows: only these (b, n, h) are formed (the
-    others stay zero)."""
+    """q'[b,n,h] = W_K[g]^T q_kg[b,n,h] as fp64 (torch.float64): the exact
+    sum of the products (math.fsum over the head dim), not rounded to the
+    storage type.  W_K [Hkv, d, D_E] maps a base key k (width D_E) to the
+    head's projected key W_K[g] k, so <q_kg, W_K[g] k> = <q', k> and ranking
+    base keys by <q', k> ranks the projected keys by their logits.  rows: only
+    these (b, n, h) are formed (the others stay zero)."""
     q, dt = _as_f64(q_kg)
     w, _ = _as_f64(w_k)
     B, N, Hq, d = q.shape
@@ -365,7 +337,8 @@ def folded_query(q_kg, w_k, rows=None):
     for b, n, h in todo:
         prod = w[h // G] * q[b, n, h][:, None]                  # [d, D_E], exact products
         out[b, n, h] = [math.fsum(prod[:, j]) for j in range(DE)]
-    return _round_to(out, dt)
+    import torch
+    return torch.from_numpy(out)
 
 
 def folded_rows(base_tree, q, w_k, w_v, seq_k, seq_v, K, rows, scale=None, q_kg=None,
@@ -387,7 +360,10 @@ def folded_rows(base_tree, q, w_k, w_v, seq_k, seq_v, K, rows, scale=None, q_kg=
     d = q.shape[-1]
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     qf = folded_query(q if q_kg is None else q_kg, w_k, rows)
-    P = Problem(qf, root_k, mid_k, leaf_k, leaf_v, root_off, mid_off, None, None, K, scale=sc)
+    # no sequence half here: the descent reads only the exact KG query qf
+    # (q is a placeholder of the storage type that is never read)
+    stub_q = torch.zeros(qf.shape, dtype=root_k.dtype)
+    P = Problem(stub_q, root_k, mid_k, leaf_k, leaf_v, root_off, mid_off, None, None, K, scale=sc, q_kg=qf)
     r = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
     ph1 = select_mids_rows(P, r)                 # roots and mids under q'
     KL = int(K[2])

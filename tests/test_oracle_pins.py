@@ -523,35 +523,6 @@ def test_replay_with_forced_selection(oracle_mod):
 # shared selections (one descent per KV group or per sequence)
 # ---------------------------------------------------------------------------
 
-def _bf16_value(bits):
-    return float(np.array([int(bits) << 16], np.uint32).view(np.float32)[0])
-
-
-@pytest.mark.parametrize("seed", range(3))
-def test_round_bf16_is_nearest_ties_to_even(oracle_mod, seed):
-    """The group-query rounding against its definition: the nearest bf16 of
-    the two that bracket x, the even code on a tie."""
-    rng = np.random.default_rng(seed)
-    x = rng.standard_normal(4000) * 10.0 ** rng.integers(-3, 4, 4000)
-    # exact ties: a bf16 value plus half an ulp
-    base = np.array([_bf16_value(b) for b in rng.integers(0x3C00, 0x4400, 200)])
-    half_ulp = 2.0 ** (np.frexp(base)[1] - 9.0)                # |base| in [2^(e-1), 2^e)
-    x = np.concatenate([x, base + half_ulp * np.where(rng.random(200) < 0.5, 1, -1),
-                        [0.0, -0.0, 1.0, -3.0]])
-    got = oracle_mod._round_bf16_bits(x)
-    nties = 0
-    for xi, gi in zip(x, got):
-        t = int(np.array([xi], np.float32).view(np.uint32)[0]) >> 16       # a nearby code
-        cands = [c & 0xFFFF for c in (t - 1, t, t + 1, t + 2) if np.isfinite(_bf16_value(c & 0xFFFF))]
-        best = min(cands, key=lambda c: (abs(_bf16_value(c) - xi), c & 1))
-        assert abs(_bf16_value(int(gi)) - xi) == abs(_bf16_value(best) - xi), (xi, gi, best)
-        ties = [c for c in cands if abs(_bf16_value(c) - xi) == abs(_bf16_value(int(gi)) - xi)]
-        if len(ties) > 1:
-            assert int(gi) & 1 == 0, (xi, gi)
-            nties += 1
-    assert nties >= 150   # the constructed half-ulp points are exact ties
-
-
 def test_shared_kv_group_of_one_is_per_row(oracle_mod):
     """Hq == Hkv: a KV group is one row, its summed query is the row's own,
     so the shared variant equals the per-row descent."""
@@ -616,19 +587,57 @@ def test_shared_selection_is_top_k_of_summed_logits(oracle_mod, share):
         np.testing.assert_allclose(o["out"][i], ref, rtol=1e-12, atol=1e-12)
 
 
-def test_shared_group_query_rounds_the_sum_once(oracle_mod):
-    """bf16 storage: the group query is the exact member sum rounded once."""
+def test_shared_group_query_is_the_exact_member_sum(oracle_mod):
+    """bf16 storage: the group query is the members' sum itself (fp64, not
+    rounded to bf16); two bf16 values always add exactly in fp64."""
     c = synth.make_case("custom", seed=133, ragged=True, dtype="bf16", B=1, N=3, S_kv=3, Hq=4,
                         Hkv=2, d=8, M_R=3, M_I=7, M=23, K=(2, 2, 3))
     P = _problem(oracle_mod, c, f64=False)
-    gq = oracle_mod.group_queries(P, oracle_mod.SHARE_KV_GROUP).float().numpy()
+    gq = oracle_mod.group_queries(P, oracle_mod.SHARE_KV_GROUP)
+    assert gq.dtype == torch.float64
     q = c.q.double().numpy()
     want = q.reshape(1, 3, 2, 2, 8).sum(axis=3)
     for b, n, h in oracle_mod.all_rows(1, 3, 4):
-        exact = want[b, n, h // 2]
-        np.testing.assert_array_equal(gq[b, n, h], [_bf16_value(x) for x in oracle_mod._round_bf16_bits(exact)])
-        # and it is within half a bf16 ulp of the exact sum
-        assert np.all(np.abs(gq[b, n, h] - exact) <= np.abs(exact) * 2.0 ** -8 + 1e-300)
+        np.testing.assert_array_equal(gq.numpy()[b, n, h], want[b, n, h // 2])
+
+
+@pytest.mark.parametrize("share", [1, 2])
+def test_shared_bf16_selection_is_top_k_of_summed_logits(oracle_mod, share):
+    """bf16 storage: each level's shared selection is the brute-force Top-K
+    of the sum of the members' fp64 logits (the sum of G logits, each a
+    sequential fp64 dot product of stored values), with no rounding of the
+    group query in between.  (At these seeds, rounding the group query to
+    bf16 first changes the selected leaf set of some rows.)"""
+    c = synth.make_case("custom", seed={1: 140, 2: 149}[share], ragged=True, dtype="bf16", B=2, N=3, S_kv=4, Hq=8,
+                        Hkv=2, d=32, M_R=7, M_I=40, M=400, K=(3, 5, 8))
+    P = _problem(oracle_mod, c, f64=False)
+    rows = oracle_mod.all_rows(c.B, c.N, c.Hq)
+    o = oracle_mod.shared_rows(P, rows, share)
+    q = c.q.double().numpy()
+    G = c.Hq // c.Hkv
+    ro, mo = c.root_off.numpy(), c.mid_off.numpy()
+    keys = [c.root_k.double().numpy(), c.mid_k.double().numpy(), c.leaf_k.double().numpy()]
+    for i, (b, n, h) in enumerate(rows):
+        g = h // G
+        toks = [n] if share == 1 else list(range(c.N))
+        members = [(b, t, hh) for t in toks for hh in range(g * G, (g + 1) * G)]
+        parents = None
+        for lev, (key, Kl) in enumerate(zip(("sel_R", "sel_I", "sel_L"), c.K)):
+            if lev == 0:
+                cand = np.arange(c.M_R)
+            else:
+                off = ro if lev == 1 else mo
+                cand = np.concatenate([np.arange(off[p], off[p + 1]) for p in parents])
+            score = np.zeros(len(cand))
+            for (mb, mn, mh) in members:
+                score += keys[lev][g, cand] @ q[mb, mn, mh]
+            order = sorted(range(len(cand)), key=lambda j: (-score[j], cand[j]))
+            if len(cand) > Kl:   # a near-tie at the boundary could flip on fp64 rounding
+                s0, s1 = score[order[Kl - 1]], score[order[Kl]]
+                assert abs(s0 - s1) > 1e-9 * max(abs(s0), abs(s1)), (i, key)
+            want = sorted(cand[j] for j in order[:Kl])
+            assert sorted(x for x in o[key][i] if x >= 0) == want, (i, key)
+            parents = want
 
 
 # ---------------------------------------------------------------------------
@@ -685,13 +694,42 @@ def test_folded_equals_projected_per_head_trees(oracle_mod, seed):
     np.testing.assert_allclose(a["lse_kg"], b["lse_kg"], rtol=1e-12, atol=1e-12)
 
 
-def test_folded_query_rounds_the_exact_product_sum_once(oracle_mod):
+def test_folded_query_is_the_exact_product_sum(oracle_mod):
+    """bf16 inputs: q' = W_K^T q_kg is formed exactly (products of two bf16
+    values are exact in fp64, and so is their sum here) and not rounded."""
     rng = np.random.default_rng(7)
     q = torch.from_numpy(rng.standard_normal((1, 2, 2, 8))).to(torch.bfloat16)
     wk = torch.from_numpy(rng.standard_normal((1, 8, 5))).to(torch.bfloat16)
-    got = oracle_mod.folded_query(q, wk).float().double().numpy()
+    got = oracle_mod.folded_query(q, wk)
+    assert got.dtype == torch.float64
     exact = np.einsum("bnht,td->bnhd", q.double().numpy(), wk.double().numpy()[0])
-    assert np.all(np.abs(got - exact) <= np.abs(exact) * 2.0 ** -8 + 1e-30)   # half a bf16 ulp
-    codes = oracle_mod._round_bf16_bits(exact.reshape(-1))
-    np.testing.assert_array_equal(got.reshape(-1), [_bf16_value(x) for x in codes])
+    np.testing.assert_array_equal(got.numpy(), exact)
 
+
+@pytest.mark.parametrize("seed", range(2))
+def test_folded_bf16_equals_projected_per_head_trees(oracle_mod, seed):
+    """bf16 storage of the base tree, W_K, W_V and the queries: the folded
+    variant (the base tree ranked by <W_K^T q, k> with the exact folded
+    query) selects and outputs what the per-row descent selects over the
+    per-head trees projected in fp64 (W_K k, W_V v) with the stored q, since
+    both score the same exact sum of products."""
+    rng = np.random.default_rng(10 + seed)
+    d, DE, Hkv, Hq = 8, 24, 2, 4
+    tree = _base_tree(160 + seed, DE, 5, 17, 140, dtype=torch.bfloat16)
+    c = _small_case(160 + seed, B=2, N=3, S=4, Hq=Hq, Hkv=Hkv, d=d, MR=5, MI=17, M=140)
+    bf = lambda x: x.to(torch.bfloat16)
+    q, sk, sv = bf(c.q), bf(c.seq_k), bf(c.seq_v)
+    wk = bf(torch.from_numpy(rng.standard_normal((Hkv, d, DE)) / 3.0))
+    wv = bf(torch.from_numpy(rng.standard_normal((Hkv, d, DE)) / 3.0))
+    proj = lambda t, w: torch.stack([t[0].double() @ w[g].double().T for g in range(Hkv)])
+    rk, mk, lk, lv, ro, mo = tree
+    K = (2, 4, 6)
+    rows = oracle_mod.all_rows(c.B, c.N, c.Hq)
+    a = oracle_mod.folded_rows(tree, q, wk, wv, sk, sv, K, rows)
+    b = oracle_mod.hikvp_rows(oracle_mod.Problem(q.double(), proj(rk, wk), proj(mk, wk), proj(lk, wk),
+                                                 proj(lv, wv), ro, mo, sk.double(), sv.double(), K), rows)
+    assert np.all(b["gap"] > 1e-9)          # no boundary that fp64 rounding could flip
+    for k in ("sel_R", "sel_I", "sel_L"):
+        np.testing.assert_array_equal(a[k], b[k])
+    np.testing.assert_allclose(a["out"], b["out"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(a["lse_kg"], b["lse_kg"], rtol=1e-12, atol=1e-12)
