@@ -16,7 +16,8 @@ Timing: W warm-up steps, then max(K, 50) steps each timed alone with HIP
 events on the launch stream after a 1 GiB read has evicted the 256 MB MALL
 (cold); the headline is their median (p10 / p90 beside it).  K steps back
 to back give the warm figure.  Run without --workload, the benchmark first
-measures the m1e7_decode and m1e8_slice workloads (one JSON line each on
+measures the m1e7_decode and m1e8_slice workloads and the m1e6 layer folded
+onto one base-embedding tree of width D_E = 384 (one JSON line each on
 stderr) and ends with the m1e6 line on stdout.
 
 With --tree-placement host-leaves the leaf keys and values sit in pinned host
@@ -283,7 +284,8 @@ def parse_args(argv=None):
                          "median is the headline), and `steps` warm steps back to back")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, choices=sorted(synth.CONFIGS),
-                    help="one workload only (default: m1e7_decode and m1e8_slice on stderr, then m1e6)")
+                    help="one workload only (default: m1e7_decode, m1e8_slice and m1e6 folded at "
+                         "D_E = 384 on stderr, then m1e6)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--phase-steps", type=int, default=None,
@@ -570,9 +572,11 @@ def main():
     if args.workload is not None:
         print(json.dumps(run_one(args, args.workload, dev, with_cpu=True)), flush=True)
         return
-    # the other target workloads first (stderr), the headline workload last (stdout)
-    for extra in ("m1e7_decode", "m1e8_slice"):
-        line = run_one(args, extra, dev, with_cpu=False)
+    # the other target workloads first (stderr), the headline workload last (stdout):
+    # the decode and slice workloads, and the m1e6 layer folded onto one base
+    # tree of width D_E = 384
+    for extra, over in (("m1e7_decode", {}), ("m1e8_slice", {}), ("m1e6", {"fold": True, "fold_width": 384})):
+        line = run_one(argparse.Namespace(**{**vars(args), **over}), extra, dev, with_cpu=False)
         print(json.dumps(line), file=sys.stderr, flush=True)
     print(json.dumps(run_one(args, "m1e6", dev, with_cpu=True)), flush=True)
 

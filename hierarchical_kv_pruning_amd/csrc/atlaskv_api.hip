@@ -113,7 +113,9 @@ atlaskv_status check_tree_tensors(const atlaskv_tensor* root_k, const atlaskv_te
     return fail(ATLASKV_ERR_DTYPE, "tree tensors must share one dtype");
   const int64_t Hkv = root_k->shape[0], d = root_k->shape[2];
   if (Hkv < 1) return fail(ATLASKV_ERR_SHAPE, "root_k: need at least one KV head");
-  if (d != 64 && d != 128) return fail(ATLASKV_ERR_UNSUPPORTED, "head dim %lld not in {64, 128}", (long long)d);
+  if (d != 64 && d != 128 && !(d > 128 && d <= kMaxWideD && d % 128 == 0))
+    return fail(ATLASKV_ERR_UNSUPPORTED, "key width %lld: 64, 128, or a multiple of 128 up to %d (a base-embedding "
+                "tree for the folded entry point)", (long long)d, kMaxWideD);
   if (mid_k->shape[0] != Hkv || leaf_k->shape[0] != Hkv || leaf_v->shape[0] != Hkv)
     return fail(ATLASKV_ERR_SHAPE, "tree tensors disagree on the KV head count");
   if (mid_k->shape[2] != d || leaf_k->shape[2] != d || leaf_v->shape[2] != d)
@@ -202,8 +204,10 @@ struct Plan {
   size_t off_fpart;
   int group_rows;                                    // shared selections only
   size_t off_gq, off_gpart;
+  size_t off_gqx, off_glo, off_gdelta;
   int fold_Hkv, fold_d, fold_kg_empty;               // folded projections only
-  size_t off_qf;
+  size_t off_qf, off_qx, off_qlo, off_qdelta;
+  int exact_logits;                                  // the KG softmax takes its logits from rows.q_exact
 };
 
 // Candidate capacity per row at the mid level (children of K_R distinct
@@ -218,7 +222,9 @@ void candidate_capacity(const atlaskv_tree_view_s* v, const int K[3], int64_t* c
   *c2 = b < 1 ? 1 : b;
 }
 
-enum { kModeHikvp = 0, kModeFlat = 1, kModeSharedKvGroup = 2, kModeSharedSequence = 3 };
+// kModeFoldedDescent: the pruned path on the folded rows of a base-embedding
+// tree, the only one that takes a tree wider than 128.
+enum { kModeHikvp = 0, kModeFlat = 1, kModeSharedKvGroup = 2, kModeSharedSequence = 3, kModeFoldedDescent = 4 };
 
 // The group rows of a shared-selection call: [B, Ng, Hkv, d] contiguous in
 // the tree's dtype, Ng = N (one group per KV head and token) or 1 (per KV
@@ -247,6 +253,9 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   if (!Kpl && !flat) return fail(ATLASKV_ERR_NULL, "K_per_level is NULL");
   if ((st = check_tensor(q, "q", 4, true))) return st;
   const TreeDev& t = v->dev;
+  if (t.d > kMaxD && mode != kModeFoldedDescent)
+    return fail(ATLASKV_ERR_UNSUPPORTED, "a tree of width %d (above %d) serves the folded entry point only", t.d,
+                kMaxD);
   if (q->dtype != t.dtype) return fail(ATLASKV_ERR_DTYPE, "q dtype differs from the tree's");
   if (q->shape[3] != t.d) return fail(ATLASKV_ERR_SHAPE, "q head dim %lld != tree head dim %d",
                                       (long long)q->shape[3], t.d);
@@ -350,6 +359,9 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
     size_t o = align256(pg.total);
     p.group_rows = (int)(B * Ng * t.Hkv);
     p.off_gq = o;    o = align256(o + (size_t)p.group_rows * t.d * esize(t.dtype));
+    p.off_gqx = o;   o = align256(o + (size_t)p.group_rows * t.d * 8);
+    p.off_glo = o;   o = align256(o + (t.dtype == ATLASKV_BF16 ? (size_t)p.group_rows * t.d * 2 : 0));
+    p.off_gdelta = o; o = align256(o + (size_t)p.group_rows * 4);
     int tn = 1;
     const int chunks = group_chunks(p.N, (int)Ng, &tn);
     p.off_gpart = o; o = align256(o + (size_t)p.group_rows * chunks * t.d * 8);
@@ -428,6 +440,9 @@ void fill_rows(RowsDev& r, const atlaskv_tensor* q, const atlaskv_attend_opts* o
   for (int i = 0; i < 3; ++i) { r.qs[i] = q->stride[i]; r.qks[i] = qk->stride[i]; }
   r.B = p.B; r.N = p.N; r.Hq = p.Hq; r.G = p.G; r.R = p.R;
   r.scale = p.scale;
+  r.q_exact = nullptr;
+  r.q_delta = nullptr;
+  r.q_lo = nullptr;
 }
 
 // Selection arrays of one descent (plan pd): the caller's outputs where their
@@ -562,11 +577,15 @@ atlaskv_status plan_folded(const atlaskv_tensor* q, const atlaskv_tree_view_s* v
   size_t o = 0;
   if (!kg_empty) {
     atlaskv_tensor qd = group_rows_desc(B, N, (int)Hq, t.d, t.dtype, (void*)(uintptr_t)256);
-    if ((st = plan_call(&qd, v, nullptr, nullptr, Kpl, nullptr, nullptr, false, pd, kModeHikvp))) return st;
+    if ((st = plan_call(&qd, v, nullptr, nullptr, Kpl, nullptr, nullptr, false, pd, kModeFoldedDescent))) return st;
+    pd.exact_logits = 1;
     o = align256(pd.total);
   }
   const size_t R = (size_t)p.R;
   p.off_qf = o;   o = align256(o + R * (size_t)t.d * esize(t.dtype));
+  p.off_qx = o;   o = align256(o + R * (size_t)t.d * 8);
+  p.off_qlo = o;  o = align256(o + (t.dtype == ATLASKV_BF16 ? R * (size_t)t.d * 2 : 0));
+  p.off_qdelta = o; o = align256(o + R * 4);
   p.off_okg = o;  o = align256(o + R * (size_t)d * 4);
   p.off_lse = o;  o = align256(o + R * 4);
   p.nsplit = seq_splits(p.B, p.N, (int)Hkv, p.G, p.S, t.dtype);
@@ -745,6 +764,7 @@ hipError_t launch_descent(const Plan& p, const RowsDev& rows, atlaskv_tree_view_
   a.junk = (float*)(ws + p.off_junk);
   a.o_kg = o_kg;
   a.lse_kg = lse_kg;
+  a.exact_logits = p.exact_logits;
   const int per_head = rows.B * rows.N * rows.G;  // row blocks per KV head
   if (p.nparts < 2 || !v->part_s[0] || pm.ev) {
     a.g0 = 0;
@@ -1112,6 +1132,9 @@ atlaskv_status atlaskv_shared_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vi
   fill_rows(rows, q, opts, p);
   fill_rows(grows, &gd, nullptr, pg);
   grows.scale = p.scale;
+  grows.q_exact = (const double*)(ws + p.off_gqx);   // the selection is exact for the unrounded sums
+  grows.q_delta = (const float*)(ws + p.off_gdelta);
+  grows.q_lo = v->dev.dtype == ATLASKV_BF16 ? (const void*)(ws + p.off_glo) : nullptr;
   const SelTargets st3 = sel_targets(pg, opts, ws);
   int32_t* const* sel = st3.sel;
   float* lse_kg = (opts && opts->lse_kg) ? opts->lse_kg : (float*)(ws + p.off_lse);
@@ -1123,6 +1146,9 @@ atlaskv_status atlaskv_shared_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vi
   sa.B = p.B;
   sa.Ng = Ng;
   sa.gq = ws + p.off_gq;
+  sa.gqx = (double*)(ws + p.off_gqx);
+  sa.glo = ws + p.off_glo;
+  sa.gdelta = (float*)(ws + p.off_gdelta);
   sa.gpart = (double*)(ws + p.off_gpart);
   sa.chunks = group_chunks(p.N, Ng, &sa.tn);
   sa.sel_leaf = sel[2];
@@ -1223,6 +1249,9 @@ atlaskv_status atlaskv_folded_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vi
   fa.DE = v->dev.d;
   fa.dtype = v->dev.dtype;
   fa.qf = ws + p.off_qf;
+  fa.qx = (double*)(ws + p.off_qx);
+  fa.qlo = ws + p.off_qlo;
+  fa.qdelta = (float*)(ws + p.off_qdelta);
   fa.o_base = p.fold_kg_empty ? nullptr : (const float*)(ws + pd.off_okg);
   fa.o_kg = o_kg;
   fa.lse_kg = lse_kg;
@@ -1240,6 +1269,9 @@ atlaskv_status atlaskv_folded_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vi
     RowsDev frows;
     fill_rows(frows, &qd, nullptr, pd);
     frows.scale = p.scale;
+    frows.q_exact = fa.qx;
+    frows.q_delta = fa.qdelta;
+    frows.q_lo = v->dev.dtype == ATLASKV_BF16 ? fa.qlo : nullptr;
     const SelTargets st3 = sel_targets(pd, opts, ws);
     if (e == hipSuccess) e = launch_descent(pd, frows, v, ws, st3.sel, (float*)(ws + pd.off_okg), lse_kg, s, pm, &sh);
     if (e == hipSuccess) e = finish_sel(st3, pd, s);

@@ -293,9 +293,9 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 // tile row/column l%16 with the 16-byte pieces m*64 + (l/16)*16 of its row
 // (m < KCH); the same element permutation on both operands leaves the dot
 // products unchanged.
+// tile_dot_acc adds the tile to acc (key rows scored slice by slice).
 template <class E, int KCH>
-__device__ inline float4_t tile_dot(const uint4* a, const uint4* b) {
-  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+__device__ inline float4_t tile_dot_acc(const uint4* a, const uint4* b, float4_t acc) {
   if constexpr (E::kBytes == 2) {
 #pragma unroll
     for (int m = 0; m < KCH; ++m) {
@@ -317,6 +317,10 @@ __device__ inline float4_t tile_dot(const uint4* a, const uint4* b) {
     }
   }
   return acc;
+}
+template <class E, int KCH>
+__device__ inline float4_t tile_dot(const uint4* a, const uint4* b) {
+  return tile_dot_acc<E, KCH>(a, b, float4_t{0.f, 0.f, 0.f, 0.f});
 }
 
 // Half-split 16x16 tiles for streaming many rows: tile row (or column) i is
@@ -391,26 +395,37 @@ struct SelWork {
   int* tmp_node;                 // [K + kBand]
   int* tmp_slot;                 // [K + kBand]
   int* tmp_rank;                 // [K + kBand]
-  float* kbuf;                   // [kExactGroup][D+1] staged key rows (padded: no bank conflicts)
-  float* qrow;                   // [D] KG query row, fp32 (exact copy of the stored values)
+  float* kbuf;                   // [kExactGroup][W+1] staged key-row slices (W = slice width; padded)
+  float* qrow;                   // [d] KG query row, fp32 (exact copy of the stored values)
+  const double* qx;              // [d] exact KG query (global) when the stored one is rounded, else NULL
+  int d;                         // query / key width
 };
+
+// Key rows of width d are handled in slices of W = SliceW<D> elements: the
+// whole row for the head dims 64 and 128 (D = d), 128-element slices for
+// wide rows (D = 0: d a multiple of 128, base-embedding trees).
+template <int D>
+struct SliceW {
+  static constexpr int W = D == 0 ? 128 : D;
+};
+__host__ __device__ inline int slice_width(int d) { return d <= 128 ? d : 128; }
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-// Bytes of a SelWork for NT threads, Top-K K, head dim D.
-__host__ __device__ inline size_t selwork_bytes(int NT, int K, int D) {
+// Bytes of a SelWork for NT threads, Top-K K, row width d.
+__host__ __device__ inline size_t selwork_bytes(int NT, int K, int d) {
   size_t b = 0;
   b += align16(8 * 4);
   b += align16((size_t)(NT / 64) * 256 * 4);
   b += align16(kBand * 4) * 2 + align16(kBand * 8);
   b += align16((size_t)K * 4) * 2 + align16((size_t)K * 8) + align16((size_t)K * 4);
   b += align16((size_t)(K + kBand) * 8) + 3 * align16((size_t)(K + kBand) * 4);
-  b += align16((size_t)kExactGroup * (D + 1) * 4);
-  b += align16((size_t)D * 4);
+  b += align16((size_t)kExactGroup * (slice_width(d) + 1) * 4);
+  b += align16((size_t)d * 4);
   return b;
 }
 
-__device__ inline SelWork carve_selwork(char*& p, int NT, int K, int D) {
+__device__ inline SelWork carve_selwork(char*& p, int NT, int K, int d) {
   SelWork w;
   auto take = [&](size_t bytes) { char* q = p; p += align16(bytes); return q; };
   w.ctl = (int*)take(8 * 4);
@@ -426,8 +441,10 @@ __device__ inline SelWork carve_selwork(char*& p, int NT, int K, int D) {
   w.tmp_node = (int*)take((size_t)(K + kBand) * 4);
   w.tmp_slot = (int*)take((size_t)(K + kBand) * 4);
   w.tmp_rank = (int*)take((size_t)(K + kBand) * 4);
-  w.kbuf = (float*)take((size_t)kExactGroup * (D + 1) * 4);
-  w.qrow = (float*)take((size_t)D * 4);
+  w.kbuf = (float*)take((size_t)kExactGroup * (slice_width(d) + 1) * 4);
+  w.qrow = (float*)take((size_t)d * 4);
+  w.qx = nullptr;
+  w.d = d;
   return w;
 }
 
@@ -436,33 +453,85 @@ struct KeyRows {                 // keys of one level and KV head
   int64_t rsb;                   // row stride in bytes
 };
 
-// fp64 logits of band members [0, m): stage key rows in LDS (coalesced), then
-// one thread per member sums the products left to right.
-template <class E, int D, int NT>
+// Wide rows (a base-embedding tree): 16 lanes a band member, each summing
+// every 16th 16-byte piece of the member's key row against the query in
+// fp64, then the 16 partial sums are added; NT / 16 members at a time.
+template <class E, int NT>
+__device__ inline void exact_rescore_wide(const SelWork& S, int m, const KeyRows& kr, double scale, int tid) {
+  constexpr int L = 16, EPV = E::kEPV;
+  const int npieces = S.d / EPV;
+  for (int b0 = 0; b0 < m; b0 += NT / L) {
+    const int mem = b0 + tid / L;
+    double acc = 0.0;
+    if (mem < m) {
+      const char* row = kr.base + (int64_t)S.band_node[mem] * kr.rsb;
+      for (int c = tid % L; c < npieces; c += L) {
+        const uint4 v = *(const uint4*)(row + (int64_t)c * 16);
+        float f[EPV];
+        unpack<E>(v, f);
+        if (S.qx) {
+#pragma unroll
+          for (int t = 0; t < EPV; ++t) acc = fma(S.qx[c * EPV + t], (double)f[t], acc);
+        } else {
+#pragma unroll
+          for (int t = 0; t < EPV; ++t) acc = fma((double)S.qrow[c * EPV + t], (double)f[t], acc);
+        }
+      }
+    }
+#pragma unroll
+    for (int x = 1; x < L; x <<= 1) acc += __shfl_xor(acc, x);
+    if (mem < m && tid % L == 0) S.band_s[mem] = scale * acc;
+  }
+  group_sync<NT>();
+}
+
+// fp64 logits of band members [0, m): stage key-row slices of W elements in
+// LDS (coalesced), then one thread per member sums the products left to
+// right over the whole row (the sum runs on across slices).  The query is the
+// stored one (S.qrow) or, when that is a rounding of an exact query, the exact
+// one (S.qx): the ranking is then exact with respect to the exact query.
+template <class E, int W, int NT>
 __device__ inline void exact_rescore(const SelWork& S, int m, const KeyRows& kr, double scale,
                                      int tid) {
-  constexpr int EPV = E::kEPV, CPK = D / EPV;
+  constexpr int EPV = E::kEPV, CPK = W / EPV;
+  const int ns = S.d / W;
   for (int b0 = 0; b0 < m; b0 += kExactGroup) {
     const int mm = (m - b0) < kExactGroup ? (m - b0) : kExactGroup;
-    for (int idx = tid; idx < mm * CPK; idx += NT) {
-      const int mem = idx / CPK, ch = idx % CPK;
-      const int64_t node = S.band_node[b0 + mem];
-      const uint4 v = *(const uint4*)(kr.base + node * kr.rsb + ch * 16);
-      float f[EPV];
-      unpack<E>(v, f);
+    double acc = 0.0;
+    for (int sl = 0; sl < ns; ++sl) {
+      for (int idx = tid; idx < mm * CPK; idx += NT) {
+        const int mem = idx / CPK, ch = idx % CPK;
+        const int64_t node = S.band_node[b0 + mem];
+        const uint4 v = *(const uint4*)(kr.base + node * kr.rsb + ((int64_t)sl * W + ch * EPV) * E::kBytes);
+        float f[EPV];
+        unpack<E>(v, f);
 #pragma unroll
-      for (int t = 0; t < EPV; ++t) S.kbuf[mem * (D + 1) + ch * EPV + t] = f[t];
-    }
-    group_sync<NT>();
-    if (tid < mm) {
-      double acc = 0.0;
-      const float* kr_row = S.kbuf + tid * (D + 1);
+        for (int t = 0; t < EPV; ++t) S.kbuf[mem * (W + 1) + ch * EPV + t] = f[t];
+      }
+      group_sync<NT>();
+      if (tid < mm) {
+        const float* kr_row = S.kbuf + tid * (W + 1);
+        if (S.qx) {
+          const double* q = S.qx + sl * W;
 #pragma unroll 4
-      for (int t = 0; t < D; ++t) acc += (double)S.qrow[t] * (double)kr_row[t];
-      S.band_s[b0 + tid] = scale * acc;
+          for (int t = 0; t < W; ++t) acc += q[t] * (double)kr_row[t];
+        } else {
+          const float* q = S.qrow + sl * W;
+#pragma unroll 4
+          for (int t = 0; t < W; ++t) acc += (double)q[t] * (double)kr_row[t];
+        }
+      }
+      group_sync<NT>();
     }
+    if (tid < mm) S.band_s[b0 + tid] = scale * acc;
     group_sync<NT>();
   }
+}
+
+template <class E, int D, int NT>
+__device__ inline void exact_band(const SelWork& S, int m, const KeyRows& kr, double scale, int tid) {
+  if constexpr (D == 0) exact_rescore_wide<E, NT>(S, m, kr, scale, tid);
+  else exact_rescore<E, D, NT>(S, m, kr, scale, tid);
 }
 
 __device__ inline bool ranks_before(double sa, int na, double sb, int nb) {
@@ -710,7 +779,7 @@ __device__ int select_topk(const Src& src, int n, int K, double err2, double sca
     for (int i = tid; i < nband; i += NT) S.band_node[i] = (int)map(S.band_slot[i]);
     qload();
     group_sync<NT>();
-    exact_rescore<E, D, NT>(S, nband, kr, scale, tid);
+    exact_band<E, D, NT>(S, nband, kr, scale, tid);
     for (int i = tid; i < nband; i += NT) {
       const double si = S.band_s[i];
       const int ni = S.band_node[i];
@@ -744,7 +813,7 @@ __device__ int select_topk(const Src& src, int n, int K, double err2, double sca
       group_sync<NT>();
       const int m = S.ctl[4];
       if (m == 0) continue;
-      exact_rescore<E, D, NT>(S, m, kr, scale, tid);
+      exact_band<E, D, NT>(S, m, kr, scale, tid);
       const int tot = nbest + m;
       // rank every element of (best so far) + (this chunk's band) in LDS
       for (int e = tid; e < tot; e += NT) {
@@ -788,10 +857,29 @@ __device__ int select_topk(const Src& src, int n, int K, double err2, double sca
   return K;
 }
 
-// 2E for a query of norm qnorm against keys of norm <= knorm (head dim D).
-template <int D>
-__device__ inline double twice_err_bound(double qnorm, double knorm) {
-  return 2.0 * qnorm * knorm * (double)D * (1.0 / 8388608.0);
+// Factor that turns the square root of an fp32 sum of d squares into an
+// upper bound of the 2-norm (the sum's rounding is below d * 2^-24 relative).
+__host__ __device__ inline float norm_slack(int d) { return 1.0001f + (float)d * 6.0e-8f; }
+
+// Sum over the wave's 64 lanes, fp64.
+__device__ inline double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Rounding steps the error bound of a score over d elements counts: d for
+// rows of up to 128 (one fp32 accumulation), 128 + d/128 for wide rows, whose
+// 128-element slices are accumulated from zero each and then added (the
+// slice sums' bounds add up to 128 * 2^-23 |q||k| by Cauchy-Schwarz, the
+// d/128 additions another d/128 * 2^-23 |q||k|).
+__host__ __device__ inline int err_terms(int d) { return d <= 128 ? d : 128 + d / 128; }
+
+// 2E for a query of norm qnorm against keys of norm <= knorm over d
+// elements; qdelta > 0 bounds |q_stored - q_exact| when the stored query is a
+// rounding of an exact one, whose score differs by at most qdelta * knorm.
+__device__ inline double twice_err_bound(double qnorm, double knorm, int d, double qdelta = 0.0) {
+  return 2.0 * qnorm * knorm * (double)err_terms(d) * (1.0 / 8388608.0) + 2.0 * qdelta * knorm * 1.0001;
 }
 
 }  // namespace hikvp

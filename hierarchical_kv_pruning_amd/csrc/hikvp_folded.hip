@@ -6,7 +6,10 @@
 // <q, W_K k> = <W_K^T q, k> and sum p W_V v = W_V sum p v, a single base tree
 // serves all heads: the query is folded into q' = W_K[g]^T q (k_fold_query),
 // the pruned descent runs on the base tree with q', and W_V[g] is applied to
-// the softmax-weighted base values afterwards (k_unfold_values).
+// the softmax-weighted base values afterwards (k_unfold_values).  The
+// descent scores with q' rounded to the tree's dtype; its selections are
+// exact for the unrounded q' and the KG softmax takes the selected leaves'
+// logits from it, so the result is the projected trees' up to fp32 rounding.
 #include "hikvp_device.h"
 #include "hikvp_round.h"
 
@@ -44,67 +47,100 @@ __device__ inline float lds_elem(const char* base, int idx) {
 }
 
 // q'[j] = sum_i W_K[g][i][j] q_kg[i]: products exact in fp64 and summed in
-// fp64 in i order (exact for stored bf16 / fp32 inputs of ordinary range),
-// rounded once into the tree's dtype.  Lanes own output columns j.
-template <class E, int D, int DE>
+// fp64 in i order (exact for stored bf16 / fp32 inputs of ordinary range).
+// The sums go out as they are (qx, fp64: the exact query the selection is
+// exact for) and as the query the scores are computed with: rounded once
+// into the tree's dtype (qf), in bf16 with the rounded residual beside it
+// (qlo), and an upper bound of what that leaves out, per row (qdelta).
+// Lanes own output columns j; the columns are taken in chunks of JC = 64*JPL,
+// each chunk's slice of W_K[g] staged in LDS once for the workgroup's rows.
+template <class E, int D, int JPL>
 __global__ __launch_bounds__(256) void k_fold_query(FoldArgs a, int tiles_per_head) {
-  constexpr int JPL = DE / 64;
-  __shared__ __align__(16) char w_lds[D * DE * E::kBytes];   // W_K[g] as stored, [i][j]
+  constexpr int JC = 64 * JPL;
+  __shared__ __align__(16) char w_lds[D * JC * E::kBytes];   // W_K[g][:, chunk] as stored, [i][j]
   __shared__ float q_lds[4][kFoldRPW][D];                     // the waves' KG queries (exact)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = blockIdx.x / tiles_per_head, tile = blockIdx.x % tiles_per_head;
+  const int DE = a.DE;
   const char* wg = (const char*)a.w_k + (int64_t)g * a.wks[0] * E::kBytes;
-  // 16-byte row pieces (the API requires 16-byte aligned projection rows)
-  constexpr int CPR = DE / E::kEPV;
-  for (int idx = threadIdx.x; idx < D * CPR; idx += 256) {
-    const int i = idx / CPR, c = idx % CPR;
-    *(uint4*)(w_lds + (i * DE + c * E::kEPV) * E::kBytes) =
-        *(const uint4*)(wg + ((int64_t)i * a.wks[1] + c * E::kEPV) * E::kBytes);
-  }
   for (int rho = 0; rho < kFoldRPW; ++rho) {
     const FoldRow f = fold_row(a, g, tile, wave, rho);
     const int64_t qb = q_off(a.r.qks, f.b, f.n, f.h);
     for (int t = lane; t < D; t += 64) q_lds[wave][rho][t] = f.ok ? load_f32<E>(a.r.q_kg, qb + t) : 0.f;
   }
-  __syncthreads();
-  double acc[kFoldRPW][JPL];
+  double dq2[kFoldRPW];                                       // |qf - qx|^2, this lane's columns
 #pragma unroll
-  for (int rho = 0; rho < kFoldRPW; ++rho)
+  for (int rho = 0; rho < kFoldRPW; ++rho) dq2[rho] = 0.0;
+  // 16-byte row pieces (the API requires 16-byte aligned projection rows)
+  constexpr int CPR = JC / E::kEPV;
+  for (int j0 = 0; j0 < DE; j0 += JC) {
+    __syncthreads();                                          // the previous chunk is consumed
+    for (int idx = threadIdx.x; idx < D * CPR; idx += 256) {
+      const int i = idx / CPR, c = idx % CPR;
+      *(uint4*)(w_lds + (i * JC + c * E::kEPV) * E::kBytes) =
+          *(const uint4*)(wg + ((int64_t)i * a.wks[1] + j0 + c * E::kEPV) * E::kBytes);
+    }
+    __syncthreads();
+    double acc[kFoldRPW][JPL];
 #pragma unroll
-    for (int e = 0; e < JPL; ++e) acc[rho][e] = 0.0;
-  for (int i = 0; i < D; ++i) {
-    double w[JPL];
+    for (int rho = 0; rho < kFoldRPW; ++rho)
 #pragma unroll
-    for (int e = 0; e < JPL; ++e) w[e] = (double)lds_elem<E>(w_lds, i * DE + e * 64 + lane);
+      for (int e = 0; e < JPL; ++e) acc[rho][e] = 0.0;
+    for (int i = 0; i < D; ++i) {
+      double w[JPL];
+#pragma unroll
+      for (int e = 0; e < JPL; ++e) w[e] = (double)lds_elem<E>(w_lds, i * JC + e * 64 + lane);
+#pragma unroll
+      for (int rho = 0; rho < kFoldRPW; ++rho) {
+        const double qi = (double)q_lds[wave][rho][i];
+#pragma unroll
+        for (int e = 0; e < JPL; ++e) acc[rho][e] = fma(qi, w[e], acc[rho][e]);
+      }
+    }
 #pragma unroll
     for (int rho = 0; rho < kFoldRPW; ++rho) {
-      const double qi = (double)q_lds[wave][rho][i];
+      const FoldRow f = fold_row(a, g, tile, wave, rho);
+      if (!f.ok) continue;
 #pragma unroll
-      for (int e = 0; e < JPL; ++e) acc[rho][e] = fma(qi, w[e], acc[rho][e]);
+      for (int e = 0; e < JPL; ++e) {
+        const int64_t o = (int64_t)f.row * DE + j0 + e * 64 + lane;
+        const double x = acc[rho][e];
+        double rest;
+        if constexpr (E::kBytes == 2) {
+          const Bf16Split sp = split_bf16(x);
+          ((uint16_t*)a.qf)[o] = sp.hi;
+          ((uint16_t*)a.qlo)[o] = sp.lo;
+          rest = sp.rest;
+        } else {
+          const float v = (float)x;
+          ((float*)a.qf)[o] = v;
+          rest = x - (double)v;
+        }
+        a.qx[o] = x;
+        dq2[rho] = fma(rest, rest, dq2[rho]);
+      }
     }
   }
 #pragma unroll
   for (int rho = 0; rho < kFoldRPW; ++rho) {
     const FoldRow f = fold_row(a, g, tile, wave, rho);
-    if (!f.ok) continue;
-#pragma unroll
-    for (int e = 0; e < JPL; ++e) {
-      const int64_t o = (int64_t)f.row * DE + e * 64 + lane;
-      if constexpr (E::kBytes == 2) ((uint16_t*)a.qf)[o] = f64_to_bf16_rne(acc[rho][e]);
-      else ((float*)a.qf)[o] = (float)acc[rho][e];
-    }
+    const double t = wave_sum_f64(dq2[rho]);
+    // rounded up: the fp32 conversion's relative error is below 2^-24
+    if (f.ok && lane == 0) a.qdelta[f.row] = (float)(sqrt(t) * (1.0 + 1e-6));
   }
 }
 
 // o_kg[i] = sum_j W_V[g][i][j] o_base[j] in fp32, j in order; lanes own
-// output rows i of W_V, staged transposed ([j][i]) so a lane's reads are
-// consecutive.  empty: the KG half has no leaves at all (o_kg = 0, lse_kg =
-// -inf).
-template <class E, int D, int DE>
+// output rows i of W_V.  The columns j are taken in chunks of JC = 64*JPL,
+// each chunk's slice of W_V[g] staged transposed ([j][i]) so a lane's reads
+// are consecutive.  empty: the KG half has no leaves at all (o_kg = 0,
+// lse_kg = -inf).
+template <class E, int D, int JPL>
 __global__ __launch_bounds__(256) void k_unfold_values(FoldArgs a, int tiles_per_head, int empty) {
   constexpr int IPL = D / 64;
-  __shared__ __align__(16) char wt_lds[DE * D * E::kBytes];  // W_V[g]^T, [j][i]
-  __shared__ float o_lds[4][kFoldRPW][DE];                    // the waves' weighted base values
+  constexpr int JC = 64 * JPL;
+  __shared__ __align__(16) char wt_lds[JC * D * E::kBytes];  // W_V[g][:, chunk]^T, [j][i]
+  __shared__ float o_lds[4][kFoldRPW][JC];                    // the waves' weighted base values
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = blockIdx.x / tiles_per_head, tile = blockIdx.x % tiles_per_head;
   if (empty) {
@@ -117,39 +153,43 @@ __global__ __launch_bounds__(256) void k_unfold_values(FoldArgs a, int tiles_per
     }
     return;
   }
+  const int DE = a.DE;
   const char* wg = (const char*)a.w_v + (int64_t)g * a.wvs[0] * E::kBytes;
-  // 16-byte row pieces (16-byte aligned rows), scattered transposed
-  constexpr int CPR = DE / E::kEPV;
-  for (int idx = threadIdx.x; idx < D * CPR; idx += 256) {
-    const int i = idx / CPR, c = idx % CPR;
-    const uint4 v = *(const uint4*)(wg + ((int64_t)i * a.wvs[1] + c * E::kEPV) * E::kBytes);
-    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int k = 0; k < E::kEPV; ++k) {
-      const int j = c * E::kEPV + k;
-      if constexpr (E::kBytes == 2) ((uint16_t*)wt_lds)[j * D + i] = (uint16_t)(w4[k >> 1] >> (16 * (k & 1)));
-      else ((uint32_t*)wt_lds)[j * D + i] = w4[k];
-    }
-  }
-  for (int rho = 0; rho < kFoldRPW; ++rho) {
-    const FoldRow f = fold_row(a, g, tile, wave, rho);
-    for (int j = lane; j < DE; j += 64) o_lds[wave][rho][j] = f.ok ? a.o_base[(int64_t)f.row * DE + j] : 0.f;
-  }
-  __syncthreads();
   float acc[kFoldRPW][IPL];
 #pragma unroll
   for (int rho = 0; rho < kFoldRPW; ++rho)
 #pragma unroll
     for (int e = 0; e < IPL; ++e) acc[rho][e] = 0.f;
-  for (int j = 0; j < DE; ++j) {
-    float w[IPL];
+  // 16-byte row pieces (16-byte aligned rows), scattered transposed
+  constexpr int CPR = JC / E::kEPV;
+  for (int j0 = 0; j0 < DE; j0 += JC) {
+    __syncthreads();                                          // the previous chunk is consumed
+    for (int idx = threadIdx.x; idx < D * CPR; idx += 256) {
+      const int i = idx / CPR, c = idx % CPR;
+      const uint4 v = *(const uint4*)(wg + ((int64_t)i * a.wvs[1] + j0 + c * E::kEPV) * E::kBytes);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int e = 0; e < IPL; ++e) w[e] = lds_elem<E>(wt_lds, j * D + e * 64 + lane);
-#pragma unroll
+      for (int k = 0; k < E::kEPV; ++k) {
+        const int j = c * E::kEPV + k;
+        if constexpr (E::kBytes == 2) ((uint16_t*)wt_lds)[j * D + i] = (uint16_t)(w4[k >> 1] >> (16 * (k & 1)));
+        else ((uint32_t*)wt_lds)[j * D + i] = w4[k];
+      }
+    }
     for (int rho = 0; rho < kFoldRPW; ++rho) {
-      const float ob = o_lds[wave][rho][j];
+      const FoldRow f = fold_row(a, g, tile, wave, rho);
+      for (int j = lane; j < JC; j += 64) o_lds[wave][rho][j] = f.ok ? a.o_base[(int64_t)f.row * DE + j0 + j] : 0.f;
+    }
+    __syncthreads();
+    for (int j = 0; j < JC; ++j) {
+      float w[IPL];
 #pragma unroll
-      for (int e = 0; e < IPL; ++e) acc[rho][e] = fmaf(w[e], ob, acc[rho][e]);
+      for (int e = 0; e < IPL; ++e) w[e] = lds_elem<E>(wt_lds, j * D + e * 64 + lane);
+#pragma unroll
+      for (int rho = 0; rho < kFoldRPW; ++rho) {
+        const float ob = o_lds[wave][rho][j];
+#pragma unroll
+        for (int e = 0; e < IPL; ++e) acc[rho][e] = fmaf(w[e], ob, acc[rho][e]);
+      }
     }
   }
 #pragma unroll
@@ -161,22 +201,25 @@ __global__ __launch_bounds__(256) void k_unfold_values(FoldArgs a, int tiles_per
   }
 }
 
+// Column chunks of 128 for bf16 when D_E allows (32 KB of W per chunk), of
+// 64 otherwise (fp32 rows are twice as wide).
 template <class E, int D>
 hipError_t fold_dispatch(const FoldArgs& a, hipStream_t s, bool unfold, int empty) {
   const int G = a.r.G, Hkv = a.r.Hq / G;
   const int tiles = (a.r.B * a.r.N * G + kFoldRows - 1) / kFoldRows;
   const dim3 grid((unsigned)(Hkv * tiles)), block(256);
-  if (a.DE == 128) {
-    if (unfold) hipLaunchKernelGGL((k_unfold_values<E, D, 128>), grid, block, 0, s, a, tiles, empty);
-    else hipLaunchKernelGGL((k_fold_query<E, D, 128>), grid, block, 0, s, a, tiles);
+  if (E::kBytes == 2 && a.DE % 128 == 0) {
+    if (unfold) hipLaunchKernelGGL((k_unfold_values<E, D, 2>), grid, block, 0, s, a, tiles, empty);
+    else hipLaunchKernelGGL((k_fold_query<E, D, 2>), grid, block, 0, s, a, tiles);
   } else {
-    if (unfold) hipLaunchKernelGGL((k_unfold_values<E, D, 64>), grid, block, 0, s, a, tiles, empty);
-    else hipLaunchKernelGGL((k_fold_query<E, D, 64>), grid, block, 0, s, a, tiles);
+    if (unfold) hipLaunchKernelGGL((k_unfold_values<E, D, 1>), grid, block, 0, s, a, tiles, empty);
+    else hipLaunchKernelGGL((k_fold_query<E, D, 1>), grid, block, 0, s, a, tiles);
   }
   return hipGetLastError();
 }
 
 hipError_t fold_launch(const FoldArgs& a, hipStream_t s, bool unfold, int empty) {
+  if (a.DE % 64 || a.DE < 64) return hipErrorInvalidValue;
   if (a.dtype == kDtypeBF16)
     return a.d == 128 ? fold_dispatch<BF16, 128>(a, s, unfold, empty) : fold_dispatch<BF16, 64>(a, s, unfold, empty);
   return a.d == 128 ? fold_dispatch<F32, 128>(a, s, unfold, empty) : fold_dispatch<F32, 64>(a, s, unfold, empty);

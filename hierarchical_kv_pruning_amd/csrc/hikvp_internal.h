@@ -7,7 +7,8 @@
 namespace hikvp {
 
 constexpr int kMaxK = 256;        // largest Top-K per level
-constexpr int kMaxD = 128;        // largest head dim
+constexpr int kMaxD = 128;        // largest head dim of the per-head trees and the sequence half
+constexpr int kMaxWideD = 4096;   // largest width of a base-embedding tree (a multiple of 128)
 constexpr int kBucketSlots = 32;  // members of a (head, mid) bucket stored without a list walk
 constexpr int kJunkSlots = 1024;  // per-wave sinks for masked-off score stores
 constexpr int kRootTile = 64;     // member rows per mid-GEMM work item (four waves of 16 rows)
@@ -63,6 +64,17 @@ struct RowsDev {
   int B, N, Hq, G;            // G = Hq / Hkv
   int R;                      // B*N*Hq
   double scale;               // logit scale (the fp64 ranking uses exactly this value)
+  // When q_kg holds a rounding (to the tree's dtype) of an exact query -- a
+  // folded W_K^T q or a sum of member queries -- the exact one, by row
+  // index, and a bound on the rounding: the selection is then exact with
+  // respect to the exact query.  NULL otherwise.  In bf16 the scores take
+  // the exact query as the sum of two bf16 rows, q_kg (rounded) + q_lo (the
+  // residual rounded), two MFMA passes on the same keys: the part left out
+  // is ~2^-8 of one bf16 rounding, so the band of exactly re-scored
+  // candidates stays as narrow as for a stored query.
+  const double* q_exact;      // [R, d] fp64
+  const float* q_delta;       // [R] upper bound of |q_kg + q_lo - q_exact|_2 (q_lo NULL: 0)
+  const void* q_lo;           // [R, d] tree dtype (bf16 only), or NULL
 };
 
 // One attend call's selection path (root -> mid -> leaf -> KG attention),
@@ -114,6 +126,8 @@ struct StepArgs {
   int32_t* bucket_ovf;        // [rows * K[1] / (kBucketSlots + 1) + 1] keys (g*M_I + mid) with overflow members
   float* o_kg;                // [R, d] softmax-weighted leaf values (fp32)
   float* lse_kg;              // [R] log-sum-exp of the selected leaf logits
+  int exact_logits;           // non-zero: the KG softmax takes the selected leaves' logits from the
+                              // exact query r.q_exact (fp64 dot products), not from the scores
 };
 
 // Bucket array index of key = g*M_I + mid: a bijective transpose of [0, 64*q)
@@ -158,6 +172,9 @@ struct SharedArgs {
   RowsDev r;                  // the real rows (their own q / q_kg)
   int B, Ng;                  // groups: [B, Ng, Hkv], Ng = N (per token) or 1 (per sequence)
   void* gq;                   // [B, Ng, Hkv, d] group queries, tree dtype
+  double* gqx;                // [B, Ng, Hkv, d] the exact sums (fp64) gq rounds
+  void* glo;                  // [B, Ng, Hkv, d] bf16 only: gqx - gq rounded to bf16
+  float* gdelta;              // [B, Ng, Hkv] upper bound of |gq + glo - gqx|_2 (fp32: |gq - gqx|_2)
   double* gpart;              // [B*Ng*Hkv, chunks, d] fp64 partial sums over chunks of tn tokens
   int chunks, tn;
   const int32_t* sel_leaf;    // [B*Ng*Hkv, KL] leaves selected for each group, -1 padded
@@ -174,6 +191,9 @@ struct FoldArgs {
   int64_t wks[2], wvs[2];     // element strides of head and row (innermost 1)
   int d, DE, dtype;
   void* qf;                   // [R, D_E] folded queries W_K[g]^T q_kg, tree dtype
+  double* qx;                 // [R, D_E] the exact products' sums (fp64) qf rounds
+  void* qlo;                  // [R, D_E] bf16 only: qx - qf rounded to bf16
+  float* qdelta;              // [R] upper bound of |qf + qlo - qx|_2 (fp32: |qf - qx|_2)
   const float* o_base;        // [R, D_E] softmax-weighted base values (the descent's KG half)
   float* o_kg;                // [R, d]
   float* lse_kg;              // [R] (written only when the KG half is empty)

@@ -23,4 +23,21 @@ __device__ inline uint16_t f64_to_bf16_rne(double x) {
   return (uint16_t)((sign << 15) | ((uint32_t)e << 7) | (uint32_t)(keep & 0x7fu));
 }
 
+__device__ inline double bf16_value(uint16_t h) { return (double)__uint_as_float((uint32_t)h << 16); }
+
+// An exact value as the sum of two bf16 values: hi = x rounded, lo = the
+// residual x - hi (exact in fp64) rounded, and what the pair leaves out.
+struct Bf16Split {
+  uint16_t hi, lo;
+  double rest;                 // x - hi - lo
+};
+__device__ inline Bf16Split split_bf16(double x) {
+  Bf16Split s;
+  s.hi = f64_to_bf16_rne(x);
+  const double r = x - bf16_value(s.hi);
+  s.lo = f64_to_bf16_rne(r);
+  s.rest = r - bf16_value(s.lo);
+  return s;
+}
+
 }  // namespace hikvp

@@ -64,14 +64,14 @@ struct RowWork {
   float* stage;                  // [stage] staged scores (or unused)
 };
 
-__host__ __device__ inline size_t rowwork_bytes(int K, int Kp, int D, int stage, int NT = 64) {
-  return selwork_bytes(NT, K, D) + 2 * align16((size_t)K * 4) + align16((size_t)(Kp + 1) * 4) +
+__host__ __device__ inline size_t rowwork_bytes(int K, int Kp, int d, int stage, int NT = 64) {
+  return selwork_bytes(NT, K, d) + 2 * align16((size_t)K * 4) + align16((size_t)(Kp + 1) * 4) +
          align16((size_t)Kp * 8) + align16((size_t)stage * 4);
 }
 
-__device__ inline RowWork carve_rowwork(char* p, int K, int Kp, int D, int stage, int NT = 64) {
+__device__ inline RowWork carve_rowwork(char* p, int K, int Kp, int d, int stage, int NT = 64) {
   RowWork w;
-  w.sel = carve_selwork(p, NT, K, D);
+  w.sel = carve_selwork(p, NT, K, d);
   auto take = [&](size_t bytes) { char* q = p; p += align16(bytes); return q; };
   w.out_node = (int*)take((size_t)K * 4);
   w.out_logit = (float*)take((size_t)K * 4);
@@ -81,18 +81,68 @@ __device__ inline RowWork carve_rowwork(char* p, int K, int Kp, int D, int stage
   return w;
 }
 
+// One MFMA tile of a key-row slice added to acc: the query fragment's
+// products (plus its bf16 residual's, LO) accumulated onto acc, or, for the
+// slices of a wide row (SLICED), accumulated from zero and then added, which
+// keeps the score's error bound at that of 128 + d/128 rounding steps.
+template <class E, int KCH, bool LO, bool SLICED>
+__device__ inline float4_t slice_tile(const uint4 (&afr)[KCH], const uint4 (&alo)[KCH], const uint4 (&bfr)[KCH],
+                                      float4_t acc) {
+  if constexpr (SLICED) {
+    float4_t t = tile_dot<E, KCH>(afr, bfr);
+    if constexpr (LO) t = tile_dot_acc<E, KCH>(alo, bfr, t);
+    return acc + t;
+  } else {
+    acc = tile_dot_acc<E, KCH>(afr, bfr, acc);
+    if constexpr (LO) acc = tile_dot_acc<E, KCH>(alo, bfr, acc);
+    return acc;
+  }
+}
+
+// With a bf16 residual row lo beside the rounded query q (|lo| <= 2^-8 |q|
+// (1 + 2^-8)^2), the scores sum the products of q and of lo: their error
+// bound takes |q| + |lo| <= |q| * kLoNorm, the filter's squared form
+// kLoNorm2.
+constexpr float kLoNorm = 1.004f;
+constexpr float kLoNorm2 = kLoNorm * kLoNorm;
+
 // The row's KG query (exact fp32 copy in LDS) and its 2-norm (rounded up).
-template <class E, int D>
-__device__ inline double load_query(const RowsDev& r, int b, int n, int h, float* qrow, int lane) {
+template <class E>
+__device__ inline double load_query(const RowsDev& r, int b, int n, int h, int d, float* qrow, int lane) {
   const char* qp = (const char*)r.q_kg + q_off(r.qks, b, n, h) * E::kBytes;
   float qq = 0.f;
-  for (int t = lane; t < D; t += 64) {
+  for (int t = lane; t < d; t += 64) {
     const float v = load_f32<E>(qp, t);
     qrow[t] = v;
     qq = fmaf(v, v, qq);
   }
   qq = wave_sum(qq);
-  return sqrt((double)qq) * 1.0001;
+  return sqrt((double)qq) * norm_slack(d) * (r.q_lo ? kLoNorm : 1.f);
+}
+
+// The exact query of a row and the bound on its rounding, when the stored
+// KG query is a rounding of one (else NULL and 0).
+__device__ inline const double* exact_query(const RowsDev& r, int row, int d) {
+  return r.q_exact ? r.q_exact + (int64_t)row * d : nullptr;
+}
+__device__ inline double query_delta(const RowsDev& r, int row) {
+  return r.q_delta ? (double)r.q_delta[row] : 0.0;
+}
+
+// The 16-byte pieces m*64 of a query row from qp (NULL: zeros) for an MFMA
+// fragment, and the sum of their squares.
+template <class E, int KCH>
+__device__ inline float load_frag(uint4 (&afr)[KCH], const char* qp) {
+  float qq = 0.f;
+#pragma unroll
+  for (int m = 0; m < KCH; ++m) {
+    afr[m] = qp ? *(const uint4*)(qp + m * 64) : make_uint4(0, 0, 0, 0);
+    float f[E::kEPV];
+    unpack<E>(afr[m], f);
+#pragma unroll
+    for (int e = 0; e < E::kEPV; ++e) qq = fmaf(f[e], f[e], qq);
+  }
+  return qq;
 }
 
 // The root scores of a row, between k_root_mfma and k_root: the first M_R
@@ -110,10 +160,11 @@ __device__ inline float* root_score_row(const StepArgs& a, int row) {
 // disjoint rows), which k_root reads before the mid level reuses it.
 constexpr int kRootChunk = 64;  // roots per k_root_mfma wave
 
-template <class E, int D>
+template <class E, int D, bool LO>
 __global__ __launch_bounds__(256) void k_root_mfma(StepArgs a, int tph, int nrc) {
-  constexpr int KCH = D * E::kBytes / 64;  // 16-byte pieces per lane per row
-  constexpr int NU = kRootChunk / 16;      // root tiles in flight
+  constexpr int SW = SliceW<D>::W;          // key-row slice width (the whole row unless wide)
+  constexpr int KCH = SW * E::kBytes / 64;  // 16-byte pieces per lane per row slice
+  constexpr int NU = kRootChunk / 16;       // root tiles in flight
   const int lane = threadIdx.x & 63, quad = lane >> 4, col = lane & 15;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (w >= (a.g1 - a.g0) * tph * nrc) return;
@@ -122,16 +173,21 @@ __global__ __launch_bounds__(256) void k_root_mfma(StepArgs a, int tph, int nrc)
   const int per_head = a.r.B * a.r.N * a.r.G;  // rows of one KV head
   const int hb = g * per_head;                 // its first block
   const int MR = (int)a.t.count[0];
-  uint4 afr[KCH];
+  const int d = D ? D : a.t.d;
+  const int ns = d / SW;                       // slices per row
+  const char* qp = nullptr;                    // the lane's row query (+ quad * 16)
+  const char* lp = nullptr;                    // its bf16 residual (LO)
   if (m0 + col < per_head) {
     int b, n, h;
-    decode_row(a.r, row_of_block(a.r, hb + m0 + col), b, n, h);
-    const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes + quad * 16;
-#pragma unroll
-    for (int m = 0; m < KCH; ++m) afr[m] = *(const uint4*)(qp + m * 64);
-  } else {
-#pragma unroll
-    for (int m = 0; m < KCH; ++m) afr[m] = make_uint4(0, 0, 0, 0);
+    const int row = row_of_block(a.r, hb + m0 + col);
+    decode_row(a.r, row, b, n, h);
+    qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes + quad * 16;
+    if constexpr (LO) lp = (const char*)a.r.q_lo + (int64_t)row * d * E::kBytes + quad * 16;
+  }
+  uint4 afr[KCH], alo[KCH];
+  if constexpr (D != 0) {
+    load_frag<E, KCH>(afr, qp);
+    if constexpr (LO) load_frag<E, KCH>(alo, lp);
   }
   // this lane's outputs: rows m0 + 4*quad + v, root j0 + 16*u + col
   float* dst[4];
@@ -144,21 +200,32 @@ __global__ __launch_bounds__(256) void k_root_mfma(StepArgs a, int tph, int nrc)
   const char* kb = key_base(a.t, 0, g, rsb, E::kBytes) + quad * 16;
   const int j1 = min(MR, (rc + 1) * kRootChunk);
   for (int j0 = rc * kRootChunk; j0 < j1; j0 += 16 * NU) {
-    uint4 bfr[NU][KCH];
+    float4_t sc[NU];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const char* kp = kb + (int64_t)min(j0 + 16 * u + col, j1 - 1) * rsb;
+    for (int u = 0; u < NU; ++u) sc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int sl = 0; sl < ns; ++sl) {
+      const int64_t so = (int64_t)sl * SW * E::kBytes;
+      if constexpr (D == 0) {
+        load_frag<E, KCH>(afr, qp ? qp + so : nullptr);
+        if constexpr (LO) load_frag<E, KCH>(alo, lp ? lp + so : nullptr);
+      }
+      uint4 bfr[NU][KCH];
 #pragma unroll
-      for (int m = 0; m < KCH; ++m) bfr[u][m] = *(const uint4*)(kp + m * 64);
+      for (int u = 0; u < NU; ++u) {
+        const char* kp = kb + (int64_t)min(j0 + 16 * u + col, j1 - 1) * rsb + so;
+#pragma unroll
+        for (int m = 0; m < KCH; ++m) bfr[u][m] = *(const uint4*)(kp + m * 64);
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u) sc[u] = slice_tile<E, KCH, LO, D == 0>(afr, alo, bfr[u], sc[u]);
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const float4_t sc = tile_dot<E, KCH>(afr, bfr[u]);
       const int j = j0 + 16 * u + col;
       if (j < j1)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          if (dst[v]) dst[v][j] = sc[v];
+          if (dst[v]) dst[v][j] = sc[u][v];
     }
   }
 }
@@ -171,8 +238,10 @@ __global__ __launch_bounds__(256) void k_root(StepArgs a, size_t wave_bytes, int
   if (blk >= a.blk1) return;  // whole wave; waves never meet at a barrier
   const int MR = (int)a.t.count[0];
   const int K = a.K[0];
-  RowWork W = carve_rowwork(smem + (size_t)wave * wave_bytes, K, 0, D, stage);
+  const int d = D ? D : a.t.d;
+  RowWork W = carve_rowwork(smem + (size_t)wave * wave_bytes, K, 0, d, stage);
   const int row = row_of_block(a.r, blk);
+  W.sel.qx = exact_query(a.r, row, d);
   // the row's scores, from k_root_mfma in the row's mid-candidate region (by
   // row, as the mid level uses it: concurrent parts own disjoint rows),
   // staged in LDS when they fit
@@ -183,15 +252,16 @@ __global__ __launch_bounds__(256) void k_root(StepArgs a, size_t wave_bytes, int
   const int g = h / a.r.G;
   if (stage)
     for (int j = lane; j < MR; j += 64) sc[j] = gsc[j];
-  const double qnorm = load_query<E, D>(a.r, b, n, h, W.sel.qrow, lane);
+  const double qnorm = load_query<E>(a.r, b, n, h, d, W.sel.qrow, lane);
   wave_sync();
 
   int64_t rsb;
   const char* kb = key_base(a.t, 0, g, rsb, E::kBytes);
   const SlotMap ident{nullptr, nullptr, -1};
-  const int k = select_topk<E, D, 64, MemScores<64>, true>(MemScores<64>{sc}, MR, K, twice_err_bound<D>(qnorm, a.t.norm[g]),
-                                      a.r.scale, ident, KeyRows{kb, rsb}, W.sel, W.out_node, W.out_logit,
-                                      lane);
+  const double err2 = twice_err_bound(qnorm, a.t.norm[g], d, query_delta(a.r, row));
+  const int k = select_topk<E, D, 64, MemScores<64>, true>(MemScores<64>{sc}, MR, K, err2, a.r.scale, ident,
+                                                           KeyRows{kb, rsb}, W.sel, W.out_node, W.out_logit,
+                                                           lane);
   int32_t* out = a.sel[0] + (int64_t)row * K;
   for (int i = lane; i < K; i += 64) out[i] = i < k ? W.out_node[i] : -1;
   // count the row in each selected (head, root) group, on the row's
@@ -388,17 +458,18 @@ __device__ inline void stage_put(const U32x4 (&stg)[PPT], char* buf, int tid) {
   }
 }
 
-template <class E, int D>
+template <class E, int D, bool LO>
 __global__ __launch_bounds__(64 * kMidWaves) void k_mid_gemm(StepArgs a) {
-  constexpr int KCH = D * E::kBytes / 64;  // 16-byte pieces per lane per row
-  constexpr int RB = D * E::kBytes;        // bytes per key row
+  constexpr int SW = SliceW<D>::W;         // key-row slice width (the whole row unless wide)
+  constexpr int KCH = SW * E::kBytes / 64; // 16-byte pieces per lane per row slice
+  constexpr int RB = SW * E::kBytes;       // bytes per staged key-row slice
   constexpr int LRB = RB + kMidPad;        // LDS bytes per staged child
   constexpr int TU = 2;                    // child tiles per round = consecutive children per lane
   constexpr int RC = 16 * TU;              // children per round
   constexpr int CR = kChunkRounds;         // rounds per chunk
   constexpr int NV = CR * TU;              // keys per lane per row in a chunk
   constexpr int NT = 64 * kMidWaves;
-  constexpr int PPT = RC * RB / 16 / NT;   // 16-byte pieces each thread stages per round
+  constexpr int PPT = RC * RB / 16 / NT;   // 16-byte pieces each thread stages per round slice
   static_assert(PPT >= 1 && RC * RB / 16 == PPT * NT, "a round's children split evenly over the threads");
   __shared__ __align__(16) char lds[2][RC * LRB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -406,6 +477,8 @@ __global__ __launch_bounds__(64 * kMidWaves) void k_mid_gemm(StepArgs a) {
   const int ntiles = *a.root_ntiles;
   const int MR = (int)a.t.count[0];
   const int K0 = a.K[0], K1 = a.K[1];
+  const int d = D ? D : a.t.d;
+  const int ns = d / SW;                   // slices per key row; a stage is one (round, slice)
   const bool filt = K1 <= kFilterK;
   const int64_t* off0 = a.t.off[0];
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {  // uniform over the workgroup
@@ -420,48 +493,45 @@ __global__ __launch_bounds__(64 * kMidWaves) void k_mid_gemm(StepArgs a) {
     const float knorm = a.t.norm[a.t.Hkv + g];
     int64_t rsb;
     const char* kb = key_base(a.t, 1, g, rsb, E::kBytes) + first * rsb;
-    if (F > 0) {  // round 0 staged
+    if (F > 0) {  // stage 0 staged
       U32x4 stg[PPT];
       stage_round<RB, NT, PPT>(stg, kb, rsb, 0, F, tid);
       stage_put<RB, LRB, NT, PPT>(stg, lds[0], tid);
     }
     // A fragment (members) and this lane's output rows (member 4*quad + v):
     // row, first slot | selection index << 24 (row -1: none)
-    uint4 afr[KCH];
+    uint4 afr[KCH], alo[KCH];
+    const char* qp = nullptr;                  // this lane's member query (+ quad * 16), NULL past the members
+    const char* lp = nullptr;                  // its bf16 residual (LO)
     int orow[4], obk[4];
     float qnv[4], wf[4];                       // query-norm bound, filter margin
     {
       const int mi = m0 + col;
       const int2 mem = active && mi < cnt ? a.root_members[(int64_t)toff * kRootTile + mi] : make_int2(-1, 0);
-      float qq = 0.f;
       if (mem.x >= 0) {
         int b, n, h;
         decode_row(a.r, mem.x, b, n, h);
-        const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes;
-#pragma unroll
-        for (int m = 0; m < KCH; ++m) {
-          afr[m] = *(const uint4*)(qp + m * 64 + quad * 16);
-          float f[E::kEPV];
-          unpack<E>(afr[m], f);
-#pragma unroll
-          for (int e = 0; e < E::kEPV; ++e) qq = fmaf(f[e], f[e], qq);
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < KCH; ++m) afr[m] = make_uint4(0, 0, 0, 0);
+        qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes + quad * 16;
+        if constexpr (LO) lp = (const char*)a.r.q_lo + (int64_t)mem.x * d * E::kBytes + quad * 16;
       }
+      float qq = 0.f;
+      for (int sl = 0; sl < ns; ++sl) qq += load_frag<E, KCH>(afr, qp ? qp + (int64_t)sl * RB : nullptr);
+      if constexpr (D != 0 && LO) load_frag<E, KCH>(alo, lp);
       qq += __shfl_xor(qq, 16);
       qq += __shfl_xor(qq, 32);                // member col's |q|^2 (every quad)
+      if constexpr (LO) qq *= kLoNorm2;        // |q + lo|^2 <= |q|^2 * kLoNorm2
+      const float qd = mem.x >= 0 && a.r.q_delta ? a.r.q_delta[mem.x] : 0.f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int ms = 4 * quad + v;
         orow[v] = __shfl(mem.x, ms);           // -1 past the members
         obk[v] = __shfl(mem.y, ms);
-        // the row's |q| bound (fp32 sum of squares in any order: 0.1 %
-        // slack) and twice the select's band half-width for it (its error
-        // bound 2E and its slack on T, |T| <= |q| max|k|)
-        qnv[v] = sqrtf(__shfl(qq, ms)) * 1.001f;
-        const float e2 = 2.f * qnv[v] * knorm * (float)D * (1.f / 8388608.f);
+        // the row's |q| bound (fp32 sum of squares in any order) and twice
+        // the select's band half-width for it (its error bound 2E, with the
+        // rounding of an exact query if any, and its slack on T, |T| <= |q| max|k|)
+        qnv[v] = sqrtf(__shfl(qq, ms)) * norm_slack(d) * 1.001f;
+        const float e2 = 2.f * qnv[v] * knorm * (float)err_terms(d) * (1.f / 8388608.f) +
+                         2.f * __shfl(qd, ms) * knorm * 1.001f;
         wf[v] = 2.f * (e2 * 1.01f + 4.f * qnv[v] * knorm * (1.f / 8388608.f)) + 1e-30f;
       }
     }
@@ -474,33 +544,51 @@ __global__ __launch_bounds__(64 * kMidWaves) void k_mid_gemm(StepArgs a) {
 #pragma unroll
       for (int i = 0; i < kLaneTop; ++i) top[v][i] = 0;
     }
-    __syncthreads();                           // round 0 staged
+    __syncthreads();                           // stage 0 staged
     const int nr = (F + RC - 1) / RC;
+    const int nst = nr * ns;                   // stages
     for (int cc = 0; cc < nr; cc += CR) {      // chunks of CR rounds
       uint32_t x[4][NV];                       // the chunk's keys (0: past the span)
 #pragma unroll
       for (int r = 0; r < CR; ++r) {
         const int rr = cc + r;
         if (rr < nr) {                         // uniform over the workgroup
-          const bool more = rr + 1 < nr;
-          U32x4 stg[PPT];                      // the next round, in flight while this one is scored
-          if (more) stage_round<RB, NT, PPT>(stg, kb, rsb, (rr + 1) * RC, F, tid);
-          if (active) {
-            // in tile u, lane column col is child rr*RC + col*TU + u
-            const char* lb = lds[rr & 1] + quad * 16;
+          float4_t p[TU];
+#pragma unroll
+          for (int u = 0; u < TU; ++u) p[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+          for (int sl = 0; sl < ns; ++sl) {
+            const int st = rr * ns + sl;
+            const bool more = st + 1 < nst;
+            U32x4 stg[PPT];                    // the next stage, in flight while this one is scored
+            if (more) {
+              const int nrr = (st + 1) / ns, nsl = (st + 1) % ns;
+              stage_round<RB, NT, PPT>(stg, kb + (int64_t)nsl * RB, rsb, nrr * RC, F, tid);
+            }
+            if (active) {
+              if constexpr (D == 0) {
+                load_frag<E, KCH>(afr, qp ? qp + (int64_t)sl * RB : nullptr);
+                if constexpr (LO) load_frag<E, KCH>(alo, lp ? lp + (int64_t)sl * RB : nullptr);
+              }
+              // in tile u, lane column col is child rr*RC + col*TU + u
+              const char* lb = lds[st & 1] + quad * 16;
+#pragma unroll
+              for (int u = 0; u < TU; ++u) {
+                uint4 bfr[KCH];
+#pragma unroll
+                for (int m = 0; m < KCH; ++m) bfr[m] = *(const uint4*)(lb + (col * TU + u) * LRB + m * 64);
+                p[u] = slice_tile<E, KCH, LO, D == 0>(afr, alo, bfr, p[u]);
+              }
+            }
+            if (more) stage_put<RB, LRB, NT, PPT>(stg, lds[(st + 1) & 1], tid);
+            __syncthreads();
+          }
+          if (active)
 #pragma unroll
             for (int u = 0; u < TU; ++u) {
-              uint4 bfr[KCH];
-#pragma unroll
-              for (int m = 0; m < KCH; ++m) bfr[m] = *(const uint4*)(lb + (col * TU + u) * LRB + m * 64);
-              const float4_t p = tile_dot<E, KCH>(afr, bfr);
               const bool valid = rr * RC + col * TU + u < F;
 #pragma unroll
-              for (int v = 0; v < 4; ++v) x[v][r * TU + u] = valid ? ord_key(p[v]) : 0u;
+              for (int v = 0; v < 4; ++v) x[v][r * TU + u] = valid ? ord_key(p[u][v]) : 0u;
             }
-          }
-          if (more) stage_put<RB, LRB, NT, PPT>(stg, lds[(rr + 1) & 1], tid);
-          __syncthreads();
         } else {
 #pragma unroll
           for (int u = 0; u < TU; ++u)
@@ -536,13 +624,13 @@ __global__ __launch_bounds__(64 * kMidWaves) void k_mid_gemm(StepArgs a) {
         for (int q = 0; q < NV; ++q) nk += (x[v][q] != 0u && x[v][q] >= lo[v]) ? 1 : 0;
         const int incl = row_incl_sum(nk);
         if (orow[v] >= 0) {
-          uint2* d = a.mid_pairs + (int64_t)orow[v] * a.c1max + (obk[v] & 0xffffff);
+          uint2* dp = a.mid_pairs + (int64_t)orow[v] * a.c1max + (obk[v] & 0xffffff);
           int pos = run[v] + incl - nk;
 #pragma unroll
           for (int q = 0; q < NV; ++q)
             if (x[v][q] != 0u && x[v][q] >= lo[v])
-              d[pos++] = make_uint2(__float_as_uint(ord_float(x[v][q])),
-                                    (uint32_t)(cc * RC + RC * (q / TU) + col * TU + (q % TU)));
+              dp[pos++] = make_uint2(__float_as_uint(ord_float(x[v][q])),
+                                     (uint32_t)(cc * RC + RC * (q / TU) + col * TU + (q % TU)));
         }
         run[v] += __shfl(incl, (lane & 48) | 15);   // the row's total: the DPP row's last lane
       }
@@ -574,14 +662,17 @@ __device__ inline int first_parent(const StepArgs& a, int row, int lev, int gtid
 template <class E, int D, int NT>
 __device__ inline int select_prologue(const StepArgs& a, const RowWork& W, int row, int lev, int& g,
                                       double& qnorm, int gtid, int p0) {
-  constexpr int QPT = (D + NT - 1) / NT;
+  constexpr int QPT = D ? (D + NT - 1) / NT : 1;  // query elements per thread held (fixed widths)
+  const int d = D ? D : a.t.d;
   int b, n, h;
   decode_row(a.r, row, b, n, h);
   g = h / a.r.G;
   const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes;
   float qv[QPT];
+  if constexpr (D != 0) {
 #pragma unroll
-  for (int j = 0; j < QPT; ++j) qv[j] = gtid + j * NT < D ? load_f32<E>(qp, gtid + j * NT) : 0.f;
+    for (int j = 0; j < QPT; ++j) qv[j] = gtid + j * NT < D ? load_f32<E>(qp, gtid + j * NT) : 0.f;
+  }
   const int64_t* off = a.t.off[lev - 1];
   int64_t first0 = 0;
   int fan0 = 0;
@@ -589,16 +680,21 @@ __device__ inline int select_prologue(const StepArgs& a, const RowWork& W, int r
     first0 = off[p0];
     fan0 = (int)(off[p0 + 1] - first0);
   }
+  if constexpr (D != 0) {
 #pragma unroll
-  for (int j = 0; j < QPT; ++j)
-    if (gtid + j * NT < D) W.sel.qrow[gtid + j * NT] = qv[j];
+    for (int j = 0; j < QPT; ++j)
+      if (gtid + j * NT < D) W.sel.qrow[gtid + j * NT] = qv[j];
+  } else {
+    for (int t = gtid; t < d; t += NT) W.sel.qrow[t] = load_f32<E>(qp, t);
+  }
   group_sync<NT>();
   const int Kp = a.K[lev - 1];
   if (gtid < 64) {
     float qq = 0.f;
-    for (int t = gtid; t < D; t += 64) qq = fmaf(W.sel.qrow[t], W.sel.qrow[t], qq);
+    for (int t = gtid; t < d; t += 64) qq = fmaf(W.sel.qrow[t], W.sel.qrow[t], qq);
     qq = wave_sum(qq);
-    if (gtid == 0) W.sel.ctl[7] = __float_as_int((float)(sqrt((double)qq) * 1.0001));
+    if (gtid == 0)
+      W.sel.ctl[7] = __float_as_int((float)(sqrt((double)qq) * norm_slack(d) * (a.r.q_lo ? kLoNorm : 1.f)));
     build_candidates(a.sel[lev - 1] + (int64_t)row * Kp, Kp, off, gtid, W.pre, W.base, first0, fan0);
   }
   group_sync<NT>();
@@ -704,19 +800,21 @@ struct MidMemMap {
 
 // LDS of one k_mid_select wave: the select's work area, cpre, (k, j) of the
 // register-held entries.
-__host__ __device__ inline size_t mid_select_wave_bytes(int K1, int K0, int D, int SPT) {
-  return rowwork_bytes(K1, K0, D, 0) + align16((size_t)(K0 + 1) * 4) + align16((size_t)64 * SPT * 4);
+__host__ __device__ inline size_t mid_select_wave_bytes(int K1, int K0, int d, int SPT) {
+  return rowwork_bytes(K1, K0, d, 0) + align16((size_t)(K0 + 1) * 4) + align16((size_t)64 * SPT * 4);
 }
 
 // Stages the row's KG query in the select's work area (exact fp32 copy), for
-// the exact re-score of a band, which needs it.
-template <class E, int D>
+// the exact re-score of a band, which needs it (unless it re-scores with the
+// exact query).
+template <class E>
 struct StageQuery {
   const char* qp;
   float* qrow;
+  int d;
   int lane;
   __device__ void operator()() const {
-    for (int t = lane; t < D; t += 64) qrow[t] = load_f32<E>(qp, t);
+    for (int t = lane; t < d; t += 64) qrow[t] = load_f32<E>(qp, t);
     wave_sync();
   }
 };
@@ -731,13 +829,15 @@ __device__ inline void mid_select_row(StepArgs a, size_t wave_bytes) {
   const int blk = a.blk0 + blockIdx.x * nwave + wave;
   if (blk >= a.blk1) return;  // whole wave; waves never meet at a barrier
   const int K0 = a.K[0], K1 = a.K[1];
+  const int d = D ? D : a.t.d;
   char* p = smem + (size_t)wave * wave_bytes;
-  RowWork W = carve_rowwork(p, K1, K0, D, 0);
-  p += rowwork_bytes(K1, K0, D, 0);
+  RowWork W = carve_rowwork(p, K1, K0, d, 0);
+  p += rowwork_bytes(K1, K0, d, 0);
   int* cpre = (int*)p;
   p += align16((size_t)(K0 + 1) * 4);
   int* kj = (int*)p;
   const int row = row_of_block(a.r, blk);
+  W.sel.qx = exact_query(a.r, row, d);
   int b, n, h;
   decode_row(a.r, row, b, n, h);
   const int g = h / a.r.G;
@@ -762,8 +862,8 @@ __device__ inline void mid_select_row(StepArgs a, size_t wave_bytes) {
   const MidEntries me{a.mid_pairs + (int64_t)row * a.c1max, cpre, W.pre, W.base, K0};
   int64_t rsb;
   const char* kb = key_base(a.t, 1, g, rsb, E::kBytes);
-  const double err2 = twice_err_bound<D>((double)qn, a.t.norm[a.t.Hkv + g]);
-  const StageQuery<E, D> ql{(const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes, W.sel.qrow, lane};
+  const double err2 = twice_err_bound((double)qn, a.t.norm[a.t.Hkv + g], d, query_delta(a.r, row));
+  const StageQuery<E> ql{(const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes, W.sel.qrow, d, lane};
   int k1;
   if (cnt <= 64 * SPT) {
     MidRegScores<SPT> src;
@@ -780,11 +880,11 @@ __device__ inline void mid_select_row(StepArgs a, size_t wave_bytes) {
       }
     }
     wave_sync();
-    k1 = select_topk<E, D, 64, MidRegScores<SPT>, true, MidRegMap, StageQuery<E, D>>(
+    k1 = select_topk<E, D, 64, MidRegScores<SPT>, true, MidRegMap, StageQuery<E>>(
         src, cnt, K1, err2, a.r.scale, MidRegMap{kj, W.pre, W.base}, KeyRows{kb, rsb}, W.sel, W.out_node,
         W.out_logit, lane, ql);
   } else {
-    k1 = select_topk<E, D, 64, MidMemScores, false, MidMemMap, StageQuery<E, D>>(
+    k1 = select_topk<E, D, 64, MidMemScores, false, MidMemMap, StageQuery<E>>(
         MidMemScores{me}, cnt, K1, err2, a.r.scale, MidMemMap{me}, KeyRows{kb, rsb}, W.sel, W.out_node,
         W.out_logit, lane, ql);
   }
@@ -914,6 +1014,15 @@ __global__ void k_bucket_link(StepArgs a) {
   }
 }
 
+// One tile of member scores: the query fragment's products, plus those of
+// its bf16 residual (LO) on the same keys.
+template <class E, int KP, bool LO>
+__device__ inline float4_t member_tile(const uint4 (&afr)[KP], const uint4 (&alo)[KP], const uint4 (&bfr)[KP]) {
+  float4_t t = tile_dot<E, KP>(afr, bfr);
+  if constexpr (LO) t = tile_dot_acc<E, KP>(alo, bfr, t);
+  return t;
+}
+
 // Scores of one group of up to 8 member rows of a bucket over its leaf span,
 // on half-split MFMA tiles: the group is the M side and the span's keys the N
 // side.  Lanes g0 .. g0+7 of mem hold the members (row, first leaf slot),
@@ -923,7 +1032,7 @@ __global__ void k_bucket_link(StepArgs a) {
 // written with one 16-byte store.  Every member's scores go through exactly
 // this arithmetic, whichever group or kernel it lands in, so they do not
 // depend on the (atomic) order in which members joined the bucket.
-template <class E, int D>
+template <class E, int D, bool LO>
 __device__ inline void score_member_group(const StepArgs& a, const char* kp, int64_t rsb, int F, int2 mem,
                                           int g0, int gcnt, int lane) {
   constexpr int RB = D * E::kBytes;        // bytes per key row
@@ -931,8 +1040,8 @@ __device__ inline void score_member_group(const StepArgs& a, const char* kp, int
   constexpr int TU = 4;                    // tiles per round = consecutive keys per lane
   const int quad = lane >> 4, item = lane & 7;
   const bool owner = lane < 32 && (lane & 15) < 8;   // holds combined scores
-  // A fragment: member `item`, zeros past the members
-  uint4 afr[KP];
+  // A fragment: member `item` (and its bf16 residual, LO), zeros past the members
+  uint4 afr[KP], alo[KP];
   const int row = __shfl(mem.x, g0 + item);
   if (item < gcnt) {
     int b, n, h;
@@ -940,9 +1049,14 @@ __device__ inline void score_member_group(const StepArgs& a, const char* kp, int
     const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes + split_off(lane, 0);
 #pragma unroll
     for (int m = 0; m < KP; ++m) afr[m] = *(const uint4*)(qp + m * 128);
+    if constexpr (LO) {
+      const char* lp = (const char*)a.r.q_lo + (int64_t)row * D * E::kBytes + split_off(lane, 0);
+#pragma unroll
+      for (int m = 0; m < KP; ++m) alo[m] = *(const uint4*)(lp + m * 128);
+    }
   } else {
 #pragma unroll
-    for (int m = 0; m < KP; ++m) afr[m] = make_uint4(0, 0, 0, 0);
+    for (int m = 0; m < KP; ++m) afr[m] = alo[m] = make_uint4(0, 0, 0, 0);
   }
   // owners store members 4*quad + vv, keys t0 + item*TU .. + TU-1
   float* dst[4];
@@ -985,7 +1099,7 @@ __device__ inline void score_member_group(const StepArgs& a, const char* kp, int
     load_round(t0, bfr);
     store_full();
 #pragma unroll
-    for (int u = 0; u < TU; ++u) prev[u] = split_combine(tile_dot<E, KP>(afr, bfr[u]), lane);
+    for (int u = 0; u < TU; ++u) prev[u] = split_combine(member_tile<E, KP, LO>(afr, alo, bfr[u]), lane);
     pt0 = t0;
   }
   if (t0 < F) {  // last, partial round
@@ -993,7 +1107,7 @@ __device__ inline void score_member_group(const StepArgs& a, const char* kp, int
     load_round(t0, bfr);
     store_full();
 #pragma unroll
-    for (int u = 0; u < TU; ++u) prev[u] = split_combine(tile_dot<E, KP>(afr, bfr[u]), lane);
+    for (int u = 0; u < TU; ++u) prev[u] = split_combine(member_tile<E, KP, LO>(afr, alo, bfr[u]), lane);
     const int c0 = t0 + item * TU;
 #pragma unroll
     for (int vv = 0; vv < 4; ++vv)
@@ -1005,10 +1119,80 @@ __device__ inline void score_member_group(const StepArgs& a, const char* kp, int
   }
 }
 
+// Wide key rows (base-embedding trees): the same tiles and item layout over
+// 128-element slices of the row, each round's tiles accumulated over the
+// slices before the two halves are combined; no software pipelining.
+template <class E, bool LO>
+__device__ inline void score_member_group_wide(const StepArgs& a, const char* kp, int64_t rsb, int F, int2 mem,
+                                               int g0, int gcnt, int lane) {
+  constexpr int SW = 128;
+  constexpr int RB = SW * E::kBytes;       // bytes per key-row slice
+  constexpr int KP = RB / 128;             // 16-byte pieces per lane per tile and slice
+  constexpr int TU = 4;                    // tiles per round = consecutive keys per lane
+  const int ns = a.t.d / SW;
+  const int quad = lane >> 4, item = lane & 7;
+  const bool owner = lane < 32 && (lane & 15) < 8;   // holds combined scores
+  const int row = __shfl(mem.x, g0 + item);
+  const char* qp = nullptr;                // member `item`'s query (+ this lane's piece offset)
+  const char* lp = nullptr;                // its bf16 residual (LO)
+  if (item < gcnt) {
+    int b, n, h;
+    decode_row(a.r, row, b, n, h);
+    qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes + split_off(lane, 0);
+    if constexpr (LO) lp = (const char*)a.r.q_lo + (int64_t)row * a.t.d * E::kBytes + split_off(lane, 0);
+  }
+  float* dst[4];
+#pragma unroll
+  for (int vv = 0; vv < 4; ++vv) {
+    const int ms = 4 * (quad & 1) + vv;
+    const int srow = __shfl(mem.x, g0 + ms), sbase = __shfl(mem.y, g0 + ms);
+    dst[vv] = (owner && ms < gcnt) ? a.leaf_scores + (int64_t)srow * a.c2max + sbase + item * TU : nullptr;
+  }
+  for (int t0 = 0; t0 < F; t0 += 8 * TU) {
+    float4_t acc[TU];
+#pragma unroll
+    for (int u = 0; u < TU; ++u) acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int sl = 0; sl < ns; ++sl) {
+      const int64_t so = (int64_t)sl * RB;
+      uint4 afr[KP], alo[KP], bfr[TU][KP];
+#pragma unroll
+      for (int m = 0; m < KP; ++m) {
+        afr[m] = qp ? *(const uint4*)(qp + so + m * 128) : make_uint4(0, 0, 0, 0);
+        if constexpr (LO) alo[m] = lp ? *(const uint4*)(lp + so + m * 128) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < TU; ++u) {
+        const char* p = kp + (int64_t)min(t0 + item * TU + u, F - 1) * rsb + so;
+#pragma unroll
+        for (int m = 0; m < KP; ++m) bfr[u][m] = load_nt(p + m * 128);
+      }
+#pragma unroll
+      for (int u = 0; u < TU; ++u) acc[u] = slice_tile<E, KP, LO, true>(afr, alo, bfr[u], acc[u]);
+    }
+    float4_t sc[TU];
+#pragma unroll
+    for (int u = 0; u < TU; ++u) sc[u] = split_combine(acc[u], lane);
+    const int c0 = t0 + item * TU;
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv)
+      if (dst[vv])
+#pragma unroll
+        for (int u = 0; u < TU; ++u)
+          if (c0 + u < F) dst[vv][t0 + u] = sc[u][vv];
+  }
+}
+
+template <class E, int D, bool LO>
+__device__ inline void score_members(const StepArgs& a, const char* kp, int64_t rsb, int F, int2 mem, int g0,
+                                     int gcnt, int lane) {
+  if constexpr (D == 0) score_member_group_wide<E, LO>(a, kp, rsb, F, mem, g0, gcnt, lane);
+  else score_member_group<E, D, LO>(a, kp, rsb, F, mem, g0, gcnt, lane);
+}
+
 // One wave per bucket: its first kBucketSlots members, 8 at a time (a bucket
 // with more than 8 members makes further passes over its span, mostly L2
 // hits); members past kBucketSlots are left to k_leaf_score_overflow.
-template <class E, int D>
+template <class E, int D, bool LO>
 __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
   // descriptor v of the concatenated sub-lists: lane s holds sub-list s's
@@ -1036,7 +1220,7 @@ __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
     cnt = cnt < kBucketSlots ? cnt : kBucketSlots;
     const int2 mem = lane < kBucketSlots ? a.bucket_slot[(int64_t)key * kBucketSlots + lane] : make_int2(-1, 0);
     for (int g0 = 0; g0 < cnt; g0 += 8)
-      score_member_group<E, D>(a, kp, rsb, F, mem, g0, min(8, cnt - g0), lane);
+      score_members<E, D, LO>(a, kp, rsb, F, mem, g0, min(8, cnt - g0), lane);
     cur = nxt;
     v = vn;
   }
@@ -1045,7 +1229,7 @@ __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
 // Members of buckets with more than kBucketSlots rows: one wave per listed
 // bucket walks its overflow list and scores the members 8 at a time with the
 // same group arithmetic as k_leaf_score.
-template <class E, int D>
+template <class E, int D, bool LO>
 __global__ __launch_bounds__(256) void k_leaf_score_overflow(StepArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
   const int nov = a.bucket_count[kDescSub];
@@ -1068,7 +1252,7 @@ __global__ __launch_bounds__(256) void k_leaf_score_overflow(StepArgs a) {
         e = a.bucket_next[e];
       }
       const int2 gm = (lane < gcnt) ? make_int2(mine / K1, a.mid_base[mine]) : make_int2(-1, 0);
-      score_member_group<E, D>(a, kp, rsb, F, gm, 0, gcnt, lane);
+      score_members<E, D, LO>(a, kp, rsb, F, gm, 0, gcnt, lane);
     }
   }
 }
@@ -1078,14 +1262,16 @@ __global__ __launch_bounds__(256) void k_leaf_score_overflow(StepArgs a) {
 // ---------------------------------------------------------------------------
 template <class E, int D, int NT, int SPT>
 __device__ inline void leaf_select_body(const StepArgs& a, size_t group_bytes) {
-  constexpr int DPL = D / 64;
+  constexpr int SW = SliceW<D>::W;  // value-row slice width (the whole row unless wide)
   extern __shared__ __align__(16) char smem[];
   const int groups = blockDim.x / NT, grp = threadIdx.x / NT, gtid = threadIdx.x % NT;
   const int blk = a.blk0 + blockIdx.x * groups + grp;
   if (blk >= a.blk1) return;
   const int K2 = a.K[2];
-  RowWork W = carve_rowwork(smem + (size_t)grp * group_bytes, K2, a.K[1], D, 0, NT);
+  const int d = D ? D : a.t.d;
+  RowWork W = carve_rowwork(smem + (size_t)grp * group_bytes, K2, a.K[1], d, 0, NT);
   const int row = row_of_block(a.r, blk);
+  W.sel.qx = exact_query(a.r, row, d);
   const int p0 = first_parent(a, row, 2, gtid);
   const auto sc = RowScores<NT, SPT>::make(a.leaf_scores + (int64_t)row * a.c2max, (int)a.c2max, gtid);
   int g;
@@ -1093,22 +1279,48 @@ __device__ inline void leaf_select_body(const StepArgs& a, size_t group_bytes) {
   const int n2 = select_prologue<E, D, NT>(a, W, row, 2, g, qnorm, gtid, p0);
   int64_t rsb;
   const char* kb = key_base(a.t, 2, g, rsb, E::kBytes);
-  const int k2 = select_topk<E, D, NT>(sc, n2, K2,
-                                       twice_err_bound<D>(qnorm, a.t.norm[2 * a.t.Hkv + g]), a.r.scale,
-                                       SlotMap{W.pre, W.base, a.K[1]}, KeyRows{kb, rsb}, W.sel,
-                                       W.out_node, W.out_logit, gtid);
+  const double err2 = twice_err_bound(qnorm, a.t.norm[2 * a.t.Hkv + g], d, query_delta(a.r, row));
+  const int k2 = select_topk<E, D, NT>(sc, n2, K2, err2, a.r.scale, SlotMap{W.pre, W.base, a.K[1]},
+                                       KeyRows{kb, rsb}, W.sel, W.out_node, W.out_logit, gtid);
   int32_t* o2 = a.sel[2] + (int64_t)row * K2;
   for (int i = gtid; i < K2; i += NT) o2[i] = i < k2 ? W.out_node[i] : -1;
   if (gtid >= 64) return;  // the KG half is formed by the group's first wave
   const int lane = gtid;
 
   // KG half: softmax over the selected leaves' logits, weighted values
-  float* okg = a.o_kg + (int64_t)row * D;
+  float* okg = a.o_kg + (int64_t)row * d;
   if (k2 == 0) {
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) okg[lane * DPL + e] = 0.f;
+    for (int e = lane; e < d; e += 64) okg[e] = 0.f;
     if (lane == 0) a.lse_kg[row] = -INFINITY;
     return;
+  }
+  if (a.exact_logits && W.sel.qx) {
+    // the logits of an exact query: fp64 dot products of it with the
+    // selected keys (the scores are those of its rounding).  L lanes a key
+    // (as many keys at once as fit the wave), each summing every L-th
+    // 16-byte piece of the key row, then the L partial sums are added.
+    int p2 = 1;
+    while (p2 < k2 && p2 < 64) p2 <<= 1;
+    const int L = 64 / p2;
+    const int npieces = d / E::kEPV;
+    for (int i0 = 0; i0 < k2; i0 += p2) {
+      const int i = i0 + lane / L;
+      double acc = 0.0;
+      if (i < k2) {
+        const char* kr = kb + (int64_t)W.out_node[i] * rsb;
+        for (int c = lane % L; c < npieces; c += L) {
+          const uint4 v = *(const uint4*)(kr + c * 16);
+          float f[E::kEPV];
+          unpack<E>(v, f);
+          const double* q = W.sel.qx + c * E::kEPV;
+#pragma unroll
+          for (int t = 0; t < E::kEPV; ++t) acc = fma(q[t], (double)f[t], acc);
+        }
+      }
+      for (int m = 1; m < L; m <<= 1) acc += __shfl_xor(acc, m);
+      if (i < k2 && lane % L == 0) W.out_logit[i] = (float)(a.r.scale * acc);
+    }
+    wave_sync();
   }
   float mx = -INFINITY;
   for (int i = lane; i < k2; i += 64) mx = fmaxf(mx, W.out_logit[i]);
@@ -1121,45 +1333,48 @@ __device__ inline void leaf_select_body(const StepArgs& a, size_t group_bytes) {
   }
   sum = wave_sum(sum);
   wave_sync();
-  // Value rows are read 16 bytes a lane, LPK lanes a row, so one load
-  // instruction covers KPW rows and VU instructions in flight cover the
+  // Value rows are read 16 bytes a lane, LPK lanes a row (slice), so one
+  // load instruction covers KPW rows and VU instructions in flight cover the
   // K_L rows of a row in one or two memory round trips; each lane sums its
   // dims over the rows of its lane group, then the KPW groups are added.
-  constexpr int EPV = E::kEPV, LPK = D / EPV, KPW = 64 / LPK;
+  // Wide rows take their 128-element slices one after the other.
+  constexpr int EPV = E::kEPV, LPK = SW / EPV, KPW = 64 / LPK;
   constexpr int VU = 8;
   const int sub = lane / LPK, ch = lane % LPK;
-  const char* vb = (const char*)a.t.leaf_v + (int64_t)g * a.t.hs[3] * E::kBytes + ch * 16;
   const int64_t vrs = a.t.rs[3] * E::kBytes;
-  float acc[EPV];
-#pragma unroll
-  for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
-  for (int i0 = 0; i0 < k2; i0 += KPW * VU) {
-    uint4 raw[VU];
-#pragma unroll
-    for (int u = 0; u < VU; ++u) {
-      const int i = i0 + u * KPW + sub;
-      raw[u] = i < k2 ? *(const uint4*)(vb + (int64_t)W.out_node[i] * vrs) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < VU; ++u) {
-      const int i = i0 + u * KPW + sub;
-      const float w = i < k2 ? W.out_logit[i] : 0.f;
-      float v[EPV];
-      unpack<E>(raw[u], v);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) acc[e] = fmaf(w, v[e], acc[e]);
-    }
-  }
-#pragma unroll
-  for (int m = LPK; m < 64; m <<= 1)
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) acc[e] += __shfl_xor(acc[e], m);
   const float inv = 1.f / sum;
-  if (sub == 0) {
-    float4* dst = (float4*)(okg + ch * EPV);
+  for (int s0 = 0; s0 < d; s0 += SW) {
+    const char* vb = (const char*)a.t.leaf_v + ((int64_t)g * a.t.hs[3] + s0) * E::kBytes + ch * 16;
+    float acc[EPV];
 #pragma unroll
-    for (int e = 0; e < EPV; e += 4)
-      dst[e / 4] = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+    for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
+    for (int i0 = 0; i0 < k2; i0 += KPW * VU) {
+      uint4 raw[VU];
+#pragma unroll
+      for (int u = 0; u < VU; ++u) {
+        const int i = i0 + u * KPW + sub;
+        raw[u] = i < k2 ? *(const uint4*)(vb + (int64_t)W.out_node[i] * vrs) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < VU; ++u) {
+        const int i = i0 + u * KPW + sub;
+        const float w = i < k2 ? W.out_logit[i] : 0.f;
+        float v[EPV];
+        unpack<E>(raw[u], v);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[e] = fmaf(w, v[e], acc[e]);
+      }
+    }
+#pragma unroll
+    for (int m = LPK; m < 64; m <<= 1)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc[e] += __shfl_xor(acc[e], m);
+    if (sub == 0) {
+      float4* dst = (float4*)(okg + s0 + ch * EPV);
+#pragma unroll
+      for (int e = 0; e < EPV; e += 4)
+        dst[e / 4] = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+    }
   }
   if (lane == 0) a.lse_kg[row] = mx + logf(sum);
 }
@@ -1171,12 +1386,18 @@ __global__ __launch_bounds__(256) void k_leaf_select(StepArgs a, size_t gb) {
 
 }  // namespace
 
+// Width template argument: 64 and 128 as such, 0 for the wide rows of a
+// base-embedding tree (a multiple of 128, handled in 128-element slices).
+__host__ inline bool wide_width(int d) { return d > 128 && d <= kMaxWideD && d % 128 == 0; }
+
 #define HIKVP_DISPATCH(dtype, d, KERNEL, ...)                                                        \
   do {                                                                                               \
     if ((dtype) == kDtypeBF16 && (d) == 128) hipLaunchKernelGGL((KERNEL<BF16, 128>), __VA_ARGS__);   \
     else if ((dtype) == kDtypeBF16 && (d) == 64) hipLaunchKernelGGL((KERNEL<BF16, 64>), __VA_ARGS__); \
+    else if ((dtype) == kDtypeBF16 && wide_width(d)) hipLaunchKernelGGL((KERNEL<BF16, 0>), __VA_ARGS__); \
     else if ((dtype) == kDtypeF32 && (d) == 128) hipLaunchKernelGGL((KERNEL<F32, 128>), __VA_ARGS__); \
     else if ((dtype) == kDtypeF32 && (d) == 64) hipLaunchKernelGGL((KERNEL<F32, 64>), __VA_ARGS__);  \
+    else if ((dtype) == kDtypeF32 && wide_width(d)) hipLaunchKernelGGL((KERNEL<F32, 0>), __VA_ARGS__); \
     else return hipErrorInvalidValue;                                                                \
   } while (0)
 
@@ -1184,9 +1405,32 @@ __global__ __launch_bounds__(256) void k_leaf_select(StepArgs a, size_t gb) {
   do {                                                                                               \
     if ((dtype) == kDtypeBF16 && (d) == 128) hipLaunchKernelGGL((KERNEL<BF16, 128, NT, SPT>), __VA_ARGS__); \
     else if ((dtype) == kDtypeBF16 && (d) == 64) hipLaunchKernelGGL((KERNEL<BF16, 64, NT, SPT>), __VA_ARGS__); \
+    else if ((dtype) == kDtypeBF16 && wide_width(d)) hipLaunchKernelGGL((KERNEL<BF16, 0, NT, SPT>), __VA_ARGS__); \
     else if ((dtype) == kDtypeF32 && (d) == 128) hipLaunchKernelGGL((KERNEL<F32, 128, NT, SPT>), __VA_ARGS__); \
     else if ((dtype) == kDtypeF32 && (d) == 64) hipLaunchKernelGGL((KERNEL<F32, 64, NT, SPT>), __VA_ARGS__); \
+    else if ((dtype) == kDtypeF32 && wide_width(d)) hipLaunchKernelGGL((KERNEL<F32, 0, NT, SPT>), __VA_ARGS__); \
     else return hipErrorInvalidValue;                                                                \
+  } while (0)
+
+// Scoring kernels: KERNEL<E, D, LO>, LO when the rows carry a bf16 residual
+// query (rows of an exact query in bf16).
+#define HIKVP_DISPATCH_LO(a, KERNEL, ...)                                                            \
+  do {                                                                                               \
+    const int dt_ = (a).t.dtype, d_ = (a).t.d;                                                       \
+    if ((a).r.q_lo) {                                                                                \
+      if (dt_ == kDtypeBF16 && d_ == 128) hipLaunchKernelGGL((KERNEL<BF16, 128, true>), __VA_ARGS__); \
+      else if (dt_ == kDtypeBF16 && d_ == 64) hipLaunchKernelGGL((KERNEL<BF16, 64, true>), __VA_ARGS__); \
+      else if (dt_ == kDtypeBF16 && wide_width(d_)) hipLaunchKernelGGL((KERNEL<BF16, 0, true>), __VA_ARGS__); \
+      else return hipErrorInvalidValue;                                                              \
+    } else {                                                                                         \
+      if (dt_ == kDtypeBF16 && d_ == 128) hipLaunchKernelGGL((KERNEL<BF16, 128, false>), __VA_ARGS__); \
+      else if (dt_ == kDtypeBF16 && d_ == 64) hipLaunchKernelGGL((KERNEL<BF16, 64, false>), __VA_ARGS__); \
+      else if (dt_ == kDtypeBF16 && wide_width(d_)) hipLaunchKernelGGL((KERNEL<BF16, 0, false>), __VA_ARGS__); \
+      else if (dt_ == kDtypeF32 && d_ == 128) hipLaunchKernelGGL((KERNEL<F32, 128, false>), __VA_ARGS__); \
+      else if (dt_ == kDtypeF32 && d_ == 64) hipLaunchKernelGGL((KERNEL<F32, 64, false>), __VA_ARGS__); \
+      else if (dt_ == kDtypeF32 && wide_width(d_)) hipLaunchKernelGGL((KERNEL<F32, 0, false>), __VA_ARGS__); \
+      else return hipErrorInvalidValue;                                                              \
+    }                                                                                                \
   } while (0)
 
 // Per-row select shape: one wave per row while the list fits 16 scores per
@@ -1245,7 +1489,7 @@ hipError_t launch_root(const StepArgs& a, hipStream_t s) {
   const int nrc = (int)((a.t.count[0] + kRootChunk - 1) / kRootChunk);
   const int64_t waves = (int64_t)(a.g1 - a.g0) * tph * nrc;
   if (waves > 0)
-    HIKVP_DISPATCH(a.t.dtype, a.t.d, k_root_mfma, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a, tph, nrc);
+    HIKVP_DISPATCH_LO(a, k_root_mfma, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a, tph, nrc);
   const unsigned blocks = (unsigned)((a.blk1 - a.blk0 + wpb - 1) / wpb);
   HIKVP_DISPATCH(a.t.dtype, a.t.d, k_root, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb, stage);
   return hipGetLastError();
@@ -1266,7 +1510,7 @@ hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s) {
   if (a.blk1 <= a.blk0 || a.t.count[0] <= 0 || a.K[0] <= 0) return hipSuccess;
   int64_t blocks = a.root_tiles_max;       // one workgroup per tile (grid-stride past 8192)
   if (blocks > 8192) blocks = 8192;
-  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_mid_gemm, dim3((unsigned)blocks), dim3(64 * kMidWaves), 0, s, a);
+  HIKVP_DISPATCH_LO(a, k_mid_gemm, dim3((unsigned)blocks), dim3(64 * kMidWaves), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1307,7 +1551,7 @@ hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s) {
   const int64_t nb_max = (int64_t)(a.blk1 - a.blk0) * a.K[1];
   int64_t blocks = (nb_max + 3) / 4;
   if (blocks > 2048) blocks = 2048;
-  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_score, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  HIKVP_DISPATCH_LO(a, k_leaf_score, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1317,7 +1561,7 @@ hipError_t launch_leaf_overflow(const StepArgs& a, hipStream_t s) {
   const int64_t nb_max = (int64_t)(a.blk1 - a.blk0) * a.K[1];
   int64_t blocks = (nb_max / (kBucketSlots + 1) + 4) / 4;
   if (blocks > 1024) blocks = 1024;
-  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_leaf_score_overflow, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  HIKVP_DISPATCH_LO(a, k_leaf_score_overflow, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

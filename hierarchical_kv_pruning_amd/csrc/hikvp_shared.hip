@@ -4,24 +4,59 @@
 // bound that reads like one selected key set shared by the tokens of a layer
 // (速读 › 怎么做的, complexity).  In this variant the rows of one KV head at
 // one token (or in one whole sequence) share a selection: the descent runs on
-// the group's query, the sum of its members' KG queries rounded once to the
-// tree's storage type, which ranks every node by the members' summed logits.
-// Each member then takes its own softmax over the group's selected leaves
-// with its own logits, merged with its own sequence half as usual.
+// the group's query, the sum of its members' KG queries, which ranks every
+// node by the members' summed logits.  The scores are computed with the sum
+// rounded once to the tree's storage type; the selection is exact for the
+// unrounded sum (its band is widened by the rounding's bound and re-scored
+// with the fp64 sum).  Each member then takes its own softmax over the
+// group's selected leaves with its own logits, merged with its own sequence
+// half as usual.
 #include "hikvp_device.h"
 #include "hikvp_round.h"
 
 namespace hikvp {
 namespace {
 
-// The group query is the exact sum of the members' stored KG queries, rounded
-// once.  It is formed in fp64 in two passes: one wave per (group, chunk of
+// The group query is the exact sum of the members' stored KG queries.  It is
+// formed in fp64 in two passes: one wave per (group, chunk of
 // a.tn tokens) sums its tokens' G heads, one workgroup per group sums its
 // chunks.  Both are exact whenever the exact sum fits fp64's 53 bits (the
 // members' magnitudes spanning less than ~2^40), so the order of the
 // additions does not change the result; where it does not fit, the order is
 // still fixed, so the result is reproducible.  With one chunk per group (a
-// group per token) the first pass rounds and writes the group query itself.
+// group per token) the first pass writes the group query itself.
+
+// Group row gr's sums (this lane's DPL elements): as they are (gqx, the exact
+// query the selection is exact for) and as the query the scores are
+// computed with: rounded once to the tree's dtype (gq), in bf16 with the
+// rounded residual beside it (glo), and an upper bound of what that leaves
+// out (gdelta).  One wave.
+template <class E, int D>
+__device__ inline void store_group_query(const SharedArgs& a, int64_t gr, const double (&x)[D / 64], int lane) {
+  constexpr int DPL = D / 64;
+  double dq2 = 0.0;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    const int64_t o = gr * D + lane * DPL + e;
+    double rest;
+    if constexpr (E::kBytes == 2) {
+      const Bf16Split sp = split_bf16(x[e]);
+      ((uint16_t*)a.gq)[o] = sp.hi;
+      ((uint16_t*)a.glo)[o] = sp.lo;
+      rest = sp.rest;
+    } else {
+      const float v = (float)x[e];
+      ((float*)a.gq)[o] = v;
+      rest = x[e] - (double)v;
+    }
+    a.gqx[o] = x[e];
+    dq2 = fma(rest, rest, dq2);
+  }
+  dq2 = wave_sum_f64(dq2);
+  // rounded up: the fp32 conversion's relative error is below 2^-24
+  if (lane == 0) a.gdelta[gr] = (float)(sqrt(dq2) * (1.0 + 1e-6));
+}
+
 template <class E, int D>
 __global__ __launch_bounds__(256) void k_group_partial(SharedArgs a) {
   constexpr int DPL = D / 64;
@@ -53,12 +88,11 @@ __global__ __launch_bounds__(256) void k_group_partial(SharedArgs a) {
 #pragma unroll
         for (int e = 0; e < DPL; ++e) acc[e] += (double)v[u][e];
   }
+  if (a.chunks > 1) {
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) {
-    const int64_t o = (int64_t)w * D + lane * DPL + e;
-    if (a.chunks > 1) a.gpart[o] = acc[e];
-    else if constexpr (E::kBytes == 2) ((uint16_t*)a.gq)[o] = f64_to_bf16_rne(acc[e]);
-    else ((float*)a.gq)[o] = (float)acc[e];
+    for (int e = 0; e < DPL; ++e) a.gpart[(int64_t)w * D + lane * DPL + e] = acc[e];
+  } else {
+    store_group_query<E, D>(a, w, acc, lane);
   }
 }
 
@@ -92,14 +126,13 @@ __global__ __launch_bounds__(256) void k_group_query(SharedArgs a) {
   for (int e = 0; e < DPL; ++e) part[wave][lane * DPL + e] = acc[e];
   __syncthreads();
   if (wave != 0) return;
+  double x[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) {
     const int i = lane * DPL + e;
-    const double x = ((part[0][i] + part[1][i]) + part[2][i]) + part[3][i];
-    const int64_t o = (int64_t)gr * D + i;
-    if constexpr (E::kBytes == 2) ((uint16_t*)a.gq)[o] = f64_to_bf16_rne(x);
-    else ((float*)a.gq)[o] = (float)x;
+    x[e] = ((part[0][i] + part[1][i]) + part[2][i]) + part[3][i];
   }
+  store_group_query<E, D>(a, gr, x, lane);
 }
 
 // One wave per (token, KV head) and up to kSharedRW of its query heads: the

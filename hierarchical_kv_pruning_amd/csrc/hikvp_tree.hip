@@ -40,10 +40,13 @@ __global__ void k_validate(const int64_t* off, int64_t count, int64_t children, 
   }
 }
 
+// Upper bound of the 2-norms of `rows` key rows of width d per KV head.  The
+// rows of width 64 / 128 are read LPK lanes a row; wide rows (D = 0, a
+// base-embedding tree) one wave a row.
 template <class E, int D>
 __global__ __launch_bounds__(256) void k_key_norms(const void* key, int64_t rows, int64_t hs,
-                                                   int64_t rs, unsigned int* out_bits) {
-  constexpr int EPV = E::kEPV, LPK = D / EPV, KPW = 64 / LPK;
+                                                   int64_t rs, int d, unsigned int* out_bits) {
+  constexpr int EPV = E::kEPV, LPK = D ? D / EPV : 64, KPW = 64 / LPK;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
   const int g = blockIdx.y;
   const int j = lane % LPK;
@@ -54,17 +57,19 @@ __global__ __launch_bounds__(256) void k_key_norms(const void* key, int64_t rows
     const int64_t r = r0 + lane / LPK;
     float s = 0.f;
     if (r < rows) {
-      const uint4 kv = *(const uint4*)(kb + r * rs * E::kBytes + j * 16);
-      float kf[EPV];
-      unpack<E>(kv, kf);
+      for (int c = j; c < (D ? D : d) / EPV; c += LPK) {
+        const uint4 kv = *(const uint4*)(kb + r * rs * E::kBytes + c * 16);
+        float kf[EPV];
+        unpack<E>(kv, kf);
 #pragma unroll
-      for (int t = 0; t < EPV; ++t) s = fmaf(kf[t], kf[t], s);
+        for (int t = 0; t < EPV; ++t) s = fmaf(kf[t], kf[t], s);
+      }
     }
     s = group_sum<LPK>(s);
     mx = fmaxf(mx, s);
   }
   mx = wave_max(mx);
-  if (lane == 0) atomicMax(&out_bits[g], __float_as_uint(sqrtf(mx) * 1.0001f));
+  if (lane == 0) atomicMax(&out_bits[g], __float_as_uint(sqrtf(mx) * norm_slack(D ? D : d)));
 }
 
 
@@ -72,10 +77,13 @@ __global__ __launch_bounds__(256) void k_key_norms(const void* key, int64_t rows
 
 #define HIKVP_DISPATCH(dtype, d, KERNEL, ...)                                                        \
   do {                                                                                               \
+    const bool wide_ = (d) > 128 && (d) <= kMaxWideD && (d) % 128 == 0;                              \
     if ((dtype) == kDtypeBF16 && (d) == 128) hipLaunchKernelGGL((KERNEL<BF16, 128>), __VA_ARGS__);   \
     else if ((dtype) == kDtypeBF16 && (d) == 64) hipLaunchKernelGGL((KERNEL<BF16, 64>), __VA_ARGS__); \
+    else if ((dtype) == kDtypeBF16 && wide_) hipLaunchKernelGGL((KERNEL<BF16, 0>), __VA_ARGS__);     \
     else if ((dtype) == kDtypeF32 && (d) == 128) hipLaunchKernelGGL((KERNEL<F32, 128>), __VA_ARGS__); \
     else if ((dtype) == kDtypeF32 && (d) == 64) hipLaunchKernelGGL((KERNEL<F32, 64>), __VA_ARGS__);  \
+    else if ((dtype) == kDtypeF32 && wide_) hipLaunchKernelGGL((KERNEL<F32, 0>), __VA_ARGS__);       \
     else return hipErrorInvalidValue;                                                                \
   } while (0)
 
@@ -94,7 +102,7 @@ hipError_t launch_key_norms(const void* key, int dtype, int d, int Hkv, int64_t 
   int64_t blocks = (rows + 63) / 64;
   if (blocks > 2048) blocks = 2048;
   HIKVP_DISPATCH(dtype, d, k_key_norms, dim3((unsigned)blocks, (unsigned)Hkv), dim3(256), 0, s, key,
-                 rows, hs, rs, out_bits);
+                 rows, hs, rs, d, out_bits);
   return hipGetLastError();
 }
 

@@ -93,7 +93,8 @@ typedef enum {
   ATLASKV_ERR_TREE = 4,        /* malformed child offsets */
   ATLASKV_ERR_K = 5,           /* K < 0, a clamped K above 256, or both halves empty */
   ATLASKV_ERR_WORKSPACE = 6,   /* workspace missing, too small or misaligned */
-  ATLASKV_ERR_UNSUPPORTED = 7, /* head dim not 64/128, node counts >= 2^31, scale <= 0 */
+  ATLASKV_ERR_UNSUPPORTED = 7, /* head dim not 64/128 (or a wide tree outside the folded entry
+                                  point), node counts >= 2^31, scale <= 0 */
   ATLASKV_ERR_HIP = 8          /* a HIP runtime call failed */
 } atlaskv_status;
 
@@ -121,7 +122,9 @@ typedef struct atlaskv_tree_view_s* atlaskv_tree_view;
  *   root_child_off  device int64 [M_R + 1]: mids of root j are
  *                   root_child_off[j] .. root_child_off[j+1]-1
  *   mid_child_off   device int64 [M_I + 1]: leaves of mid m likewise
- * All float tensors share one dtype and head dim d.  Offsets must start at 0,
+ * All float tensors share one dtype and head dim d (64 or 128; a base-
+ * embedding tree for atlaskv_folded_attend_ex may also be a multiple of 128
+ * up to 4096 wide).  Offsets must start at 0,
  * be non-decreasing and end at M_I (resp. M); empty ranges are allowed.
  * stream: hipStream_t (NULL = default stream) used for validation and as the
  * default stream of attend calls.  The call validates the offsets and
@@ -290,11 +293,15 @@ const char* atlaskv_flat_phase_name(int32_t phase);
  *                           (B*N*Hkv groups);
  *   ATLASKV_SHARE_SEQUENCE  every token and query head of one KV head in one
  *                           sequence (B*Hkv groups).
- * The group's query is the exact sum of its members' KG queries rounded once
- * (nearest, ties to even) to the tree's dtype; ranking nodes by it ranks them
- * by the members' summed logits.  The sum is formed in fp64 (token chunks,
- * then chunks), exact whenever it fits 53 bits, i.e. unless the members'
- * magnitudes span more than ~2^40.
+ * The group's query is the exact sum of its members' KG queries; ranking
+ * nodes by it ranks them by the members' summed logits.  The sum is formed in
+ * fp64 (token chunks, then chunks), exact whenever it fits 53 bits, i.e.
+ * unless the members' magnitudes span more than ~2^40.  The scores are
+ * computed with the sum rounded to the tree's dtype (in bf16 as the rounded
+ * sum plus its rounded residual, two bf16 rows); the selection is exact for
+ * the unrounded sum all the same: the band of candidates that the rounding
+ * could reorder is widened by its bound and re-scored in fp64 with the
+ * fp64 sum.
  * The descent (roots -> mids -> leaves, Top-K per level, ties to the lower
  * index) runs on the group queries; every row then takes the softmax of its
  * own KG logits over its group's K_L selected leaves, and its own sequence
@@ -329,18 +336,25 @@ const char* atlaskv_shared_phase_name(int32_t phase);
  * Because <q, W_K k> = <W_K^T q, k> and sum p W_V v = W_V sum p v, the tree
  * need not be projected per head:
  *   tree   a view whose root_k / mid_k / leaf_k / leaf_v are the base
- *          embeddings, ONE head ([1, M_x, D_E]), D_E in {64, 128};
+ *          embeddings, ONE head ([1, M_x, D_E]), D_E 64, 128 or a multiple
+ *          of 128 up to 4096 (views of such wide trees serve this entry
+ *          point only; the others return ATLASKV_ERR_UNSUPPORTED);
  *   w_k, w_v  [Hkv, d, D_E]: head g's projected key is w_k[g] k, its
  *          projected value w_v[g] v; d in {64, 128};
  *   q, seq_k, seq_v, out as atlaskv_hikvp_attend with the layer's Hkv and d.
  * Row (b, n, h) with g = h / (Hq/Hkv) folds its KG query into
- * q' = w_k[g]^T q_kg (exact product sum, rounded once to the tree dtype),
- * runs the pruned descent over the base tree with q' (logit scale 1/sqrt(d)
- * unless given), applies w_v[g] to its softmax-weighted base values, and
- * merges with its causal sequence half.  The result equals
+ * q' = w_k[g]^T q_kg (exact product sum in fp64), runs the pruned descent
+ * over the base tree with q' (logit scale 1/sqrt(d) unless given), applies
+ * w_v[g] to its softmax-weighted base values, and merges with its causal
+ * sequence half.  The scores are computed with q' rounded to the tree dtype
+ * (in bf16 as the rounded q' plus its rounded residual); the selections are
+ * exact for the unrounded q' (the rounding's bound widens the band that is
+ * re-scored in fp64 with q') and the KG softmax takes the selected leaves'
+ * logits from the unrounded q' in fp64.  The result equals
  * atlaskv_hikvp_attend on the per-head projected trees (w_k[g] k, w_v[g] v)
- * up to the rounding of q'.  opts->sel_* receive per-row selections of base
- * nodes.  Workspace size from atlaskv_folded_workspace_size.
+ * up to fp32 rounding.  opts->sel_* receive per-row selections of base
+ * nodes.  Workspace size from atlaskv_folded_workspace_size (it holds q' in
+ * fp64, 8 * D_E bytes a row).
  */
 atlaskv_status atlaskv_folded_workspace_size(atlaskv_tree_view tree, const atlaskv_tensor* q,
                                              const atlaskv_tensor* w_k, const atlaskv_tensor* seq_k,

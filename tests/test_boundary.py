@@ -160,9 +160,32 @@ def test_scale_must_be_positive(lib):
 
 
 def test_unsupported_head_dim(lib):
-    with pytest.raises(atlaskv.AtlasKVError) as e:
-        _view(d=96)
-    assert e.value.status == atlaskv.ERR_UNSUPPORTED
+    for d in (96, 192, 4224):   # not 64 / 128 / a multiple of 128 up to 4096
+        with pytest.raises(atlaskv.AtlasKVError) as e:
+            _view(d=d)
+        assert e.value.status == atlaskv.ERR_UNSUPPORTED, d
+
+
+def test_wide_tree_serves_the_folded_entry_point_only(lib):
+    """A tree wider than 128 (a base-embedding tree of width D_E, a multiple
+    of 128 up to 4096) is a valid view, but only the folded entry point
+    takes it: the per-row, flat and shared paths refuse it."""
+    for DE in (256, 384, 3072, 4096):
+        v = _view(Hkv=1, d=DE)
+        q = torch.zeros(1, 4, 2, DE, dtype=torch.bfloat16)
+        assert _call(v, q=q, seq=False) == atlaskv.ERR_UNSUPPORTED
+        ws = torch.zeros(4096, dtype=torch.uint8)
+        fake = type("W", (), {"data_ptr": lambda self: (ws.data_ptr() + 255) // 256 * 256,
+                              "numel": lambda self: 1 << 34})()
+        assert atlaskv.flat_check_args(q, v, None, None, q, workspace=fake) == atlaskv.ERR_UNSUPPORTED
+        assert atlaskv.shared_check_args(q, v, None, None, (2, 2, 4), atlaskv.SHARE_KV_GROUP, q,
+                                         workspace=fake) == atlaskv.ERR_UNSUPPORTED
+        ql = torch.zeros(1, 4, 8, 128, dtype=torch.bfloat16)
+        wk = torch.zeros(2, 128, DE, dtype=torch.bfloat16)
+        sk = torch.zeros(1, 6, 2, 128, dtype=torch.bfloat16)
+        assert atlaskv.folded_check_args(ql, v, wk, wk, sk, sk, (2, 2, 4), ql, workspace=fake) == atlaskv.OK
+        # the workspace holds the exact folded queries (fp64) besides the rounded ones
+        assert atlaskv.folded_workspace_size(v, ql, wk, sk, (2, 2, 4)) >= 4 * 8 * DE * (8 + 2)
 
 
 def test_describe_rejects_bad_fanouts_and_tree_mismatch(lib):

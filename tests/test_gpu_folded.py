@@ -1,8 +1,12 @@
 """GPU parity of folded projections (one base-embedding tree for every head;
 W_K^T folded into the query, W_V applied after the softmax-weighted base
-values) against the fp64 oracle, through the C ABI.  Selections of base
-nodes are compared per row as sets (1e-6 boundary-gap exemption: such rows
-must hold valid Top-Ks and are compared in replay); outputs to
+values) against the fp64 oracle, through the C ABI.  The oracle ranks and
+scores with the exact folded query W_K^T q (not rounded to the storage
+type), so the selections must be exact for it.  Base widths D_E of 64 and
+128, and 384 and 3072 (wide base-embedding trees, scored in 128-element
+slices).  Selections of base nodes are compared per row as sets (1e-6
+boundary-gap exemption: such rows must hold valid Top-Ks and are compared in
+replay); outputs to
 the usual bar on an fp32 output (fp32 max-abs <= 1e-5; bf16 max-abs <= 2e-2 x
 RMS, cosine >= 0.9999), and a bf16 output must be that fp32 output rounded to
 nearest even."""
@@ -92,9 +96,10 @@ def check(f, rows=None, K=None, with_seq=True, q_kg=None):
         if lev < 0:
             continue
         assert ora["gap"][i][lev] < parity.GAP_EXEMPT, (tuple(rows[i]), lev, ora["gap"][i][lev])
-        if P is None:
+        if P is None:  # the descent's problem: the exact folded queries as KG queries
             qf = oracle.folded_query(h(f.q if q_kg is None else q_kg), h(f.w_k), rows)
-            P = oracle.Problem(qf, *(h(t) for t in f.tree), None, None, K, scale=1.0 / f.d ** 0.5)
+            stub_q = torch.zeros(qf.shape, dtype=f.tree[0].dtype)
+            P = oracle.Problem(stub_q, *(h(t) for t in f.tree), None, None, K, scale=1.0 / f.d ** 0.5, q_kg=qf)
             base_leaf = h(f.tree[2])
         parity.check_selection_chain(
             None, P, rows[i], g,
@@ -127,9 +132,21 @@ def check(f, rows=None, K=None, with_seq=True, q_kg=None):
 
 
 @pytest.mark.parametrize("dtype,DE,d", [("bf16", 128, 128), ("bf16", 64, 128), ("bf16", 128, 64),
-                                        ("f32", 128, 128), ("f32", 64, 64)])
+                                        ("f32", 128, 128), ("f32", 64, 64),
+                                        ("bf16", 384, 128), ("bf16", 384, 64), ("f32", 384, 128),
+                                        ("bf16", 3072, 128), ("f32", 3072, 64)])
 def test_folded_widths_and_dtypes(dtype, DE, d):
     check(Folded(1, dtype=dtype, DE=DE, d=d))
+
+
+@pytest.mark.parametrize("DE", [384, 3072])
+def test_folded_wide_k_edges(DE):
+    """Wide base trees: K = 1 everywhere, K above every level's candidates,
+    and a long mid list (K_I = 64, past the mid tiles' filter)."""
+    f = Folded(8, DE=DE, M=3001)
+    check(f, K=(1, 1, 1))
+    check(f, K=(37, 256, 256), with_seq=False)
+    check(f, K=(6, 64, 40))
 
 
 def test_folded_k_edges_and_no_sequence():
@@ -179,8 +196,10 @@ def test_folded_identity_projections_match_the_per_row_path():
         assert a == b, lev
 
 
-def test_folded_one_million_base_leaves_sampled_rows():
+@pytest.mark.parametrize("DE,nrows", [(128, 256), (384, 256), (3072, 64)])
+def test_folded_one_million_base_leaves_sampled_rows(DE, nrows):
     """The m1e6 layer (32/8 heads, 512 tokens, K 8/8/32) over a one-head base
-    tree of 1e6 leaves at D_E = 128."""
-    f = Folded(6, B=1, N=512, S=512, Hq=32, Hkv=8, MR=100, MI=10000, M=1000000, K=(8, 8, 32), ragged=False)
-    check(f, rows=parity.sample_rows(type("C", (), dict(B=1, N=512, Hq=32))(), 256, seed=9))
+    tree of 1e6 leaves at D_E = 128, 384 and 3072, on sampled rows."""
+    f = Folded(6, DE=DE, B=1, N=512, S=512, Hq=32, Hkv=8, MR=100, MI=10000, M=1000000, K=(8, 8, 32),
+               ragged=False)
+    check(f, rows=parity.sample_rows(type("C", (), dict(B=1, N=512, Hq=32))(), nrows, seed=9))
