@@ -765,6 +765,14 @@ hipError_t launch_descent(const Plan& p, const RowsDev& rows, atlaskv_tree_view_
   a.o_kg = o_kg;
   a.lse_kg = lse_kg;
   a.exact_logits = p.exact_logits;
+  {
+    // the mid tiles keep, of each selected root's children, about the K_I
+    // best and the band around them: K_R * min(fanout, 4 K_I) estimates a
+    // row's survivors generously; the smaller register list (less LDS a
+    // wave, more rows in flight) when that fits it
+    const int64_t f = v->maxfan[0] < 4 * (int64_t)p.K[1] ? v->maxfan[0] : 4 * (int64_t)p.K[1];
+    a.mid_spt = (int64_t)p.K[0] * f <= 64 * 4 ? 4 : 16;
+  }
   const int per_head = rows.B * rows.N * rows.G;  // row blocks per KV head
   if (p.nparts < 2 || !v->part_s[0] || pm.ev) {
     a.g0 = 0;

@@ -89,6 +89,7 @@ struct StepArgs {
   int g0, g1;                 // KV heads of this part
   int blk0, blk1;             // row blocks of this part
   int K[3];                   // Top-K per level (plan-clamped; a row takes min(K, its candidates))
+  int mid_spt;                // surviving mid candidates a lane of the mid select holds in registers (4, 16)
   int64_t c1max;              // mid candidates per row: capacity and row stride of mid_pairs
   int64_t c2max;              // leaf candidates per row: capacity
   uint2* mid_pairs;           // [R, c1max] surviving mid candidates: (unscaled fp32 score bits, child

@@ -892,11 +892,12 @@ __device__ inline void mid_select_row(StepArgs a, size_t wave_bytes) {
   for (int i = lane; i < K1; i += 64) o1[i] = i < k1 ? W.out_node[i] : -1;
 }
 
-constexpr int kMidSelectSPT = 16;   // survivors a lane holds in registers (1024 a row)
-
-template <class E, int D>
+// Survivors a lane holds in registers: 4 (256 a row) or 16 (1024).  The
+// smaller list keeps less LDS a wave (its (k, j) index), so more rows are in
+// flight; rows with more survivors read them from the workspace instead.
+template <class E, int D, int SPT>
 __global__ __launch_bounds__(256) void k_mid_select(StepArgs a, size_t wave_bytes) {
-  mid_select_row<E, D, kMidSelectSPT>(a, wave_bytes);
+  mid_select_row<E, D, SPT>(a, wave_bytes);
 }
 
 // ---------------------------------------------------------------------------
@@ -1516,13 +1517,28 @@ hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s) {
 
 hipError_t launch_mid_select(const StepArgs& a, hipStream_t s) {
   if (a.blk1 <= a.blk0) return hipSuccess;
-  // one wave per row; up to 1024 surviving candidates held in registers
-  const size_t wb = mid_select_wave_bytes(a.K[1], a.K[0], a.t.d, kMidSelectSPT);
+  // one wave per row
+  const int spt = a.mid_spt;
+  if (spt != 4 && spt != 16) return hipErrorInvalidValue;
+  const size_t wb = mid_select_wave_bytes(a.K[1], a.K[0], a.t.d, spt);
   int wpb = 4;
   while (wpb > 1 && wb * wpb > 64 * 1024) --wpb;
   if (wb * wpb > 64 * 1024) return hipErrorInvalidValue;
   const unsigned blocks = (unsigned)((a.blk1 - a.blk0 + wpb - 1) / wpb);
-  HIKVP_DISPATCH(a.t.dtype, a.t.d, k_mid_select, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb);
+#define HIKVP_MID_SEL(SPT_)                                                                          \
+  do {                                                                                               \
+    const dim3 g_(blocks), b_(64 * wpb);                                                             \
+    if (a.t.dtype == kDtypeBF16 && a.t.d == 128) hipLaunchKernelGGL((k_mid_select<BF16, 128, SPT_>), g_, b_, wb * wpb, s, a, wb); \
+    else if (a.t.dtype == kDtypeBF16 && a.t.d == 64) hipLaunchKernelGGL((k_mid_select<BF16, 64, SPT_>), g_, b_, wb * wpb, s, a, wb); \
+    else if (a.t.dtype == kDtypeBF16 && wide_width(a.t.d)) hipLaunchKernelGGL((k_mid_select<BF16, 0, SPT_>), g_, b_, wb * wpb, s, a, wb); \
+    else if (a.t.dtype == kDtypeF32 && a.t.d == 128) hipLaunchKernelGGL((k_mid_select<F32, 128, SPT_>), g_, b_, wb * wpb, s, a, wb); \
+    else if (a.t.dtype == kDtypeF32 && a.t.d == 64) hipLaunchKernelGGL((k_mid_select<F32, 64, SPT_>), g_, b_, wb * wpb, s, a, wb); \
+    else if (a.t.dtype == kDtypeF32 && wide_width(a.t.d)) hipLaunchKernelGGL((k_mid_select<F32, 0, SPT_>), g_, b_, wb * wpb, s, a, wb); \
+    else return hipErrorInvalidValue;                                                                \
+  } while (0)
+  if (spt == 4) HIKVP_MID_SEL(4);
+  else HIKVP_MID_SEL(16);
+#undef HIKVP_MID_SEL
   return hipGetLastError();
 }
 
