@@ -708,8 +708,7 @@ struct LateFork {
 // holds the view's mutex when `fork` is given.
 hipError_t descent_part(const StepArgs& a, hipStream_t s, PhaseMarks& pm, const LateFork* fork = nullptr) {
   auto mark = [&](hipError_t prev) { return pm.mark(prev); };
-  hipError_t e = launch_clear(a, s);
-  if (e == hipSuccess) e = launch_root(a, s);
+  hipError_t e = launch_root(a, s);
   if (e == hipSuccess) e = mark(launch_root_groups(a, s));
   if (e == hipSuccess) e = mark(launch_mid_gemm(a, s));
   if (e == hipSuccess) e = mark(launch_mid_select(a, s));

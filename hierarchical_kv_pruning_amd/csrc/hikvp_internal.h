@@ -213,8 +213,7 @@ hipError_t launch_key_norms(const void* key, int dtype, int d, int Hkv, int64_t 
                             int64_t hs, int64_t rs, unsigned int* out_bits, hipStream_t s);
 // dst[r, i] = src[r, i] for i < Ks, -1 for Ks <= i < Kd (rows r < R)
 hipError_t launch_expand_sel(const int32_t* src, int Ks, int32_t* dst, int Kd, int R, hipStream_t s);
-hipError_t launch_clear(const StepArgs& a, hipStream_t s);        // bucket counters of both levels
-hipError_t launch_root(const StepArgs& a, hipStream_t s);
+hipError_t launch_root(const StepArgs& a, hipStream_t s);          // (clears the group and bucket counters)
 hipError_t launch_root_groups(const StepArgs& a, hipStream_t s);  // rows by selected (head, root)
 hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s);
 hipError_t launch_mid_select(const StepArgs& a, hipStream_t s);

@@ -6,10 +6,10 @@
 // branches and keep the Top-K, and so on down to the leaves; the selected
 // leaves' softmax then forms the KG half of the merged output.
 //
-//   k_clear     zeroes the group and bucket counters of the part's KV heads.
-//   k_root_mfma one wave per 16 rows of one KV head: their scores against all
-//               M_R root keys of the head on MFMA 16x16 tiles (a root key is
-//               read once per 16 rows).
+//   k_root_mfma zeroes the group and bucket counters of the part's KV heads,
+//               then, one wave per 16 rows of one KV head: their scores
+//               against all M_R root keys of the head on MFMA 16x16 tiles (a
+//               root key is read once per 16 rows).
 //   k_root      one wave per row: exact-boundary Top-K_R over the row's root
 //               scores; each selection is counted in its (KV head, root)
 //               group.  The per-row select kernels keep a few KB of LDS per
@@ -151,6 +151,31 @@ __device__ inline float* root_score_row(const StepArgs& a, int row) {
   return (float*)(a.mid_pairs + (int64_t)row * a.c1max);
 }
 
+// The part's group and bucket counters zeroed (its keys of the (head, root)
+// sub-counters and (head, mid) buckets, the descriptor counts), by thread
+// tid of nthreads: done by k_root_mfma, whose grid every part launches
+// first, so that no launch of its own is spent on it.
+__device__ inline void clear_counters(const StepArgs& a, int64_t tid, int64_t nthreads) {
+  const int64_t MI = a.t.count[1], MR = a.t.count[0];
+  const int64_t nk1 = (a.g1 - a.g0) * MI, nk0 = (a.g1 - a.g0) * MR;  // the part's keys
+  const int64_t nall = (int64_t)a.t.Hkv * MR;
+  if (a.g0 == 0 && a.g1 == a.t.Hkv) {  // all heads: the whole arrays, in order
+    for (int64_t i = tid; i < (int64_t)a.bucket_q * 64; i += nthreads) {
+      a.bucket_cnt[i] = 0;
+      a.bucket_head[i] = -1;
+    }
+  } else {
+    for (int64_t i = tid; i < nk1; i += nthreads) {
+      const int64_t bix = bucket_index(a, a.g0 * MI + i);
+      a.bucket_cnt[bix] = 0;
+      a.bucket_head[bix] = -1;
+    }
+  }
+  for (int64_t i = tid; i < nk0 * kRootSub; i += nthreads)
+    a.root_cnt[(i / nk0) * nall + a.g0 * MR + i % nk0] = 0;
+  if (tid <= kDescSub) a.bucket_count[tid] = 0;
+}
+
 // Root scores on MFMA: one wave per 16 consecutive rows of one KV head and
 // kRootChunk of its roots (the rows are the M side, 16 roots the N side of
 // each 16x16 tile, the chunk's tiles loaded at once), so a root key is read
@@ -166,6 +191,7 @@ __global__ __launch_bounds__(256) void k_root_mfma(StepArgs a, int tph, int nrc)
   constexpr int KCH = SW * E::kBytes / 64;  // 16-byte pieces per lane per row slice
   constexpr int NU = kRootChunk / 16;       // root tiles in flight
   const int lane = threadIdx.x & 63, quad = lane >> 4, col = lane & 15;
+  clear_counters(a, (int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x);
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (w >= (a.g1 - a.g0) * tph * nrc) return;
   const int rc = w % nrc, t = w / nrc;     // root chunk, row tile
@@ -911,28 +937,6 @@ __global__ __launch_bounds__(256) void k_mid_select(StepArgs a, size_t wave_byte
 // Each member's dot products are computed independently, so results do not
 // depend on the (atomic) member or bucket order.
 // ---------------------------------------------------------------------------
-__global__ void k_clear(StepArgs a) {
-  const int64_t MI = a.t.count[1], MR = a.t.count[0];
-  const int64_t nk1 = (a.g1 - a.g0) * MI, nk0 = (a.g1 - a.g0) * MR;  // the part's keys
-  const int64_t nall = (int64_t)a.t.Hkv * MR;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  if (a.g0 == 0 && a.g1 == a.t.Hkv) {  // all heads: the whole arrays, in order
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < (int64_t)a.bucket_q * 64; i += stride) {
-      a.bucket_cnt[i] = 0;
-      a.bucket_head[i] = -1;
-    }
-  } else {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nk1; i += stride) {
-      const int64_t bix = bucket_index(a, a.g0 * MI + i);
-      a.bucket_cnt[bix] = 0;
-      a.bucket_head[bix] = -1;
-    }
-  }
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nk0 * kRootSub; i += stride)
-    a.root_cnt[(i / nk0) * nall + a.g0 * MR + i % nk0] = 0;
-  if (blockIdx.x == 0 && threadIdx.x <= kDescSub) a.bucket_count[threadIdx.x] = 0;
-}
-
 // Register selection e = (row, mid) in its (KV head, mid) bucket, given its
 // rank from the bucket's counter (-1: nothing to register): the first
 // kBucketSlots members in fixed slots (row, first leaf slot), later ones in
@@ -1489,8 +1493,9 @@ hipError_t launch_root(const StepArgs& a, hipStream_t s) {
   const int tph = (int)((per_head + 15) / 16);
   const int nrc = (int)((a.t.count[0] + kRootChunk - 1) / kRootChunk);
   const int64_t waves = (int64_t)(a.g1 - a.g0) * tph * nrc;
-  if (waves > 0)
-    HIKVP_DISPATCH_LO(a, k_root_mfma, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a, tph, nrc);
+  // at least one block: the kernel also clears the part's counters
+  const unsigned mblocks = (unsigned)(waves > 0 ? (waves + 3) / 4 : 1);
+  HIKVP_DISPATCH_LO(a, k_root_mfma, dim3(mblocks), dim3(256), 0, s, a, tph, nrc);
   const unsigned blocks = (unsigned)((a.blk1 - a.blk0 + wpb - 1) / wpb);
   HIKVP_DISPATCH(a.t.dtype, a.t.d, k_root, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb, stage);
   return hipGetLastError();
@@ -1539,17 +1544,6 @@ hipError_t launch_mid_select(const StepArgs& a, hipStream_t s) {
   if (spt == 4) HIKVP_MID_SEL(4);
   else HIKVP_MID_SEL(16);
 #undef HIKVP_MID_SEL
-  return hipGetLastError();
-}
-
-hipError_t launch_clear(const StepArgs& a, hipStream_t s) {
-  if (a.blk1 <= a.blk0) return hipSuccess;
-  const int64_t nk1 = (a.g0 == 0 && a.g1 == a.t.Hkv) ? (int64_t)a.bucket_q * 64 : (int64_t)(a.g1 - a.g0) * a.t.count[1];
-  const int64_t nk0 = (int64_t)(a.g1 - a.g0) * a.t.count[0] * kRootSub;
-  int64_t blocks = ((nk1 > nk0 ? nk1 : nk0) + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(k_clear, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
