@@ -163,6 +163,172 @@ def read_traffic(kernel, workload):
         return None
 
 
+# The summaries themselves: `python3 bench.py --summarize {hbm,busy,stats} ...`
+# reads the csv output of the rocprofv3 runs named in each summary's header
+# and writes profiles/.  Kernels of each phase (the phase-timed steps run the
+# descent as one part over all KV heads, serially, one dispatch of each
+# kernel a step: their last `phase_steps` dispatches are the ones the
+# roofline divides by).
+PHASE_OF = {
+    "k_root_mfma": "root_score_topk", "k_root": "root_score_topk",
+    "k_root_scan": "root_score_topk (grouping)", "k_root_fill": "root_score_topk (grouping)",
+    "k_mid_gemm": "mid_bucket_gemm", "k_mid_select": "mid_topk", "k_bucket_link": "leaf_bucket_link",
+    "k_leaf_score": "leaf_score_stream", "k_leaf_score_overflow": "leaf_score_overflow",
+    "k_leaf_select": "leaf_topk_kg_attention", "k_seq_mfma": "seq_attention",
+    "k_seq_decode_mfma": "seq_attention", "k_seq_decode": "seq_attention", "k_seq_flash": "seq_attention",
+    "k_seq_combine": "seq_split_combine",
+}
+# the kernel each phase's HBM summary counts (a phase's main kernel)
+HBM_SUMMARY_KERNELS = {
+    "root_score_topk": ("k_root",), "mid_bucket_gemm": ("k_mid_gemm",), "mid_topk": ("k_mid_select",),
+    "leaf_bucket_link": ("k_bucket_link",), "leaf_score_stream": ("k_leaf_score",),
+    "leaf_score_overflow": ("k_leaf_score_overflow",), "leaf_topk_kg_attention": ("k_leaf_select",),
+    "seq_attention": ("k_seq_mfma", "k_seq_decode_mfma", "k_seq_decode", "k_seq_flash"),
+}
+BUSY_KERNELS = ("k_root_mfma", "k_root", "k_mid_gemm", "k_mid_select", "k_bucket_link", "k_leaf_score",
+                "k_leaf_select", "k_seq_mfma", "k_seq_decode_mfma", "k_seq_combine")
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _short_kernel(name):
+    import re
+    m = re.search(r"hikvp::(?:\(anonymous namespace\)::)?(k_\w+)", name)
+    if m:
+        return m.group(1)
+    return COPY_KERNEL if COPY_KERNEL in name else None
+
+
+def _read_csv(directory, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def _counter_dispatches(directory):
+    """{kernel: [(dispatch id, {counter: value}, duration ns)]} in dispatch order."""
+    per = {}
+    for r in _read_csv(directory, "counter_collection.csv"):
+        k = _short_kernel(r["Kernel_Name"])
+        if not k:
+            continue
+        d = int(r["Dispatch_Id"])
+        ent = per.setdefault(k, {}).setdefault(d, [{}, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])])
+        ent[0][r["Counter_Name"]] = ent[0].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return {k: [(d, v[0], v[1]) for d, v in sorted(m.items())] for k, m in per.items()}
+
+
+def _bench_cmd(args, extra):
+    return (f"python3 bench.py --workload {args.workload} --steps {args.steps} --warmup {args.warmup} "
+            f"--phase-steps {args.phase_steps} --no-cpu-baseline{extra}")
+
+
+def summarize(args):
+    """Write the profiles/ summaries of one workload from rocprofv3 csv output."""
+    w, nph = args.workload, args.phase_steps
+    if not w or not nph:
+        raise SystemExit("--summarize needs --workload and --phase-steps")
+    hsh = kernel_source_hash()
+    written = []
+    if args.summarize == "hbm":
+        fetch, write = _counter_dispatches(args.fetch_dir), _counter_dispatches(args.write_dir)
+        calib_gib = 1
+        cf = fetch[COPY_KERNEL][-1][1]["FETCH_SIZE"]
+        cw = write[COPY_KERNEL][-1][1]["WRITE_SIZE"]
+        fscale, wscale = calib_gib * (1 << 20) / cf, calib_gib * (1 << 20) / cw
+        bench_cmd = _bench_cmd(args, f" --calib-copy-gib {calib_gib}")
+        for phase, kernels in HBM_SUMMARY_KERNELS.items():
+            k = next((k for k in kernels if k in fetch and k in write), None)
+            if k is None:
+                continue
+            fk = float(np.mean([c["FETCH_SIZE"] for _, c, _ in fetch[k][-nph:]]))
+            wk = float(np.mean([c["WRITE_SIZE"] for _, c, _ in write[k][-nph:]]))
+            path = os.path.join(PROFILES, f"{phase}_{w}_hbm_counters.txt")
+            with open(path, "w") as f:
+                f.write(f"# HBM traffic of {k} ({phase}), workload {w}, from two rocprofv3 counter passes\n")
+                f.write(f"# fetch pass: rocprofv3 --pmc FETCH_SIZE --output-format csv -d {args.fetch_dir} -o run -- "
+                        f"{bench_cmd}\n")
+                f.write(f"# write pass: rocprofv3 --pmc WRITE_SIZE --output-format csv -d {args.write_dir} -o run -- "
+                        f"{bench_cmd}\n")
+                f.write(f"# summary: python3 bench.py --summarize hbm --workload {w} --steps {args.steps} "
+                        f"--warmup {args.warmup} --phase-steps {nph} --fetch-dir {args.fetch_dir} "
+                        f"--write-dir {args.write_dir}\n")
+                f.write(f"# calibration: the same passes count a {calib_gib} GiB device-to-device copy ({COPY_KERNEL})\n")
+                f.write(f"calib_copy_fetch_kib: {cf:.1f}\ncalib_copy_write_kib: {cw:.1f}\n")
+                f.write(f"fetch_scale: {fscale:.4f}\nwrite_scale: {wscale:.4f}\n")
+                f.write(f"dispatches: {len(fetch[k])} (the last {nph}, the bench's phase-timed steps, are averaged)\n")
+                f.write(f"fetch_kib_per_dispatch: {fk:.1f}\nwrite_kib_per_dispatch: {wk:.1f}\n")
+                f.write(f"hbm_bytes_per_launch: {int(round((fk * fscale + wk * wscale) * 1024))}\n")
+                f.write(f"kernel_source_sha256_16: {hsh}\n")
+            written.append(path)
+    elif args.summarize == "busy":
+        per = _counter_dispatches(args.pmc_dir)
+        path = os.path.join(PROFILES, f"busy_counters_{w}.txt")
+        with open(path, "w") as f:
+            f.write(f"# MFMA and VALU activity per kernel, workload {w} (MI355X: 256 CUs, 1024 SIMDs)\n")
+            f.write("# counter pass: rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_BUSY_CYCLES "
+                    "SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_WAIT_INST_ANY SQ_WAVES GRBM_GUI_ACTIVE "
+                    f"--output-format csv -d {args.pmc_dir} -o run -- {_bench_cmd(args, '')}\n")
+            f.write(f"# summary: python3 bench.py --summarize busy --workload {w} --steps {args.steps} "
+                    f"--warmup {args.warmup} --phase-steps {nph} --pmc-dir {args.pmc_dir}\n")
+            f.write("# mean over the last phase-steps dispatches of each kernel (the phase-timed steps):\n")
+            f.write("#   mfma_busy_pct = 100 * SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * 1024 SIMDs)\n")
+            f.write("#                   (rocprofv3's MfmaUtil metric)\n")
+            f.write("#   valu_busy_pct = 100 * SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE * 256 CUs)\n")
+            f.write("#                   (rocprofv3's VALUBusy metric)\n")
+            f.write(f"# kernel sources sha256[:16]: {hsh}\n")
+            f.write("kernel | phase | dispatches | us | mfma_busy_pct | valu_busy_pct | waves | valu_insts_per_wave | "
+                    "mfma_insts_per_wave\n")
+            for k in BUSY_KERNELS:
+                if k not in per:
+                    continue
+                last = per[k][-nph:]
+                mean = lambda c: float(np.mean([x[1].get(c, 0.0) for x in last]))
+                g = mean("GRBM_GUI_ACTIVE")
+                waves = max(mean("SQ_WAVES"), 1.0)
+                f.write(f"{k} | {PHASE_OF.get(k, '-')} | {len(per[k])} | {np.mean([x[2] for x in last]) / 1e3:.1f} | "
+                        f"{100 * mean('SQ_VALU_MFMA_BUSY_CYCLES') / (g * 1024):.2f} | "
+                        f"{100 * mean('SQ_ACTIVE_INST_VALU') / (g * 256):.2f} | {waves:.0f} | "
+                        f"{mean('SQ_INSTS_VALU') / waves:.0f} | {mean('SQ_INSTS_MFMA') / waves:.1f}\n")
+        written.append(path)
+    elif args.summarize == "stats":
+        per = {}
+        for r in _read_csv(args.trace_dir, "kernel_trace.csv"):
+            k = _short_kernel(r["Kernel_Name"])
+            if k and k != COPY_KERNEL:
+                per.setdefault((k, r["Kernel_Name"]), []).append(
+                    (int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+        path = os.path.join(PROFILES, f"kernel_stats_{w}.txt")
+        rows = []
+        for (k, full), v in per.items():
+            v.sort()
+            us = [x[1] for x in v]
+            rows.append((float(np.mean(us[-nph:])), full, k, us))
+        with open(path, "w") as f:
+            f.write(f"# rocprofv3 kernel statistics, workload {w} (MI355X, one GPU)\n")
+            f.write(f"# command (from the repository root): rocprofv3 --kernel-trace --stats --output-format csv "
+                    f"-d {args.trace_dir} -o run -- {_bench_cmd(args, '')}\n")
+            f.write(f"# summary: python3 bench.py --summarize stats --workload {w} --steps {args.steps} "
+                    f"--warmup {args.warmup} --phase-steps {nph} --trace-dir {args.trace_dir}\n")
+            f.write(f"# kernel sources sha256[:16]: {hsh}\n")
+            f.write(f"# 'timed us': mean of the kernel's last {nph} dispatches, the bench's phase-timed steps (one\n")
+            f.write("# descent part over all KV heads; the roofline divides by this); 'all' columns: every dispatch,\n")
+            f.write("# including warm-up and headline steps, where 16384+ rows run the descent as two concurrent parts\n")
+            f.write("# kernel | phase | calls | timed us | all average us | all min us | all max us\n")
+            for t, full, k, us in sorted(rows, key=lambda x: -x[0]):
+                name = full.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+                f.write(f"{name} | {PHASE_OF.get(k, '-')} | {len(us)} | {t:.1f} | {np.mean(us):.1f} | "
+                        f"{min(us):.1f} | {max(us):.1f}\n")
+        written.append(path)
+    for p in written:
+        print(os.path.relpath(p, ROOT))
+
+
 # ---------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample, two-phase: leaves fetched per row)
 # ---------------------------------------------------------------------------
@@ -303,6 +469,13 @@ def parse_args(argv=None):
     ap.add_argument("--fold-width", type=int, default=0,
                     help="base width D_E of the folded tree (default: the head dim, using the workload's "
                          "head-0 tree; otherwise a fresh base tree of that width with the workload's topology)")
+    ap.add_argument("--summarize", default=None, choices=["hbm", "busy", "stats"],
+                    help="write profiles/ summaries from rocprofv3 csv output (no GPU work): hbm needs "
+                         "--fetch-dir and --write-dir, busy --pmc-dir, stats --trace-dir")
+    ap.add_argument("--fetch-dir", default=None)
+    ap.add_argument("--write-dir", default=None)
+    ap.add_argument("--pmc-dir", default=None)
+    ap.add_argument("--trace-dir", default=None)
     ap.add_argument("--tree-placement", default="hbm", choices=["hbm", "host-leaves"],
                     help="host-leaves: leaf keys and values in pinned host memory, read by the "
                          "kernels over the host link (roots, mids, offsets stay in HBM)")
@@ -560,6 +733,9 @@ def run_one(args, workload, dev, with_cpu):
 
 def main():
     args = parse_args()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
