@@ -370,11 +370,14 @@ __device__ inline float4_t split_combine(float4_t acc, int lane) {
 // s = scale * Σ_t q_t k_t, summed
 // left to right over the exact products of the stored values, ties to the
 // lower node index.  The fp32 scores f differ from the fp64 sums by at most
-// E = d * 2^-23 * |q| * max|k| (a bound for any summation order with at most
-// 2 ulp per operation).  With T the K-th largest fp32 score (radix select),
-// every candidate with f > T + 2E is certainly selected and every candidate
-// with f < T - 2E certainly is not; the candidates in between are re-scored
-// in fp64 exactly as defined and the remaining places filled by rank.
+// E = n_e * 2^-23 * |q| * max|k| (a bound for any summation order with at
+// most 2 ulp per operation; n_e = d, or 128 + d/128 for wide rows summed
+// slice by slice, err_terms), plus |q_kg - q_exact| * max|k| when the stored
+// query is a rounding of an exact one that the ranking is defined by.  With
+// T the K-th largest fp32 score (radix select), every candidate with
+// f > T + 2E is certainly selected and every candidate with f < T - 2E
+// certainly is not; the candidates in between are re-scored in fp64 exactly
+// as defined and the remaining places filled by rank.
 // ---------------------------------------------------------------------------
 constexpr int kBand = 32;        // band members handled per round
 constexpr int kLoadBatch = 8;    // score loads kept in flight per lane in the select passes

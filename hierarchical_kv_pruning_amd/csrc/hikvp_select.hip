@@ -14,15 +14,17 @@
 //               scores; each selection is counted in its (KV head, root)
 //               group.  The per-row select kernels keep a few KB of LDS per
 //               wave so many rows are in flight per CU.
-//   k_root_scan / k_root_fill  lay the groups out in tiles of 32 rows; the
+//   k_root_scan / k_root_fill  lay the groups out in tiles of 64 rows; the
 //               fill also records where each selected root's children start
 //               in the row's mid candidate list.
-//   k_mid_gemm  one wave per tile: the tile's rows against the root's child
-//               span on bf16 (or fp32) MFMA 16x16 tiles; the span is read once
-//               per tile instead of once per row.  Scores land in each row's
-//               candidate slots of the workspace.
-//   k_mid_select   one wave per row (a workgroup per row for long candidate
-//               lists): Top-K_I over the row's mid scores.
+//   k_mid_gemm  one workgroup (four waves of 16 rows) per tile: the tile's
+//               rows against the root's child span on bf16 (or fp32) MFMA
+//               16x16 tiles, the span staged in LDS and read once per tile
+//               instead of once per row.  Only the children that can still be
+//               among a row's K_I best are written, as (score, child) pairs.
+//   k_mid_select   one wave per row: Top-K_I over the row's surviving mid
+//               candidates (held in registers, or read from the workspace in
+//               every pass when there are more than the register list holds).
 //   k_bucket_link  registers each selection in its (KV head, mid) bucket,
 //               with where the mid's children start in the row's leaf
 //               candidate list.
