@@ -109,3 +109,65 @@ def test_source_hash_covers_every_library_source():
     csrc = os.path.join(ROOT, "hierarchical_kv_pruning_amd", "csrc")
     want = {f for f in os.listdir(csrc) if f.endswith((".hip", ".h"))} | {"atlaskv.h"}
     assert want <= names
+
+
+def _write_counter_csv(path, dispatches):
+    """rocprofv3-style counter_collection.csv: dispatches = [(kernel, {counter: value})]."""
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+                    "End_Timestamp"])
+        for i, (kernel, counters) in enumerate(dispatches):
+            for name, value in counters.items():
+                w.writerow([i + 1, kernel, name, value, 1000 * i, 1000 * i + 500 + i])
+
+
+def test_hbm_summary_scales_by_the_copy_and_averages_the_phase_steps(tmp_path, monkeypatch):
+    """--summarize hbm: a kernel's fetch and write KiB are scaled by what the
+    same counters read for the 1 GiB calibration copy, and only its last
+    phase-steps dispatches (the phase-timed ones) are averaged."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    os.makedirs(bench.PROFILES)
+    leaf = "void hikvp::(anonymous namespace)::k_leaf_score<hikvp::BF16, 128, false>(hikvp::StepArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    # five dispatches of the leaf stream (the last two are the phase-timed ones), then the copy
+    fetch = [(leaf, {"FETCH_SIZE": v}) for v in (1.0, 2.0, 3.0, 100.0, 300.0)] + [(copy, {"FETCH_SIZE": 524288.0})]
+    write = [(leaf, {"WRITE_SIZE": v}) for v in (9.0, 9.0, 9.0, 10.0, 30.0)] + [(copy, {"WRITE_SIZE": 1048576.0})]
+    _write_counter_csv(str(tmp_path / "f" / "run_counter_collection.csv"), fetch)
+    _write_counter_csv(str(tmp_path / "w" / "run_counter_collection.csv"), write)
+    args = bench.parse_args(["--summarize", "hbm", "--workload", "m1e6", "--steps", "3", "--warmup", "1",
+                             "--phase-steps", "2", "--fetch-dir", str(tmp_path / "f"),
+                             "--write-dir", str(tmp_path / "w")])
+    bench.summarize(args)
+    path = os.path.join(bench.PROFILES, "leaf_score_stream_m1e6_hbm_counters.txt")
+    fields = dict(line.split(":", 1) for line in open(path) if ":" in line and not line.startswith("#"))
+    assert float(fields["fetch_scale"]) == pytest.approx(2.0)
+    assert float(fields["write_scale"]) == pytest.approx(1.0)
+    assert float(fields["fetch_kib_per_dispatch"]) == pytest.approx(200.0)
+    assert float(fields["write_kib_per_dispatch"]) == pytest.approx(20.0)
+    assert int(fields["hbm_bytes_per_launch"]) == (200 * 2 + 20) * 1024
+    assert fields["kernel_source_sha256_16"].strip() == bench.kernel_source_hash()
+    assert bench.read_traffic("leaf_score_stream", "m1e6") == (200 * 2 + 20) * 1024
+    text = open(path).read()
+    assert "# fetch pass: rocprofv3 --pmc FETCH_SIZE" in text and "--calib-copy-gib 1" in text
+
+
+def test_busy_summary_uses_the_tools_metric_definitions(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    os.makedirs(bench.PROFILES)
+    k = "void hikvp::(anonymous namespace)::k_mid_gemm<hikvp::BF16, 128, false>(hikvp::StepArgs)"
+    c = {"SQ_VALU_MFMA_BUSY_CYCLES": 1024 * 50.0, "SQ_ACTIVE_INST_VALU": 256 * 25.0, "GRBM_GUI_ACTIVE": 100.0,
+         "SQ_WAVES": 10.0, "SQ_INSTS_VALU": 1000.0, "SQ_INSTS_MFMA": 40.0}
+    _write_counter_csv(str(tmp_path / "b" / "run_counter_collection.csv"), [(k, c), (k, c)])
+    args = bench.parse_args(["--summarize", "busy", "--workload", "m1e6", "--steps", "3", "--warmup", "1",
+                             "--phase-steps", "2", "--pmc-dir", str(tmp_path / "b")])
+    bench.summarize(args)
+    rows = [l for l in open(os.path.join(bench.PROFILES, "busy_counters_m1e6.txt")) if l.startswith("k_mid_gemm")]
+    cols = [x.strip() for x in rows[0].split("|")]
+    assert cols[1] == "mid_bucket_gemm" and cols[2] == "2"
+    assert float(cols[4]) == pytest.approx(50.0)     # MfmaUtil
+    assert float(cols[5]) == pytest.approx(25.0)     # VALUBusy
+    assert float(cols[7]) == pytest.approx(100.0)    # VALU instructions a wave
+    assert float(cols[8]) == pytest.approx(4.0)      # MFMA instructions a wave
