@@ -238,8 +238,9 @@ def summarize(args):
     if args.summarize == "hbm":
         fetch, write = _counter_dispatches(args.fetch_dir), _counter_dispatches(args.write_dir)
         calib_gib = 1
-        cf = fetch[COPY_KERNEL][-1][1]["FETCH_SIZE"]
-        cw = write[COPY_KERNEL][-1][1]["WRITE_SIZE"]
+        # the calibration copy is the largest device copy of each pass
+        cf = max(c["FETCH_SIZE"] for _, c, _ in fetch[COPY_KERNEL])
+        cw = max(c["WRITE_SIZE"] for _, c, _ in write[COPY_KERNEL])
         fscale, wscale = calib_gib * (1 << 20) / cf, calib_gib * (1 << 20) / cw
         bench_cmd = _bench_cmd(args, f" --calib-copy-gib {calib_gib}")
         for phase, kernels in HBM_SUMMARY_KERNELS.items():
