@@ -893,14 +893,18 @@ atlaskv_status atlaskv_build_tree_view(const atlaskv_tensor* root_k, const atlas
   v->stream = (hipStream_t)stream;
   const int Hkv = v->dev.Hkv;
   const size_t stats_bytes = offsetof(BuildStats, norm_bits) + sizeof(unsigned int) * 3 * (size_t)Hkv;
-  // all streams at the default priority
+  // all streams at the default priority.  The fork/join events only order
+  // kernels of this device's streams (no host waits on them), so they skip
+  // the system-scope fence an event record otherwise issues (an L2
+  // write-back for host visibility in the middle of the step)
+  const unsigned evf = hipEventDisableTiming | hipEventDisableSystemFence;
   hipError_t e = hipStreamCreateWithFlags(&v->aux, hipStreamNonBlocking);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&v->fork, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&v->join, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&v->part_fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&v->fork, evf);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&v->join, evf);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&v->part_fork, evf);
   for (int i = 0; i < kMaxParts - 1 && e == hipSuccess; ++i) {
     e = hipStreamCreateWithFlags(&v->part_s[i], hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&v->part_join[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&v->part_join[i], evf);
   }
   if (e != hipSuccess) { release_view(v); return hip_fail(e, "stream/event creation"); }
   e = hipMalloc((void**)&v->stats, stats_bytes);
