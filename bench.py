@@ -188,6 +188,10 @@ HBM_SUMMARY_KERNELS = {
 BUSY_KERNELS = ("k_root_mfma", "k_root", "k_mid_gemm", "k_mid_select", "k_bucket_link", "k_leaf_score",
                 "k_leaf_select", "k_seq_mfma", "k_seq_decode_mfma", "k_seq_combine")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
+# the busy pass: the tool's two derived metrics and the raw counters behind them
+BUSY_COUNTERS = ("MfmaUtil", "VALUBusy", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU",
+                 "SQ_INSTS_MFMA", "SQ_WAVES", "GRBM_GUI_ACTIVE")
+XCDS = 8  # MI355X accelerator complex dies; the csv sums GRBM_GUI_ACTIVE over them
 
 
 def _short_kernel(name):
@@ -271,28 +275,31 @@ def summarize(args):
         per = _counter_dispatches(args.pmc_dir)
         path = os.path.join(PROFILES, f"busy_counters_{w}.txt")
         with open(path, "w") as f:
-            f.write(f"# MFMA and VALU activity per kernel, workload {w} (MI355X: 256 CUs, 1024 SIMDs)\n")
-            f.write("# counter pass: rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_BUSY_CYCLES "
-                    "SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_WAIT_INST_ANY SQ_WAVES GRBM_GUI_ACTIVE "
+            f.write(f"# MFMA and VALU activity per kernel, workload {w} (MI355X: 8 XCDs, 256 CUs, 1024 SIMDs)\n")
+            f.write(f"# counter pass: rocprofv3 --pmc {' '.join(BUSY_COUNTERS)} "
                     f"--output-format csv -d {args.pmc_dir} -o run -- {_bench_cmd(args, '')}\n")
             f.write(f"# summary: python3 bench.py --summarize busy --workload {w} --steps {args.steps} "
                     f"--warmup {args.warmup} --phase-steps {nph} --pmc-dir {args.pmc_dir}\n")
             f.write("# mean over the last phase-steps dispatches of each kernel (the phase-timed steps):\n")
-            f.write("#   mfma_busy_pct = 100 * SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * 1024 SIMDs)\n")
-            f.write("#                   (rocprofv3's MfmaUtil metric)\n")
-            f.write("#   valu_busy_pct = 100 * SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE * 256 CUs)\n")
-            f.write("#                   (rocprofv3's VALUBusy metric)\n")
+            f.write("#   mfma_busy_pct: rocprofv3's MfmaUtil, 100 * sum(SQ_VALU_MFMA_BUSY_CYCLES) /\n")
+            f.write("#                  (max(GRBM_GUI_ACTIVE) * 1024 SIMDs)\n")
+            f.write("#   valu_busy_pct: rocprofv3's VALUBusy, 100 * sum(SQ_ACTIVE_INST_VALU) / 256 CUs /\n")
+            f.write("#                  max(GRBM_GUI_ACTIVE)\n")
+            f.write("#   max(GRBM_GUI_ACTIVE) is one XCD's active cycles; the csv's GRBM_GUI_ACTIVE column sums\n")
+            f.write("#   the 8 XCDs' counters, so the raw columns below divide it by 8 (the '(raw)' figures, a\n")
+            f.write("#   check on the tool's metrics)\n")
             f.write(f"# kernel sources sha256[:16]: {hsh}\n")
-            f.write("kernel | phase | dispatches | us | mfma_busy_pct | valu_busy_pct | waves | valu_insts_per_wave | "
-                    "mfma_insts_per_wave\n")
+            f.write("kernel | phase | dispatches | us | mfma_busy_pct | valu_busy_pct | mfma_busy_pct (raw) | "
+                    "valu_busy_pct (raw) | waves | valu_insts_per_wave | mfma_insts_per_wave\n")
             for k in BUSY_KERNELS:
                 if k not in per:
                     continue
                 last = per[k][-nph:]
-                mean = lambda c: float(np.mean([x[1].get(c, 0.0) for x in last]))
-                g = mean("GRBM_GUI_ACTIVE")
+                mean = lambda c: float(np.mean([x[1].get(c, float("nan")) for x in last]))
+                g = mean("GRBM_GUI_ACTIVE") / XCDS
                 waves = max(mean("SQ_WAVES"), 1.0)
                 f.write(f"{k} | {PHASE_OF.get(k, '-')} | {len(per[k])} | {np.mean([x[2] for x in last]) / 1e3:.1f} | "
+                        f"{mean('MfmaUtil'):.2f} | {mean('VALUBusy'):.2f} | "
                         f"{100 * mean('SQ_VALU_MFMA_BUSY_CYCLES') / (g * 1024):.2f} | "
                         f"{100 * mean('SQ_ACTIVE_INST_VALU') / (g * 256):.2f} | {waves:.0f} | "
                         f"{mean('SQ_INSTS_VALU') / waves:.0f} | {mean('SQ_INSTS_MFMA') / waves:.1f}\n")

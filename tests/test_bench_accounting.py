@@ -158,8 +158,9 @@ def test_busy_summary_uses_the_tools_metric_definitions(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
     os.makedirs(bench.PROFILES)
     k = "void hikvp::(anonymous namespace)::k_mid_gemm<hikvp::BF16, 128, false>(hikvp::StepArgs)"
-    c = {"SQ_VALU_MFMA_BUSY_CYCLES": 1024 * 50.0, "SQ_ACTIVE_INST_VALU": 256 * 25.0, "GRBM_GUI_ACTIVE": 100.0,
-         "SQ_WAVES": 10.0, "SQ_INSTS_VALU": 1000.0, "SQ_INSTS_MFMA": 40.0}
+    # GRBM_GUI_ACTIVE as the csv holds it: the 8 XCDs' counts summed (100 cycles each)
+    c = {"SQ_VALU_MFMA_BUSY_CYCLES": 1024 * 50.0, "SQ_ACTIVE_INST_VALU": 256 * 25.0, "GRBM_GUI_ACTIVE": 800.0,
+         "SQ_WAVES": 10.0, "SQ_INSTS_VALU": 1000.0, "SQ_INSTS_MFMA": 40.0, "MfmaUtil": 49.0, "VALUBusy": 24.0}
     _write_counter_csv(str(tmp_path / "b" / "run_counter_collection.csv"), [(k, c), (k, c)])
     args = bench.parse_args(["--summarize", "busy", "--workload", "m1e6", "--steps", "3", "--warmup", "1",
                              "--phase-steps", "2", "--pmc-dir", str(tmp_path / "b")])
@@ -167,7 +168,9 @@ def test_busy_summary_uses_the_tools_metric_definitions(tmp_path, monkeypatch):
     rows = [l for l in open(os.path.join(bench.PROFILES, "busy_counters_m1e6.txt")) if l.startswith("k_mid_gemm")]
     cols = [x.strip() for x in rows[0].split("|")]
     assert cols[1] == "mid_bucket_gemm" and cols[2] == "2"
-    assert float(cols[4]) == pytest.approx(50.0)     # MfmaUtil
-    assert float(cols[5]) == pytest.approx(25.0)     # VALUBusy
-    assert float(cols[7]) == pytest.approx(100.0)    # VALU instructions a wave
-    assert float(cols[8]) == pytest.approx(4.0)      # MFMA instructions a wave
+    assert float(cols[4]) == pytest.approx(49.0)     # the tool's MfmaUtil as collected
+    assert float(cols[5]) == pytest.approx(24.0)     # the tool's VALUBusy as collected
+    assert float(cols[6]) == pytest.approx(50.0)     # MfmaUtil from the raw counters, per-XCD GRBM
+    assert float(cols[7]) == pytest.approx(25.0)     # VALUBusy from the raw counters, per-XCD GRBM
+    assert float(cols[9]) == pytest.approx(100.0)    # VALU instructions a wave
+    assert float(cols[10]) == pytest.approx(4.0)     # MFMA instructions a wave
