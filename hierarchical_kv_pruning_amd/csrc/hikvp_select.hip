@@ -574,56 +574,63 @@ __global__ __launch_bounds__(64 * kMidWaves) void k_mid_gemm(StepArgs a) {
     }
     __syncthreads();                           // stage 0 staged
     const int nr = (F + RC - 1) / RC;
-    const int nst = nr * ns;                   // stages
+    // Stages go chunk by chunk, within a chunk slice by slice and within a
+    // slice round by round (one slice for rows of up to 128: stage = round),
+    // so a wide row's query slice is read once per chunk and slice rather
+    // than once per round; the chunk's rounds accumulate side by side.
+    int st = 0;                                // the current stage (its buffer: st & 1)
     for (int cc = 0; cc < nr; cc += CR) {      // chunks of CR rounds
-      uint32_t x[4][NV];                       // the chunk's keys (0: past the span)
+      const int nrc = min(CR, nr - cc);        // rounds in this chunk
+      float4_t p[CR][TU];
 #pragma unroll
-      for (int r = 0; r < CR; ++r) {
-        const int rr = cc + r;
-        if (rr < nr) {                         // uniform over the workgroup
-          float4_t p[TU];
+      for (int r = 0; r < CR; ++r)
 #pragma unroll
-          for (int u = 0; u < TU; ++u) p[u] = float4_t{0.f, 0.f, 0.f, 0.f};
-          for (int sl = 0; sl < ns; ++sl) {
-            const int st = rr * ns + sl;
-            const bool more = st + 1 < nst;
+        for (int u = 0; u < TU; ++u) p[r][u] = float4_t{0.f, 0.f, 0.f, 0.f};
+      for (int sl = 0; sl < ns; ++sl) {
+        if constexpr (D == 0) {
+          if (active) {
+            load_frag<E, KCH>(afr, qp ? qp + (int64_t)sl * RB : nullptr);
+            if constexpr (LO) load_frag<E, KCH>(alo, lp ? lp + (int64_t)sl * RB : nullptr);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < CR; ++r) {
+          if (r < nrc) {                       // uniform over the workgroup
+            // the next stage: the chunk's next round, else the next slice's
+            // first round, else the next chunk's first stage
+            int nrr = -1, nsl = 0;
+            if (r + 1 < nrc) nrr = cc + r + 1, nsl = sl;
+            else if (sl + 1 < ns) nrr = cc, nsl = sl + 1;
+            else if (cc + CR < nr) nrr = cc + CR, nsl = 0;
+            const bool more = nrr >= 0;
             U32x4 stg[PPT];                    // the next stage, in flight while this one is scored
-            if (more) {
-              const int nrr = (st + 1) / ns, nsl = (st + 1) % ns;
-              stage_round<RB, NT, PPT>(stg, kb + (int64_t)nsl * RB, rsb, nrr * RC, F, tid);
-            }
+            if (more) stage_round<RB, NT, PPT>(stg, kb + (int64_t)nsl * RB, rsb, nrr * RC, F, tid);
             if (active) {
-              if constexpr (D == 0) {
-                load_frag<E, KCH>(afr, qp ? qp + (int64_t)sl * RB : nullptr);
-                if constexpr (LO) load_frag<E, KCH>(alo, lp ? lp + (int64_t)sl * RB : nullptr);
-              }
-              // in tile u, lane column col is child rr*RC + col*TU + u
+              // in tile u, lane column col is child (cc+r)*RC + col*TU + u
               const char* lb = lds[st & 1] + quad * 16;
 #pragma unroll
               for (int u = 0; u < TU; ++u) {
                 uint4 bfr[KCH];
 #pragma unroll
                 for (int m = 0; m < KCH; ++m) bfr[m] = *(const uint4*)(lb + (col * TU + u) * LRB + m * 64);
-                p[u] = slice_tile<E, KCH, LO, D == 0>(afr, alo, bfr, p[u]);
+                p[r][u] = slice_tile<E, KCH, LO, D == 0>(afr, alo, bfr, p[r][u]);
               }
             }
             if (more) stage_put<RB, LRB, NT, PPT>(stg, lds[(st + 1) & 1], tid);
             __syncthreads();
+            ++st;
           }
-          if (active)
-#pragma unroll
-            for (int u = 0; u < TU; ++u) {
-              const bool valid = rr * RC + col * TU + u < F;
-#pragma unroll
-              for (int v = 0; v < 4; ++v) x[v][r * TU + u] = valid ? ord_key(p[u][v]) : 0u;
-            }
-        } else {
-#pragma unroll
-          for (int u = 0; u < TU; ++u)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) x[v][r * TU + u] = 0u;
         }
       }
+      uint32_t x[4][NV];                       // the chunk's keys (0: past the span)
+#pragma unroll
+      for (int r = 0; r < CR; ++r)
+#pragma unroll
+        for (int u = 0; u < TU; ++u) {
+          const bool valid = r < nrc && (cc + r) * RC + col * TU + u < F;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) x[v][r * TU + u] = valid ? ord_key(p[r][u][v]) : 0u;
+        }
       if (!active) continue;
       uint32_t lo[4] = {0u, 0u, 0u, 0u};       // keep every valid child
       if (filt) {
