@@ -579,6 +579,13 @@ __global__ __launch_bounds__(64 * kMidWaves) void k_mid_gemm(StepArgs a) {
     // so a wide row's query slice is read once per chunk and slice rather
     // than once per round; the chunk's rounds accumulate side by side.
     int st = 0;                                // the current stage (its buffer: st & 1)
+    uint4 anx[KCH], lnx[KCH];                  // wide rows: the next query slice, loaded a slice ahead
+    if constexpr (D == 0) {
+      if (active) {
+        load_frag<E, KCH>(anx, qp);
+        if constexpr (LO) load_frag<E, KCH>(lnx, lp);
+      }
+    }
     for (int cc = 0; cc < nr; cc += CR) {      // chunks of CR rounds
       const int nrc = min(CR, nr - cc);        // rounds in this chunk
       float4_t p[CR][TU];
@@ -589,8 +596,17 @@ __global__ __launch_bounds__(64 * kMidWaves) void k_mid_gemm(StepArgs a) {
       for (int sl = 0; sl < ns; ++sl) {
         if constexpr (D == 0) {
           if (active) {
-            load_frag<E, KCH>(afr, qp ? qp + (int64_t)sl * RB : nullptr);
-            if constexpr (LO) load_frag<E, KCH>(alo, lp ? lp + (int64_t)sl * RB : nullptr);
+#pragma unroll
+            for (int m = 0; m < KCH; ++m) {
+              afr[m] = anx[m];
+              if constexpr (LO) alo[m] = lnx[m];
+            }
+            // the next (chunk, slice)'s query slice, in flight during this slice's rounds
+            if (sl + 1 < ns || cc + CR < nr) {
+              const int64_t no = (int64_t)(sl + 1 < ns ? sl + 1 : 0) * RB;
+              load_frag<E, KCH>(anx, qp ? qp + no : nullptr);
+              if constexpr (LO) load_frag<E, KCH>(lnx, lp ? lp + no : nullptr);
+            }
           }
         }
 #pragma unroll
