@@ -578,7 +578,13 @@ atlaskv_status plan_folded(const atlaskv_tensor* q, const atlaskv_tree_view_s* v
   if (!kg_empty) {
     atlaskv_tensor qd = group_rows_desc(B, N, (int)Hq, t.d, t.dtype, (void*)(uintptr_t)256);
     if ((st = plan_call(&qd, v, nullptr, nullptr, Kpl, nullptr, nullptr, false, pd, kModeFoldedDescent))) return st;
-    pd.exact_logits = 1;
+    // fp32 trees: the KG softmax takes fp64 logits of the exact folded query
+    // (their fp32 scores can be off by more than an fp32 output resolves at
+    // wide D_E).  bf16 trees keep the scores of the rounded pair hi + lo
+    // (each component within about 2^-18 of the exact one; q_delta bounds the
+    // norm of the rest), whose logit error lies far below the rounding of a
+    // bf16 output, and skip re-reading the selected keys
+    pd.exact_logits = t.dtype == ATLASKV_F32;
     o = align256(pd.total);
   }
   const size_t R = (size_t)p.R;

@@ -8,8 +8,9 @@
 // the pruned descent runs on the base tree with q', and W_V[g] is applied to
 // the softmax-weighted base values afterwards (k_unfold_values).  The
 // descent scores with q' rounded to the tree's dtype; its selections are
-// exact for the unrounded q' and the KG softmax takes the selected leaves'
-// logits from it, so the result is the projected trees' up to fp32 rounding.
+// exact for the unrounded q', and the KG softmax takes the selected leaves'
+// logits from it on fp32 trees (from the scores of the rounded pair on bf16
+// trees), so the result is the projected trees' up to fp32 rounding.
 #include "hikvp_device.h"
 #include "hikvp_round.h"
 

@@ -127,8 +127,9 @@ struct StepArgs {
   int32_t* bucket_ovf;        // [rows * K[1] / (kBucketSlots + 1) + 1] keys (g*M_I + mid) with overflow members
   float* o_kg;                // [R, d] softmax-weighted leaf values (fp32)
   float* lse_kg;              // [R] log-sum-exp of the selected leaf logits
-  int exact_logits;           // non-zero: the KG softmax takes the selected leaves' logits from the
-                              // exact query r.q_exact (fp64 dot products), not from the scores
+  int exact_logits;           // non-zero (folded calls on fp32 trees): the KG softmax takes the selected
+                              // leaves' logits from the exact query r.q_exact (fp64 dot products),
+                              // not from the scores
 };
 
 // Bucket array index of key = g*M_I + mid: a bijective transpose of [0, 64*q)

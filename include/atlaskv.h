@@ -349,8 +349,10 @@ const char* atlaskv_shared_phase_name(int32_t phase);
  * sequence half.  The scores are computed with q' rounded to the tree dtype
  * (in bf16 as the rounded q' plus its rounded residual); the selections are
  * exact for the unrounded q' (the rounding's bound widens the band that is
- * re-scored in fp64 with q') and the KG softmax takes the selected leaves'
- * logits from the unrounded q' in fp64.  The result equals
+ * re-scored in fp64 with q').  On fp32 trees the KG softmax takes the
+ * selected leaves' logits from the unrounded q' in fp64; on bf16 trees it
+ * uses their scores (rounded q' plus residual, fp32 sums), whose error lies
+ * far below a bf16 output's rounding.  The result equals
  * atlaskv_hikvp_attend on the per-head projected trees (w_k[g] k, w_v[g] v)
  * up to fp32 rounding.  opts->sel_* receive per-row selections of base
  * nodes.  Workspace size from atlaskv_folded_workspace_size (it holds q' in
