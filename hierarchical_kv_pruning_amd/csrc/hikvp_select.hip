@@ -1151,45 +1151,45 @@ __device__ inline void score_member_group(const StepArgs& a, const char* kp, int
 
 // Wide key rows (base-embedding trees): the same tiles and item layout over
 // 128-element slices of the row, each round's tiles accumulated over the
-// slices before the two halves are combined; no software pipelining.
-template <class E, bool LO>
-__device__ inline void score_member_group_wide(const StepArgs& a, const char* kp, int64_t rsb, int F, int2 mem,
-                                               int g0, int gcnt, int lane) {
+// slices before the two halves are combined.  Up to NG groups of 8 members
+// (members g0 .. g0 + cnt - 1) are scored together: each round's key slices
+// are loaded once for all of them, so a bucket's span is read once however
+// many members it holds (with base-embedding trees every query head selects
+// from the one tree, and a bucket holds ~13 rows at the m1e6 layer).
+template <class E, bool LO, int NG, int TU>
+__device__ inline void score_members_wide(const StepArgs& a, const char* kp, int64_t rsb, int F, int2 mem,
+                                          int g0, int cnt, int lane) {
   constexpr int SW = 128;
   constexpr int RB = SW * E::kBytes;       // bytes per key-row slice
   constexpr int KP = RB / 128;             // 16-byte pieces per lane per tile and slice
-  constexpr int TU = 4;                    // tiles per round = consecutive keys per lane
+  // TU: tiles per round = consecutive keys per lane
   const int ns = a.t.d / SW;
   const int quad = lane >> 4, item = lane & 7;
   const bool owner = lane < 32 && (lane & 15) < 8;   // holds combined scores
-  const int row = __shfl(mem.x, g0 + item);
-  const char* qp = nullptr;                // member `item`'s query (+ this lane's piece offset)
-  const char* lp = nullptr;                // its bf16 residual (LO)
-  if (item < gcnt) {
-    int b, n, h;
-    decode_row(a.r, row, b, n, h);
-    qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes + split_off(lane, 0);
-    if constexpr (LO) lp = (const char*)a.r.q_lo + (int64_t)row * a.t.d * E::kBytes + split_off(lane, 0);
-  }
-  float* dst[4];
+  const char* qp[NG];                      // group g's member `item`: its query (+ this lane's piece offset)
+  const char* lp[NG];                      // its bf16 residual (LO)
 #pragma unroll
-  for (int vv = 0; vv < 4; ++vv) {
-    const int ms = 4 * (quad & 1) + vv;
-    const int srow = __shfl(mem.x, g0 + ms), sbase = __shfl(mem.y, g0 + ms);
-    dst[vv] = (owner && ms < gcnt) ? a.leaf_scores + (int64_t)srow * a.c2max + sbase + item * TU : nullptr;
+  for (int g = 0; g < NG; ++g) {
+    const int mi = 8 * g + item;
+    const int row = __shfl(mem.x, g0 + mi);
+    qp[g] = nullptr;
+    lp[g] = nullptr;
+    if (mi < cnt) {
+      int b, n, h;
+      decode_row(a.r, row, b, n, h);
+      qp[g] = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes + split_off(lane, 0);
+      if constexpr (LO) lp[g] = (const char*)a.r.q_lo + (int64_t)row * a.t.d * E::kBytes + split_off(lane, 0);
+    }
   }
   for (int t0 = 0; t0 < F; t0 += 8 * TU) {
-    float4_t acc[TU];
+    float4_t acc[NG][TU];
 #pragma unroll
-    for (int u = 0; u < TU; ++u) acc[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int u = 0; u < TU; ++u) acc[g][u] = float4_t{0.f, 0.f, 0.f, 0.f};
     for (int sl = 0; sl < ns; ++sl) {
       const int64_t so = (int64_t)sl * RB;
-      uint4 afr[KP], alo[KP], bfr[TU][KP];
-#pragma unroll
-      for (int m = 0; m < KP; ++m) {
-        afr[m] = qp ? *(const uint4*)(qp + so + m * 128) : make_uint4(0, 0, 0, 0);
-        if constexpr (LO) alo[m] = lp ? *(const uint4*)(lp + so + m * 128) : make_uint4(0, 0, 0, 0);
-      }
+      uint4 bfr[TU][KP];
 #pragma unroll
       for (int u = 0; u < TU; ++u) {
         const char* p = kp + (int64_t)min(t0 + item * TU + u, F - 1) * rsb + so;
@@ -1197,31 +1197,53 @@ __device__ inline void score_member_group_wide(const StepArgs& a, const char* kp
         for (int m = 0; m < KP; ++m) bfr[u][m] = load_nt(p + m * 128);
       }
 #pragma unroll
-      for (int u = 0; u < TU; ++u) acc[u] = slice_tile<E, KP, LO, true>(afr, alo, bfr[u], acc[u]);
-    }
-    float4_t sc[TU];
+      for (int g = 0; g < NG; ++g) {
+        if (8 * g < cnt) {                 // uniform over the wave
+          uint4 afr[KP], alo[KP];
 #pragma unroll
-    for (int u = 0; u < TU; ++u) sc[u] = split_combine(acc[u], lane);
+          for (int m = 0; m < KP; ++m) {
+            afr[m] = qp[g] ? *(const uint4*)(qp[g] + so + m * 128) : make_uint4(0, 0, 0, 0);
+            if constexpr (LO) alo[m] = lp[g] ? *(const uint4*)(lp[g] + so + m * 128) : make_uint4(0, 0, 0, 0);
+          }
+#pragma unroll
+          for (int u = 0; u < TU; ++u) acc[g][u] = slice_tile<E, KP, LO, true>(afr, alo, bfr[u], acc[g][u]);
+        }
+      }
+    }
     const int c0 = t0 + item * TU;
 #pragma unroll
-    for (int vv = 0; vv < 4; ++vv)
-      if (dst[vv])
+    for (int g = 0; g < NG; ++g) {
+      if (8 * g < cnt) {                   // uniform over the wave
+        float4_t sc[TU];
 #pragma unroll
-        for (int u = 0; u < TU; ++u)
-          if (c0 + u < F) dst[vv][t0 + u] = sc[u][vv];
+        for (int u = 0; u < TU; ++u) sc[u] = split_combine(acc[g][u], lane);
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) {
+          const int mi = 8 * g + 4 * (quad & 1) + vv;
+          const int srow = __shfl(mem.x, g0 + mi), sbase = __shfl(mem.y, g0 + mi);
+          if (owner && mi < cnt) {
+            float* d = a.leaf_scores + (int64_t)srow * a.c2max + sbase + c0;
+#pragma unroll
+            for (int u = 0; u < TU; ++u)
+              if (c0 + u < F) d[u] = sc[u][vv];
+          }
+        }
+      }
+    }
   }
 }
 
 template <class E, int D, bool LO>
 __device__ inline void score_members(const StepArgs& a, const char* kp, int64_t rsb, int F, int2 mem, int g0,
                                      int gcnt, int lane) {
-  if constexpr (D == 0) score_member_group_wide<E, LO>(a, kp, rsb, F, mem, g0, gcnt, lane);
+  if constexpr (D == 0) score_members_wide<E, LO, 1, 4>(a, kp, rsb, F, mem, g0, gcnt, lane);
   else score_member_group<E, D, LO>(a, kp, rsb, F, mem, g0, gcnt, lane);
 }
 
 // One wave per bucket: its first kBucketSlots members, 8 at a time (a bucket
 // with more than 8 members makes further passes over its span, mostly L2
-// hits); members past kBucketSlots are left to k_leaf_score_overflow.
+// hits; wide rows take all of them in one pass); members past kBucketSlots
+// are left to k_leaf_score_overflow.
 template <class E, int D, bool LO>
 __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
@@ -1249,8 +1271,16 @@ __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
     int cnt = a.bucket_cnt[key];
     cnt = cnt < kBucketSlots ? cnt : kBucketSlots;
     const int2 mem = lane < kBucketSlots ? a.bucket_slot[(int64_t)key * kBucketSlots + lane] : make_int2(-1, 0);
-    for (int g0 = 0; g0 < cnt; g0 += 8)
-      score_members<E, D, LO>(a, kp, rsb, F, mem, g0, min(8, cnt - g0), lane);
+    if constexpr (D == 0) {
+      // three groups (24 members) a pass, four keys a lane a round: at one
+      // group a pass the span is read once a group, and fewer keys a round
+      // keep too few bytes in flight (measured)
+      for (int g0 = 0; g0 < cnt; g0 += 24)
+        score_members_wide<E, LO, 3, 4>(a, kp, rsb, F, mem, g0, min(24, cnt - g0), lane);
+    } else {
+      for (int g0 = 0; g0 < cnt; g0 += 8)
+        score_members<E, D, LO>(a, kp, rsb, F, mem, g0, min(8, cnt - g0), lane);
+    }
     cur = nxt;
     v = vn;
   }
