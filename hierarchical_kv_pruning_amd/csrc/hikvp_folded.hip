@@ -17,21 +17,24 @@
 namespace hikvp {
 namespace {
 
-// Work tiles: kFoldRows rows sharing one KV head g, the layer's tokens in
-// order with the group's G heads each (row u of the tile: token
-// (tile*kFoldRows + u) / G, head g*G + u % G); a workgroup stages the head's
-// projection in LDS once for its 16 rows (4 waves x 4 rows), instead of
-// every row reading the 32-64 KB matrix through L2.
-constexpr int kFoldRows = 16, kFoldRPW = 4;
+// Work tiles: 4*RPW rows sharing one KV head g, the layer's tokens in order
+// with the group's G heads each (row u of the tile: token (tile*4*RPW + u) /
+// G, head g*G + u % G); a workgroup stages the head's projection in LDS once
+// for its rows (4 waves x RPW rows), instead of every row reading the 32-64 KB
+// matrix through L2.  The fold takes 4 rows a wave (fp64 sums: more rows did
+// not help), the unfold 8 (its fp32 sums reuse each staged weight for more
+// rows: 82 -> 72 us at D_E = 384, 607 -> 481 us at 3072; 16 rows were slower).
+constexpr int kFoldRPW = 4, kUnfoldRPW = 8;
 
 struct FoldRow {
   int row, b, n, h;
   bool ok;
 };
+template <int RPW>
 __device__ inline FoldRow fold_row(const FoldArgs& a, int g, int tile, int wave, int rho) {
   FoldRow f;
   const int G = a.r.G;
-  const int u = tile * kFoldRows + wave * kFoldRPW + rho;
+  const int u = tile * 4 * RPW + wave * RPW + rho;
   f.ok = u < a.r.B * a.r.N * G;
   const int tok = f.ok ? u / G : 0;
   f.b = tok / a.r.N;
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(256) void k_fold_query(FoldArgs a, int tiles_per_he
   const int DE = a.DE;
   const char* wg = (const char*)a.w_k + (int64_t)g * a.wks[0] * E::kBytes;
   for (int rho = 0; rho < kFoldRPW; ++rho) {
-    const FoldRow f = fold_row(a, g, tile, wave, rho);
+    const FoldRow f = fold_row<kFoldRPW>(a, g, tile, wave, rho);
     const int64_t qb = q_off(a.r.qks, f.b, f.n, f.h);
     for (int t = lane; t < D; t += 64) q_lds[wave][rho][t] = f.ok ? load_f32<E>(a.r.q_kg, qb + t) : 0.f;
   }
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(256) void k_fold_query(FoldArgs a, int tiles_per_he
     }
 #pragma unroll
     for (int rho = 0; rho < kFoldRPW; ++rho) {
-      const FoldRow f = fold_row(a, g, tile, wave, rho);
+      const FoldRow f = fold_row<kFoldRPW>(a, g, tile, wave, rho);
       if (!f.ok) continue;
 #pragma unroll
       for (int e = 0; e < JPL; ++e) {
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(256) void k_fold_query(FoldArgs a, int tiles_per_he
   }
 #pragma unroll
   for (int rho = 0; rho < kFoldRPW; ++rho) {
-    const FoldRow f = fold_row(a, g, tile, wave, rho);
+    const FoldRow f = fold_row<kFoldRPW>(a, g, tile, wave, rho);
     const double t = wave_sum_f64(dq2[rho]);
     // rounded up: the fp32 conversion's relative error is below 2^-24
     if (f.ok && lane == 0) a.qdelta[f.row] = (float)(sqrt(t) * (1.0 + 1e-6));
@@ -141,12 +144,12 @@ __global__ __launch_bounds__(256) void k_unfold_values(FoldArgs a, int tiles_per
   constexpr int IPL = D / 64;
   constexpr int JC = 64 * JPL;
   __shared__ __align__(16) char wt_lds[JC * D * E::kBytes];  // W_V[g][:, chunk]^T, [j][i]
-  __shared__ float o_lds[4][kFoldRPW][JC];                    // the waves' weighted base values
+  __shared__ float o_lds[4][kUnfoldRPW][JC];                    // the waves' weighted base values
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = blockIdx.x / tiles_per_head, tile = blockIdx.x % tiles_per_head;
   if (empty) {
-    for (int rho = 0; rho < kFoldRPW; ++rho) {
-      const FoldRow f = fold_row(a, g, tile, wave, rho);
+    for (int rho = 0; rho < kUnfoldRPW; ++rho) {
+      const FoldRow f = fold_row<kUnfoldRPW>(a, g, tile, wave, rho);
       if (!f.ok) continue;
 #pragma unroll
       for (int e = 0; e < IPL; ++e) a.o_kg[(int64_t)f.row * D + e * 64 + lane] = 0.f;
@@ -156,9 +159,9 @@ __global__ __launch_bounds__(256) void k_unfold_values(FoldArgs a, int tiles_per
   }
   const int DE = a.DE;
   const char* wg = (const char*)a.w_v + (int64_t)g * a.wvs[0] * E::kBytes;
-  float acc[kFoldRPW][IPL];
+  float acc[kUnfoldRPW][IPL];
 #pragma unroll
-  for (int rho = 0; rho < kFoldRPW; ++rho)
+  for (int rho = 0; rho < kUnfoldRPW; ++rho)
 #pragma unroll
     for (int e = 0; e < IPL; ++e) acc[rho][e] = 0.f;
   // 16-byte row pieces (16-byte aligned rows), scattered transposed
@@ -176,8 +179,8 @@ __global__ __launch_bounds__(256) void k_unfold_values(FoldArgs a, int tiles_per
         else ((uint32_t*)wt_lds)[j * D + i] = w4[k];
       }
     }
-    for (int rho = 0; rho < kFoldRPW; ++rho) {
-      const FoldRow f = fold_row(a, g, tile, wave, rho);
+    for (int rho = 0; rho < kUnfoldRPW; ++rho) {
+      const FoldRow f = fold_row<kUnfoldRPW>(a, g, tile, wave, rho);
       for (int j = lane; j < JC; j += 64) o_lds[wave][rho][j] = f.ok ? a.o_base[(int64_t)f.row * DE + j0 + j] : 0.f;
     }
     __syncthreads();
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(256) void k_unfold_values(FoldArgs a, int tiles_per
 #pragma unroll
       for (int e = 0; e < IPL; ++e) w[e] = lds_elem<E>(wt_lds, j * D + e * 64 + lane);
 #pragma unroll
-      for (int rho = 0; rho < kFoldRPW; ++rho) {
+      for (int rho = 0; rho < kUnfoldRPW; ++rho) {
         const float ob = o_lds[wave][rho][j];
 #pragma unroll
         for (int e = 0; e < IPL; ++e) acc[rho][e] = fmaf(w[e], ob, acc[rho][e]);
@@ -194,8 +197,8 @@ __global__ __launch_bounds__(256) void k_unfold_values(FoldArgs a, int tiles_per
     }
   }
 #pragma unroll
-  for (int rho = 0; rho < kFoldRPW; ++rho) {
-    const FoldRow f = fold_row(a, g, tile, wave, rho);
+  for (int rho = 0; rho < kUnfoldRPW; ++rho) {
+    const FoldRow f = fold_row<kUnfoldRPW>(a, g, tile, wave, rho);
     if (!f.ok) continue;
 #pragma unroll
     for (int e = 0; e < IPL; ++e) a.o_kg[(int64_t)f.row * D + e * 64 + lane] = acc[rho][e];
@@ -207,7 +210,8 @@ __global__ __launch_bounds__(256) void k_unfold_values(FoldArgs a, int tiles_per
 template <class E, int D>
 hipError_t fold_dispatch(const FoldArgs& a, hipStream_t s, bool unfold, int empty) {
   const int G = a.r.G, Hkv = a.r.Hq / G;
-  const int tiles = (a.r.B * a.r.N * G + kFoldRows - 1) / kFoldRows;
+  const int rows_per_tile = 4 * (unfold ? kUnfoldRPW : kFoldRPW);
+  const int tiles = (a.r.B * a.r.N * G + rows_per_tile - 1) / rows_per_tile;
   const dim3 grid((unsigned)(Hkv * tiles)), block(256);
   if (E::kBytes == 2 && a.DE % 128 == 0) {
     if (unfold) hipLaunchKernelGGL((k_unfold_values<E, D, 2>), grid, block, 0, s, a, tiles, empty);
