@@ -21,10 +21,12 @@ namespace {
 // with the group's G heads each (row u of the tile: token (tile*4*RPW + u) /
 // G, head g*G + u % G); a workgroup stages the head's projection in LDS once
 // for its rows (4 waves x RPW rows), instead of every row reading the 32-64 KB
-// matrix through L2.  The fold takes 4 rows a wave (fp64 sums: more rows did
-// not help), the unfold 8 (its fp32 sums reuse each staged weight for more
-// rows: 82 -> 72 us at D_E = 384, 607 -> 481 us at 3072; 16 rows were slower).
-constexpr int kFoldRPW = 4, kUnfoldRPW = 8;
+// matrix through L2.  Both take 8 rows a wave, each staged weight converted
+// once for 8 rows (the fold keeps its rows' queries in LDS as fp64, so its
+// inner loop is fp64 FMAs and weight conversions only: 90 -> 79 us at D_E =
+// 384, 587 -> 514 us at 3072; the unfold 82 -> 72 and 607 -> 481 us; 16 rows
+// a wave were slower).
+constexpr int kFoldRPW = 8, kUnfoldRPW = 8;
 
 struct FoldRow {
   int row, b, n, h;
@@ -62,7 +64,7 @@ template <class E, int D, int JPL>
 __global__ __launch_bounds__(256) void k_fold_query(FoldArgs a, int tiles_per_head) {
   constexpr int JC = 64 * JPL;
   __shared__ __align__(16) char w_lds[D * JC * E::kBytes];   // W_K[g][:, chunk] as stored, [i][j]
-  __shared__ float q_lds[4][kFoldRPW][D];                     // the waves' KG queries (exact)
+  __shared__ double q_lds[4][kFoldRPW][D];                    // the waves' KG queries (exact)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = blockIdx.x / tiles_per_head, tile = blockIdx.x % tiles_per_head;
   const int DE = a.DE;
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(256) void k_fold_query(FoldArgs a, int tiles_per_he
   for (int rho = 0; rho < kFoldRPW; ++rho) {
     const FoldRow f = fold_row<kFoldRPW>(a, g, tile, wave, rho);
     const int64_t qb = q_off(a.r.qks, f.b, f.n, f.h);
-    for (int t = lane; t < D; t += 64) q_lds[wave][rho][t] = f.ok ? load_f32<E>(a.r.q_kg, qb + t) : 0.f;
+    for (int t = lane; t < D; t += 64) q_lds[wave][rho][t] = f.ok ? (double)load_f32<E>(a.r.q_kg, qb + t) : 0.0;
   }
   double dq2[kFoldRPW];                                       // |qf - qx|^2, this lane's columns
 #pragma unroll
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(256) void k_fold_query(FoldArgs a, int tiles_per_he
       for (int e = 0; e < JPL; ++e) w[e] = (double)lds_elem<E>(w_lds, i * JC + e * 64 + lane);
 #pragma unroll
       for (int rho = 0; rho < kFoldRPW; ++rho) {
-        const double qi = (double)q_lds[wave][rho][i];
+        const double qi = q_lds[wave][rho][i];
 #pragma unroll
         for (int e = 0; e < JPL; ++e) acc[rho][e] = fma(qi, w[e], acc[rho][e]);
       }
