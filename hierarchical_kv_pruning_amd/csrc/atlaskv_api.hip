@@ -192,7 +192,7 @@ struct Plan {
   size_t off_mid_base, off_bcnt, off_bslot, off_bhead, off_bnext, off_blist, off_bcount, off_bovf, off_junk;
   size_t off_rcnt, off_rtot, off_rtoff, off_rtkey, off_rnt, off_rmem;
   int64_t root_tiles_max;
-  int32_t desc_per_sub, bucket_q;
+  int32_t desc_per_sub, bucket_q, bslots;
   // descent parts: KV heads [part_g[i], part_g[i+1]) with their own tile,
   // descriptor, count and overflow-key regions (totals above: one part over
   // all heads uses the regions concatenated)
@@ -391,6 +391,7 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   const size_t nroot = (size_t)t.Hkv * (size_t)t.count[0];
   // the descent runs in concurrent parts (ranges of KV heads) when there
   // are enough rows for each part's kernels to fill the GPU
+  p.bslots = mode == kModeFoldedDescent ? kBucketSlotsFolded : kBucketSlots;
   p.nparts = descent_parts(t.Hkv, (int64_t)R);
   int64_t tiles_all = 0, ovf_all = 0, desc_all = 0;
   for (int i = 0; i < p.nparts; ++i) {
@@ -400,7 +401,7 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
     p.part_tiles[i] = rows * p.K[0] / kRootTile + heads * t.count[0] + 1;
     p.part_desc[i] = (int32_t)(((int64_t)row_chunks((int)rows, p.K[1]) + kDescSub - 1) / kDescSub *
                                row_chunk_entries(p.K[1]));
-    p.part_ovf[i] = rows * p.K[1] / (kBucketSlots + 1) + 1;
+    p.part_ovf[i] = rows * p.K[1] / (p.bslots + 1) + 1;
     tiles_all += p.part_tiles[i];
     desc_all += p.part_desc[i];
     ovf_all += p.part_ovf[i];
@@ -415,7 +416,7 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   p.bucket_q = (int32_t)(((size_t)t.Hkv * (size_t)t.count[1] + 63) / 64);
   const size_t nbix = (size_t)p.bucket_q * 64;
   p.off_bcnt = o;      o = align256(o + nbix * 4);
-  p.off_bslot = o;     o = align256(o + nbix * 8 * kBucketSlots);
+  p.off_bslot = o;     o = align256(o + nbix * 8 * (size_t)p.bslots);
   p.off_bhead = o;     o = align256(o + nbix * 4);
   p.off_bnext = o;     o = align256(o + R * (size_t)p.K[1] * 4);
   // link chunk c appends to sub-list c mod kDescSub (of its part)
@@ -765,6 +766,7 @@ hipError_t launch_descent(const Plan& p, const RowsDev& rows, atlaskv_tree_view_
   a.bucket_count = (int32_t*)(ws + p.off_bcount);
   a.desc_per_sub = p.desc_per_sub;
   a.bucket_q = p.bucket_q;
+  a.bslots = p.bslots;
   a.bucket_ovf = (int32_t*)(ws + p.off_bovf);
   a.junk = (float*)(ws + p.off_junk);
   a.o_kg = o_kg;

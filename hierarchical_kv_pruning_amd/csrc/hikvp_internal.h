@@ -9,7 +9,12 @@ namespace hikvp {
 constexpr int kMaxK = 256;        // largest Top-K per level
 constexpr int kMaxD = 128;        // largest head dim of the per-head trees and the sequence half
 constexpr int kMaxWideD = 4096;   // largest width of a base-embedding tree (a multiple of 128)
-constexpr int kBucketSlots = 32;  // members of a (head, mid) bucket stored without a list walk
+// Members of a (head, mid) bucket stored in fixed slots (no list walk): 32
+// for per-head trees, 64 for a folded call's base tree, where every query
+// head selects from the one tree and a bucket holds ~13 rows with a long
+// tail (64 slots: folded D_E = 384 overflow 42 -> 6 us, step 0.917 -> 0.888
+// ms; the per-row paths lost ~1 % with 64, reading twice the slot bytes).
+constexpr int kBucketSlots = 32, kBucketSlotsFolded = 64;
 constexpr int kJunkSlots = 1024;  // per-wave sinks for masked-off score stores
 constexpr int kRootTile = 64;     // member rows per mid-GEMM work item (four waves of 16 rows)
 constexpr int kRootSub = 16;      // counters per (head, root) group, picked by token
@@ -113,18 +118,19 @@ struct StepArgs {
   // (head, mid) bucket arrays are indexed by bucket_index(key) (below), which
   // spreads neighbouring mids (siblings, selected together) over cache lines
   int32_t* bucket_cnt;        // [64 * bucket_q] rows that selected the (head, mid)
-  int2* bucket_slot;          // [64 * bucket_q * kBucketSlots] first members: (row, first leaf slot)
+  int2* bucket_slot;          // [64 * bucket_q * bslots] first members: (row, first leaf slot)
   int32_t* bucket_head;       // [64 * bucket_q] overflow members: list head, -1 none
   int32_t* bucket_next;       // [R * K[1]] next overflow entry of the same (head, mid)
   int4* bucket_desc;          // [kDescSub, desc_per_sub] distinct (head, mid): key g*M_I+mid, fanout,
                               // first leaf element (lo, hi); sub-list s holds buckets first
                               // registered by a link chunk c with c mod kDescSub = s
   int32_t* bucket_count;      // [kDescSub + 1] descriptors per sub-list; [kDescSub]: keys with more
-                              // than kBucketSlots rows
+                              // than bslots rows
   int32_t desc_per_sub;       // ceil(row_chunks(rows, K[1]) / kDescSub) * row_chunk_entries(K[1])
   int32_t bucket_q;           // ceil(Hkv * M_I / 64)
+  int32_t bslots;             // fixed member slots a bucket (kBucketSlots or kBucketSlotsFolded)
   float* junk;                // [kJunkSlots * 16] write-only sinks for the mid GEMM's idle score lanes
-  int32_t* bucket_ovf;        // [rows * K[1] / (kBucketSlots + 1) + 1] keys (g*M_I + mid) with overflow members
+  int32_t* bucket_ovf;        // [rows * K[1] / (bslots + 1) + 1] keys (g*M_I + mid) with overflow members
   float* o_kg;                // [R, d] softmax-weighted leaf values (fp32)
   float* lse_kg;              // [R] log-sum-exp of the selected leaf logits
   int exact_logits;           // non-zero (folded calls on fp32 trees): the KG softmax takes the selected
@@ -219,8 +225,8 @@ hipError_t launch_root_groups(const StepArgs& a, hipStream_t s);  // rows by sel
 hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s);
 hipError_t launch_mid_select(const StepArgs& a, hipStream_t s);
 hipError_t launch_leaf_link(const StepArgs& a, hipStream_t s);    // rows grouped by selected (head, mid)
-hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s);   // buckets' first kBucketSlots members
-hipError_t launch_leaf_overflow(const StepArgs& a, hipStream_t s);  // members past kBucketSlots
+hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s);   // buckets' first bslots members
+hipError_t launch_leaf_overflow(const StepArgs& a, hipStream_t s);  // members past bslots
 hipError_t launch_leaf_select(const StepArgs& a, hipStream_t s);
 hipError_t launch_seq_attend(const SeqArgs& a, hipStream_t s);   // + λ merge when keys are not split
 hipError_t launch_seq_combine(const SeqArgs& a, hipStream_t s);  // split partials: LSE combine + λ merge

@@ -955,7 +955,7 @@ __global__ __launch_bounds__(256) void k_mid_select(StepArgs a, size_t wave_byte
 // leaf scoring, deduplicated: every distinct (KV head, mid) selected by any
 // row is one bucket.  The link kernel writes one 16-byte descriptor per bucket
 // (key, fanout, element offset of the span) and stores the first
-// kBucketSlots member rows as (row, first leaf slot) pairs; later members go
+// bslots member rows as (row, first leaf slot) pairs; later members go
 // to a linked list scored by k_leaf_score_overflow.  One wave per bucket
 // streams the mid's leaf span (contiguous in the head-major layout) once and
 // scores it for every member row, prefetching its next bucket's descriptor.
@@ -964,7 +964,7 @@ __global__ __launch_bounds__(256) void k_mid_select(StepArgs a, size_t wave_byte
 // ---------------------------------------------------------------------------
 // Register selection e = (row, mid) in its (KV head, mid) bucket, given its
 // rank from the bucket's counter (-1: nothing to register): the first
-// kBucketSlots members in fixed slots (row, first leaf slot), later ones in
+// bslots members in fixed slots (row, first leaf slot), later ones in
 // the bucket's list; a new bucket appends its 16-byte descriptor (bucket
 // index, fanout, first leaf element) to descriptor sub-list `sub`, one atomic
 // per wave.  All lanes of a wave call it.
@@ -985,11 +985,11 @@ __device__ inline void register_in_bucket(const StepArgs& a, int64_t e, int row,
   }
   if (rank < 0) return;
   const int64_t bix = bucket_index(a, key);
-  if (rank < kBucketSlots) {
-    a.bucket_slot[bix * kBucketSlots + rank] = make_int2(row, slot_base);
+  if (rank < a.bslots) {
+    a.bucket_slot[bix * a.bslots + rank] = make_int2(row, slot_base);
   } else {
     a.bucket_next[e] = atomicExch(&a.bucket_head[bix], (int)e);
-    if (rank == kBucketSlots) a.bucket_ovf[atomicAdd(&a.bucket_count[kDescSub], 1)] = (int)key;
+    if (rank == a.bslots) a.bucket_ovf[atomicAdd(&a.bucket_count[kDescSub], 1)] = (int)key;
   }
 }
 
@@ -1241,10 +1241,10 @@ __device__ inline void score_members(const StepArgs& a, const char* kp, int64_t 
   else score_member_group<E, D, LO>(a, kp, rsb, F, mem, g0, gcnt, lane);
 }
 
-// One wave per bucket: its first kBucketSlots members, 8 at a time (a bucket
-// with more than 8 members makes further passes over its span, mostly L2
-// hits; wide rows take all of them in one pass); members past kBucketSlots
-// are left to k_leaf_score_overflow.
+// One wave per bucket: its first bslots members (32, or 64 in a folded
+// call), 8 at a time (a bucket with more than 8 members makes further passes
+// over its span, mostly L2 hits; wide rows take 24 a pass); members past
+// bslots are left to k_leaf_score_overflow.
 template <class E, int D, bool LO>
 __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
@@ -1270,8 +1270,8 @@ __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
     const int64_t first = (int64_t)(uint32_t)cur.z | ((int64_t)cur.w << 32);
     const char* kp = (const char*)kbase + first * E::kBytes + split_off(lane, 0);  // + key * rsb
     int cnt = a.bucket_cnt[key];
-    cnt = cnt < kBucketSlots ? cnt : kBucketSlots;
-    const int2 mem = lane < kBucketSlots ? a.bucket_slot[(int64_t)key * kBucketSlots + lane] : make_int2(-1, 0);
+    cnt = cnt < a.bslots ? cnt : a.bslots;
+    const int2 mem = lane < a.bslots ? a.bucket_slot[(int64_t)key * a.bslots + lane] : make_int2(-1, 0);
     if constexpr (D == 0) {
       // three groups (24 members) a pass, four keys a lane a round: at one
       // group a pass the span is read once a group, and fewer keys a round
@@ -1287,7 +1287,7 @@ __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
   }
 }
 
-// Members of buckets with more than kBucketSlots rows: one wave per listed
+// Members of buckets with more than bslots rows: one wave per listed
 // bucket walks its overflow list and scores the members 8 at a time with the
 // same group arithmetic as k_leaf_score.
 template <class E, int D, bool LO>
@@ -1623,9 +1623,9 @@ hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s) {
 
 hipError_t launch_leaf_overflow(const StepArgs& a, hipStream_t s) {
   if (a.blk1 <= a.blk0 || a.K[1] <= 0) return hipSuccess;
-  // at most rows * K_I / (kBucketSlots + 1) buckets overflow
+  // at most rows * K_I / (bslots + 1) buckets overflow
   const int64_t nb_max = (int64_t)(a.blk1 - a.blk0) * a.K[1];
-  int64_t blocks = (nb_max / (kBucketSlots + 1) + 4) / 4;
+  int64_t blocks = (nb_max / (a.bslots + 1) + 4) / 4;
   if (blocks > 1024) blocks = 1024;
   HIKVP_DISPATCH_LO(a, k_leaf_score_overflow, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
