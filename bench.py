@@ -115,7 +115,6 @@ def algorithmic_bytes(case, sel, share=0):
             "mid_bucket_gemm": mids_b,
             "mid_topk": 0, "leaf_bucket_link": 0,
             "leaf_score_stream": leafk_b,
-            "leaf_score_overflow": 0,
             "leaf_topk_kg_attention": leafv_b,
             "shared_kg_attention": leafv_b,   # the selected leaves' keys (values counted above)
             "seq_attention": seq_b,
@@ -130,7 +129,6 @@ def algorithmic_bytes(case, sel, share=0):
         "mid_topk": 0,
         "leaf_bucket_link": 0,
         "leaf_score_stream": leafk_b,
-        "leaf_score_overflow": 0,
         "leaf_topk_kg_attention": leafv_b,
         "seq_attention": seq_b,
         "seq_split_combine": out_b,
@@ -173,7 +171,7 @@ PHASE_OF = {
     "k_root_mfma": "root_score_topk", "k_root": "root_score_topk",
     "k_root_scan": "root_score_topk (grouping)", "k_root_fill": "root_score_topk (grouping)",
     "k_mid_gemm": "mid_bucket_gemm", "k_mid_select": "mid_topk", "k_bucket_link": "leaf_bucket_link",
-    "k_leaf_score": "leaf_score_stream", "k_leaf_score_overflow": "leaf_score_overflow",
+    "k_leaf_score": "leaf_score_stream",
     "k_leaf_select": "leaf_topk_kg_attention", "k_seq_mfma": "seq_attention",
     "k_seq_decode_mfma": "seq_attention", "k_seq_decode": "seq_attention", "k_seq_flash": "seq_attention",
     "k_seq_combine": "seq_split_combine",
@@ -182,7 +180,7 @@ PHASE_OF = {
 HBM_SUMMARY_KERNELS = {
     "root_score_topk": ("k_root",), "mid_bucket_gemm": ("k_mid_gemm",), "mid_topk": ("k_mid_select",),
     "leaf_bucket_link": ("k_bucket_link",), "leaf_score_stream": ("k_leaf_score",),
-    "leaf_score_overflow": ("k_leaf_score_overflow",), "leaf_topk_kg_attention": ("k_leaf_select",),
+    "leaf_topk_kg_attention": ("k_leaf_select",),
     "seq_attention": ("k_seq_mfma", "k_seq_decode_mfma", "k_seq_decode", "k_seq_flash"),
 }
 BUSY_KERNELS = ("k_root_mfma", "k_root", "k_mid_gemm", "k_mid_select", "k_bucket_link", "k_leaf_score",

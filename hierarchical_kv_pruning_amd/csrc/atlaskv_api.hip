@@ -624,16 +624,19 @@ struct PhaseMarks {
 // view's aux stream and writes (o, m, l) partials; the call's stream waits for
 // it before k_seq_combine merges both halves.  Decode blocks (under 16
 // tokens: one light HBM-bound wave per SIMD) fork before the KG kernels.
-// Prefill blocks fork just before the last descent part's leaf stream: the
-// matrix-core prefill kernels hold most of a SIMD's registers and LDS, which
-// slowed the latency-bound descent kernels beside them, while the leaf
-// stream, bound by HBM, leaves the SIMDs room.  With phase timing both
+// Prefill blocks fork from the last descent part: with one part just before
+// its leaf stream (the matrix-core prefill kernels hold most of a SIMD's
+// registers and LDS, which slowed the one chain of latency-bound descent
+// kernels beside them), with several parts after its root phase (the other
+// parts' kernels fill the gaps, and the half is done before the leaf streams
+// take every wave slot: 0.531 -> 0.519 ms at 16384 rows over 8 KV heads,
+// where before the leaf stream it finished only with the last leaf select).  With phase timing both
 // phases (attention, split combine) run after the KG half, through the same
 // partials and merge.
 struct SeqHalf {
   SeqArgs sa;
   bool overlap;                // on the aux stream, joined before k_seq_combine
-  bool at_leaf;                // forked before the last part's leaf stream (else before the KG half)
+  bool at_leaf;                // forked from the last descent part (else before the KG half)
   mutable bool forked;         // the fork was enqueued (else the half runs after the KG half)
 };
 
@@ -705,31 +708,37 @@ hipError_t seq_finish(const SeqHalf& h, atlaskv_tree_view_s* v, hipStream_t s, P
 }
 
 // A prefill block's sequence half, forked from a descent part's stream just
-// before its leaf stream (NULL: none to fork there).
+// before its leaf stream, or after its root phase (early) (h NULL: none to
+// fork there).
 struct LateFork {
   const SeqHalf* h;
   atlaskv_tree_view_s* v;
+  bool early;
 };
 
 // One part of the descent (KV heads [a.g0, a.g1)) on stream s; the caller
 // holds the view's mutex when `fork` is given.
 hipError_t descent_part(const StepArgs& a, hipStream_t s, PhaseMarks& pm, const LateFork* fork = nullptr) {
   auto mark = [&](hipError_t prev) { return pm.mark(prev); };
+  auto fork_at = [&](bool early, hipError_t prev) {
+    if (prev != hipSuccess || !fork || !fork->h || fork->early != early) return prev;
+    return seq_fork_locked(*fork->h, fork->v, s);
+  };
   hipError_t e = launch_root(a, s);
   if (e == hipSuccess) e = mark(launch_root_groups(a, s));
+  e = fork_at(true, e);
   if (e == hipSuccess) e = mark(launch_mid_gemm(a, s));
   if (e == hipSuccess) e = mark(launch_mid_select(a, s));
   if (e == hipSuccess) e = mark(launch_leaf_link(a, s));
-  if (e == hipSuccess && fork && fork->h) e = seq_fork_locked(*fork->h, fork->v, s);
+  e = fork_at(false, e);
   if (e == hipSuccess) e = mark(launch_leaf_score(a, s));
-  if (e == hipSuccess) e = mark(launch_leaf_overflow(a, s));
   if (e == hipSuccess) e = mark(launch_leaf_select(a, s));
   return e;
 }
 
 // The pruned descent for `rows` (速读 › 怎么做的: roots -> Top-K -> their
 // children -> Top-K -> leaves -> Top-K, then the KG softmax over the selected
-// leaves into o_kg / lse_kg): seven timing phases.  Every index structure of
+// leaves into o_kg / lse_kg): six timing phases.  Every index structure of
 // the descent is keyed by KV head, so the heads split into parts that share
 // no state; part 0 runs on s and parts 1.. on the view's part streams
 // (forked from s, joined back to it), so that one part's kernel tails and
@@ -738,8 +747,9 @@ hipError_t descent_part(const StepArgs& a, hipStream_t s, PhaseMarks& pm, const 
 hipError_t launch_descent(const Plan& p, const RowsDev& rows, atlaskv_tree_view_s* v, char* ws,
                           int32_t* const sel[3], float* o_kg, float* lse_kg, hipStream_t s, PhaseMarks& pm,
                           const SeqHalf* seq = nullptr) {
-  // a prefill sequence half to fork before the last part's leaf stream
-  const LateFork late{(seq && seq->overlap && seq->at_leaf) ? seq : nullptr, v};
+  // a prefill sequence half to fork from the last part (after its root phase
+  // when there are several parts, else before its leaf stream)
+  LateFork late{(seq && seq->overlap && seq->at_leaf) ? seq : nullptr, v, false};
   StepArgs a;
   memset(&a, 0, sizeof a);
   a.t = v->dev;
@@ -811,6 +821,7 @@ hipError_t launch_descent(const Plan& p, const RowsDev& rows, atlaskv_tree_view_
     desc += p.part_desc[i];
     ovf += p.part_ovf[i];
   }
+  late.early = true;
   std::lock_guard<std::mutex> lock(v->mu);  // one call's records / waits / launches stay together
   hipError_t e = hipEventRecord(v->part_fork, s);
   for (int i = 1; i < p.nparts && e == hipSuccess; ++i) {
@@ -862,8 +873,8 @@ const char* atlaskv_last_error(void) { return g_err.c_str(); }
 const char* atlaskv_version(void) { return "atlaskv-mi355x 0.1 (gfx950)"; }
 
 static const char* const kPhaseNames[] = {"root_score_topk", "mid_bucket_gemm", "mid_topk",
-                                          "leaf_bucket_link", "leaf_score_stream", "leaf_score_overflow",
-                                          "leaf_topk_kg_attention", "seq_attention", "seq_split_combine"};
+                                          "leaf_bucket_link", "leaf_score_stream", "leaf_topk_kg_attention",
+                                          "seq_attention", "seq_split_combine"};
 static const int kPhases = (int)(sizeof kPhaseNames / sizeof kPhaseNames[0]);
 
 int32_t atlaskv_phase_count(void) { return kPhases; }
@@ -1089,7 +1100,7 @@ size_t atlaskv_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 static const char* const kSharedPhaseNames[] = {
     "group_query", "root_score_topk", "mid_bucket_gemm", "mid_topk", "leaf_bucket_link",
-    "leaf_score_stream", "leaf_score_overflow", "leaf_topk_kg_attention", "shared_kg_attention",
+    "leaf_score_stream", "leaf_topk_kg_attention", "shared_kg_attention",
     "seq_attention", "seq_split_combine"};
 static const int kSharedPhases = (int)(sizeof kSharedPhaseNames / sizeof kSharedPhaseNames[0]);
 
@@ -1192,7 +1203,7 @@ atlaskv_status atlaskv_shared_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vi
 
 static const char* const kFoldedPhaseNames[] = {
     "fold_query", "root_score_topk", "mid_bucket_gemm", "mid_topk", "leaf_bucket_link",
-    "leaf_score_stream", "leaf_score_overflow", "leaf_topk_kg_attention", "unfold_values",
+    "leaf_score_stream", "leaf_topk_kg_attention", "unfold_values",
     "seq_attention", "seq_split_combine"};
 static const int kFoldedPhases = (int)(sizeof kFoldedPhaseNames / sizeof kFoldedPhaseNames[0]);
 
@@ -1280,8 +1291,9 @@ atlaskv_status atlaskv_folded_attend_ex(const atlaskv_tensor* q, atlaskv_tree_vi
   hipError_t e = pm.mark(hipSuccess);
   if (e == hipSuccess) e = seq_start(sh, v, s);
   if (p.fold_kg_empty) {
-    // no descent: seven empty phases keep the event numbering
-    for (int i = 0; i < 8 && e == hipSuccess; ++i) e = pm.mark(hipSuccess);
+    // no descent: seven empty phases (the fold and the six descent phases)
+    // keep the event numbering
+    for (int i = 0; i < 7 && e == hipSuccess; ++i) e = pm.mark(hipSuccess);
   } else if (e == hipSuccess) {
     e = pm.mark(launch_fold_query(fa, s));
     atlaskv_tensor qd = group_rows_desc(p.B, p.N, p.Hq, v->dev.d, v->dev.dtype, fa.qf);

@@ -225,8 +225,7 @@ hipError_t launch_root_groups(const StepArgs& a, hipStream_t s);  // rows by sel
 hipError_t launch_mid_gemm(const StepArgs& a, hipStream_t s);
 hipError_t launch_mid_select(const StepArgs& a, hipStream_t s);
 hipError_t launch_leaf_link(const StepArgs& a, hipStream_t s);    // rows grouped by selected (head, mid)
-hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s);   // buckets' first bslots members
-hipError_t launch_leaf_overflow(const StepArgs& a, hipStream_t s);  // members past bslots
+hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s);   // every member of every bucket
 hipError_t launch_leaf_select(const StepArgs& a, hipStream_t s);
 hipError_t launch_seq_attend(const SeqArgs& a, hipStream_t s);   // + λ merge when keys are not split
 hipError_t launch_seq_combine(const SeqArgs& a, hipStream_t s);  // split partials: LSE combine + λ merge

@@ -30,7 +30,8 @@
 //               candidate list.
 //   k_leaf_score   one wave per bucket: streams the mid's leaf span once (it is
 //               contiguous in the head-major layout) and writes the scores of
-//               every member row into that row's candidate slots.
+//               every member row into that row's candidate slots; then the
+//               members past a bucket's fixed slots, from its list.
 //   k_leaf_select  one wave (or workgroup) per row: Top-K_L, then the KG softmax over the
 //               selected leaves and the weighted sum of their values.
 #include <hip/hip_runtime.h>
@@ -956,7 +957,7 @@ __global__ __launch_bounds__(256) void k_mid_select(StepArgs a, size_t wave_byte
 // row is one bucket.  The link kernel writes one 16-byte descriptor per bucket
 // (key, fanout, element offset of the span) and stores the first
 // bslots member rows as (row, first leaf slot) pairs; later members go
-// to a linked list scored by k_leaf_score_overflow.  One wave per bucket
+// to a linked list, scored at the end of the same kernel.  One wave per bucket
 // streams the mid's leaf span (contiguous in the head-major layout) once and
 // scores it for every member row, prefetching its next bucket's descriptor.
 // Each member's dot products are computed independently, so results do not
@@ -1241,10 +1242,41 @@ __device__ inline void score_members(const StepArgs& a, const char* kp, int64_t 
   else score_member_group<E, D, LO>(a, kp, rsb, F, mem, g0, gcnt, lane);
 }
 
+// Members of buckets with more than bslots rows: wave `wave0` of `nwaves`
+// takes every nwaves-th listed bucket, walks its list and scores the members
+// 8 at a time with the same group arithmetic as the fixed slots.
+template <class E, int D, bool LO>
+__device__ inline void score_overflow(const StepArgs& a, int wave0, int nwaves, int lane) {
+  const int nov = a.bucket_count[kDescSub];
+  const int K1 = a.K[1];
+  const int MI = (int)a.t.count[1];
+  const char* kbase = (const char*)a.t.key[2];
+  const int64_t rsb = a.t.rs[2] * E::kBytes;
+  for (int v = wave0; v < nov; v += nwaves) {
+    const int key = a.bucket_ovf[v];
+    const int g = key / MI, mid = key % MI;
+    const int64_t bix = bucket_index(a, key);
+    const int64_t f0 = a.t.off[1][mid];
+    const int F = (int)(a.t.off[1][mid + 1] - f0);
+    const char* kp = kbase + ((int64_t)g * a.t.hs[2] + f0 * a.t.rs[2]) * E::kBytes + split_off(lane, 0);
+    int e = a.bucket_head[bix];
+    while (e != -1) {  // wave-uniform walk: lane i takes the group's i-th entry
+      int mine = -1, gcnt = 0;
+      for (; gcnt < 8 && e != -1; ++gcnt) {
+        if (lane == gcnt) mine = e;
+        e = a.bucket_next[e];
+      }
+      const int2 gm = (lane < gcnt) ? make_int2(mine / K1, a.mid_base[mine]) : make_int2(-1, 0);
+      score_members<E, D, LO>(a, kp, rsb, F, gm, 0, gcnt, lane);
+    }
+  }
+}
+
 // One wave per bucket: its first bslots members (32, or 64 in a folded
 // call), 8 at a time (a bucket with more than 8 members makes further passes
-// over its span, mostly L2 hits; wide rows take 24 a pass); members past
-// bslots are left to k_leaf_score_overflow.
+// over its span, mostly L2 hits; wide rows take 24 a pass).  Then the
+// members past bslots (score_overflow; the lists are complete once the link
+// kernel has run): a separate launch for them cost ~5 us a step.
 template <class E, int D, bool LO>
 __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
@@ -1285,37 +1317,7 @@ __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
     cur = nxt;
     v = vn;
   }
-}
-
-// Members of buckets with more than bslots rows: one wave per listed
-// bucket walks its overflow list and scores the members 8 at a time with the
-// same group arithmetic as k_leaf_score.
-template <class E, int D, bool LO>
-__global__ __launch_bounds__(256) void k_leaf_score_overflow(StepArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
-  const int nov = a.bucket_count[kDescSub];
-  const int K1 = a.K[1];
-  const int MI = (int)a.t.count[1];
-  const char* kbase = (const char*)a.t.key[2];
-  const int64_t rsb = a.t.rs[2] * E::kBytes;
-  for (int v = blockIdx.x * nwave + wave; v < nov; v += gridDim.x * nwave) {
-    const int key = a.bucket_ovf[v];
-    const int g = key / MI, mid = key % MI;
-    const int64_t bix = bucket_index(a, key);
-    const int64_t f0 = a.t.off[1][mid];
-    const int F = (int)(a.t.off[1][mid + 1] - f0);
-    const char* kp = kbase + ((int64_t)g * a.t.hs[2] + f0 * a.t.rs[2]) * E::kBytes + split_off(lane, 0);
-    int e = a.bucket_head[bix];
-    while (e != -1) {  // wave-uniform walk: lane i takes the group's i-th entry
-      int mine = -1, gcnt = 0;
-      for (; gcnt < 8 && e != -1; ++gcnt) {
-        if (lane == gcnt) mine = e;
-        e = a.bucket_next[e];
-      }
-      const int2 gm = (lane < gcnt) ? make_int2(mine / K1, a.mid_base[mine]) : make_int2(-1, 0);
-      score_members<E, D, LO>(a, kp, rsb, F, gm, 0, gcnt, lane);
-    }
-  }
+  score_overflow<E, D, LO>(a, blockIdx.x * nwave + wave, stride, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1618,16 +1620,6 @@ hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s) {
   int64_t blocks = (nb_max + 3) / 4;
   if (blocks > 2048) blocks = 2048;
   HIKVP_DISPATCH_LO(a, k_leaf_score, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_leaf_overflow(const StepArgs& a, hipStream_t s) {
-  if (a.blk1 <= a.blk0 || a.K[1] <= 0) return hipSuccess;
-  // at most rows * K_I / (bslots + 1) buckets overflow
-  const int64_t nb_max = (int64_t)(a.blk1 - a.blk0) * a.K[1];
-  int64_t blocks = (nb_max / (a.bslots + 1) + 4) / 4;
-  if (blocks > 1024) blocks = 1024;
-  HIKVP_DISPATCH_LO(a, k_leaf_score_overflow, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -231,7 +231,7 @@ def test_phase_names_in_launch_order(lib):
     the merge when keys are not split), the combine of key splits."""
     assert atlaskv.phase_names() == [
         "root_score_topk", "mid_bucket_gemm", "mid_topk", "leaf_bucket_link", "leaf_score_stream",
-        "leaf_score_overflow", "leaf_topk_kg_attention", "seq_attention", "seq_split_combine"]
+        "leaf_topk_kg_attention", "seq_attention", "seq_split_combine"]
     assert lib.atlaskv_phase_name(-1) is None
     assert lib.atlaskv_phase_name(lib.atlaskv_phase_count()) is None
 
@@ -283,7 +283,7 @@ def test_flat_workspace_grows_with_leaves(lib):
 def test_shared_phase_names_and_checks(lib):
     assert atlaskv.shared_phase_names() == [
         "group_query", "root_score_topk", "mid_bucket_gemm", "mid_topk", "leaf_bucket_link",
-        "leaf_score_stream", "leaf_score_overflow", "leaf_topk_kg_attention", "shared_kg_attention",
+        "leaf_score_stream", "leaf_topk_kg_attention", "shared_kg_attention",
         "seq_attention", "seq_split_combine"]
     v = _view()
     q = torch.zeros(1, 4, 4, 128, dtype=torch.bfloat16)
@@ -306,7 +306,7 @@ def test_shared_phase_names_and_checks(lib):
 def test_folded_phase_names_and_checks(lib):
     assert atlaskv.folded_phase_names() == [
         "fold_query", "root_score_topk", "mid_bucket_gemm", "mid_topk", "leaf_bucket_link",
-        "leaf_score_stream", "leaf_score_overflow", "leaf_topk_kg_attention", "unfold_values",
+        "leaf_score_stream", "leaf_topk_kg_attention", "unfold_values",
         "seq_attention", "seq_split_combine"]
     base = _view(Hkv=1, d=128)                      # one-head base tree, D_E = 128
     q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)          # layer: Hq 8, d 64
