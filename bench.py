@@ -175,6 +175,7 @@ PHASE_OF = {
     "k_leaf_select": "leaf_topk_kg_attention", "k_seq_mfma": "seq_attention",
     "k_seq_decode_mfma": "seq_attention", "k_seq_decode": "seq_attention", "k_seq_flash": "seq_attention",
     "k_seq_combine": "seq_split_combine",
+    "k_flat_mfma": "flat_kg_partial", "k_flat_valu": "flat_kg_partial", "k_flat_combine": "flat_kg_combine",
 }
 # the kernel each phase's HBM summary counts (a phase's main kernel)
 HBM_SUMMARY_KERNELS = {
@@ -225,9 +226,19 @@ def _counter_dispatches(directory):
     return {k: [(d, v[0], v[1]) for d, v in sorted(m.items())] for k, m in per.items()}
 
 
+def _variant(args):
+    """(file-name suffix, bench flags, description) of a summary's path variant."""
+    if getattr(args, "path", "hikvp") == "flat":
+        return "_flat", " --path flat", ", unpruned equivalent attention (every leaf)"
+    if getattr(args, "tree_placement", "hbm") == "host-leaves":
+        return ("_host_leaves", " --tree-placement host-leaves",
+                " with leaf keys and values in pinned host memory")
+    return "", "", ""
+
+
 def _bench_cmd(args, extra):
-    return (f"python3 bench.py --workload {args.workload} --steps {args.steps} --warmup {args.warmup} "
-            f"--phase-steps {args.phase_steps} --no-cpu-baseline{extra}")
+    return (f"python3 bench.py --workload {args.workload}{_variant(args)[1]} --steps {args.steps} "
+            f"--warmup {args.warmup} --phase-steps {args.phase_steps} --no-cpu-baseline{extra}")
 
 
 def summarize(args):
@@ -309,17 +320,18 @@ def summarize(args):
             if k and k != COPY_KERNEL:
                 per.setdefault((k, r["Kernel_Name"]), []).append(
                     (int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
-        path = os.path.join(PROFILES, f"kernel_stats_{w}.txt")
+        sfx, vflags, vdesc = _variant(args)
+        path = os.path.join(PROFILES, f"kernel_stats_{w}{sfx}.txt")
         rows = []
         for (k, full), v in per.items():
             v.sort()
             us = [x[1] for x in v]
             rows.append((float(np.mean(us[-nph:])), full, k, us))
         with open(path, "w") as f:
-            f.write(f"# rocprofv3 kernel statistics, workload {w} (MI355X, one GPU)\n")
+            f.write(f"# rocprofv3 kernel statistics, workload {w}{vdesc} (MI355X, one GPU)\n")
             f.write(f"# command (from the repository root): rocprofv3 --kernel-trace --stats --output-format csv "
                     f"-d {args.trace_dir} -o run -- {_bench_cmd(args, '')}\n")
-            f.write(f"# summary: python3 bench.py --summarize stats --workload {w} --steps {args.steps} "
+            f.write(f"# summary: python3 bench.py --summarize stats --workload {w}{vflags} --steps {args.steps} "
                     f"--warmup {args.warmup} --phase-steps {nph} --trace-dir {args.trace_dir}\n")
             f.write(f"# kernel sources sha256[:16]: {hsh}\n")
             f.write(f"# 'timed us': mean of the kernel's last {nph} dispatches, the bench's phase-timed steps (one\n")
