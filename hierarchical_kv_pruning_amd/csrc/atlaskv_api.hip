@@ -208,6 +208,8 @@ struct Plan {
   int fold_Hkv, fold_d, fold_kg_empty;               // folded projections only
   size_t off_qf, off_qx, off_qlo, off_qdelta;
   int exact_logits;                                  // the KG softmax takes its logits from rows.q_exact
+  int leaf_nst, leaf_fpad, leaf_spt;                 // leaf candidates filtered in the leaf stream
+  size_t off_lcnt;
 };
 
 // Candidate capacity per row at the mid level (children of K_R distinct
@@ -385,7 +387,29 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   if (v->dev.count[0] > p.c1max) p.c1max = v->dev.count[0];
   p.off_mid = o;       o = align256(o + R * (size_t)p.c1max * 8);
   p.off_mid_meta = o;  o = align256(o + R * (size_t)p.K[0] * 16);
-  p.off_leaf = o;      o = align256(o + R * (size_t)p.c2max * 4);
+  // Leaf candidates are filtered in the leaf stream on per-head trees whose
+  // mids can have at least kLeafFilterRatio * K_L children: each leaf-stream
+  // wave stages at most kLeafStageFloats scores, so a scoring group takes
+  // leaf_nst members; the survivors are (score, index) pairs, 8 bytes a
+  // candidate slot, and the mid's place in the row's selection rides in the
+  // top byte of a member's slot base.  With shorter spans the staging and
+  // the per-member threshold cost the stream more than the smaller select
+  // saves (measured: 100-leaf spans at K_L = 32 step 0.529 -> 0.574 ms;
+  // 215-leaf spans at K_L = 32 0.444 -> 0.434 ms; 463-leaf spans at K_L = 64
+  // unchanged, the select 119 -> 69 us and the stream 1102 -> 1130 us).
+  if (mode != kModeFoldedDescent && (t.d == 64 || t.d == 128) && p.K[1] > 0 && p.K[2] > 0 &&
+      v->maxfan[1] >= kLeafFilterRatio * (int64_t)p.K[2] && v->maxfan[1] <= kLeafFilterMaxFan &&
+      p.c2max < kMaxMidCands) {
+    p.leaf_fpad = (int)((v->maxfan[1] + 3) & ~(int64_t)3);
+    const int nst = kLeafStageFloats / p.leaf_fpad;
+    p.leaf_nst = nst < 1 ? 1 : nst > 8 ? 8 : nst;
+    // survivors a row: K_L of each span longer than K_L, a few more near its
+    // threshold; rows past the register list read theirs from the workspace
+    const int64_t est = (int64_t)p.K[1] * (p.K[2] + 2) + 64;
+    p.leaf_spt = est <= 512 ? 8 : est <= 1024 ? 16 : est <= 1536 ? 24 : 40;
+  }
+  p.off_leaf = o;      o = align256(o + R * (size_t)p.c2max * (p.leaf_nst > 0 ? 8 : 4));
+  p.off_lcnt = o;      o = align256(o + (p.leaf_nst > 0 ? R * (size_t)p.K[1] * 4 : 0));
   for (int i = 0; i < 3; ++i) { p.off_sel[i] = o; o = align256(o + R * (size_t)p.K[i] * 4); }
   p.off_mid_base = o;  o = align256(o + R * (size_t)p.K[1] * 4);
   const size_t nroot = (size_t)t.Hkv * (size_t)t.count[0];
@@ -760,6 +784,13 @@ hipError_t launch_descent(const Plan& p, const RowsDev& rows, atlaskv_tree_view_
   a.mid_pairs = (uint2*)(ws + p.off_mid);
   a.mid_meta = (int4*)(ws + p.off_mid_meta);
   a.leaf_scores = (float*)(ws + p.off_leaf);
+  if (p.leaf_nst > 0) {
+    a.leaf_pairs = (uint2*)(ws + p.off_leaf);
+    a.leaf_cnt = (int32_t*)(ws + p.off_lcnt);
+    a.leaf_nst = p.leaf_nst;
+    a.leaf_fpad = p.leaf_fpad;
+    a.leaf_spt = p.leaf_spt;
+  }
   a.mid_base = (int32_t*)(ws + p.off_mid_base);
   a.root_cnt = (int32_t*)(ws + p.off_rcnt);
   a.root_tot = (int32_t*)(ws + p.off_rtot);

@@ -22,6 +22,9 @@ constexpr int kDescSub = 64;      // bucket descriptor sub-lists, picked by link
 constexpr int kFilterK = 32;      // largest K_I the mid tiles filter their scores for (else all are kept)
 constexpr int64_t kMaxMidCands = (int64_t)1 << 24;  // mid candidates per row (slot bases pack in 24 bits)
 constexpr int kMaxParts = 2;      // descent parts (KV-head ranges run concurrently)
+constexpr int kLeafStageFloats = 1024;  // staged scores a leaf-stream wave holds (per-member groups)
+constexpr int kLeafFilterMaxFan = 1024; // largest mid fanout the leaf-stream filter stages
+constexpr int kLeafFilterRatio = 4;     // the filter runs when the largest mid fanout is >= this x K_L
 constexpr int kDtypeF32 = 0;
 
 // Row-aligned work chunks of the kernels that scan a row's K selections in
@@ -133,6 +136,17 @@ struct StepArgs {
   int32_t* bucket_ovf;        // [rows * K[1] / (bslots + 1) + 1] keys (g*M_I + mid) with overflow members
   float* o_kg;                // [R, d] softmax-weighted leaf values (fp32)
   float* lse_kg;              // [R] log-sum-exp of the selected leaf logits
+  // Leaf candidates filtered in the leaf stream (leaf_nst > 0; per-head trees):
+  // a member's scores over a bucket's span are staged in LDS and only those
+  // that can still be among the row's K_L best are written, as (unscaled fp32
+  // score bits, leaf index in the span) pairs from the mid's first candidate
+  // slot on; the bucket members then carry (row, first slot | k << 24), k the
+  // mid's place in the row's selection.
+  uint2* leaf_pairs;          // [R, c2max] survivors (leaf_nst > 0; else leaf_scores is used)
+  int32_t* leaf_cnt;          // [R, K[1]] survivors per (row, selected mid)
+  int leaf_nst;               // members scored per pass (their scores staged), 0: no filter
+  int leaf_fpad;              // staged scores per member: max mid fanout rounded up to 4
+  int leaf_spt;               // survivors a lane of the filtered leaf select holds in registers
   int exact_logits;           // non-zero (folded calls on fp32 trees): the KG softmax takes the selected
                               // leaves' logits from the exact query r.q_exact (fp64 dot products),
                               // not from the scores

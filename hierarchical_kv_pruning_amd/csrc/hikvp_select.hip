@@ -1013,7 +1013,9 @@ __device__ inline int link_part(const StepArgs& a, bool ok, int64_t e, int row, 
   const int excl = incl - fan;
   const int base = carry + excl - __shfl(excl, s0);
   if (ok) a.mid_base[e] = base;
-  register_in_bucket(a, e, row, sub, g, key, rank, f0, fan, base, lane);
+  // filtered leaf scoring also needs the mid's place k in the row's selection
+  const int tag = a.leaf_nst > 0 ? (int)(e - (int64_t)row * a.K[1]) << 24 : 0;
+  register_in_bucket(a, e, row, sub, g, key, rank, f0, fan, base | tag, lane);
   return carry + __builtin_amdgcn_readlane(incl, 63);
 }
 
@@ -1150,6 +1152,165 @@ __device__ inline void score_member_group(const StepArgs& a, const char* kp, int
   }
 }
 
+// Filtered scoring (per-head trees, leaf_nst > 0): a group of up to leaf_nst
+// members is scored with exactly the arithmetic of score_member_group, but
+// the scores go to the wave's LDS stage [leaf_nst][leaf_fpad] instead of the
+// workspace.  Then, member by member: T_b, the K_L-th largest score of the
+// span to 24 bits of its order key (a lower bound), is at most the K_L-th
+// largest score of the member's whole leaf candidate list (the span's K_L
+// best are candidates of that list), so every candidate the row's select can
+// take -- above its band or inside it, i.e. f >= T - W with T >= T_b -- has
+// f >= T_b - Wf, Wf >= 2 W being the mid tiles' filter margin; those are
+// written as (score bits, index in the span) pairs from the mid's first
+// slot on, in span order, and their number to leaf_cnt[row, k].  A span of
+// at most K_L leaves keeps every leaf.
+template <class E, int D, bool LO>
+__device__ inline void score_member_group_filtered(const StepArgs& a, const char* kp, int64_t rsb, int F,
+                                                   int2 mem, int g0, int gcnt, int lane, float* stage) {
+  int* hist = (int*)(stage + a.leaf_nst * a.leaf_fpad);  // [256] radix histogram of the wave
+  constexpr int RB = D * E::kBytes;        // bytes per key row
+  constexpr int KP = RB / 128;             // 16-byte pieces per lane per tile
+  constexpr int TU = 4;                    // tiles per round = consecutive keys per lane
+  const int quad = lane >> 4, item = lane & 7;
+  const bool owner = lane < 32 && (lane & 15) < 8;   // holds combined scores
+  const int fpad = a.leaf_fpad;
+  // A fragment: member `item` (and its bf16 residual, LO), zeros past the
+  // members; qq: the sum of squares of this lane's pieces of member item
+  uint4 afr[KP], alo[KP];
+  const int row = __shfl(mem.x, g0 + item);
+  float qq = 0.f;
+  if (item < gcnt) {
+    int b, n, h;
+    decode_row(a.r, row, b, n, h);
+    const char* qp = (const char*)a.r.q_kg + q_off(a.r.qks, b, n, h) * E::kBytes + split_off(lane, 0);
+#pragma unroll
+    for (int m = 0; m < KP; ++m) {
+      afr[m] = *(const uint4*)(qp + m * 128);
+      float f[E::kEPV];
+      unpack<E>(afr[m], f);
+#pragma unroll
+      for (int e = 0; e < E::kEPV; ++e) qq = fmaf(f[e], f[e], qq);
+    }
+    if constexpr (LO) {
+      const char* lp = (const char*)a.r.q_lo + (int64_t)row * D * E::kBytes + split_off(lane, 0);
+#pragma unroll
+      for (int m = 0; m < KP; ++m) alo[m] = *(const uint4*)(lp + m * 128);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < KP; ++m) afr[m] = alo[m] = make_uint4(0, 0, 0, 0);
+  }
+  // the 8 lanes item, item + 8, ..., item + 56 hold member item's pieces
+  qq += __shfl_xor(qq, 8);
+  qq += __shfl_xor(qq, 16);
+  qq += __shfl_xor(qq, 32);
+  // owners stage members 4*quad + vv, keys t0 + item*TU .. + TU-1
+  float* sdst[4];
+#pragma unroll
+  for (int vv = 0; vv < 4; ++vv) {
+    const int ms = 4 * (quad & 1) + vv;
+    sdst[vv] = (owner && ms < gcnt) ? stage + ms * fpad + item * TU : nullptr;
+  }
+  for (int t0 = 0; t0 < F; t0 += 8 * TU) {
+    uint4 bfr[TU][KP];
+#pragma unroll
+    for (int u = 0; u < TU; ++u) {
+      const char* p = kp + (int64_t)min(t0 + item * TU + u, F - 1) * rsb;
+#pragma unroll
+      for (int m = 0; m < KP; ++m) bfr[u][m] = load_nt(p + m * 128);
+    }
+    float4_t sc[TU];
+#pragma unroll
+    for (int u = 0; u < TU; ++u) sc[u] = split_combine(member_tile<E, KP, LO>(afr, alo, bfr[u]), lane);
+    const bool full = t0 + 8 * TU <= F;
+#pragma unroll
+    for (int vv = 0; vv < 4; ++vv) {
+      if (!sdst[vv]) continue;
+      if (full) {
+        *(float4*)(sdst[vv] + t0) = make_float4(sc[0][vv], sc[1][vv], sc[2][vv], sc[3][vv]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < TU; ++u)
+          if (t0 + item * TU + u < F) sdst[vv][t0 + u] = sc[u][vv];
+      }
+    }
+  }
+  wave_sync();
+  const int K2 = a.K[2], K1 = a.K[1];
+  const int nv = (F + 63) >> 6;                      // wave-uniform
+  for (int ms = 0; ms < gcnt; ++ms) {                // wave-uniform
+    const int srow = __shfl(mem.x, g0 + ms);
+    const uint32_t sy = (uint32_t)__shfl(mem.y, g0 + ms);
+    const float* sp = stage + ms * fpad;
+    // order key of staged score lane + 64 j (0 past the span)
+    auto key_at = [&](int j) { return lane + 64 * j < F ? ord_key(sp[lane + 64 * j]) : 0u; };
+    uint32_t lo = 0u;                                // keep keys >= lo (0: every leaf)
+    if (F > K2) {
+      // the K_L-th largest key's top two bytes: two 8-bit radix passes with
+      // an LDS histogram (pass 2 over the keys in pass 1's bin)
+      uint32_t pre = 0u;
+      int krem = K2;
+      for (int pass = 0; pass < 2; ++pass) {
+        const int shift = 24 - 8 * pass;
+        const uint32_t mask = pass ? 0xff000000u : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hist[lane + 64 * i] = 0;
+        wave_sync();
+        for (int j = 0; j < nv; ++j) {
+          const uint32_t x = key_at(j);
+          if (x != 0u && (x & mask) == pre) atomicAdd(&hist[(x >> shift) & 255u], 1);
+        }
+        wave_sync();
+        // lane l holds bins 4l .. 4l+3; the bin where the count from the top reaches krem
+        const int c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
+        const int tot = c0 + c1 + c2 + c3;
+        const int incl = wave_incl_sum(tot);
+        const int suf = __builtin_amdgcn_readlane(incl, 63) - incl + tot;
+        const int above = suf - tot;
+        const uint64_t hit = __ballot(above < krem && krem <= suf);
+        const int src = (int)__builtin_ctzll(hit);   // one lane holds the crossing (krem <= the bins' total)
+        int bin = 0, nk = 0;
+        if (lane == src) {
+          int cum = above;
+          const int c4[4] = {c0, c1, c2, c3};
+          bin = 4 * lane;
+          nk = krem - cum;
+          for (int q = 3; q >= 0; --q) {
+            if (cum + c4[q] >= krem) { bin = 4 * lane + q; nk = krem - cum; break; }
+            cum += c4[q];
+          }
+        }
+        pre |= (uint32_t)__builtin_amdgcn_readlane(bin, src) << shift;
+        krem = __builtin_amdgcn_readlane(nk, src);
+        wave_sync();                                   // the histogram is read before the next pass clears it
+      }
+      // the select's band for this row, doubled (the mid tiles' margin)
+      const int g = (srow % a.r.Hq) / a.r.G;
+      const float knorm = a.t.norm[2 * a.t.Hkv + g];
+      const float qsq = __shfl(qq, ms) * (LO ? kLoNorm2 : 1.f);
+      const float qnv = sqrtf(qsq) * norm_slack(D) * 1.001f;
+      const float qd = a.r.q_delta ? a.r.q_delta[srow] : 0.f;
+      const float e2 = 2.f * qnv * knorm * (float)err_terms(D) * (1.f / 8388608.f) + 2.f * qd * knorm * 1.001f;
+      const float wf = 2.f * (e2 * 1.01f + 4.f * qnv * knorm * (1.f / 8388608.f)) + 1e-30f;
+      if (pre >= 0x00800000u) lo = ord_key(ord_float(pre) - wf);  // (finite scores have keys above it)
+    }
+    uint2* dp = a.leaf_pairs + (int64_t)srow * a.c2max + (sy & 0xffffffu);
+    int cnt = 0;
+    for (int j = 0; j < nv; ++j) {
+      const uint32_t x = key_at(j);
+      const bool keep = x != 0u && x >= lo;
+      const uint64_t bal = __ballot(keep);
+      if (keep) {
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        dp[cnt + below] = make_uint2(__float_as_uint(ord_float(x)), (uint32_t)(lane + 64 * j));
+      }
+      cnt += __popcll(bal);
+    }
+    if (lane == 0) a.leaf_cnt[(int64_t)srow * K1 + (sy >> 24)] = cnt;
+  }
+  wave_sync();                                       // the stage is free for the next group
+}
+
 // Wide key rows (base-embedding trees): the same tiles and item layout over
 // 128-element slices of the row, each round's tiles accumulated over the
 // slices before the two halves are combined.  Up to NG groups of 8 members
@@ -1242,11 +1403,25 @@ __device__ inline void score_members(const StepArgs& a, const char* kp, int64_t 
   else score_member_group<E, D, LO>(a, kp, rsb, F, mem, g0, gcnt, lane);
 }
 
+// Members per scoring group, and one group scored: filtered (staged in the
+// wave's LDS `stage`) when the call filters leaf candidates, else written
+// whole to the workspace.
+template <bool FILT>
+__device__ inline int group_size(const StepArgs& a) {
+  return FILT ? a.leaf_nst : 8;
+}
+template <class E, int D, bool LO, bool FILT>
+__device__ inline void score_group(const StepArgs& a, const char* kp, int64_t rsb, int F, int2 mem, int g0,
+                                   int gcnt, int lane, float* stage) {
+  if constexpr (FILT && D != 0) score_member_group_filtered<E, D, LO>(a, kp, rsb, F, mem, g0, gcnt, lane, stage);
+  else score_members<E, D, LO>(a, kp, rsb, F, mem, g0, gcnt, lane);
+}
+
 // Members of buckets with more than bslots rows: wave `wave0` of `nwaves`
 // takes every nwaves-th listed bucket, walks its list and scores the members
-// 8 at a time with the same group arithmetic as the fixed slots.
-template <class E, int D, bool LO>
-__device__ inline void score_overflow(const StepArgs& a, int wave0, int nwaves, int lane) {
+// a group at a time with the same group arithmetic as the fixed slots.
+template <class E, int D, bool LO, bool FILT>
+__device__ inline void score_overflow(const StepArgs& a, int wave0, int nwaves, int lane, float* stage) {
   const int nov = a.bucket_count[kDescSub];
   const int K1 = a.K[1];
   const int MI = (int)a.t.count[1];
@@ -1259,15 +1434,18 @@ __device__ inline void score_overflow(const StepArgs& a, int wave0, int nwaves, 
     const int64_t f0 = a.t.off[1][mid];
     const int F = (int)(a.t.off[1][mid + 1] - f0);
     const char* kp = kbase + ((int64_t)g * a.t.hs[2] + f0 * a.t.rs[2]) * E::kBytes + split_off(lane, 0);
+    const int gsz = group_size<FILT>(a);
     int e = a.bucket_head[bix];
     while (e != -1) {  // wave-uniform walk: lane i takes the group's i-th entry
       int mine = -1, gcnt = 0;
-      for (; gcnt < 8 && e != -1; ++gcnt) {
+      for (; gcnt < gsz && e != -1; ++gcnt) {
         if (lane == gcnt) mine = e;
         e = a.bucket_next[e];
       }
-      const int2 gm = (lane < gcnt) ? make_int2(mine / K1, a.mid_base[mine]) : make_int2(-1, 0);
-      score_members<E, D, LO>(a, kp, rsb, F, gm, 0, gcnt, lane);
+      // (row, first slot), with the mid's place in the row's selection when filtered
+      const int2 gm = (lane < gcnt) ? make_int2(mine / K1, a.mid_base[mine] | (FILT ? (mine % K1) << 24 : 0))
+                                    : make_int2(-1, 0);
+      score_group<E, D, LO, FILT>(a, kp, rsb, F, gm, 0, gcnt, lane, stage);
     }
   }
 }
@@ -1277,9 +1455,12 @@ __device__ inline void score_overflow(const StepArgs& a, int wave0, int nwaves, 
 // over its span, mostly L2 hits; wide rows take 24 a pass).  Then the
 // members past bslots (score_overflow; the lists are complete once the link
 // kernel has run): a separate launch for them cost ~5 us a step.
-template <class E, int D, bool LO>
-__global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
+template <class E, int D, bool LO, bool FILT>
+__device__ inline void leaf_score_body(const StepArgs& a) {
+  extern __shared__ __align__(16) char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+  // this wave's score stage (filtered calls)
+  float* stage = (float*)smem + (size_t)wave * (FILT ? a.leaf_nst * a.leaf_fpad + 256 : 0);
   // descriptor v of the concatenated sub-lists: lane s holds sub-list s's
   // count and its inclusive prefix
   const int scnt = a.bucket_count[lane];  // lane < kDescSub = 64
@@ -1311,46 +1492,37 @@ __global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
       for (int g0 = 0; g0 < cnt; g0 += 24)
         score_members_wide<E, LO, 3, 4>(a, kp, rsb, F, mem, g0, min(24, cnt - g0), lane);
     } else {
-      for (int g0 = 0; g0 < cnt; g0 += 8)
-        score_members<E, D, LO>(a, kp, rsb, F, mem, g0, min(8, cnt - g0), lane);
+      const int gsz = group_size<FILT>(a);
+      for (int g0 = 0; g0 < cnt; g0 += gsz)
+        score_group<E, D, LO, FILT>(a, kp, rsb, F, mem, g0, min(gsz, cnt - g0), lane, stage);
     }
     cur = nxt;
     v = vn;
   }
-  score_overflow<E, D, LO>(a, blockIdx.x * nwave + wave, stride, lane);
+  score_overflow<E, D, LO, FILT>(a, blockIdx.x * nwave + wave, stride, lane, stage);
+}
+template <class E, int D, bool LO>
+__global__ __launch_bounds__(256) void k_leaf_score(StepArgs a) {
+  leaf_score_body<E, D, LO, false>(a);
+}
+// Filtered calls (per-head trees, D = 64 or 128; the wide instances are
+// never launched)
+template <class E, int D, bool LO>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_leaf_score_filtered(StepArgs a) {
+  if constexpr (D != 0) leaf_score_body<E, D, LO, true>(a);
 }
 
 // ---------------------------------------------------------------------------
 // leaf Top-K and the KG softmax over the selected leaves, one wave per row
 // ---------------------------------------------------------------------------
-template <class E, int D, int NT, int SPT>
-__device__ inline void leaf_select_body(const StepArgs& a, size_t group_bytes) {
+// KG half of one row (one wave): softmax over the selected leaves' logits
+// (W.out_node / W.out_logit, k2 of them) and the weighted sum of their values
+// into o_kg, the log-sum-exp into lse_kg.
+template <class E, int D>
+__device__ inline void kg_half(const StepArgs& a, const RowWork& W, int row, int g, int k2, const char* kb,
+                               int64_t rsb, int lane) {
   constexpr int SW = SliceW<D>::W;  // value-row slice width (the whole row unless wide)
-  extern __shared__ __align__(16) char smem[];
-  const int groups = blockDim.x / NT, grp = threadIdx.x / NT, gtid = threadIdx.x % NT;
-  const int blk = a.blk0 + blockIdx.x * groups + grp;
-  if (blk >= a.blk1) return;
-  const int K2 = a.K[2];
   const int d = D ? D : a.t.d;
-  RowWork W = carve_rowwork(smem + (size_t)grp * group_bytes, K2, a.K[1], d, 0, NT);
-  const int row = row_of_block(a.r, blk);
-  W.sel.qx = exact_query(a.r, row, d);
-  const int p0 = first_parent(a, row, 2, gtid);
-  const auto sc = RowScores<NT, SPT>::make(a.leaf_scores + (int64_t)row * a.c2max, (int)a.c2max, gtid);
-  int g;
-  double qnorm;
-  const int n2 = select_prologue<E, D, NT>(a, W, row, 2, g, qnorm, gtid, p0);
-  int64_t rsb;
-  const char* kb = key_base(a.t, 2, g, rsb, E::kBytes);
-  const double err2 = twice_err_bound(qnorm, a.t.norm[2 * a.t.Hkv + g], d, query_delta(a.r, row));
-  const int k2 = select_topk<E, D, NT>(sc, n2, K2, err2, a.r.scale, SlotMap{W.pre, W.base, a.K[1]},
-                                       KeyRows{kb, rsb}, W.sel, W.out_node, W.out_logit, gtid);
-  int32_t* o2 = a.sel[2] + (int64_t)row * K2;
-  for (int i = gtid; i < K2; i += NT) o2[i] = i < k2 ? W.out_node[i] : -1;
-  if (gtid >= 64) return;  // the KG half is formed by the group's first wave
-  const int lane = gtid;
-
-  // KG half: softmax over the selected leaves' logits, weighted values
   float* okg = a.o_kg + (int64_t)row * d;
   if (k2 == 0) {
     for (int e = lane; e < d; e += 64) okg[e] = 0.f;
@@ -1443,8 +1615,113 @@ __device__ inline void leaf_select_body(const StepArgs& a, size_t group_bytes) {
 }
 
 template <class E, int D, int NT, int SPT>
+__device__ inline void leaf_select_body(const StepArgs& a, size_t group_bytes) {
+  extern __shared__ __align__(16) char smem[];
+  const int groups = blockDim.x / NT, grp = threadIdx.x / NT, gtid = threadIdx.x % NT;
+  const int blk = a.blk0 + blockIdx.x * groups + grp;
+  if (blk >= a.blk1) return;
+  const int K2 = a.K[2];
+  const int d = D ? D : a.t.d;
+  RowWork W = carve_rowwork(smem + (size_t)grp * group_bytes, K2, a.K[1], d, 0, NT);
+  const int row = row_of_block(a.r, blk);
+  W.sel.qx = exact_query(a.r, row, d);
+  const int p0 = first_parent(a, row, 2, gtid);
+  const auto sc = RowScores<NT, SPT>::make(a.leaf_scores + (int64_t)row * a.c2max, (int)a.c2max, gtid);
+  int g;
+  double qnorm;
+  const int n2 = select_prologue<E, D, NT>(a, W, row, 2, g, qnorm, gtid, p0);
+  int64_t rsb;
+  const char* kb = key_base(a.t, 2, g, rsb, E::kBytes);
+  const double err2 = twice_err_bound(qnorm, a.t.norm[2 * a.t.Hkv + g], d, query_delta(a.r, row));
+  const int k2 = select_topk<E, D, NT>(sc, n2, K2, err2, a.r.scale, SlotMap{W.pre, W.base, a.K[1]},
+                                       KeyRows{kb, rsb}, W.sel, W.out_node, W.out_logit, gtid);
+  int32_t* o2 = a.sel[2] + (int64_t)row * K2;
+  for (int i = gtid; i < K2; i += NT) o2[i] = i < k2 ? W.out_node[i] : -1;
+  if (gtid >= 64) return;  // the KG half is formed by the group's first wave
+  const int lane = gtid;
+  kg_half<E, D>(a, W, row, g, k2, kb, rsb, lane);
+}
+
+template <class E, int D, int NT, int SPT>
 __global__ __launch_bounds__(256) void k_leaf_select(StepArgs a, size_t gb) {
   leaf_select_body<E, D, NT, SPT>(a, gb);
+}
+
+// LDS of one k_leaf_select_pairs wave: the select's work area, cpre, (k, j)
+// of the register-held survivors.
+__host__ __device__ inline size_t leaf_pairs_wave_bytes(int K2, int K1, int d, int SPT) {
+  return rowwork_bytes(K2, K1, d, 0) + align16((size_t)(K1 + 1) * 4) + align16((size_t)64 * SPT * 4);
+}
+
+// Leaf Top-K over the survivors of the filtered leaf stream, one wave per
+// row, then the KG half.  The survivors of the row's k-th selected mid sit
+// from its first candidate slot pre[k] on (leaf_cnt of them), so the mid
+// select's entry machinery serves: entry e of mid k is slot pre[k] + j and
+// node base[k] + j for the span index j stored with its score.
+template <class E, int D, int SPT>
+__global__ __launch_bounds__(256) void k_leaf_select_pairs(StepArgs a, size_t wave_bytes) {
+  extern __shared__ __align__(16) char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+  const int blk = a.blk0 + blockIdx.x * nwave + wave;
+  if (blk >= a.blk1) return;  // whole wave; waves never meet at a barrier
+  const int K1 = a.K[1], K2 = a.K[2];
+  const int d = D ? D : a.t.d;
+  char* p = smem + (size_t)wave * wave_bytes;
+  RowWork W = carve_rowwork(p, K2, K1, d, 0);
+  p += rowwork_bytes(K2, K1, d, 0);
+  int* cpre = (int*)p;
+  p += align16((size_t)(K1 + 1) * 4);
+  int* kj = (int*)p;
+  const int row = row_of_block(a.r, blk);
+  W.sel.qx = exact_query(a.r, row, d);
+  const int p0 = first_parent(a, row, 2, lane);
+  int g;
+  double qnorm;
+  select_prologue<E, D, 64>(a, W, row, 2, g, qnorm, lane, p0);  // query, its norm, pre[] and base[]
+  // survivors of each selected mid (a mid without children has none: its
+  // count is never written)
+  int carry = 0;
+  if (lane == 0) cpre[0] = 0;
+  for (int k0 = 0; k0 < K1; k0 += 64) {
+    const int k = k0 + lane;
+    const int c = (k < K1 && W.pre[k + 1] > W.pre[k]) ? a.leaf_cnt[(int64_t)row * K1 + k] : 0;
+    const int incl = wave_incl_sum(c);
+    if (k < K1) cpre[k + 1] = carry + incl;
+    carry += __builtin_amdgcn_readlane(incl, 63);
+  }
+  wave_sync();
+  const int cnt = carry;
+  const MidEntries me{a.leaf_pairs + (int64_t)row * a.c2max, cpre, W.pre, W.base, K1};
+  int64_t rsb;
+  const char* kb = key_base(a.t, 2, g, rsb, E::kBytes);
+  const double err2 = twice_err_bound(qnorm, a.t.norm[2 * a.t.Hkv + g], d, query_delta(a.r, row));
+  int k2;
+  if (cnt <= 64 * SPT) {
+    MidRegScores<SPT> src;
+    src.m = me;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int e = i * 64 + lane;
+      src.v[i] = 0.f;
+      if (e < cnt) {
+        int k;
+        const uint2 pr = me.pair(e, k);
+        src.v[i] = __uint_as_float(pr.x);
+        kj[e] = (k << 24) | (int)pr.y;
+      }
+    }
+    wave_sync();
+    k2 = select_topk<E, D, 64, MidRegScores<SPT>, false, MidRegMap>(
+        src, cnt, K2, err2, a.r.scale, MidRegMap{kj, W.pre, W.base}, KeyRows{kb, rsb}, W.sel, W.out_node,
+        W.out_logit, lane);
+  } else {
+    k2 = select_topk<E, D, 64, MidMemScores, false, MidMemMap>(
+        MidMemScores{me}, cnt, K2, err2, a.r.scale, MidMemMap{me}, KeyRows{kb, rsb}, W.sel, W.out_node,
+        W.out_logit, lane);
+  }
+  int32_t* o2 = a.sel[2] + (int64_t)row * K2;
+  for (int i = lane; i < K2; i += 64) o2[i] = i < k2 ? W.out_node[i] : -1;
+  kg_half<E, D>(a, W, row, g, k2, kb, rsb, lane);
 }
 
 }  // namespace
@@ -1619,12 +1896,44 @@ hipError_t launch_leaf_score(const StepArgs& a, hipStream_t s) {
   const int64_t nb_max = (int64_t)(a.blk1 - a.blk0) * a.K[1];
   int64_t blocks = (nb_max + 3) / 4;
   if (blocks > 2048) blocks = 2048;
-  HIKVP_DISPATCH_LO(a, k_leaf_score, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  // filtered calls: each of the 4 waves stages leaf_nst members' scores
+  if (a.leaf_nst > 0) {
+    const size_t lds = (size_t)4 * (a.leaf_nst * a.leaf_fpad + 256) * 4;
+    if (lds > 64 * 1024 || (a.t.d != 64 && a.t.d != 128)) return hipErrorInvalidValue;
+    HIKVP_DISPATCH_LO(a, k_leaf_score_filtered, dim3((unsigned)blocks), dim3(256), lds, s, a);
+  } else {
+    HIKVP_DISPATCH_LO(a, k_leaf_score, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_leaf_select(const StepArgs& a, hipStream_t s) {
   if (a.blk1 <= a.blk0) return hipSuccess;
+  if (a.leaf_nst > 0) {
+    // the filtered stream's survivors: one wave per row
+    const int spt = a.leaf_spt;
+    if ((spt != 8 && spt != 16 && spt != 24 && spt != 40) || (a.t.d != 64 && a.t.d != 128))
+      return hipErrorInvalidValue;
+    const size_t wb = leaf_pairs_wave_bytes(a.K[2], a.K[1], a.t.d, spt);
+    int wpb = 4;
+    while (wpb > 1 && wb * wpb > 64 * 1024) --wpb;
+    if (wb * wpb > 64 * 1024) return hipErrorInvalidValue;
+    const dim3 g_((unsigned)((a.blk1 - a.blk0 + wpb - 1) / wpb)), b_(64 * wpb);
+    const bool bf = a.t.dtype == kDtypeBF16, d128 = a.t.d == 128;
+#define HIKVP_LEAF_PAIRS(SPT_)                                                                          \
+    do {                                                                                               \
+      if (bf && d128) hipLaunchKernelGGL((k_leaf_select_pairs<BF16, 128, SPT_>), g_, b_, wb * wpb, s, a, wb); \
+      else if (bf) hipLaunchKernelGGL((k_leaf_select_pairs<BF16, 64, SPT_>), g_, b_, wb * wpb, s, a, wb); \
+      else if (d128) hipLaunchKernelGGL((k_leaf_select_pairs<F32, 128, SPT_>), g_, b_, wb * wpb, s, a, wb); \
+      else hipLaunchKernelGGL((k_leaf_select_pairs<F32, 64, SPT_>), g_, b_, wb * wpb, s, a, wb);    \
+    } while (0)
+    if (spt == 8) HIKVP_LEAF_PAIRS(8);
+    else if (spt == 16) HIKVP_LEAF_PAIRS(16);
+    else if (spt == 24) HIKVP_LEAF_PAIRS(24);
+    else HIKVP_LEAF_PAIRS(40);
+#undef HIKVP_LEAF_PAIRS
+    return hipGetLastError();
+  }
   HIKVP_SELECT_LAUNCH(a, a.c2max, k_leaf_select, a.K[2], a.K[1], s);
   return hipGetLastError();
 }

@@ -171,9 +171,9 @@ def test_deterministic_reruns():
 
 def test_deterministic_with_overflowing_buckets():
     """Buckets of far more than 32 rows (eight query heads on one KV head, most
-    mids selected): members past the fixed slots are scored by a second kernel
-    with the same arithmetic, so reruns agree bit for bit although which
-    members overflow depends on atomic order."""
+    mids selected): members past the fixed slots are scored from their lists
+    at the end of the leaf stream with the same arithmetic, so reruns agree
+    bit for bit although which members overflow depends on atomic order."""
     case = _small(seed=19, dtype="bf16", B=2, N=9, S_kv=13, Hq=8, Hkv=1, M_R=37, M_I=411, M=3001)
     K = (37, 256, 256)
     a = parity.gpu_run(case, K=K, out_dtype=torch.float32)
@@ -182,6 +182,26 @@ def test_deterministic_with_overflowing_buckets():
     for x, y in zip(a["sel"], b["sel"]):
         assert np.array_equal(x, y)
     _check(case, K=K)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 128), ("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_filtered_leaf_stream(dtype, d):
+    """Mids with at least four times K_L children (ragged spans of 15 to 728
+    leaves): the leaf stream writes only the candidates that can still be
+    among a row's K_L best, and the select over them takes the same leaves."""
+    _check(_small(seed=31, dtype=dtype, d=d, M_I=40, M=6000, K=(5, 7, 19)))
+
+
+@pytest.mark.parametrize("K", [(6, 30, 1), (3, 5, 64), (6, 12, 200)])
+def test_filtered_leaf_stream_overflow_and_k(K):
+    """The filtered leaf stream with buckets of up to 144 rows (most past the
+    fixed slots, scored from their lists), K_L = 1, K_L = 64 over spans of
+    18 to 454 leaves, and K_L = 200 (filter off: spans too short for it);
+    reruns agree bit for bit."""
+    case = _small(seed=33, dtype="bf16", B=2, N=9, S_kv=13, Hq=8, Hkv=1, M_R=6, M_I=30, M=6000)
+    gpu, _, _ = _check(case, K=K)
+    again = parity.gpu_run(case, K=K)
+    assert np.array_equal(gpu["out"], again["out"]) and np.array_equal(gpu["sel"][2], again["sel"][2])
 
 
 @pytest.mark.parametrize("N,S_kv", [(33, 45), (1, 300)])
