@@ -22,7 +22,7 @@ constexpr int kDescSub = 64;      // bucket descriptor sub-lists, picked by link
 constexpr int kFilterK = 32;      // largest K_I the mid tiles filter their scores for (else all are kept)
 constexpr int64_t kMaxMidCands = (int64_t)1 << 24;  // mid candidates per row (slot bases pack in 24 bits)
 constexpr int kMaxParts = 2;      // descent parts (KV-head ranges run concurrently)
-constexpr int kLeafStageFloats = 1024;  // staged scores a leaf-stream wave holds (per-member groups)
+constexpr int kLeafStageFloats = 2048;  // staged scores a leaf-stream wave holds (per-member groups)
 constexpr int kLeafFilterMaxFan = 1024; // largest mid fanout the leaf-stream filter stages
 constexpr int kLeafFilterRatio = 4;     // the filter runs when the largest mid fanout is >= this x K_L
 constexpr int kDtypeF32 = 0;
