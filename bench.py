@@ -171,7 +171,8 @@ PHASE_OF = {
     "k_root_mfma": "root_score_topk", "k_root": "root_score_topk",
     "k_root_scan": "root_score_topk (grouping)", "k_root_fill": "root_score_topk (grouping)",
     "k_mid_gemm": "mid_bucket_gemm", "k_mid_select": "mid_topk", "k_bucket_link": "leaf_bucket_link",
-    "k_leaf_score": "leaf_score_stream",
+    "k_leaf_score": "leaf_score_stream", "k_leaf_score_filtered": "leaf_score_stream",
+    "k_leaf_select_pairs": "leaf_topk_kg_attention",
     "k_leaf_select": "leaf_topk_kg_attention", "k_seq_mfma": "seq_attention",
     "k_seq_decode_mfma": "seq_attention", "k_seq_decode": "seq_attention", "k_seq_flash": "seq_attention",
     "k_seq_combine": "seq_split_combine",
@@ -180,12 +181,14 @@ PHASE_OF = {
 # the kernel each phase's HBM summary counts (a phase's main kernel)
 HBM_SUMMARY_KERNELS = {
     "root_score_topk": ("k_root",), "mid_bucket_gemm": ("k_mid_gemm",), "mid_topk": ("k_mid_select",),
-    "leaf_bucket_link": ("k_bucket_link",), "leaf_score_stream": ("k_leaf_score",),
-    "leaf_topk_kg_attention": ("k_leaf_select",),
+    "leaf_bucket_link": ("k_bucket_link",),
+    "leaf_score_stream": ("k_leaf_score", "k_leaf_score_filtered"),
+    "leaf_topk_kg_attention": ("k_leaf_select", "k_leaf_select_pairs"),
     "seq_attention": ("k_seq_mfma", "k_seq_decode_mfma", "k_seq_decode", "k_seq_flash"),
 }
 BUSY_KERNELS = ("k_root_mfma", "k_root", "k_mid_gemm", "k_mid_select", "k_bucket_link", "k_leaf_score",
-                "k_leaf_select", "k_seq_mfma", "k_seq_decode_mfma", "k_seq_combine")
+                "k_leaf_score_filtered", "k_leaf_select", "k_leaf_select_pairs", "k_seq_mfma", "k_seq_decode_mfma",
+                "k_seq_combine")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 # the busy pass: the tool's two derived metrics and the raw counters behind them
 BUSY_COUNTERS = ("MfmaUtil", "VALUBusy", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU",
