@@ -1921,9 +1921,15 @@ hipError_t launch_leaf_select(const StepArgs& a, hipStream_t s) {
     if ((spt != 8 && spt != 16 && spt != 24 && spt != 40) || (a.t.d != 64 && a.t.d != 128))
       return hipErrorInvalidValue;
     const size_t wb = leaf_pairs_wave_bytes(a.K[2], a.K[1], a.t.d, spt);
-    int wpb = 4;
-    while (wpb > 1 && wb * wpb > 64 * 1024) --wpb;
-    if (wb * wpb > 64 * 1024) return hipErrorInvalidValue;
+    // waves a workgroup: the most waves a CU can hold by LDS (160 KB; 13.6 KB
+    // a wave at K_I = 16, K_L = 64 takes 11 as single waves, 8 as groups of 4)
+    int wpb = 0, best = -1;
+    for (int w = 4; w >= 1; --w) {
+      if (wb * w > 64 * 1024) continue;
+      const int fit = w * (int)((size_t)160 * 1024 / (wb * w));
+      if (fit > best) { best = fit; wpb = w; }
+    }
+    if (wpb == 0) return hipErrorInvalidValue;
     const dim3 g_((unsigned)((a.blk1 - a.blk0 + wpb - 1) / wpb)), b_(64 * wpb);
     const bool bf = a.t.dtype == kDtypeBF16, d128 = a.t.d == 128;
 #define HIKVP_LEAF_PAIRS(SPT_)                                                                          \
