@@ -395,9 +395,12 @@ atlaskv_status plan_call(const atlaskv_tensor* q, const atlaskv_tree_view_s* v,
   // top byte of a member's slot base.  With shorter spans the staging and
   // the per-member threshold cost the stream more than the smaller select
   // saves (measured: 100-leaf spans at K_L = 32 step 0.529 -> 0.574 ms;
-  // 215-leaf spans at K_L = 32 0.444 -> 0.434 ms; 463-leaf spans at K_L = 64
-  // unchanged, the select 119 -> 69 us and the stream 1102 -> 1130 us).
+  // 215-leaf spans at K_L = 32 0.444 -> 0.435 ms; 463-leaf spans at K_L = 64
+  // 1.398 -> 1.313 ms).  Not for leaf keys in host memory: there the link
+  // bounds the stream, and the filter's pauses between spans cost it more
+  // (m1e7 decode 17.5 -> 19.2 ms).
   if (mode != kModeFoldedDescent && (t.d == 64 || t.d == 128) && p.K[1] > 0 && p.K[2] > 0 &&
+      !(v->host_mask & (1 << 2)) &&
       v->maxfan[1] >= kLeafFilterRatio * (int64_t)p.K[2] && v->maxfan[1] <= kLeafFilterMaxFan &&
       p.c2max < kMaxMidCands) {
     p.leaf_fpad = (int)((v->maxfan[1] + 3) & ~(int64_t)3);
