@@ -56,11 +56,13 @@
  *   - attend calls are asynchronous on their stream; device faults surface at
  *     the caller's next synchronisation.  Calls on different streams need
  *     separate workspaces; calls sharing a workspace must be stream-ordered.
- *     For query blocks under 16 tokens (decode) and unless phase events are
- *     requested, the causal sequence half runs on a second stream that the
- *     view owns (default priority), forked from the call's stream by an
- *     event before the KG kernels and joined back before the merge, so it
- *     overlaps the KG half; longer query blocks run it after the KG half.
+ *     Unless phase events are requested, the causal sequence half runs on a
+ *     second stream that the view owns (default priority), forked by an
+ *     event and joined back before the merge, so it overlaps the KG half:
+ *     for query blocks under 16 tokens (decode) it is forked from the call's
+ *     stream before the KG kernels, for longer blocks from the last descent
+ *     part (after its root phase when the descent runs in two parts, else
+ *     just before its leaf scoring).
  *     With 16384 query rows or more (B*N*Hq, or groups for shared
  *     selections) and two KV heads or more, the KG descent itself runs in two
  *     concurrent parts (the two halves of the KV heads, which share no index
