@@ -34,6 +34,10 @@
 //               members past a bucket's fixed slots, from its list.
 //   k_leaf_select  one wave (or workgroup) per row: Top-K_L, then the KG softmax over the
 //               selected leaves and the weighted sum of their values.
+//   k_leaf_score_filtered / k_leaf_select_pairs  the same two steps when mids
+//               have at least 4 K_L children: the stream keeps, per member
+//               and span, only the leaves that can still be among the row's
+//               K_L best, and the select reads just those.
 #include <hip/hip_runtime.h>
 
 #include "hikvp_device.h"
@@ -1173,7 +1177,8 @@ __device__ inline void score_member_group(const StepArgs& a, const char* kp, int
 // members is scored with exactly the arithmetic of score_member_group, but
 // the scores go to the wave's LDS stage [leaf_nst][leaf_fpad] instead of the
 // workspace.  Then, member by member: T_b, the K_L-th largest score of the
-// span to 24 bits of its order key (a lower bound), is at most the K_L-th
+// span cut to the top 16 bits of its order key (two 8-bit radix passes over
+// the staged keys; a lower bound of that score), is at most the K_L-th
 // largest score of the member's whole leaf candidate list (the span's K_L
 // best are candidates of that list), so every candidate the row's select can
 // take -- above its band or inside it, i.e. f >= T - W with T >= T_b -- has
