@@ -142,6 +142,15 @@ def test_shared_ragged_dtypes_and_head_dims(share, dtype, d):
 
 
 @pytest.mark.parametrize("share", [KVG, SEQ])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_shared_filtered_leaf_stream(share, dtype, d):
+    """Mids with at least four times K_L children (ragged spans of 15 to 728
+    leaves): the group descent runs the filtered leaf stream; in bf16 with
+    the summed query's residual pass and its rounding bound in the margin."""
+    check(_small(31, dtype=dtype, d=d, M_I=40, M=6000), share)
+
+
+@pytest.mark.parametrize("share", [KVG, SEQ])
 @pytest.mark.parametrize("Hq,dtype,d", [(6, "bf16", 128), (12, "f32", 64), (16, "bf16", 64)])
 def test_shared_group_sizes(share, Hq, dtype, d):
     """KV groups of 3, 6 and 8 query heads: the KG kernel takes a group's
