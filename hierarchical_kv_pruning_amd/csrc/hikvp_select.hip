@@ -1785,10 +1785,13 @@ __host__ inline bool wide_width(int d) { return d > 128 && d <= kMaxWideD && d %
   } while (0)
 
 // Per-row select shape: one wave per row while the list fits 16 scores per
-// lane, else a 256-thread workgroup with 8, 16 or 32 scores per thread held
-// in registers (the fewest that cover the list: fewer registers held means
-// more rows in flight, which these latency-bound kernels need); lists above
-// 8192 are re-read from the workspace in every pass.
+// lane, else a 256-thread workgroup; a wave holds 8, 13 or 16 scores a lane,
+// a workgroup 8, 16 or 32 a thread, in registers (the fewest that cover the
+// list: fewer registers held means more rows in flight, which these
+// latency-bound kernels need; 13 for the 800-candidate lists of 8 mids x 100
+// leaves takes 98 -> 89 registers, 4 -> 5 waves a SIMD: leaf Top-K + KG 72 ->
+// 64 us at 16384 rows); lists above 8192 are re-read from the workspace in
+// every pass.
 #define HIKVP_SELECT_LAUNCH(a, cap, KERNEL, Kc, Kp, s)                                               \
   do {                                                                                               \
     const int64_t cap_ = (cap);                                                                      \
@@ -1799,6 +1802,8 @@ __host__ inline bool wide_width(int d) { return d > 128 && d <= kMaxWideD && d %
       const unsigned blocks = (unsigned)(((a).blk1 - (a).blk0 + wpb - 1) / wpb);                     \
       if (cap_ <= 64 * 8)                                                                            \
         HIKVP_DISPATCH_SEL((a).t.dtype, (a).t.d, KERNEL, 64, 8, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb); \
+      else if (cap_ <= 64 * 13)                                                                      \
+        HIKVP_DISPATCH_SEL((a).t.dtype, (a).t.d, KERNEL, 64, 13, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb); \
       else                                                                                           \
         HIKVP_DISPATCH_SEL((a).t.dtype, (a).t.d, KERNEL, 64, 16, dim3(blocks), dim3(64 * wpb), wb * wpb, s, a, wb); \
     } else {                                                                                         \
